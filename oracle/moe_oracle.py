@@ -1,0 +1,325 @@
+"""Plain, slow, fp64 CPU oracle for the routed Mixture-of-Experts FFN.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code, table or
+helper with the HIP library; the only thing both sides consume is the seeded
+input data made by ``block_quantized_expert_amd.inputs``.
+
+What it computes, and where the pages define it (pages cited by title):
+
+* [Kernel Guide] "DeepSeek-V4-Flash 284B (13.17B Active) -- Deep-Dive
+  Mathematical & Kernel Guide" (llama-modchip):
+  - section 1 (Architectural Profile): 256 routed experts + 1 shared, 6 routed
+    experts active, routed weight scale 1.5; learned layers gate with
+    SQRT_SOFTPLUS; hash layers map a token id to 6 experts through the
+    ``ffn_gate_tid2eid`` table.
+  - section 3.2, MoE combine equation: y = e_shared(x) + sum_i w_i e_{k_i}(x)
+    with sum_i w_i = 1.5.
+  - section 4, SwiGLU equation: h = SiLU(W_gate x) * (W_up x), y = W_down h,
+    h_j = g_j / (1 + exp(-g_j)) * u_j.
+* [colibri] "DeepSeek V4 target engine (CPU + optional CUDA tier)",
+  introduction: routed experts are native fp4 (MXFP4); the dense set is
+  fp8-e4m3 with UE8M0 block scales.
+* [cism] "Development Snapshot Validation", 4-bit quantization scheme study
+  table: MXFP4 is "E2M1 + E8M0, blocks of 32" at 4.25 bits per weight.
+
+Readings taken where the pages are silent (each also listed in the design doc):
+
+* E2M1 element: sign bit 3, two exponent bits (bias 1), one mantissa bit,
+  i.e. the OCP MX v1.0 element; magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}.
+* UE8M0 scale byte u means 2**(u - 127); u = 255 is NaN (never generated).
+* Packing: row-major ``[out][in]`` rows; byte b of a row holds element 2b in
+  its low nibble and element 2b+1 in its high nibble; scale j of a row covers
+  elements 32j .. 32j+31 (blocks run along the reduction dimension).
+* fp8 e4m3 is the OCP "fn" variant (bias 7, max 448, no infinities, S.1111.111
+  is NaN); one UE8M0 scale per 128 consecutive elements of a row.
+* Learned routing selects on the raw fp32 logits (sqrt o softplus is strictly
+  increasing, so the set equals selection on scores); ties go to the lower
+  expert index; output slot i = 0 holds the largest.  Expert groups are read
+  as one group (plain top-k over all experts).
+* Weights: s = sqrt(softplus(logit)), w = scale * s / sum(s) over the top-k,
+  evaluated in fp64 and rounded to fp32 once.
+* Grouping: perm lists flat indices f = t*top_k + i stably sorted by expert
+  (ascending f inside an expert); inv_perm[perm[p]] = p.
+* The shared expert sees every token with weight 1 and has its own
+  intermediate size.  No clamp is applied to the SwiGLU gate.
+* y is accumulated in fp64 and rounded to fp32 (round-to-nearest-even) once.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# ----------------------------------------------------------------------------
+# Element formats (closed forms, one value at a time)
+# ----------------------------------------------------------------------------
+
+
+def e2m1_value(code: int) -> float:
+    """Value of one 4-bit E2M1 code (OCP MX element; [cism] 4-bit study)."""
+    code = int(code)
+    if not 0 <= code < 16:
+        raise ValueError("e2m1 code out of range")
+    sign = -1.0 if code & 0x8 else 1.0
+    exp_field = (code >> 1) & 0x3
+    mant = code & 0x1
+    if exp_field == 0:
+        mag = 0.5 * mant  # subnormal: 0 or 0.5
+    else:
+        mag = math.ldexp(1.0 + 0.5 * mant, exp_field - 1)
+    return sign * mag  # code 8 gives -0.0
+
+
+def ue8m0_value(u: int) -> float:
+    """Value of one UE8M0 scale byte: 2**(u-127); 255 is NaN."""
+    u = int(u)
+    if not 0 <= u < 256:
+        raise ValueError("ue8m0 byte out of range")
+    if u == 255:
+        return math.nan
+    return math.ldexp(1.0, u - 127)
+
+
+def e4m3_value(code: int) -> float:
+    """Value of one OCP fp8 E4M3 ("fn") byte: bias 7, no inf, S.1111.111 NaN."""
+    code = int(code)
+    if not 0 <= code < 256:
+        raise ValueError("e4m3 code out of range")
+    sign = -1.0 if code & 0x80 else 1.0
+    exp_field = (code >> 3) & 0xF
+    mant = code & 0x7
+    if exp_field == 0xF and mant == 0x7:
+        return math.nan
+    if exp_field == 0:
+        mag = math.ldexp(mant / 8.0, 1 - 7)  # subnormal: m * 2**-9
+    else:
+        mag = math.ldexp(1.0 + mant / 8.0, exp_field - 7)
+    return sign * mag
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 is the upper 16 bits of an IEEE binary32; widen exactly."""
+    b = np.asarray(bits).astype(np.uint16).astype(np.uint32) << 16
+    with np.errstate(invalid="ignore"):
+        return b.view(np.float32).astype(np.float64)
+
+
+# ----------------------------------------------------------------------------
+# Block decode (tables built from the closed forms above)
+# ----------------------------------------------------------------------------
+
+_E2M1_TABLE = np.array([e2m1_value(c) for c in range(16)], dtype=np.float64)
+_UE8M0_TABLE = np.array([ue8m0_value(u) for u in range(256)], dtype=np.float64)
+_E4M3_TABLE = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+
+
+def decode_mxfp4(codes: np.ndarray, scales: np.ndarray, cols: int) -> np.ndarray:
+    """Decode an MXFP4 matrix ``[rows][cols/2]`` codes + ``[rows][cols/32]``
+    scales to fp64 ``[rows][cols]`` (exact)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.uint8)
+    rows = codes.shape[0]
+    if codes.shape != (rows, cols // 2) or scales.shape != (rows, cols // 32):
+        raise ValueError("mxfp4 shapes do not match cols")
+    vals = np.empty((rows, cols), dtype=np.float64)
+    vals[:, 0::2] = _E2M1_TABLE[codes & 0x0F]  # low nibble: even element
+    vals[:, 1::2] = _E2M1_TABLE[codes >> 4]  # high nibble: odd element
+    vals = vals.reshape(rows, cols // 32, 32) * _UE8M0_TABLE[scales][:, :, None]
+    return vals.reshape(rows, cols)
+
+
+def decode_fp8_b128(codes: np.ndarray, scales: np.ndarray, cols: int) -> np.ndarray:
+    """Decode fp8-e4m3 ``[rows][cols]`` with one UE8M0 per 128 elements of a
+    row to fp64 (exact)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.uint8)
+    rows = codes.shape[0]
+    if codes.shape != (rows, cols) or scales.shape != (rows, cols // 128):
+        raise ValueError("fp8 shapes do not match cols")
+    vals = _E4M3_TABLE[codes].reshape(rows, cols // 128, 128)
+    vals = vals * _UE8M0_TABLE[scales][:, :, None]
+    return vals.reshape(rows, cols)
+
+
+def decode_proj(proj: dict, index, cols: int, rows_subset=None) -> np.ndarray:
+    """Decode one expert matrix of a projection description.
+
+    ``proj`` = {"type": "mxfp4" | "fp8_e4m3_b128", "codes": ..., "scales": ...};
+    ``codes[index]`` / ``scales[index]`` select the expert (``index`` None for
+    an unstacked matrix).  ``rows_subset`` restricts the decoded rows.
+    """
+    codes = proj["codes"] if index is None else proj["codes"][index]
+    scales = proj["scales"] if index is None else proj["scales"][index]
+    codes = np.asarray(codes)
+    scales = np.asarray(scales)
+    if rows_subset is not None:
+        codes = codes[rows_subset]
+        scales = scales[rows_subset]
+    if proj["type"] == "mxfp4":
+        return decode_mxfp4(codes, scales, cols)
+    if proj["type"] == "fp8_e4m3_b128":
+        return decode_fp8_b128(codes, scales, cols)
+    raise ValueError("unknown weight type %r" % (proj["type"],))
+
+
+def decode_activations(x: np.ndarray, act_type: str) -> np.ndarray:
+    """Activations as given: fp32 values or bf16 bit patterns -> fp64."""
+    if act_type == "f32":
+        return np.asarray(x, dtype=np.float32).astype(np.float64)
+    if act_type == "bf16":
+        return bf16_bits_to_f64(x)
+    raise ValueError("unknown activation type %r" % (act_type,))
+
+
+# ----------------------------------------------------------------------------
+# Routing ([Kernel Guide] section 1 and section 3.2)
+# ----------------------------------------------------------------------------
+
+
+def softplus(v: float) -> float:
+    """log(1 + e^v) written so that it neither overflows nor cancels."""
+    return max(v, 0.0) + math.log1p(math.exp(-abs(v)))
+
+
+def route_topk(logits: np.ndarray, top_k: int, routed_scale: float):
+    """Learned SQRT_SOFTPLUS router.
+
+    For each token: the ``top_k`` largest fp32 logits (ties to the lower
+    expert index, slot 0 = largest), s_i = sqrt(softplus(l_i)),
+    w_i = routed_scale * s_i / sum_j s_j.  Returns ids int32 [N][k] and
+    weights fp32 [N][k].
+    """
+    logits = np.asarray(logits, dtype=np.float32)
+    n_tokens, n_experts = logits.shape
+    if not 0 < top_k <= n_experts:
+        raise ValueError("bad top_k")
+    ids = np.zeros((n_tokens, top_k), dtype=np.int32)
+    w = np.zeros((n_tokens, top_k), dtype=np.float32)
+    for t in range(n_tokens):
+        row = [float(v) for v in logits[t]]
+        order = sorted(range(n_experts), key=lambda e: (-row[e], e))
+        chosen = order[:top_k]
+        s = [math.sqrt(softplus(row[e])) for e in chosen]
+        total = 0.0
+        for si in s:
+            total += si
+        for i, e in enumerate(chosen):
+            ids[t, i] = e
+            w[t, i] = np.float32(routed_scale * s[i] / total)
+    return ids, w
+
+
+def route_hash(token_ids: np.ndarray, tid2eid: np.ndarray, tid2w: np.ndarray):
+    """Token-id hash routing: the table row of the token, in table order."""
+    token_ids = np.asarray(token_ids)
+    ids = np.asarray(tid2eid)[token_ids].astype(np.int32)
+    w = np.asarray(tid2w)[token_ids].astype(np.float32)
+    return ids, w
+
+
+# ----------------------------------------------------------------------------
+# Grouping (token-to-expert bucketing)
+# ----------------------------------------------------------------------------
+
+
+def group(ids: np.ndarray, n_experts: int):
+    """counts, exclusive offsets, stable permutation and its inverse.
+
+    Two plain passes: count, then place each flat index f = t*k + i (in
+    ascending f) at the next free position of its expert.
+    """
+    flat = [int(v) for v in np.asarray(ids).reshape(-1)]
+    counts = [0] * n_experts
+    for e in flat:
+        counts[e] += 1
+    offsets = [0] * (n_experts + 1)
+    for e in range(n_experts):
+        offsets[e + 1] = offsets[e] + counts[e]
+    fill = offsets[:n_experts]
+    perm = [0] * len(flat)
+    inv_perm = [0] * len(flat)
+    for f, e in enumerate(flat):
+        p = fill[e]
+        perm[p] = f
+        inv_perm[f] = p
+        fill[e] = p + 1
+    as_i32 = lambda v: np.array(v, dtype=np.int32)  # noqa: E731
+    return as_i32(counts), as_i32(offsets), as_i32(perm), as_i32(inv_perm)
+
+
+# ----------------------------------------------------------------------------
+# Expert FFN and combine ([Kernel Guide] section 4 and section 3.2)
+# ----------------------------------------------------------------------------
+
+
+def silu(g: np.ndarray) -> np.ndarray:
+    """g / (1 + exp(-g)) in fp64 (the SwiGLU gate, no clamp)."""
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
+def expert_ffn(xs: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray,
+               w_down: np.ndarray) -> np.ndarray:
+    """o = W_down (SiLU(W_gate x) * (W_up x)) for each row x of ``xs``."""
+    g = xs @ w_gate.T
+    u = xs @ w_up.T
+    h = silu(g) * u
+    return h @ w_down.T
+
+
+def ffn(layer: dict, x: np.ndarray, act_type: str, ids: np.ndarray,
+        w: np.ndarray, tokens=None, out_rows=None, with_shared: bool = True):
+    """MoE FFN output y (fp32) for ``tokens`` (default: all) and output
+    features ``out_rows`` (default: all).
+
+    y_t = e_shared(x_t) + sum_i w[t,i] e_{ids[t,i]}(x_t), accumulated in fp64,
+    rounded to fp32 once.  Each routed expert's three matrices are decoded to
+    fp64 once; the tokens that chose it are found by scanning ``ids``.
+    """
+    hidden, inter = layer["hidden"], layer["inter"]
+    ids = np.asarray(ids)
+    w = np.asarray(w, dtype=np.float32)
+    n_tokens, top_k = ids.shape
+    tokens = list(range(n_tokens)) if tokens is None else [int(t) for t in tokens]
+    xs = decode_activations(np.asarray(x)[tokens], act_type)
+    n_out = hidden if out_rows is None else len(out_rows)
+    y = np.zeros((len(tokens), n_out), dtype=np.float64)
+
+    members = {}  # expert -> list of (row in xs, weight)
+    for j, t in enumerate(tokens):
+        for i in range(top_k):
+            members.setdefault(int(ids[t, i]), []).append((j, float(w[t, i])))
+    for e in sorted(members):
+        wg = decode_proj(layer["gate"], e, hidden)
+        wu = decode_proj(layer["up"], e, hidden)
+        wd = decode_proj(layer["down"], e, inter, out_rows)
+        rows = [j for j, _ in members[e]]
+        o = expert_ffn(xs[rows], wg, wu, wd)
+        for r, (j, wt) in enumerate(members[e]):
+            y[j] += wt * o[r]
+
+    shared = layer.get("shared")
+    if with_shared and shared is not None:
+        s_inter = shared["inter"]
+        wg = decode_proj(shared["gate"], None, hidden)
+        wu = decode_proj(shared["up"], None, hidden)
+        wd = decode_proj(shared["down"], None, s_inter, out_rows)
+        y += expert_ffn(xs, wg, wu, wd)
+    return y.astype(np.float32)
+
+
+def moe_layer_forward(layer: dict, x: np.ndarray, act_type: str, routing: dict,
+                      top_k: int, routed_scale: float = 1.5, tokens=None,
+                      out_rows=None, with_shared: bool = True):
+    """Whole path: route (learned or hash), then the FFN and combine."""
+    if routing["kind"] == "learned":
+        ids, w = route_topk(routing["logits"], top_k, routed_scale)
+    elif routing["kind"] == "hash":
+        ids, w = route_hash(routing["token_ids"], routing["tid2eid"], routing["tid2w"])
+    else:
+        raise ValueError("unknown routing kind")
+    y = ffn(layer, x, act_type, ids, w, tokens, out_rows, with_shared)
+    return ids, w, y
