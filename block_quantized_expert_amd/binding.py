@@ -1,0 +1,226 @@
+"""Thin ctypes binding over libmoe.so (declared in include/moe.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  Tensors are passed as device pointers (``data_ptr()``) together with
+the current HIP stream of torch.  There is no fallback: if the library is
+missing, loading fails loudly.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE = range(5)
+MOE_ACT_F32, MOE_ACT_BF16 = 0, 1
+MOE_W_MXFP4, MOE_W_FP8E4M3_B128 = 0, 1
+MOE_DEVERR_EXPERT_ID, MOE_DEVERR_TOKEN_ID = 1, 2
+
+# every symbol include/moe.h declares
+EXPORTED = ["moe_route", "moe_route_hash", "moe_group_workspace_bytes", "moe_group",
+            "moe_ffn_workspace_bytes", "moe_ffn_forward", "moe_ffn_gate_up", "moe_ffn_down",
+            "moe_status_string"]
+
+WEIGHT_TYPES = {"mxfp4": MOE_W_MXFP4, "fp8_e4m3_b128": MOE_W_FP8E4M3_B128}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__("%s: %s" % (where, status_string(status)))
+        self.status = status
+
+
+class MoeProj(ctypes.Structure):
+    _fields_ = [("type", ctypes.c_int32), ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+
+
+class MoeLayer(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("gate", MoeProj), ("up", MoeProj), ("down", MoeProj),
+                ("has_shared", ctypes.c_int32), ("shared_inter", ctypes.c_int32),
+                ("shared_gate", MoeProj), ("shared_up", MoeProj), ("shared_down", MoeProj)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libmoe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError("libmoe.so is not built (%s); run "
+                               "python -m block_quantized_expert_amd.build" % _LIB_PATH)
+        L = ctypes.CDLL(_LIB_PATH)
+        P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.moe_route.argtypes = [P, I, I, I, F, P, P, P]
+        L.moe_route_hash.argtypes = [P, I, P, P, I, I, I, P, P, P, P]
+        L.moe_group_workspace_bytes.argtypes = [I, I, I]
+        L.moe_group_workspace_bytes.restype = S
+        L.moe_group.argtypes = [P, I, I, I, P, P, P, P, P, P, S, P]
+        L.moe_ffn_workspace_bytes.argtypes = [ctypes.POINTER(MoeLayer), I]
+        L.moe_ffn_workspace_bytes.restype = S
+        ffn_args = [ctypes.POINTER(MoeLayer), P, I, I, P, P, P, P, P, P, P, S, P]
+        for name in ("moe_ffn_forward", "moe_ffn_gate_up", "moe_ffn_down"):
+            getattr(L, name).argtypes = ffn_args
+        for name in ("moe_route", "moe_route_hash", "moe_group", "moe_ffn_forward",
+                     "moe_ffn_gate_up", "moe_ffn_down"):
+            getattr(L, name).restype = ctypes.c_int
+        L.moe_status_string.argtypes = [ctypes.c_int]
+        L.moe_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().moe_status_string(status).decode()
+
+
+def _check(status: int, where: str):
+    if status != MOE_OK:
+        raise MoeError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+# ----------------------------------------------------------------------------
+# Layer description
+# ----------------------------------------------------------------------------
+
+
+class Layer:
+    """A moe_layer over device tensors; keeps the tensors alive.
+
+    ``weights`` is the dict made by ``inputs.make_layer`` (stacked routed
+    tensors [E][rows][...], optional ``shared``)."""
+
+    def __init__(self, weights: dict, top_k: int):
+        self.weights = weights
+        L = MoeLayer()
+        L.hidden = weights["hidden"]
+        L.inter = weights["inter"]
+        L.n_experts = weights["n_experts"]
+        L.top_k = top_k
+        for name in ("gate", "up", "down"):
+            setattr(L, name, self._proj(weights[name]))
+        shared = weights.get("shared")
+        L.has_shared = 1 if shared is not None else 0
+        if shared is not None:
+            L.shared_inter = shared["inter"]
+            L.shared_gate = self._proj(shared["gate"])
+            L.shared_up = self._proj(shared["up"])
+            L.shared_down = self._proj(shared["down"])
+        self.c = L
+
+    @staticmethod
+    def _proj(p: dict) -> MoeProj:
+        return MoeProj(WEIGHT_TYPES[p["type"]], p["codes"].data_ptr(), p["scales"].data_ptr())
+
+    @property
+    def hidden(self):
+        return self.c.hidden
+
+    @property
+    def top_k(self):
+        return self.c.top_k
+
+    def workspace_bytes(self, n_tokens: int) -> int:
+        return lib().moe_ffn_workspace_bytes(ctypes.byref(self.c), n_tokens)
+
+
+# ----------------------------------------------------------------------------
+# Entry points (same names as the C ABI)
+# ----------------------------------------------------------------------------
+
+
+def moe_route(logits, top_k, routed_scale=1.5, ids=None, w=None, stream=None):
+    n, e = logits.shape
+    dev = logits.device
+    ids = torch.empty((n, top_k), dtype=torch.int32, device=dev) if ids is None else ids
+    w = torch.empty((n, top_k), dtype=torch.float32, device=dev) if w is None else w
+    _check(lib().moe_route(_ptr(logits), n, e, top_k, routed_scale, _ptr(ids), _ptr(w),
+                           _stream(stream)), "moe_route")
+    return ids, w
+
+
+def moe_route_hash(token_ids, tid2eid, tid2w, n_experts, ids=None, w=None, dev_error=None,
+                   stream=None):
+    n = token_ids.shape[0]
+    vocab, top_k = tid2eid.shape
+    dev = token_ids.device
+    ids = torch.empty((n, top_k), dtype=torch.int32, device=dev) if ids is None else ids
+    w = torch.empty((n, top_k), dtype=torch.float32, device=dev) if w is None else w
+    _check(lib().moe_route_hash(_ptr(token_ids), n, _ptr(tid2eid), _ptr(tid2w), vocab, n_experts,
+                                top_k, _ptr(ids), _ptr(w), _ptr(dev_error), _stream(stream)),
+           "moe_route_hash")
+    return ids, w
+
+
+def moe_group(ids, n_experts, out=None, dev_error=None, stream=None):
+    """Returns (counts, offsets, perm, inv_perm)."""
+    n, k = ids.shape
+    dev = ids.device
+    if out is None:
+        out = (torch.empty(n_experts, dtype=torch.int32, device=dev),
+               torch.empty(n_experts + 1, dtype=torch.int32, device=dev),
+               torch.empty(n * k, dtype=torch.int32, device=dev),
+               torch.empty(n * k, dtype=torch.int32, device=dev))
+    counts, offsets, perm, inv_perm = out
+    _check(lib().moe_group(_ptr(ids), n, k, n_experts, _ptr(counts), _ptr(offsets), _ptr(perm),
+                           _ptr(inv_perm), _ptr(dev_error), None, 0, _stream(stream)),
+           "moe_group")
+    return counts, offsets, perm, inv_perm
+
+
+def _ffn_call(name, layer: Layer, x, w, grouping, y, workspace, stream):
+    n = x.shape[0]
+    x_type = MOE_ACT_BF16 if x.dtype == torch.bfloat16 else MOE_ACT_F32
+    if y is None:
+        y = torch.empty((n, layer.hidden), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(layer.workspace_bytes(n), 1), dtype=torch.uint8,
+                                device=x.device)
+    counts, offsets, perm, inv_perm = grouping
+    fn = getattr(lib(), name)
+    _check(fn(ctypes.byref(layer.c), _ptr(x), x_type, n, _ptr(w), _ptr(counts), _ptr(offsets),
+              _ptr(perm), _ptr(inv_perm), _ptr(y), _ptr(workspace), workspace.numel(),
+              _stream(stream)), name)
+    return y
+
+
+def moe_ffn_forward(layer: Layer, x, w, grouping, y=None, workspace=None, stream=None):
+    return _ffn_call("moe_ffn_forward", layer, x, w, grouping, y, workspace, stream)
+
+
+def moe_ffn_gate_up(layer: Layer, x, w, grouping, y=None, workspace=None, stream=None):
+    return _ffn_call("moe_ffn_gate_up", layer, x, w, grouping, y, workspace, stream)
+
+
+def moe_ffn_down(layer: Layer, x, w, grouping, y=None, workspace=None, stream=None):
+    return _ffn_call("moe_ffn_down", layer, x, w, grouping, y, workspace, stream)
+
+
+def forward(layer: Layer, x, routing: dict, routed_scale=1.5, stream=None):
+    """Route, group and run the FFN (all on the device).  Returns
+    (y, ids, w, grouping)."""
+    if routing["kind"] == "learned":
+        ids, w = moe_route(routing["logits"], layer.top_k, routed_scale, stream=stream)
+    else:
+        ids, w = moe_route_hash(routing["token_ids"], routing["tid2eid"], routing["tid2w"],
+                                layer.c.n_experts, stream=stream)
+    grouping = moe_group(ids, layer.c.n_experts, stream=stream)
+    y = moe_ffn_forward(layer, x, w, grouping, stream=stream)
+    return y, ids, w, grouping

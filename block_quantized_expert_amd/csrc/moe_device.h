@@ -1,0 +1,67 @@
+// Device-side building blocks for gfx950 (CDNA4): block-format decode to
+// bfloat16 with the hardware scaled converts, the 16x16x32 bf16 MFMA, and
+// wavefront helpers.  Everything here is for 64-wide wavefronts.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// UE8M0 byte u -> the fp32 number 2^(u-127) (u in 1..254).
+__device__ __forceinline__ float ue8m0_to_f32(uint32_t u) { return __uint_as_float(u << 23); }
+
+__device__ __forceinline__ bf16x8 join(bf16x2 a, bf16x2 b, bf16x2 c, bf16x2 d) {
+  bf16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+// Eight E2M1 codes packed in one little-endian word (element 2b in the low
+// nibble of byte b) -> eight bf16 values, each times the power of two s.
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t w, float s) {
+  return join(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0),
+              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1),
+              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2),
+              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3));
+}
+
+// Eight OCP E4M3 bytes (two little-endian words) -> eight bf16 values times s.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t w0, uint32_t w1, float s) {
+  return join(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, false),
+              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, true),
+              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, false),
+              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, true));
+}
+
+// D = A * B + C on one 16x16x32 bf16 tile with fp32 accumulation.
+// Operand lanes: lane l supplies A[l % 16][8*(l/16) .. +7] and
+// B[8*(l/16) .. +7][l % 16]; the result lane l holds D[4*(l/16) + r][l % 16]
+// for r = 0..3.
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 load16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// v = hi + lo with hi = bf16(v) and lo = bf16(v - hi), both round to
+// nearest even; hi + lo carries 16 significant bits of v.
+__device__ __forceinline__ void split_bf16(float v, __bf16& hi, __bf16& lo) {
+  hi = static_cast<__bf16>(v);
+  lo = static_cast<__bf16>(v - static_cast<float>(hi));
+}
+
+}  // namespace moe

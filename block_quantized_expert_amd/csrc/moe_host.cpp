@@ -1,0 +1,127 @@
+// Host-side argument checks and workspace planning (see moe_host.h).
+#include "moe_host.h"
+
+#include <math.h>
+
+namespace moe {
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool dim_ok(int v) { return v >= 128 && v <= MOE_MAX_DIM && v % 128 == 0; }
+
+moe_status check_tokens_k(int n_tokens, int n_experts, int top_k) {
+  if (n_tokens < 0 || n_experts <= 0 || top_k <= 0) return MOE_ERR_INVALID;
+  if (top_k > n_experts) return MOE_ERR_INVALID;
+  if (n_experts > MOE_MAX_EXPERTS || top_k > MOE_MAX_TOP_K) return MOE_ERR_UNSUPPORTED;
+  if (n_tokens > MOE_MAX_TOKENS) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status check_proj(const moe_proj& p) {
+  if (p.type != MOE_W_MXFP4 && p.type != MOE_W_FP8E4M3_B128) return MOE_ERR_UNSUPPORTED;
+  if (p.codes == nullptr || p.scales == nullptr) return MOE_ERR_INVALID;
+  if (!aligned16(p.codes)) return MOE_ERR_INVALID;
+  return MOE_OK;
+}
+
+}  // namespace
+
+moe_status check_route(const float* logits, int n_tokens, int n_experts, int top_k,
+                       float routed_scale, const int32_t* ids, const float* w) {
+  moe_status s = check_tokens_k(n_tokens, n_experts, top_k);
+  if (s != MOE_OK) return s;
+  if (!(routed_scale > 0.0f) || !isfinite(routed_scale)) return MOE_ERR_INVALID;
+  if (n_tokens > 0 && (logits == nullptr || ids == nullptr || w == nullptr)) return MOE_ERR_INVALID;
+  return MOE_OK;
+}
+
+moe_status check_route_hash(const int32_t* token_ids, int n_tokens, const int32_t* tid2eid,
+                            const float* tid2w, int vocab, int n_experts, int top_k,
+                            const int32_t* ids, const float* w) {
+  moe_status s = check_tokens_k(n_tokens, n_experts, top_k);
+  if (s != MOE_OK) return s;
+  if (vocab <= 0) return MOE_ERR_INVALID;
+  if (n_tokens > 0 && (token_ids == nullptr || tid2eid == nullptr || tid2w == nullptr ||
+                       ids == nullptr || w == nullptr))
+    return MOE_ERR_INVALID;
+  return MOE_OK;
+}
+
+moe_status check_group(const int32_t* ids, int n_tokens, int top_k, int n_experts,
+                       const int32_t* counts, const int32_t* offsets, const int32_t* perm,
+                       const int32_t* inv_perm) {
+  moe_status s = check_tokens_k(n_tokens, n_experts, top_k);
+  if (s != MOE_OK) return s;
+  if (counts == nullptr || offsets == nullptr) return MOE_ERR_INVALID;
+  if (n_tokens > 0 && (ids == nullptr || perm == nullptr || inv_perm == nullptr))
+    return MOE_ERR_INVALID;
+  return MOE_OK;
+}
+
+moe_status check_layer(const moe_layer* layer) {
+  if (layer == nullptr) return MOE_ERR_INVALID;
+  moe_status s = check_tokens_k(0, layer->n_experts, layer->top_k);
+  if (s != MOE_OK) return s;
+  if (layer->hidden <= 0 || layer->inter <= 0) return MOE_ERR_INVALID;
+  if (!dim_ok(layer->hidden) || !dim_ok(layer->inter)) return MOE_ERR_UNSUPPORTED;
+  if ((s = check_proj(layer->gate)) != MOE_OK) return s;
+  if ((s = check_proj(layer->up)) != MOE_OK) return s;
+  if ((s = check_proj(layer->down)) != MOE_OK) return s;
+  // the kernels read one weight type for the routed matrices and one for
+  // the shared ones
+  if (layer->up.type != layer->gate.type || layer->down.type != layer->gate.type)
+    return MOE_ERR_UNSUPPORTED;
+  if (layer->has_shared != 0 && layer->has_shared != 1) return MOE_ERR_INVALID;
+  if (layer->has_shared) {
+    if (layer->shared_inter <= 0) return MOE_ERR_INVALID;
+    if (!dim_ok(layer->shared_inter)) return MOE_ERR_UNSUPPORTED;
+    if ((s = check_proj(layer->shared_gate)) != MOE_OK) return s;
+    if ((s = check_proj(layer->shared_up)) != MOE_OK) return s;
+    if ((s = check_proj(layer->shared_down)) != MOE_OK) return s;
+    if (layer->shared_up.type != layer->shared_gate.type ||
+        layer->shared_down.type != layer->shared_gate.type)
+      return MOE_ERR_UNSUPPORTED;
+  }
+  return MOE_OK;
+}
+
+moe_status plan_ffn(const moe_layer* layer, int n_tokens, FfnPlan* plan) {
+  if (n_tokens < 0) return MOE_ERR_INVALID;
+  if (n_tokens > MOE_MAX_TOKENS) return MOE_ERR_UNSUPPORTED;
+  const int64_t n = n_tokens;
+  plan->slots = n * layer->top_k + (layer->has_shared ? n : 0);
+  int64_t hs = layer->inter;
+  if (layer->has_shared && layer->shared_inter > hs) hs = layer->shared_inter;
+  plan->h_stride = hs;
+  const size_t h_bytes = align_up((size_t)(plan->slots * hs) * 2u, 256);
+  const size_t o_bytes = align_up((size_t)(plan->slots * layer->hidden) * 4u, 256);
+  plan->off_h_hi = 0;
+  plan->off_h_lo = h_bytes;
+  plan->off_obuf = 2 * h_bytes;
+  plan->total = 2 * h_bytes + o_bytes;
+  return MOE_OK;
+}
+
+moe_status check_ffn(const moe_layer* layer, const void* x, int x_type, int n_tokens,
+                     const float* topk_w, const int32_t* counts, const int32_t* offsets,
+                     const int32_t* perm, const int32_t* inv_perm, const float* y,
+                     const void* workspace, size_t workspace_bytes, FfnPlan* plan) {
+  moe_status s = check_layer(layer);
+  if (s != MOE_OK) return s;
+  if (n_tokens < 0) return MOE_ERR_INVALID;
+  if (x_type != MOE_ACT_F32 && x_type != MOE_ACT_BF16) return MOE_ERR_UNSUPPORTED;
+  if ((s = plan_ffn(layer, n_tokens, plan)) != MOE_OK) return s;
+  if (n_tokens == 0) return MOE_OK;
+  if (x == nullptr || topk_w == nullptr || counts == nullptr || offsets == nullptr ||
+      perm == nullptr || inv_perm == nullptr || y == nullptr)
+    return MOE_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(y)) return MOE_ERR_INVALID;
+  if (workspace == nullptr || workspace_bytes < plan->total) return MOE_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MOE_ERR_INVALID;
+  return MOE_OK;
+}
+
+}  // namespace moe

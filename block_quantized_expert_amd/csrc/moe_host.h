@@ -1,0 +1,44 @@
+// Host-side argument checks and workspace planning for the moe_* entry
+// points.  Pure host C++: no HIP call is made here, so every rule can be
+// exercised without a GPU.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// Byte layout of the moe_ffn workspace.
+//   h_hi, h_lo : bf16 [slots][h_stride]   SwiGLU output split into a bf16
+//                                         high part and a bf16 low part
+//   obuf       : fp32 [slots][hidden]     weighted expert outputs
+// A slot is one (token, routed expert) pair in grouped order
+// (p in [0, n_tokens*top_k)) or, for the shared expert, n_tokens*top_k + t.
+struct FfnPlan {
+  int64_t slots;
+  int64_t h_stride;
+  size_t off_h_hi;
+  size_t off_h_lo;
+  size_t off_obuf;
+  size_t total;
+};
+
+moe_status check_route(const float* logits, int n_tokens, int n_experts, int top_k,
+                       float routed_scale, const int32_t* ids, const float* w);
+moe_status check_route_hash(const int32_t* token_ids, int n_tokens, const int32_t* tid2eid,
+                            const float* tid2w, int vocab, int n_experts, int top_k,
+                            const int32_t* ids, const float* w);
+moe_status check_group(const int32_t* ids, int n_tokens, int top_k, int n_experts,
+                       const int32_t* counts, const int32_t* offsets, const int32_t* perm,
+                       const int32_t* inv_perm);
+moe_status check_layer(const moe_layer* layer);
+// Fills `plan` for a valid layer; the layer must have passed check_layer.
+moe_status plan_ffn(const moe_layer* layer, int n_tokens, FfnPlan* plan);
+moe_status check_ffn(const moe_layer* layer, const void* x, int x_type, int n_tokens,
+                     const float* topk_w, const int32_t* counts, const int32_t* offsets,
+                     const int32_t* perm, const int32_t* inv_perm, const float* y,
+                     const void* workspace, size_t workspace_bytes, FfnPlan* plan);
+
+}  // namespace moe

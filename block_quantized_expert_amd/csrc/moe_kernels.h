@@ -1,0 +1,49 @@
+// Internal launch interface between the C ABI (moe_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// Everything the FFN kernels read, passed by value.
+struct FfnParams {
+  int n_tokens;
+  int top_k;
+  int n_experts;
+  int hidden;
+  int inter;         // routed intermediate size
+  int shared_inter;  // shared intermediate size (0 without a shared expert)
+  int has_shared;
+  int w_type;   // routed weight type (moe_weight_type)
+  int sw_type;  // shared weight type
+  int x_f32;    // activations are fp32 (else bf16)
+  const uint8_t *gate_c, *gate_s, *up_c, *up_s, *down_c, *down_s;
+  const uint8_t *sgate_c, *sgate_s, *sup_c, *sup_s, *sdown_c, *sdown_s;
+  const void* x;
+  const float* topk_w;
+  const int32_t* counts;
+  const int32_t* offsets;
+  const int32_t* perm;
+  const int32_t* inv_perm;
+  __bf16* h_hi;  // [slots][h_stride]
+  __bf16* h_lo;
+  int64_t h_stride;
+  float* obuf;  // [slots][hidden]
+  float* y;     // [n_tokens][hidden]
+};
+
+hipError_t launch_route(const float* logits, int n_tokens, int n_experts, int top_k,
+                        float routed_scale, int32_t* ids, float* w, hipStream_t stream);
+hipError_t launch_route_hash(const int32_t* token_ids, int n_tokens, const int32_t* tid2eid,
+                             const float* tid2w, int vocab, int n_experts, int top_k,
+                             int32_t* ids, float* w, int32_t* dev_error, hipStream_t stream);
+hipError_t launch_group(const int32_t* ids, int n_tokens, int top_k, int n_experts,
+                        int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                        int32_t* dev_error, hipStream_t stream);
+hipError_t launch_ffn_gate_up(const FfnParams& p, hipStream_t stream);
+hipError_t launch_ffn_down(const FfnParams& p, hipStream_t stream);
+
+}  // namespace moe

@@ -49,6 +49,7 @@ class Workload:
     seed: int
     vocab: int = 129280
     min_gap: float = 1e-3  # every pair of logits of a token differs by this
+    shared_inter: int = 0  # 0: same as inter
 
 
 WORKLOADS = {
@@ -148,10 +149,13 @@ PROJ_IDS = {"gate": 0, "up": 1, "down": 2,
 
 def proj_shape(wl: Workload, proj: str):
     """(rows, cols) of one expert matrix: rows are output features."""
+    inter = wl.inter
+    if proj.startswith("shared_") and wl.shared_inter:
+        inter = wl.shared_inter
     base = proj.replace("shared_", "")
     if base in ("gate", "up"):
-        return wl.inter, wl.hidden
-    return wl.hidden, wl.inter
+        return inter, wl.hidden
+    return wl.hidden, inter
 
 
 def _mxfp4_block(wl, proj, copy, first, n_exp, device):
@@ -213,7 +217,7 @@ def make_layer(wl: Workload, device="cpu", copy: int = 0, experts=None,
             scales = {e: v[1] for e, v in ew.items()}
         layer[proj] = {"type": "mxfp4", "codes": codes, "scales": scales}
     if with_shared:
-        shared = {"inter": wl.inter}
+        shared = {"inter": wl.shared_inter or wl.inter}
         for proj in ("shared_gate", "shared_up", "shared_down"):
             if wl.shared == "mxfp4":
                 c, s = _mxfp4_block(wl, proj, copy, 0, 1, device)

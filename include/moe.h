@@ -1,0 +1,208 @@
+/*
+ * moe.h -- C ABI of libmoe.so: the routed Mixture-of-Experts FFN of a
+ * DeepSeek-V4-Flash-shaped layer with block-quantized (MXFP4) experts,
+ * computed by hand-written HIP kernels for gfx950 (MI355X).
+ *
+ * The method (pages cited by title):
+ *   "DeepSeek-V4-Flash 284B (13.17B Active) -- Deep-Dive Mathematical &
+ *   Kernel Guide" (llama-modchip):
+ *     section 1: 256 routed experts + 1 shared, 6 active, routed scale 1.5;
+ *       learned layers gate with SQRT_SOFTPLUS, hash layers look token ids up
+ *       in a token-id -> 6-expert table (ffn_gate_tid2eid);
+ *     section 3.2, MoE combine equation: y = e_shared(x) + sum_i w_i e_{k_i}(x),
+ *       sum_i w_i = 1.5;
+ *     section 4, SwiGLU equation: h = SiLU(W_gate x) * (W_up x), y = W_down h.
+ *   "DeepSeek V4 target engine (CPU + optional CUDA tier)", introduction:
+ *     routed experts in native fp4 (MXFP4), dense weights in fp8-e4m3 with
+ *     UE8M0 block scales.
+ *   "Development Snapshot Validation" (cism), 4-bit quantization scheme
+ *     study: MXFP4 = E2M1 elements + one E8M0 scale per 32 elements.
+ *
+ * Conventions for every entry point
+ *   - Array arguments are device pointers owned by the caller.  moe_layer
+ *     itself is host memory that is read during the call only.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; 0 is the
+ *     null stream); the caller synchronises.  Calls keep no state between
+ *     them and allocate nothing; scratch memory comes from the caller's
+ *     workspace, sized by the matching *_workspace_bytes query.
+ *   - Host-checkable argument errors return MOE_ERR_INVALID,
+ *     MOE_ERR_UNSUPPORTED or MOE_ERR_WORKSPACE before anything is enqueued.
+ *     A failed kernel launch returns MOE_ERR_DEVICE.  Nothing is thrown.
+ *   - Data errors found on the device (an expert id or token id out of
+ *     range) are OR-ed into the optional `dev_error` word (never cleared by
+ *     the library) with no host synchronisation; the offending entry is
+ *     skipped and every access stays in bounds.
+ *   - n_tokens == 0 is valid and enqueues nothing.
+ *
+ * Weight layout (the pages print no layout; this is the reading used):
+ *   A projection is a stack of experts, expert e at byte offset
+ *   e * rows * row_bytes of `codes` (and likewise for `scales`).  Rows are
+ *   output features; gate/up have rows = inter, cols = hidden; down has
+ *   rows = hidden, cols = inter.
+ *   MOE_W_MXFP4: codes uint8 [rows][cols/2]; byte b of a row holds element
+ *     2b in bits 0..3 and element 2b+1 in bits 4..7; an element is an E2M1
+ *     code (sign, 2 exponent bits with bias 1, 1 mantissa bit: magnitudes
+ *     0, .5, 1, 1.5, 2, 3, 4, 6).  scales uint8 [rows][cols/32]; scale j of
+ *     a row is a UE8M0 byte u meaning 2^(u-127) for elements 32j..32j+31.
+ *   MOE_W_FP8E4M3_B128: codes uint8 [rows][cols], OCP E4M3 ("fn": bias 7,
+ *     max 448, no infinities); scales uint8 [rows][cols/128], one UE8M0 per
+ *     128 elements of a row.
+ *   The three routed matrices share one weight type, and so do the three
+ *   shared ones (MOE_ERR_UNSUPPORTED otherwise).
+ *   Decode is exact for scale bytes 2..252 (every element times its scale
+ *   is then a normal bfloat16 number); other bytes are outside the
+ *   supported range and give unspecified (but in-bounds) results.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID = 1,     /* a null/misaligned pointer or an impossible size */
+  MOE_ERR_UNSUPPORTED = 2, /* valid request outside what the kernels cover    */
+  MOE_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required      */
+  MOE_ERR_DEVICE = 4       /* a HIP call or kernel launch failed              */
+} moe_status;
+
+typedef enum { MOE_ACT_F32 = 0, MOE_ACT_BF16 = 1 } moe_act_type;
+
+typedef enum { MOE_W_MXFP4 = 0, MOE_W_FP8E4M3_B128 = 1 } moe_weight_type;
+
+/* Bits OR-ed into dev_error. */
+#define MOE_DEVERR_EXPERT_ID 1 /* an expert id outside [0, n_experts)  */
+#define MOE_DEVERR_TOKEN_ID 2  /* a token id outside [0, vocab)        */
+
+/* Limits of this build. */
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOP_K 8
+#define MOE_MAX_DIM 65536
+#define MOE_MAX_TOKENS (1 << 22)
+
+typedef struct {
+  int32_t type; /* moe_weight_type */
+  const uint8_t* codes;  /* 16-byte aligned */
+  const uint8_t* scales;
+} moe_proj;
+
+typedef struct {
+  int32_t hidden;    /* multiple of 128, <= MOE_MAX_DIM                  */
+  int32_t inter;     /* routed expert intermediate size, multiple of 128 */
+  int32_t n_experts; /* routed experts, 1..MOE_MAX_EXPERTS               */
+  int32_t top_k;     /* 1..MOE_MAX_TOP_K, <= n_experts                   */
+  moe_proj gate, up, down; /* routed, stacked over n_experts             */
+  int32_t has_shared;      /* 0 or 1: one shared expert, weight 1        */
+  int32_t shared_inter;    /* multiple of 128 when has_shared            */
+  moe_proj shared_gate, shared_up, shared_down; /* one matrix each       */
+} moe_layer;
+
+/*
+ * Learned router ("Deep-Dive Mathematical & Kernel Guide", section 1,
+ * gating_func SQRT_SOFTPLUS; section 3.2, sum of routed weights 1.5).
+ *   logits     fp32 [n_tokens][n_experts], row-major, finite.
+ *   topk_ids   out int32 [n_tokens][top_k]: the top_k largest logits of the
+ *              token, slot 0 the largest, ties to the lower expert index
+ *              (-0 equals +0).
+ *   topk_w     out fp32 [n_tokens][top_k]: s_i = sqrt(softplus(logit_i)),
+ *              w_i = routed_scale * s_i / sum_j s_j (evaluated in fp64,
+ *              rounded to fp32 once).
+ *   Expert groups are read as a single group (plain top-k over all experts).
+ */
+moe_status moe_route(const float* logits, int n_tokens, int n_experts, int top_k,
+                     float routed_scale, int32_t* topk_ids, float* topk_w,
+                     hipStream_t stream);
+
+/*
+ * Token-id hash router ("Deep-Dive Mathematical & Kernel Guide", section 1
+ * and section 3.2 item 1: ffn_gate_tid2eid maps a token id to 6 experts with
+ * flat weights).
+ *   token_ids  int32 [n_tokens], each in [0, vocab).
+ *   tid2eid    int32 [vocab][top_k] expert ids; tid2w fp32 [vocab][top_k].
+ *   topk_ids / topk_w  out, [n_tokens][top_k]: the token's table row in table
+ *              order.  A token id out of range gives ids -1 and weights 0
+ *              and sets MOE_DEVERR_TOKEN_ID in *dev_error (dev_error may be
+ *              NULL).
+ */
+moe_status moe_route_hash(const int32_t* token_ids, int n_tokens, const int32_t* tid2eid,
+                          const float* tid2w, int vocab, int n_experts, int top_k,
+                          int32_t* topk_ids, float* topk_w, int32_t* dev_error,
+                          hipStream_t stream);
+
+/* Workspace bytes moe_group needs (currently 0: it works in LDS). */
+size_t moe_group_workspace_bytes(int n_tokens, int top_k, int n_experts);
+
+/*
+ * Token-to-expert grouping (the expert bucketing behind MUL_MAT_ID row-group
+ * reuse, "Deep-Dive Mathematical & Kernel Guide" section 2 table A and
+ * section 6 item 2).  With f = t*top_k + i the flat index of slot i of
+ * token t:
+ *   counts    out int32 [n_experts]: number of f with topk_ids[f] == e.
+ *   offsets   out int32 [n_experts+1]: exclusive prefix of counts.
+ *   perm      out int32 [n_tokens*top_k]: the flat indices sorted by expert,
+ *             ascending f inside an expert (stable); only the first
+ *             offsets[n_experts] entries are written.
+ *   inv_perm  out int32 [n_tokens*top_k]: inv_perm[perm[p]] = p; -1 for an
+ *             entry whose id is out of range (then MOE_DEVERR_EXPERT_ID is
+ *             set in *dev_error; dev_error may be NULL).
+ *   Results are deterministic (no order depends on atomics).
+ */
+moe_status moe_group(const int32_t* topk_ids, int n_tokens, int top_k, int n_experts,
+                     int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                     int32_t* dev_error, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+/* Workspace bytes moe_ffn_forward (and its two stages) need for n_tokens. */
+size_t moe_ffn_workspace_bytes(const moe_layer* layer, int n_tokens);
+
+/*
+ * Expert FFN and combine ("Deep-Dive Mathematical & Kernel Guide", section 4
+ * SwiGLU equation and section 3.2 combine equation):
+ *   y[t] = e_shared(x_t) + sum_i topk_w[t][i] * e_{topk_ids[t][i]}(x_t),
+ *   e(x) = W_down (SiLU(W_gate x) * (W_up x)), SiLU(g) = g / (1 + exp(-g)).
+ *   x        [n_tokens][hidden], fp32 or bf16 (x_type), 16-byte aligned.
+ *   topk_w   fp32 [n_tokens][top_k] as made by a router.
+ *   counts, offsets, perm, inv_perm   as made by moe_group for the same ids.
+ *   y        out fp32 [n_tokens][hidden], fully overwritten.
+ *   Weights are decoded exactly to bfloat16 and multiplied on the matrix
+ *   cores with fp32 accumulation; the SwiGLU output (and fp32 x) enter the
+ *   matrix cores as a bf16 high + bf16 low pair.  The combine sums each
+ *   token's terms in a fixed order (shared first, then slot 0..top_k-1), so
+ *   y is deterministic.
+ */
+moe_status moe_ffn_forward(const moe_layer* layer, const void* x, int x_type, int n_tokens,
+                           const float* topk_w, const int32_t* counts, const int32_t* offsets,
+                           const int32_t* perm, const int32_t* inv_perm, float* y,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The two stages of moe_ffn_forward, for callers that time or interleave
+ * them; the same arguments, run in this order on the same workspace.
+ *   moe_ffn_gate_up: gate/up matmuls with on-the-fly decode and SwiGLU,
+ *                    writing h into the workspace.
+ *   moe_ffn_down:    down projection, routing weights and combine into y.
+ */
+moe_status moe_ffn_gate_up(const moe_layer* layer, const void* x, int x_type, int n_tokens,
+                           const float* topk_w, const int32_t* counts, const int32_t* offsets,
+                           const int32_t* perm, const int32_t* inv_perm, float* y,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+moe_status moe_ffn_down(const moe_layer* layer, const void* x, int x_type, int n_tokens,
+                        const float* topk_w, const int32_t* counts, const int32_t* offsets,
+                        const int32_t* perm, const int32_t* inv_perm, float* y,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* A static, human-readable name of a status code. */
+const char* moe_status_string(moe_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

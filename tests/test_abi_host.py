@@ -1,0 +1,170 @@
+"""The C ABI on the host: the library loads, exports every symbol that
+include/moe.h declares, sizes workspaces, and rejects bad arguments before
+anything reaches a GPU (every call here fails validation, so no HIP call is
+made)."""
+
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from block_quantized_expert_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(moe_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = B.lib()
+    declared = _declared_functions()
+    assert declared, "no declarations parsed"
+    assert sorted(B.EXPORTED) == declared
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    for s in range(5):
+        assert B.status_string(s).startswith("MOE_")
+    assert "unknown" in B.status_string(99)
+
+
+def test_struct_layout_matches_c():
+    # int32 x4, 3 x {int32 type; 2 pointers}, int32 x2, 3 x proj
+    assert ctypes.sizeof(B.MoeProj) == 24
+    assert B.MoeLayer.gate.offset == 16
+    assert B.MoeLayer.has_shared.offset == 88
+    assert ctypes.sizeof(B.MoeLayer) == 168
+
+
+FAKE = ctypes.c_void_p(0x10000)  # 16-byte aligned, never dereferenced
+MIS = ctypes.c_void_p(0x10004)
+
+
+def _layer(hidden=4096, inter=2048, e=256, k=6, shared=True, wtype=0, swtype=0, codes=FAKE):
+    L = B.MoeLayer()
+    L.hidden, L.inter, L.n_experts, L.top_k = hidden, inter, e, k
+    for name in ("gate", "up", "down"):
+        setattr(L, name, B.MoeProj(wtype, codes.value, FAKE.value))
+    L.has_shared = 1 if shared else 0
+    if shared:
+        L.shared_inter = inter
+        for name in ("shared_gate", "shared_up", "shared_down"):
+            setattr(L, name, B.MoeProj(swtype, FAKE.value, FAKE.value))
+    return L
+
+
+def test_ffn_workspace_bytes():
+    L = _layer()
+    n = 4096
+    slots = n * 6 + n
+    h = -(-slots * 2048 * 2 // 256) * 256
+    o = -(-slots * 4096 * 4 // 256) * 256
+    assert B.lib().moe_ffn_workspace_bytes(ctypes.byref(L), n) == 2 * h + o
+    assert B.lib().moe_ffn_workspace_bytes(ctypes.byref(L), 0) == 0
+    assert B.lib().moe_ffn_workspace_bytes(ctypes.byref(_layer(hidden=100)), 8) == 0
+    assert B.lib().moe_ffn_workspace_bytes(None, 8) == 0
+    assert B.lib().moe_group_workspace_bytes(8, 2, 16) == 0
+
+
+def _ffn(L, x=FAKE, x_type=1, n=4, ws=FAKE, ws_bytes=1 << 40, y=FAKE, w=FAKE):
+    return B.lib().moe_ffn_forward(ctypes.byref(L) if L is not None else None, x, x_type, n, w,
+                                   FAKE, FAKE, FAKE, FAKE, y, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kwargs,layer_kwargs,expected", [
+    ({"x": None}, {}, B.MOE_ERR_INVALID),
+    ({"x": MIS}, {}, B.MOE_ERR_INVALID),
+    ({"y": MIS}, {}, B.MOE_ERR_INVALID),
+    ({"w": None}, {}, B.MOE_ERR_INVALID),
+    ({"n": -1}, {}, B.MOE_ERR_INVALID),
+    ({"n": (1 << 22) + 1}, {}, B.MOE_ERR_UNSUPPORTED),
+    ({"x_type": 7}, {}, B.MOE_ERR_UNSUPPORTED),
+    ({"ws": None}, {}, B.MOE_ERR_WORKSPACE),
+    ({"ws_bytes": 1000}, {}, B.MOE_ERR_WORKSPACE),
+    ({"ws": MIS}, {}, B.MOE_ERR_INVALID),
+    ({}, {"hidden": 4000}, B.MOE_ERR_UNSUPPORTED),
+    ({}, {"inter": 96}, B.MOE_ERR_UNSUPPORTED),
+    ({}, {"hidden": 0}, B.MOE_ERR_INVALID),
+    ({}, {"k": 9, "e": 16}, B.MOE_ERR_UNSUPPORTED),
+    ({}, {"k": 17, "e": 16}, B.MOE_ERR_INVALID),
+    ({}, {"e": 2000}, B.MOE_ERR_UNSUPPORTED),
+    ({}, {"wtype": 5}, B.MOE_ERR_UNSUPPORTED),
+    ({}, {"codes": MIS}, B.MOE_ERR_INVALID),
+    ({}, {"swtype": 3}, B.MOE_ERR_UNSUPPORTED),
+])
+def test_ffn_rejects_bad_arguments(kwargs, layer_kwargs, expected):
+    assert _ffn(_layer(**layer_kwargs), **kwargs) == expected
+
+
+def test_ffn_null_layer_and_mixed_types():
+    assert _ffn(None) == B.MOE_ERR_INVALID
+    L = _layer()
+    L.down = B.MoeProj(1, FAKE.value, FAKE.value)  # gate mxfp4, down fp8
+    assert _ffn(L) == B.MOE_ERR_UNSUPPORTED
+    L = _layer()
+    L.has_shared = 2
+    assert _ffn(L) == B.MOE_ERR_INVALID
+    L = _layer()
+    L.shared_inter = 0
+    assert _ffn(L) == B.MOE_ERR_INVALID
+    L = _layer()
+    L.shared_up = B.MoeProj(0, 0, FAKE.value)
+    assert _ffn(L) == B.MOE_ERR_INVALID
+
+
+def test_ffn_zero_tokens_is_a_no_op():
+    assert _ffn(_layer(), n=0, x=None, ws=None, y=None) == B.MOE_OK
+
+
+def test_route_rejects_bad_arguments():
+    R = B.lib().moe_route
+    assert R(None, 4, 256, 6, 1.5, FAKE, FAKE, None) == B.MOE_ERR_INVALID
+    assert R(FAKE, 4, 256, 6, 0.0, FAKE, FAKE, None) == B.MOE_ERR_INVALID
+    assert R(FAKE, 4, 256, 6, float("nan"), FAKE, FAKE, None) == B.MOE_ERR_INVALID
+    assert R(FAKE, 4, 256, 6, float("inf"), FAKE, FAKE, None) == B.MOE_ERR_INVALID
+    assert R(FAKE, 4, 4, 6, 1.5, FAKE, FAKE, None) == B.MOE_ERR_INVALID
+    assert R(FAKE, 4, 256, 9, 1.5, FAKE, FAKE, None) == B.MOE_ERR_UNSUPPORTED
+    assert R(FAKE, 4, 1025, 6, 1.5, FAKE, FAKE, None) == B.MOE_ERR_UNSUPPORTED
+    assert R(FAKE, -1, 256, 6, 1.5, FAKE, FAKE, None) == B.MOE_ERR_INVALID
+    assert R(FAKE, 4, 256, 0, 1.5, FAKE, FAKE, None) == B.MOE_ERR_INVALID
+    assert R(None, 0, 256, 6, 1.5, None, None, None) == B.MOE_OK  # nothing to do
+
+
+def test_route_hash_and_group_reject_bad_arguments():
+    H = B.lib().moe_route_hash
+    assert H(FAKE, 4, FAKE, FAKE, 0, 256, 6, FAKE, FAKE, None, None) == B.MOE_ERR_INVALID
+    assert H(FAKE, 4, None, FAKE, 100, 256, 6, FAKE, FAKE, None, None) == B.MOE_ERR_INVALID
+    assert H(FAKE, 4, FAKE, FAKE, 100, 256, 9, FAKE, FAKE, None, None) == B.MOE_ERR_UNSUPPORTED
+    G = B.lib().moe_group
+    assert G(FAKE, 4, 6, 256, None, FAKE, FAKE, FAKE, None, None, 0, None) == B.MOE_ERR_INVALID
+    assert G(FAKE, 4, 6, 256, FAKE, FAKE, None, FAKE, None, None, 0, None) == B.MOE_ERR_INVALID
+    assert G(FAKE, 4, 6, 2048, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == B.MOE_ERR_UNSUPPORTED
+    assert G(FAKE, 4, 9, 256, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == B.MOE_ERR_UNSUPPORTED
+    assert G(FAKE, 4, 300, 256, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == B.MOE_ERR_INVALID
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="needs g++")
+def test_host_validator_under_address_and_ub_sanitizers(tmp_path):
+    # The pure-host validator, built with ASan + UBSan and driven through its
+    # accept and reject paths.
+    csrc = os.path.join(ROOT, "block_quantized_expert_amd", "csrc")
+    exe = str(tmp_path / "validator")
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+           "-I" + os.path.join(ROOT, "include"), "-I" + csrc,
+           os.path.join(csrc, "moe_host.cpp"),
+           os.path.join(ROOT, "tests", "native", "validator_main.cpp"), "-o", exe]
+    subprocess.run(cmd, check=True, capture_output=True)
+    r = subprocess.run([exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "validator ok" in r.stdout

@@ -1,0 +1,197 @@
+"""GPU parity of the whole path (route -> group -> gate/up -> down ->
+combine) against the fp64 oracle, plus metamorphic checks that need no
+oracle.  Bar: max|err| <= 2e-3 * rms(oracle y) over the compared outputs."""
+
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from block_quantized_expert_amd import binding as B
+from block_quantized_expert_amd import inputs as I
+
+from moe_testlib import assert_y_close, gpu_inputs, oracle_routing, oracle_y
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+    yield
+    torch.cuda.empty_cache()
+
+
+def _run(wl, copy=0, with_shared=True):
+    layer, x, x_d, routing, routing_d = gpu_inputs(wl, copy, with_shared)
+    y, ids, w, grouping = B.forward(layer, x_d, routing_d, wl.routed_scale)
+    torch.cuda.synchronize()
+    return layer, x, routing, y, ids, w, grouping
+
+
+def _sample(n, k, seed):
+    return sorted(np.random.default_rng(seed).choice(n, size=min(n, k), replace=False).tolist())
+
+
+# ----------------------------------------------------------------- full size
+
+
+@pytest.mark.parametrize("with_shared", [True, False])
+def test_tiny_full(with_shared):
+    wl = I.WORKLOADS["tiny"]
+    print("case tiny shared=%s" % with_shared, flush=True)
+    _, x, routing, y, ids, w, _ = _run(wl, with_shared=with_shared)
+    rids, rw = oracle_routing(wl, routing)
+    assert np.array_equal(ids.cpu().numpy(), rids)
+    ref = oracle_y(wl, x, rids, rw, with_shared=with_shared)
+    assert_y_close(y.cpu().numpy(), ref)
+
+
+def test_decode1_full():
+    wl = I.WORKLOADS["decode1"]
+    print("case decode1", flush=True)
+    _, x, routing, y, ids, w, _ = _run(wl)
+    rids, rw = oracle_routing(wl, routing)
+    assert np.array_equal(ids.cpu().numpy(), rids)
+    ref = oracle_y(wl, x, rids, rw)
+    assert_y_close(y.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("name,n_tok,n_rows,with_shared", [
+    ("decode32", 8, 1024, True),
+    ("decode32", 4, 512, False),
+    ("prefill512", 6, 512, True),
+    ("hash4096", 4, 512, True),
+])
+def test_sampled_full_size(name, n_tok, n_rows, with_shared):
+    wl = I.WORKLOADS[name]
+    print("case %s sampled tokens=%d rows=%d shared=%s" % (name, n_tok, n_rows, with_shared),
+          flush=True)
+    _, x, routing, y, ids, w, _ = _run(wl, with_shared=with_shared)
+    rids, rw = oracle_routing(wl, routing)
+    assert np.array_equal(ids.cpu().numpy(), rids)
+    tokens = _sample(wl.n_tokens, n_tok, 11)
+    rows = _sample(wl.hidden, n_rows, 12)
+    ref = oracle_y(wl, x, rids, rw, tokens=tokens, rows=rows, with_shared=with_shared)
+    assert_y_close(y.cpu().numpy()[tokens][:, rows], ref)
+
+
+# ------------------------------------------------------- small, several tiles
+
+SMALL = I.Workload("small", 100, 256, 128, 8, 2, 1.5, "bf16", "learned", 119, 124,
+                   "mxfp4", "none", 21)
+
+
+@pytest.mark.parametrize("wl", [
+    SMALL,                                                       # 2 token tiles, ragged
+    replace(SMALL, n_tokens=40, shared="fp8_e4m3_b128", seed=22),  # fp8 shared, 3 blocks
+    replace(SMALL, n_tokens=33, shared_inter=256, seed=23),      # shared inter != inter
+    replace(SMALL, n_tokens=17, act="f32", top_k=3, seed=24),     # fp32 x, hi/lo split
+    replace(SMALL, n_tokens=130, n_experts=5, top_k=5, seed=25),  # every expert, 3 tiles
+    replace(SMALL, n_tokens=1, hidden=512, inter=384, seed=26),   # K steps 4 and 3
+], ids=["ragged100", "fp8shared40", "sharedinter33", "f32x17", "allexperts130", "odd_k1"])
+def test_small_layers_full(wl):
+    print("case small", wl, flush=True)
+    _, x, routing, y, ids, w, _ = _run(wl)
+    rids, rw = oracle_routing(wl, routing)
+    assert np.array_equal(ids.cpu().numpy(), rids)
+    ref = oracle_y(wl, x, rids, rw)
+    assert_y_close(y.cpu().numpy(), ref)
+
+
+def test_stages_equal_forward():
+    wl = replace(SMALL, n_tokens=50, seed=27)
+    print("case stages", flush=True)
+    layer, x, x_d, routing, routing_d = gpu_inputs(wl)
+    ids, w = B.moe_route(routing_d["logits"], wl.top_k)
+    g = B.moe_group(ids, wl.n_experts)
+    ws = torch.empty(layer.workspace_bytes(wl.n_tokens), dtype=torch.uint8, device=DEV)
+    y1 = B.moe_ffn_forward(layer, x_d, w, g, workspace=ws)
+    y2 = torch.empty_like(y1)
+    B.moe_ffn_gate_up(layer, x_d, w, g, y=y2, workspace=ws)
+    B.moe_ffn_down(layer, x_d, w, g, y=y2, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+
+
+def test_zero_tokens():
+    wl = replace(SMALL, n_tokens=0)
+    print("case zero tokens", flush=True)
+    layer = B.Layer(I.make_layer(wl, device=DEV), wl.top_k)
+    x = torch.zeros((0, wl.hidden), dtype=torch.bfloat16, device=DEV)
+    w = torch.zeros((0, wl.top_k), dtype=torch.float32, device=DEV)
+    z = torch.zeros(1, dtype=torch.int32, device=DEV)
+    y = torch.zeros((0, wl.hidden), dtype=torch.float32, device=DEV)
+    ws = torch.zeros(1, dtype=torch.uint8, device=DEV)
+    B.moe_ffn_forward(layer, x, w, (z, z, z, z), y=y, workspace=ws)
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------- metamorphic checks
+
+
+def _with_scales_bumped(weights, proj):
+    out = dict(weights)
+    out[proj] = dict(weights[proj], scales=weights[proj]["scales"] + 1)
+    if weights.get("shared") is not None:
+        sh = dict(weights["shared"])
+        sh[proj] = dict(sh[proj], scales=sh[proj]["scales"] + 1)
+        out["shared"] = sh
+    return out
+
+
+@pytest.mark.parametrize("proj", ["down", "up"])
+def test_scale_increment_doubles_output_bitwise(proj):
+    # one more in every UE8M0 byte of a linear projection multiplies every
+    # expert output by exactly 2; the kernels' arithmetic commutes with that
+    wl = I.WORKLOADS["decode32"]
+    print("case doubling", proj, flush=True)
+    layer, x, x_d, routing, routing_d = gpu_inputs(wl)
+    y1, *_ = B.forward(layer, x_d, routing_d)
+    layer2 = B.Layer(_with_scales_bumped(layer.weights, proj), wl.top_k)
+    y2, *_ = B.forward(layer2, x_d, routing_d)
+    torch.cuda.synchronize()
+    assert torch.equal(y2, 2 * y1)
+
+
+def test_repeat_runs_are_bitwise_equal():
+    wl = I.WORKLOADS["prefill512"]
+    print("case repeat", flush=True)
+    layer, x, x_d, routing, routing_d = gpu_inputs(wl)
+    y1, *_ = B.forward(layer, x_d, routing_d)
+    y2, *_ = B.forward(layer, x_d, routing_d)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+
+
+def test_shared_split_is_additive():
+    # y(with shared) - y(routed only) equals the shared expert alone (a
+    # layer whose routed weights are all zero), within the tolerance
+    wl = replace(I.WORKLOADS["decode32"], n_tokens=8)
+    print("case shared additivity", flush=True)
+    layer, x, x_d, routing, routing_d = gpu_inputs(wl)
+    y_all, ids, w, g = B.forward(layer, x_d, routing_d)
+    layer_r = B.Layer(dict(layer.weights, shared=None), wl.top_k)
+    y_r = B.moe_ffn_forward(layer_r, x_d, w, g)
+    y_s = B.moe_ffn_forward(layer, x_d, torch.zeros_like(w), g)
+    torch.cuda.synchronize()
+    d = (y_all - y_r - y_s).abs().max().item()
+    rms = y_all.pow(2).mean().sqrt().item()
+    assert d <= 1e-5 * rms
+
+
+def test_token_permutation_permutes_output():
+    wl = I.WORKLOADS["decode32"]
+    print("case permutation", flush=True)
+    layer, x, x_d, routing, routing_d = gpu_inputs(wl)
+    y, *_ = B.forward(layer, x_d, routing_d)
+    p = torch.randperm(wl.n_tokens, generator=torch.Generator().manual_seed(3))
+    yp, *_ = B.forward(layer, x_d[p.to(DEV)].contiguous(),
+                       {"kind": "learned", "logits": routing_d["logits"][p.to(DEV)].contiguous()})
+    torch.cuda.synchronize()
+    d = (yp - y[p.to(DEV)]).abs().max().item()
+    assert d <= 1e-5 * y.pow(2).mean().sqrt().item()
