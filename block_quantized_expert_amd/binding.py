@@ -21,9 +21,9 @@ MOE_W_MXFP4, MOE_W_FP8E4M3_B128 = 0, 1
 MOE_DEVERR_EXPERT_ID, MOE_DEVERR_TOKEN_ID = 1, 2
 
 # every symbol include/moe.h declares
-EXPORTED = ["moe_route", "moe_route_hash", "moe_group_workspace_bytes", "moe_group",
-            "moe_ffn_workspace_bytes", "moe_ffn_forward", "moe_ffn_gate_up", "moe_ffn_down",
-            "moe_status_string"]
+EXPORTED = ["moe_route", "moe_route_hash", "moe_route_group", "moe_group_workspace_bytes",
+            "moe_group", "moe_ffn_workspace_bytes", "moe_ffn_forward", "moe_ffn_gate_up",
+            "moe_ffn_down", "moe_ffn_forward_timed", "moe_status_string"]
 
 WEIGHT_TYPES = {"mxfp4": MOE_W_MXFP4, "fp8_e4m3_b128": MOE_W_FP8E4M3_B128}
 
@@ -63,13 +63,17 @@ def lib() -> ctypes.CDLL:
         L.moe_group_workspace_bytes.argtypes = [I, I, I]
         L.moe_group_workspace_bytes.restype = S
         L.moe_group.argtypes = [P, I, I, I, P, P, P, P, P, P, S, P]
+        L.moe_route_group.argtypes = [P, I, I, I, F, P, P, P, P, P, P, P, P]
+        L.moe_ffn_forward_timed.argtypes = [ctypes.POINTER(MoeLayer), P, I, I, P, P, P, P, P,
+                                            P, P, S, P, P, P, P, P]
         L.moe_ffn_workspace_bytes.argtypes = [ctypes.POINTER(MoeLayer), I]
         L.moe_ffn_workspace_bytes.restype = S
         ffn_args = [ctypes.POINTER(MoeLayer), P, I, I, P, P, P, P, P, P, P, S, P]
         for name in ("moe_ffn_forward", "moe_ffn_gate_up", "moe_ffn_down"):
             getattr(L, name).argtypes = ffn_args
-        for name in ("moe_route", "moe_route_hash", "moe_group", "moe_ffn_forward",
-                     "moe_ffn_gate_up", "moe_ffn_down"):
+        for name in ("moe_route", "moe_route_hash", "moe_route_group", "moe_group",
+                     "moe_ffn_forward", "moe_ffn_gate_up", "moe_ffn_down",
+                     "moe_ffn_forward_timed"):
             getattr(L, name).restype = ctypes.c_int
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
@@ -185,6 +189,22 @@ def moe_group(ids, n_experts, out=None, dev_error=None, stream=None):
     return counts, offsets, perm, inv_perm
 
 
+def moe_route_group(logits, top_k, routed_scale=1.5, dev_error=None, stream=None):
+    """Fused route + group.  Returns (ids, w, (counts, offsets, perm, inv_perm))."""
+    n, e = logits.shape
+    dev = logits.device
+    ids = torch.empty((n, top_k), dtype=torch.int32, device=dev)
+    w = torch.empty((n, top_k), dtype=torch.float32, device=dev)
+    g = (torch.empty(e, dtype=torch.int32, device=dev),
+         torch.empty(e + 1, dtype=torch.int32, device=dev),
+         torch.empty(n * top_k, dtype=torch.int32, device=dev),
+         torch.empty(n * top_k, dtype=torch.int32, device=dev))
+    _check(lib().moe_route_group(_ptr(logits), n, e, top_k, routed_scale, _ptr(ids), _ptr(w),
+                                 *[_ptr(t) for t in g], _ptr(dev_error), _stream(stream)),
+           "moe_route_group")
+    return ids, w, g
+
+
 def _ffn_call(name, layer: Layer, x, w, grouping, y, workspace, stream):
     n = x.shape[0]
     x_type = MOE_ACT_BF16 if x.dtype == torch.bfloat16 else MOE_ACT_F32
@@ -213,14 +233,35 @@ def moe_ffn_down(layer: Layer, x, w, grouping, y=None, workspace=None, stream=No
     return _ffn_call("moe_ffn_down", layer, x, w, grouping, y, workspace, stream)
 
 
+def moe_ffn_forward_timed(layer: Layer, x, w, grouping, events, y=None, workspace=None,
+                          stream=None):
+    """``events``: four torch.cuda.Event(enable_timing=True) (or None) for
+    gate/up start, gate/up stop, down start, down stop."""
+    n = x.shape[0]
+    x_type = MOE_ACT_BF16 if x.dtype == torch.bfloat16 else MOE_ACT_F32
+    if y is None:
+        y = torch.empty((n, layer.hidden), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(layer.workspace_bytes(n), 1), dtype=torch.uint8,
+                                device=x.device)
+    counts, offsets, perm, inv_perm = grouping
+    evs = [None if e is None else ctypes.c_void_p(e.cuda_event) for e in events]
+    _check(lib().moe_ffn_forward_timed(ctypes.byref(layer.c), _ptr(x), x_type, n, _ptr(w),
+                                       _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(inv_perm),
+                                       _ptr(y), _ptr(workspace), workspace.numel(),
+                                       _stream(stream), *evs), "moe_ffn_forward_timed")
+    return y
+
+
 def forward(layer: Layer, x, routing: dict, routed_scale=1.5, stream=None):
     """Route, group and run the FFN (all on the device).  Returns
     (y, ids, w, grouping)."""
     if routing["kind"] == "learned":
-        ids, w = moe_route(routing["logits"], layer.top_k, routed_scale, stream=stream)
+        ids, w, grouping = moe_route_group(routing["logits"], layer.top_k, routed_scale,
+                                           stream=stream)
     else:
         ids, w = moe_route_hash(routing["token_ids"], routing["tid2eid"], routing["tid2w"],
                                 layer.c.n_experts, stream=stream)
-    grouping = moe_group(ids, layer.c.n_experts, stream=stream)
+        grouping = moe_group(ids, layer.c.n_experts, stream=stream)
     y = moe_ffn_forward(layer, x, w, grouping, stream=stream)
     return y, ids, w, grouping

@@ -50,6 +50,7 @@ moe::FfnParams make_params(const moe_layer* L, const void* x, int x_type, int n_
   p.h_lo = reinterpret_cast<__bf16*>(ws + plan.off_h_lo);
   p.h_stride = plan.h_stride;
   p.obuf = reinterpret_cast<float*>(ws + plan.off_obuf);
+  p.rb_count = reinterpret_cast<int32_t*>(ws + plan.off_count);
   p.y = y;
   return p;
 }
@@ -59,18 +60,22 @@ enum Stage { kGateUp = 1, kDown = 2, kBoth = 3 };
 moe_status ffn_stages(int stages, const moe_layer* layer, const void* x, int x_type,
                       int n_tokens, const float* topk_w, const int32_t* counts,
                       const int32_t* offsets, const int32_t* perm, const int32_t* inv_perm,
-                      float* y, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                      float* y, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                      hipEvent_t const* events = nullptr) {
   moe::FfnPlan plan;
   moe_status s = moe::check_ffn(layer, x, x_type, n_tokens, topk_w, counts, offsets, perm,
                                 inv_perm, y, workspace, workspace_bytes, &plan);
   if (s != MOE_OK || n_tokens == 0) return s;
   const moe::FfnParams p = make_params(layer, x, x_type, n_tokens, topk_w, counts, offsets, perm,
                                        inv_perm, y, workspace, plan);
+  hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
+  if (events)
+    for (int i = 0; i < 4; ++i) ev[i] = events[i];
   if (stages & kGateUp) {
-    if ((s = launched(moe::launch_ffn_gate_up(p, stream))) != MOE_OK) return s;
+    if ((s = launched(moe::launch_ffn_gate_up(p, stream, ev[0], ev[1]))) != MOE_OK) return s;
   }
   if (stages & kDown) {
-    if ((s = launched(moe::launch_ffn_down(p, stream))) != MOE_OK) return s;
+    if ((s = launched(moe::launch_ffn_down(p, stream, ev[2], ev[3]))) != MOE_OK) return s;
   }
   return MOE_OK;
 }
@@ -98,6 +103,18 @@ moe_status moe_route_hash(const int32_t* token_ids, int n_tokens, const int32_t*
   if (s != MOE_OK || n_tokens == 0) return s;
   return launched(moe::launch_route_hash(token_ids, n_tokens, tid2eid, tid2w, vocab, n_experts,
                                          top_k, topk_ids, topk_w, dev_error, stream));
+}
+
+moe_status moe_route_group(const float* logits, int n_tokens, int n_experts, int top_k,
+                           float routed_scale, int32_t* topk_ids, float* topk_w, int32_t* counts,
+                           int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                           int32_t* dev_error, hipStream_t stream) {
+  moe_status s = moe::check_route_group(logits, n_tokens, n_experts, top_k, routed_scale,
+                                        topk_ids, topk_w, counts, offsets, perm, inv_perm);
+  if (s != MOE_OK) return s;
+  return launched(moe::launch_route_group(logits, n_tokens, n_experts, top_k, routed_scale,
+                                          topk_ids, topk_w, counts, offsets, perm, inv_perm,
+                                          dev_error, stream));
 }
 
 size_t moe_group_workspace_bytes(int n_tokens, int top_k, int n_experts) {
@@ -150,6 +167,18 @@ moe_status moe_ffn_down(const moe_layer* layer, const void* x, int x_type, int n
                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return ffn_stages(kDown, layer, x, x_type, n_tokens, topk_w, counts, offsets, perm, inv_perm,
                     y, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_ffn_forward_timed(const moe_layer* layer, const void* x, int x_type,
+                                 int n_tokens, const float* topk_w, const int32_t* counts,
+                                 const int32_t* offsets, const int32_t* perm,
+                                 const int32_t* inv_perm, float* y, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream,
+                                 hipEvent_t gate_up_start, hipEvent_t gate_up_stop,
+                                 hipEvent_t down_start, hipEvent_t down_stop) {
+  const hipEvent_t ev[4] = {gate_up_start, gate_up_stop, down_start, down_stop};
+  return ffn_stages(kBoth, layer, x, x_type, n_tokens, topk_w, counts, offsets, perm, inv_perm,
+                    y, workspace, workspace_bytes, stream, ev);
 }
 
 const char* moe_status_string(moe_status s) {

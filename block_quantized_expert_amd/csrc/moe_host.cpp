@@ -38,6 +38,15 @@ moe_status check_route(const float* logits, int n_tokens, int n_experts, int top
   return MOE_OK;
 }
 
+moe_status check_route_group(const float* logits, int n_tokens, int n_experts, int top_k,
+                             float routed_scale, const int32_t* ids, const float* w,
+                             const int32_t* counts, const int32_t* offsets, const int32_t* perm,
+                             const int32_t* inv_perm) {
+  moe_status s = check_route(logits, n_tokens, n_experts, top_k, routed_scale, ids, w);
+  if (s != MOE_OK) return s;
+  return check_group(ids, n_tokens, top_k, n_experts, counts, offsets, perm, inv_perm);
+}
+
 moe_status check_route_hash(const int32_t* token_ids, int n_tokens, const int32_t* tid2eid,
                             const float* tid2w, int vocab, int n_experts, int top_k,
                             const int32_t* ids, const float* w) {
@@ -100,8 +109,11 @@ moe_status plan_ffn(const moe_layer* layer, int n_tokens, FfnPlan* plan) {
   const size_t o_bytes = align_up((size_t)(plan->slots * layer->hidden) * 4u, 256);
   plan->off_h_hi = 0;
   plan->off_h_lo = h_bytes;
+  // nothing runs for an empty batch, so it needs no workspace
+  const size_t c_bytes = n == 0 ? 0 : align_up((size_t)(layer->hidden / 16) * 4u, 256);
   plan->off_obuf = 2 * h_bytes;
-  plan->total = 2 * h_bytes + o_bytes;
+  plan->off_count = 2 * h_bytes + o_bytes;
+  plan->total = 2 * h_bytes + o_bytes + c_bytes;
   return MOE_OK;
 }
 

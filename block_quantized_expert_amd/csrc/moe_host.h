@@ -14,6 +14,7 @@ namespace moe {
 //   h_hi, h_lo : bf16 [slots][h_stride]   SwiGLU output split into a bf16
 //                                         high part and a bf16 low part
 //   obuf       : fp32 [slots][hidden]     weighted expert outputs
+//   rb_count   : int32 [hidden/16]        finished work items per row block
 // A slot is one (token, routed expert) pair in grouped order
 // (p in [0, n_tokens*top_k)) or, for the shared expert, n_tokens*top_k + t.
 struct FfnPlan {
@@ -22,9 +23,14 @@ struct FfnPlan {
   size_t off_h_hi;
   size_t off_h_lo;
   size_t off_obuf;
+  size_t off_count;
   size_t total;
 };
 
+moe_status check_route_group(const float* logits, int n_tokens, int n_experts, int top_k,
+                             float routed_scale, const int32_t* ids, const float* w,
+                             const int32_t* counts, const int32_t* offsets, const int32_t* perm,
+                             const int32_t* inv_perm);
 moe_status check_route(const float* logits, int n_tokens, int n_experts, int top_k,
                        float routed_scale, const int32_t* ids, const float* w);
 moe_status check_route_hash(const int32_t* token_ids, int n_tokens, const int32_t* tid2eid,

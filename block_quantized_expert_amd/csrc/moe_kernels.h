@@ -31,8 +31,9 @@ struct FfnParams {
   __bf16* h_hi;  // [slots][h_stride]
   __bf16* h_lo;
   int64_t h_stride;
-  float* obuf;  // [slots][hidden]
-  float* y;     // [n_tokens][hidden]
+  float* obuf;        // [slots][hidden] weighted per-slot outputs
+  int32_t* rb_count;  // [hidden/16] finished items per 16-row block
+  float* y;           // [n_tokens][hidden]
 };
 
 hipError_t launch_route(const float* logits, int n_tokens, int n_experts, int top_k,
@@ -43,7 +44,15 @@ hipError_t launch_route_hash(const int32_t* token_ids, int n_tokens, const int32
 hipError_t launch_group(const int32_t* ids, int n_tokens, int top_k, int n_experts,
                         int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
                         int32_t* dev_error, hipStream_t stream);
-hipError_t launch_ffn_gate_up(const FfnParams& p, hipStream_t stream);
-hipError_t launch_ffn_down(const FfnParams& p, hipStream_t stream);
+hipError_t launch_route_group(const float* logits, int n_tokens, int n_experts, int top_k,
+                              float routed_scale, int32_t* ids, float* w, int32_t* counts,
+                              int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                              int32_t* dev_error, hipStream_t stream);
+// start/stop may be null; when given they record the kernel's own start and
+// end times (taken from its dispatch, no extra packets on the stream)
+hipError_t launch_ffn_gate_up(const FfnParams& p, hipStream_t stream, hipEvent_t start,
+                              hipEvent_t stop);
+hipError_t launch_ffn_down(const FfnParams& p, hipStream_t stream, hipEvent_t start,
+                           hipEvent_t stop);
 
 }  // namespace moe

@@ -1,0 +1,362 @@
+// Routers (learned sqrt(softplus) top-k, token-id hash lookup) and the
+// token-to-expert grouping (histogram -> exclusive scan -> stable scatter).
+//
+// "DeepSeek-V4-Flash 284B -- Deep-Dive Mathematical & Kernel Guide":
+//   section 1: SQRT_SOFTPLUS gating for the learned layers, ffn_gate_tid2eid
+//     for the hash layers; section 3.2: routed weights sum to 1.5;
+//   section 2 (tables A and B) and section 6 item 2: MUL_MAT_ID groups tokens
+//     by expert so each expert's weights stream once per batch.
+//
+// The grouping is deterministic: the position of flat index f inside its
+// expert's segment is the number of earlier flat indices with the same
+// expert, from per-wavefront match masks and a per-expert prefix over
+// wavefronts, never from the order in which atomics land.
+#include <hip/hip_runtime.h>
+#include <limits.h>
+
+#include "moe_device.h"
+#include "moe_kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int kGroupThreads = 1024;
+constexpr int kGroupWaves = kGroupThreads / kWave;
+// flat indices held in LDS by the fused route+group kernel
+constexpr int kFusedMaxFlat = 4096;
+
+// ---------------------------------------------------------------- routing
+
+// Top-k of one token's logits by one wavefront: lane l holds experts
+// j*64 + l.  top_k rounds of a wave-wide arg-max on (value, lower index),
+// then the weights of the winners in fp64, summed in rank order.  Lane r < k
+// returns slot r.
+template <int PER>
+__device__ __forceinline__ void route_token(const float* __restrict__ row, int n_experts,
+                                            int top_k, float routed_scale, int lane,
+                                            int& out_id, float& out_w) {
+  float v[PER];
+  bool live[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int e = j * kWave + lane;
+    live[j] = e < n_experts;
+    v[j] = live[j] ? row[e] : 0.0f;
+  }
+  int my_id = -1;
+  float my_v = 0.0f;
+  for (int r = 0; r < top_k; ++r) {
+    // best live entry of this lane: j ascending is index ascending, so a
+    // strict '>' keeps the lower index on ties
+    float bv = 0.0f;
+    int bi = INT_MAX;
+    int have = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      if (live[j] && (!have || v[j] > bv)) {
+        bv = v[j];
+        bi = j * kWave + lane;
+        have = 1;
+      }
+    }
+    // butterfly arg-max: (larger value, then lower index) is a total order,
+    // so every lane ends with the same winner
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      const int oh = __shfl_xor(have, off);
+      if (oh && (!have || ov > bv || (ov == bv && oi < bi))) {
+        bv = ov;
+        bi = oi;
+        have = 1;
+      }
+    }
+    if (lane == r) {
+      my_id = bi;
+      my_v = bv;
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      if (j * kWave + lane == bi) live[j] = false;
+  }
+  double s = 0.0;
+  if (lane < top_k) {
+    const double l = (double)my_v;
+    s = sqrt(fmax(l, 0.0) + log1p(exp(-fabs(l))));
+  }
+  double total = 0.0;
+  for (int r = 0; r < top_k; ++r) total += __shfl(s, r);
+  out_id = my_id;
+  out_w = (float)((double)routed_scale * s / total);
+}
+
+template <int PER>
+__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits,
+                                                         int n_tokens, int n_experts, int top_k,
+                                                         float routed_scale,
+                                                         int32_t* __restrict__ ids,
+                                                         float* __restrict__ w) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= n_tokens) return;  // the whole wavefront leaves together
+  int id;
+  float wt;
+  route_token<PER>(logits + (size_t)t * n_experts, n_experts, top_k, routed_scale, lane, id, wt);
+  if (lane < top_k) {
+    ids[(size_t)t * top_k + lane] = id;
+    w[(size_t)t * top_k + lane] = wt;
+  }
+}
+
+__global__ __launch_bounds__(256) void route_hash_kernel(const int32_t* __restrict__ token_ids,
+                                                         int n_tokens,
+                                                         const int32_t* __restrict__ tid2eid,
+                                                         const float* __restrict__ tid2w,
+                                                         int vocab, int n_experts, int top_k,
+                                                         int32_t* __restrict__ ids,
+                                                         float* __restrict__ w,
+                                                         int32_t* __restrict__ dev_error) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)n_tokens * top_k) return;
+  const int64_t t = i / top_k;
+  const int j = (int)(i - t * top_k);
+  const int tok = token_ids[t];
+  int32_t id = -1;
+  float wt = 0.0f;
+  int err = 0;
+  if (tok < 0 || tok >= vocab) {
+    err = MOE_DEVERR_TOKEN_ID;
+  } else {
+    id = tid2eid[(int64_t)tok * top_k + j];
+    wt = tid2w[(int64_t)tok * top_k + j];
+    if (id < 0 || id >= n_experts) {
+      id = -1;
+      wt = 0.0f;
+      err = MOE_DEVERR_EXPERT_ID;
+    }
+  }
+  ids[i] = id;
+  w[i] = wt;
+  if (err && dev_error) atomicOr(dev_error, err);
+}
+
+// ---------------------------------------------------------------- grouping
+
+struct GroupShared {
+  // s_count: histogram, later each expert's count in the current round;
+  // s_next: next free position of each expert; s_wave[w][e]: count of
+  // wavefront w, then its offset inside the round (<= 1024).
+  int s_count[MOE_MAX_EXPERTS];
+  int s_next[MOE_MAX_EXPERTS];
+  uint16_t s_wave[kGroupWaves][MOE_MAX_EXPERTS];
+  int s_wave_sum[kGroupWaves];
+};
+
+__device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (1ull << lane) - 1ull; }
+
+// The whole grouping by one 1024-thread workgroup.  `ids` may point at
+// global memory or LDS.
+__device__ void group_block(const int32_t* ids, int nk, int n_experts, int32_t* __restrict__ counts,
+                            int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+                            int32_t* __restrict__ inv_perm, int32_t* __restrict__ dev_error,
+                            GroupShared& sh) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+
+  for (int e = tid; e < n_experts; e += kGroupThreads) sh.s_count[e] = 0;
+  for (int i = tid; i < kGroupWaves * MOE_MAX_EXPERTS; i += kGroupThreads)
+    (&sh.s_wave[0][0])[i] = 0;
+  __syncthreads();
+
+  // 1. histogram (order-free)
+  int bad = 0;
+  for (int f = tid; f < nk; f += kGroupThreads) {
+    const int e = ids[f];
+    if (e >= 0 && e < n_experts)
+      atomicAdd(&sh.s_count[e], 1);
+    else
+      bad = 1;
+  }
+  __syncthreads();
+
+  // 2. exclusive scan over experts (n_experts <= 1024: one per thread)
+  const int c = tid < n_experts ? sh.s_count[tid] : 0;
+  int incl = c;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int t = __shfl_up(incl, off);
+    if (lane >= off) incl += t;
+  }
+  if (lane == kWave - 1) sh.s_wave_sum[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += sh.s_wave_sum[w];
+  incl += before;
+  const int excl = incl - c;
+  if (tid < n_experts) {
+    counts[tid] = c;
+    offsets[tid] = excl;
+    sh.s_next[tid] = excl;
+    if (tid == n_experts - 1) offsets[n_experts] = incl;
+  }
+  __syncthreads();
+
+  // 3. stable scatter, 1024 flat indices per round, in ascending order
+  int nbits = 0;
+  while ((1 << nbits) < n_experts) ++nbits;
+  for (int base = 0; base < nk; base += kGroupThreads) {
+    const int f = base + tid;
+    const int e = f < nk ? ids[f] : -1;
+    const bool valid = e >= 0 && e < n_experts;
+    // lanes of this wavefront holding the same expert
+    uint64_t same = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = valid && ((e >> b) & 1);
+      const uint64_t m = __ballot(bit);
+      same &= bit ? m : ~m;
+    }
+    const int rank = __popcll(same & lanemask_lt(lane));
+    const bool last = valid && (same >> lane) == 1ull;
+    if (last) sh.s_wave[wave][e] = (uint16_t)(rank + 1);
+    __syncthreads();
+    // per expert: wavefront counts -> offsets inside this round
+    for (int x = tid; x < n_experts; x += kGroupThreads) {
+      int run = 0;
+#pragma unroll
+      for (int w = 0; w < kGroupWaves; ++w) {
+        const int cnt = sh.s_wave[w][x];
+        sh.s_wave[w][x] = (uint16_t)run;
+        run += cnt;
+      }
+      sh.s_count[x] = run;
+    }
+    __syncthreads();
+    if (valid) {
+      const int p = sh.s_next[e] + (int)sh.s_wave[wave][e] + rank;
+      perm[p] = f;
+      inv_perm[f] = p;
+    } else if (f < nk) {
+      inv_perm[f] = -1;
+    }
+    __syncthreads();
+    for (int x = tid; x < n_experts; x += kGroupThreads) {
+      sh.s_next[x] += sh.s_count[x];
+#pragma unroll
+      for (int w = 0; w < kGroupWaves; ++w) sh.s_wave[w][x] = 0;
+    }
+    __syncthreads();
+  }
+  if (bad && dev_error) atomicOr(dev_error, MOE_DEVERR_EXPERT_ID);
+}
+
+__global__ __launch_bounds__(kGroupThreads) void group_kernel(
+    const int32_t* __restrict__ ids, int nk, int n_experts, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
+    int32_t* __restrict__ dev_error) {
+  __shared__ GroupShared sh;
+  group_block(ids, nk, n_experts, counts, offsets, perm, inv_perm, dev_error, sh);
+}
+
+// Learned routing and grouping of a small batch by one workgroup: the
+// sixteen wavefronts route the tokens (token t by wavefront t % 16), keep
+// the ids in LDS, then group them.
+template <int PER>
+__global__ __launch_bounds__(kGroupThreads) void route_group_kernel(
+    const float* __restrict__ logits, int n_tokens, int n_experts, int top_k, float routed_scale,
+    int32_t* __restrict__ ids, float* __restrict__ w, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
+    int32_t* __restrict__ dev_error) {
+  __shared__ GroupShared sh;
+  __shared__ int32_t s_ids[kFusedMaxFlat];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  for (int t = wave; t < n_tokens; t += kGroupWaves) {
+    int id;
+    float wt;
+    route_token<PER>(logits + (size_t)t * n_experts, n_experts, top_k, routed_scale, lane, id,
+                     wt);
+    if (lane < top_k) {
+      ids[t * top_k + lane] = id;
+      w[t * top_k + lane] = wt;
+      s_ids[t * top_k + lane] = id;
+    }
+  }
+  __syncthreads();
+  group_block(s_ids, n_tokens * top_k, n_experts, counts, offsets, perm, inv_perm, dev_error, sh);
+}
+
+int per_lane(int n_experts) { return (n_experts + kWave - 1) / kWave; }
+
+}  // namespace
+
+hipError_t launch_route(const float* logits, int n_tokens, int n_experts, int top_k,
+                        float routed_scale, int32_t* ids, float* w, hipStream_t stream) {
+  const dim3 grid((n_tokens + 3) / 4), block(256);
+  const int per = per_lane(n_experts);
+#define MOE_ROUTE(P)                                                                   \
+  route_topk_kernel<P><<<grid, block, 0, stream>>>(logits, n_tokens, n_experts, top_k, \
+                                                   routed_scale, ids, w)
+  if (per <= 1)
+    MOE_ROUTE(1);
+  else if (per <= 2)
+    MOE_ROUTE(2);
+  else if (per <= 4)
+    MOE_ROUTE(4);
+  else if (per <= 8)
+    MOE_ROUTE(8);
+  else
+    MOE_ROUTE(16);
+#undef MOE_ROUTE
+  return hipGetLastError();
+}
+
+hipError_t launch_route_hash(const int32_t* token_ids, int n_tokens, const int32_t* tid2eid,
+                             const float* tid2w, int vocab, int n_experts, int top_k,
+                             int32_t* ids, float* w, int32_t* dev_error, hipStream_t stream) {
+  const int64_t n = (int64_t)n_tokens * top_k;
+  const dim3 grid((unsigned)((n + 255) / 256)), block(256);
+  route_hash_kernel<<<grid, block, 0, stream>>>(token_ids, n_tokens, tid2eid, tid2w, vocab,
+                                                n_experts, top_k, ids, w, dev_error);
+  return hipGetLastError();
+}
+
+hipError_t launch_group(const int32_t* ids, int n_tokens, int top_k, int n_experts,
+                        int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                        int32_t* dev_error, hipStream_t stream) {
+  group_kernel<<<1, kGroupThreads, 0, stream>>>(ids, n_tokens * top_k, n_experts, counts, offsets,
+                                                perm, inv_perm, dev_error);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_group(const float* logits, int n_tokens, int n_experts, int top_k,
+                              float routed_scale, int32_t* ids, float* w, int32_t* counts,
+                              int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                              int32_t* dev_error, hipStream_t stream) {
+  if ((int64_t)n_tokens * top_k > kFusedMaxFlat) {
+    hipError_t e = launch_route(logits, n_tokens, n_experts, top_k, routed_scale, ids, w, stream);
+    if (e != hipSuccess) return e;
+    return launch_group(ids, n_tokens, top_k, n_experts, counts, offsets, perm, inv_perm,
+                        dev_error, stream);
+  }
+  const int per = per_lane(n_experts);
+#define MOE_RG(P)                                                                          \
+  route_group_kernel<P><<<1, kGroupThreads, 0, stream>>>(logits, n_tokens, n_experts,      \
+                                                         top_k, routed_scale, ids, w, counts, \
+                                                         offsets, perm, inv_perm, dev_error)
+  if (per <= 1)
+    MOE_RG(1);
+  else if (per <= 2)
+    MOE_RG(2);
+  else if (per <= 4)
+    MOE_RG(4);
+  else if (per <= 8)
+    MOE_RG(8);
+  else
+    MOE_RG(16);
+#undef MOE_RG
+  return hipGetLastError();
+}
+
+}  // namespace moe

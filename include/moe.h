@@ -32,7 +32,8 @@
  *     range) are OR-ed into the optional `dev_error` word (never cleared by
  *     the library) with no host synchronisation; the offending entry is
  *     skipped and every access stays in bounds.
- *   - n_tokens == 0 is valid and enqueues nothing.
+ *   - n_tokens == 0 is valid; moe_group (and moe_route_group) then write
+ *     zero counts and offsets, every other call enqueues nothing.
  *
  * Weight layout (the pages print no layout; this is the reading used):
  *   A projection is a stack of experts, expert e at byte offset
@@ -136,6 +137,18 @@ moe_status moe_route_hash(const int32_t* token_ids, int n_tokens, const int32_t*
                           int32_t* topk_ids, float* topk_w, int32_t* dev_error,
                           hipStream_t stream);
 
+/*
+ * moe_route followed by moe_group on the same ids, with the same outputs
+ * and rules as those two calls.  Batches with n_tokens*top_k <= 4096 run in
+ * a single launch (one workgroup routes the tokens and groups them in LDS),
+ * which matters when the batch is a few decode tokens; larger batches use
+ * the two kernels.
+ */
+moe_status moe_route_group(const float* logits, int n_tokens, int n_experts, int top_k,
+                           float routed_scale, int32_t* topk_ids, float* topk_w, int32_t* counts,
+                           int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                           int32_t* dev_error, hipStream_t stream);
+
 /* Workspace bytes moe_group needs (currently 0: it works in LDS). */
 size_t moe_group_workspace_bytes(int n_tokens, int top_k, int n_experts);
 
@@ -197,6 +210,21 @@ moe_status moe_ffn_down(const moe_layer* layer, const void* x, int x_type, int n
                         const float* topk_w, const int32_t* counts, const int32_t* offsets,
                         const int32_t* perm, const int32_t* inv_perm, float* y,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_ffn_forward that also records, into caller-created events (each may
+ * be NULL), the start and end of the gate/up kernel and of the down kernel.
+ * The times come from the kernels' own dispatches, so no extra packets are
+ * queued and the stream runs as it would untimed.  For benchmarks and
+ * profilers: hipEventElapsedTime(start, stop) is the kernel's duration.
+ */
+moe_status moe_ffn_forward_timed(const moe_layer* layer, const void* x, int x_type,
+                                 int n_tokens, const float* topk_w, const int32_t* counts,
+                                 const int32_t* offsets, const int32_t* perm,
+                                 const int32_t* inv_perm, float* y, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream,
+                                 hipEvent_t gate_up_start, hipEvent_t gate_up_stop,
+                                 hipEvent_t down_start, hipEvent_t down_stop);
 
 /* A static, human-readable name of a status code. */
 const char* moe_status_string(moe_status s);

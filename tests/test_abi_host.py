@@ -69,7 +69,8 @@ def test_ffn_workspace_bytes():
     slots = n * 6 + n
     h = -(-slots * 2048 * 2 // 256) * 256
     o = -(-slots * 4096 * 4 // 256) * 256
-    assert B.lib().moe_ffn_workspace_bytes(ctypes.byref(L), n) == 2 * h + o
+    c = 4096 // 16 * 4  # one int32 counter per 16-row block
+    assert B.lib().moe_ffn_workspace_bytes(ctypes.byref(L), n) == 2 * h + o + c
     assert B.lib().moe_ffn_workspace_bytes(ctypes.byref(L), 0) == 0
     assert B.lib().moe_ffn_workspace_bytes(ctypes.byref(_layer(hidden=100)), 8) == 0
     assert B.lib().moe_ffn_workspace_bytes(None, 8) == 0
@@ -151,6 +152,13 @@ def test_route_hash_and_group_reject_bad_arguments():
     assert G(FAKE, 4, 6, 2048, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == B.MOE_ERR_UNSUPPORTED
     assert G(FAKE, 4, 9, 256, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == B.MOE_ERR_UNSUPPORTED
     assert G(FAKE, 4, 300, 256, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == B.MOE_ERR_INVALID
+    RG = B.lib().moe_route_group
+    assert RG(FAKE, 4, 256, 6, 1.5, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None) == \
+        B.MOE_ERR_INVALID
+    assert RG(FAKE, 4, 256, 6, -1.5, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == \
+        B.MOE_ERR_INVALID
+    assert RG(FAKE, 4, 256, 9, 1.5, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == \
+        B.MOE_ERR_UNSUPPORTED
 
 
 @pytest.mark.skipif(shutil.which("g++") is None, reason="needs g++")

@@ -195,3 +195,20 @@ def test_token_permutation_permutes_output():
     torch.cuda.synchronize()
     d = (yp - y[p.to(DEV)]).abs().max().item()
     assert d <= 1e-5 * y.pow(2).mean().sqrt().item()
+
+
+def test_timed_entry_point_matches_and_times():
+    wl = I.WORKLOADS["decode1"]
+    print("case timed", flush=True)
+    layer, x, x_d, routing, routing_d = gpu_inputs(wl)
+    y, ids, w, g = B.forward(layer, x_d, routing_d)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    y2 = B.moe_ffn_forward_timed(layer, x_d, w, g, evs)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    gu = evs[0].elapsed_time(evs[1])
+    dn = evs[2].elapsed_time(evs[3])
+    assert 0 < gu < 100 and 0 < dn < 100, (gu, dn)  # milliseconds
+    y3 = B.moe_ffn_forward_timed(layer, x_d, w, g, [None, None, None, None])
+    torch.cuda.synchronize()
+    assert torch.equal(y, y3)

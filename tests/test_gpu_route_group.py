@@ -168,3 +168,20 @@ def test_route_and_group_deterministic():
     torch.cuda.synchronize()
     for x, y in zip(list(a) + list(ga), list(b) + list(gb)):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("name,n_tokens", [("tiny", None), ("decode1", None), ("decode32", None),
+                                           ("prefill512", None), ("prefill512", 1000)])
+def test_route_group_fused_equals_oracle(name, n_tokens):
+    # n_tokens*top_k <= 4096 runs as one launch; 1000 tokens x 6 takes the
+    # two-kernel path
+    wl = I.WORKLOADS[name]
+    print("case route_group", name, n_tokens, flush=True)
+    lg = I.router_logits(wl, n_tokens=n_tokens)
+    ids, w, g = B.moe_route_group(lg.to(DEV), wl.top_k, wl.routed_scale)
+    torch.cuda.synchronize()
+    rids, rw = O.route_topk(lg.numpy(), wl.top_k, wl.routed_scale)
+    assert np.array_equal(ids.cpu().numpy(), rids)
+    assert_w_close(w.cpu().numpy(), rw)
+    for got, ref in zip(g, O.group(rids, wl.n_experts)):
+        assert np.array_equal(got.cpu().numpy(), ref)
