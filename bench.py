@@ -288,9 +288,8 @@ def main():
         runner.step(s)
     torch.cuda.synchronize()
 
-    mk = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    evs = [tuple(mk() for _ in range(4)) for _ in range(steps)]
-    ev_handles = [tuple(ctypes.c_void_p(e.cuda_event) for e in four) for four in evs]
+    evs = [tuple(B.HipEvent() for _ in range(4)) for _ in range(steps)]
+    ev_handles = [tuple(e.handle for e in four) for four in evs]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for j in range(steps):
@@ -298,8 +297,8 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
 
-    gate_up_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    down_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    gate_up_ms = [e[0].elapsed_ms(e[1]) for e in evs]
+    down_ms = [e[2].elapsed_ms(e[3]) for e in evs]
     gu_avg_s = float(np.mean(gate_up_ms)) / 1e3
     dn_avg_s = float(np.mean(down_ms)) / 1e3
     counts_list = routed_counts(runner, n_pool)

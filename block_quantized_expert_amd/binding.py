@@ -81,6 +81,43 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
+class HipEvent:
+    """A timing hipEvent_t made with the HIP runtime the process has already
+    loaded (the one torch and libmoe.so share).  Events recorded by the
+    library from kernel dispatches are read with ``elapsed_ms``."""
+
+    _rt = None
+
+    @classmethod
+    def runtime(cls):
+        if cls._rt is None:
+            rt = ctypes.CDLL("libamdhip64.so.7")
+            rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+            rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                               ctypes.c_void_p]
+            rt.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+            cls._rt = rt
+        return cls._rt
+
+    def __init__(self):
+        self.handle = ctypes.c_void_p()
+        if self.runtime().hipEventCreate(ctypes.byref(self.handle)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+
+    def __del__(self):
+        if self._rt is not None and self.handle:
+            self._rt.hipEventDestroy(self.handle)
+
+    def elapsed_ms(self, stop: "HipEvent") -> float:
+        ms = ctypes.c_float()
+        rt = self.runtime()
+        rt.hipEventSynchronize(stop.handle)
+        if rt.hipEventElapsedTime(ctypes.byref(ms), self.handle, stop.handle) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+
 def status_string(status: int) -> str:
     return lib().moe_status_string(status).decode()
 
@@ -235,8 +272,8 @@ def moe_ffn_down(layer: Layer, x, w, grouping, y=None, workspace=None, stream=No
 
 def moe_ffn_forward_timed(layer: Layer, x, w, grouping, events, y=None, workspace=None,
                           stream=None):
-    """``events``: four torch.cuda.Event(enable_timing=True) (or None) for
-    gate/up start, gate/up stop, down start, down stop."""
+    """``events``: four HipEvent (or None) for gate/up start, gate/up stop,
+    down start, down stop."""
     n = x.shape[0]
     x_type = MOE_ACT_BF16 if x.dtype == torch.bfloat16 else MOE_ACT_F32
     if y is None:
@@ -245,7 +282,7 @@ def moe_ffn_forward_timed(layer: Layer, x, w, grouping, events, y=None, workspac
         workspace = torch.empty(max(layer.workspace_bytes(n), 1), dtype=torch.uint8,
                                 device=x.device)
     counts, offsets, perm, inv_perm = grouping
-    evs = [None if e is None else ctypes.c_void_p(e.cuda_event) for e in events]
+    evs = [None if e is None else e.handle for e in events]
     _check(lib().moe_ffn_forward_timed(ctypes.byref(layer.c), _ptr(x), x_type, n, _ptr(w),
                                        _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(inv_perm),
                                        _ptr(y), _ptr(workspace), workspace.numel(),

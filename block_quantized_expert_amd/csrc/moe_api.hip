@@ -50,7 +50,6 @@ moe::FfnParams make_params(const moe_layer* L, const void* x, int x_type, int n_
   p.h_lo = reinterpret_cast<__bf16*>(ws + plan.off_h_lo);
   p.h_stride = plan.h_stride;
   p.obuf = reinterpret_cast<float*>(ws + plan.off_obuf);
-  p.rb_count = reinterpret_cast<int32_t*>(ws + plan.off_count);
   p.y = y;
   return p;
 }

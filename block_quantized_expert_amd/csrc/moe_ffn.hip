@@ -26,11 +26,13 @@
 // CH steps before decoding any of them, so each one keeps several KiB of
 // weights in flight.  The partial sums of the four wavefronts meet in LDS.
 //
-// Combine.  The down kernel writes each slot's weighted output to the
-// workspace; the last workgroup to finish a 16-row block (an agent-scope
-// counter per block) sums that block for every token in a fixed order --
-// shared first, then slots 0..k-1 -- so y is deterministic and no separate
-// combine launch is needed.
+// Small batches (decode) stage the tile's activation rows in LDS once per
+// item, and run the down projection and the combine as one pass in which a
+// workgroup owns 16 output rows for every token and walks all active
+// experts: the routing weight is folded into the staged h, so each token's
+// sum builds up in one accumulator in a fixed order (deterministic, no
+// per-slot outputs).  Larger batches write weighted per-slot outputs and
+// sum them in a separate combine kernel, shared first then slots 0..k-1.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -44,6 +46,7 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxSeg = MOE_MAX_EXPERTS + 1;
 constexpr int kMaxGrid = 256 * 8;  // 256 CUs, up to 8 resident workgroups each
+constexpr int kLdsBudget = 140 * 1024;  // dynamic LDS a kernel may ask for
 
 // ------------------------------------------------------------ work items
 
@@ -195,6 +198,39 @@ __device__ __forceinline__ void load_f32_32(const float* src, bf16x8 (&hi)[4], b
   }
 }
 
+// The same from the LDS copy of the activations: `row` is a byte offset into
+// s_x (negative: zeros), `k` the first reduction index.
+__device__ __forceinline__ void load_bf16_32_lds(const char* s_x, int row, int k,
+                                                 bf16x8 (&b)[4]) {
+  if (row >= 0) {
+    const char* src = s_x + row + k * 2;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(src + 16 * j));
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = as_bf16x8(u32x4{0, 0, 0, 0});
+  }
+}
+
+__device__ __forceinline__ void load_f32_32_lds(const char* s_x, int row, int k,
+                                                bf16x8 (&hi)[4], bf16x8 (&lo)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      f32x4 v = row >= 0 ? *reinterpret_cast<const f32x4*>(s_x + row + (k + 8 * j + 4 * h) * 4)
+                         : f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        __bf16 a, b;
+        split_bf16(v[r], a, b);
+        hi[j][4 * h + r] = a;
+        lo[j][4 * h + r] = b;
+      }
+    }
+  }
+}
+
 // number of reduction steps ks = wave + 4j below nks
 __device__ __forceinline__ int wave_steps(int nks, int wave) {
   return nks > wave ? (nks - wave + kWaves - 1) / kWaves : 0;
@@ -202,12 +238,19 @@ __device__ __forceinline__ int wave_steps(int nks, int wave) {
 
 // ------------------------------------------------------- gate/up
 
-template <int NBT, bool XF32, int WT>
+// Activation rows of an item's token columns: in global memory, or staged
+// in LDS (row stride x_stride bytes) when XLDS.
+struct XRows {
+  const char* row[4];
+};
+
+template <int NBT, bool XF32, bool XLDS, int WT>
 __device__ __forceinline__ void gate_up_item(const FfnParams& p, const Item& it, bool shared,
-                                             int wave, int g, int r16, f32x4 (&ag)[NBT],
-                                             f32x4 (&au)[NBT]) {
+                                             int wave, int g, int r16, char* s_x, int x_stride,
+                                             f32x4 (&ag)[NBT], f32x4 (&au)[NBT]) {
   using F = Fmt<WT>;
   constexpr int CH = F::CH;
+  constexpr int XB = XF32 ? 4 : 2;  // activation bytes
   const int rows = shared ? p.shared_inter : p.inter;
   const int64_t cb = F::row_bytes(p.hidden);
   const int64_t sb = F::scale_row_bytes(p.hidden);
@@ -216,33 +259,69 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const Item& it,
   const uint8_t* gsr = (shared ? p.sgate_s : p.gate_s) + row * sb;
   const uint8_t* ucr = (shared ? p.sup_c : p.up_c) + row * cb;
   const uint8_t* usr = (shared ? p.sup_s : p.up_s) + row * sb;
-
-  // activation row of each of this lane's token columns
   const int64_t shared_base = (int64_t)p.n_tokens * p.top_k;
-  const char* xr[NBT];
+  const int S = wave_steps(p.hidden / 128, wave);
+  const int nbt = (it.m + 15) >> 4;
+
+  // chunk 0's codes are requested before the activations are staged
+  u32x4 qg[CH][F::Q], qu[CH][F::Q];
+  uint32_t sg[CH], su[CH];
+  const int rem0 = min(CH, S);
 #pragma unroll
-  for (int tb = 0; tb < NBT; ++tb) {
-    const int n = tb * 16 + r16;
-    xr[tb] = nullptr;
-    if (n < it.m) {
-      const int64_t slot = it.slot0 + n;
-      const int64_t tok = shared ? slot - shared_base : p.perm[slot] / p.top_k;
-      xr[tb] = static_cast<const char*>(p.x) + tok * p.hidden * (XF32 ? 4 : 2);
+  for (int i = 0; i < CH; ++i) {
+    if (i < rem0) {
+      const int ks = wave + kWaves * i;
+      load_codes<WT>(gcr, gsr, ks, g, qg[i], sg[i]);
+      load_codes<WT>(ucr, usr, ks, g, qu[i], su[i]);
     }
   }
-  const int nbt = (it.m + 15) >> 4;
-  const int S = wave_steps(p.hidden / 128, wave);
+
+  // token columns: a global activation row, or a byte offset into the LDS
+  // copy of the tile (-1 for an empty column)
+  const char* xr[NBT];
+  int xo[NBT];
+  if constexpr (XLDS) {
+    const int per_row = p.hidden * XB / 16;
+    const int chunks = it.m * per_row;
+    for (int c = threadIdx.x; c < chunks; c += kThreads) {
+      const int n = c / per_row;
+      const int off = (c - n * per_row) * 16;
+      const int64_t slot = it.slot0 + n;
+      const int64_t tok = shared ? slot - shared_base : p.perm[slot] / p.top_k;
+      *reinterpret_cast<u32x4*>(s_x + n * x_stride + off) =
+          load16(static_cast<const char*>(p.x) + tok * p.hidden * XB + off);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int tb = 0; tb < NBT; ++tb) {
+      const int n = tb * 16 + r16;
+      xo[tb] = n < it.m ? n * x_stride : -1;
+      xr[tb] = nullptr;
+    }
+  } else {
+#pragma unroll
+    for (int tb = 0; tb < NBT; ++tb) {
+      const int n = tb * 16 + r16;
+      xr[tb] = nullptr;
+      xo[tb] = -1;
+      if (n < it.m) {
+        const int64_t slot = it.slot0 + n;
+        const int64_t tok = shared ? slot - shared_base : p.perm[slot] / p.top_k;
+        xr[tb] = static_cast<const char*>(p.x) + tok * p.hidden * XB;
+      }
+    }
+  }
 
   for (int j0 = 0; j0 < S; j0 += CH) {
     const int rem = min(CH, S - j0);
-    u32x4 qg[CH][F::Q], qu[CH][F::Q];
-    uint32_t sg[CH], su[CH];
+    if (j0 > 0) {
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      if (i < rem) {
-        const int ks = wave + kWaves * (j0 + i);
-        load_codes<WT>(gcr, gsr, ks, g, qg[i], sg[i]);
-        load_codes<WT>(ucr, usr, ks, g, qu[i], su[i]);
+      for (int i = 0; i < CH; ++i) {
+        if (i < rem) {
+          const int ks = wave + kWaves * (j0 + i);
+          load_codes<WT>(gcr, gsr, ks, g, qg[i], sg[i]);
+          load_codes<WT>(ucr, usr, ks, g, qu[i], su[i]);
+        }
       }
     }
 #pragma unroll
@@ -257,8 +336,11 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const Item& it,
           if (tb >= nbt) break;
           if constexpr (XF32) {
             bf16x8 bh[4], bl[4];
-            load_f32_32(xr[tb] ? reinterpret_cast<const float*>(xr[tb]) + kofs : nullptr, bh,
-                        bl);
+            if constexpr (XLDS)
+              load_f32_32_lds(s_x, xo[tb], kofs, bh, bl);
+            else
+              load_f32_32(xr[tb] ? reinterpret_cast<const float*>(xr[tb]) + kofs : nullptr, bh,
+                          bl);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               ag[tb] = mfma_bf16(wg[j], bh[j], ag[tb]);
@@ -268,7 +350,10 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const Item& it,
             }
           } else {
             bf16x8 b[4];
-            load_bf16_32(xr[tb] ? reinterpret_cast<const __bf16*>(xr[tb]) + kofs : nullptr, b);
+            if constexpr (XLDS)
+              load_bf16_32_lds(s_x, xo[tb], kofs, b);
+            else
+              load_bf16_32(xr[tb] ? reinterpret_cast<const __bf16*>(xr[tb]) + kofs : nullptr, b);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               ag[tb] = mfma_bf16(wg[j], b[j], ag[tb]);
@@ -281,18 +366,15 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const Item& it,
   }
 }
 
-template <int NBT, bool XF32>
-__global__ __launch_bounds__(kThreads) void gate_up_kernel(FfnParams p) {
+template <int NBT, bool XF32, bool XLDS>
+__global__ __launch_bounds__(kThreads) void gate_up_kernel(FfnParams p, int x_stride) {
   constexpr int TN = 16 * NBT;
+  extern __shared__ __align__(16) char s_x[];
   __shared__ int s_pref[kMaxSeg + 1];
   __shared__ int s_tmp[kWaves];
   __shared__ f32x4 s_red[kWaves - 1][2 * NBT][kWave];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, r16 = lane & 15;
-
-  // the down kernel's per-row-block counters start from zero every call
-  if (blockIdx.x == 0)
-    for (int i = threadIdx.x; i < p.hidden / 16; i += kThreads) p.rb_count[i] = 0;
 
   const int total = build_item_prefix(p, TN, false, s_pref, s_tmp);
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
@@ -305,9 +387,11 @@ __global__ __launch_bounds__(kThreads) void gate_up_kernel(FfnParams p) {
       au[tb] = f32x4{0, 0, 0, 0};
     }
     if ((shared ? p.sw_type : p.w_type) == MOE_W_MXFP4)
-      gate_up_item<NBT, XF32, MOE_W_MXFP4>(p, it, shared, wave, g, r16, ag, au);
+      gate_up_item<NBT, XF32, XLDS, MOE_W_MXFP4>(p, it, shared, wave, g, r16, s_x, x_stride,
+                                                 ag, au);
     else
-      gate_up_item<NBT, XF32, MOE_W_FP8E4M3_B128>(p, it, shared, wave, g, r16, ag, au);
+      gate_up_item<NBT, XF32, XLDS, MOE_W_FP8E4M3_B128>(p, it, shared, wave, g, r16, s_x,
+                                                        x_stride, ag, au);
 
     if (wave > 0) {
 #pragma unroll
@@ -351,7 +435,7 @@ __global__ __launch_bounds__(kThreads) void gate_up_kernel(FfnParams p) {
   }
 }
 
-// ------------------------------------------------------- down + combine
+// ------------------------------------------------------- down (per slot)
 
 template <int NBT, int WT>
 __device__ __forceinline__ void down_item(const FfnParams& p, const Item& it, bool shared,
@@ -411,34 +495,15 @@ __device__ __forceinline__ void down_item(const FfnParams& p, const Item& it, bo
   }
 }
 
-// y rows [row0, row0+16) of every token from the per-slot outputs, in the
-// fixed order shared, slot 0, ..., slot k-1.
-__device__ void combine_rows(const FfnParams& p, int row0) {
-  const int64_t nk = (int64_t)p.n_tokens * p.top_k;
-  for (int idx = threadIdx.x; idx < p.n_tokens * 4; idx += kThreads) {
-    const int t = idx >> 2;
-    const int64_t q = row0 + 4 * (idx & 3);
-    f32x4 acc = f32x4{0, 0, 0, 0};
-    if (p.has_shared) acc = *reinterpret_cast<const f32x4*>(p.obuf + (nk + t) * p.hidden + q);
-    for (int j = 0; j < p.top_k; ++j) {
-      const int pp = p.inv_perm[(int64_t)t * p.top_k + j];
-      if (pp >= 0) acc += *reinterpret_cast<const f32x4*>(p.obuf + (int64_t)pp * p.hidden + q);
-    }
-    *reinterpret_cast<f32x4*>(p.y + (int64_t)t * p.hidden + q) = acc;
-  }
-}
-
 template <int NBT>
 __global__ __launch_bounds__(kThreads) void down_kernel(FfnParams p) {
   constexpr int TN = 16 * NBT;
   __shared__ int s_pref[kMaxSeg + 1];
   __shared__ int s_tmp[kWaves];
-  __shared__ int s_last;
   __shared__ f32x4 s_red[kWaves - 1][NBT][kWave];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, r16 = lane & 15;
   const int total = build_item_prefix(p, TN, true, s_pref, s_tmp);
-  const int per_block = total / (p.hidden >> 4);  // items that feed one row block
 
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
     const Item it = find_item(p, s_pref, item, TN, true);
@@ -472,18 +537,242 @@ __global__ __launch_bounds__(kThreads) void down_kernel(FfnParams p) {
         }
       }
     }
-    // publish this item's outputs, then count it against its row block
-    __threadfence();
     __syncthreads();
-    const int rb = it.row0 >> 4;
-    if (threadIdx.x == 0) s_last = atomicAdd(&p.rb_count[rb], 1) == per_block - 1;
-    __syncthreads();
-    if (s_last) {
-      __threadfence();  // see every other item's outputs
-      combine_rows(p, it.row0);
-      if (threadIdx.x == 0) p.rb_count[rb] = 0;
+  }
+}
+
+// y[t] = o_shared[t] + sum_i o[inv_perm[t*k + i]] (weights already applied),
+// in that fixed order; four features per thread.
+__global__ __launch_bounds__(256) void combine_kernel(FfnParams p) {
+  const int h4 = p.hidden / 4;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)p.n_tokens * h4) return;
+  const int64_t t = i / h4;
+  const int64_t q = (i - t * h4) * 4;
+  f32x4 acc = f32x4{0, 0, 0, 0};
+  if (p.has_shared)
+    acc = *reinterpret_cast<const f32x4*>(p.obuf +
+                                          ((int64_t)p.n_tokens * p.top_k + t) * p.hidden + q);
+  for (int j = 0; j < p.top_k; ++j) {
+    const int pp = p.inv_perm[t * p.top_k + j];
+    if (pp >= 0) acc += *reinterpret_cast<const f32x4*>(p.obuf + (int64_t)pp * p.hidden + q);
+  }
+  *reinterpret_cast<f32x4*>(p.y + t * p.hidden + q) = acc;
+}
+
+// ------------------------------------------------------- down + combine, small batch
+
+constexpr int kSmallWaves = 8;
+constexpr int kSmallThreads = kSmallWaves * kWave;
+constexpr int kSmallMaxTokens = 16;  // one MFMA column per token
+constexpr int kSmallMaxSlots = 128;
+constexpr int kSmallMaxActive = kSmallMaxSlots + 1;
+constexpr int kStageRow = 136;  // bf16 per staged row: 128 + 8 so rows start on other banks
+constexpr int kSmallBatch = 8;  // units whose codes a wavefront requests together
+
+// One workgroup per 16 output rows.  Units (active expert a, step s of the
+// current chunk) are dealt to the eight wavefronts; a unit decodes the 16
+// rows x 128 reduction indices of expert a's down matrix and multiplies
+// them with the staged w*h of every token (column n = token n, zero where
+// the token did not pick the expert).
+template <int WT, int SWT>
+__global__ __launch_bounds__(kSmallThreads) void down_combine_small_kernel(FfnParams p,
+                                                                            int spc) {
+  extern __shared__ __align__(16) char smem[];
+  __shared__ int s_act[kSmallMaxActive];   // expert id (n_experts: shared)
+  __shared__ int s_off[kSmallMaxActive];   // first slot of the active expert
+  __shared__ int16_t s_col[kSmallMaxActive][kSmallMaxTokens];  // slot of token n or -1
+  __shared__ float s_w[kSmallMaxSlots];
+  __shared__ int s_nact, s_nroute;
+  __shared__ f32x4 s_red[kSmallWaves - 1][kWave];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int row0 = blockIdx.x * 16;
+  const int nk = p.n_tokens * p.top_k;
+  const int n_slots = nk + (p.has_shared ? p.n_tokens : 0);
+
+  // active experts, compacted in expert order, then the shared expert
+  if (wave == 0) {
+    int nact = 0;
+    for (int e0 = 0; e0 < p.n_experts; e0 += kWave) {
+      const int e = e0 + lane;
+      const bool on = e < p.n_experts && p.counts[e] > 0;
+      const uint64_t m = __ballot(on);
+      if (on) {
+        const int a = nact + __popcll(m & ((1ull << lane) - 1ull));
+        s_act[a] = e;
+        s_off[a] = p.offsets[e];
+      }
+      nact += __popcll(m);
+    }
+    if (lane == 0) {
+      s_nroute = nact;
+      if (p.has_shared) {
+        s_act[nact] = p.n_experts;
+        s_off[nact] = nk;
+      }
+      s_nact = nact + (p.has_shared ? 1 : 0);
+    }
+  }
+  for (int i = tid; i < kSmallMaxActive * kSmallMaxTokens; i += kSmallThreads)
+    (&s_col[0][0])[i] = -1;
+  __syncthreads();
+  const int A = s_nact, AR = s_nroute;
+  const int nvalid = AR > 0 ? s_off[AR - 1] + p.counts[s_act[AR - 1]] : 0;
+  for (int q = tid; q < n_slots; q += kSmallThreads) {
+    if (q < nk) {
+      if (q >= nvalid) continue;  // slots of out-of-range ids do not exist
+      int lo = 0, hi = AR;        // active expert owning slot q
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_off[mid] <= q)
+          lo = mid;
+        else
+          hi = mid;
+      }
+      const int f = p.perm[q];
+      s_col[lo][f / p.top_k] = (int16_t)q;
+      s_w[q] = p.topk_w[f];
+    } else {
+      s_col[A - 1][q - nk] = (int16_t)q;
+      s_w[q] = 1.0f;
+    }
+  }
+  __syncthreads();
+
+  __bf16* s_bh = reinterpret_cast<__bf16*>(smem);
+  __bf16* s_bl = s_bh + (size_t)spc * n_slots * kStageRow;
+  const int nks = max(p.inter, p.has_shared ? p.shared_inter : 0) / 128;
+  f32x4 acc = f32x4{0, 0, 0, 0};
+
+  for (int ks0 = 0; ks0 < nks; ks0 += spc) {
+    const int steps = min(spc, nks - ks0);
+    // stage w * (h_hi + h_lo) for every slot, split again into hi + lo
+    const int groups = steps * n_slots * 16;
+    for (int i = tid; i < groups; i += kSmallThreads) {
+      const int q8 = i & 15;
+      const int rest = i >> 4;
+      const int slot = rest % n_slots;
+      const int s = rest / n_slots;
+      const int k = (ks0 + s) * 128 + q8 * 8;
+      const int kdim = slot < nk ? p.inter : p.shared_inter;
+      u32x4 vh = u32x4{0, 0, 0, 0}, vl = u32x4{0, 0, 0, 0};
+      if ((slot >= nk || slot < nvalid) && k < kdim) {
+        const bf16x8 hi = as_bf16x8(load16(p.h_hi + (int64_t)slot * p.h_stride + k));
+        const bf16x8 lo = as_bf16x8(load16(p.h_lo + (int64_t)slot * p.h_stride + k));
+        const float wt = s_w[slot];
+        bf16x8 oh, ol;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float v = wt * (static_cast<float>(hi[j]) + static_cast<float>(lo[j]));
+          __bf16 a, b;
+          split_bf16(v, a, b);
+          oh[j] = a;
+          ol[j] = b;
+        }
+        vh = __builtin_bit_cast(u32x4, oh);
+        vl = __builtin_bit_cast(u32x4, ol);
+      }
+      const size_t o = ((size_t)s * n_slots + slot) * kStageRow + q8 * 8;
+      *reinterpret_cast<u32x4*>(s_bh + o) = vh;
+      *reinterpret_cast<u32x4*>(s_bl + o) = vl;
     }
     __syncthreads();
+
+    // units u = s * A + a, dealt round-robin to the wavefronts
+    const int units = steps * A;
+    for (int u0 = wave; u0 < units; u0 += kSmallWaves * kSmallBatch) {
+      u32x4 q[kSmallBatch][Fmt<WT>::Q];
+      uint32_t su[kSmallBatch];
+      int ua[kSmallBatch], us[kSmallBatch];
+#pragma unroll
+      for (int b = 0; b < kSmallBatch; ++b) {
+        const int u = u0 + b * kSmallWaves;
+        ua[b] = -1;
+        if (u < units) {
+          const int s = u / A;
+          const int a = u - s * A;
+          const int e = s_act[a];
+          const int ks = ks0 + s;
+          if (e == p.n_experts) {  // shared: its own loop below
+            us[b] = s;
+            continue;
+          }
+          if (ks * 128 >= p.inter) continue;
+          ua[b] = a;
+          us[b] = s;
+          const int64_t cb = Fmt<WT>::row_bytes(p.inter);
+          const int64_t sb = Fmt<WT>::scale_row_bytes(p.inter);
+          const int64_t row = (int64_t)e * p.hidden + row0 + r16;
+          load_codes<WT>(p.down_c + row * cb, p.down_s + row * sb, ks, g, q[b], su[b]);
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < kSmallBatch; ++b) {
+        if (ua[b] < 0) continue;
+        bf16x8 a[4];
+        Fmt<WT>::decode(q[b], su[b], a);
+        const int slot = s_col[ua[b]][r16];
+        bf16x8 bh[4], bl[4];
+        if (slot >= 0) {
+          const size_t o = ((size_t)us[b] * n_slots + slot) * kStageRow + g * 32;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            bh[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(s_bh + o + 8 * j));
+            bl[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(s_bl + o + 8 * j));
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            bh[j] = as_bf16x8(u32x4{0, 0, 0, 0});
+            bl[j] = bh[j];
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc = mfma_bf16(a[j], bh[j], acc);
+          acc = mfma_bf16(a[j], bl[j], acc);
+        }
+      }
+    }
+    // the shared expert's units of this chunk
+    if (p.has_shared) {
+      const int a = A - 1;
+      for (int s = wave; s < steps; s += kSmallWaves) {
+        const int ks = ks0 + s;
+        if (ks * 128 >= p.shared_inter) continue;
+        const int64_t cb = Fmt<SWT>::row_bytes(p.shared_inter);
+        const int64_t sb = Fmt<SWT>::scale_row_bytes(p.shared_inter);
+        const int64_t row = row0 + r16;
+        u32x4 q[Fmt<SWT>::Q];
+        uint32_t su;
+        load_codes<SWT>(p.sdown_c + row * cb, p.sdown_s + row * sb, ks, g, q, su);
+        bf16x8 w4[4];
+        Fmt<SWT>::decode(q, su, w4);
+        const int slot = s_col[a][r16];
+        if (slot >= 0) {
+          const size_t o = ((size_t)s * n_slots + slot) * kStageRow + g * 32;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bf16x8 bh = as_bf16x8(*reinterpret_cast<const u32x4*>(s_bh + o + 8 * j));
+            const bf16x8 bl = as_bf16x8(*reinterpret_cast<const u32x4*>(s_bl + o + 8 * j));
+            acc = mfma_bf16(w4[j], bh, acc);
+            acc = mfma_bf16(w4[j], bl, acc);
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  if (wave > 0) s_red[wave - 1][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int w = 0; w < kSmallWaves - 1; ++w) acc += s_red[w][lane];
+    if (r16 < p.n_tokens)
+      *reinterpret_cast<f32x4*>(p.y + (int64_t)r16 * p.hidden + row0 + 4 * g) = acc;
   }
 }
 
@@ -507,18 +796,41 @@ int grid_for(int64_t items) {
   return (int)(items < kMaxGrid ? items : kMaxGrid);
 }
 
+// Kernels that ask for more than 64 KiB of dynamic LDS say so once.
+template <typename K>
+hipError_t allow_lds(K kernel) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget);
+}
+
+template <int NBT, bool XF32>
+hipError_t gate_up_launch(const FfnParams& p, dim3 grid, hipStream_t stream, hipEvent_t start,
+                          hipEvent_t stop) {
+  // a small tile's activation rows fit in LDS: stage them once per item
+  const int x_stride = p.hidden * (XF32 ? 4 : 2) + 16;
+  const int rows = p.n_tokens < 16 * NBT ? p.n_tokens : 16 * NBT;
+  const size_t lds = (size_t)rows * x_stride;
+  if (NBT == 1 && lds <= (size_t)kLdsBudget) {
+    static const hipError_t attr = allow_lds(gate_up_kernel<NBT, XF32, true>);
+    if (attr != hipSuccess) return attr;
+    hipExtLaunchKernelGGL(gate_up_kernel<NBT, XF32, true>, grid, dim3(kThreads), (uint32_t)lds,
+                          stream, start, stop, 0, p, x_stride);
+  } else {
+    hipExtLaunchKernelGGL(gate_up_kernel<NBT, XF32, false>, grid, dim3(kThreads), 0, stream,
+                          start, stop, 0, p, 0);
+  }
+  return hipGetLastError();
+}
+
 template <int NBT>
 hipError_t gate_up_nbt(const FfnParams& p, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   constexpr int TN = 16 * NBT;
   const int64_t shared_tiles = p.has_shared ? (p.n_tokens + TN - 1) / TN : 0;
   const int64_t items = routed_tiles_bound(p, TN) * (p.inter / 16) +
                         shared_tiles * (p.shared_inter / 16);
-  const dim3 grid(grid_for(items)), block(kThreads);
-  if (p.x_f32)
-    hipExtLaunchKernelGGL(gate_up_kernel<NBT, true>, grid, block, 0, stream, start, stop, 0, p);
-  else
-    hipExtLaunchKernelGGL(gate_up_kernel<NBT, false>, grid, block, 0, stream, start, stop, 0, p);
-  return hipGetLastError();
+  const dim3 grid(grid_for(items));
+  if (p.x_f32) return gate_up_launch<NBT, true>(p, grid, stream, start, stop);
+  return gate_up_launch<NBT, false>(p, grid, stream, start, stop);
 }
 
 template <int NBT>
@@ -527,7 +839,32 @@ hipError_t down_nbt(const FfnParams& p, hipStream_t stream, hipEvent_t start, hi
   const int64_t shared_tiles = p.has_shared ? (p.n_tokens + TN - 1) / TN : 0;
   const int64_t items = (routed_tiles_bound(p, TN) + shared_tiles) * (p.hidden / 16);
   hipExtLaunchKernelGGL(down_kernel<NBT>, dim3(grid_for(items)), dim3(kThreads), 0, stream,
-                        start, stop, 0, p);
+                        start, nullptr, 0, p);
+  const int64_t n = (int64_t)p.n_tokens * (p.hidden / 4);
+  hipExtLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                        nullptr, stop, 0, p);
+  return hipGetLastError();
+}
+
+// Slots of a small batch; 0 when the batch takes the per-slot path.
+int small_slots(const FfnParams& p) {
+  const int slots = p.n_tokens * p.top_k + (p.has_shared ? p.n_tokens : 0);
+  if (p.n_tokens > kSmallMaxTokens || slots > kSmallMaxSlots) return 0;
+  return slots;
+}
+
+template <int WT, int SWT>
+hipError_t down_small_launch(const FfnParams& p, int slots, hipStream_t stream, hipEvent_t start,
+                             hipEvent_t stop) {
+  const int nks = (p.inter > p.shared_inter ? p.inter : p.shared_inter) / 128;
+  const int per_step = slots * kStageRow * 2 * 2;  // hi + lo bf16
+  int spc = kLdsBudget / per_step;
+  spc = spc < 1 ? 1 : (spc > nks ? nks : spc);
+  static const hipError_t attr = allow_lds(down_combine_small_kernel<WT, SWT>);
+  if (attr != hipSuccess) return attr;
+  hipExtLaunchKernelGGL(down_combine_small_kernel<WT, SWT>, dim3(p.hidden / 16),
+                        dim3(kSmallThreads), (uint32_t)(spc * per_step), stream, start, stop, 0,
+                        p, spc);
   return hipGetLastError();
 }
 
@@ -545,6 +882,16 @@ hipError_t launch_ffn_gate_up(const FfnParams& p, hipStream_t stream, hipEvent_t
 
 hipError_t launch_ffn_down(const FfnParams& p, hipStream_t stream, hipEvent_t start,
                            hipEvent_t stop) {
+  const int slots = small_slots(p);
+  if (slots > 0) {
+    const bool r4 = p.w_type == MOE_W_MXFP4;
+    const bool s4 = !p.has_shared || p.sw_type == MOE_W_MXFP4;
+    if (r4 && s4) return down_small_launch<MOE_W_MXFP4, MOE_W_MXFP4>(p, slots, stream, start, stop);
+    if (r4) return down_small_launch<MOE_W_MXFP4, MOE_W_FP8E4M3_B128>(p, slots, stream, start, stop);
+    if (s4) return down_small_launch<MOE_W_FP8E4M3_B128, MOE_W_MXFP4>(p, slots, stream, start, stop);
+    return down_small_launch<MOE_W_FP8E4M3_B128, MOE_W_FP8E4M3_B128>(p, slots, stream, start,
+                                                                      stop);
+  }
   switch (pick_nbt(p.n_tokens)) {
     case 1: return down_nbt<1>(p, stream, start, stop);
     case 2: return down_nbt<2>(p, stream, start, stop);

@@ -109,11 +109,8 @@ moe_status plan_ffn(const moe_layer* layer, int n_tokens, FfnPlan* plan) {
   const size_t o_bytes = align_up((size_t)(plan->slots * layer->hidden) * 4u, 256);
   plan->off_h_hi = 0;
   plan->off_h_lo = h_bytes;
-  // nothing runs for an empty batch, so it needs no workspace
-  const size_t c_bytes = n == 0 ? 0 : align_up((size_t)(layer->hidden / 16) * 4u, 256);
   plan->off_obuf = 2 * h_bytes;
-  plan->off_count = 2 * h_bytes + o_bytes;
-  plan->total = 2 * h_bytes + o_bytes + c_bytes;
+  plan->total = 2 * h_bytes + o_bytes;
   return MOE_OK;
 }
 

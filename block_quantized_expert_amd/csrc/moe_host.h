@@ -13,8 +13,9 @@ namespace moe {
 // Byte layout of the moe_ffn workspace.
 //   h_hi, h_lo : bf16 [slots][h_stride]   SwiGLU output split into a bf16
 //                                         high part and a bf16 low part
-//   obuf       : fp32 [slots][hidden]     weighted expert outputs
-//   rb_count   : int32 [hidden/16]        finished work items per row block
+//   obuf       : fp32 [slots][hidden]     weighted expert outputs (used when
+//                                         the batch is too large for the
+//                                         single-pass down + combine)
 // A slot is one (token, routed expert) pair in grouped order
 // (p in [0, n_tokens*top_k)) or, for the shared expert, n_tokens*top_k + t.
 struct FfnPlan {
@@ -23,7 +24,6 @@ struct FfnPlan {
   size_t off_h_hi;
   size_t off_h_lo;
   size_t off_obuf;
-  size_t off_count;
   size_t total;
 };
 

@@ -31,9 +31,8 @@ struct FfnParams {
   __bf16* h_hi;  // [slots][h_stride]
   __bf16* h_lo;
   int64_t h_stride;
-  float* obuf;        // [slots][hidden] weighted per-slot outputs
-  int32_t* rb_count;  // [hidden/16] finished items per 16-row block
-  float* y;           // [n_tokens][hidden]
+  float* obuf;  // [slots][hidden] weighted per-slot outputs
+  float* y;     // [n_tokens][hidden]
 };
 
 hipError_t launch_route(const float* logits, int n_tokens, int n_experts, int top_k,

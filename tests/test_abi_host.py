@@ -69,8 +69,7 @@ def test_ffn_workspace_bytes():
     slots = n * 6 + n
     h = -(-slots * 2048 * 2 // 256) * 256
     o = -(-slots * 4096 * 4 // 256) * 256
-    c = 4096 // 16 * 4  # one int32 counter per 16-row block
-    assert B.lib().moe_ffn_workspace_bytes(ctypes.byref(L), n) == 2 * h + o + c
+    assert B.lib().moe_ffn_workspace_bytes(ctypes.byref(L), n) == 2 * h + o
     assert B.lib().moe_ffn_workspace_bytes(ctypes.byref(L), 0) == 0
     assert B.lib().moe_ffn_workspace_bytes(ctypes.byref(_layer(hidden=100)), 8) == 0
     assert B.lib().moe_ffn_workspace_bytes(None, 8) == 0

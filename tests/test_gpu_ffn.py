@@ -202,12 +202,12 @@ def test_timed_entry_point_matches_and_times():
     print("case timed", flush=True)
     layer, x, x_d, routing, routing_d = gpu_inputs(wl)
     y, ids, w, g = B.forward(layer, x_d, routing_d)
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    evs = [B.HipEvent() for _ in range(4)]
     y2 = B.moe_ffn_forward_timed(layer, x_d, w, g, evs)
     torch.cuda.synchronize()
     assert torch.equal(y, y2)
-    gu = evs[0].elapsed_time(evs[1])
-    dn = evs[2].elapsed_time(evs[3])
+    gu = evs[0].elapsed_ms(evs[1])
+    dn = evs[2].elapsed_ms(evs[3])
     assert 0 < gu < 100 and 0 < dn < 100, (gu, dn)  # milliseconds
     y3 = B.moe_ffn_forward_timed(layer, x_d, w, g, [None, None, None, None])
     torch.cuda.synchronize()
