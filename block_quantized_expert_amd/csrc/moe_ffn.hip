@@ -751,15 +751,16 @@ __global__ __launch_bounds__(kSmallThreads) void down_combine_small_kernel(FfnPa
         bf16x8 w4[4];
         Fmt<SWT>::decode(q, su, w4);
         const int slot = s_col[a][r16];
-        if (slot >= 0) {
-          const size_t o = ((size_t)s * n_slots + slot) * kStageRow + g * 32;
+        const size_t o = ((size_t)s * n_slots + (slot >= 0 ? slot : 0)) * kStageRow + g * 32;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const bf16x8 bh = as_bf16x8(*reinterpret_cast<const u32x4*>(s_bh + o + 8 * j));
-            const bf16x8 bl = as_bf16x8(*reinterpret_cast<const u32x4*>(s_bl + o + 8 * j));
-            acc = mfma_bf16(w4[j], bh, acc);
-            acc = mfma_bf16(w4[j], bl, acc);
-          }
+        for (int j = 0; j < 4; ++j) {
+          const u32x4 z = u32x4{0, 0, 0, 0};
+          const bf16x8 bh =
+              as_bf16x8(slot >= 0 ? *reinterpret_cast<const u32x4*>(s_bh + o + 8 * j) : z);
+          const bf16x8 bl =
+              as_bf16x8(slot >= 0 ? *reinterpret_cast<const u32x4*>(s_bl + o + 8 * j) : z);
+          acc = mfma_bf16(w4[j], bh, acc);
+          acc = mfma_bf16(w4[j], bl, acc);
         }
       }
     }
@@ -796,6 +797,18 @@ int grid_for(int64_t items) {
   return (int)(items < kMaxGrid ? items : kMaxGrid);
 }
 
+// hipExtLaunchKernel with its status returned; start/stop (may be null)
+// record the kernel's own start and end.
+template <typename... Params, typename... Args>
+hipError_t launch(void (*kernel)(Params...), dim3 grid, dim3 block, size_t lds,
+                  hipStream_t stream, hipEvent_t start, hipEvent_t stop, Args... args) {
+  static_assert(sizeof...(Params) == sizeof...(Args), "argument count");
+  void* argv[] = {const_cast<void*>(static_cast<const void*>(&args))...};
+  const hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block,
+                                          argv, lds, stream, start, stop, 0);
+  return e != hipSuccess ? e : hipGetLastError();
+}
+
 // Kernels that ask for more than 64 KiB of dynamic LDS say so once.
 template <typename K>
 hipError_t allow_lds(K kernel) {
@@ -813,13 +826,11 @@ hipError_t gate_up_launch(const FfnParams& p, dim3 grid, hipStream_t stream, hip
   if (NBT == 1 && lds <= (size_t)kLdsBudget) {
     static const hipError_t attr = allow_lds(gate_up_kernel<NBT, XF32, true>);
     if (attr != hipSuccess) return attr;
-    hipExtLaunchKernelGGL(gate_up_kernel<NBT, XF32, true>, grid, dim3(kThreads), (uint32_t)lds,
-                          stream, start, stop, 0, p, x_stride);
-  } else {
-    hipExtLaunchKernelGGL(gate_up_kernel<NBT, XF32, false>, grid, dim3(kThreads), 0, stream,
-                          start, stop, 0, p, 0);
+    return launch(gate_up_kernel<NBT, XF32, true>, grid, dim3(kThreads), lds, stream, start, stop,
+                  p, x_stride);
   }
-  return hipGetLastError();
+  return launch(gate_up_kernel<NBT, XF32, false>, grid, dim3(kThreads), 0, stream, start, stop,
+                p, 0);
 }
 
 template <int NBT>
@@ -838,12 +849,12 @@ hipError_t down_nbt(const FfnParams& p, hipStream_t stream, hipEvent_t start, hi
   constexpr int TN = 16 * NBT;
   const int64_t shared_tiles = p.has_shared ? (p.n_tokens + TN - 1) / TN : 0;
   const int64_t items = (routed_tiles_bound(p, TN) + shared_tiles) * (p.hidden / 16);
-  hipExtLaunchKernelGGL(down_kernel<NBT>, dim3(grid_for(items)), dim3(kThreads), 0, stream,
-                        start, nullptr, 0, p);
+  hipError_t e = launch(down_kernel<NBT>, dim3(grid_for(items)), dim3(kThreads), 0, stream, start,
+                        nullptr, p);
+  if (e != hipSuccess) return e;
   const int64_t n = (int64_t)p.n_tokens * (p.hidden / 4);
-  hipExtLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
-                        nullptr, stop, 0, p);
-  return hipGetLastError();
+  return launch(combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, nullptr,
+                stop, p);
 }
 
 // Slots of a small batch; 0 when the batch takes the per-slot path.
@@ -862,10 +873,8 @@ hipError_t down_small_launch(const FfnParams& p, int slots, hipStream_t stream, 
   spc = spc < 1 ? 1 : (spc > nks ? nks : spc);
   static const hipError_t attr = allow_lds(down_combine_small_kernel<WT, SWT>);
   if (attr != hipSuccess) return attr;
-  hipExtLaunchKernelGGL(down_combine_small_kernel<WT, SWT>, dim3(p.hidden / 16),
-                        dim3(kSmallThreads), (uint32_t)(spc * per_step), stream, start, stop, 0,
-                        p, spc);
-  return hipGetLastError();
+  return launch(down_combine_small_kernel<WT, SWT>, dim3(p.hidden / 16), dim3(kSmallThreads),
+                (size_t)spc * per_step, stream, start, stop, p, spc);
 }
 
 }  // namespace
