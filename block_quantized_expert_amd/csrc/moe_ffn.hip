@@ -48,6 +48,14 @@ constexpr int kMaxSeg = MOE_MAX_EXPERTS + 1;
 constexpr int kMaxGrid = 256 * 8;  // 256 CUs, up to 8 resident workgroups each
 constexpr int kLdsBudget = 140 * 1024;  // dynamic LDS a kernel may ask for
 
+// ------------------------------------------------------------ uniformity
+
+// Values that are the same on every lane of a wavefront, moved to scalar
+// registers so that branches on them are scalar branches: a batch of loads
+// then sits in one basic block with no wait between its requests.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int wave_id() { return uniform(threadIdx.x >> 6); }
+
 // ------------------------------------------------------------ work items
 
 struct Item {
@@ -113,10 +121,10 @@ __device__ __forceinline__ Item find_item(const FfnParams& p, const int* s_pref,
   const int m_all = shared ? p.n_tokens : p.counts[lo];
   const int start = shared ? p.n_tokens * p.top_k : p.offsets[lo];
   Item it;
-  it.seg = lo;
-  it.slot0 = start + tile * tn;
-  it.m = min(tn, m_all - tile * tn);
-  it.row0 = rb * 16;
+  it.seg = uniform(lo);
+  it.slot0 = uniform(start + tile * tn);
+  it.m = uniform(min(tn, m_all - tile * tn));
+  it.row0 = uniform(rb * 16);
   return it;
 }
 
@@ -260,21 +268,24 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const Item& it,
   const uint8_t* ucr = (shared ? p.sup_c : p.up_c) + row * cb;
   const uint8_t* usr = (shared ? p.sup_s : p.up_s) + row * sb;
   const int64_t shared_base = (int64_t)p.n_tokens * p.top_k;
-  const int S = wave_steps(p.hidden / 128, wave);
+  const int S = uniform(wave_steps(p.hidden / 128, wave));
   const int nbt = (it.m + 15) >> 4;
 
-  // chunk 0's codes are requested before the activations are staged
+  // chunk 0's codes are requested before the activations are staged; a
+  // chunk's loads are unconditional (steps past the end repeat the last
+  // one) so they leave in one burst
   u32x4 qg[CH][F::Q], qu[CH][F::Q];
   uint32_t sg[CH], su[CH];
-  const int rem0 = min(CH, S);
+  auto load_chunk = [&](int j0) {
+    const int last = S - 1;
 #pragma unroll
-  for (int i = 0; i < CH; ++i) {
-    if (i < rem0) {
-      const int ks = wave + kWaves * i;
+    for (int i = 0; i < CH; ++i) {
+      const int ks = wave + kWaves * min(j0 + i, last);
       load_codes<WT>(gcr, gsr, ks, g, qg[i], sg[i]);
       load_codes<WT>(ucr, usr, ks, g, qu[i], su[i]);
     }
-  }
+  };
+  if (S > 0) load_chunk(0);
 
   // token columns: a global activation row, or a byte offset into the LDS
   // copy of the tile (-1 for an empty column)
@@ -314,16 +325,7 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const Item& it,
 
   for (int j0 = 0; j0 < S; j0 += CH) {
     const int rem = min(CH, S - j0);
-    if (j0 > 0) {
-#pragma unroll
-      for (int i = 0; i < CH; ++i) {
-        if (i < rem) {
-          const int ks = wave + kWaves * (j0 + i);
-          load_codes<WT>(gcr, gsr, ks, g, qg[i], sg[i]);
-          load_codes<WT>(ucr, usr, ks, g, qu[i], su[i]);
-        }
-      }
-    }
+    if (j0 > 0) load_chunk(j0);
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       if (i < rem) {
@@ -373,7 +375,7 @@ __global__ __launch_bounds__(kThreads) void gate_up_kernel(FfnParams p, int x_st
   __shared__ int s_pref[kMaxSeg + 1];
   __shared__ int s_tmp[kWaves];
   __shared__ f32x4 s_red[kWaves - 1][2 * NBT][kWave];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int g = lane >> 4, r16 = lane & 15;
 
   const int total = build_item_prefix(p, TN, false, s_pref, s_tmp);
@@ -435,6 +437,166 @@ __global__ __launch_bounds__(kThreads) void gate_up_kernel(FfnParams p, int x_st
   }
 }
 
+// ------------------------------------------------------- gate/up, decode
+
+constexpr int kDecodeMaxTokens = 16;  // one MFMA column block
+constexpr int kMaxChunks = MOE_MAX_EXPERTS / kWave;
+
+// Index of the a-th routed expert that has a token, or -1.  Every
+// wavefront works it out on its own (no barrier); the count loads are
+// issued before any of them is used.
+__device__ __forceinline__ int nth_active_expert(const FfnParams& p, int a, int lane) {
+  const int nch = (p.n_experts + kWave - 1) / kWave;
+  int cnt[kMaxChunks];
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) {
+    const int x = c * kWave + lane;
+    cnt[c] = (c < nch && x < p.n_experts) ? p.counts[x] : 0;
+  }
+  int seen = 0, e = -1;
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) {
+    const uint64_t on = __ballot(cnt[c] > 0);
+    const int pc = __popcll(on);
+    if (e < 0 && a < seen + pc) {
+      const uint64_t below = (1ull << lane) - 1ull;
+      const bool me = cnt[c] > 0 && __popcll(on & below) == a - seen;
+      e = c * kWave + __builtin_ctzll(__ballot(me));
+    }
+    seen += pc;
+  }
+  return uniform(e);
+}
+
+// Gate/up for a decode batch (at most 16 tokens, bf16 activations, MXFP4
+// gate and up, hidden = 512*S).  Block b < a_bound*inter/16 is row block
+// b % (inter/16) of the (b / (inter/16))-th routed expert that has tokens
+// (blocks past the last such expert leave at once); the rest are the shared
+// expert's row blocks.  Wavefront w owns reduction steps w*S .. w*S+S-1, so
+// its 2*S code vectors and its scale bytes (4*S contiguous bytes of each
+// row) leave as one burst, and it stages only its own quarter of the
+// activations in LDS.  The four partial sums meet in LDS for the SwiGLU.
+template <int S>
+__global__ __launch_bounds__(kThreads) void gate_up_decode_kernel(FfnParams p, int a_bound,
+                                                                  int m_max) {
+  constexpr int kRow = S * 128 + 8;  // bf16 per staged token row (+8: other banks)
+  extern __shared__ __align__(16) char s_dyn[];
+  __shared__ f32x4 s_red[kWaves - 1][2][kWave];
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int g = lane >> 4, r16 = lane & 15;
+  const int rb_r = p.inter >> 4;
+  const int routed_blocks = a_bound * rb_r;
+  const int blk = blockIdx.x;
+  int e, rb;
+  if (blk < routed_blocks) {
+    const int a = blk / rb_r;
+    rb = blk - a * rb_r;
+    e = nth_active_expert(p, a, lane);
+    if (e < 0) return;  // the same on every wavefront: the block leaves whole
+  } else {
+    e = p.n_experts;
+    rb = blk - routed_blocks;
+  }
+  const bool shared = e == p.n_experts;
+  const int rows = shared ? p.shared_inter : p.inter;
+  const int64_t cb = p.hidden / 2, sb = p.hidden / 32;
+  const int64_t row = (shared ? 0 : (int64_t)e * rows) + rb * 16 + r16;
+  const uint8_t* gc = (shared ? p.sgate_c : p.gate_c) + row * cb + wave * S * 64 + g * 16;
+  const uint8_t* uc = (shared ? p.sup_c : p.up_c) + row * cb + wave * S * 64 + g * 16;
+  const uint8_t* gs = (shared ? p.sgate_s : p.gate_s) + row * sb + wave * S * 4;
+  const uint8_t* us = (shared ? p.sup_s : p.up_s) + row * sb + wave * S * 4;
+
+  // one burst: codes, then the 4*S scale bytes of each row as whole words
+  u32x4 qg[S], qu[S];
+#pragma unroll
+  for (int j = 0; j < S; ++j) {
+    qg[j] = load16(gc + j * 64);
+    qu[j] = load16(uc + j * 64);
+  }
+  uint32_t wg[S], wu[S];
+  if constexpr (S >= 4) {
+#pragma unroll
+    for (int v = 0; v < S / 4; ++v) {
+      const u32x4 a4 = load16(gs + 16 * v), b4 = load16(us + 16 * v);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        wg[4 * v + i] = a4[i];
+        wu[4 * v + i] = b4[i];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+      wg[j] = reinterpret_cast<const uint32_t*>(gs)[j];
+      wu[j] = reinterpret_cast<const uint32_t*>(us)[j];
+    }
+  }
+
+  // tokens of the tile and this wavefront's quarter of their activations;
+  // distinct ids per token keep m <= N (<= m_max), the clamp keeps repeated
+  // ids (outside the ABI's preconditions) inside the staged rows
+  const int m = uniform(min(shared ? p.n_tokens : p.counts[e], m_max));
+  const int slot0 = uniform(shared ? p.n_tokens * p.top_k : p.offsets[e]);
+  __bf16* s_xq = reinterpret_cast<__bf16*>(s_dyn) + (size_t)wave * m_max * kRow;
+  for (int c = lane; c < m * 16 * S; c += kWave) {
+    const int n = c / (16 * S);
+    const int off = c - n * 16 * S;  // 16-byte chunk inside the quarter
+    const int64_t tok = shared ? n : p.perm[slot0 + n] / p.top_k;
+    *reinterpret_cast<u32x4*>(s_xq + n * kRow + off * 8) =
+        load16(static_cast<const __bf16*>(p.x) + tok * p.hidden + wave * S * 128 + off * 8);
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wavefront's LDS rows are written
+  __builtin_amdgcn_wave_barrier();
+
+  f32x4 ag = f32x4{0, 0, 0, 0}, au = f32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int j = 0; j < S; ++j) {
+    bf16x8 b[4];
+    if (r16 < m) {
+      const __bf16* src = s_xq + r16 * kRow + j * 128 + g * 32;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) b[t] = as_bf16x8(*reinterpret_cast<const u32x4*>(src + 8 * t));
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) b[t] = as_bf16x8(u32x4{0, 0, 0, 0});
+    }
+    const float sgv = ue8m0_to_f32((wg[j] >> (8 * g)) & 0xFF);
+    const float suv = ue8m0_to_f32((wu[j] >> (8 * g)) & 0xFF);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) ag = mfma_bf16(fp4x8_to_bf16(qg[j][t], sgv), b[t], ag);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) au = mfma_bf16(fp4x8_to_bf16(qu[j][t], suv), b[t], au);
+  }
+
+  if (wave > 0) {
+    s_red[wave - 1][0][lane] = ag;
+    s_red[wave - 1][1][lane] = au;
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int w = 0; w < kWaves - 1; ++w) {
+      ag += s_red[w][0][lane];
+      au += s_red[w][1][lane];
+    }
+    if (r16 < m) {
+      bf16x4 hi, lo;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float gv = ag[r];
+        const float h = gv / (1.0f + expf(-gv)) * au[r];
+        __bf16 a, b;
+        split_bf16(h, a, b);
+        hi[r] = a;
+        lo[r] = b;
+      }
+      const int64_t o = (int64_t)(slot0 + r16) * p.h_stride + rb * 16 + 4 * g;
+      *reinterpret_cast<bf16x4*>(p.h_hi + o) = hi;
+      *reinterpret_cast<bf16x4*>(p.h_lo + o) = lo;
+    }
+  }
+}
+
 // ------------------------------------------------------- down (per slot)
 
 template <int NBT, int WT>
@@ -463,15 +625,15 @@ __device__ __forceinline__ void down_item(const FfnParams& p, const Item& it, bo
     }
   }
   const int nbt = (it.m + 15) >> 4;
-  const int S = wave_steps(kdim / 128, wave);
+  const int S = uniform(wave_steps(kdim / 128, wave));
 
   for (int j0 = 0; j0 < S; j0 += CH) {
     const int rem = min(CH, S - j0);
     u32x4 q[CH][F::Q];
     uint32_t su[CH];
 #pragma unroll
-    for (int i = 0; i < CH; ++i)
-      if (i < rem) load_codes<WT>(dcr, dsr, wave + kWaves * (j0 + i), g, q[i], su[i]);
+    for (int i = 0; i < CH; ++i)  // unconditional: one burst of requests
+      load_codes<WT>(dcr, dsr, wave + kWaves * min(j0 + i, S - 1), g, q[i], su[i]);
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       if (i < rem) {
@@ -501,7 +663,7 @@ __global__ __launch_bounds__(kThreads) void down_kernel(FfnParams p) {
   __shared__ int s_pref[kMaxSeg + 1];
   __shared__ int s_tmp[kWaves];
   __shared__ f32x4 s_red[kWaves - 1][NBT][kWave];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int g = lane >> 4, r16 = lane & 15;
   const int total = build_item_prefix(p, TN, true, s_pref, s_tmp);
 
@@ -568,7 +730,6 @@ constexpr int kSmallMaxTokens = 16;  // one MFMA column per token
 constexpr int kSmallMaxSlots = 128;
 constexpr int kSmallMaxActive = kSmallMaxSlots + 1;
 constexpr int kStageRow = 136;  // bf16 per staged row: 128 + 8 so rows start on other banks
-constexpr int kSmallBatch = 8;  // units whose codes a wavefront requests together
 
 // One workgroup per 16 output rows.  Units (active expert a, step s of the
 // current chunk) are dealt to the eight wavefronts; a unit decodes the 16
@@ -586,7 +747,7 @@ __global__ __launch_bounds__(kSmallThreads) void down_combine_small_kernel(FfnPa
   __shared__ int s_nact, s_nroute;
   __shared__ f32x4 s_red[kSmallWaves - 1][kWave];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int g = lane >> 4, r16 = lane & 15;
   const int row0 = blockIdx.x * 16;
   const int nk = p.n_tokens * p.top_k;
@@ -646,8 +807,59 @@ __global__ __launch_bounds__(kSmallThreads) void down_combine_small_kernel(FfnPa
   const int nks = max(p.inter, p.has_shared ? p.shared_inter : 0) / 128;
   f32x4 acc = f32x4{0, 0, 0, 0};
 
+  // units u = s * A + a of a chunk are dealt round-robin to the wavefronts,
+  // kSmallBatch at a time: the codes of a whole batch are requested before
+  // any of them is decoded
+  constexpr int kSmallBatch = 2 * Fmt<WT>::CH;  // 16 MXFP4 or 8 fp8 units
+  u32x4 q[kSmallBatch][Fmt<WT>::Q];
+  uint32_t su[kSmallBatch];
+  int ua[kSmallBatch], us[kSmallBatch];
+  // a unit that does not exist (past the end, the shared expert, a step
+  // beyond a routed expert's width) loads routed expert 0's first step, which
+  // always exists, and is skipped by compute_batch; the loads of a batch stay
+  // one burst
+  auto load_batch = [&](int ks0, int units, int u0) {
+    const int64_t cb = Fmt<WT>::row_bytes(p.inter);
+    const int64_t sb = Fmt<WT>::scale_row_bytes(p.inter);
+#pragma unroll
+    for (int b = 0; b < kSmallBatch; ++b) {
+      const int u = u0 + b * kSmallWaves;
+      const int s = u / A;
+      const int a = u - s * A;
+      const int e = uniform(s_act[u < units ? a : 0]);
+      const int ks = ks0 + s;
+      const bool real = u < units && e != p.n_experts && ks * 128 < p.inter;
+      ua[b] = real ? a : -1;
+      us[b] = s;
+      const int64_t row = (int64_t)(real ? e : 0) * p.hidden + row0 + r16;
+      load_codes<WT>(p.down_c + row * cb, p.down_s + row * sb, real ? ks : 0, g, q[b], su[b]);
+    }
+  };
+  auto compute_batch = [&]() {
+#pragma unroll
+    for (int b = 0; b < kSmallBatch; ++b) {
+      if (ua[b] < 0) continue;  // uniform over the wavefront
+      bf16x8 a[4];
+      Fmt<WT>::decode(q[b], su[b], a);
+      const int slot = s_col[ua[b]][r16];
+      const size_t o = ((size_t)us[b] * n_slots + (slot >= 0 ? slot : 0)) * kStageRow + g * 32;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 z = u32x4{0, 0, 0, 0};
+        const bf16x8 bh =
+            as_bf16x8(slot >= 0 ? *reinterpret_cast<const u32x4*>(s_bh + o + 8 * j) : z);
+        const bf16x8 bl =
+            as_bf16x8(slot >= 0 ? *reinterpret_cast<const u32x4*>(s_bl + o + 8 * j) : z);
+        acc = mfma_bf16(a[j], bh, acc);
+        acc = mfma_bf16(a[j], bl, acc);
+      }
+    }
+  };
+
   for (int ks0 = 0; ks0 < nks; ks0 += spc) {
     const int steps = min(spc, nks - ks0);
+    const int units = steps * A;
+    load_batch(ks0, units, wave);  // in flight while h is staged
     // stage w * (h_hi + h_lo) for every slot, split again into hi + lo
     const int groups = steps * n_slots * 16;
     for (int i = tid; i < groups; i += kSmallThreads) {
@@ -679,62 +891,11 @@ __global__ __launch_bounds__(kSmallThreads) void down_combine_small_kernel(FfnPa
       *reinterpret_cast<u32x4*>(s_bl + o) = vl;
     }
     __syncthreads();
-
-    // units u = s * A + a, dealt round-robin to the wavefronts
-    const int units = steps * A;
-    for (int u0 = wave; u0 < units; u0 += kSmallWaves * kSmallBatch) {
-      u32x4 q[kSmallBatch][Fmt<WT>::Q];
-      uint32_t su[kSmallBatch];
-      int ua[kSmallBatch], us[kSmallBatch];
-#pragma unroll
-      for (int b = 0; b < kSmallBatch; ++b) {
-        const int u = u0 + b * kSmallWaves;
-        ua[b] = -1;
-        if (u < units) {
-          const int s = u / A;
-          const int a = u - s * A;
-          const int e = s_act[a];
-          const int ks = ks0 + s;
-          if (e == p.n_experts) {  // shared: its own loop below
-            us[b] = s;
-            continue;
-          }
-          if (ks * 128 >= p.inter) continue;
-          ua[b] = a;
-          us[b] = s;
-          const int64_t cb = Fmt<WT>::row_bytes(p.inter);
-          const int64_t sb = Fmt<WT>::scale_row_bytes(p.inter);
-          const int64_t row = (int64_t)e * p.hidden + row0 + r16;
-          load_codes<WT>(p.down_c + row * cb, p.down_s + row * sb, ks, g, q[b], su[b]);
-        }
-      }
-#pragma unroll
-      for (int b = 0; b < kSmallBatch; ++b) {
-        if (ua[b] < 0) continue;
-        bf16x8 a[4];
-        Fmt<WT>::decode(q[b], su[b], a);
-        const int slot = s_col[ua[b]][r16];
-        bf16x8 bh[4], bl[4];
-        if (slot >= 0) {
-          const size_t o = ((size_t)us[b] * n_slots + slot) * kStageRow + g * 32;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            bh[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(s_bh + o + 8 * j));
-            bl[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(s_bl + o + 8 * j));
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            bh[j] = as_bf16x8(u32x4{0, 0, 0, 0});
-            bl[j] = bh[j];
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc = mfma_bf16(a[j], bh[j], acc);
-          acc = mfma_bf16(a[j], bl[j], acc);
-        }
-      }
+    compute_batch();
+    for (int u0 = wave + kSmallWaves * kSmallBatch; u0 < units;
+         u0 += kSmallWaves * kSmallBatch) {
+      load_batch(ks0, units, u0);
+      compute_batch();
     }
     // the shared expert's units of this chunk
     if (p.has_shared) {
@@ -877,10 +1038,42 @@ hipError_t down_small_launch(const FfnParams& p, int slots, hipStream_t stream, 
                 (size_t)spc * per_step, stream, start, stop, p, spc);
 }
 
+template <int S>
+hipError_t gate_up_decode_launch(const FfnParams& p, hipStream_t stream, hipEvent_t start,
+                                 hipEvent_t stop) {
+  const int64_t nk = (int64_t)p.n_tokens * p.top_k;
+  const int a_bound = (int)(nk < p.n_experts ? nk : p.n_experts);
+  const int blocks = a_bound * (p.inter / 16) + (p.has_shared ? p.shared_inter / 16 : 0);
+  // every tile holds at most min(N, 16) tokens
+  const int m_max = p.n_tokens < kDecodeMaxTokens ? p.n_tokens : kDecodeMaxTokens;
+  const size_t lds = (size_t)kWaves * m_max * (S * 128 + 8) * 2;
+  static const hipError_t attr = allow_lds(gate_up_decode_kernel<S>);
+  if (attr != hipSuccess) return attr;
+  return launch(gate_up_decode_kernel<S>, dim3(blocks), dim3(kThreads), lds, stream, start, stop,
+                p, a_bound, m_max);
+}
+
+// The decode kernel covers small batches of bf16 activations with MXFP4
+// gate/up matrices and hidden = 512, 1024, 2048 or 4096; 0 when it does not.
+int decode_steps(const FfnParams& p) {
+  if (p.n_tokens > kDecodeMaxTokens || p.x_f32 || p.w_type != MOE_W_MXFP4) return 0;
+  if (p.has_shared && p.sw_type != MOE_W_MXFP4) return 0;
+  const int s = p.hidden / 512;
+  if (p.hidden % 512 != 0 || (s != 1 && s != 2 && s != 4 && s != 8)) return 0;
+  return s;
+}
+
 }  // namespace
 
 hipError_t launch_ffn_gate_up(const FfnParams& p, hipStream_t stream, hipEvent_t start,
                               hipEvent_t stop) {
+  switch (decode_steps(p)) {
+    case 1: return gate_up_decode_launch<1>(p, stream, start, stop);
+    case 2: return gate_up_decode_launch<2>(p, stream, start, stop);
+    case 4: return gate_up_decode_launch<4>(p, stream, start, stop);
+    case 8: return gate_up_decode_launch<8>(p, stream, start, stop);
+    default: break;
+  }
   switch (pick_nbt(p.n_tokens)) {
     case 1: return gate_up_nbt<1>(p, stream, start, stop);
     case 2: return gate_up_nbt<2>(p, stream, start, stop);

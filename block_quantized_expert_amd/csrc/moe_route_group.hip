@@ -287,6 +287,74 @@ __global__ __launch_bounds__(kGroupThreads) void route_group_kernel(
   group_block(s_ids, n_tokens * top_k, n_experts, counts, offsets, perm, inv_perm, dev_error, sh);
 }
 
+// Route and group a batch of at most 64 flat entries with one wavefront:
+// lane f holds entry f, so the histogram, the scan over experts and the
+// stable ranks need no workgroup barrier.
+template <int PER>
+__global__ __launch_bounds__(kWave) void route_group_wave_kernel(
+    const float* __restrict__ logits, int n_tokens, int n_experts, int top_k, float routed_scale,
+    int32_t* __restrict__ ids, float* __restrict__ w, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm) {
+  __shared__ int s_count[MOE_MAX_EXPERTS];
+  __shared__ int s_ids[kWave];
+  const int lane = threadIdx.x;
+  for (int e = lane; e < n_experts; e += kWave) s_count[e] = 0;
+  for (int t = 0; t < n_tokens; ++t) {
+    int id;
+    float wt;
+    route_token<PER>(logits + (size_t)t * n_experts, n_experts, top_k, routed_scale, lane, id,
+                     wt);
+    if (lane < top_k) {
+      ids[t * top_k + lane] = id;
+      w[t * top_k + lane] = wt;
+      s_ids[t * top_k + lane] = id;
+    }
+  }
+  __syncthreads();
+  const int nk = n_tokens * top_k;
+  const int e = lane < nk ? s_ids[lane] : -1;
+  if (e >= 0) atomicAdd(&s_count[e], 1);
+  __syncthreads();
+  // exclusive scan of the counts, PER experts per lane
+  int local = 0;
+  for (int j = 0; j < PER; ++j) {
+    const int x = lane * PER + j;
+    local += x < n_experts ? s_count[x] : 0;
+  }
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int t = __shfl_up(incl, off);
+    if (lane >= off) incl += t;
+  }
+  int run = incl - local;
+  for (int j = 0; j < PER; ++j) {
+    const int x = lane * PER + j;
+    if (x < n_experts) {
+      const int c = s_count[x];
+      counts[x] = c;
+      offsets[x] = run;
+      s_count[x] = run;  // now the first slot of the expert
+      run += c;
+    }
+  }
+  if (lane == kWave - 1) offsets[n_experts] = incl;
+  __syncthreads();
+  // stable rank: earlier lanes holding the same expert
+  const bool valid = e >= 0;
+  uint64_t same = __ballot(valid);
+  for (int b = 0; (1 << b) < n_experts; ++b) {
+    const bool bit = valid && ((e >> b) & 1);
+    const uint64_t m = __ballot(bit);
+    same &= bit ? m : ~m;
+  }
+  if (valid) {
+    const int p = s_count[e] + __popcll(same & lanemask_lt(lane));
+    perm[p] = lane;
+    inv_perm[lane] = p;
+  }
+}
+
 int per_lane(int n_experts) { return (n_experts + kWave - 1) / kWave; }
 
 }  // namespace
@@ -341,6 +409,24 @@ hipError_t launch_route_group(const float* logits, int n_tokens, int n_experts, 
                         dev_error, stream);
   }
   const int per = per_lane(n_experts);
+  if ((int64_t)n_tokens * top_k <= kWave) {
+#define MOE_RGW(P)                                                                           \
+  route_group_wave_kernel<P><<<1, kWave, 0, stream>>>(logits, n_tokens, n_experts, top_k,    \
+                                                      routed_scale, ids, w, counts, offsets, \
+                                                      perm, inv_perm)
+    if (per <= 1)
+      MOE_RGW(1);
+    else if (per <= 2)
+      MOE_RGW(2);
+    else if (per <= 4)
+      MOE_RGW(4);
+    else if (per <= 8)
+      MOE_RGW(8);
+    else
+      MOE_RGW(16);
+#undef MOE_RGW
+    return hipGetLastError();
+  }
 #define MOE_RG(P)                                                                          \
   route_group_kernel<P><<<1, kGroupThreads, 0, stream>>>(logits, n_tokens, n_experts,      \
                                                          top_k, routed_scale, ids, w, counts, \

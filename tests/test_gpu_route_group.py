@@ -170,11 +170,12 @@ def test_route_and_group_deterministic():
         assert torch.equal(x, y)
 
 
-@pytest.mark.parametrize("name,n_tokens", [("tiny", None), ("decode1", None), ("decode32", None),
+@pytest.mark.parametrize("name,n_tokens", [("tiny", None), ("tiny", 32), ("tiny", 33),
+                                           ("decode1", None), ("decode32", None),
                                            ("prefill512", None), ("prefill512", 1000)])
 def test_route_group_fused_equals_oracle(name, n_tokens):
-    # n_tokens*top_k <= 4096 runs as one launch; 1000 tokens x 6 takes the
-    # two-kernel path
+    # up to 64 flat entries: one wavefront; up to 4096: one workgroup;
+    # 1000 tokens x 6 takes the two-kernel path
     wl = I.WORKLOADS[name]
     print("case route_group", name, n_tokens, flush=True)
     lg = I.router_logits(wl, n_tokens=n_tokens)
