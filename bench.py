@@ -14,7 +14,11 @@ pool, so no expert is served from the 256 MB last-level cache or the L2s.
 Prints ONE JSON line.  `value` is tokens/s over the K timed steps
 (wall clock, synchronised on both sides).  `roofline` is for the dominant
 kernel (gate/up): algorithmic bytes per launch over its average duration
-measured with HIP events on the launch stream inside the timed region.
+measured with HIP events on the launch stream inside the timed region.  The
+kernels record those events from their own dispatch packets; recording them
+costs the host several microseconds per step, so at decode sizes (where the
+host would otherwise fall behind the GPU) only every --event-every-th timed
+step carries them.
 `cpu_baseline` times the fp64 oracle on a bounded sample of the same
 workload on the host cores.
 """
@@ -36,12 +40,12 @@ METRIC = "MoE-FFN tokens/s + % HBM peak (decode) / % MFMA peak (prefill), 1 GPU"
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
 
-DEFAULTS = {  # workload: (steps, warmup, copies, pool)
-    "decode1": (2000, 100, 8, 64),
-    "decode32": (400, 20, 8, 16),
-    "prefill512": (50, 5, 8, 4),
-    "hash4096": (20, 3, 2, 2),
-    "tiny": (2000, 100, 1, 8),
+DEFAULTS = {  # workload: (steps, warmup, copies, pool, event_every)
+    "decode1": (2000, 100, 8, 64, 8),
+    "decode32": (400, 20, 8, 16, 1),
+    "prefill512": (50, 5, 8, 4, 1),
+    "hash4096": (20, 3, 2, 2, 1),
+    "tiny": (2000, 100, 1, 8, 8),
 }
 
 # Traffic of the gate/up kernel on decode1 measured with rocprofv3 --pmc
@@ -247,6 +251,8 @@ def main():
     ap.add_argument("--workload", default="decode1")
     ap.add_argument("--copies", type=int, default=None)
     ap.add_argument("--pool", type=int, default=None)
+    ap.add_argument("--event-every", type=int, default=None,
+                    help="record the per-kernel events on every n-th timed step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()
@@ -269,11 +275,12 @@ def main():
     from block_quantized_expert_amd import inputs as I
 
     wl = I.WORKLOADS[args.workload]
-    d_steps, d_warm, d_copies, d_pool = DEFAULTS[wl.name]
+    d_steps, d_warm, d_copies, d_pool, d_every = DEFAULTS[wl.name]
     steps = args.steps if args.steps is not None else d_steps
     warmup = args.warmup if args.warmup is not None else d_warm
     copies = args.copies if args.copies is not None else d_copies
     n_pool = args.pool if args.pool is not None else d_pool
+    every = max(1, args.event_every if args.event_every is not None else d_every)
 
     dev = torch.device("cuda:0")
     t0 = time.perf_counter()
@@ -288,8 +295,11 @@ def main():
         runner.step(s)
     torch.cuda.synchronize()
 
-    evs = [tuple(B.HipEvent() for _ in range(4)) for _ in range(steps)]
-    ev_handles = [tuple(e.handle for e in four) for four in evs]
+    sampled = list(range(0, steps, every))
+    evs = [tuple(B.HipEvent() for _ in range(4)) for _ in sampled]
+    ev_handles = [None] * steps
+    for i, j in enumerate(sampled):
+        ev_handles[j] = tuple(e.handle for e in evs[i])
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for j in range(steps):
@@ -342,6 +352,7 @@ def main():
             "traffic": traffic,
             "bytes_per_launch": costs["gate_up_bytes"],
             "avg_launch_us": gu_avg_s * 1e6,
+            "timed_launches": len(sampled),
         },
         "down_kernel": {
             "bytes_per_launch": costs["down_bytes"],

@@ -736,9 +736,17 @@ constexpr int kStageRow = 136;  // bf16 per staged row: 128 + 8 so rows start on
 // rows x 128 reduction indices of expert a's down matrix and multiplies
 // them with the staged w*h of every token (column n = token n, zero where
 // the token did not pick the expert).
+//
+// Latency order: the routing inputs arrive in one round trip (the slot and
+// weight of every flat entry through inv_perm and topk_w, the counts and
+// first slots of every expert); then the chunk's first h values and all of
+// a wavefront's weight codes leave as one burst, so the h staging overlaps
+// the weight transfer; the B fragments of unit b+1 are read from LDS while
+// unit b multiplies.
 template <int WT, int SWT>
 __global__ __launch_bounds__(kSmallThreads) void down_combine_small_kernel(FfnParams p,
                                                                             int spc) {
+  constexpr bool kMerged = WT == SWT;  // the shared expert's units join the bursts
   extern __shared__ __align__(16) char smem[];
   __shared__ int s_act[kSmallMaxActive];   // expert id (n_experts: shared)
   __shared__ int s_off[kSmallMaxActive];   // first slot of the active expert
@@ -750,20 +758,35 @@ __global__ __launch_bounds__(kSmallThreads) void down_combine_small_kernel(FfnPa
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int g = lane >> 4, r16 = lane & 15;
   const int row0 = blockIdx.x * 16;
-  const int nk = p.n_tokens * p.top_k;
+  const int nk = p.n_tokens * p.top_k;  // >= 1 on this path
   const int n_slots = nk + (p.has_shared ? p.n_tokens : 0);
 
-  // active experts, compacted in expert order, then the shared expert
+  // routing inputs in one round trip
+  const int fi = min(tid, nk - 1);
+  const int my_slot = p.inv_perm[fi];
+  const float my_w = p.topk_w[fi];
   if (wave == 0) {
+    const int nch = uniform((p.n_experts + kWave - 1) / kWave);
+    int cnt[kMaxChunks], off[kMaxChunks];
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) {
+      cnt[c] = 0;
+      off[c] = 0;
+      if (c < nch) {
+        const int x = min(c * kWave + lane, p.n_experts - 1);
+        cnt[c] = p.counts[x];
+        off[c] = p.offsets[x];
+      }
+    }
     int nact = 0;
-    for (int e0 = 0; e0 < p.n_experts; e0 += kWave) {
-      const int e = e0 + lane;
-      const bool on = e < p.n_experts && p.counts[e] > 0;
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) {
+      const bool on = c < nch && c * kWave + lane < p.n_experts && cnt[c] > 0;
       const uint64_t m = __ballot(on);
       if (on) {
         const int a = nact + __popcll(m & ((1ull << lane) - 1ull));
-        s_act[a] = e;
-        s_off[a] = p.offsets[e];
+        s_act[a] = c * kWave + lane;
+        s_off[a] = off[c];
       }
       nact += __popcll(m);
     }
@@ -778,34 +801,31 @@ __global__ __launch_bounds__(kSmallThreads) void down_combine_small_kernel(FfnPa
   }
   for (int i = tid; i < kSmallMaxActive * kSmallMaxTokens; i += kSmallThreads)
     (&s_col[0][0])[i] = -1;
+  for (int i = tid; i < kSmallMaxSlots; i += kSmallThreads) s_w[i] = 0.0f;
   __syncthreads();
   const int A = s_nact, AR = s_nroute;
-  const int nvalid = AR > 0 ? s_off[AR - 1] + p.counts[s_act[AR - 1]] : 0;
-  for (int q = tid; q < n_slots; q += kSmallThreads) {
-    if (q < nk) {
-      if (q >= nvalid) continue;  // slots of out-of-range ids do not exist
-      int lo = 0, hi = AR;        // active expert owning slot q
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (s_off[mid] <= q)
-          lo = mid;
-        else
-          hi = mid;
-      }
-      const int f = p.perm[q];
-      s_col[lo][f / p.top_k] = (int16_t)q;
-      s_w[q] = p.topk_w[f];
-    } else {
-      s_col[A - 1][q - nk] = (int16_t)q;
-      s_w[q] = 1.0f;
+  if (tid < nk && my_slot >= 0) {
+    int lo = 0, hi = AR;  // active expert owning the slot
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_off[mid] <= my_slot)
+        lo = mid;
+      else
+        hi = mid;
     }
+    s_col[lo][tid / p.top_k] = (int16_t)my_slot;
+    s_w[my_slot] = my_w;
+  }
+  for (int q = nk + tid; q < n_slots; q += kSmallThreads) {
+    s_col[A - 1][q - nk] = (int16_t)q;
+    s_w[q] = 1.0f;
   }
   __syncthreads();
 
   __bf16* s_bh = reinterpret_cast<__bf16*>(smem);
   __bf16* s_bl = s_bh + (size_t)spc * n_slots * kStageRow;
   const int nks = max(p.inter, p.has_shared ? p.shared_inter : 0) / 128;
-  f32x4 acc = f32x4{0, 0, 0, 0};
+  f32x4 acc_h = f32x4{0, 0, 0, 0}, acc_l = f32x4{0, 0, 0, 0};
 
   // units u = s * A + a of a chunk are dealt round-robin to the wavefronts,
   // kSmallBatch at a time: the codes of a whole batch are requested before
@@ -813,82 +833,156 @@ __global__ __launch_bounds__(kSmallThreads) void down_combine_small_kernel(FfnPa
   constexpr int kSmallBatch = 2 * Fmt<WT>::CH;  // 16 MXFP4 or 8 fp8 units
   u32x4 q[kSmallBatch][Fmt<WT>::Q];
   uint32_t su[kSmallBatch];
-  int ua[kSmallBatch], us[kSmallBatch];
-  // a unit that does not exist (past the end, the shared expert, a step
-  // beyond a routed expert's width) loads routed expert 0's first step, which
-  // always exists, and is skipped by compute_batch; the loads of a batch stay
-  // one burst
+  int ua[kSmallBatch], us[kSmallBatch], uslot[kSmallBatch];
+  // a unit that does not exist (past the end, a step beyond the expert's
+  // width, the shared expert when its format differs) loads routed expert
+  // 0's first step, which always exists, and is skipped by compute_batch;
+  // the loads of a batch stay one burst
+  const int Ad = max(A, 1);  // A == 0 only with no units at all
+  const int64_t cb_r = Fmt<WT>::row_bytes(p.inter), sb_r = Fmt<WT>::scale_row_bytes(p.inter);
+  const int64_t cb_s = Fmt<WT>::row_bytes(p.shared_inter);
+  const int64_t sb_s = Fmt<WT>::scale_row_bytes(p.shared_inter);
+  // byte offsets from down_c / down_s: one routed expert, this row block of
+  // routed expert 0, this row block of the shared matrix
+  const uint64_t estride_c = (uint64_t)(p.hidden * cb_r), estride_s = (uint64_t)(p.hidden * sb_r);
+  const uint64_t cbase_r = (uint64_t)(row0 * cb_r), sbase_r = (uint64_t)(row0 * sb_r);
+  const uint64_t cbase_s = (uint64_t)p.sdown_c - (uint64_t)p.down_c + (uint64_t)(row0 * cb_s);
+  const uint64_t sbase_s = (uint64_t)p.sdown_s - (uint64_t)p.down_s + (uint64_t)(row0 * sb_s);
+  const int kmax_r = p.inter / 128, kmax_s = kMerged ? p.shared_inter / 128 : 0;
+  const int64_t lane_cr = r16 * cb_r + Fmt<WT>::code_off(0, g);
+  const int64_t lane_cs = r16 * cb_s + Fmt<WT>::code_off(0, g);
+  const int64_t lane_sr = r16 * sb_r + Fmt<WT>::scale_off(0, g);
+  const int64_t lane_ss = r16 * sb_s + Fmt<WT>::scale_off(0, g);
   auto load_batch = [&](int ks0, int units, int u0) {
-    const int64_t cb = Fmt<WT>::row_bytes(p.inter);
-    const int64_t sb = Fmt<WT>::scale_row_bytes(p.inter);
+    // pass 1: the LDS lookups of every unit of the batch (expert, slot of
+    // the lane's token), stepping (s, a) along u = u0 + 8b without divisions
+    int be[kSmallBatch], bslot[kSmallBatch], ba[kSmallBatch];
+    int s = uniform(u0 / Ad), a = uniform(u0 - s * Ad);
 #pragma unroll
     for (int b = 0; b < kSmallBatch; ++b) {
-      const int u = u0 + b * kSmallWaves;
-      const int s = u / A;
-      const int a = u - s * A;
-      const int e = uniform(s_act[u < units ? a : 0]);
-      const int ks = ks0 + s;
-      const bool real = u < units && e != p.n_experts && ks * 128 < p.inter;
-      ua[b] = real ? a : -1;
+      const bool in = u0 + b * kSmallWaves < units;
+      ba[b] = a;
       us[b] = s;
-      const int64_t row = (int64_t)(real ? e : 0) * p.hidden + row0 + r16;
-      load_codes<WT>(p.down_c + row * cb, p.down_s + row * sb, real ? ks : 0, g, q[b], su[b]);
+      be[b] = s_act[in ? a : 0];
+      bslot[b] = s_col[in ? a : 0][r16];
+      a += kSmallWaves;
+      while (a >= Ad) {
+        a -= Ad;
+        ++s;
+      }
+    }
+    // pass 2: one burst of code and scale loads.  An address is a wave-
+    // uniform part (matrix, expert, row block, step) plus the lane's part
+    // (row r16, quarter g); the shared matrix is reached by adding the
+    // distance between the two allocations, so no pointer is reloaded
+#pragma unroll
+    for (int b = 0; b < kSmallBatch; ++b) {
+      const int e = uniform(be[b]);
+      const int sh = e == p.n_experts;
+      const int ks = ks0 + us[b];
+      const int real = (u0 + b * kSmallWaves < units) & (ks < (sh ? kmax_s : kmax_r));
+      const int use_sh = real & sh;
+      const uint32_t e_eff = (real & !sh) ? (uint32_t)e : 0u;
+      const uint32_t ks_eff = real ? (uint32_t)ks : 0u;
+      const uint64_t cu = (uint64_t)e_eff * estride_c + (use_sh ? cbase_s : cbase_r) +
+                          (uint64_t)(ks_eff * (uint32_t)Fmt<WT>::code_off(1, 0));
+      const uint64_t su_ = (uint64_t)e_eff * estride_s + (use_sh ? sbase_s : sbase_r) +
+                           (uint64_t)(ks_eff * (uint32_t)Fmt<WT>::scale_off(1, 0));
+      const uint8_t* c = p.down_c + cu + (use_sh ? lane_cs : lane_cr);
+      const uint8_t* sc = p.down_s + su_ + (use_sh ? lane_ss : lane_sr);
+#pragma unroll
+      for (int i = 0; i < Fmt<WT>::Q; ++i) q[b][i] = load16(c + 16 * i);
+      su[b] = *sc;
+      ua[b] = real ? ba[b] : -1;
+      uslot[b] = real ? bslot[b] : -1;
     }
   };
-  auto compute_batch = [&]() {
+  // B fragments of unit b: the staged w*h of the lane's token, or zeros
+  auto read_b = [&](int b, u32x4 (&bh)[4], u32x4 (&bl)[4]) {
 #pragma unroll
-    for (int b = 0; b < kSmallBatch; ++b) {
-      if (ua[b] < 0) continue;  // uniform over the wavefront
-      bf16x8 a[4];
-      Fmt<WT>::decode(q[b], su[b], a);
-      const int slot = s_col[ua[b]][r16];
-      const size_t o = ((size_t)us[b] * n_slots + (slot >= 0 ? slot : 0)) * kStageRow + g * 32;
+    for (int j = 0; j < 4; ++j) bh[j] = bl[j] = u32x4{0, 0, 0, 0};
+    const int slot = uslot[b];
+    if (slot >= 0) {
+      const size_t o = ((size_t)us[b] * n_slots + slot) * kStageRow + g * 32;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const u32x4 z = u32x4{0, 0, 0, 0};
-        const bf16x8 bh =
-            as_bf16x8(slot >= 0 ? *reinterpret_cast<const u32x4*>(s_bh + o + 8 * j) : z);
-        const bf16x8 bl =
-            as_bf16x8(slot >= 0 ? *reinterpret_cast<const u32x4*>(s_bl + o + 8 * j) : z);
-        acc = mfma_bf16(a[j], bh, acc);
-        acc = mfma_bf16(a[j], bl, acc);
+        bh[j] = *reinterpret_cast<const u32x4*>(s_bh + o + 8 * j);
+        bl[j] = *reinterpret_cast<const u32x4*>(s_bl + o + 8 * j);
       }
     }
   };
+  auto compute_batch = [&]() {
+    u32x4 bh[2][4], bl[2][4];
+    read_b(0, bh[0], bl[0]);
+#pragma unroll
+    for (int b = 0; b < kSmallBatch; ++b) {
+      if (b + 1 < kSmallBatch) read_b(b + 1, bh[(b + 1) & 1], bl[(b + 1) & 1]);
+      if (ua[b] < 0) continue;  // uniform over the wavefront
+      bf16x8 a[4];
+      Fmt<WT>::decode(q[b], su[b], a);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc_h = mfma_bf16(a[j], as_bf16x8(bh[b & 1][j]), acc_h);
+        acc_l = mfma_bf16(a[j], as_bf16x8(bl[b & 1][j]), acc_l);
+      }
+    }
+  };
+  // staging of one group of 8 reduction indices of one slot:
+  // w * (h_hi + h_lo), split again into hi + lo
+  auto group_at = [&](int gi, int& s, int& slot, int& q8) {
+    q8 = gi & 15;
+    const int rest = gi >> 4;
+    slot = rest % n_slots;
+    s = rest / n_slots;
+  };
+  auto stage = [&](int s, int slot, int q8, u32x4 rh, u32x4 rl) {
+    const bf16x8 hi = as_bf16x8(rh), lo = as_bf16x8(rl);
+    const float wt = s_w[slot];
+    bf16x8 oh, ol;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float v = wt * (static_cast<float>(hi[j]) + static_cast<float>(lo[j]));
+      __bf16 x, y;
+      split_bf16(v, x, y);
+      oh[j] = x;
+      ol[j] = y;
+    }
+    const size_t o = ((size_t)s * n_slots + slot) * kStageRow + q8 * 8;
+    *reinterpret_cast<u32x4*>(s_bh + o) = __builtin_bit_cast(u32x4, oh);
+    *reinterpret_cast<u32x4*>(s_bl + o) = __builtin_bit_cast(u32x4, ol);
+  };
+  constexpr int kPre = 4;  // groups per thread requested ahead of the weights
 
   for (int ks0 = 0; ks0 < nks; ks0 += spc) {
     const int steps = min(spc, nks - ks0);
     const int units = steps * A;
-    load_batch(ks0, units, wave);  // in flight while h is staged
-    // stage w * (h_hi + h_lo) for every slot, split again into hi + lo
     const int groups = steps * n_slots * 16;
-    for (int i = tid; i < groups; i += kSmallThreads) {
-      const int q8 = i & 15;
-      const int rest = i >> 4;
-      const int slot = rest % n_slots;
-      const int s = rest / n_slots;
-      const int k = (ks0 + s) * 128 + q8 * 8;
-      const int kdim = slot < nk ? p.inter : p.shared_inter;
-      u32x4 vh = u32x4{0, 0, 0, 0}, vl = u32x4{0, 0, 0, 0};
-      if ((slot >= nk || slot < nvalid) && k < kdim) {
-        const bf16x8 hi = as_bf16x8(load16(p.h_hi + (int64_t)slot * p.h_stride + k));
-        const bf16x8 lo = as_bf16x8(load16(p.h_lo + (int64_t)slot * p.h_stride + k));
-        const float wt = s_w[slot];
-        bf16x8 oh, ol;
+    // every staged row lies inside the workspace (slot < n_slots, index <
+    // h_stride); rows of slots that no token owns are staged but never read
+    u32x4 ph[kPre], pl[kPre];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float v = wt * (static_cast<float>(hi[j]) + static_cast<float>(lo[j]));
-          __bf16 a, b;
-          split_bf16(v, a, b);
-          oh[j] = a;
-          ol[j] = b;
-        }
-        vh = __builtin_bit_cast(u32x4, oh);
-        vl = __builtin_bit_cast(u32x4, ol);
+    for (int i = 0; i < kPre; ++i) {
+      int s, slot, q8;
+      group_at(min(tid + i * kSmallThreads, groups - 1), s, slot, q8);
+      const int64_t o = (int64_t)slot * p.h_stride + (ks0 + s) * 128 + q8 * 8;
+      ph[i] = load16(p.h_hi + o);
+      pl[i] = load16(p.h_lo + o);
+    }
+    load_batch(ks0, units, wave);
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) {
+      const int gi = tid + i * kSmallThreads;
+      if (gi < groups) {
+        int s, slot, q8;
+        group_at(gi, s, slot, q8);
+        stage(s, slot, q8, ph[i], pl[i]);
       }
-      const size_t o = ((size_t)s * n_slots + slot) * kStageRow + q8 * 8;
-      *reinterpret_cast<u32x4*>(s_bh + o) = vh;
-      *reinterpret_cast<u32x4*>(s_bl + o) = vl;
+    }
+    for (int gi = tid + kPre * kSmallThreads; gi < groups; gi += kSmallThreads) {
+      int s, slot, q8;
+      group_at(gi, s, slot, q8);
+      const int64_t o = (int64_t)slot * p.h_stride + (ks0 + s) * 128 + q8 * 8;
+      stage(s, slot, q8, load16(p.h_hi + o), load16(p.h_lo + o));
     }
     __syncthreads();
     compute_batch();
@@ -897,8 +991,8 @@ __global__ __launch_bounds__(kSmallThreads) void down_combine_small_kernel(FfnPa
       load_batch(ks0, units, u0);
       compute_batch();
     }
-    // the shared expert's units of this chunk
-    if (p.has_shared) {
+    // the shared expert in another format: its own loop
+    if (!kMerged && p.has_shared) {
       const int a = A - 1;
       for (int s = wave; s < steps; s += kSmallWaves) {
         const int ks = ks0 + s;
@@ -906,11 +1000,11 @@ __global__ __launch_bounds__(kSmallThreads) void down_combine_small_kernel(FfnPa
         const int64_t cb = Fmt<SWT>::row_bytes(p.shared_inter);
         const int64_t sb = Fmt<SWT>::scale_row_bytes(p.shared_inter);
         const int64_t row = row0 + r16;
-        u32x4 q[Fmt<SWT>::Q];
-        uint32_t su;
-        load_codes<SWT>(p.sdown_c + row * cb, p.sdown_s + row * sb, ks, g, q, su);
+        u32x4 qs[Fmt<SWT>::Q];
+        uint32_t ss;
+        load_codes<SWT>(p.sdown_c + row * cb, p.sdown_s + row * sb, ks, g, qs, ss);
         bf16x8 w4[4];
-        Fmt<SWT>::decode(q, su, w4);
+        Fmt<SWT>::decode(qs, ss, w4);
         const int slot = s_col[a][r16];
         const size_t o = ((size_t)s * n_slots + (slot >= 0 ? slot : 0)) * kStageRow + g * 32;
 #pragma unroll
@@ -920,14 +1014,16 @@ __global__ __launch_bounds__(kSmallThreads) void down_combine_small_kernel(FfnPa
               as_bf16x8(slot >= 0 ? *reinterpret_cast<const u32x4*>(s_bh + o + 8 * j) : z);
           const bf16x8 bl =
               as_bf16x8(slot >= 0 ? *reinterpret_cast<const u32x4*>(s_bl + o + 8 * j) : z);
-          acc = mfma_bf16(w4[j], bh, acc);
-          acc = mfma_bf16(w4[j], bl, acc);
+          acc_h = mfma_bf16(w4[j], bh, acc_h);
+          acc_l = mfma_bf16(w4[j], bl, acc_l);
         }
       }
     }
     __syncthreads();
   }
 
+  // the eight partial sums, added in wavefront order
+  f32x4 acc = acc_h + acc_l;
   if (wave > 0) s_red[wave - 1][lane] = acc;
   __syncthreads();
   if (wave == 0) {
