@@ -761,7 +761,31 @@ __global__ __launch_bounds__(kSmallThreads) void down_combine_small_kernel(FfnPa
   const int nk = p.n_tokens * p.top_k;  // >= 1 on this path
   const int n_slots = nk + (p.has_shared ? p.n_tokens : 0);
 
-  // routing inputs in one round trip
+  const int nks = max(p.inter, p.has_shared ? p.shared_inter : 0) / 128;
+  // staging of one group of 8 reduction indices of one slot of a chunk
+  auto group_at = [&](int gi, int& s, int& slot, int& q8) {
+    q8 = gi & 15;
+    const int rest = gi >> 4;
+    slot = rest % n_slots;
+    s = rest / n_slots;
+  };
+  constexpr int kPre = 4;  // h groups per thread requested ahead
+  u32x4 ph[kPre], pl[kPre];
+  // every staged row lies inside the workspace (slot < n_slots, index <
+  // h_stride); rows of slots that no token owns are staged but never read
+  auto prefetch_h = [&](int ks0, int groups) {
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) {
+      int s, slot, q8;
+      group_at(min(tid + i * kSmallThreads, groups - 1), s, slot, q8);
+      const int64_t o = (int64_t)slot * p.h_stride + (ks0 + s) * 128 + q8 * 8;
+      ph[i] = load16(p.h_hi + o);
+      pl[i] = load16(p.h_lo + o);
+    }
+  };
+  // the first chunk's h and the routing inputs in one round trip, before
+  // the weight traffic of the whole chip starts
+  prefetch_h(0, min(spc, nks) * n_slots * 16);
   const int fi = min(tid, nk - 1);
   const int my_slot = p.inv_perm[fi];
   const float my_w = p.topk_w[fi];
@@ -802,6 +826,10 @@ __global__ __launch_bounds__(kSmallThreads) void down_combine_small_kernel(FfnPa
   for (int i = tid; i < kSmallMaxActive * kSmallMaxTokens; i += kSmallThreads)
     (&s_col[0][0])[i] = -1;
   for (int i = tid; i < kSmallMaxSlots; i += kSmallThreads) s_w[i] = 0.0f;
+  if (tid < kStageRow * 2 / 16) {
+    char* z = smem + (size_t)2 * spc * n_slots * kStageRow * 2;
+    *reinterpret_cast<u32x4*>(z + tid * 16) = u32x4{0, 0, 0, 0};
+  }
   __syncthreads();
   const int A = s_nact, AR = s_nroute;
   if (tid < nk && my_slot >= 0) {
@@ -824,7 +852,7 @@ __global__ __launch_bounds__(kSmallThreads) void down_combine_small_kernel(FfnPa
 
   __bf16* s_bh = reinterpret_cast<__bf16*>(smem);
   __bf16* s_bl = s_bh + (size_t)spc * n_slots * kStageRow;
-  const int nks = max(p.inter, p.has_shared ? p.shared_inter : 0) / 128;
+  const __bf16* s_z = s_bl + (size_t)spc * n_slots * kStageRow;  // zero row
   f32x4 acc_h = f32x4{0, 0, 0, 0}, acc_l = f32x4{0, 0, 0, 0};
 
   // units u = s * A + a of a chunk are dealt round-robin to the wavefronts,
@@ -897,22 +925,29 @@ __global__ __launch_bounds__(kSmallThreads) void down_combine_small_kernel(FfnPa
       uslot[b] = real ? bslot[b] : -1;
     }
   };
-  // B fragments of unit b: the staged w*h of the lane's token, or zeros
+  // B fragments of unit b: the staged w*h of the lane's token, or the zero
+  // row when the token did not pick the unit's expert.  Lanes of absent
+  // tokens (r16 >= n_tokens) read nothing and keep the zeros set once per
+  // batch, so no fragment is cleared per unit.
   auto read_b = [&](int b, u32x4 (&bh)[4], u32x4 (&bl)[4]) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) bh[j] = bl[j] = u32x4{0, 0, 0, 0};
-    const int slot = uslot[b];
-    if (slot >= 0) {
+    if (r16 < p.n_tokens) {
+      const int slot = uslot[b];
       const size_t o = ((size_t)us[b] * n_slots + slot) * kStageRow + g * 32;
+      const __bf16* srch = slot >= 0 ? s_bh + o : s_z + g * 32;
+      const __bf16* srcl = slot >= 0 ? s_bl + o : s_z + g * 32;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        bh[j] = *reinterpret_cast<const u32x4*>(s_bh + o + 8 * j);
-        bl[j] = *reinterpret_cast<const u32x4*>(s_bl + o + 8 * j);
+        bh[j] = *reinterpret_cast<const u32x4*>(srch + 8 * j);
+        bl[j] = *reinterpret_cast<const u32x4*>(srcl + 8 * j);
       }
     }
   };
   auto compute_batch = [&]() {
     u32x4 bh[2][4], bl[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bh[i][j] = bl[i][j] = u32x4{0, 0, 0, 0};
     read_b(0, bh[0], bl[0]);
 #pragma unroll
     for (int b = 0; b < kSmallBatch; ++b) {
@@ -927,14 +962,7 @@ __global__ __launch_bounds__(kSmallThreads) void down_combine_small_kernel(FfnPa
       }
     }
   };
-  // staging of one group of 8 reduction indices of one slot:
-  // w * (h_hi + h_lo), split again into hi + lo
-  auto group_at = [&](int gi, int& s, int& slot, int& q8) {
-    q8 = gi & 15;
-    const int rest = gi >> 4;
-    slot = rest % n_slots;
-    s = rest / n_slots;
-  };
+  // staging: w * (h_hi + h_lo), split again into hi + lo
   auto stage = [&](int s, int slot, int q8, u32x4 rh, u32x4 rl) {
     const bf16x8 hi = as_bf16x8(rh), lo = as_bf16x8(rl);
     const float wt = s_w[slot];
@@ -951,24 +979,11 @@ __global__ __launch_bounds__(kSmallThreads) void down_combine_small_kernel(FfnPa
     *reinterpret_cast<u32x4*>(s_bh + o) = __builtin_bit_cast(u32x4, oh);
     *reinterpret_cast<u32x4*>(s_bl + o) = __builtin_bit_cast(u32x4, ol);
   };
-  constexpr int kPre = 4;  // groups per thread requested ahead of the weights
-
   for (int ks0 = 0; ks0 < nks; ks0 += spc) {
     const int steps = min(spc, nks - ks0);
     const int units = steps * A;
     const int groups = steps * n_slots * 16;
-    // every staged row lies inside the workspace (slot < n_slots, index <
-    // h_stride); rows of slots that no token owns are staged but never read
-    u32x4 ph[kPre], pl[kPre];
-#pragma unroll
-    for (int i = 0; i < kPre; ++i) {
-      int s, slot, q8;
-      group_at(min(tid + i * kSmallThreads, groups - 1), s, slot, q8);
-      const int64_t o = (int64_t)slot * p.h_stride + (ks0 + s) * 128 + q8 * 8;
-      ph[i] = load16(p.h_hi + o);
-      pl[i] = load16(p.h_lo + o);
-    }
-    load_batch(ks0, units, wave);
+    if (ks0 > 0) prefetch_h(ks0, groups);
 #pragma unroll
     for (int i = 0; i < kPre; ++i) {
       const int gi = tid + i * kSmallThreads;
@@ -985,6 +1000,7 @@ __global__ __launch_bounds__(kSmallThreads) void down_combine_small_kernel(FfnPa
       stage(s, slot, q8, load16(p.h_hi + o), load16(p.h_lo + o));
     }
     __syncthreads();
+    load_batch(ks0, units, wave);
     compute_batch();
     for (int u0 = wave + kSmallWaves * kSmallBatch; u0 < units;
          u0 += kSmallWaves * kSmallBatch) {
@@ -1126,12 +1142,13 @@ hipError_t down_small_launch(const FfnParams& p, int slots, hipStream_t stream, 
                              hipEvent_t stop) {
   const int nks = (p.inter > p.shared_inter ? p.inter : p.shared_inter) / 128;
   const int per_step = slots * kStageRow * 2 * 2;  // hi + lo bf16
-  int spc = kLdsBudget / per_step;
+  const int zero_row = kStageRow * 2;
+  int spc = (kLdsBudget - zero_row) / per_step;
   spc = spc < 1 ? 1 : (spc > nks ? nks : spc);
   static const hipError_t attr = allow_lds(down_combine_small_kernel<WT, SWT>);
   if (attr != hipSuccess) return attr;
   return launch(down_combine_small_kernel<WT, SWT>, dim3(p.hidden / 16), dim3(kSmallThreads),
-                (size_t)spc * per_step, stream, start, stop, p, spc);
+                (size_t)spc * per_step + zero_row, stream, start, stop, p, spc);
 }
 
 template <int S>
