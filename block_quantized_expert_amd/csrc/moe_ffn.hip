@@ -37,6 +37,7 @@
 #include <hip/hip_runtime.h>
 
 #include "moe_device.h"
+#include "moe_formats.h"
 #include "moe_kernels.h"
 
 namespace moe {
@@ -47,14 +48,6 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxSeg = MOE_MAX_EXPERTS + 1;
 constexpr int kMaxGrid = 256 * 8;  // 256 CUs, up to 8 resident workgroups each
 constexpr int kLdsBudget = 140 * 1024;  // dynamic LDS a kernel may ask for
-
-// ------------------------------------------------------------ uniformity
-
-// Values that are the same on every lane of a wavefront, moved to scalar
-// registers so that branches on them are scalar branches: a batch of loads
-// then sits in one basic block with no wait between its requests.
-__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
-__device__ __forceinline__ int wave_id() { return uniform(threadIdx.x >> 6); }
 
 // ------------------------------------------------------------ work items
 
@@ -126,53 +119,6 @@ __device__ __forceinline__ Item find_item(const FfnParams& p, const int* s_pref,
   it.m = uniform(min(tn, m_all - tile * tn));
   it.row0 = uniform(rb * 16);
   return it;
-}
-
-// ------------------------------------------------------- weight formats
-
-// Per reduction step a lane holds Q 16-byte code vectors and one scale.
-template <int WT>
-struct Fmt;
-
-template <>
-struct Fmt<MOE_W_MXFP4> {
-  static constexpr int Q = 1;
-  static constexpr int CH = 8;  // steps preloaded per chunk
-  __device__ static int64_t row_bytes(int cols) { return cols / 2; }
-  __device__ static int64_t scale_row_bytes(int cols) { return cols / 32; }
-  __device__ static int code_off(int ks, int g) { return ks * 64 + g * 16; }
-  __device__ static int scale_off(int ks, int g) { return ks * 4 + g; }
-  __device__ static void decode(const u32x4 (&q)[Q], uint32_t u, bf16x8 (&a)[4]) {
-    const float s = ue8m0_to_f32(u);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) a[j] = fp4x8_to_bf16(q[0][j], s);
-  }
-};
-
-template <>
-struct Fmt<MOE_W_FP8E4M3_B128> {
-  static constexpr int Q = 2;
-  static constexpr int CH = 4;
-  __device__ static int64_t row_bytes(int cols) { return cols; }
-  __device__ static int64_t scale_row_bytes(int cols) { return cols / 128; }
-  __device__ static int code_off(int ks, int g) { return ks * 128 + g * 32; }
-  __device__ static int scale_off(int ks, int) { return ks; }
-  __device__ static void decode(const u32x4 (&q)[Q], uint32_t u, bf16x8 (&a)[4]) {
-    const float s = ue8m0_to_f32(u);
-    a[0] = fp8x8_to_bf16(q[0][0], q[0][1], s);
-    a[1] = fp8x8_to_bf16(q[0][2], q[0][3], s);
-    a[2] = fp8x8_to_bf16(q[1][0], q[1][1], s);
-    a[3] = fp8x8_to_bf16(q[1][2], q[1][3], s);
-  }
-};
-
-template <int WT>
-__device__ __forceinline__ void load_codes(const uint8_t* crow, const uint8_t* srow, int ks,
-                                           int g, u32x4 (&q)[Fmt<WT>::Q], uint32_t& u) {
-  const uint8_t* c = crow + Fmt<WT>::code_off(ks, g);
-#pragma unroll
-  for (int i = 0; i < Fmt<WT>::Q; ++i) q[i] = load16(c + 16 * i);
-  u = srow[Fmt<WT>::scale_off(ks, g)];
 }
 
 // ------------------------------------------------------- B operands
@@ -597,111 +543,7 @@ __global__ __launch_bounds__(kThreads) void gate_up_decode_kernel(FfnParams p, i
   }
 }
 
-// ------------------------------------------------------- down (per slot)
-
-template <int NBT, int WT>
-__device__ __forceinline__ void down_item(const FfnParams& p, const Item& it, bool shared,
-                                          int wave, int g, int r16, f32x4 (&acc)[NBT]) {
-  using F = Fmt<WT>;
-  constexpr int CH = F::CH;
-  const int kdim = shared ? p.shared_inter : p.inter;
-  const int64_t cb = F::row_bytes(kdim);
-  const int64_t sb = F::scale_row_bytes(kdim);
-  const int64_t row = (shared ? 0 : (int64_t)it.seg * p.hidden) + it.row0 + r16;
-  const uint8_t* dcr = (shared ? p.sdown_c : p.down_c) + row * cb;
-  const uint8_t* dsr = (shared ? p.sdown_s : p.down_s) + row * sb;
-
-  const __bf16* hh[NBT];
-  const __bf16* hl[NBT];
-#pragma unroll
-  for (int tb = 0; tb < NBT; ++tb) {
-    const int n = tb * 16 + r16;
-    hh[tb] = nullptr;
-    hl[tb] = nullptr;
-    if (n < it.m) {
-      const int64_t o = (int64_t)(it.slot0 + n) * p.h_stride;
-      hh[tb] = p.h_hi + o;
-      hl[tb] = p.h_lo + o;
-    }
-  }
-  const int nbt = (it.m + 15) >> 4;
-  const int S = uniform(wave_steps(kdim / 128, wave));
-
-  for (int j0 = 0; j0 < S; j0 += CH) {
-    const int rem = min(CH, S - j0);
-    u32x4 q[CH][F::Q];
-    uint32_t su[CH];
-#pragma unroll
-    for (int i = 0; i < CH; ++i)  // unconditional: one burst of requests
-      load_codes<WT>(dcr, dsr, wave + kWaves * min(j0 + i, S - 1), g, q[i], su[i]);
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      if (i < rem) {
-        const int kofs = (wave + kWaves * (j0 + i)) * 128 + g * 32;
-        bf16x8 a[4];
-        F::decode(q[i], su[i], a);
-#pragma unroll
-        for (int tb = 0; tb < NBT; ++tb) {
-          if (tb >= nbt) break;
-          bf16x8 bh[4], bl[4];
-          load_bf16_32(hh[tb] ? hh[tb] + kofs : nullptr, bh);
-          load_bf16_32(hl[tb] ? hl[tb] + kofs : nullptr, bl);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            acc[tb] = mfma_bf16(a[j], bh[j], acc[tb]);
-            acc[tb] = mfma_bf16(a[j], bl[j], acc[tb]);
-          }
-        }
-      }
-    }
-  }
-}
-
-template <int NBT>
-__global__ __launch_bounds__(kThreads) void down_kernel(FfnParams p) {
-  constexpr int TN = 16 * NBT;
-  __shared__ int s_pref[kMaxSeg + 1];
-  __shared__ int s_tmp[kWaves];
-  __shared__ f32x4 s_red[kWaves - 1][NBT][kWave];
-  const int lane = threadIdx.x & 63, wave = wave_id();
-  const int g = lane >> 4, r16 = lane & 15;
-  const int total = build_item_prefix(p, TN, true, s_pref, s_tmp);
-
-  for (int item = blockIdx.x; item < total; item += gridDim.x) {
-    const Item it = find_item(p, s_pref, item, TN, true);
-    const bool shared = it.seg == p.n_experts;
-    f32x4 acc[NBT];
-#pragma unroll
-    for (int tb = 0; tb < NBT; ++tb) acc[tb] = f32x4{0, 0, 0, 0};
-    if ((shared ? p.sw_type : p.w_type) == MOE_W_MXFP4)
-      down_item<NBT, MOE_W_MXFP4>(p, it, shared, wave, g, r16, acc);
-    else
-      down_item<NBT, MOE_W_FP8E4M3_B128>(p, it, shared, wave, g, r16, acc);
-
-    if (wave > 0) {
-#pragma unroll
-      for (int tb = 0; tb < NBT; ++tb) s_red[wave - 1][tb][lane] = acc[tb];
-    }
-    __syncthreads();
-    if (wave == 0) {
-#pragma unroll
-      for (int w = 0; w < kWaves - 1; ++w) {
-#pragma unroll
-        for (int tb = 0; tb < NBT; ++tb) acc[tb] += s_red[w][tb][lane];
-      }
-#pragma unroll
-      for (int tb = 0; tb < NBT; ++tb) {
-        const int n = tb * 16 + r16;
-        if (n < it.m) {
-          const int64_t slot = it.slot0 + n;
-          const float wt = shared ? 1.0f : p.topk_w[p.perm[slot]];
-          *reinterpret_cast<f32x4*>(p.obuf + slot * p.hidden + it.row0 + 4 * g) = acc[tb] * wt;
-        }
-      }
-    }
-    __syncthreads();
-  }
-}
+// ------------------------------------------------------- combine
 
 // y[t] = o_shared[t] + sum_i o[inv_perm[t*k + i]] (weights already applied),
 // in that fixed order; four features per thread.
@@ -1117,19 +959,6 @@ hipError_t gate_up_nbt(const FfnParams& p, hipStream_t stream, hipEvent_t start,
   return gate_up_launch<NBT, false>(p, grid, stream, start, stop);
 }
 
-template <int NBT>
-hipError_t down_nbt(const FfnParams& p, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
-  constexpr int TN = 16 * NBT;
-  const int64_t shared_tiles = p.has_shared ? (p.n_tokens + TN - 1) / TN : 0;
-  const int64_t items = (routed_tiles_bound(p, TN) + shared_tiles) * (p.hidden / 16);
-  hipError_t e = launch(down_kernel<NBT>, dim3(grid_for(items)), dim3(kThreads), 0, stream, start,
-                        nullptr, p);
-  if (e != hipSuccess) return e;
-  const int64_t n = (int64_t)p.n_tokens * (p.hidden / 4);
-  return launch(combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, nullptr,
-                stop, p);
-}
-
 // Slots of a small batch; 0 when the batch takes the per-slot path.
 int small_slots(const FfnParams& p) {
   const int slots = p.n_tokens * p.top_k + (p.has_shared ? p.n_tokens : 0);
@@ -1187,6 +1016,7 @@ hipError_t launch_ffn_gate_up(const FfnParams& p, hipStream_t stream, hipEvent_t
     case 8: return gate_up_decode_launch<8>(p, stream, start, stop);
     default: break;
   }
+  if (!p.x_f32) return launch_gemm_gate_up(p, stream, start, stop);
   switch (pick_nbt(p.n_tokens)) {
     case 1: return gate_up_nbt<1>(p, stream, start, stop);
     case 2: return gate_up_nbt<2>(p, stream, start, stop);
@@ -1207,12 +1037,12 @@ hipError_t launch_ffn_down(const FfnParams& p, hipStream_t stream, hipEvent_t st
     return down_small_launch<MOE_W_FP8E4M3_B128, MOE_W_FP8E4M3_B128>(p, slots, stream, start,
                                                                       stop);
   }
-  switch (pick_nbt(p.n_tokens)) {
-    case 1: return down_nbt<1>(p, stream, start, stop);
-    case 2: return down_nbt<2>(p, stream, start, stop);
-    case 3: return down_nbt<3>(p, stream, start, stop);
-    default: return down_nbt<4>(p, stream, start, stop);
-  }
+  // weighted per-slot outputs, then each token's sum in a fixed order
+  hipError_t e = launch_gemm_down(p, stream, start, nullptr);
+  if (e != hipSuccess) return e;
+  const int64_t n = (int64_t)p.n_tokens * (p.hidden / 4);
+  return launch(combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, nullptr,
+                stop, p);
 }
 
 }  // namespace moe

@@ -1,0 +1,558 @@
+// Expert FFN for batches in which experts see many tokens (prefill): grouped
+// matrix products on the matrix cores with the weights decoded in registers.
+//
+// "DeepSeek-V4-Flash 284B -- Deep-Dive Mathematical & Kernel Guide":
+//   section 4, SwiGLU equation h = SiLU(W_gate x) * (W_up x), y = W_down h;
+//   section 3.2, combine equation y = e_shared(x) + sum_i w_i e_{k_i}(x);
+//   section 2 (table B, prefill): MUL_MAT_ID batches the tokens of each
+//   expert so that its weights stream once per batch.
+// "DeepSeek V4 target engine (CPU + optional CUDA tier)", introduction and
+//   GPU coverage: routed experts in MXFP4, dense weights fp8-e4m3 + UE8M0;
+//   expert-grouped GEMM on the GPU.
+//
+// A work item is (segment, row tile, token tile of up to kTileTok slots).  A
+// segment is a routed expert (slots offsets[e] .. offsets[e+1]) or the shared
+// expert (slot N*k + t is token t).  Items of one row tile are consecutive, so
+// the workgroups that multiply the same weights with different token tiles
+// run at the same time and share them through the caches.  The grid is
+// persistent; every workgroup rebuilds the item prefix from the device-side
+// counts (no host synchronisation).
+//
+// Inside an item each wavefront owns whole output rows over the full
+// reduction: no partial sums cross wavefronts.  The reduction runs in steps
+// of 128.  The token operand of a step (activation rows gathered through
+// perm, or the h rows of the slots) is staged in LDS, double buffered; the
+// weight codes of step ks+1 and its token operand are in flight while step ks
+// multiplies.
+//
+// Gate/up: a workgroup owns 128 intermediate rows and up to 128 tokens;
+// wavefront w owns rows 32w .. 32w+31 of the gate and of the up matrix
+// (four 16-row blocks), so one token fragment read from LDS feeds four
+// MFMAs and one decoded weight fragment feeds up to eight token blocks.  The
+// epilogue applies SwiGLU and writes h as a bf16 hi/lo pair.
+//
+// Down: a workgroup owns 256 hidden rows and up to 64 tokens; wavefront w
+// owns rows 64w .. 64w+63 (four blocks) and multiplies them with h_hi and
+// h_lo.  The epilogue scales each token column by its routing weight (1 for
+// the shared expert) and writes the per-slot output; a separate pass sums
+// the slots of every token in a fixed order.
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+
+#include "moe_device.h"
+#include "moe_formats.h"
+#include "moe_kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int kGThreads = 256;
+constexpr int kRow = 136;  // bf16 per staged row: 128 + 8, so rows start on other banks
+constexpr int kGuRows = 128;  // intermediate rows per gate/up item
+constexpr int kDnRows = 256;  // hidden rows per down item
+constexpr int kSegMax = MOE_MAX_EXPERTS + 1;
+constexpr int kGemmLds = 72 * 1024;  // dynamic LDS of either kernel (two per CU)
+
+struct GItem {
+  int seg;
+  int slot0;  // first slot of the token tile
+  int m;      // slots in the tile
+  int row0;   // first output row of the row tile
+};
+
+__device__ __forceinline__ int seg_rows(const FfnParams& p, int s, bool down) {
+  return down ? p.hidden : (s == p.n_experts ? p.shared_inter : p.inter);
+}
+
+__device__ __forceinline__ int seg_count(const FfnParams& p, int s) {
+  return s == p.n_experts ? p.n_tokens : p.counts[s];
+}
+
+template <int TT, int RT, bool DOWN>
+__device__ __forceinline__ int seg_items(const FfnParams& p, int s) {
+  const int rows = seg_rows(p, s, DOWN);
+  return (seg_count(p, s) + TT - 1) / TT * ((rows + RT - 1) / RT);
+}
+
+// s_pref[s] = items of the segments before s; returns the total.
+// Segments seg_lo .. seg_hi-1 take part; s_pref is indexed from seg_lo.
+template <int TT, int RT, bool DOWN>
+__device__ int item_prefix(const FfnParams& p, int seg_lo, int seg_hi, int* s_pref, int* s_tmp) {
+  const int nseg = seg_hi - seg_lo;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int per = (nseg + kGThreads - 1) / kGThreads;
+  const int s0 = tid * per, s1 = min(s0 + per, nseg);
+  int local = 0;
+  for (int s = s0; s < s1; ++s) local += seg_items<TT, RT, DOWN>(p, seg_lo + s);
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int t = __shfl_up(incl, off);
+    if (lane >= off) incl += t;
+  }
+  if (lane == kWave - 1) s_tmp[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += s_tmp[w];
+  int run = before + incl - local;
+  for (int s = s0; s < s1; ++s) {
+    s_pref[s] = run;
+    run += seg_items<TT, RT, DOWN>(p, seg_lo + s);
+  }
+  if (tid == kGThreads - 1) s_pref[nseg] = before + incl;
+  __syncthreads();
+  return s_pref[nseg];
+}
+
+template <int TT, int RT, bool DOWN>
+__device__ __forceinline__ GItem find_item(const FfnParams& p, int seg_lo, int seg_hi,
+                                           const int* s_pref, int item) {
+  int lo = 0, hi = seg_hi - seg_lo;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s_pref[mid] <= item)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  const int local = item - s_pref[lo];
+  lo += seg_lo;
+  const bool shared = lo == p.n_experts;
+  const int m_all = seg_count(p, lo);
+  const int ntt = (m_all + TT - 1) / TT;
+  const int rt = local / ntt;
+  const int tile = local - rt * ntt;
+  const int start = shared ? p.n_tokens * p.top_k : p.offsets[lo];
+  GItem it;
+  it.seg = uniform(lo);
+  it.slot0 = uniform(start + tile * TT);
+  it.m = uniform(min(TT, m_all - tile * TT));
+  it.row0 = uniform(rt * RT);
+  return it;
+}
+
+// Token-operand staging: a tile of TT rows x 128 bf16 per reduction step.
+// Thread tid copies 16-byte chunk (tid & 15) of rows (tid >> 4) + 16 i; a
+// row that is not part of the tile is written as zeros.  Row offsets of
+// missing rows point at a valid row so that every load is unconditional.
+template <int TT>
+struct Stage {
+  static constexpr int kPer = TT / 16;  // rows per thread
+  int row[kPer];                        // source row of each staged row
+  uint32_t valid;                       // bit i: row (tid >> 4) + 16 i exists
+  u32x4 v[kPer];
+
+  __device__ void load(const __bf16* base, int64_t stride, int ks, int nbt) {
+    const int c = (threadIdx.x & 15) * 8 + ks * 128;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      if (i < nbt) v[i] = load16(base + (int64_t)row[i] * stride + c);
+  }
+  __device__ void store(char* buf, int nbt) const {
+    const int n0 = threadIdx.x >> 4, c = (threadIdx.x & 15) * 8;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      if (i < nbt)
+        *reinterpret_cast<u32x4*>(buf + ((n0 + 16 * i) * kRow + c) * 2) =
+            ((valid >> i) & 1) ? v[i] : u32x4{0, 0, 0, 0};
+  }
+};
+
+// Token fragment of token block tb, sub-step j, from a staged step.
+__device__ __forceinline__ bf16x8 token_frag(const char* buf, int tb, int j, int g, int r16) {
+  return as_bf16x8(
+      *reinterpret_cast<const u32x4*>(buf + ((tb * 16 + r16) * kRow + 32 * g + 8 * j) * 2));
+}
+
+// ------------------------------------------------------------- gate/up
+
+template <int WT, int TT>
+__device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it, char* smem,
+                                             int wave, int lane) {
+  using F = Fmt<WT>;
+  constexpr int Q = F::Q;
+  constexpr int TB = TT / 16;
+  const int g = lane >> 4, r16 = lane & 15;
+  const bool shared = it.seg == p.n_experts;
+  const int rows = shared ? p.shared_inter : p.inter;
+  const int64_t cb = F::row_bytes(p.hidden), sb = F::scale_row_bytes(p.hidden);
+  const int nks = p.hidden / 128;
+  const int nbt = uniform((it.m + 15) >> 4);
+  const int nk = p.n_tokens * p.top_k;
+
+  // the lane's rows: gate/up (mat) x two 16-row blocks (rb); row block 1
+  // lies 16 rows after row block 0
+  const int64_t lrow =
+      (shared ? 0 : (int64_t)it.seg * rows) + it.row0 + 32 * wave + r16;
+  const int64_t lc = lrow * cb + F::code_off(0, g), ls = lrow * sb + F::scale_off(0, g);
+  const uint8_t* cbase[2] = {shared ? p.sgate_c : p.gate_c, shared ? p.sup_c : p.up_c};
+  const uint8_t* sbase[2] = {shared ? p.sgate_s : p.gate_s, shared ? p.sup_s : p.up_s};
+
+  // activation rows of the tile (missing rows repeat the first one)
+  Stage<TT> st;
+  st.valid = 0;
+  {
+    const int n0 = threadIdx.x >> 4;
+#pragma unroll
+    for (int i = 0; i < Stage<TT>::kPer; ++i) {
+      const int n = n0 + 16 * i;
+      const int slot = it.slot0 + (n < it.m ? n : 0);
+      st.row[i] = shared ? slot - nk : p.perm[slot] / p.top_k;
+      if (n < it.m) st.valid |= 1u << i;
+    }
+  }
+  const __bf16* xb = static_cast<const __bf16*>(p.x);
+
+  u32x4 qc[2][2][Q], qn[2][2][Q];
+  uint32_t uc[2][2], un[2][2];
+  auto load_w = [&](int ks, u32x4 (&q)[2][2][Q], uint32_t (&u)[2][2]) {
+#pragma unroll
+    for (int mat = 0; mat < 2; ++mat)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+        for (int i = 0; i < Q; ++i)
+          q[mat][rb][i] = load16(cbase[mat] + lc + 16 * rb * cb + F::code_off(ks, 0) + 16 * i);
+        u[mat][rb] = sbase[mat][ls + 16 * rb * sb + F::scale_off(ks, 0)];
+      }
+  };
+
+  f32x4 acc[2][2][TB];
+#pragma unroll
+  for (int mat = 0; mat < 2; ++mat)
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) acc[mat][rb][tb] = f32x4{0, 0, 0, 0};
+
+  char* buf0 = smem;
+  char* buf1 = smem + TT * kRow * 2;
+  load_w(0, qc, uc);
+  st.load(xb, p.hidden, 0, nbt);
+  st.store(buf0, nbt);
+  __syncthreads();
+  for (int ks = 0; ks < nks; ++ks) {
+    const bool more = ks + 1 < nks;
+    if (more) {
+      load_w(ks + 1, qn, un);
+      st.load(xb, p.hidden, ks + 1, nbt);
+    }
+    const char* buf = (ks & 1) ? buf1 : buf0;
+    float sc[2][2];
+#pragma unroll
+    for (int mat = 0; mat < 2; ++mat)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) sc[mat][rb] = ue8m0_to_f32(uc[mat][rb]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bf16x8 a[2][2];
+#pragma unroll
+      for (int mat = 0; mat < 2; ++mat)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) a[mat][rb] = F::decode_j(qc[mat][rb], sc[mat][rb], j);
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) {
+        if (tb < nbt) {
+          const bf16x8 b = token_frag(buf, tb, j, g, r16);
+#pragma unroll
+          for (int mat = 0; mat < 2; ++mat)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+              acc[mat][rb][tb] = mfma_bf16(a[mat][rb], b, acc[mat][rb][tb]);
+        }
+      }
+      // keep one sub-step's fragments live at a time
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (more) st.store((ks & 1) ? buf0 : buf1, nbt);
+    __syncthreads();
+#pragma unroll
+    for (int mat = 0; mat < 2; ++mat)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+        for (int i = 0; i < Q; ++i) qc[mat][rb][i] = qn[mat][rb][i];
+        uc[mat][rb] = un[mat][rb];
+      }
+  }
+
+  // SwiGLU; lane holds rows 4g .. 4g+3 of each block for token column r16
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      const int n = tb * 16 + r16;
+      if (tb < nbt && n < it.m) {
+        bf16x4 hi, lo;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float gv = acc[0][rb][tb][r];
+          const float h = gv / (1.0f + expf(-gv)) * acc[1][rb][tb][r];
+          __bf16 a, b;
+          split_bf16(h, a, b);
+          hi[r] = a;
+          lo[r] = b;
+        }
+        const int64_t o =
+            (int64_t)(it.slot0 + n) * p.h_stride + it.row0 + 32 * wave + 16 * rb + 4 * g;
+        *reinterpret_cast<bf16x4*>(p.h_hi + o) = hi;
+        *reinterpret_cast<bf16x4*>(p.h_lo + o) = lo;
+      }
+    }
+}
+
+template <int WT, int TT>
+__global__ __launch_bounds__(kGThreads, 2) void gemm_gate_up_kernel(FfnParams p, int seg_lo,
+                                                                     int seg_hi) {
+  extern __shared__ __align__(16) char smem[];
+  __shared__ int s_pref[kSegMax + 1];
+  __shared__ int s_tmp[kGThreads / kWave];
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int total = item_prefix<TT, kGuRows, false>(p, seg_lo, seg_hi, s_pref, s_tmp);
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    const GItem it = find_item<TT, kGuRows, false>(p, seg_lo, seg_hi, s_pref, item);
+    gate_up_item<WT, TT>(p, it, smem, wave, lane);
+    __syncthreads();  // the LDS tiles are reused by the next item
+  }
+}
+
+// ------------------------------------------------------------- down
+
+template <int WT, int TT>
+__device__ __forceinline__ void down_item(const FfnParams& p, const GItem& it, char* smem,
+                                          int wave, int lane) {
+  using F = Fmt<WT>;
+  constexpr int Q = F::Q;
+  constexpr int TB = TT / 16;
+  constexpr int RB = kDnRows / (16 * 4);  // row blocks per wavefront
+  const int g = lane >> 4, r16 = lane & 15;
+  const bool shared = it.seg == p.n_experts;
+  const int kdim = shared ? p.shared_inter : p.inter;
+  const int64_t cb = F::row_bytes(kdim), sb = F::scale_row_bytes(kdim);
+  const int nks = kdim / 128;
+  const int nbt = uniform((it.m + 15) >> 4);
+  // row blocks of this wavefront inside the matrix (the last tile may be short)
+  const int wrow0 = it.row0 + 64 * wave;
+  const int nrb = uniform(max(0, min(RB, (p.hidden - wrow0) / 16)));
+
+  // the lane's row in block 0 (blocks past the matrix end reuse it and are
+  // not multiplied)
+  const int64_t r0 = wrow0 + r16 < p.hidden ? wrow0 + r16 : r16;
+  const int64_t lrow = (shared ? 0 : (int64_t)it.seg * p.hidden) + r0;
+  const int64_t lc = lrow * cb + F::code_off(0, g), ls = lrow * sb + F::scale_off(0, g);
+  const uint8_t* cbase = shared ? p.sdown_c : p.down_c;
+  const uint8_t* sbase = shared ? p.sdown_s : p.down_s;
+
+  Stage<TT> sh, sl;
+  sh.valid = 0;
+  {
+    const int n0 = threadIdx.x >> 4;
+#pragma unroll
+    for (int i = 0; i < Stage<TT>::kPer; ++i) {
+      const int n = n0 + 16 * i;
+      sh.row[i] = it.slot0 + (n < it.m ? n : 0);
+      sl.row[i] = sh.row[i];
+      if (n < it.m) sh.valid |= 1u << i;
+    }
+    sl.valid = sh.valid;
+  }
+
+  u32x4 qc[RB][Q], qn[RB][Q];
+  uint32_t uc[RB], un[RB];
+  auto load_w = [&](int ks, u32x4 (&q)[RB][Q], uint32_t (&u)[RB]) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int rr = rb < nrb ? rb : 0;
+#pragma unroll
+      for (int i = 0; i < Q; ++i)
+        q[rb][i] = load16(cbase + lc + 16 * rr * cb + F::code_off(ks, 0) + 16 * i);
+      u[rb] = sbase[ls + 16 * rr * sb + F::scale_off(ks, 0)];
+    }
+  };
+
+  f32x4 acc[RB][TB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) acc[rb][tb] = f32x4{0, 0, 0, 0};
+
+  constexpr int kTile = TT * kRow * 2;
+  char* bh[2] = {smem, smem + 2 * kTile};
+  char* bl[2] = {smem + kTile, smem + 3 * kTile};
+  load_w(0, qc, uc);
+  sh.load(p.h_hi, p.h_stride, 0, nbt);
+  sl.load(p.h_lo, p.h_stride, 0, nbt);
+  sh.store(bh[0], nbt);
+  sl.store(bl[0], nbt);
+  __syncthreads();
+  for (int ks = 0; ks < nks; ++ks) {
+    const bool more = ks + 1 < nks;
+    if (more) {
+      load_w(ks + 1, qn, un);
+      sh.load(p.h_hi, p.h_stride, ks + 1, nbt);
+      sl.load(p.h_lo, p.h_stride, ks + 1, nbt);
+    }
+    const char* bufh = bh[ks & 1];
+    const char* bufl = bl[ks & 1];
+    float sc[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) sc[rb] = ue8m0_to_f32(uc[rb]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bf16x8 a[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) a[rb] = F::decode_j(qc[rb], sc[rb], j);
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) {
+        if (tb < nbt) {
+          const bf16x8 fh = token_frag(bufh, tb, j, g, r16);
+          const bf16x8 fl = token_frag(bufl, tb, j, g, r16);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            if (rb < nrb) {
+              acc[rb][tb] = mfma_bf16(a[rb], fh, acc[rb][tb]);
+              acc[rb][tb] = mfma_bf16(a[rb], fl, acc[rb][tb]);
+            }
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (more) {
+      sh.store(bh[(ks + 1) & 1], nbt);
+      sl.store(bl[(ks + 1) & 1], nbt);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+      for (int i = 0; i < Q; ++i) qc[rb][i] = qn[rb][i];
+      uc[rb] = un[rb];
+    }
+  }
+
+  // routing weight of each token column, then the per-slot outputs
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb) {
+    const int n = tb * 16 + r16;
+    if (tb < nbt && n < it.m) {
+      const int64_t slot = it.slot0 + n;
+      const float w = shared ? 1.0f : p.topk_w[p.perm[slot]];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        if (rb < nrb) {
+          *reinterpret_cast<f32x4*>(p.obuf + slot * p.hidden + wrow0 + 16 * rb + 4 * g) =
+              acc[rb][tb] * w;
+        }
+      }
+    }
+  }
+}
+
+template <int WT, int TT>
+__global__ __launch_bounds__(kGThreads, 2) void gemm_down_kernel(FfnParams p, int seg_lo,
+                                                                  int seg_hi) {
+  extern __shared__ __align__(16) char smem[];
+  __shared__ int s_pref[kSegMax + 1];
+  __shared__ int s_tmp[kGThreads / kWave];
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int total = item_prefix<TT, kDnRows, true>(p, seg_lo, seg_hi, s_pref, s_tmp);
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    const GItem it = find_item<TT, kDnRows, true>(p, seg_lo, seg_hi, s_pref, item);
+    down_item<WT, TT>(p, it, smem, wave, lane);
+    __syncthreads();
+  }
+}
+
+template <typename... Params, typename... Args>
+hipError_t launch(void (*kernel)(Params...), dim3 grid, dim3 block, size_t lds,
+                  hipStream_t stream, hipEvent_t start, hipEvent_t stop, Args... args) {
+  static_assert(sizeof...(Params) == sizeof...(Args), "argument count");
+  void* argv[] = {const_cast<void*>(static_cast<const void*>(&args))...};
+  const hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block,
+                                          argv, lds, stream, start, stop, 0);
+  return e != hipSuccess ? e : hipGetLastError();
+}
+
+template <typename K>
+hipError_t allow_lds(K kernel) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
+}
+
+// Upper bound on the items of segments seg_lo .. seg_hi-1: routed token
+// tiles number at most N*k/TT + min(E, N*k); the shared expert has
+// ceil(N/TT).
+int64_t items_bound(const FfnParams& p, int seg_lo, int seg_hi, int tt, int rt, bool down) {
+  int64_t items = 0;
+  if (seg_lo < p.n_experts) {
+    const int64_t nk = (int64_t)p.n_tokens * p.top_k;
+    const int64_t tiles = nk / tt + (nk < p.n_experts ? nk : p.n_experts);
+    const int64_t rows = down ? p.hidden : p.inter;
+    items += tiles * ((rows + rt - 1) / rt);
+  }
+  if (seg_hi > p.n_experts) {
+    const int64_t rows = down ? p.hidden : p.shared_inter;
+    items += (p.n_tokens + tt - 1) / tt * ((rows + rt - 1) / rt);
+  }
+  return items;
+}
+
+constexpr int kGemmGrid = 256 * 2;  // 256 CUs, two workgroups each
+
+int grid_for(int64_t items) {
+  return (int)(items < kGemmGrid ? (items > 0 ? items : 1) : kGemmGrid);
+}
+
+template <int WT, int TT>
+hipError_t gate_up_range(const FfnParams& p, int seg_lo, int seg_hi, hipStream_t stream,
+                         hipEvent_t start, hipEvent_t stop) {
+  static const hipError_t attr = allow_lds(gemm_gate_up_kernel<WT, TT>);
+  if (attr != hipSuccess) return attr;
+  const int grid = grid_for(items_bound(p, seg_lo, seg_hi, TT, kGuRows, false));
+  return launch(gemm_gate_up_kernel<WT, TT>, dim3(grid), dim3(kGThreads),
+                (size_t)2 * TT * kRow * 2, stream, start, stop, p, seg_lo, seg_hi);
+}
+
+template <int WT, int TT>
+hipError_t down_range(const FfnParams& p, int seg_lo, int seg_hi, hipStream_t stream,
+                      hipEvent_t start, hipEvent_t stop) {
+  static const hipError_t attr = allow_lds(gemm_down_kernel<WT, TT>);
+  if (attr != hipSuccess) return attr;
+  const int grid = grid_for(items_bound(p, seg_lo, seg_hi, TT, kDnRows, true));
+  return launch(gemm_down_kernel<WT, TT>, dim3(grid), dim3(kGThreads), (size_t)4 * TT * kRow * 2,
+                stream, start, stop, p, seg_lo, seg_hi);
+}
+
+// Segments of one weight type go through one launch: everything at once when
+// the shared expert is stored like the routed ones, else the routed experts
+// and then the shared expert.
+template <typename Range>
+hipError_t by_type(const FfnParams& p, hipStream_t stream, hipEvent_t start, hipEvent_t stop,
+                   Range run) {
+  const int E = p.n_experts;
+  if (!p.has_shared || p.sw_type == p.w_type) return run(p.w_type, 0, E + p.has_shared, start, stop);
+  const hipError_t e = run(p.w_type, 0, E, start, nullptr);
+  if (e != hipSuccess) return e;
+  return run(p.sw_type, E, E + 1, nullptr, stop);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_gate_up(const FfnParams& p, hipStream_t stream, hipEvent_t start,
+                               hipEvent_t stop) {
+  return by_type(p, stream, start, stop, [&](int wt, int lo, int hi, hipEvent_t a, hipEvent_t b) {
+    return wt == MOE_W_MXFP4 ? gate_up_range<MOE_W_MXFP4, 112>(p, lo, hi, stream, a, b)
+                             : gate_up_range<MOE_W_FP8E4M3_B128, 64>(p, lo, hi, stream, a, b);
+  });
+}
+
+hipError_t launch_gemm_down(const FfnParams& p, hipStream_t stream, hipEvent_t start,
+                            hipEvent_t stop) {
+  return by_type(p, stream, start, stop, [&](int wt, int lo, int hi, hipEvent_t a, hipEvent_t b) {
+    return wt == MOE_W_MXFP4 ? down_range<MOE_W_MXFP4, 64>(p, lo, hi, stream, a, b)
+                             : down_range<MOE_W_FP8E4M3_B128, 64>(p, lo, hi, stream, a, b);
+  });
+}
+
+}  // namespace moe

@@ -53,5 +53,10 @@ hipError_t launch_ffn_gate_up(const FfnParams& p, hipStream_t stream, hipEvent_t
                               hipEvent_t stop);
 hipError_t launch_ffn_down(const FfnParams& p, hipStream_t stream, hipEvent_t start,
                            hipEvent_t stop);
+// grouped-GEMM kernels for batches in which experts see many tokens
+hipError_t launch_gemm_gate_up(const FfnParams& p, hipStream_t stream, hipEvent_t start,
+                               hipEvent_t stop);
+hipError_t launch_gemm_down(const FfnParams& p, hipStream_t stream, hipEvent_t start,
+                            hipEvent_t stop);
 
 }  // namespace moe
