@@ -47,7 +47,6 @@ namespace moe {
 namespace {
 
 constexpr int kGThreads = 256;
-constexpr int kRow = 136;  // bf16 per staged row: 128 + 8, so rows start on other banks
 constexpr int kGuRows = 128;  // intermediate rows per gate/up item
 constexpr int kDnRows = 256;  // hidden rows per down item
 constexpr int kSegMax = MOE_MAX_EXPERTS + 1;
@@ -131,37 +130,47 @@ __device__ __forceinline__ GItem find_item(const FfnParams& p, int seg_lo, int s
   return it;
 }
 
-// Token-operand staging: a tile of TT rows x 128 bf16 per reduction step.
-// Thread tid copies 16-byte chunk (tid & 15) of rows (tid >> 4) + 16 i; a
-// row that is not part of the tile is written as zeros.  Row offsets of
-// missing rows point at a valid row so that every load is unconditional.
+// Token-operand staging: a tile of TT rows x 128 bf16 (256 bytes) per
+// reduction step, copied straight from global memory into LDS (no register
+// round trip).  One wavefront copy instruction fills four rows: lane l lands
+// at byte 16 l of the block, i.e. row 4w + 16i + (l >> 4), 16-byte position
+// l & 15.  Positions are swizzled, chunk c of row n sits at position
+// c ^ (n & 15), so the sixteen rows that one fragment read touches hit
+// sixteen different bank groups; each lane therefore fetches the chunk that
+// belongs at its position.  Rows past the tile repeat a valid row: they only
+// feed token columns that the epilogue drops.
 template <int TT>
 struct Stage {
-  static constexpr int kPer = TT / 16;  // rows per thread
-  int row[kPer];                        // source row of each staged row
-  uint32_t valid;                       // bit i: row (tid >> 4) + 16 i exists
-  u32x4 v[kPer];
+  static constexpr int kPer = TT / 16;  // copy instructions per wavefront
+  int row[kPer];                        // source row of each copied row
+  int chunk;                            // source chunk of this lane
 
-  __device__ void load(const __bf16* base, int64_t stride, int ks, int nbt) {
-    const int c = (threadIdx.x & 15) * 8 + ks * 128;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i)
-      if (i < nbt) v[i] = load16(base + (int64_t)row[i] * stride + c);
-  }
-  __device__ void store(char* buf, int nbt) const {
-    const int n0 = threadIdx.x >> 4, c = (threadIdx.x & 15) * 8;
+  __device__ void init(int lane) { chunk = (lane & 15) ^ ((4 * wave_id() + (lane >> 4)) & 15); }
+  __device__ void copy(const __bf16* base, int64_t stride, int ks, char* buf, int nbt) const {
+    const int c = ks * 128 + chunk * 8;
+    char* dst = buf + (4 * wave_id()) * 256;
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
       if (i < nbt)
-        *reinterpret_cast<u32x4*>(buf + ((n0 + 16 * i) * kRow + c) * 2) =
-            ((valid >> i) & 1) ? v[i] : u32x4{0, 0, 0, 0};
+        __builtin_amdgcn_global_load_lds(base + (int64_t)row[i] * stride + c,
+                                         (__attribute__((address_space(3))) void*)(dst + i * 16 * 256),
+                                         16, 0, 0);
   }
 };
 
-// Token fragment of token block tb, sub-step j, from a staged step.
+// Token fragment of token block tb, sub-step j: row n = 16 tb + r16, chunk
+// 4g + j, at its swizzled position.
 __device__ __forceinline__ bf16x8 token_frag(const char* buf, int tb, int j, int g, int r16) {
-  return as_bf16x8(
-      *reinterpret_cast<const u32x4*>(buf + ((tb * 16 + r16) * kRow + 32 * g + 8 * j) * 2));
+  return as_bf16x8(*reinterpret_cast<const u32x4*>(buf + (tb * 16 + r16) * 256 +
+                                                     (((4 * g + j) ^ r16) << 4)));
+}
+
+// Wait until at most n vector memory operations of this wavefront are
+// outstanding (n < 16), leaving the other counters alone.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8));
 }
 
 // ------------------------------------------------------------- gate/up
@@ -172,6 +181,7 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
   using F = Fmt<WT>;
   constexpr int Q = F::Q;
   constexpr int TB = TT / 16;
+  constexpr int kLoads = 4 * (Q + 1);  // vector loads of one step's weights
   const int g = lane >> 4, r16 = lane & 15;
   const bool shared = it.seg == p.n_experts;
   const int rows = shared ? p.shared_inter : p.inter;
@@ -182,38 +192,44 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
 
   // the lane's rows: gate/up (mat) x two 16-row blocks (rb); row block 1
   // lies 16 rows after row block 0
-  const int64_t lrow =
-      (shared ? 0 : (int64_t)it.seg * rows) + it.row0 + 32 * wave + r16;
+  const int64_t lrow = (shared ? 0 : (int64_t)it.seg * rows) + it.row0 + 32 * wave + r16;
   const int64_t lc = lrow * cb + F::code_off(0, g), ls = lrow * sb + F::scale_off(0, g);
   const uint8_t* cbase[2] = {shared ? p.sgate_c : p.gate_c, shared ? p.sup_c : p.up_c};
   const uint8_t* sbase[2] = {shared ? p.sgate_s : p.gate_s, shared ? p.sup_s : p.up_s};
 
-  // activation rows of the tile (missing rows repeat the first one)
+  // activation rows copied by this lane (rows past the tile repeat row 0)
   Stage<TT> st;
-  st.valid = 0;
+  st.init(lane);
   {
-    const int n0 = threadIdx.x >> 4;
+    // all perm loads first (clamped into perm; the shared expert needs none)
+    int pv[Stage<TT>::kPer];
 #pragma unroll
     for (int i = 0; i < Stage<TT>::kPer; ++i) {
-      const int n = n0 + 16 * i;
+      const int n = 4 * wave + 16 * i + (lane >> 4);
+      pv[i] = p.perm[min(it.slot0 + (n < it.m ? n : 0), nk - 1)];
+    }
+#pragma unroll
+    for (int i = 0; i < Stage<TT>::kPer; ++i) {
+      const int n = 4 * wave + 16 * i + (lane >> 4);
       const int slot = it.slot0 + (n < it.m ? n : 0);
-      st.row[i] = shared ? slot - nk : p.perm[slot] / p.top_k;
-      if (n < it.m) st.valid |= 1u << i;
+      st.row[i] = shared ? slot - nk : pv[i] / p.top_k;
     }
   }
   const __bf16* xb = static_cast<const __bf16*>(p.x);
 
-  u32x4 qc[2][2][Q], qn[2][2][Q];
-  uint32_t uc[2][2], un[2][2];
+  // weight codes: the current step and the next
+  u32x4 q0[2][2][Q], q1[2][2][Q];
+  uint32_t u0[2][2], u1[2][2];
   auto load_w = [&](int ks, u32x4 (&q)[2][2][Q], uint32_t (&u)[2][2]) {
+    const int k = min(ks, nks - 1);  // past the end: reload the last step
 #pragma unroll
     for (int mat = 0; mat < 2; ++mat)
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
         for (int i = 0; i < Q; ++i)
-          q[mat][rb][i] = load16(cbase[mat] + lc + 16 * rb * cb + F::code_off(ks, 0) + 16 * i);
-        u[mat][rb] = sbase[mat][ls + 16 * rb * sb + F::scale_off(ks, 0)];
+          q[mat][rb][i] = load16(cbase[mat] + lc + 16 * rb * cb + F::code_off(k, 0) + 16 * i);
+        u[mat][rb] = sbase[mat][ls + 16 * rb * sb + F::scale_off(k, 0)];
       }
   };
 
@@ -225,35 +241,33 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) acc[mat][rb][tb] = f32x4{0, 0, 0, 0};
 
-  char* buf0 = smem;
-  char* buf1 = smem + TT * kRow * 2;
-  load_w(0, qc, uc);
-  st.load(xb, p.hidden, 0, nbt);
-  st.store(buf0, nbt);
+  // buffer b at smem + b * TT * 256 (offsets from smem keep LDS addressing)
+  auto buf = [&](int b) { return smem + (b & 1) * (TT * 256); };
+  load_w(0, q0, u0);
+  st.copy(xb, p.hidden, 0, buf(0), nbt);
+  wait_vm<0>();
   __syncthreads();
   for (int ks = 0; ks < nks; ++ks) {
-    const bool more = ks + 1 < nks;
-    if (more) {
-      load_w(ks + 1, qn, un);
-      st.load(xb, p.hidden, ks + 1, nbt);
-    }
-    const char* buf = (ks & 1) ? buf1 : buf0;
+    // step ks+1's weights and activations fly while step ks multiplies
+    load_w(ks + 1, q1, u1);
+    if (ks + 1 < nks) st.copy(xb, p.hidden, ks + 1, buf(ks + 1), nbt);
+    const char* cur = buf(ks);
     float sc[2][2];
 #pragma unroll
     for (int mat = 0; mat < 2; ++mat)
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) sc[mat][rb] = ue8m0_to_f32(uc[mat][rb]);
+      for (int rb = 0; rb < 2; ++rb) sc[mat][rb] = ue8m0_to_f32(u0[mat][rb]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       bf16x8 a[2][2];
 #pragma unroll
       for (int mat = 0; mat < 2; ++mat)
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) a[mat][rb] = F::decode_j(qc[mat][rb], sc[mat][rb], j);
+        for (int rb = 0; rb < 2; ++rb) a[mat][rb] = F::decode_j(q0[mat][rb], sc[mat][rb], j);
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) {
         if (tb < nbt) {
-          const bf16x8 b = token_frag(buf, tb, j, g, r16);
+          const bf16x8 b = token_frag(cur, tb, j, g, r16);
 #pragma unroll
           for (int mat = 0; mat < 2; ++mat)
 #pragma unroll
@@ -264,17 +278,18 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
       // keep one sub-step's fragments live at a time
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (more) st.store((ks & 1) ? buf0 : buf1, nbt);
+    wait_vm<0>();  // this wavefront's copies of step ks+1 have landed
     __syncthreads();
 #pragma unroll
     for (int mat = 0; mat < 2; ++mat)
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
-        for (int i = 0; i < Q; ++i) qc[mat][rb][i] = qn[mat][rb][i];
-        uc[mat][rb] = un[mat][rb];
+        for (int i = 0; i < Q; ++i) q0[mat][rb][i] = q1[mat][rb][i];
+        u0[mat][rb] = u1[mat][rb];
       }
   }
+  wait_vm<0>();  // the reloads past the end
 
   // SwiGLU; lane holds rows 4g .. 4g+3 of each block for token column r16
 #pragma unroll
@@ -288,10 +303,10 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
         for (int r = 0; r < 4; ++r) {
           const float gv = acc[0][rb][tb][r];
           const float h = gv / (1.0f + expf(-gv)) * acc[1][rb][tb][r];
-          __bf16 a, b;
-          split_bf16(h, a, b);
-          hi[r] = a;
-          lo[r] = b;
+          __bf16 x, y;
+          split_bf16(h, x, y);
+          hi[r] = x;
+          lo[r] = y;
         }
         const int64_t o =
             (int64_t)(it.slot0 + n) * p.h_stride + it.row0 + 32 * wave + 16 * rb + 4 * g;
@@ -325,6 +340,7 @@ __device__ __forceinline__ void down_item(const FfnParams& p, const GItem& it, c
   constexpr int Q = F::Q;
   constexpr int TB = TT / 16;
   constexpr int RB = kDnRows / (16 * 4);  // row blocks per wavefront
+  constexpr int kLoads = RB * (Q + 1);
   const int g = lane >> 4, r16 = lane & 15;
   const bool shared = it.seg == p.n_experts;
   const int kdim = shared ? p.shared_inter : p.inter;
@@ -343,30 +359,34 @@ __device__ __forceinline__ void down_item(const FfnParams& p, const GItem& it, c
   const uint8_t* cbase = shared ? p.sdown_c : p.down_c;
   const uint8_t* sbase = shared ? p.sdown_s : p.down_s;
 
-  Stage<TT> sh, sl;
-  sh.valid = 0;
-  {
-    const int n0 = threadIdx.x >> 4;
+  // h rows (slots) copied by this lane; rows past the tile repeat row 0
+  Stage<TT> st;
+  st.init(lane);
 #pragma unroll
-    for (int i = 0; i < Stage<TT>::kPer; ++i) {
-      const int n = n0 + 16 * i;
-      sh.row[i] = it.slot0 + (n < it.m ? n : 0);
-      sl.row[i] = sh.row[i];
-      if (n < it.m) sh.valid |= 1u << i;
-    }
-    sl.valid = sh.valid;
+  for (int i = 0; i < Stage<TT>::kPer; ++i) {
+    const int n = 4 * wave + 16 * i + (lane >> 4);
+    st.row[i] = it.slot0 + (n < it.m ? n : 0);
   }
 
-  u32x4 qc[RB][Q], qn[RB][Q];
-  uint32_t uc[RB], un[RB];
+  // routing weight of each token column, fetched now, used by the epilogue
+  float wcol[TB];
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb) {
+    const int n = min(tb * 16 + r16, it.m - 1);
+    wcol[tb] = shared ? 1.0f : p.topk_w[p.perm[it.slot0 + n]];
+  }
+
+  u32x4 q0[RB][Q], q1[RB][Q], q2[RB][Q];
+  uint32_t u0[RB], u1[RB], u2[RB];
   auto load_w = [&](int ks, u32x4 (&q)[RB][Q], uint32_t (&u)[RB]) {
+    const int k = min(ks, nks - 1);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const int rr = rb < nrb ? rb : 0;
 #pragma unroll
       for (int i = 0; i < Q; ++i)
-        q[rb][i] = load16(cbase + lc + 16 * rr * cb + F::code_off(ks, 0) + 16 * i);
-      u[rb] = sbase[ls + 16 * rr * sb + F::scale_off(ks, 0)];
+        q[rb][i] = load16(cbase + lc + 16 * rr * cb + F::code_off(k, 0) + 16 * i);
+      u[rb] = sbase[ls + 16 * rr * sb + F::scale_off(k, 0)];
     }
   };
 
@@ -376,37 +396,39 @@ __device__ __forceinline__ void down_item(const FfnParams& p, const GItem& it, c
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) acc[rb][tb] = f32x4{0, 0, 0, 0};
 
-  constexpr int kTile = TT * kRow * 2;
-  char* bh[2] = {smem, smem + 2 * kTile};
-  char* bl[2] = {smem + kTile, smem + 3 * kTile};
-  load_w(0, qc, uc);
-  sh.load(p.h_hi, p.h_stride, 0, nbt);
-  sl.load(p.h_lo, p.h_stride, 0, nbt);
-  sh.store(bh[0], nbt);
-  sl.store(bl[0], nbt);
+  constexpr int kTile = TT * 256;
+  // h_hi of step parity b at smem + 2b * kTile, h_lo right after it
+  auto bh = [&](int b) { return smem + (b & 1) * (2 * kTile); };
+  auto bl = [&](int b) { return smem + (b & 1) * (2 * kTile) + kTile; };
+  load_w(0, q0, u0);
+  load_w(1, q1, u1);
+  st.copy(p.h_hi, p.h_stride, 0, bh(0), nbt);
+  st.copy(p.h_lo, p.h_stride, 0, bl(0), nbt);
+  wait_vm<0>();
   __syncthreads();
   for (int ks = 0; ks < nks; ++ks) {
-    const bool more = ks + 1 < nks;
-    if (more) {
-      load_w(ks + 1, qn, un);
-      sh.load(p.h_hi, p.h_stride, ks + 1, nbt);
-      sl.load(p.h_lo, p.h_stride, ks + 1, nbt);
+    if (ks + 1 < nks) {
+      st.copy(p.h_hi, p.h_stride, ks + 1, bh(ks + 1), nbt);
+      st.copy(p.h_lo, p.h_stride, ks + 1, bl(ks + 1), nbt);
     }
-    const char* bufh = bh[ks & 1];
-    const char* bufl = bl[ks & 1];
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(ks + 2, q2, u2);
+    __builtin_amdgcn_sched_barrier(0);
+    const char* curh = bh(ks);
+    const char* curl = bl(ks);
     float sc[RB];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) sc[rb] = ue8m0_to_f32(uc[rb]);
+    for (int rb = 0; rb < RB; ++rb) sc[rb] = ue8m0_to_f32(u0[rb]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       bf16x8 a[RB];
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) a[rb] = F::decode_j(qc[rb], sc[rb], j);
+      for (int rb = 0; rb < RB; ++rb) a[rb] = F::decode_j(q0[rb], sc[rb], j);
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) {
         if (tb < nbt) {
-          const bf16x8 fh = token_frag(bufh, tb, j, g, r16);
-          const bf16x8 fl = token_frag(bufl, tb, j, g, r16);
+          const bf16x8 fh = token_frag(curh, tb, j, g, r16);
+          const bf16x8 fl = token_frag(curl, tb, j, g, r16);
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) {
             if (rb < nrb) {
@@ -418,18 +440,20 @@ __device__ __forceinline__ void down_item(const FfnParams& p, const GItem& it, c
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (more) {
-      sh.store(bh[(ks + 1) & 1], nbt);
-      sl.store(bl[(ks + 1) & 1], nbt);
-    }
+    wait_vm<kLoads>();
     __syncthreads();
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-      for (int i = 0; i < Q; ++i) qc[rb][i] = qn[rb][i];
-      uc[rb] = un[rb];
+      for (int i = 0; i < Q; ++i) {
+        q0[rb][i] = q1[rb][i];
+        q1[rb][i] = q2[rb][i];
+      }
+      u0[rb] = u1[rb];
+      u1[rb] = u2[rb];
     }
   }
+  wait_vm<0>();
 
   // routing weight of each token column, then the per-slot outputs
 #pragma unroll
@@ -437,7 +461,7 @@ __device__ __forceinline__ void down_item(const FfnParams& p, const GItem& it, c
     const int n = tb * 16 + r16;
     if (tb < nbt && n < it.m) {
       const int64_t slot = it.slot0 + n;
-      const float w = shared ? 1.0f : p.topk_w[p.perm[slot]];
+      const float w = wcol[tb];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         if (rb < nrb) {
@@ -511,7 +535,7 @@ hipError_t gate_up_range(const FfnParams& p, int seg_lo, int seg_hi, hipStream_t
   if (attr != hipSuccess) return attr;
   const int grid = grid_for(items_bound(p, seg_lo, seg_hi, TT, kGuRows, false));
   return launch(gemm_gate_up_kernel<WT, TT>, dim3(grid), dim3(kGThreads),
-                (size_t)2 * TT * kRow * 2, stream, start, stop, p, seg_lo, seg_hi);
+                (size_t)2 * TT * 256, stream, start, stop, p, seg_lo, seg_hi);
 }
 
 template <int WT, int TT>
@@ -520,7 +544,7 @@ hipError_t down_range(const FfnParams& p, int seg_lo, int seg_hi, hipStream_t st
   static const hipError_t attr = allow_lds(gemm_down_kernel<WT, TT>);
   if (attr != hipSuccess) return attr;
   const int grid = grid_for(items_bound(p, seg_lo, seg_hi, TT, kDnRows, true));
-  return launch(gemm_down_kernel<WT, TT>, dim3(grid), dim3(kGThreads), (size_t)4 * TT * kRow * 2,
+  return launch(gemm_down_kernel<WT, TT>, dim3(grid), dim3(kGThreads), (size_t)4 * TT * 256,
                 stream, start, stop, p, seg_lo, seg_hi);
 }
 
@@ -542,7 +566,7 @@ hipError_t by_type(const FfnParams& p, hipStream_t stream, hipEvent_t start, hip
 hipError_t launch_gemm_gate_up(const FfnParams& p, hipStream_t stream, hipEvent_t start,
                                hipEvent_t stop) {
   return by_type(p, stream, start, stop, [&](int wt, int lo, int hi, hipEvent_t a, hipEvent_t b) {
-    return wt == MOE_W_MXFP4 ? gate_up_range<MOE_W_MXFP4, 112>(p, lo, hi, stream, a, b)
+    return wt == MOE_W_MXFP4 ? gate_up_range<MOE_W_MXFP4, 128>(p, lo, hi, stream, a, b)
                              : gate_up_range<MOE_W_FP8E4M3_B128, 64>(p, lo, hi, stream, a, b);
   });
 }
