@@ -46,9 +46,10 @@
 namespace moe {
 namespace {
 
-constexpr int kGThreads = 256;
-constexpr int kGuRows = 128;  // intermediate rows per gate/up item
-constexpr int kDnRows = 256;  // hidden rows per down item
+constexpr int kGThreads = 256;  // four wavefronts, two workgroups per CU
+constexpr int kGWaves = kGThreads / kWave;
+constexpr int kGuRows = 32 * kGWaves;  // intermediate rows per gate/up item
+constexpr int kDnRows = 64 * kGWaves;  // hidden rows per down item
 constexpr int kSegMax = MOE_MAX_EXPERTS + 1;
 constexpr int kGemmLds = 72 * 1024;  // dynamic LDS of either kernel (two per CU)
 
@@ -133,28 +134,35 @@ __device__ __forceinline__ GItem find_item(const FfnParams& p, int seg_lo, int s
 // Token-operand staging: a tile of TT rows x 128 bf16 (256 bytes) per
 // reduction step, copied straight from global memory into LDS (no register
 // round trip).  One wavefront copy instruction fills four rows: lane l lands
-// at byte 16 l of the block, i.e. row 4w + 16i + (l >> 4), 16-byte position
-// l & 15.  Positions are swizzled, chunk c of row n sits at position
-// c ^ (n & 15), so the sixteen rows that one fragment read touches hit
-// sixteen different bank groups; each lane therefore fetches the chunk that
-// belongs at its position.  Rows past the tile repeat a valid row: they only
-// feed token columns that the epilogue drops.
+// at byte 16 l of the block.  In round i wavefront w fills rows
+// R i + 4w .. +3 (R = 4 * wavefronts), lane l row R i + 4w + (l >> 4),
+// 16-byte position l & 15.  Positions are swizzled, chunk c of row n sits at
+// position c ^ (n & 15), so the sixteen rows that one fragment read touches
+// hit sixteen different bank groups; each lane therefore fetches the chunk
+// that belongs at its position.  Only rows below 16 * nbt are copied; rows
+// past the tile repeat a valid row: they only feed token columns that the
+// epilogue drops.
 template <int TT>
 struct Stage {
-  static constexpr int kPer = TT / 16;  // copy instructions per wavefront
-  int row[kPer];                        // source row of each copied row
-  int chunk;                            // source chunk of this lane
+  static constexpr int kRound = 4 * kGWaves;             // rows per round
+  static constexpr int kPer = (TT + kRound - 1) / kRound;  // copy rounds
+  int row[kPer];                                          // source row per round
+  int chunk;                                              // source chunk of this lane
 
+  __device__ static int row_of(int i, int wave, int lane) {
+    return kRound * i + 4 * wave + (lane >> 4);
+  }
   __device__ void init(int lane) { chunk = (lane & 15) ^ ((4 * wave_id() + (lane >> 4)) & 15); }
   __device__ void copy(const __bf16* base, int64_t stride, int ks, char* buf, int nbt) const {
     const int c = ks * 128 + chunk * 8;
-    char* dst = buf + (4 * wave_id()) * 256;
+    const int w = wave_id();
+    char* dst = buf + (4 * w) * 256;
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
-      if (i < nbt)
-        __builtin_amdgcn_global_load_lds(base + (int64_t)row[i] * stride + c,
-                                         (__attribute__((address_space(3))) void*)(dst + i * 16 * 256),
-                                         16, 0, 0);
+      if (kRound * i + 4 * w < 16 * nbt)
+        __builtin_amdgcn_global_load_lds(
+            base + (int64_t)row[i] * stride + c,
+            (__attribute__((address_space(3))) void*)(dst + i * kRound * 256), 16, 0, 0);
   }
 };
 
@@ -173,26 +181,70 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8));
 }
 
+// End of a reduction step: this wavefront's copies into LDS have landed
+// (at most N later loads, the weights of a later step, still in flight),
+// then the workgroup barrier.  A plain barrier, not __syncthreads(): its
+// release fence would also wait for those later weight loads.  The LDS
+// reads of the step are complete here, since the MFMAs consumed them.
+template <int N>
+__device__ __forceinline__ void step_barrier() {
+  wait_vm<N>();
+  __builtin_amdgcn_s_barrier();
+}
+
+// Workgroups are dealt to the eight XCDs round-robin (workgroup b runs on
+// XCD b % 8), and each XCD has its own L2.  The item order is cut into eight
+// contiguous chunks, one per XCD: the row tiles of one expert (which share
+// its token rows) and the token tiles of one row tile (which share its
+// weights) then meet in the same L2.  Returns -1 for the padding indices.
+__device__ __forceinline__ int xcd_item(int i, int total) {
+  const int per = (total + 7) >> 3;
+  const int l = (i & 7) * per + (i >> 3);
+  return l < total ? l : -1;
+}
+
+// Calls f(std::integral_constant<int, n>) for the runtime n in 1..MAX.
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
+template <int MAX, typename Fn>
+__device__ __forceinline__ void dispatch_nbt(int n, Fn&& f) {
+  if constexpr (MAX >= 1) {
+    if (n == MAX) {
+      f(IntC<MAX>{});
+      return;
+    }
+    dispatch_nbt<MAX - 1>(n, f);
+  }
+}
+
 // ------------------------------------------------------------- gate/up
 
-template <int WT, int TT>
+// NBT = token blocks of the tile (ceil(m / 16)), a compile-time constant so
+// that a step's fragment reads and MFMAs form one branch-free block.
+template <int WT, int TT, int NBT>
 __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it, char* smem,
                                              int wave, int lane) {
   using F = Fmt<WT>;
   constexpr int Q = F::Q;
-  constexpr int TB = TT / 16;
+  constexpr int TB = NBT;
   constexpr int kLoads = 4 * (Q + 1);  // vector loads of one step's weights
   const int g = lane >> 4, r16 = lane & 15;
   const bool shared = it.seg == p.n_experts;
   const int rows = shared ? p.shared_inter : p.inter;
   const int64_t cb = F::row_bytes(p.hidden), sb = F::scale_row_bytes(p.hidden);
   const int nks = p.hidden / 128;
-  const int nbt = uniform((it.m + 15) >> 4);
+  constexpr int nbt = NBT;
   const int nk = p.n_tokens * p.top_k;
 
   // the lane's rows: gate/up (mat) x two 16-row blocks (rb); row block 1
-  // lies 16 rows after row block 0
-  const int64_t lrow = (shared ? 0 : (int64_t)it.seg * rows) + it.row0 + 32 * wave + r16;
+  // lies 16 rows after row block 0.  A wavefront past the matrix end (the
+  // last row tile of a matrix whose rows are not a multiple of kGuRows)
+  // reads row block 0 of the tile and stores nothing.
+  const int wrow = it.row0 + 32 * wave;
+  const bool live = wrow < rows;
+  const int64_t lrow = (shared ? 0 : (int64_t)it.seg * rows) + (live ? wrow : it.row0) + r16;
   const int64_t lc = lrow * cb + F::code_off(0, g), ls = lrow * sb + F::scale_off(0, g);
   const uint8_t* cbase[2] = {shared ? p.sgate_c : p.gate_c, shared ? p.sup_c : p.up_c};
   const uint8_t* sbase[2] = {shared ? p.sgate_s : p.gate_s, shared ? p.sup_s : p.up_s};
@@ -205,21 +257,21 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
     int pv[Stage<TT>::kPer];
 #pragma unroll
     for (int i = 0; i < Stage<TT>::kPer; ++i) {
-      const int n = 4 * wave + 16 * i + (lane >> 4);
+      const int n = Stage<TT>::row_of(i, wave, lane);
       pv[i] = p.perm[min(it.slot0 + (n < it.m ? n : 0), nk - 1)];
     }
 #pragma unroll
     for (int i = 0; i < Stage<TT>::kPer; ++i) {
-      const int n = 4 * wave + 16 * i + (lane >> 4);
+      const int n = Stage<TT>::row_of(i, wave, lane);
       const int slot = it.slot0 + (n < it.m ? n : 0);
       st.row[i] = shared ? slot - nk : pv[i] / p.top_k;
     }
   }
   const __bf16* xb = static_cast<const __bf16*>(p.x);
 
-  // weight codes: the current step and the next
-  u32x4 q0[2][2][Q], q1[2][2][Q];
-  uint32_t u0[2][2], u1[2][2];
+  // weight codes: the current step and the next two
+  u32x4 q0[2][2][Q], q1[2][2][Q], q2[2][2][Q];
+  uint32_t u0[2][2], u1[2][2], u2[2][2];
   auto load_w = [&](int ks, u32x4 (&q)[2][2][Q], uint32_t (&u)[2][2]) {
     const int k = min(ks, nks - 1);  // past the end: reload the last step
 #pragma unroll
@@ -244,49 +296,63 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
   // buffer b at smem + b * TT * 256 (offsets from smem keep LDS addressing)
   auto buf = [&](int b) { return smem + (b & 1) * (TT * 256); };
   load_w(0, q0, u0);
+  load_w(1, q1, u1);
   st.copy(xb, p.hidden, 0, buf(0), nbt);
   wait_vm<0>();
   __syncthreads();
   for (int ks = 0; ks < nks; ++ks) {
-    // step ks+1's weights and activations fly while step ks multiplies
-    load_w(ks + 1, q1, u1);
+    // step ks+1's activations, then step ks+2's weights: the end-of-step
+    // wait lets the weights stay in flight
     if (ks + 1 < nks) st.copy(xb, p.hidden, ks + 1, buf(ks + 1), nbt);
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(ks + 2, q2, u2);
+    __builtin_amdgcn_sched_barrier(0);
     const char* cur = buf(ks);
     float sc[2][2];
 #pragma unroll
     for (int mat = 0; mat < 2; ++mat)
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) sc[mat][rb] = ue8m0_to_f32(u0[mat][rb]);
+    // sub-step j+1 is decoded while sub-step j multiplies, so the converts
+    // overlap the matrix-core work
+    bf16x8 a[2][2][2];
+#pragma unroll
+    for (int mat = 0; mat < 2; ++mat)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) a[0][mat][rb] = F::decode_j(q0[mat][rb], sc[mat][rb], 0);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      bf16x8 a[2][2];
+      if (j + 1 < 4) {
 #pragma unroll
-      for (int mat = 0; mat < 2; ++mat)
+        for (int mat = 0; mat < 2; ++mat)
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) a[mat][rb] = F::decode_j(q0[mat][rb], sc[mat][rb], j);
+          for (int rb = 0; rb < 2; ++rb)
+            a[(j + 1) & 1][mat][rb] = F::decode_j(q0[mat][rb], sc[mat][rb], j + 1);
+      }
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) {
-        if (tb < nbt) {
-          const bf16x8 b = token_frag(cur, tb, j, g, r16);
+        const bf16x8 b = token_frag(cur, tb, j, g, r16);
 #pragma unroll
-          for (int mat = 0; mat < 2; ++mat)
+        for (int mat = 0; mat < 2; ++mat)
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-              acc[mat][rb][tb] = mfma_bf16(a[mat][rb], b, acc[mat][rb][tb]);
-        }
+          for (int rb = 0; rb < 2; ++rb)
+            acc[mat][rb][tb] = mfma_bf16(a[j & 1][mat][rb], b, acc[mat][rb][tb]);
       }
-      // keep one sub-step's fragments live at a time
+      // keep two sub-steps' fragments live at a time
       __builtin_amdgcn_sched_barrier(0);
     }
-    wait_vm<0>();  // this wavefront's copies of step ks+1 have landed
-    __syncthreads();
+    step_barrier<kLoads>();
 #pragma unroll
     for (int mat = 0; mat < 2; ++mat)
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
-        for (int i = 0; i < Q; ++i) q0[mat][rb][i] = q1[mat][rb][i];
+        for (int i = 0; i < Q; ++i) {
+          q0[mat][rb][i] = q1[mat][rb][i];
+          q1[mat][rb][i] = q2[mat][rb][i];
+        }
         u0[mat][rb] = u1[mat][rb];
+        u1[mat][rb] = u2[mat][rb];
       }
   }
   wait_vm<0>();  // the reloads past the end
@@ -297,7 +363,7 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
       const int n = tb * 16 + r16;
-      if (tb < nbt && n < it.m) {
+      if (live && tb < nbt && n < it.m) {
         bf16x4 hi, lo;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -324,29 +390,34 @@ __global__ __launch_bounds__(kGThreads, 2) void gemm_gate_up_kernel(FfnParams p,
   __shared__ int s_tmp[kGThreads / kWave];
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int total = item_prefix<TT, kGuRows, false>(p, seg_lo, seg_hi, s_pref, s_tmp);
-  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+  const int slots = (total + 7) & ~7;
+  for (int i = blockIdx.x; i < slots; i += gridDim.x) {
+    const int item = xcd_item(i, total);
+    if (item < 0) continue;
     const GItem it = find_item<TT, kGuRows, false>(p, seg_lo, seg_hi, s_pref, item);
-    gate_up_item<WT, TT>(p, it, smem, wave, lane);
+    dispatch_nbt<TT / 16>((it.m + 15) >> 4, [&](auto nb) {
+      gate_up_item<WT, TT, decltype(nb)::value>(p, it, smem, wave, lane);
+    });
     __syncthreads();  // the LDS tiles are reused by the next item
   }
 }
 
 // ------------------------------------------------------------- down
 
-template <int WT, int TT>
+template <int WT, int TT, int NBT>
 __device__ __forceinline__ void down_item(const FfnParams& p, const GItem& it, char* smem,
                                           int wave, int lane) {
   using F = Fmt<WT>;
   constexpr int Q = F::Q;
-  constexpr int TB = TT / 16;
-  constexpr int RB = kDnRows / (16 * 4);  // row blocks per wavefront
+  constexpr int TB = NBT;
+  constexpr int RB = kDnRows / (16 * kGWaves);  // row blocks per wavefront
   constexpr int kLoads = RB * (Q + 1);
   const int g = lane >> 4, r16 = lane & 15;
   const bool shared = it.seg == p.n_experts;
   const int kdim = shared ? p.shared_inter : p.inter;
   const int64_t cb = F::row_bytes(kdim), sb = F::scale_row_bytes(kdim);
   const int nks = kdim / 128;
-  const int nbt = uniform((it.m + 15) >> 4);
+  constexpr int nbt = NBT;
   // row blocks of this wavefront inside the matrix (the last tile may be short)
   const int wrow0 = it.row0 + 64 * wave;
   const int nrb = uniform(max(0, min(RB, (p.hidden - wrow0) / 16)));
@@ -364,7 +435,7 @@ __device__ __forceinline__ void down_item(const FfnParams& p, const GItem& it, c
   st.init(lane);
 #pragma unroll
   for (int i = 0; i < Stage<TT>::kPer; ++i) {
-    const int n = 4 * wave + 16 * i + (lane >> 4);
+    const int n = Stage<TT>::row_of(i, wave, lane);
     st.row[i] = it.slot0 + (n < it.m ? n : 0);
   }
 
@@ -419,29 +490,30 @@ __device__ __forceinline__ void down_item(const FfnParams& p, const GItem& it, c
     float sc[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) sc[rb] = ue8m0_to_f32(u0[rb]);
+    bf16x8 a[2][RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) a[0][rb] = F::decode_j(q0[rb], sc[rb], 0);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      bf16x8 a[RB];
+      if (j + 1 < 4) {
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) a[rb] = F::decode_j(q0[rb], sc[rb], j);
+        for (int rb = 0; rb < RB; ++rb) a[(j + 1) & 1][rb] = F::decode_j(q0[rb], sc[rb], j + 1);
+      }
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) {
-        if (tb < nbt) {
-          const bf16x8 fh = token_frag(curh, tb, j, g, r16);
-          const bf16x8 fl = token_frag(curl, tb, j, g, r16);
+        const bf16x8 fh = token_frag(curh, tb, j, g, r16);
+        const bf16x8 fl = token_frag(curl, tb, j, g, r16);
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb) {
-            if (rb < nrb) {
-              acc[rb][tb] = mfma_bf16(a[rb], fh, acc[rb][tb]);
-              acc[rb][tb] = mfma_bf16(a[rb], fl, acc[rb][tb]);
-            }
+        for (int rb = 0; rb < RB; ++rb) {
+          if (rb < nrb) {
+            acc[rb][tb] = mfma_bf16(a[j & 1][rb], fh, acc[rb][tb]);
+            acc[rb][tb] = mfma_bf16(a[j & 1][rb], fl, acc[rb][tb]);
           }
         }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    wait_vm<kLoads>();
-    __syncthreads();
+    step_barrier<kLoads>();
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
@@ -481,9 +553,14 @@ __global__ __launch_bounds__(kGThreads, 2) void gemm_down_kernel(FfnParams p, in
   __shared__ int s_tmp[kGThreads / kWave];
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int total = item_prefix<TT, kDnRows, true>(p, seg_lo, seg_hi, s_pref, s_tmp);
-  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+  const int slots = (total + 7) & ~7;
+  for (int i = blockIdx.x; i < slots; i += gridDim.x) {
+    const int item = xcd_item(i, total);
+    if (item < 0) continue;
     const GItem it = find_item<TT, kDnRows, true>(p, seg_lo, seg_hi, s_pref, item);
-    down_item<WT, TT>(p, it, smem, wave, lane);
+    dispatch_nbt<TT / 16>((it.m + 15) >> 4, [&](auto nb) {
+      down_item<WT, TT, decltype(nb)::value>(p, it, smem, wave, lane);
+    });
     __syncthreads();
   }
 }
@@ -566,7 +643,7 @@ hipError_t by_type(const FfnParams& p, hipStream_t stream, hipEvent_t start, hip
 hipError_t launch_gemm_gate_up(const FfnParams& p, hipStream_t stream, hipEvent_t start,
                                hipEvent_t stop) {
   return by_type(p, stream, start, stop, [&](int wt, int lo, int hi, hipEvent_t a, hipEvent_t b) {
-    return wt == MOE_W_MXFP4 ? gate_up_range<MOE_W_MXFP4, 128>(p, lo, hi, stream, a, b)
+    return wt == MOE_W_MXFP4 ? gate_up_range<MOE_W_MXFP4, 112>(p, lo, hi, stream, a, b)
                              : gate_up_range<MOE_W_FP8E4M3_B128, 64>(p, lo, hi, stream, a, b);
   });
 }
