@@ -48,11 +48,25 @@ DEFAULTS = {  # workload: (steps, warmup, copies, pool, event_every)
     "tiny": (2000, 100, 1, 8, 8),
 }
 
-# Traffic of the gate/up kernel on decode1 measured with rocprofv3 --pmc
-# (FETCH_SIZE and WRITE_SIZE, KiB per dispatch) and scaled by the factor that
-# makes the same counters read a plain copy of known size correctly; None
-# until measured for the current kernel.
-GATE_UP_TRAFFIC = {}
+# HBM traffic of the gate/up kernel per launch, from two rocprofv3 --pmc
+# passes over this script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch,
+# averaged over the timed dispatches), each scaled by what the same counter
+# reads for a plain 256 MiB device copy run in the same process
+# (--copy-mib 256): FETCH_SIZE read 131083.5 KiB for 262144 KiB read,
+# WRITE_SIZE read 262144 KiB for 262144 KiB written.  Only workloads whose
+# gate/up kernel is unchanged since the counters were taken are listed.
+FETCH_SCALE = 262144.0 / 131083.5
+WRITE_SCALE = 1.0
+GATE_UP_TRAFFIC_KIB = {  # workload: (FETCH_SIZE, WRITE_SIZE) per dispatch
+    "decode1": (30622.1, 56.0),
+}
+
+
+def gate_up_traffic(name):
+    kib = GATE_UP_TRAFFIC_KIB.get(name)
+    if kib is None:
+        return None
+    return (kib[0] * FETCH_SCALE + kib[1] * WRITE_SCALE) * 1024.0
 
 
 def proj_bytes(wtype: str, rows: int, cols: int) -> int:
@@ -91,9 +105,10 @@ def workload_costs(wl, counts_list):
         path += g + dd + route_in + n * wl.top_k * 8
         flops += 2.0 * (3 * i * h) * (n * wl.top_k) + 2.0 * (3 * si * h) * n
     k = len(counts_list)
+    gu_flops = 2.0 * (2 * i * h) * (n * wl.top_k) + 2.0 * (2 * si * h) * n
     return {"gate_up_bytes": gu / k, "down_bytes": dn / k, "path_bytes": path / k,
-            "path_flops": flops / k, "per_routed_gate_up_bytes": per_routed_gu,
-            "shared_gate_up_bytes": sh_gu}
+            "path_flops": flops / k, "gate_up_flops": gu_flops,
+            "per_routed_gate_up_bytes": per_routed_gu, "shared_gate_up_bytes": sh_gu}
 
 
 class Runner:
@@ -254,6 +269,9 @@ def main():
     ap.add_argument("--event-every", type=int, default=None,
                     help="record the per-kernel events on every n-th timed step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="before the warm-up, copy this many MiB once with a plain device "
+                         "copy kernel (a known byte count for calibrating memory counters)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()
 
@@ -291,6 +309,15 @@ def main():
     print("setup %.1f s: %d layer copies, %d inputs" % (time.perf_counter() - t0, copies, n_pool),
           file=sys.stderr, flush=True)
 
+    if args.copy_mib > 0:
+        # one read and one write of exactly copy_mib MiB, outside the timed region
+        n = args.copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for s in range(warmup):
         runner.step(s)
     torch.cuda.synchronize()
@@ -317,10 +344,15 @@ def main():
 
     ms_per_step = elapsed / steps * 1e3
     tokens_per_s = wl.n_tokens * steps / elapsed
+    # the gate/up kernel's roof: HBM below the ridge point, the bf16 MFMA
+    # peak above it (its contraction runs in bf16)
+    intensity = costs["gate_up_flops"] / costs["gate_up_bytes"]
+    mfma_bound = intensity > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
     achieved = costs["gate_up_bytes"] / gu_avg_s / 1e9
+    gu_tflops = costs["gate_up_flops"] / gu_avg_s / 1e12
     path_gbps = costs["path_bytes"] / (elapsed / steps) / 1e9
     path_tflops = costs["path_flops"] / (elapsed / steps) / 1e12
-    traffic = GATE_UP_TRAFFIC.get(wl.name)
+    traffic = gate_up_traffic(wl.name)
     result = {
         "metric": METRIC,
         "value": tokens_per_s,
@@ -343,14 +375,16 @@ def main():
             "n_tokens": wl.n_tokens,
         },
         "roofline": {
-            "kernel": "gate_up_kernel (moe_ffn_gate_up)",
-            "bound": "hbm",
-            "achieved": achieved,
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBPS,
+            "kernel": "gate/up + SwiGLU stage (moe_ffn_gate_up)",
+            "bound": "mfma" if mfma_bound else "hbm",
+            "achieved": gu_tflops if mfma_bound else achieved,
+            "peak": MFMA_BF16_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBPS,
+            "unit": "TFLOP/s" if mfma_bound else "GB/s",
+            "frac": gu_tflops / MFMA_BF16_PEAK_TFLOPS if mfma_bound else achieved / HBM_PEAK_GBPS,
             "traffic": traffic,
             "bytes_per_launch": costs["gate_up_bytes"],
+            "flops_per_launch": costs["gate_up_flops"],
+            "flop_per_byte": intensity,
             "avg_launch_us": gu_avg_s * 1e6,
             "timed_launches": len(sampled),
         },
