@@ -14,7 +14,9 @@ pool, so no expert is served from the 256 MB last-level cache or the L2s.
 Prints ONE JSON line.  `value` is tokens/s over the K timed steps
 (wall clock, synchronised on both sides).  `roofline` is for the dominant
 kernel (gate/up): algorithmic bytes per launch over its average duration
-measured with HIP events on the launch stream inside the timed region.  The
+measured with HIP events on the launch stream inside the timed region (at
+one token the whole layer is one kernel, and that kernel is the one
+reported).  The
 kernels record those events from their own dispatch packets; recording them
 costs the host several microseconds per step, so at decode sizes (where the
 host would otherwise fall behind the GPU) only every --event-every-th timed
@@ -48,22 +50,21 @@ DEFAULTS = {  # workload: (steps, warmup, copies, pool, event_every)
     "tiny": (2000, 100, 1, 8, 8),
 }
 
-# HBM traffic of the gate/up kernel per launch, from two rocprofv3 --pmc
+# HBM traffic of the roofline kernel per launch, from two rocprofv3 --pmc
 # passes over this script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch,
 # averaged over the timed dispatches), each scaled by what the same counter
 # reads for a plain 256 MiB device copy run in the same process
 # (--copy-mib 256): FETCH_SIZE read 131083.5 KiB for 262144 KiB read,
 # WRITE_SIZE read 262144 KiB for 262144 KiB written.  Only workloads whose
-# gate/up kernel is unchanged since the counters were taken are listed.
+# roofline kernel is unchanged since the counters were taken are listed.
 FETCH_SCALE = 262144.0 / 131083.5
 WRITE_SCALE = 1.0
-GATE_UP_TRAFFIC_KIB = {  # workload: (FETCH_SIZE, WRITE_SIZE) per dispatch
-    "decode1": (30622.1, 56.0),
+KERNEL_TRAFFIC_KIB = {  # workload: (FETCH_SIZE, WRITE_SIZE) per dispatch
 }
 
 
-def gate_up_traffic(name):
-    kib = GATE_UP_TRAFFIC_KIB.get(name)
+def kernel_traffic(name):
+    kib = KERNEL_TRAFFIC_KIB.get(name)
     if kib is None:
         return None
     return (kib[0] * FETCH_SCALE + kib[1] * WRITE_SCALE) * 1024.0
@@ -156,6 +157,21 @@ class Runner:
                     P(item["tid2w"].data_ptr()), item["tid2eid"].shape[0], e, k,
                     P(self.ids.data_ptr()), P(self.w.data_ptr()), None, s)),
                     ("moe_group", self.group_args)])
+        # single-token learned routing: the whole layer is one moe_forward call
+        # (one fused kernel); its outputs land in one set of buffers
+        x_type_c = B.MOE_ACT_F32 if wl.act == "f32" else B.MOE_ACT_BF16
+        self.fused = (wl.routing == "learned" and
+                      self.L.moe_forward_single_kernel(ctypes.byref(layers[0].c), n,
+                                                       x_type_c) == 1)
+        self.fwd_args = {}
+        if self.fused:
+            self.fwd = B.ForwardBuffers(layers[0], n, dev)
+            for c, layer in enumerate(layers):
+                for r, item in enumerate(pool):
+                    self.fwd_args[(c, r)] = (
+                        [ctypes.byref(layer.c), P(item["logits"].data_ptr()),
+                         ctypes.c_float(wl.routed_scale), P(item["x"].data_ptr()), x_type, n]
+                        + self.fwd.args() + [s])
         self.ffn_args = {}
         for c, layer in enumerate(layers):
             for r, item in enumerate(pool):
@@ -167,10 +183,16 @@ class Runner:
 
     def step(self, s, ev=None):
         """One pass of the path; ``ev`` = four events that the library
-        records from the gate/up and down kernel dispatches themselves."""
+        records from the kernel dispatches themselves: gate/up start and stop,
+        down start and stop, or (single fused kernel) its start and stop."""
         c = s % len(self.layers)
         r = s % len(self.pool)
         L = self.L
+        if self.fused:
+            evs = (None, None) if ev is None else ev[:2]
+            if L.moe_forward_timed(*self.fwd_args[(c, r)], *evs):
+                raise RuntimeError("moe_forward failed in step %d" % s)
+            return
         st = 0
         for name, args in self.route_args[r]:
             st |= getattr(L, name)(*args)
@@ -335,24 +357,32 @@ def main():
     elapsed = time.perf_counter() - t_start
 
     gate_up_ms = [e[0].elapsed_ms(e[1]) for e in evs]
-    down_ms = [e[2].elapsed_ms(e[3]) for e in evs]
     gu_avg_s = float(np.mean(gate_up_ms)) / 1e3
-    dn_avg_s = float(np.mean(down_ms)) / 1e3
+    dn_avg_s = float("nan") if runner.fused else float(np.mean(
+        [e[2].elapsed_ms(e[3]) for e in evs])) / 1e3
     counts_list = routed_counts(runner, n_pool)
     used = [counts_list[(warmup + j) % n_pool] for j in range(steps)]
     costs = workload_costs(wl, used)
 
     ms_per_step = elapsed / steps * 1e3
     tokens_per_s = wl.n_tokens * steps / elapsed
-    # the gate/up kernel's roof: HBM below the ridge point, the bf16 MFMA
-    # peak above it (its contraction runs in bf16)
-    intensity = costs["gate_up_flops"] / costs["gate_up_bytes"]
+    if runner.fused:
+        # one kernel does the whole layer: its roof is HBM for all the
+        # layer's bytes
+        kernel_name = "decode_fused_kernel (moe_forward: route + group + FFN)"
+        k_bytes, k_flops = costs["path_bytes"], costs["path_flops"]
+    else:
+        kernel_name = "gate/up + SwiGLU stage (moe_ffn_gate_up)"
+        k_bytes, k_flops = costs["gate_up_bytes"], costs["gate_up_flops"]
+    # HBM below the ridge point, the bf16 MFMA peak above it (the
+    # contractions run in bf16)
+    intensity = k_flops / k_bytes
     mfma_bound = intensity > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
-    achieved = costs["gate_up_bytes"] / gu_avg_s / 1e9
-    gu_tflops = costs["gate_up_flops"] / gu_avg_s / 1e12
+    achieved = k_bytes / gu_avg_s / 1e9
+    gu_tflops = k_flops / gu_avg_s / 1e12
     path_gbps = costs["path_bytes"] / (elapsed / steps) / 1e9
     path_tflops = costs["path_flops"] / (elapsed / steps) / 1e12
-    traffic = gate_up_traffic(wl.name)
+    traffic = kernel_traffic(wl.name)
     result = {
         "metric": METRIC,
         "value": tokens_per_s,
@@ -375,20 +405,20 @@ def main():
             "n_tokens": wl.n_tokens,
         },
         "roofline": {
-            "kernel": "gate/up + SwiGLU stage (moe_ffn_gate_up)",
+            "kernel": kernel_name,
             "bound": "mfma" if mfma_bound else "hbm",
             "achieved": gu_tflops if mfma_bound else achieved,
             "peak": MFMA_BF16_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBPS,
             "unit": "TFLOP/s" if mfma_bound else "GB/s",
             "frac": gu_tflops / MFMA_BF16_PEAK_TFLOPS if mfma_bound else achieved / HBM_PEAK_GBPS,
             "traffic": traffic,
-            "bytes_per_launch": costs["gate_up_bytes"],
-            "flops_per_launch": costs["gate_up_flops"],
+            "bytes_per_launch": k_bytes,
+            "flops_per_launch": k_flops,
             "flop_per_byte": intensity,
             "avg_launch_us": gu_avg_s * 1e6,
             "timed_launches": len(sampled),
         },
-        "down_kernel": {
+        "down_kernel": None if runner.fused else {
             "bytes_per_launch": costs["down_bytes"],
             "avg_launch_us": dn_avg_s * 1e6,
             "achieved_GBps": costs["down_bytes"] / dn_avg_s / 1e9,
@@ -402,10 +432,15 @@ def main():
             "mfma_bf16_frac": path_tflops / MFMA_BF16_PEAK_TFLOPS,
         },
     }
-    print("timed %d steps in %.3f s: %.2f us/step, gate/up %.2f us (%.0f GB/s), down %.2f us "
-          "(%.0f GB/s), path %.0f GB/s"
-          % (steps, elapsed, ms_per_step * 1e3, gu_avg_s * 1e6, achieved, dn_avg_s * 1e6,
-             costs["down_bytes"] / dn_avg_s / 1e9, path_gbps), file=sys.stderr, flush=True)
+    if runner.fused:
+        print("timed %d steps in %.3f s: %.2f us/step, fused kernel %.2f us (%.0f GB/s), "
+              "path %.0f GB/s" % (steps, elapsed, ms_per_step * 1e3, gu_avg_s * 1e6, achieved,
+                                  path_gbps), file=sys.stderr, flush=True)
+    else:
+        print("timed %d steps in %.3f s: %.2f us/step, gate/up %.2f us (%.0f GB/s), down %.2f us "
+              "(%.0f GB/s), path %.0f GB/s"
+              % (steps, elapsed, ms_per_step * 1e3, gu_avg_s * 1e6, achieved, dn_avg_s * 1e6,
+                 costs["down_bytes"] / dn_avg_s / 1e9, path_gbps), file=sys.stderr, flush=True)
     del runner, layers, pool
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:

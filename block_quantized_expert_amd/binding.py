@@ -18,12 +18,15 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "lib
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE = range(5)
 MOE_ACT_F32, MOE_ACT_BF16 = 0, 1
 MOE_W_MXFP4, MOE_W_FP8E4M3_B128 = 0, 1
-MOE_DEVERR_EXPERT_ID, MOE_DEVERR_TOKEN_ID = 1, 2
+MOE_DEVERR_EXPERT_ID, MOE_DEVERR_TOKEN_ID, MOE_DEVERR_SYNC = 1, 2, 4
+MOE_FORWARD_SYNC_BYTES = 53248
 
 # every symbol include/moe.h declares
 EXPORTED = ["moe_route", "moe_route_hash", "moe_route_group", "moe_group_workspace_bytes",
             "moe_group", "moe_ffn_workspace_bytes", "moe_ffn_forward", "moe_ffn_gate_up",
-            "moe_ffn_down", "moe_ffn_forward_timed", "moe_status_string"]
+            "moe_ffn_down", "moe_ffn_forward_timed", "moe_forward_workspace_bytes",
+            "moe_forward_single_kernel", "moe_forward_workspace_init", "moe_forward",
+            "moe_forward_timed", "moe_status_string"]
 
 WEIGHT_TYPES = {"mxfp4": MOE_W_MXFP4, "fp8_e4m3_b128": MOE_W_FP8E4M3_B128}
 
@@ -74,6 +77,16 @@ def lib() -> ctypes.CDLL:
         for name in ("moe_route", "moe_route_hash", "moe_route_group", "moe_group",
                      "moe_ffn_forward", "moe_ffn_gate_up", "moe_ffn_down",
                      "moe_ffn_forward_timed"):
+            getattr(L, name).restype = ctypes.c_int
+        L.moe_forward_workspace_bytes.argtypes = [ctypes.POINTER(MoeLayer), I]
+        L.moe_forward_workspace_bytes.restype = S
+        L.moe_forward_workspace_init.argtypes = [P, S, P]
+        L.moe_forward_single_kernel.argtypes = [ctypes.POINTER(MoeLayer), I, I]
+        L.moe_forward_single_kernel.restype = ctypes.c_int
+        fwd = [ctypes.POINTER(MoeLayer), P, F, P, I, I, P, P, P, P, P, P, P, P, S, P, P]
+        L.moe_forward.argtypes = fwd
+        L.moe_forward_timed.argtypes = fwd + [P, P]
+        for name in ("moe_forward_workspace_init", "moe_forward", "moe_forward_timed"):
             getattr(L, name).restype = ctypes.c_int
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
@@ -180,6 +193,9 @@ class Layer:
 
     def workspace_bytes(self, n_tokens: int) -> int:
         return lib().moe_ffn_workspace_bytes(ctypes.byref(self.c), n_tokens)
+
+    def forward_workspace_bytes(self, n_tokens: int) -> int:
+        return lib().moe_forward_workspace_bytes(ctypes.byref(self.c), n_tokens)
 
 
 # ----------------------------------------------------------------------------
@@ -302,3 +318,49 @@ def forward(layer: Layer, x, routing: dict, routed_scale=1.5, stream=None):
         grouping = moe_group(ids, layer.c.n_experts, stream=stream)
     y = moe_ffn_forward(layer, x, w, grouping, stream=stream)
     return y, ids, w, grouping
+
+
+class ForwardBuffers:
+    """Outputs and workspace of moe_forward for a batch of n tokens; the
+    workspace's synchronisation words are zeroed once here."""
+
+    def __init__(self, layer: Layer, n_tokens: int, device, stream=None):
+        n, k, e = n_tokens, layer.top_k, layer.c.n_experts
+        self.n = n
+        self.ids = torch.empty((n, k), dtype=torch.int32, device=device)
+        self.w = torch.empty((n, k), dtype=torch.float32, device=device)
+        self.grouping = (torch.empty(e, dtype=torch.int32, device=device),
+                         torch.empty(e + 1, dtype=torch.int32, device=device),
+                         torch.empty(max(n * k, 1), dtype=torch.int32, device=device),
+                         torch.empty(max(n * k, 1), dtype=torch.int32, device=device))
+        self.y = torch.empty((n, layer.hidden), dtype=torch.float32, device=device)
+        nbytes = max(layer.forward_workspace_bytes(n), MOE_FORWARD_SYNC_BYTES)
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.dev_error = torch.zeros(1, dtype=torch.int32, device=device)
+        _check(lib().moe_forward_workspace_init(_ptr(self.workspace), nbytes, _stream(stream)),
+               "moe_forward_workspace_init")
+
+    def args(self):
+        counts, offsets, perm, inv_perm = self.grouping
+        return [_ptr(self.ids), _ptr(self.w), _ptr(counts), _ptr(offsets), _ptr(perm),
+                _ptr(inv_perm), _ptr(self.y), _ptr(self.workspace), self.workspace.numel(),
+                _ptr(self.dev_error)]
+
+
+def moe_forward(layer: Layer, logits, x, routed_scale=1.5, buffers: ForwardBuffers = None,
+                stream=None, events=None):
+    """The whole layer from router logits (learned routing) in one call.
+    Returns the ForwardBuffers holding y, ids, w, grouping and dev_error.
+    ``events``: (start, stop) HipEvents or None."""
+    n = x.shape[0]
+    if buffers is None:
+        buffers = ForwardBuffers(layer, n, x.device, stream)
+    x_type = MOE_ACT_BF16 if x.dtype == torch.bfloat16 else MOE_ACT_F32
+    common = [ctypes.byref(layer.c), _ptr(logits), routed_scale, _ptr(x), x_type, n]
+    if events is None:
+        _check(lib().moe_forward(*common, *buffers.args(), _stream(stream)), "moe_forward")
+    else:
+        evs = [None if e is None else e.handle for e in events]
+        _check(lib().moe_forward_timed(*common, *buffers.args(), _stream(stream), *evs),
+               "moe_forward_timed")
+    return buffers

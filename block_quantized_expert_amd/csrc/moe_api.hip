@@ -2,6 +2,10 @@
 // validate on the host, then enqueue the kernels on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <chrono>
+#include <random>
+
 #include "moe.h"
 #include "moe_host.h"
 #include "moe_kernels.h"
@@ -76,6 +80,72 @@ moe_status ffn_stages(int stages, const moe_layer* layer, const void* x, int x_t
   if (stages & kDown) {
     if ((s = launched(moe::launch_ffn_down(p, stream, ev[2], ev[3]))) != MOE_OK) return s;
   }
+  return MOE_OK;
+}
+
+static_assert(sizeof(moe::FusedSync) <= MOE_FORWARD_SYNC_BYTES, "sync area of the workspace");
+
+// A value no earlier call of this process used: a counter that starts at a
+// random point of the 64-bit range (so flags left by another process do not
+// match either) and skips 0 (the value moe_forward_workspace_init writes).
+unsigned long long next_epoch() {
+  static std::atomic<unsigned long long> counter{[] {
+    std::random_device rd;
+    const unsigned long long t = (unsigned long long)
+        std::chrono::steady_clock::now().time_since_epoch().count();
+    return (((unsigned long long)rd() << 32) ^ rd() ^ (t * 0x9E3779B97F4A7C15ull)) | 1ull;
+  }()};
+  unsigned long long v;
+  do {
+    v = counter.fetch_add(1, std::memory_order_relaxed);
+  } while (v == 0);
+  return v;
+}
+
+moe_status forward_impl(const moe_layer* layer, const float* logits, float routed_scale,
+                        const void* x, int x_type, int n_tokens, int32_t* topk_ids,
+                        float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                        int32_t* inv_perm, float* y, void* workspace, size_t workspace_bytes,
+                        int32_t* dev_error, hipStream_t stream, hipEvent_t start,
+                        hipEvent_t stop) {
+  moe::ForwardPlan plan;
+  moe_status s = moe::check_forward(layer, logits, routed_scale, x, x_type, n_tokens, topk_ids,
+                                    topk_w, counts, offsets, perm, inv_perm, y, workspace,
+                                    workspace_bytes, &plan);
+  if (s != MOE_OK) return s;
+  char* ws = static_cast<char*>(workspace);
+  moe::FfnParams p{};
+  if (n_tokens > 0)
+    p = make_params(layer, x, x_type, n_tokens, topk_w, counts, offsets, perm, inv_perm, y,
+                    ws + plan.off_ffn, plan.ffn);
+  const int steps = n_tokens > 0 ? moe::fused_decode_steps(p) : 0;
+  if (steps > 0) {
+    moe::FusedParams f{};
+    f.p = p;
+    f.logits = logits;
+    f.routed_scale = routed_scale;
+    f.topk_ids = topk_ids;
+    f.topk_w = topk_w;
+    f.counts = counts;
+    f.offsets = offsets;
+    f.perm = perm;
+    f.inv_perm = inv_perm;
+    f.partial = reinterpret_cast<float*>(ws + plan.off_partial);
+    f.sync = reinterpret_cast<moe::FusedSync*>(ws);
+    f.epoch = next_epoch();
+    f.dev_error = dev_error;
+    return launched(moe::launch_decode_fused(f, stream, start, stop));
+  }
+  if (start && hipEventRecord(start, stream) != hipSuccess) return MOE_ERR_DEVICE;
+  s = launched(moe::launch_route_group(logits, n_tokens, layer->n_experts, layer->top_k,
+                                       routed_scale, topk_ids, topk_w, counts, offsets, perm,
+                                       inv_perm, dev_error, stream));
+  if (s != MOE_OK) return s;
+  if (n_tokens > 0) {
+    if ((s = launched(moe::launch_ffn_gate_up(p, stream, nullptr, nullptr))) != MOE_OK) return s;
+    if ((s = launched(moe::launch_ffn_down(p, stream, nullptr, nullptr))) != MOE_OK) return s;
+  }
+  if (stop && hipEventRecord(stop, stream) != hipSuccess) return MOE_ERR_DEVICE;
   return MOE_OK;
 }
 
@@ -178,6 +248,50 @@ moe_status moe_ffn_forward_timed(const moe_layer* layer, const void* x, int x_ty
   const hipEvent_t ev[4] = {gate_up_start, gate_up_stop, down_start, down_stop};
   return ffn_stages(kBoth, layer, x, x_type, n_tokens, topk_w, counts, offsets, perm, inv_perm,
                     y, workspace, workspace_bytes, stream, ev);
+}
+
+size_t moe_forward_workspace_bytes(const moe_layer* layer, int n_tokens) {
+  moe::ForwardPlan plan;
+  if (moe::check_layer(layer) != MOE_OK) return 0;
+  if (moe::plan_forward(layer, n_tokens, &plan) != MOE_OK) return 0;
+  return plan.total;
+}
+
+int moe_forward_single_kernel(const moe_layer* layer, int n_tokens, int x_type) {
+  if (moe::check_layer(layer) != MOE_OK) return -1;
+  if (n_tokens != 1 || (x_type != MOE_ACT_F32 && x_type != MOE_ACT_BF16)) return 0;
+  moe::FfnPlan plan;
+  if (moe::plan_ffn(layer, n_tokens, &plan) != MOE_OK) return -1;
+  const moe::FfnParams p = make_params(layer, nullptr, x_type, n_tokens, nullptr, nullptr,
+                                       nullptr, nullptr, nullptr, nullptr, nullptr, plan);
+  return moe::fused_decode_steps(p) > 0 ? 1 : 0;
+}
+
+moe_status moe_forward_workspace_init(void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
+  if (workspace == nullptr || workspace_bytes < MOE_FORWARD_SYNC_BYTES) return MOE_ERR_WORKSPACE;
+  return launched(hipMemsetAsync(workspace, 0, MOE_FORWARD_SYNC_BYTES, stream));
+}
+
+moe_status moe_forward(const moe_layer* layer, const float* logits, float routed_scale,
+                       const void* x, int x_type, int n_tokens, int32_t* topk_ids,
+                       float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                       int32_t* inv_perm, float* y, void* workspace, size_t workspace_bytes,
+                       int32_t* dev_error, hipStream_t stream) {
+  return forward_impl(layer, logits, routed_scale, x, x_type, n_tokens, topk_ids, topk_w, counts,
+                      offsets, perm, inv_perm, y, workspace, workspace_bytes, dev_error, stream,
+                      nullptr, nullptr);
+}
+
+moe_status moe_forward_timed(const moe_layer* layer, const float* logits, float routed_scale,
+                             const void* x, int x_type, int n_tokens, int32_t* topk_ids,
+                             float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                             int32_t* inv_perm, float* y, void* workspace,
+                             size_t workspace_bytes, int32_t* dev_error, hipStream_t stream,
+                             hipEvent_t start, hipEvent_t stop) {
+  return forward_impl(layer, logits, routed_scale, x, x_type, n_tokens, topk_ids, topk_w, counts,
+                      offsets, perm, inv_perm, y, workspace, workspace_bytes, dev_error, stream,
+                      start, stop);
 }
 
 const char* moe_status_string(moe_status s) {

@@ -133,4 +133,37 @@ moe_status check_ffn(const moe_layer* layer, const void* x, int x_type, int n_to
   return MOE_OK;
 }
 
+static_assert(MOE_FORWARD_SYNC_BYTES % 256 == 0, "sync area keeps the rest aligned");
+
+
+moe_status plan_forward(const moe_layer* layer, int n_tokens, ForwardPlan* plan) {
+  moe_status s = plan_ffn(layer, n_tokens, &plan->ffn);
+  if (s != MOE_OK) return s;
+  plan->off_ffn = MOE_FORWARD_SYNC_BYTES;
+  plan->off_partial = plan->off_ffn + align_up(plan->ffn.total, 256);
+  const size_t parts = (size_t)(layer->inter + 511) / 512;
+  plan->total = plan->off_partial + align_up(parts * (size_t)layer->hidden * 4u, 256);
+  return MOE_OK;
+}
+
+moe_status check_forward(const moe_layer* layer, const float* logits, float routed_scale,
+                         const void* x, int x_type, int n_tokens, const int32_t* ids,
+                         const float* w, const int32_t* counts, const int32_t* offsets,
+                         const int32_t* perm, const int32_t* inv_perm, const float* y,
+                         const void* workspace, size_t workspace_bytes, ForwardPlan* plan) {
+  moe_status s = check_layer(layer);
+  if (s != MOE_OK) return s;
+  s = check_route_group(logits, n_tokens, layer->n_experts, layer->top_k, routed_scale, ids, w,
+                        counts, offsets, perm, inv_perm);
+  if (s != MOE_OK) return s;
+  if (x_type != MOE_ACT_F32 && x_type != MOE_ACT_BF16) return MOE_ERR_UNSUPPORTED;
+  if ((s = plan_forward(layer, n_tokens, plan)) != MOE_OK) return s;
+  if (n_tokens == 0) return MOE_OK;
+  if (x == nullptr || y == nullptr) return MOE_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(y)) return MOE_ERR_INVALID;
+  if (workspace == nullptr || workspace_bytes < plan->total) return MOE_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MOE_ERR_INVALID;
+  return MOE_OK;
+}
+
 }  // namespace moe

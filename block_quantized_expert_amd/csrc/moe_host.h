@@ -42,6 +42,23 @@ moe_status check_group(const int32_t* ids, int n_tokens, int top_k, int n_expert
 moe_status check_layer(const moe_layer* layer);
 // Fills `plan` for a valid layer; the layer must have passed check_layer.
 moe_status plan_ffn(const moe_layer* layer, int n_tokens, FfnPlan* plan);
+// Byte layout of the moe_forward workspace.
+//   sync    : [0, MOE_FORWARD_SYNC_BYTES)  the flags of the single-token
+//             kernel (FusedSync in moe_kernels.h)
+//   ffn     : the moe_ffn workspace (FfnPlan), at off_ffn
+//   partial : fp32 [inter / 512][hidden] per-part down sums (single token)
+struct ForwardPlan {
+  FfnPlan ffn;
+  size_t off_ffn;
+  size_t off_partial;
+  size_t total;
+};
+moe_status plan_forward(const moe_layer* layer, int n_tokens, ForwardPlan* plan);
+moe_status check_forward(const moe_layer* layer, const float* logits, float routed_scale,
+                         const void* x, int x_type, int n_tokens, const int32_t* ids,
+                         const float* w, const int32_t* counts, const int32_t* offsets,
+                         const int32_t* perm, const int32_t* inv_perm, const float* y,
+                         const void* workspace, size_t workspace_bytes, ForwardPlan* plan);
 moe_status check_ffn(const moe_layer* layer, const void* x, int x_type, int n_tokens,
                      const float* topk_w, const int32_t* counts, const int32_t* offsets,
                      const int32_t* perm, const int32_t* inv_perm, const float* y,

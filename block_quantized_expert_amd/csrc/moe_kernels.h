@@ -35,6 +35,40 @@ struct FfnParams {
   float* y;     // [n_tokens][hidden]
 };
 
+// Synchronisation words of the fused single-token decode (in the caller's
+// workspace).  Each holds the epoch of the call that last posted it.
+struct FusedSync {
+  static constexpr int kMaxGrid = 2048;
+  static constexpr int kGroups = 32;
+  static constexpr int kMaxRowBlocks = 256;  // hidden <= 4096
+  static constexpr int kMaxParts = 16;       // inter <= 8192
+  unsigned long long arrive[kMaxGrid];
+  struct alignas(128) Word {
+    unsigned long long v;
+  } release[kGroups];
+  unsigned long long part[kMaxRowBlocks * kMaxParts];
+};
+
+// The fused single-token decode (route + group + FFN in one kernel).  The
+// routing outputs are written by the kernel; p's topk_w, counts, offsets,
+// perm and inv_perm are not read.
+struct FusedParams {
+  FfnParams p;
+  const float* logits;
+  float routed_scale;
+  int32_t* topk_ids;
+  float* topk_w;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+  int32_t* inv_perm;
+  float* partial;                 // [inter/512][hidden] per-part down sums
+  FusedSync* sync;
+  unsigned long long epoch;       // unique per call, never 0
+  int32_t* dev_error;             // nullable
+  int grid;                       // set by the launcher
+};
+
 hipError_t launch_route(const float* logits, int n_tokens, int n_experts, int top_k,
                         float routed_scale, int32_t* ids, float* w, hipStream_t stream);
 hipError_t launch_route_hash(const int32_t* token_ids, int n_tokens, const int32_t* tid2eid,
@@ -53,6 +87,11 @@ hipError_t launch_ffn_gate_up(const FfnParams& p, hipStream_t stream, hipEvent_t
                               hipEvent_t stop);
 hipError_t launch_ffn_down(const FfnParams& p, hipStream_t stream, hipEvent_t start,
                            hipEvent_t stop);
+// steps per wavefront quarter (hidden/512) when the fused single-token
+// decode applies to p (n_tokens == 1 and the formats it covers), else 0
+int fused_decode_steps(const FfnParams& p);
+hipError_t launch_decode_fused(const FusedParams& f, hipStream_t stream, hipEvent_t start,
+                               hipEvent_t stop);
 // grouped-GEMM kernels for batches in which experts see many tokens
 hipError_t launch_gemm_gate_up(const FfnParams& p, hipStream_t stream, hipEvent_t start,
                                hipEvent_t stop);

@@ -81,6 +81,8 @@ typedef enum { MOE_W_MXFP4 = 0, MOE_W_FP8E4M3_B128 = 1 } moe_weight_type;
 /* Bits OR-ed into dev_error. */
 #define MOE_DEVERR_EXPERT_ID 1 /* an expert id outside [0, n_experts)  */
 #define MOE_DEVERR_TOKEN_ID 2  /* a token id outside [0, vocab)        */
+#define MOE_DEVERR_SYNC 4      /* moe_forward: a wait of the single-token kernel timed
+                                  out (y incomplete)                    */
 
 /* Limits of this build. */
 #define MOE_MAX_EXPERTS 1024
@@ -225,6 +227,54 @@ moe_status moe_ffn_forward_timed(const moe_layer* layer, const void* x, int x_ty
                                  size_t workspace_bytes, hipStream_t stream,
                                  hipEvent_t gate_up_start, hipEvent_t gate_up_stop,
                                  hipEvent_t down_start, hipEvent_t down_stop);
+
+/*
+ * The whole layer from router logits: learned routing, grouping and the FFN
+ * ("Deep-Dive Mathematical & Kernel Guide", sections 1, 3.2 and 4), with the
+ * semantics of moe_route_group followed by moe_ffn_forward, in one call.
+ *   logits        fp32 [n_tokens][layer->n_experts]; routed_scale > 0.
+ *   topk_ids, topk_w, counts, offsets, perm, inv_perm
+ *                 out, as written by moe_route_group.
+ *   x, x_type, y  as for moe_ffn_forward.
+ *   workspace     caller-owned device memory of at least
+ *                 moe_forward_workspace_bytes(layer, n_tokens) bytes,
+ *                 16-byte aligned.  Its first MOE_FORWARD_SYNC_BYTES hold
+ *                 synchronisation flags stamped with a per-call value the
+ *                 library never repeats: zero them once with
+ *                 moe_forward_workspace_init before the first call.  Calls
+ *                 that share a workspace must not overlap in time.
+ *   dev_error     nullable; MOE_DEVERR_SYNC is set if a wait of the
+ *                 single-token kernel times out (y is then incomplete).
+ * Single-token calls with bf16 activations, MXFP4 routed experts (and an
+ * MXFP4 shared expert of the same width), n_experts <= 256, hidden in
+ * {512, 1024, 2048, 4096} and inter a multiple of 512 run as one kernel
+ * whose grid is exactly the workgroups the GPU holds at once (it waits for
+ * all of them at a grid barrier, so nothing else may keep the GPU full
+ * indefinitely meanwhile); every other call runs the route+group kernel and
+ * the FFN kernels of moe_ffn_forward.
+ */
+#define MOE_FORWARD_SYNC_BYTES 53248
+/* 1 if moe_forward runs as the single fused kernel for this layer, batch
+ * size and activation type (then its grid barrier needs the whole GPU), 0 if
+ * it runs the separate kernels, -1 for an invalid layer. */
+int moe_forward_single_kernel(const moe_layer* layer, int n_tokens, int x_type);
+size_t moe_forward_workspace_bytes(const moe_layer* layer, int n_tokens);
+moe_status moe_forward_workspace_init(void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
+moe_status moe_forward(const moe_layer* layer, const float* logits, float routed_scale,
+                       const void* x, int x_type, int n_tokens, int32_t* topk_ids,
+                       float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                       int32_t* inv_perm, float* y, void* workspace, size_t workspace_bytes,
+                       int32_t* dev_error, hipStream_t stream);
+/* moe_forward with start/stop events (nullable) around the whole layer: the
+ * single-token kernel records them from its own dispatch; the multi-kernel
+ * path records start before its first kernel and stop after its last. */
+moe_status moe_forward_timed(const moe_layer* layer, const float* logits, float routed_scale,
+                             const void* x, int x_type, int n_tokens, int32_t* topk_ids,
+                             float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                             int32_t* inv_perm, float* y, void* workspace,
+                             size_t workspace_bytes, int32_t* dev_error, hipStream_t stream,
+                             hipEvent_t start, hipEvent_t stop);
 
 /* A static, human-readable name of a status code. */
 const char* moe_status_string(moe_status s);
