@@ -130,7 +130,6 @@ moe_status forward_impl(const moe_layer* layer, const float* logits, float route
     f.offsets = offsets;
     f.perm = perm;
     f.inv_perm = inv_perm;
-    f.partial = reinterpret_cast<float*>(ws + plan.off_partial);
     f.sync = reinterpret_cast<moe::FusedSync*>(ws);
     f.epoch = next_epoch();
     f.dev_error = dev_error;

@@ -140,9 +140,7 @@ moe_status plan_forward(const moe_layer* layer, int n_tokens, ForwardPlan* plan)
   moe_status s = plan_ffn(layer, n_tokens, &plan->ffn);
   if (s != MOE_OK) return s;
   plan->off_ffn = MOE_FORWARD_SYNC_BYTES;
-  plan->off_partial = plan->off_ffn + align_up(plan->ffn.total, 256);
-  const size_t parts = (size_t)(layer->inter + 511) / 512;
-  plan->total = plan->off_partial + align_up(parts * (size_t)layer->hidden * 4u, 256);
+  plan->total = plan->off_ffn + align_up(plan->ffn.total, 256);
   return MOE_OK;
 }
 

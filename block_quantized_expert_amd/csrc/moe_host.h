@@ -46,11 +46,9 @@ moe_status plan_ffn(const moe_layer* layer, int n_tokens, FfnPlan* plan);
 //   sync    : [0, MOE_FORWARD_SYNC_BYTES)  the flags of the single-token
 //             kernel (FusedSync in moe_kernels.h)
 //   ffn     : the moe_ffn workspace (FfnPlan), at off_ffn
-//   partial : fp32 [inter / 512][hidden] per-part down sums (single token)
 struct ForwardPlan {
   FfnPlan ffn;
   size_t off_ffn;
-  size_t off_partial;
   size_t total;
 };
 moe_status plan_forward(const moe_layer* layer, int n_tokens, ForwardPlan* plan);

@@ -40,13 +40,10 @@ struct FfnParams {
 struct FusedSync {
   static constexpr int kMaxGrid = 2048;
   static constexpr int kGroups = 32;
-  static constexpr int kMaxRowBlocks = 256;  // hidden <= 4096
-  static constexpr int kMaxParts = 16;       // inter <= 8192
   unsigned long long arrive[kMaxGrid];
   struct alignas(128) Word {
     unsigned long long v;
   } release[kGroups];
-  unsigned long long part[kMaxRowBlocks * kMaxParts];
 };
 
 // The fused single-token decode (route + group + FFN in one kernel).  The
@@ -62,7 +59,6 @@ struct FusedParams {
   int32_t* offsets;
   int32_t* perm;
   int32_t* inv_perm;
-  float* partial;                 // [inter/512][hidden] per-part down sums
   FusedSync* sync;
   unsigned long long epoch;       // unique per call, never 0
   int32_t* dev_error;             // nullable

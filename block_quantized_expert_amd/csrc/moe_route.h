@@ -45,93 +45,98 @@ __device__ __forceinline__ float key_value(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-// Top-k of one token's logits by one wavefront; lane l holds experts
-// j*64 + l.  Selection runs on the logits themselves (sqrt(softplus(.)) is
-// increasing, so the order is the same) with ties to the lower expert index.
-//  1. The k-th largest key t, one bit at a time from the top: a bit stays
-//     set while at least k keys are >= the candidate (counted with ballots,
-//     so the whole search runs on the scalar unit).
-//  2. The winners are every key above t and, in index order, as many keys
-//     equal to t as are still missing; lane c collects the c-th winner in
-//     index order.
-//  3. A winner's slot is the number of winners before it in (larger value,
-//     lower index) order.  Lane r < k returns slot r: its expert and its
-//     weight routed_scale * s_r / sum_i s_i with s = sqrt(softplus(logit)),
-//     in fp64 with the sum taken in slot order, rounded to fp32 once.
+// Maximum of an unsigned value over the 64 lanes (an inclusive max-scan
+// with the shifts of wave_incl_scan; lane 63 ends with the maximum).
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));
+  return (uint32_t)read_lane((int)v, 63);
+}
+
+// One token's logits as keys: lane l holds experts j*64 + l; experts past
+// n_experts get key 0, below every live key.  All PER loads are issued
+// before any is used (a load under the e < E branch would be waited for on
+// its own).
+template <int PER>
+__device__ __forceinline__ void load_keys(const float* __restrict__ row, int n_experts, int lane,
+                                          uint32_t (&key)[PER]) {
+  float v[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) v[j] = row[min(j * kWave + lane, n_experts - 1)];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) key[j] = j * kWave + lane < n_experts ? order_key(v[j]) : 0u;
+}
+
+// Top-k selection by one wavefront (section 1 of the guide: the k largest
+// gate scores; sqrt(softplus(.)) is increasing, so the logits give the same
+// order), ties to the lower expert index.  Round r takes the largest key
+// left (wave_max), the lowest expert index holding it (the first ballot in
+// index order), and removes it; lane r receives that expert and key.  So
+// lane r < k ends with the expert of rank r in (larger value, lower index)
+// order.  Needs at least top_k live keys.
+template <int PER>
+__device__ __forceinline__ void route_select(uint32_t (&key)[PER], int top_k, int lane,
+                                             int& out_id, uint32_t& out_key) {
+  out_id = -1;
+  out_key = 0u;
+  for (int r = 0; r < top_k; ++r) {
+    uint32_t m = key[0];
+#pragma unroll
+    for (int j = 1; j < PER; ++j) m = max(m, key[j]);
+    const uint32_t top = wave_max(m);
+    int e = -1;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const uint64_t b = __ballot(key[j] == top);
+      if (e < 0 && b != 0) e = j * kWave + __builtin_ctzll(b);
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      if (e == j * kWave + lane) key[j] = 0u;
+    if (lane == r) {
+      out_id = e;
+      out_key = top;
+    }
+  }
+}
+
+// s = sqrt(softplus(l)) in fp64 (section 1 of the guide).
+__device__ __forceinline__ double gate_score(double l) {
+  return sqrt(fmax(l, 0.0) + log1p(exp(-fabs(l))));
+}
+
+// The routed weight of a winner with score s: routed_scale * s / total,
+// where total is the sum of the k winners' scores taken in rank order in
+// fp64; rounded to fp32 once (section 3.2 of the guide: the routed weights
+// sum to the routed scale).
+__device__ __forceinline__ float routed_weight(double s, double total, float routed_scale) {
+  return (float)((double)routed_scale * s / total);
+}
+
+// Top-k of one token's logits with weights: lane r < k returns the expert of
+// rank r and its weight (route_select, then routed_weight).
 template <int PER>
 __device__ __forceinline__ void route_token(const float* __restrict__ row, int n_experts,
                                             int top_k, float routed_scale, int lane,
                                             int& out_id, float& out_w) {
-  // all PER loads are issued before any is used (a load under the e < E
-  // branch would be waited for on its own)
-  float v[PER];
-#pragma unroll
-  for (int j = 0; j < PER; ++j) v[j] = row[min(j * kWave + lane, n_experts - 1)];
   uint32_t key[PER];
-#pragma unroll
-  for (int j = 0; j < PER; ++j)
-    key[j] = j * kWave + lane < n_experts ? order_key(v[j]) : 0u;  // every live key is > 0
-  uint32_t t = 0;
-  for (int b = 31; b >= 0; --b) {
-    const uint32_t c = t | (1u << b);
-    int n = 0;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) n += __popcll(__ballot(key[j] >= c));
-    if (n >= top_k) t = c;
-  }
-  int above = 0;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) above += __popcll(__ballot(key[j] > t));
-  const int need = top_k - above;
-  int eq_seen = 0, c = 0;
-  uint32_t my_key = 0u;
-  int my_idx = 0;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const uint64_t eq = __ballot(key[j] == t);
-    const int r = eq_seen + __popcll(eq & lanemask_lt(lane));
-    eq_seen += __popcll(eq);
-    uint64_t m = __ballot(key[j] > t || (key[j] == t && r < need));
-    while (m) {
-      const int l = __builtin_ctzll(m);
-      m &= m - 1;
-      const uint32_t kv = (uint32_t)read_lane((int)key[j], l);
-      if (lane == c) {
-        my_key = kv;
-        my_idx = j * kWave + l;
-      }
-      ++c;
-    }
-  }
-  int rank = 0;
-  for (int q = 0; q < top_k; ++q) {
-    const uint32_t kq = (uint32_t)read_lane((int)my_key, q);
-    rank += (kq > my_key || (kq == my_key && q < lane)) ? 1 : 0;
-  }
-  uint32_t out_key = 0u;
-  out_id = -1;
-  for (int q = 0; q < top_k; ++q) {
-    const int rq = read_lane(rank, q);
-    const uint32_t kq = (uint32_t)read_lane((int)my_key, q);
-    const int iq = read_lane(my_idx, q);
-    if (lane == rq) {
-      out_key = kq;
-      out_id = iq;
-    }
-  }
-  double s = 0.0;
-  if (lane < top_k) {
-    const double l = (double)key_value(out_key);
-    s = sqrt(fmax(l, 0.0) + log1p(exp(-fabs(l))));
-  }
+  load_keys<PER>(row, n_experts, lane, key);
+  uint32_t out_key;
+  route_select<PER>(key, top_k, lane, out_id, out_key);
+  const double s = lane < top_k ? gate_score((double)key_value(out_key)) : 0.0;
   const long long sb = __double_as_longlong(s);
+  auto s_of_rank = [&](int i) {
+    const uint32_t lo = (uint32_t)read_lane((int)(uint32_t)sb, i);
+    const uint32_t hi = (uint32_t)read_lane((int)(uint32_t)(sb >> 32), i);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+  };
   double total = 0.0;
-  for (int r = 0; r < top_k; ++r) {
-    const uint32_t lo = (uint32_t)read_lane((int)(uint32_t)sb, r);
-    const uint32_t hi = (uint32_t)read_lane((int)(uint32_t)(sb >> 32), r);
-    total += __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
-  }
-  out_w = lane < top_k ? (float)((double)routed_scale * s / total) : 0.0f;
+  for (int i = 0; i < top_k; ++i) total += s_of_rank(i);
+  out_w = lane < top_k ? routed_weight(s, total, routed_scale) : 0.0f;
 }
 
 }  // namespace

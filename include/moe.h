@@ -247,13 +247,13 @@ moe_status moe_ffn_forward_timed(const moe_layer* layer, const void* x, int x_ty
  *                 single-token kernel times out (y is then incomplete).
  * Single-token calls with bf16 activations, MXFP4 routed experts (and an
  * MXFP4 shared expert of the same width), n_experts <= 256, hidden in
- * {512, 1024, 2048, 4096} and inter a multiple of 512 run as one kernel
+ * {512, 1024, 2048, 4096} and inter a multiple of 128 run as one kernel
  * whose grid is exactly the workgroups the GPU holds at once (it waits for
  * all of them at a grid barrier, so nothing else may keep the GPU full
  * indefinitely meanwhile); every other call runs the route+group kernel and
  * the FFN kernels of moe_ffn_forward.
  */
-#define MOE_FORWARD_SYNC_BYTES 53248
+#define MOE_FORWARD_SYNC_BYTES 20480
 /* 1 if moe_forward runs as the single fused kernel for this layer, batch
  * size and activation type (then its grid barrier needs the whole GPU), 0 if
  * it runs the separate kernels, -1 for an invalid layer. */

@@ -175,3 +175,65 @@ def test_host_validator_under_address_and_ub_sanitizers(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "validator ok" in r.stdout
+
+
+def test_forward_workspace_bytes():
+    lib = B.lib()
+    for n in (1, 7, 4096):
+        L = _layer()
+        ffn = lib.moe_ffn_workspace_bytes(ctypes.byref(L), n)
+        assert lib.moe_forward_workspace_bytes(ctypes.byref(L), n) == \
+            B.MOE_FORWARD_SYNC_BYTES + -(-ffn // 256) * 256
+    assert lib.moe_forward_workspace_bytes(ctypes.byref(_layer(hidden=100)), 1) == 0
+    assert lib.moe_forward_workspace_bytes(None, 1) == 0
+
+
+@pytest.mark.parametrize("layer_kwargs,n,x_type,expected", [
+    ({}, 1, B.MOE_ACT_BF16, 1),                         # the decode layer: one kernel
+    ({"hidden": 512, "inter": 128, "e": 16, "k": 2}, 1, B.MOE_ACT_BF16, 1),
+    ({"inter": 384, "shared": False}, 1, B.MOE_ACT_BF16, 1),
+    ({}, 2, B.MOE_ACT_BF16, 0),                         # more than one token
+    ({}, 1, B.MOE_ACT_F32, 0),                          # fp32 activations
+    ({"hidden": 640}, 1, B.MOE_ACT_BF16, 0),            # hidden not a multiple of 512
+    ({"hidden": 8192}, 1, B.MOE_ACT_BF16, 0),           # x no longer fits the staging
+    ({"wtype": 1}, 1, B.MOE_ACT_BF16, 0),               # fp8 routed experts
+    ({"swtype": 1}, 1, B.MOE_ACT_BF16, 0),              # fp8 shared expert
+    ({"e": 512}, 1, B.MOE_ACT_BF16, 0),                 # more experts than the router wave holds
+    ({"hidden": 100}, 1, B.MOE_ACT_BF16, -1),           # invalid layer
+])
+def test_forward_path_choice(layer_kwargs, n, x_type, expected):
+    L = _layer(**layer_kwargs)
+    assert B.lib().moe_forward_single_kernel(ctypes.byref(L), n, x_type) == expected
+
+
+def test_forward_path_choice_shared_width():
+    L = _layer()
+    L.shared_inter = 1024  # shared expert narrower than the routed ones
+    assert B.lib().moe_forward_single_kernel(ctypes.byref(L), 1, B.MOE_ACT_BF16) == 0
+
+
+def _fwd(L, logits=FAKE, scale=1.5, x=FAKE, n=1, ids=FAKE, ws=FAKE, ws_bytes=1 << 40, y=FAKE):
+    return B.lib().moe_forward(ctypes.byref(L) if L is not None else None, logits, scale, x,
+                               B.MOE_ACT_BF16, n, ids, FAKE, FAKE, FAKE, FAKE, FAKE, y, ws,
+                               ws_bytes, None, None)
+
+
+@pytest.mark.parametrize("kwargs,expected", [
+    ({"logits": None}, B.MOE_ERR_INVALID),
+    ({"ids": None}, B.MOE_ERR_INVALID),
+    ({"x": None}, B.MOE_ERR_INVALID),
+    ({"y": MIS}, B.MOE_ERR_INVALID),
+    ({"scale": 0.0}, B.MOE_ERR_INVALID),
+    ({"ws": None}, B.MOE_ERR_WORKSPACE),
+    ({"ws_bytes": B.MOE_FORWARD_SYNC_BYTES}, B.MOE_ERR_WORKSPACE),
+    ({"ws": MIS}, B.MOE_ERR_INVALID),
+])
+def test_forward_rejects_bad_arguments(kwargs, expected):
+    assert _fwd(_layer(), **kwargs) == expected
+
+
+def test_forward_workspace_init_rejects_small_areas():
+    lib = B.lib()
+    assert lib.moe_forward_workspace_init(None, 1 << 20, None) == B.MOE_ERR_WORKSPACE
+    assert lib.moe_forward_workspace_init(FAKE, B.MOE_FORWARD_SYNC_BYTES - 1, None) == \
+        B.MOE_ERR_WORKSPACE

@@ -55,7 +55,10 @@ def test_decode1_full():
     (replace(ONE, hidden=1024, inter=1024, top_k=1, seed=32), True),
     (replace(ONE, hidden=2048, inter=512, top_k=8, seed=33), True),  # top-8
     (replace(ONE, n_experts=256, top_k=6, seed=34), True),
-    (replace(ONE, n_experts=200, hidden=4096, inter=1536, seed=35), True),  # three parts
+    (replace(ONE, n_experts=200, hidden=4096, inter=1536, seed=35), True),  # 12 down steps
+    (replace(ONE, inter=384, seed=38), True),                        # 3 down steps
+    # 1296 gate/up items: two rounds; 18 down steps: wavefronts 0-1 take two
+    (replace(ONE, n_experts=64, hidden=1024, inter=2304, top_k=8, seed=40), True),
 ])
 def test_single_token_shapes(wl, with_shared):
     _run_and_check(wl, with_shared)
@@ -64,14 +67,14 @@ def test_single_token_shapes(wl, with_shared):
 @pytest.mark.parametrize("wl", [
     replace(ONE, act="f32", seed=36),              # fp32 x: separate kernels
     replace(ONE, n_tokens=3, seed=37),             # several tokens: separate kernels
-    replace(ONE, inter=384, seed=38),              # inter not a multiple of 512
+    replace(ONE, hidden=640, seed=38),             # hidden not a multiple of 512
 ])
 def test_other_calls_take_the_separate_kernels(wl):
     _run_and_check(wl)
 
 
 def test_many_calls_share_one_workspace():
-    """The barrier and row-block counters carry over from call to call."""
+    """The barrier flags carry over from call to call."""
     wl = replace(ONE, n_experts=64, top_k=4, seed=39)
     layer, x, x_d, routing, routing_d = gpu_inputs(wl)
     buf = B.ForwardBuffers(layer, 1, x_d.device)
