@@ -19,7 +19,7 @@ MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE 
 MOE_ACT_F32, MOE_ACT_BF16 = 0, 1
 MOE_W_MXFP4, MOE_W_FP8E4M3_B128 = 0, 1
 MOE_DEVERR_EXPERT_ID, MOE_DEVERR_TOKEN_ID, MOE_DEVERR_SYNC = 1, 2, 4
-MOE_FORWARD_SYNC_BYTES = 20480
+MOE_FORWARD_SYNC_BYTES = 8192
 
 # every symbol include/moe.h declares
 EXPORTED = ["moe_route", "moe_route_hash", "moe_route_group", "moe_group_workspace_bytes",

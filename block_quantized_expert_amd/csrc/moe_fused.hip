@@ -20,12 +20,15 @@
 // number that fit on the GPU at once, so all of them are resident.  Phases:
 //  1. routing: wavefront 15 takes the top-k of the logits (k rounds of a
 //     wavefront maximum, ties to the lower expert) and copies x into LDS;
-//     meanwhile wavefronts 0-3 compute every expert's gate score in fp64,
+//     meanwhile wavefronts 4-7 compute every expert's gate score in fp64,
 //     needed only for the weights at the end of gate/up.  The k experts in
 //     ascending order are the active segments 0..k-1, the shared expert is
 //     segment k.  With one token every segment has exactly one slot, and
 //     slot a belongs to segment a.  Workgroup 0 writes the routing outputs
-//     (ids, weights, counts, offsets, perm, inv_perm).
+//     (ids, weights, counts, offsets, perm, inv_perm).  Quad 0, when its
+//     first item belongs to the shared expert, copies that item's codes into
+//     LDS once the logits have arrived, so the memory is busy during the
+//     selection.
 //  2. gate/up: items (segment, 16 intermediate rows); a quad of four
 //     wavefronts takes one item, each wavefront a quarter of the reduction
 //     (its codes leave as one burst).  SwiGLU, then w_a * h is kept as a bf16
@@ -60,7 +63,6 @@ constexpr int kFSlots = MOE_MAX_TOP_K + 1;      // one token: k routed slots + s
 constexpr int kMaxHidden = 4096;               // x staged whole in LDS
 constexpr int kHRow = 136;                      // bf16 per staged h row (128 + 8)
 constexpr uint32_t kSpinLimit = 1u << 20;       // polls of a flag (about a second)
-constexpr int kGroups = FusedSync::kGroups;
 
 struct FusedSmem {
   int ids[MOE_MAX_TOP_K];   // routed experts in rank order
@@ -68,9 +70,15 @@ struct FusedSmem {
   int ok;
   double s[kFPer * kWave];  // sqrt(softplus(logit)) of every expert
   f32x4 gu_red[kQuads][3][2][4];  // gate/up sums of wavefronts 1-3 of a quad (token lanes)
-  f32x4 dn_red[kFWaves][4];       // down sums of every wavefront (token lanes)
+  f32x4 dn_red[kFWaves][4][2];    // down sums of every wavefront (hi and lo columns)
   union {
-    __bf16 x[kMaxHidden];
+    struct {
+      __bf16 x[kMaxHidden];
+      // a shared-expert item copied from memory during the routing: per
+      // wavefront of quad 0, 2S code vectors (gate, up alternating) and
+      // 2S/4 scale vectors, each 64 lanes x 16 bytes
+      u32x4 pre[4][2 * 8 + 2 * 2][kWave];
+    } gu;
     struct {
       __bf16 hi[kFWaves][kFSlots][kHRow];  // wavefront w: w_a * h of its step
       __bf16 lo[kFWaves][kFSlots][kHRow];
@@ -109,9 +117,11 @@ __device__ __forceinline__ uint64_t ld_dev8(const void* a) {
 // Grid barrier over `grid` resident workgroups, in two halves so that the
 // caller can request loads in between: arrive() stores this workgroup's
 // arrival flag once its earlier stores have completed; wait_release() has
-// workgroup 0 wait for every flag and then post the epoch into kGroups
-// release words on separate cache lines, while workgroup b waits on word
-// b % kGroups.  wait_release() returns false on timeout (a bounded wait).
+// wavefront 0 of every workgroup read all the flags (four per lane, requested
+// together) until each holds the call's epoch.  Reading them directly, rather
+// than through one workgroup that collects them and posts a release, saves
+// two memory round trips, and these are long while the down codes stream.
+// wait_release() returns false on timeout (a bounded wait).
 __device__ void arrive(const FusedParams& f) {
   stores_done();
   __syncthreads();
@@ -119,39 +129,29 @@ __device__ void arrive(const FusedParams& f) {
 }
 
 __device__ bool wait_release(const FusedParams& f, FusedSmem& sm) {
-  const unsigned long long ep = f.epoch;
-  if (blockIdx.x == 0 && threadIdx.x < kWave) {
-    // lane l watches flags l, l + 64, ...; a flag once seen is not read again
+  if (threadIdx.x < kWave) {
+    const unsigned long long ep = f.epoch;
     const int lane = threadIdx.x;
-    const int mine = f.grid > lane ? (f.grid - 1 - lane) / kWave + 1 : 0;  // <= 32
-    const uint32_t want = mine == 32 ? 0xFFFFFFFFu : (1u << mine) - 1u;
-    uint32_t seen = 0, spins = 0;
-    int ok = 1;
-    for (;;) {
-      for (int i = 0; i < mine; ++i)
-        if (!((seen >> i) & 1u) && poll(f.sync->arrive + lane + i * kWave) == ep)
-          seen |= 1u << i;
-      if (__ballot(seen != want) == 0) break;
-      __builtin_amdgcn_s_sleep(1);
-      if (++spins > kSpinLimit) {
-        ok = 0;
-        break;
-      }
-    }
-    if (ok && lane < kGroups) post(&f.sync->release[lane].v, ep);
-    if (lane == 0) sm.ok = ok;
-  } else if (blockIdx.x != 0 && threadIdx.x == 0) {
-    const unsigned long long* r = &f.sync->release[blockIdx.x % kGroups].v;
     uint32_t spins = 0;
     int ok = 1;
-    while (poll(r) != ep) {
+    for (;;) {
+      bool mine = true;
+      for (int b0 = 0; b0 < f.grid; b0 += 4 * kWave) {
+        unsigned long long v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          v[i] = poll(f.sync->arrive + min(b0 + i * kWave + lane, f.grid - 1));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mine = mine && v[i] == ep;
+      }
+      if (__ballot(!mine) == 0) break;
       __builtin_amdgcn_s_sleep(2);
       if (++spins > kSpinLimit) {
         ok = 0;
         break;
       }
     }
-    sm.ok = ok;
+    if (lane == 0) sm.ok = ok;
   }
   __syncthreads();
   return sm.ok != 0;
@@ -211,14 +211,67 @@ __global__ __launch_bounds__(kFThreads) void decode_fused_kernel(FusedParams f) 
     }
   };
 
+  // copy a shared-expert item's codes and scales (this wavefront's quarter)
+  // into LDS: the same bytes issue() would load, lane l's 16 at 16l
+  auto issue_lds = [&](int item) {
+    const int64_t row = (int64_t)item * 16 + r16;
+    const uint8_t* gc = p.sgate_c + row * cb + wq * S * 64 + g * 16;
+    const uint8_t* uc = p.sup_c + row * cb + wq * S * 64 + g * 16;
+    const uint8_t* gs = p.sgate_s + row * sb + wq * S * 4;
+    const uint8_t* us = p.sup_s + row * sb + wq * S * 4;
+    auto dma = [&](const uint8_t* src, int slot) {
+      __builtin_amdgcn_global_load_lds(
+          src, (__attribute__((address_space(3))) void*)(&sm.u.gu.pre[wq][slot][0]), 16, 0, 0);
+    };
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+      dma(gc + j * 64, 2 * j);
+      dma(uc + j * 64, 2 * j + 1);
+    }
+#pragma unroll
+    for (int v = 0; v < S / 4; ++v) {
+      dma(gs + 16 * v, 2 * S + 2 * v);
+      dma(us + 16 * v, 2 * S + 2 * v + 1);
+    }
+  };
+  auto fetch_lds = [&]() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the copies have landed
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+      qg[j] = sm.u.gu.pre[wq][2 * j][lane];
+      qu[j] = sm.u.gu.pre[wq][2 * j + 1][lane];
+    }
+#pragma unroll
+    for (int v = 0; v < S / 4; ++v) {
+      const u32x4 a4 = sm.u.gu.pre[wq][2 * S + 2 * v][lane];
+      const u32x4 b4 = sm.u.gu.pre[wq][2 * S + 2 * v + 1][lane];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        wg[4 * v + i] = a4[i];
+        wu[4 * v + i] = b4[i];
+      }
+    }
+  };
+  // quad 0's first item, when it belongs to the shared expert, needs no
+  // routing: its bytes are requested at once, so the memory works during
+  // the routing
+  const bool early = S >= 4 && quad == 0 && (int)blockIdx.x < ns;
+
   // ---- 1. routing and grouping; x staged
+  if (early) {
+    // first wait for a logit of our own, so that these copies queue behind
+    // the routing's loads and do not delay them
+    const float first = f.logits[lane];
+    asm volatile("s_waitcnt vmcnt(0)" ::"v"(first) : "memory");
+    issue_lds(blockIdx.x);
+  }
   if (wave == kRouteWave) {
     // x goes straight from memory into LDS (lane l of copy i writes bytes
     // 16l .. 16l+15 of 1 KiB piece i), alongside the logits
     for (int i = 0; i < p.hidden / 512; ++i)
       __builtin_amdgcn_global_load_lds(
           static_cast<const __bf16*>(p.x) + i * 512 + lane * 8,
-          (__attribute__((address_space(3))) void*)(&sm.u.x[i * 512]), 16, 0, 0);
+          (__attribute__((address_space(3))) void*)(&sm.u.gu.x[i * 512]), 16, 0, 0);
     uint32_t key[kFPer];
     load_keys<kFPer>(f.logits, p.n_experts, lane, key);
     int id;
@@ -239,10 +292,10 @@ __global__ __launch_bounds__(kFThreads) void decode_fused_kernel(FusedParams f) 
       f.inv_perm[lane] = below;
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the copies of x have landed
-  } else if (wave < kFPer) {
+  } else if (quad == 1) {
     // the gate scores, in fp64, by four otherwise idle wavefronts while the
     // selection runs (only the weights need them, at the end of gate/up)
-    const int e = wave * kWave + lane;
+    const int e = wq * kWave + lane;
     if (e < p.n_experts) sm.s[e] = gate_score((double)f.logits[e]);
   }
   __syncthreads();
@@ -266,7 +319,10 @@ __global__ __launch_bounds__(kFThreads) void decode_fused_kernel(FusedParams f) 
     const bool live = item < gu_items;  // uniform per quad
     f32x4 ag = f32x4{0, 0, 0, 0}, au = f32x4{0, 0, 0, 0};
     if (live) {
-      issue(item);
+      if (it == 0 && early)
+        fetch_lds();
+      else
+        issue(item);
 #pragma unroll
       for (int j = 0; j < S; ++j) {
         // token column 0 only; the other columns multiply zeros
@@ -274,7 +330,7 @@ __global__ __launch_bounds__(kFThreads) void decode_fused_kernel(FusedParams f) 
 #pragma unroll
         for (int t = 0; t < 4; ++t)
           b[t] = as_bf16x8(r16 == 0 ? *reinterpret_cast<const u32x4*>(
-                                          &sm.u.x[(wq * S + j) * 128 + g * 32 + 8 * t])
+                                          &sm.u.gu.x[(wq * S + j) * 128 + g * 32 + 8 * t])
                                     : u32x4{0, 0, 0, 0});
         const float sgv = ue8m0_to_f32((wg[j] >> (8 * g)) & 0xFF);
         const float suv = ue8m0_to_f32((wu[j] >> (8 * g)) & 0xFF);
@@ -357,7 +413,9 @@ __global__ __launch_bounds__(kFThreads) void decode_fused_kernel(FusedParams f) 
 
   // ---- 4. down: row block rb, wavefront w takes steps w, w + 16, ...
   for (int rb = blockIdx.x; rb < n_rb; rb += G) {
-    f32x4 acc_h = f32x4{0, 0, 0, 0}, acc_l = f32x4{0, 0, 0, 0};
+    // B column 0 carries the hi halves of w_a * h, column 1 the lo halves,
+    // so one MFMA takes both
+    f32x4 acc = f32x4{0, 0, 0, 0};
     for (int ks = wave; ks < ksteps; ks += kFWaves) {
       if (!(pre && rb == (int)blockIdx.x && ks == wave)) load_down(rb, ks);
       // stage this step of w_a * h for every segment: chunk c = 16a + c16
@@ -395,24 +453,22 @@ __global__ __launch_bounds__(kFThreads) void decode_fused_kernel(FusedParams f) 
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const bf16x8 wv = fp4x8_to_bf16(dq[a][j], sc);
-            const bf16x8 bh = as_bf16x8(r16 == 0 ? *reinterpret_cast<const u32x4*>(
-                                                       &sm.u.dn.hi[wave][a][g * 32 + 8 * j])
-                                                 : u32x4{0, 0, 0, 0});
-            const bf16x8 bl = as_bf16x8(r16 == 0 ? *reinterpret_cast<const u32x4*>(
-                                                       &sm.u.dn.lo[wave][a][g * 32 + 8 * j])
-                                                 : u32x4{0, 0, 0, 0});
-            acc_h = mfma_bf16(wv, bh, acc_h);
-            acc_l = mfma_bf16(wv, bl, acc_l);
+            const __bf16* src = r16 == 0 ? &sm.u.dn.hi[wave][a][g * 32 + 8 * j]
+                                         : &sm.u.dn.lo[wave][a][g * 32 + 8 * j];
+            const bf16x8 b = as_bf16x8(r16 < 2 ? *reinterpret_cast<const u32x4*>(src)
+                                               : u32x4{0, 0, 0, 0});
+            acc = mfma_bf16(wv, b, acc);
           }
         }
       }
       __builtin_amdgcn_wave_barrier();  // the staged rows are read before the next step
     }
-    if (r16 == 0) sm.dn_red[wave][g] = acc_h + acc_l;
+    if (r16 < 2) sm.dn_red[wave][g][r16] = acc;
     __syncthreads();
     if (threadIdx.x < 16) {
+      const int gg = threadIdx.x >> 2, r = threadIdx.x & 3;
       float sum = 0.0f;
-      for (int w = 0; w < kFWaves; ++w) sum += sm.dn_red[w][threadIdx.x >> 2][threadIdx.x & 3];
+      for (int w = 0; w < kFWaves; ++w) sum += sm.dn_red[w][gg][0][r] + sm.dn_red[w][gg][1][r];
       p.y[rb * 16 + threadIdx.x] = sum;
     }
     __syncthreads();

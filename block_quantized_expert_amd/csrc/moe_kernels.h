@@ -38,12 +38,8 @@ struct FfnParams {
 // Synchronisation words of the fused single-token decode (in the caller's
 // workspace).  Each holds the epoch of the call that last posted it.
 struct FusedSync {
-  static constexpr int kMaxGrid = 2048;
-  static constexpr int kGroups = 32;
+  static constexpr int kMaxGrid = 1024;  // one workgroup per compute unit
   unsigned long long arrive[kMaxGrid];
-  struct alignas(128) Word {
-    unsigned long long v;
-  } release[kGroups];
 };
 
 // The fused single-token decode (route + group + FFN in one kernel).  The

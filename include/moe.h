@@ -253,7 +253,7 @@ moe_status moe_ffn_forward_timed(const moe_layer* layer, const void* x, int x_ty
  * indefinitely meanwhile); every other call runs the route+group kernel and
  * the FFN kernels of moe_ffn_forward.
  */
-#define MOE_FORWARD_SYNC_BYTES 20480
+#define MOE_FORWARD_SYNC_BYTES 8192
 /* 1 if moe_forward runs as the single fused kernel for this layer, batch
  * size and activation type (then its grid barrier needs the whole GPU), 0 if
  * it runs the separate kernels, -1 for an invalid layer. */
