@@ -60,6 +60,7 @@ DEFAULTS = {  # workload: (steps, warmup, copies, pool, event_every)
 FETCH_SCALE = 262144.0 / 131083.5
 WRITE_SCALE = 1.0
 KERNEL_TRAFFIC_KIB = {  # workload: (FETCH_SIZE, WRITE_SIZE) per dispatch
+    "decode1": (46214.3, 82.2),  # decode_fused_kernel<8>
 }
 
 

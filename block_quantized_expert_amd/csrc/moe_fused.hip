@@ -18,14 +18,14 @@
 //
 // One workgroup of 16 wavefronts per compute unit; the grid is exactly the
 // number that fit on the GPU at once, so all of them are resident.  Phases:
-//  1. routing: wavefront 15 takes the top-k of the logits (k rounds of a
+//  1. routing: wavefront 0 takes the top-k of the logits (k rounds of a
 //     wavefront maximum, ties to the lower expert) and copies x into LDS;
-//     meanwhile wavefronts 4-7 compute every expert's gate score in fp64,
+//     meanwhile four other wavefronts compute every expert's gate score in fp64,
 //     needed only for the weights at the end of gate/up.  The k experts in
 //     ascending order are the active segments 0..k-1, the shared expert is
 //     segment k.  With one token every segment has exactly one slot, and
 //     slot a belongs to segment a.  Workgroup 0 writes the routing outputs
-//     (ids, weights, counts, offsets, perm, inv_perm).  Quad 0, when its
+//     (ids, weights, counts, offsets, perm, inv_perm).  Quad 1, when its
 //     first item belongs to the shared expert, copies that item's codes into
 //     LDS once the logits have arrived, so the memory is busy during the
 //     selection.
@@ -57,7 +57,7 @@ namespace {
 constexpr int kFThreads = 1024;
 constexpr int kFWaves = kFThreads / kWave;     // 16
 constexpr int kQuads = kFWaves / 4;            // gate/up items in flight per workgroup
-constexpr int kRouteWave = kFWaves - 1;        // requests nothing before the logits
+constexpr int kRouteWave = 0;                  // first to start; requests the logits first
 constexpr int kFPer = 4;                       // experts per lane in routing (E <= 256)
 constexpr int kFSlots = MOE_MAX_TOP_K + 1;      // one token: k routed slots + shared
 constexpr int kMaxHidden = 4096;               // x staged whole in LDS
@@ -75,7 +75,7 @@ struct FusedSmem {
     struct {
       __bf16 x[kMaxHidden];
       // a shared-expert item copied from memory during the routing: per
-      // wavefront of quad 0, 2S code vectors (gate, up alternating) and
+      // wavefront of quad 1, 2S code vectors (gate, up alternating) and
       // 2S/4 scale vectors, each 64 lanes x 16 bytes
       u32x4 pre[4][2 * 8 + 2 * 2][kWave];
     } gu;
@@ -164,6 +164,7 @@ __global__ __launch_bounds__(kFThreads) void decode_fused_kernel(FusedParams f) 
   __shared__ FusedSmem sm;
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int quad = wave >> 2, wq = wave & 3;
+  const int slot = (quad + 3) & 3;  // quad's place in the gate/up item order
   const int g = lane >> 4, r16 = lane & 15;
   const int k = p.top_k;
   const int nseg = k + p.has_shared;
@@ -252,10 +253,15 @@ __global__ __launch_bounds__(kFThreads) void decode_fused_kernel(FusedParams f) 
       }
     }
   };
-  // quad 0's first item, when it belongs to the shared expert, needs no
+  // quad 1's first item, when it belongs to the shared expert, needs no
   // routing: its bytes are requested at once, so the memory works during
   // the routing
-  const bool early = S >= 4 && quad == 0 && (int)blockIdx.x < ns;
+  const bool early = S >= 4 && quad == 1 && (int)blockIdx.x < ns;
+
+  // the wavefronts that compute the gate scores: four that share no SIMD
+  // with the routing wavefront (wavefront w runs on SIMD w % 4) and hold no
+  // early item
+  const int score_part = wave == 9 ? 0 : wave == 10 ? 1 : wave == 11 ? 2 : wave == 13 ? 3 : -1;
 
   // ---- 1. routing and grouping; x staged
   if (early) {
@@ -266,14 +272,15 @@ __global__ __launch_bounds__(kFThreads) void decode_fused_kernel(FusedParams f) 
     issue_lds(blockIdx.x);
   }
   if (wave == kRouteWave) {
+    uint32_t key[kFPer];
+    load_keys<kFPer>(f.logits, p.n_experts, lane, key);
     // x goes straight from memory into LDS (lane l of copy i writes bytes
-    // 16l .. 16l+15 of 1 KiB piece i), alongside the logits
+    // 16l .. 16l+15 of 1 KiB piece i); requested after the logits, so that
+    // the selection does not wait for it (loads complete in order)
     for (int i = 0; i < p.hidden / 512; ++i)
       __builtin_amdgcn_global_load_lds(
           static_cast<const __bf16*>(p.x) + i * 512 + lane * 8,
           (__attribute__((address_space(3))) void*)(&sm.u.gu.x[i * 512]), 16, 0, 0);
-    uint32_t key[kFPer];
-    load_keys<kFPer>(f.logits, p.n_experts, lane, key);
     int id;
     uint32_t id_key;
     route_select<kFPer>(key, k, lane, id, id_key);
@@ -292,10 +299,10 @@ __global__ __launch_bounds__(kFThreads) void decode_fused_kernel(FusedParams f) 
       f.inv_perm[lane] = below;
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the copies of x have landed
-  } else if (quad == 1) {
+  } else if (score_part >= 0) {
     // the gate scores, in fp64, by four otherwise idle wavefronts while the
     // selection runs (only the weights need them, at the end of gate/up)
-    const int e = wq * kWave + lane;
+    const int e = score_part * kWave + lane;
     if (e < p.n_experts) sm.s[e] = gate_score((double)f.logits[e]);
   }
   __syncthreads();
@@ -312,10 +319,11 @@ __global__ __launch_bounds__(kFThreads) void decode_fused_kernel(FusedParams f) 
     if (threadIdx.x == 0) f.offsets[p.n_experts] = k;
   }
 
-  // ---- 2. gate/up: quad q takes items it * 4G + q * G + blockIdx.x
+  // ---- 2. gate/up: quad q takes items (4 it + slot) G + blockIdx.x, with
+  // slot = (q + 3) % 4: quad 1 takes the first items (the shared expert's)
   const int n_it = (gu_items + kQuads * G - 1) / (kQuads * G);  // same for every quad
   for (int it = 0; it < n_it; ++it) {
-    const int item = (it * kQuads + quad) * G + blockIdx.x;
+    const int item = (it * kQuads + slot) * G + blockIdx.x;
     const bool live = item < gu_items;  // uniform per quad
     f32x4 ag = f32x4{0, 0, 0, 0}, au = f32x4{0, 0, 0, 0};
     if (live) {
