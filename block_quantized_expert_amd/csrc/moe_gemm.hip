@@ -223,13 +223,16 @@ __device__ __forceinline__ void dispatch_nbt(int n, Fn&& f) {
 
 // NBT = token blocks of the tile (ceil(m / 16)), a compile-time constant so
 // that a step's fragment reads and MFMAs form one branch-free block.
-template <int WT, int TT, int NBT>
+template <int WT, int TT, int NBT, bool SC>
 __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it, char* smem,
                                              int wave, int lane) {
   using F = Fmt<WT>;
   constexpr int Q = F::Q;
   constexpr int TB = NBT;
-  constexpr int kLoads = 4 * (Q + 1);  // vector loads of one step's weights
+  // (seven token blocks keep byte loads: their registers are full, and their
+  // steps have the most work per load)
+  constexpr bool kSC = SC && WT == MOE_W_MXFP4 && NBT <= 6;
+  constexpr int kLoads = kSC ? 4 * Q : 4 * (Q + 1);  // vector loads of one step's weights
   const int g = lane >> 4, r16 = lane & 15;
   const bool shared = it.seg == p.n_experts;
   const int rows = shared ? p.shared_inter : p.inter;
@@ -281,7 +284,34 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
 #pragma unroll
         for (int i = 0; i < Q; ++i)
           q[mat][rb][i] = load16(cbase[mat] + lc + 16 * rb * cb + F::code_off(k, 0) + 16 * i);
-        u[mat][rb] = sbase[mat][ls + 16 * rb * sb + F::scale_off(k, 0)];
+        if (!kSC) u[mat][rb] = sbase[mat][ls + 16 * rb * sb + F::scale_off(k, 0)];
+      }
+  };
+  // scale chunks (kSC): the 16 scale bytes of steps 4c .. 4c+3 of a row
+  // arrive with one load (the four lanes of a row share it), once per four
+  // steps instead of one byte load per step: a byte load per row per step
+  // doubled the requests of the weight stream and halved its rate.  The
+  // lane keeps its own byte of each of the four steps in sp.
+  u32x4 scw[2][2];
+  uint32_t sp[2][2];
+  const int64_t srow = ls - F::scale_off(0, g);
+  auto load_sc = [&](int c) {
+    const int cc = min(c, nks / 4 - 1);
+#pragma unroll
+    for (int mat = 0; mat < 2; ++mat)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+        scw[mat][rb] = load16(sbase[mat] + srow + 16 * rb * sb + 16 * cc);
+  };
+  auto take_sc = [&]() {
+#pragma unroll
+    for (int mat = 0; mat < 2; ++mat)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v |= ((scw[mat][rb][t] >> (8 * g)) & 0xFFu) << (8 * t);
+        sp[mat][rb] = v;
       }
   };
 
@@ -295,12 +325,20 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
 
   // buffer b at smem + b * TT * 256 (offsets from smem keep LDS addressing)
   auto buf = [&](int b) { return smem + (b & 1) * (TT * 256); };
+  if (kSC) load_sc(0);
   load_w(0, q0, u0);
   load_w(1, q1, u1);
   st.copy(xb, p.hidden, 0, buf(0), nbt);
   wait_vm<0>();
   __syncthreads();
   for (int ks = 0; ks < nks; ++ks) {
+    // every fourth step: this chunk's scales out of the load registers, then
+    // the next chunk's requested (before the step's other loads, so that the
+    // end-of-step wait below still counts only the weights after the copy)
+    if (kSC && (ks & 3) == 0) {
+      take_sc();
+      load_sc((ks >> 2) + 1);
+    }
     // step ks+1's activations, then step ks+2's weights: the end-of-step
     // wait lets the weights stay in flight
     if (ks + 1 < nks) st.copy(xb, p.hidden, ks + 1, buf(ks + 1), nbt);
@@ -312,7 +350,8 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
 #pragma unroll
     for (int mat = 0; mat < 2; ++mat)
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) sc[mat][rb] = ue8m0_to_f32(u0[mat][rb]);
+      for (int rb = 0; rb < 2; ++rb)
+        sc[mat][rb] = ue8m0_to_f32(kSC ? (sp[mat][rb] >> (8 * (ks & 3))) & 0xFFu : u0[mat][rb]);
     // sub-step j+1 is decoded while sub-step j multiplies, so the converts
     // overlap the matrix-core work
     bf16x8 a[2][2][2];
@@ -382,7 +421,7 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
     }
 }
 
-template <int WT, int TT>
+template <int WT, int TT, bool SC>
 __global__ __launch_bounds__(kGThreads, 2) void gemm_gate_up_kernel(FfnParams p, int seg_lo,
                                                                      int seg_hi) {
   extern __shared__ __align__(16) char smem[];
@@ -396,7 +435,7 @@ __global__ __launch_bounds__(kGThreads, 2) void gemm_gate_up_kernel(FfnParams p,
     if (item < 0) continue;
     const GItem it = find_item<TT, kGuRows, false>(p, seg_lo, seg_hi, s_pref, item);
     dispatch_nbt<TT / 16>((it.m + 15) >> 4, [&](auto nb) {
-      gate_up_item<WT, TT, decltype(nb)::value>(p, it, smem, wave, lane);
+      gate_up_item<WT, TT, decltype(nb)::value, SC>(p, it, smem, wave, lane);
     });
     __syncthreads();  // the LDS tiles are reused by the next item
   }
@@ -404,14 +443,15 @@ __global__ __launch_bounds__(kGThreads, 2) void gemm_gate_up_kernel(FfnParams p,
 
 // ------------------------------------------------------------- down
 
-template <int WT, int TT, int NBT>
+template <int WT, int TT, int NBT, bool SC>
 __device__ __forceinline__ void down_item(const FfnParams& p, const GItem& it, char* smem,
                                           int wave, int lane) {
   using F = Fmt<WT>;
   constexpr int Q = F::Q;
   constexpr int TB = NBT;
   constexpr int RB = kDnRows / (16 * kGWaves);  // row blocks per wavefront
-  constexpr int kLoads = RB * (Q + 1);
+  constexpr bool kSC = SC && WT == MOE_W_MXFP4;
+  constexpr int kLoads = kSC ? RB * Q : RB * (Q + 1);
   const int g = lane >> 4, r16 = lane & 15;
   const bool shared = it.seg == p.n_experts;
   const int kdim = shared ? p.shared_inter : p.inter;
@@ -457,7 +497,28 @@ __device__ __forceinline__ void down_item(const FfnParams& p, const GItem& it, c
 #pragma unroll
       for (int i = 0; i < Q; ++i)
         q[rb][i] = load16(cbase + lc + 16 * rr * cb + F::code_off(k, 0) + 16 * i);
-      u[rb] = sbase[ls + 16 * rr * sb + F::scale_off(k, 0)];
+      if (!kSC) u[rb] = sbase[ls + 16 * rr * sb + F::scale_off(k, 0)];
+    }
+  };
+  // scale chunks, as in gate/up
+  u32x4 scw[RB];
+  uint32_t sp[RB];
+  const int64_t srow = ls - F::scale_off(0, g);
+  auto load_sc = [&](int c) {
+    const int cc = min(c, nks / 4 - 1);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int rr = rb < nrb ? rb : 0;
+      scw[rb] = load16(sbase + srow + 16 * rr * sb + 16 * cc);
+    }
+  };
+  auto take_sc = [&]() {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) v |= ((scw[rb][t] >> (8 * g)) & 0xFFu) << (8 * t);
+      sp[rb] = v;
     }
   };
 
@@ -471,6 +532,7 @@ __device__ __forceinline__ void down_item(const FfnParams& p, const GItem& it, c
   // h_hi of step parity b at smem + 2b * kTile, h_lo right after it
   auto bh = [&](int b) { return smem + (b & 1) * (2 * kTile); };
   auto bl = [&](int b) { return smem + (b & 1) * (2 * kTile) + kTile; };
+  if (kSC) load_sc(0);
   load_w(0, q0, u0);
   load_w(1, q1, u1);
   st.copy(p.h_hi, p.h_stride, 0, bh(0), nbt);
@@ -478,6 +540,10 @@ __device__ __forceinline__ void down_item(const FfnParams& p, const GItem& it, c
   wait_vm<0>();
   __syncthreads();
   for (int ks = 0; ks < nks; ++ks) {
+    if (kSC && (ks & 3) == 0) {
+      take_sc();
+      load_sc((ks >> 2) + 1);
+    }
     if (ks + 1 < nks) {
       st.copy(p.h_hi, p.h_stride, ks + 1, bh(ks + 1), nbt);
       st.copy(p.h_lo, p.h_stride, ks + 1, bl(ks + 1), nbt);
@@ -489,7 +555,8 @@ __device__ __forceinline__ void down_item(const FfnParams& p, const GItem& it, c
     const char* curl = bl(ks);
     float sc[RB];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) sc[rb] = ue8m0_to_f32(u0[rb]);
+    for (int rb = 0; rb < RB; ++rb)
+      sc[rb] = ue8m0_to_f32(kSC ? (sp[rb] >> (8 * (ks & 3))) & 0xFFu : u0[rb]);
     bf16x8 a[2][RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) a[0][rb] = F::decode_j(q0[rb], sc[rb], 0);
@@ -545,7 +612,7 @@ __device__ __forceinline__ void down_item(const FfnParams& p, const GItem& it, c
   }
 }
 
-template <int WT, int TT>
+template <int WT, int TT, bool SC>
 __global__ __launch_bounds__(kGThreads, 2) void gemm_down_kernel(FfnParams p, int seg_lo,
                                                                   int seg_hi) {
   extern __shared__ __align__(16) char smem[];
@@ -559,7 +626,7 @@ __global__ __launch_bounds__(kGThreads, 2) void gemm_down_kernel(FfnParams p, in
     if (item < 0) continue;
     const GItem it = find_item<TT, kDnRows, true>(p, seg_lo, seg_hi, s_pref, item);
     dispatch_nbt<TT / 16>((it.m + 15) >> 4, [&](auto nb) {
-      down_item<WT, TT, decltype(nb)::value>(p, it, smem, wave, lane);
+      down_item<WT, TT, decltype(nb)::value, SC>(p, it, smem, wave, lane);
     });
     __syncthreads();
   }
@@ -605,23 +672,23 @@ int grid_for(int64_t items) {
   return (int)(items < kGemmGrid ? (items > 0 ? items : 1) : kGemmGrid);
 }
 
-template <int WT, int TT>
+template <int WT, int TT, bool SC>
 hipError_t gate_up_range(const FfnParams& p, int seg_lo, int seg_hi, hipStream_t stream,
                          hipEvent_t start, hipEvent_t stop) {
-  static const hipError_t attr = allow_lds(gemm_gate_up_kernel<WT, TT>);
+  static const hipError_t attr = allow_lds(gemm_gate_up_kernel<WT, TT, SC>);
   if (attr != hipSuccess) return attr;
   const int grid = grid_for(items_bound(p, seg_lo, seg_hi, TT, kGuRows, false));
-  return launch(gemm_gate_up_kernel<WT, TT>, dim3(grid), dim3(kGThreads),
+  return launch(gemm_gate_up_kernel<WT, TT, SC>, dim3(grid), dim3(kGThreads),
                 (size_t)2 * TT * 256, stream, start, stop, p, seg_lo, seg_hi);
 }
 
-template <int WT, int TT>
+template <int WT, int TT, bool SC>
 hipError_t down_range(const FfnParams& p, int seg_lo, int seg_hi, hipStream_t stream,
                       hipEvent_t start, hipEvent_t stop) {
-  static const hipError_t attr = allow_lds(gemm_down_kernel<WT, TT>);
+  static const hipError_t attr = allow_lds(gemm_down_kernel<WT, TT, SC>);
   if (attr != hipSuccess) return attr;
   const int grid = grid_for(items_bound(p, seg_lo, seg_hi, TT, kDnRows, true));
-  return launch(gemm_down_kernel<WT, TT>, dim3(grid), dim3(kGThreads), (size_t)4 * TT * 256,
+  return launch(gemm_down_kernel<WT, TT, SC>, dim3(grid), dim3(kGThreads), (size_t)4 * TT * 256,
                 stream, start, stop, p, seg_lo, seg_hi);
 }
 
@@ -640,19 +707,25 @@ hipError_t by_type(const FfnParams& p, hipStream_t stream, hipEvent_t start, hip
 
 }  // namespace
 
+// Scale chunks need 16-byte scale rows and whole chunks of four steps: a
+// reduction dimension that is a multiple of 512.
 hipError_t launch_gemm_gate_up(const FfnParams& p, hipStream_t stream, hipEvent_t start,
                                hipEvent_t stop) {
+  const bool sc = p.hidden % 512 == 0;
   return by_type(p, stream, start, stop, [&](int wt, int lo, int hi, hipEvent_t a, hipEvent_t b) {
-    return wt == MOE_W_MXFP4 ? gate_up_range<MOE_W_MXFP4, 112>(p, lo, hi, stream, a, b)
-                             : gate_up_range<MOE_W_FP8E4M3_B128, 64>(p, lo, hi, stream, a, b);
+    if (wt != MOE_W_MXFP4) return gate_up_range<MOE_W_FP8E4M3_B128, 64, false>(p, lo, hi, stream, a, b);
+    return sc ? gate_up_range<MOE_W_MXFP4, 112, true>(p, lo, hi, stream, a, b)
+              : gate_up_range<MOE_W_MXFP4, 112, false>(p, lo, hi, stream, a, b);
   });
 }
 
 hipError_t launch_gemm_down(const FfnParams& p, hipStream_t stream, hipEvent_t start,
                             hipEvent_t stop) {
+  const bool sc = p.inter % 512 == 0 && (!p.has_shared || p.shared_inter % 512 == 0);
   return by_type(p, stream, start, stop, [&](int wt, int lo, int hi, hipEvent_t a, hipEvent_t b) {
-    return wt == MOE_W_MXFP4 ? down_range<MOE_W_MXFP4, 64>(p, lo, hi, stream, a, b)
-                             : down_range<MOE_W_FP8E4M3_B128, 64>(p, lo, hi, stream, a, b);
+    if (wt != MOE_W_MXFP4) return down_range<MOE_W_FP8E4M3_B128, 64, false>(p, lo, hi, stream, a, b);
+    return sc ? down_range<MOE_W_MXFP4, 64, true>(p, lo, hi, stream, a, b)
+              : down_range<MOE_W_MXFP4, 64, false>(p, lo, hi, stream, a, b);
   });
 }
 
