@@ -61,6 +61,8 @@ constexpr int kRouteWave = 0;                  // first to start; requests the l
 constexpr int kFPer = 4;                       // experts per lane in routing (E <= 256)
 constexpr int kFSlots = MOE_MAX_TOP_K + 1;      // one token: k routed slots + shared
 constexpr int kMaxHidden = 4096;               // x staged whole in LDS
+constexpr int kMaxInter = 4096;                // down scales of a row block staged in LDS
+constexpr int kDScale = 16 * (kMaxInter / 32);  // their bytes per segment
 constexpr int kHRow = 136;                      // bf16 per staged h row (128 + 8)
 constexpr uint32_t kSpinLimit = 1u << 20;       // polls of a flag (about a second)
 
@@ -71,6 +73,7 @@ struct FusedSmem {
   double s[kFPer * kWave];  // sqrt(softplus(logit)) of every expert
   f32x4 gu_red[kQuads][3][2][4];  // gate/up sums of wavefronts 1-3 of a quad (token lanes)
   f32x4 dn_red[kFWaves][4][2];    // down sums of every wavefront (hi and lo columns)
+  alignas(16) uint8_t dsc[kFSlots][kDScale];  // down scales of the row block, per segment
   union {
     struct {
       __bf16 x[kMaxHidden];
@@ -319,6 +322,30 @@ __global__ __launch_bounds__(kFThreads) void decode_fused_kernel(FusedParams f) 
     if (threadIdx.x == 0) f.offsets[p.n_experts] = k;
   }
 
+  const int ksteps = p.inter >> 7;  // 128-wide steps of the intermediate dimension
+  const int n_rb = p.hidden >> 4;
+  const int64_t dcb = p.inter / 2, dsb = p.inter / 32;
+  // The down scales of this workgroup's first row block: for each segment
+  // the 16 rows' scales are one contiguous block (16 * inter / 32 bytes),
+  // copied into LDS by wavefront 0 with one instruction per KiB.  Read from
+  // there, they cost no request per wavefront and step: one-byte loads per
+  // lane doubled the requests of the down-code stream.  The copy lands long
+  // before it is read (arrive() waits for wavefront 0's loads).
+  if (wave == 0 && (int)blockIdx.x < n_rb) {
+    const int64_t bytes = 16 * dsb;
+    for (int a = 0; a < nseg; ++a) {
+      const int e = uniform(sm.act[a]);
+      const bool shared = e == p.n_experts;
+      const uint8_t* src = (shared ? p.sdown_s : p.down_s) +
+                           ((shared ? 0 : (int64_t)e * p.hidden) + (int64_t)blockIdx.x * 16) * dsb;
+      for (int i = 0; i * 1024 < bytes; ++i)
+        if (i * 1024 + lane * 16 < bytes)
+          __builtin_amdgcn_global_load_lds(
+              src + i * 1024 + lane * 16,
+              (__attribute__((address_space(3))) void*)(&sm.dsc[a][i * 1024]), 16, 0, 0);
+    }
+  }
+
   // ---- 2. gate/up: quad q takes items (4 it + slot) G + blockIdx.x, with
   // slot = (q + 3) % 4: quad 1 takes the first items (the shared expert's)
   const int n_it = (gu_items + kQuads * G - 1) / (kQuads * G);  // same for every quad
@@ -389,11 +416,10 @@ __global__ __launch_bounds__(kFThreads) void decode_fused_kernel(FusedParams f) 
   }
 
   // ---- 3. grid barrier; the first row block's down codes requested meanwhile
-  const int ksteps = p.inter >> 7;  // 128-wide steps of the intermediate dimension
-  const int n_rb = p.hidden >> 4;
-  const int64_t dcb = p.inter / 2, dsb = p.inter / 32;
   u32x4 dq[kFSlots];
   uint32_t ds[kFSlots];
+  // (the grid covers every row block, so rb is blockIdx.x: see
+  // fused_decode_steps)
   auto load_down = [&](int rb, int ks) {
 #pragma unroll
     for (int a = 0; a < kFSlots; ++a) {
@@ -402,10 +428,9 @@ __global__ __launch_bounds__(kFThreads) void decode_fused_kernel(FusedParams f) 
       const bool shared = e == p.n_experts;
       const int64_t row = (shared ? 0 : (int64_t)e * p.hidden) + rb * 16 + r16;
       const uint8_t* c = (shared ? p.sdown_c : p.down_c) + row * dcb + ks * 64 + g * 16;
-      const uint8_t* s = (shared ? p.sdown_s : p.down_s) + row * dsb + ks * 4 + g;
       if (a < nseg) {
         dq[a] = load16(c);
-        ds[a] = *s;
+        ds[a] = sm.dsc[a][r16 * dsb + ks * 4 + g];  // copied into LDS above
       }
     }
   };
@@ -419,7 +444,7 @@ __global__ __launch_bounds__(kFThreads) void decode_fused_kernel(FusedParams f) 
     return;
   }
 
-  // ---- 4. down: row block rb, wavefront w takes steps w, w + 16, ...
+  // ---- 4. down: row block rb = blockIdx.x, wavefront w takes steps w, w + 16, ...
   for (int rb = blockIdx.x; rb < n_rb; rb += G) {
     // B column 0 carries the hi halves of w_a * h, column 1 the lo halves,
     // so one MFMA takes both
@@ -530,9 +555,22 @@ int fused_decode_steps(const FfnParams& p) {
   if (p.n_tokens != 1 || p.x_f32 || p.w_type != MOE_W_MXFP4) return 0;
   if (p.n_experts > kFPer * kWave || p.top_k > MOE_MAX_TOP_K) return 0;
   if (p.has_shared && (p.sw_type != MOE_W_MXFP4 || p.shared_inter != p.inter)) return 0;
-  if (p.inter % 128 != 0 || p.hidden % 512 != 0 || p.hidden > kMaxHidden) return 0;
+  if (p.inter % 128 != 0 || p.inter > kMaxInter) return 0;
+  if (p.hidden % 512 != 0 || p.hidden > kMaxHidden) return 0;
   const int s = p.hidden / 512;
-  return (s == 1 || s == 2 || s == 4 || s == 8) ? s : 0;
+  int grid = 0;
+  hipError_t e = hipErrorInvalidValue;
+  switch (s) {
+    case 1: e = resident_grid<1>(&grid); break;
+    case 2: e = resident_grid<2>(&grid); break;
+    case 4: e = resident_grid<4>(&grid); break;
+    case 8: e = resident_grid<8>(&grid); break;
+    default: return 0;
+  }
+  // every workgroup takes at most one row block of the down projection (a
+  // failed query means no device: then nothing launches anyway)
+  if (e == hipSuccess && min(grid, FusedSync::kMaxGrid) < p.hidden / 16) return 0;
+  return s;
 }
 
 hipError_t launch_decode_fused(const FusedParams& f, hipStream_t stream, hipEvent_t start,

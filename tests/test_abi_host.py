@@ -196,6 +196,7 @@ def test_forward_workspace_bytes():
     ({}, 1, B.MOE_ACT_F32, 0),                          # fp32 activations
     ({"hidden": 640}, 1, B.MOE_ACT_BF16, 0),            # hidden not a multiple of 512
     ({"hidden": 8192}, 1, B.MOE_ACT_BF16, 0),           # x no longer fits the staging
+    ({"inter": 4224}, 1, B.MOE_ACT_BF16, 0),            # down scales no longer fit the staging
     ({"wtype": 1}, 1, B.MOE_ACT_BF16, 0),               # fp8 routed experts
     ({"swtype": 1}, 1, B.MOE_ACT_BF16, 0),              # fp8 shared expert
     ({"e": 512}, 1, B.MOE_ACT_BF16, 0),                 # more experts than the router wave holds
