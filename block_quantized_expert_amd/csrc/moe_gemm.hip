@@ -52,6 +52,13 @@ constexpr int kGuRows = 32 * kGWaves;  // intermediate rows per gate/up item
 constexpr int kDnRows = 64 * kGWaves;  // hidden rows per down item
 constexpr int kSegMax = MOE_MAX_EXPERTS + 1;
 constexpr int kGemmLds = 72 * 1024;  // dynamic LDS of either kernel (two per CU)
+// scale blocks in LDS: after two token tiles of up to five blocks (gate/up,
+// 128 rows x H/32 bytes per matrix, H <= 4096) or two h_hi/h_lo pairs of up
+// to three blocks (down, 256 rows x I/32 bytes, I <= 2048)
+constexpr int kGuScaleOff = 2 * 16 * 5 * 256;
+constexpr int kDnScaleOff = 2 * 2 * 16 * 3 * 256;
+static_assert(kGuScaleOff + 2 * kGuRows * (4096 / 32) <= kGemmLds, "gate/up LDS");
+static_assert(kDnScaleOff + kDnRows * (2048 / 32) <= kGemmLds, "down LDS");
 
 struct GItem {
   int seg;
@@ -174,11 +181,12 @@ __device__ __forceinline__ bf16x8 token_frag(const char* buf, int tb, int j, int
 }
 
 // Wait until at most n vector memory operations of this wavefront are
-// outstanding (n < 16), leaving the other counters alone.
+// outstanding (n < 64: vmcnt bits 3:0 and 15:14), leaving the other
+// counters alone.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 16, "vmcnt");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8));
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
 // End of a reduction step: this wavefront's copies into LDS have landed
@@ -229,10 +237,17 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
   using F = Fmt<WT>;
   constexpr int Q = F::Q;
   constexpr int TB = NBT;
-  // (seven token blocks keep byte loads: their registers are full, and their
-  // steps have the most work per load)
-  constexpr bool kSC = SC && WT == MOE_W_MXFP4 && NBT <= 6;
-  constexpr int kLoads = kSC ? 4 * Q : 4 * (Q + 1);  // vector loads of one step's weights
+  // Scale bytes (SC: MXFP4, H a multiple of 512 and at most 4096):
+  //  - up to five token blocks: the item's scales sit in LDS (kSC, below);
+  //  - six: 16-byte chunks of four steps in registers (kCh, below);
+  //  - otherwise (and seven blocks, whose registers are full): one byte per
+  //    row and step, loaded with the step's codes.
+  constexpr bool kSC = SC && WT == MOE_W_MXFP4 && NBT <= 5;
+  constexpr bool kCh = SC && WT == MOE_W_MXFP4 && NBT == 6;
+  constexpr int kLoads = (kSC || kCh) ? 4 * Q : 4 * (Q + 1);  // vector loads of one step's weights
+  // weights by pairs of steps (below) for up to four token blocks and an
+  // even number of steps
+  constexpr bool kPair = kSC && NBT <= 4;
   const int g = lane >> 4, r16 = lane & 15;
   const bool shared = it.seg == p.n_experts;
   const int rows = shared ? p.shared_inter : p.inter;
@@ -284,14 +299,14 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
 #pragma unroll
         for (int i = 0; i < Q; ++i)
           q[mat][rb][i] = load16(cbase[mat] + lc + 16 * rb * cb + F::code_off(k, 0) + 16 * i);
-        if (!kSC) u[mat][rb] = sbase[mat][ls + 16 * rb * sb + F::scale_off(k, 0)];
+        if (!kSC && !kCh) u[mat][rb] = sbase[mat][ls + 16 * rb * sb + F::scale_off(k, 0)];
       }
   };
-  // scale chunks (kSC): the 16 scale bytes of steps 4c .. 4c+3 of a row
-  // arrive with one load (the four lanes of a row share it), once per four
-  // steps instead of one byte load per step: a byte load per row per step
-  // doubled the requests of the weight stream and halved its rate.  The
-  // lane keeps its own byte of each of the four steps in sp.
+  // scale chunks (kCh): the 16 scale bytes of steps 4c .. 4c+3 of a row in
+  // one load shared by the row's four lanes, once per four steps; the lane
+  // keeps its own byte of each of the four steps in sp.  (Their lines can
+  // leave the L2 between two loads, so this costs re-fetches that the LDS
+  // copy avoids; it is the fallback where that copy does not fit.)
   u32x4 scw[2][2];
   uint32_t sp[2][2];
   const int64_t srow = ls - F::scale_off(0, g);
@@ -314,6 +329,32 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
         sp[mat][rb] = v;
       }
   };
+  // scales (kSC): the item's 128 rows of each matrix are consecutive, so
+  // their scale bytes are one contiguous block (128 * H/32 bytes), copied
+  // into LDS at the start of the item (1 KiB per copy instruction) and read
+  // from there at every step.  Loaded from memory per step (one byte per
+  // row) they doubled the weight stream's requests; loaded per four steps
+  // (16 bytes) the lines left the L2 between loads and were fetched up to
+  // eight times each.
+  constexpr int kTokB = kSC ? 16 * NBT * 256 : TT * 256;  // bytes of one token tile
+  char* const sscale = smem + kGuScaleOff;                // [mat][128 rows][sb]
+  auto copy_scales = [&]() {
+    const int64_t bytes = (int64_t)kGuRows * sb;  // per matrix
+    const int64_t row0 = (shared ? 0 : (int64_t)it.seg * rows) + it.row0;
+#pragma unroll
+    for (int mat = 0; mat < 2; ++mat) {
+      const uint8_t* src = sbase[mat] + row0 * sb;
+      for (int64_t o = (int64_t)wave * 1024; o < bytes; o += kGWaves * 1024)
+        if (o + lane * 16 < bytes)
+          __builtin_amdgcn_global_load_lds(
+              src + o + lane * 16,
+              (__attribute__((address_space(3))) void*)(sscale + mat * bytes + o), 16, 0, 0);
+    }
+  };
+  auto scale_byte = [&](int mat, int rb, int ks) -> uint32_t {
+    return *reinterpret_cast<const uint8_t*>(
+        sscale + (mat * kGuRows + 32 * wave + 16 * rb + r16) * sb + ks * 4 + g);
+  };
 
   f32x4 acc[2][2][TB];
 #pragma unroll
@@ -324,41 +365,26 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
       for (int tb = 0; tb < TB; ++tb) acc[mat][rb][tb] = f32x4{0, 0, 0, 0};
 
   // buffer b at smem + b * TT * 256 (offsets from smem keep LDS addressing)
-  auto buf = [&](int b) { return smem + (b & 1) * (TT * 256); };
-  if (kSC) load_sc(0);
-  load_w(0, q0, u0);
-  load_w(1, q1, u1);
-  st.copy(xb, p.hidden, 0, buf(0), nbt);
-  wait_vm<0>();
-  __syncthreads();
-  for (int ks = 0; ks < nks; ++ks) {
-    // every fourth step: this chunk's scales out of the load registers, then
-    // the next chunk's requested (before the step's other loads, so that the
-    // end-of-step wait below still counts only the weights after the copy)
-    if (kSC && (ks & 3) == 0) {
-      take_sc();
-      load_sc((ks >> 2) + 1);
-    }
-    // step ks+1's activations, then step ks+2's weights: the end-of-step
-    // wait lets the weights stay in flight
-    if (ks + 1 < nks) st.copy(xb, p.hidden, ks + 1, buf(ks + 1), nbt);
-    __builtin_amdgcn_sched_barrier(0);
-    load_w(ks + 2, q2, u2);
-    __builtin_amdgcn_sched_barrier(0);
+  auto buf = [&](int b) { return smem + (b & 1) * kTokB; };
+  // one reduction step: step ks's weights qq (and their scale bytes uu, when
+  // not chunked) times the token tile in LDS
+  auto step_mma = [&](int ks, const u32x4 (&qq)[2][2][Q], const uint32_t (&uu)[2][2]) {
     const char* cur = buf(ks);
     float sc[2][2];
 #pragma unroll
     for (int mat = 0; mat < 2; ++mat)
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
-        sc[mat][rb] = ue8m0_to_f32(kSC ? (sp[mat][rb] >> (8 * (ks & 3))) & 0xFFu : u0[mat][rb]);
+        sc[mat][rb] = ue8m0_to_f32(kSC   ? scale_byte(mat, rb, ks)
+                                   : kCh ? (sp[mat][rb] >> (8 * (ks & 3))) & 0xFFu
+                                         : uu[mat][rb]);
     // sub-step j+1 is decoded while sub-step j multiplies, so the converts
     // overlap the matrix-core work
     bf16x8 a[2][2][2];
 #pragma unroll
     for (int mat = 0; mat < 2; ++mat)
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) a[0][mat][rb] = F::decode_j(q0[mat][rb], sc[mat][rb], 0);
+      for (int rb = 0; rb < 2; ++rb) a[0][mat][rb] = F::decode_j(qq[mat][rb], sc[mat][rb], 0);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if (j + 1 < 4) {
@@ -366,7 +392,7 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
         for (int mat = 0; mat < 2; ++mat)
 #pragma unroll
           for (int rb = 0; rb < 2; ++rb)
-            a[(j + 1) & 1][mat][rb] = F::decode_j(q0[mat][rb], sc[mat][rb], j + 1);
+            a[(j + 1) & 1][mat][rb] = F::decode_j(qq[mat][rb], sc[mat][rb], j + 1);
       }
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) {
@@ -380,19 +406,75 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
       // keep two sub-steps' fragments live at a time
       __builtin_amdgcn_sched_barrier(0);
     }
-    step_barrier<kLoads>();
+  };
+  if (kSC) copy_scales();
+  if (kCh) load_sc(0);
+  load_w(0, q0, u0);
+  load_w(1, q1, u1);
+  st.copy(xb, p.hidden, 0, buf(0), nbt);
+  wait_vm<0>();
+  __syncthreads();
+  const bool paired = kPair && (nks & 1) == 0;
+  if (paired) {
+    // weights by pairs of steps: the two halves of each 128-byte line of a
+    // row (steps 2c and 2c+1) are requested together.  Requested one step
+    // apart, about 40 % of the lines left the L2 in between and were fetched
+    // twice.  q0/q1 hold pair c, q2/q3 receive pair c+1 during step 2c.
+    u32x4 q3[2][2][Q];
+    uint32_t u3[2][2];
+    for (int ks = 0; ks < nks; ks += 2) {
+      st.copy(xb, p.hidden, ks + 1, buf(ks + 1), nbt);
+      __builtin_amdgcn_sched_barrier(0);
+      load_w(ks + 2, q2, u2);
+      load_w(ks + 3, q3, u3);
+      __builtin_amdgcn_sched_barrier(0);
+      step_mma(ks, q0, u0);
+      step_barrier<2 * kLoads>();  // step ks+1's tile has landed
+      if (ks + 2 < nks) st.copy(xb, p.hidden, ks + 2, buf(ks + 2), nbt);
+      __builtin_amdgcn_sched_barrier(0);
+      step_mma(ks + 1, q1, u1);
+      step_barrier<0>();  // step ks+2's tile and pair c+1 have landed
 #pragma unroll
-    for (int mat = 0; mat < 2; ++mat)
+      for (int mat = 0; mat < 2; ++mat)
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
+        for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int i = 0; i < Q; ++i) {
-          q0[mat][rb][i] = q1[mat][rb][i];
-          q1[mat][rb][i] = q2[mat][rb][i];
-        }
-        u0[mat][rb] = u1[mat][rb];
-        u1[mat][rb] = u2[mat][rb];
+          for (int i = 0; i < Q; ++i) {
+            q0[mat][rb][i] = q2[mat][rb][i];
+            q1[mat][rb][i] = q3[mat][rb][i];
+          }
+    }
+  } else {
+    for (int ks = 0; ks < nks; ++ks) {
+      // every fourth step (kCh): this chunk's scales out of the load
+      // registers, then the next chunk's requested (before the step's other
+      // loads, so that the end-of-step wait below still counts only the
+      // weights after the copy)
+      if (kCh && (ks & 3) == 0) {
+        take_sc();
+        load_sc((ks >> 2) + 1);
       }
+      // step ks+1's activations, then step ks+2's weights: the end-of-step
+      // wait lets the weights stay in flight
+      if (ks + 1 < nks) st.copy(xb, p.hidden, ks + 1, buf(ks + 1), nbt);
+      __builtin_amdgcn_sched_barrier(0);
+      load_w(ks + 2, q2, u2);
+      __builtin_amdgcn_sched_barrier(0);
+      step_mma(ks, q0, u0);
+      step_barrier<kLoads>();
+#pragma unroll
+      for (int mat = 0; mat < 2; ++mat)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+          for (int i = 0; i < Q; ++i) {
+            q0[mat][rb][i] = q1[mat][rb][i];
+            q1[mat][rb][i] = q2[mat][rb][i];
+          }
+          u0[mat][rb] = u1[mat][rb];
+          u1[mat][rb] = u2[mat][rb];
+        }
+    }
   }
   wait_vm<0>();  // the reloads past the end
 
@@ -450,8 +532,11 @@ __device__ __forceinline__ void down_item(const FfnParams& p, const GItem& it, c
   constexpr int Q = F::Q;
   constexpr int TB = NBT;
   constexpr int RB = kDnRows / (16 * kGWaves);  // row blocks per wavefront
-  constexpr bool kSC = SC && WT == MOE_W_MXFP4;
-  constexpr int kLoads = kSC ? RB * Q : RB * (Q + 1);
+  // scale bytes as in gate/up (SC: I a multiple of 512 and at most 2048):
+  // in LDS for up to three token blocks (kSC), in 16-byte chunks for four
+  constexpr bool kSC = SC && WT == MOE_W_MXFP4 && NBT <= 3;
+  constexpr bool kCh = SC && WT == MOE_W_MXFP4 && NBT == 4;
+  constexpr int kLoads = (kSC || kCh) ? RB * Q : RB * (Q + 1);
   const int g = lane >> 4, r16 = lane & 15;
   const bool shared = it.seg == p.n_experts;
   const int kdim = shared ? p.shared_inter : p.inter;
@@ -497,10 +582,9 @@ __device__ __forceinline__ void down_item(const FfnParams& p, const GItem& it, c
 #pragma unroll
       for (int i = 0; i < Q; ++i)
         q[rb][i] = load16(cbase + lc + 16 * rr * cb + F::code_off(k, 0) + 16 * i);
-      if (!kSC) u[rb] = sbase[ls + 16 * rr * sb + F::scale_off(k, 0)];
+      if (!kSC && !kCh) u[rb] = sbase[ls + 16 * rr * sb + F::scale_off(k, 0)];
     }
   };
-  // scale chunks, as in gate/up
   u32x4 scw[RB];
   uint32_t sp[RB];
   const int64_t srow = ls - F::scale_off(0, g);
@@ -521,6 +605,24 @@ __device__ __forceinline__ void down_item(const FfnParams& p, const GItem& it, c
       sp[rb] = v;
     }
   };
+  // scales (kSC), as in gate/up: the item's rows (up to 256, fewer in the
+  // last tile of the matrix) as one contiguous block in LDS
+  constexpr int kTokB = kSC ? 16 * NBT * 256 : TT * 256;  // bytes of one h tile
+  char* const sscale = smem + kDnScaleOff;                // [256 rows][sb]
+  auto copy_scales = [&]() {
+    const int64_t bytes = (int64_t)min(kDnRows, p.hidden - it.row0) * sb;
+    const uint8_t* src = sbase + ((shared ? 0 : (int64_t)it.seg * p.hidden) + it.row0) * sb;
+    for (int64_t o = (int64_t)wave * 1024; o < bytes; o += kGWaves * 1024)
+      if (o + lane * 16 < bytes)
+        __builtin_amdgcn_global_load_lds(
+            src + o + lane * 16, (__attribute__((address_space(3))) void*)(sscale + o), 16, 0,
+            0);
+  };
+  auto scale_byte = [&](int rb, int ks) -> uint32_t {
+    const int rr = rb < nrb ? rb : 0;
+    return *reinterpret_cast<const uint8_t*>(sscale + (64 * wave + 16 * rr + r16) * sb + ks * 4 +
+                                             g);
+  };
 
   f32x4 acc[RB][TB];
 #pragma unroll
@@ -528,11 +630,11 @@ __device__ __forceinline__ void down_item(const FfnParams& p, const GItem& it, c
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) acc[rb][tb] = f32x4{0, 0, 0, 0};
 
-  constexpr int kTile = TT * 256;
-  // h_hi of step parity b at smem + 2b * kTile, h_lo right after it
-  auto bh = [&](int b) { return smem + (b & 1) * (2 * kTile); };
-  auto bl = [&](int b) { return smem + (b & 1) * (2 * kTile) + kTile; };
-  if (kSC) load_sc(0);
+  // h_hi of step parity b at smem + 2b * kTokB, h_lo right after it
+  auto bh = [&](int b) { return smem + (b & 1) * (2 * kTokB); };
+  auto bl = [&](int b) { return smem + (b & 1) * (2 * kTokB) + kTokB; };
+  if (kSC) copy_scales();
+  if (kCh) load_sc(0);
   load_w(0, q0, u0);
   load_w(1, q1, u1);
   st.copy(p.h_hi, p.h_stride, 0, bh(0), nbt);
@@ -540,7 +642,7 @@ __device__ __forceinline__ void down_item(const FfnParams& p, const GItem& it, c
   wait_vm<0>();
   __syncthreads();
   for (int ks = 0; ks < nks; ++ks) {
-    if (kSC && (ks & 3) == 0) {
+    if (kCh && (ks & 3) == 0) {
       take_sc();
       load_sc((ks >> 2) + 1);
     }
@@ -556,7 +658,8 @@ __device__ __forceinline__ void down_item(const FfnParams& p, const GItem& it, c
     float sc[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
-      sc[rb] = ue8m0_to_f32(kSC ? (sp[rb] >> (8 * (ks & 3))) & 0xFFu : u0[rb]);
+      sc[rb] = ue8m0_to_f32(kSC ? scale_byte(rb, ks) : kCh ? (sp[rb] >> (8 * (ks & 3))) & 0xFFu
+                                                            : u0[rb]);
     bf16x8 a[2][RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) a[0][rb] = F::decode_j(q0[rb], sc[rb], 0);
@@ -679,7 +782,7 @@ hipError_t gate_up_range(const FfnParams& p, int seg_lo, int seg_hi, hipStream_t
   if (attr != hipSuccess) return attr;
   const int grid = grid_for(items_bound(p, seg_lo, seg_hi, TT, kGuRows, false));
   return launch(gemm_gate_up_kernel<WT, TT, SC>, dim3(grid), dim3(kGThreads),
-                (size_t)2 * TT * 256, stream, start, stop, p, seg_lo, seg_hi);
+                (size_t)kGemmLds, stream, start, stop, p, seg_lo, seg_hi);
 }
 
 template <int WT, int TT, bool SC>
@@ -688,7 +791,7 @@ hipError_t down_range(const FfnParams& p, int seg_lo, int seg_hi, hipStream_t st
   static const hipError_t attr = allow_lds(gemm_down_kernel<WT, TT, SC>);
   if (attr != hipSuccess) return attr;
   const int grid = grid_for(items_bound(p, seg_lo, seg_hi, TT, kDnRows, true));
-  return launch(gemm_down_kernel<WT, TT, SC>, dim3(grid), dim3(kGThreads), (size_t)4 * TT * 256,
+  return launch(gemm_down_kernel<WT, TT, SC>, dim3(grid), dim3(kGThreads), (size_t)kGemmLds,
                 stream, start, stop, p, seg_lo, seg_hi);
 }
 
@@ -707,11 +810,13 @@ hipError_t by_type(const FfnParams& p, hipStream_t stream, hipEvent_t start, hip
 
 }  // namespace
 
-// Scale chunks need 16-byte scale rows and whole chunks of four steps: a
-// reduction dimension that is a multiple of 512.
+// Scales in LDS need the scale block of an item to fit its place: H <= 4096
+// (gate/up), I <= 2048 (down); scale chunks need 16-byte scale rows and
+// whole chunks of four steps: a reduction dimension that is a multiple of
+// 512.
 hipError_t launch_gemm_gate_up(const FfnParams& p, hipStream_t stream, hipEvent_t start,
                                hipEvent_t stop) {
-  const bool sc = p.hidden % 512 == 0;
+  const bool sc = p.hidden <= 4096 && p.hidden % 512 == 0;
   return by_type(p, stream, start, stop, [&](int wt, int lo, int hi, hipEvent_t a, hipEvent_t b) {
     if (wt != MOE_W_MXFP4) return gate_up_range<MOE_W_FP8E4M3_B128, 64, false>(p, lo, hi, stream, a, b);
     return sc ? gate_up_range<MOE_W_MXFP4, 112, true>(p, lo, hi, stream, a, b)
@@ -721,7 +826,8 @@ hipError_t launch_gemm_gate_up(const FfnParams& p, hipStream_t stream, hipEvent_
 
 hipError_t launch_gemm_down(const FfnParams& p, hipStream_t stream, hipEvent_t start,
                             hipEvent_t stop) {
-  const bool sc = p.inter % 512 == 0 && (!p.has_shared || p.shared_inter % 512 == 0);
+  const bool sc = p.inter <= 2048 && p.inter % 512 == 0 &&
+                  (!p.has_shared || (p.shared_inter <= 2048 && p.shared_inter % 512 == 0));
   return by_type(p, stream, start, stop, [&](int wt, int lo, int hi, hipEvent_t a, hipEvent_t b) {
     if (wt != MOE_W_MXFP4) return down_range<MOE_W_FP8E4M3_B128, 64, false>(p, lo, hi, stream, a, b);
     return sc ? down_range<MOE_W_MXFP4, 64, true>(p, lo, hi, stream, a, b)
