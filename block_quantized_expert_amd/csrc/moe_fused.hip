@@ -447,8 +447,9 @@ __global__ __launch_bounds__(kFThreads) void decode_fused_kernel(FusedParams f) 
   // ---- 4. down: row block rb = blockIdx.x, wavefront w takes steps w, w + 16, ...
   for (int rb = blockIdx.x; rb < n_rb; rb += G) {
     // B column 0 carries the hi halves of w_a * h, column 1 the lo halves,
-    // so one MFMA takes both
-    f32x4 acc = f32x4{0, 0, 0, 0};
+    // so one MFMA takes both; two accumulators (by sub-step parity) keep
+    // consecutive MFMAs independent
+    f32x4 acc[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
     for (int ks = wave; ks < ksteps; ks += kFWaves) {
       if (!(pre && rb == (int)blockIdx.x && ks == wave)) load_down(rb, ks);
       // stage this step of w_a * h for every segment: chunk c = 16a + c16
@@ -490,13 +491,13 @@ __global__ __launch_bounds__(kFThreads) void decode_fused_kernel(FusedParams f) 
                                          : &sm.u.dn.lo[wave][a][g * 32 + 8 * j];
             const bf16x8 b = as_bf16x8(r16 < 2 ? *reinterpret_cast<const u32x4*>(src)
                                                : u32x4{0, 0, 0, 0});
-            acc = mfma_bf16(wv, b, acc);
+            acc[j & 1] = mfma_bf16(wv, b, acc[j & 1]);
           }
         }
       }
       __builtin_amdgcn_wave_barrier();  // the staged rows are read before the next step
     }
-    if (r16 < 2) sm.dn_red[wave][g][r16] = acc;
+    if (r16 < 2) sm.dn_red[wave][g][r16] = acc[0] + acc[1];
     __syncthreads();
     if (threadIdx.x < 16) {
       const int gg = threadIdx.x >> 2, r = threadIdx.x & 3;
