@@ -59,8 +59,11 @@ DEFAULTS = {  # workload: (steps, warmup, copies, pool, event_every)
 # roofline kernel is unchanged since the counters were taken are listed.
 FETCH_SCALE = 262144.0 / 131083.5
 WRITE_SCALE = 1.0
-KERNEL_TRAFFIC_KIB = {  # workload: (FETCH_SIZE, WRITE_SIZE) per dispatch
-    "decode1": (46214.3, 82.2),  # decode_fused_kernel<8>
+KERNEL_TRAFFIC_KIB = {  # workload: (FETCH_SIZE, WRITE_SIZE) per step of the roofline kernel
+    "decode1": (46171.4, 82.2),         # decode_fused_kernel<8>
+    "decode32": (472960.7, 4352.3),     # gemm_gate_up_kernel<0, 112, true>
+    "prefill512": (1156782.7, 33578.0),  # gemm_gate_up_kernel<0, 112, true>
+    "hash4096": (2312333.7, 307720.7),  # gate/up: MXFP4 routed + fp8 shared launch
 }
 
 

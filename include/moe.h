@@ -248,7 +248,8 @@ moe_status moe_ffn_forward_timed(const moe_layer* layer, const void* x, int x_ty
  * Single-token calls with bf16 activations, MXFP4 routed experts (and an
  * MXFP4 shared expert of the same width), n_experts <= 256, hidden in
  * {512, 1024, 2048, 4096} and inter a multiple of 128 up to 4096 run as one kernel
- * whose grid is exactly the workgroups the GPU holds at once (it waits for
+ * when the GPU holds at least hidden/16 of its workgroups at once (256 on
+ * MI355X); that kernel's grid is exactly the workgroups the GPU holds (it waits for
  * all of them at a grid barrier, so nothing else may keep the GPU full
  * indefinitely meanwhile); every other call runs the route+group kernel and
  * the FFN kernels of moe_ffn_forward.
