@@ -51,13 +51,23 @@ constexpr int kGWaves = kGThreads / kWave;
 constexpr int kGuRows = 32 * kGWaves;  // intermediate rows per gate/up item
 constexpr int kDnRows = 64 * kGWaves;  // hidden rows per down item
 constexpr int kSegMax = MOE_MAX_EXPERTS + 1;
-constexpr int kGemmLds = 72 * 1024;  // dynamic LDS of either kernel (two per CU)
+// dynamic LDS of either kernel; with the static item prefix (4 KiB) two
+// workgroups must fit the 160 KiB of a CU
+constexpr int kGemmLds = 74 * 1024;
 // scale blocks in LDS: after two token tiles of up to five blocks (gate/up,
 // 128 rows x H/32 bytes per matrix, H <= 4096) or two h_hi/h_lo pairs of up
 // to three blocks (down, 256 rows x I/32 bytes, I <= 2048)
 constexpr int kGuScaleOff = 2 * 16 * 5 * 256;
 constexpr int kDnScaleOff = 2 * 2 * 16 * 3 * 256;
-static_assert(kGuScaleOff + 2 * kGuRows * (4096 / 32) <= kGemmLds, "gate/up LDS");
+// gate/up: the scale bytes of two token tiles (8 per row and step, up to 128
+// rows), after the weight scales and after two full token tiles
+constexpr int kTokScaleBytes = 128 * 8;
+constexpr int kTokScaleOff = kGuScaleOff + 2 * kGuRows * (4096 / 32);
+static_assert(kTokScaleOff >= 2 * 128 * 256, "gate/up token tiles");
+static_assert(kTokScaleOff + 2 * kTokScaleBytes <= kGemmLds, "gate/up LDS");
+// dynamic LDS + the static item prefix and scan words of a workgroup (plus
+// alignment): two workgroups in the 160 KiB of a CU
+static_assert(kGemmLds + (kSegMax + 1 + kGWaves) * 4 + 64 <= 80 * 1024, "two workgroups per CU");
 static_assert(kDnScaleOff + kDnRows * (2048 / 32) <= kGemmLds, "down LDS");
 
 struct GItem {
@@ -138,9 +148,9 @@ __device__ __forceinline__ GItem find_item(const FfnParams& p, int seg_lo, int s
   return it;
 }
 
-// Token-operand staging: a tile of TT rows x 128 bf16 (256 bytes) per
-// reduction step, copied straight from global memory into LDS (no register
-// round trip).  One wavefront copy instruction fills four rows: lane l lands
+// Token-operand staging: a tile of TT rows x 256 bytes per reduction step
+// (128 bf16, or the 128 hi and 128 lo E4M3 bytes of 128 inputs), copied
+// straight from global memory into LDS (no register round trip).  One wavefront copy instruction fills four rows: lane l lands
 // at byte 16 l of the block.  In round i wavefront w fills rows
 // R i + 4w .. +3 (R = 4 * wavefronts), lane l row R i + 4w + (l >> 4),
 // 16-byte position l & 15.  Positions are swizzled, chunk c of row n sits at
@@ -149,7 +159,7 @@ __device__ __forceinline__ GItem find_item(const FfnParams& p, int seg_lo, int s
 // that belongs at its position.  Only rows below 16 * nbt are copied; rows
 // past the tile repeat a valid row: they only feed token columns that the
 // epilogue drops.
-template <int TT>
+template <int TT, bool O32 = false>
 struct Stage {
   static constexpr int kRound = 4 * kGWaves;             // rows per round
   static constexpr int kPer = (TT + kRound - 1) / kRound;  // copy rounds
@@ -160,15 +170,19 @@ struct Stage {
     return kRound * i + 4 * wave + (lane >> 4);
   }
   __device__ void init(int lane) { chunk = (lane & 15) ^ ((4 * wave_id() + (lane >> 4)) & 15); }
-  __device__ void copy(const __bf16* base, int64_t stride, int ks, char* buf, int nbt) const {
-    const int c = ks * 128 + chunk * 8;
+  // rows of `stride` bytes, 256 bytes per step; O32: every offset into the
+  // buffer is below 2^31 (one address register per row instead of two)
+  __device__ void copy(const void* base, int64_t stride, int ks, char* buf, int nbt) const {
+    const int64_t c = ks * 256 + chunk * 16;
     const int w = wave_id();
     char* dst = buf + (4 * w) * 256;
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
       if (kRound * i + 4 * w < 16 * nbt)
         __builtin_amdgcn_global_load_lds(
-            base + (int64_t)row[i] * stride + c,
+            static_cast<const char*>(base) +
+                (O32 ? (int64_t)(uint32_t)(row[i] * (uint32_t)stride + (uint32_t)c)
+                     : (int64_t)row[i] * stride + c),
             (__attribute__((address_space(3))) void*)(dst + i * kRound * 256), 16, 0, 0);
   }
 };
@@ -190,13 +204,17 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 // End of a reduction step: this wavefront's copies into LDS have landed
-// (at most N later loads, the weights of a later step, still in flight),
-// then the workgroup barrier.  A plain barrier, not __syncthreads(): its
-// release fence would also wait for those later weight loads.  The LDS
-// reads of the step are complete here, since the MFMAs consumed them.
+// (at most N later loads, the weights of a later step, still in flight) and
+// its LDS reads of the step are complete (lgkmcnt 0), then the workgroup
+// barrier; after it the next copies may overwrite the step's buffer.  The
+// compiler may place the barrier above the step's MFMAs (they touch no
+// memory), so the read wait cannot be left to their operand waits.  A plain
+// barrier, not __syncthreads(): its release fence would also wait for the
+// later weight loads.
 template <int N>
 __device__ __forceinline__ void step_barrier() {
-  wait_vm<N>();
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4));
   __builtin_amdgcn_s_barrier();
 }
 
@@ -229,25 +247,107 @@ __device__ __forceinline__ void dispatch_nbt(int n, Fn&& f) {
 
 // ------------------------------------------------------------- gate/up
 
+// The activations enter the matrix cores as E4M3 with one UE8M0 scale per 32
+// inputs, in two parts that reproduce the bf16 value exactly.  For the 32
+// inputs of a block let e be the exponent of the largest magnitude; with
+// f = x / 2^(e-7) (|f| < 256), hi = f rounded to E4M3 (4 significant bits)
+// and lo = (f - hi) * 16, which is exact in E4M3 as well: f carries at most 8
+// significant bits, its bits below hi's span at most 4 more, and
+// |lo| <= 16 * |f| / 8 < 448.  Inputs below 2^-13 of the block's largest
+// magnitude leave the E4M3 normal range and keep fewer bits (an absolute
+// error under 2^(e-17)).  hi is scaled by 2^(e-7), lo by 2^(e-11).
+//
+// Layout: xq [token][hidden/128][256 bytes] = per 128 inputs the 128 hi bytes
+// then the 128 lo bytes, in input order; xs [token][hidden/32][2 bytes] = the
+// hi and lo scale bytes of each block.  One thread per block.
+__global__ __launch_bounds__(256) void quant_x_kernel(FfnParams p) {
+  const int nb = p.hidden / 32;
+  const int64_t blk = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (blk >= (int64_t)p.n_tokens * nb) return;
+  const int64_t t = blk / nb;
+  const int j = (int)(blk - t * nb);
+  const __bf16* src = static_cast<const __bf16*>(p.x) + t * p.hidden + 32 * j;
+  u32x4 v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = load16(src + 8 * i);
+  uint32_t mag = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) mag = max(mag, max(v[i][c] & 0x7FFFu, (v[i][c] >> 16) & 0x7FFFu));
+  // bf16 keeps fp32's exponent field: bits 14:7 of the magnitude.  The hi
+  // scale byte is that biased exponent minus 7, kept at least 4 so that the
+  // lo scale byte (minus 4 more) stays a valid UE8M0 value.
+  const int sb = min(max((int)(mag >> 7) - 7, 4), 254);
+  const float inv = __uint_as_float((uint32_t)(254 - sb) << 23);  // 2^(127 - sb)
+  uint32_t hw[8], lw[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int c = 0; c < 4; c += 2) {
+      // four inputs: the bf16 pairs of words c and c+1
+      float f[4];
+      f[0] = __uint_as_float(v[i][c] << 16) * inv;
+      f[1] = __uint_as_float(v[i][c] & 0xFFFF0000u) * inv;
+      f[2] = __uint_as_float(v[i][c + 1] << 16) * inv;
+      f[3] = __uint_as_float(v[i][c + 1] & 0xFFFF0000u) * inv;
+      int h = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+      h = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], h, true);
+      const auto d0 = __builtin_amdgcn_cvt_pk_f32_fp8(h, false);
+      const auto d1 = __builtin_amdgcn_cvt_pk_f32_fp8(h, true);
+      int l = __builtin_amdgcn_cvt_pk_fp8_f32((f[0] - d0[0]) * 16.0f, (f[1] - d0[1]) * 16.0f, 0,
+                                              false);
+      l = __builtin_amdgcn_cvt_pk_fp8_f32((f[2] - d1[0]) * 16.0f, (f[3] - d1[1]) * 16.0f, l, true);
+      hw[2 * i + c / 2] = (uint32_t)h;
+      lw[2 * i + c / 2] = (uint32_t)l;
+    }
+  uint8_t* dst = p.xq + t * 2 * (int64_t)p.hidden + (j >> 2) * 256 + (j & 3) * 32;
+  *reinterpret_cast<u32x4*>(dst) = u32x4{hw[0], hw[1], hw[2], hw[3]};
+  *reinterpret_cast<u32x4*>(dst + 16) = u32x4{hw[4], hw[5], hw[6], hw[7]};
+  *reinterpret_cast<u32x4*>(dst + 128) = u32x4{lw[0], lw[1], lw[2], lw[3]};
+  *reinterpret_cast<u32x4*>(dst + 144) = u32x4{lw[4], lw[5], lw[6], lw[7]};
+  reinterpret_cast<uint16_t*>(p.xs)[blk] = (uint16_t)(sb | ((sb - 4) << 8));
+}
+
+// The weight operand of one 16x16x128 tile from the lane's code bytes: MXFP4,
+// the lane's 32-input block (16 bytes); fp8, the bytes of inputs 16g .. +15
+// and 64 + 16g .. +15 (q[0], q[1]).
+template <int WT>
+__device__ __forceinline__ i32x8 weight_operand(const u32x4 (&q)[Fmt<WT>::Q]) {
+  if constexpr (WT == MOE_W_MXFP4)
+    return i32x8{(int)q[0][0], (int)q[0][1], (int)q[0][2], (int)q[0][3], 0, 0, 0, 0};
+  else
+    return i32x8{(int)q[0][0], (int)q[0][1], (int)q[0][2], (int)q[0][3],
+                 (int)q[1][0], (int)q[1][1], (int)q[1][2], (int)q[1][3]};
+}
+
+// 16 bytes of an LDS tile row: chunk c of row n sits at position c ^ (n & 15).
+__device__ __forceinline__ u32x4 tile_chunk(const char* row, int c, int r16) {
+  return *reinterpret_cast<const u32x4*>(row + ((c ^ r16) << 4));
+}
+
+__device__ __forceinline__ i32x8 join8(u32x4 a, u32x4 b) {
+  return i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2],
+               (int)b[3]};
+}
+
 // NBT = token blocks of the tile (ceil(m / 16)), a compile-time constant so
-// that a step's fragment reads and MFMAs form one branch-free block.
-template <int WT, int TT, int NBT, bool SC>
+// that a step's operand reads and MFMAs form one branch-free block.
+template <int WT, int TT, int NBT, bool SC, bool O32>
 __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it, char* smem,
                                              int wave, int lane) {
   using F = Fmt<WT>;
   constexpr int Q = F::Q;
   constexpr int TB = NBT;
+  constexpr int FA = WT == MOE_W_MXFP4 ? 4 : 0;  // operand format of the weights
   // Scale bytes (SC: MXFP4, H a multiple of 512 and at most 4096):
   //  - up to five token blocks: the item's scales sit in LDS (kSC, below);
   //  - six: 16-byte chunks of four steps in registers (kCh, below);
-  //  - otherwise (and seven blocks, whose registers are full): one byte per
-  //    row and step, loaded with the step's codes.
+  //  - otherwise (and seven blocks): one byte per row and step, loaded with
+  //    the step's codes.
   constexpr bool kSC = SC && WT == MOE_W_MXFP4 && NBT <= 5;
   constexpr bool kCh = SC && WT == MOE_W_MXFP4 && NBT == 6;
   constexpr int kLoads = (kSC || kCh) ? 4 * Q : 4 * (Q + 1);  // vector loads of one step's weights
-  // weights by pairs of steps (below) for up to four token blocks and an
-  // even number of steps
-  constexpr bool kPair = kSC && NBT <= 4;
   const int g = lane >> 4, r16 = lane & 15;
   const bool shared = it.seg == p.n_experts;
   const int rows = shared ? p.shared_inter : p.inter;
@@ -263,33 +363,48 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
   const int wrow = it.row0 + 32 * wave;
   const bool live = wrow < rows;
   const int64_t lrow = (shared ? 0 : (int64_t)it.seg * rows) + (live ? wrow : it.row0) + r16;
-  const int64_t lc = lrow * cb + F::code_off(0, g), ls = lrow * sb + F::scale_off(0, g);
+  // code bytes of a step: MXFP4 16 at 16g; fp8 16 at 16g and 16 at 64 + 16g
+  const int64_t lc = lrow * cb + 16 * g, ls = lrow * sb + F::scale_off(0, g);
   const uint8_t* cbase[2] = {shared ? p.sgate_c : p.gate_c, shared ? p.sup_c : p.up_c};
   const uint8_t* sbase[2] = {shared ? p.sgate_s : p.gate_s, shared ? p.sup_s : p.up_s};
+  // the wavefront's first row as a uniform base, the lane's rows as a 32-bit
+  // offset (32 rows of at most H bytes), so a load needs one address register
+  const int64_t wrow_g = (shared ? 0 : (int64_t)it.seg * rows) + (live ? wrow : it.row0);
+  const uint8_t* cwave[2] = {cbase[0] + wrow_g * cb, cbase[1] + wrow_g * cb};
+  const uint32_t lco = (uint32_t)(r16 * cb) + 16 * g;
 
-  // activation rows copied by this lane (rows past the tile repeat row 0)
-  Stage<TT> st;
+  // Token rows of this lane's copies (rows past the tile repeat row 0): the
+  // 256-byte step rows of xq through Stage, and one 4-byte half of a row's
+  // 8 scale bytes per step (wavefront w copies rows 32w .. 32w+31, a lane
+  // pair per row).
+  using St = Stage<TT, O32>;
+  St st;
   st.init(lane);
+  int srow;
   {
     // all perm loads first (clamped into perm; the shared expert needs none)
-    int pv[Stage<TT>::kPer];
+    int pv[St::kPer];
 #pragma unroll
-    for (int i = 0; i < Stage<TT>::kPer; ++i) {
-      const int n = Stage<TT>::row_of(i, wave, lane);
+    for (int i = 0; i < St::kPer; ++i) {
+      const int n = St::row_of(i, wave, lane);
       pv[i] = p.perm[min(it.slot0 + (n < it.m ? n : 0), nk - 1)];
     }
+    const int ns = 32 * wave + (lane >> 1);
+    const int slot_s = it.slot0 + (ns < it.m ? ns : 0);
+    const int pvs = p.perm[min(slot_s, nk - 1)];
 #pragma unroll
-    for (int i = 0; i < Stage<TT>::kPer; ++i) {
-      const int n = Stage<TT>::row_of(i, wave, lane);
+    for (int i = 0; i < St::kPer; ++i) {
+      const int n = St::row_of(i, wave, lane);
       const int slot = it.slot0 + (n < it.m ? n : 0);
       st.row[i] = shared ? slot - nk : pv[i] / p.top_k;
     }
+    srow = shared ? slot_s - nk : pvs / p.top_k;
   }
-  const __bf16* xb = static_cast<const __bf16*>(p.x);
+  const uint8_t* xsl = p.xs + (int64_t)srow * (p.hidden / 16) + 4 * (lane & 1);
 
-  // weight codes: the current step and the next two
-  u32x4 q0[2][2][Q], q1[2][2][Q], q2[2][2][Q];
-  uint32_t u0[2][2], u1[2][2], u2[2][2];
+  // weight codes: the current step and the next
+  u32x4 q0[2][2][Q], q1[2][2][Q];
+  uint32_t u0[2][2], u1[2][2];
   auto load_w = [&](int ks, u32x4 (&q)[2][2][Q], uint32_t (&u)[2][2]) {
     const int k = min(ks, nks - 1);  // past the end: reload the last step
 #pragma unroll
@@ -298,7 +413,7 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
       for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
         for (int i = 0; i < Q; ++i)
-          q[mat][rb][i] = load16(cbase[mat] + lc + 16 * rb * cb + F::code_off(k, 0) + 16 * i);
+          q[mat][rb][i] = load16(cwave[mat] + (lco + (uint32_t)(16 * rb * cb + F::code_off(k, 0) + 64 * i)));
         if (!kSC && !kCh) u[mat][rb] = sbase[mat][ls + 16 * rb * sb + F::scale_off(k, 0)];
       }
   };
@@ -309,14 +424,14 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
   // copy avoids; it is the fallback where that copy does not fit.)
   u32x4 scw[2][2];
   uint32_t sp[2][2];
-  const int64_t srow = ls - F::scale_off(0, g);
+  const int64_t srow_w = ls - F::scale_off(0, g);
   auto load_sc = [&](int c) {
     const int cc = min(c, nks / 4 - 1);
 #pragma unroll
     for (int mat = 0; mat < 2; ++mat)
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
-        scw[mat][rb] = load16(sbase[mat] + srow + 16 * rb * sb + 16 * cc);
+        scw[mat][rb] = load16(sbase[mat] + srow_w + 16 * rb * sb + 16 * cc);
   };
   auto take_sc = [&]() {
 #pragma unroll
@@ -364,117 +479,94 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) acc[mat][rb][tb] = f32x4{0, 0, 0, 0};
 
-  // buffer b at smem + b * TT * 256 (offsets from smem keep LDS addressing)
+  // token tile b at smem + b * kTokB, its scales at kTokScaleOff + b * 1 KiB
+  // (offsets from smem keep LDS addressing)
   auto buf = [&](int b) { return smem + (b & 1) * kTokB; };
+  auto tsb = [&](int b) { return smem + kTokScaleOff + (b & 1) * kTokScaleBytes; };
+  // step ks's activations (rows and scale bytes) into buffer ks & 1
+  auto copy_tok = [&](int ks) {
+    st.copy(p.xq, 2 * (int64_t)p.hidden, ks, buf(ks), nbt);
+    if (32 * wave < 16 * nbt)
+      __builtin_amdgcn_global_load_lds(
+          xsl + ks * 8, (__attribute__((address_space(3))) void*)(tsb(ks) + 256 * wave), 4, 0, 0);
+  };
   // one reduction step: step ks's weights qq (and their scale bytes uu, when
-  // not chunked) times the token tile in LDS
+  // not chunked) times the token tile in LDS, hi and lo parts
   auto step_mma = [&](int ks, const u32x4 (&qq)[2][2][Q], const uint32_t (&uu)[2][2]) {
     const char* cur = buf(ks);
-    float sc[2][2];
+    const char* cts = tsb(ks);
+    uint32_t sa[2][2];
+    i32x8 a[2][2];
 #pragma unroll
     for (int mat = 0; mat < 2; ++mat)
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-        sc[mat][rb] = ue8m0_to_f32(kSC   ? scale_byte(mat, rb, ks)
-                                   : kCh ? (sp[mat][rb] >> (8 * (ks & 3))) & 0xFFu
-                                         : uu[mat][rb]);
-    // sub-step j+1 is decoded while sub-step j multiplies, so the converts
-    // overlap the matrix-core work
-    bf16x8 a[2][2][2];
-#pragma unroll
-    for (int mat = 0; mat < 2; ++mat)
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) a[0][mat][rb] = F::decode_j(qq[mat][rb], sc[mat][rb], 0);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (j + 1 < 4) {
-#pragma unroll
-        for (int mat = 0; mat < 2; ++mat)
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb)
-            a[(j + 1) & 1][mat][rb] = F::decode_j(qq[mat][rb], sc[mat][rb], j + 1);
+      for (int rb = 0; rb < 2; ++rb) {
+        sa[mat][rb] = kSC ? scale_byte(mat, rb, ks) : kCh ? sp[mat][rb] >> (8 * (ks & 3)) : uu[mat][rb];
+        a[mat][rb] = weight_operand<WT>(qq[mat][rb]);
       }
+    // operand u = 2 tb + part (part 0: hi bytes, chunks g and 4+g; part 1:
+    // lo bytes, chunks 8+g and 12+g) is read while operand u-1 multiplies,
+    // so two 8-register operands are live at a time
+    i32x8 bop[2];
+    uint32_t sbt[2];
+    auto read_op = [&](int u) {
+      const int n = (u >> 1) * 16 + r16;
+      const char* row = cur + n * 256;
+      const int c0 = (u & 1) * 8 + g;
+      bop[u & 1] = join8(tile_chunk(row, c0, r16), tile_chunk(row, c0 + 4, r16));
+      if ((u & 1) == 0) sbt[(u >> 1) & 1] = *reinterpret_cast<const uint16_t*>(cts + n * 8 + 2 * g);
+    };
+    read_op(0);
 #pragma unroll
-      for (int tb = 0; tb < TB; ++tb) {
-        const bf16x8 b = token_frag(cur, tb, j, g, r16);
+    for (int u = 0; u < 2 * TB; ++u) {
+      if (u + 1 < 2 * TB) read_op(u + 1);
+      const int tb = u >> 1;
 #pragma unroll
-        for (int mat = 0; mat < 2; ++mat)
+      for (int mat = 0; mat < 2; ++mat)
 #pragma unroll
-          for (int rb = 0; rb < 2; ++rb)
-            acc[mat][rb][tb] = mfma_bf16(a[j & 1][mat][rb], b, acc[mat][rb][tb]);
-      }
-      // keep two sub-steps' fragments live at a time
+        for (int rb = 0; rb < 2; ++rb) {
+          if ((u & 1) == 0)
+            acc[mat][rb][tb] = mfma_scaled<FA, 0, 0>(a[mat][rb], bop[0], acc[mat][rb][tb],
+                                                     sa[mat][rb], sbt[tb & 1]);
+          else
+            acc[mat][rb][tb] = mfma_scaled<FA, 0, 1>(a[mat][rb], bop[1], acc[mat][rb][tb],
+                                                     sa[mat][rb], sbt[tb & 1]);
+        }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
   if (kSC) copy_scales();
   if (kCh) load_sc(0);
   load_w(0, q0, u0);
-  load_w(1, q1, u1);
-  st.copy(xb, p.hidden, 0, buf(0), nbt);
+  copy_tok(0);
   wait_vm<0>();
   __syncthreads();
-  const bool paired = kPair && (nks & 1) == 0;
-  if (paired) {
-    // weights by pairs of steps: the two halves of each 128-byte line of a
-    // row (steps 2c and 2c+1) are requested together.  Requested one step
-    // apart, about 40 % of the lines left the L2 in between and were fetched
-    // twice.  q0/q1 hold pair c, q2/q3 receive pair c+1 during step 2c.
-    u32x4 q3[2][2][Q];
-    uint32_t u3[2][2];
-    for (int ks = 0; ks < nks; ks += 2) {
-      st.copy(xb, p.hidden, ks + 1, buf(ks + 1), nbt);
-      __builtin_amdgcn_sched_barrier(0);
-      load_w(ks + 2, q2, u2);
-      load_w(ks + 3, q3, u3);
-      __builtin_amdgcn_sched_barrier(0);
-      step_mma(ks, q0, u0);
-      step_barrier<2 * kLoads>();  // step ks+1's tile has landed
-      if (ks + 2 < nks) st.copy(xb, p.hidden, ks + 2, buf(ks + 2), nbt);
-      __builtin_amdgcn_sched_barrier(0);
-      step_mma(ks + 1, q1, u1);
-      step_barrier<0>();  // step ks+2's tile and pair c+1 have landed
-#pragma unroll
-      for (int mat = 0; mat < 2; ++mat)
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-          for (int i = 0; i < Q; ++i) {
-            q0[mat][rb][i] = q2[mat][rb][i];
-            q1[mat][rb][i] = q3[mat][rb][i];
-          }
+  for (int ks = 0; ks < nks; ++ks) {
+    // every fourth step (kCh): this chunk's scales out of the load
+    // registers, then the next chunk's requested (before the step's other
+    // loads, so that the end-of-step wait below still counts only the
+    // weights after the copy)
+    if (kCh && (ks & 3) == 0) {
+      take_sc();
+      load_sc((ks >> 2) + 1);
     }
-  } else {
-    for (int ks = 0; ks < nks; ++ks) {
-      // every fourth step (kCh): this chunk's scales out of the load
-      // registers, then the next chunk's requested (before the step's other
-      // loads, so that the end-of-step wait below still counts only the
-      // weights after the copy)
-      if (kCh && (ks & 3) == 0) {
-        take_sc();
-        load_sc((ks >> 2) + 1);
+    // step ks+1's activations, then its weights (one step ahead: the step
+    // ends by moving them into q0, so a deeper register ring would only
+    // wait for its loads at the same place)
+    if (ks + 1 < nks) copy_tok(ks + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(ks + 1, q1, u1);
+    __builtin_amdgcn_sched_barrier(0);
+    step_mma(ks, q0, u0);
+    step_barrier<kLoads>();  // the copies have landed (the weights in flight)
+#pragma unroll
+    for (int mat = 0; mat < 2; ++mat)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+        for (int i = 0; i < Q; ++i) q0[mat][rb][i] = q1[mat][rb][i];
+        u0[mat][rb] = u1[mat][rb];
       }
-      // step ks+1's activations, then step ks+2's weights: the end-of-step
-      // wait lets the weights stay in flight
-      if (ks + 1 < nks) st.copy(xb, p.hidden, ks + 1, buf(ks + 1), nbt);
-      __builtin_amdgcn_sched_barrier(0);
-      load_w(ks + 2, q2, u2);
-      __builtin_amdgcn_sched_barrier(0);
-      step_mma(ks, q0, u0);
-      step_barrier<kLoads>();
-#pragma unroll
-      for (int mat = 0; mat < 2; ++mat)
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-#pragma unroll
-          for (int i = 0; i < Q; ++i) {
-            q0[mat][rb][i] = q1[mat][rb][i];
-            q1[mat][rb][i] = q2[mat][rb][i];
-          }
-          u0[mat][rb] = u1[mat][rb];
-          u1[mat][rb] = u2[mat][rb];
-        }
-    }
   }
   wait_vm<0>();  // the reloads past the end
 
@@ -503,7 +595,7 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
     }
 }
 
-template <int WT, int TT, bool SC>
+template <int WT, int TT, bool SC, bool O32>
 __global__ __launch_bounds__(kGThreads, 2) void gemm_gate_up_kernel(FfnParams p, int seg_lo,
                                                                      int seg_hi) {
   extern __shared__ __align__(16) char smem[];
@@ -517,7 +609,7 @@ __global__ __launch_bounds__(kGThreads, 2) void gemm_gate_up_kernel(FfnParams p,
     if (item < 0) continue;
     const GItem it = find_item<TT, kGuRows, false>(p, seg_lo, seg_hi, s_pref, item);
     dispatch_nbt<TT / 16>((it.m + 15) >> 4, [&](auto nb) {
-      gate_up_item<WT, TT, decltype(nb)::value, SC>(p, it, smem, wave, lane);
+      gate_up_item<WT, TT, decltype(nb)::value, SC, O32>(p, it, smem, wave, lane);
     });
     __syncthreads();  // the LDS tiles are reused by the next item
   }
@@ -637,8 +729,8 @@ __device__ __forceinline__ void down_item(const FfnParams& p, const GItem& it, c
   if (kCh) load_sc(0);
   load_w(0, q0, u0);
   load_w(1, q1, u1);
-  st.copy(p.h_hi, p.h_stride, 0, bh(0), nbt);
-  st.copy(p.h_lo, p.h_stride, 0, bl(0), nbt);
+  st.copy(p.h_hi, 2 * p.h_stride, 0, bh(0), nbt);
+  st.copy(p.h_lo, 2 * p.h_stride, 0, bl(0), nbt);
   wait_vm<0>();
   __syncthreads();
   for (int ks = 0; ks < nks; ++ks) {
@@ -647,8 +739,8 @@ __device__ __forceinline__ void down_item(const FfnParams& p, const GItem& it, c
       load_sc((ks >> 2) + 1);
     }
     if (ks + 1 < nks) {
-      st.copy(p.h_hi, p.h_stride, ks + 1, bh(ks + 1), nbt);
-      st.copy(p.h_lo, p.h_stride, ks + 1, bl(ks + 1), nbt);
+      st.copy(p.h_hi, 2 * p.h_stride, ks + 1, bh(ks + 1), nbt);
+      st.copy(p.h_lo, 2 * p.h_stride, ks + 1, bl(ks + 1), nbt);
     }
     __builtin_amdgcn_sched_barrier(0);
     load_w(ks + 2, q2, u2);
@@ -775,13 +867,13 @@ int grid_for(int64_t items) {
   return (int)(items < kGemmGrid ? (items > 0 ? items : 1) : kGemmGrid);
 }
 
-template <int WT, int TT, bool SC>
+template <int WT, int TT, bool SC, bool O32>
 hipError_t gate_up_range(const FfnParams& p, int seg_lo, int seg_hi, hipStream_t stream,
                          hipEvent_t start, hipEvent_t stop) {
-  static const hipError_t attr = allow_lds(gemm_gate_up_kernel<WT, TT, SC>);
+  static const hipError_t attr = allow_lds(gemm_gate_up_kernel<WT, TT, SC, O32>);
   if (attr != hipSuccess) return attr;
   const int grid = grid_for(items_bound(p, seg_lo, seg_hi, TT, kGuRows, false));
-  return launch(gemm_gate_up_kernel<WT, TT, SC>, dim3(grid), dim3(kGThreads),
+  return launch(gemm_gate_up_kernel<WT, TT, SC, O32>, dim3(grid), dim3(kGThreads),
                 (size_t)kGemmLds, stream, start, stop, p, seg_lo, seg_hi);
 }
 
@@ -817,10 +909,21 @@ hipError_t by_type(const FfnParams& p, hipStream_t stream, hipEvent_t start, hip
 hipError_t launch_gemm_gate_up(const FfnParams& p, hipStream_t stream, hipEvent_t start,
                                hipEvent_t stop) {
   const bool sc = p.hidden <= 4096 && p.hidden % 512 == 0;
-  return by_type(p, stream, start, stop, [&](int wt, int lo, int hi, hipEvent_t a, hipEvent_t b) {
-    if (wt != MOE_W_MXFP4) return gate_up_range<MOE_W_FP8E4M3_B128, 64, false>(p, lo, hi, stream, a, b);
-    return sc ? gate_up_range<MOE_W_MXFP4, 112, true>(p, lo, hi, stream, a, b)
-              : gate_up_range<MOE_W_MXFP4, 112, false>(p, lo, hi, stream, a, b);
+  const int64_t blocks = (int64_t)p.n_tokens * (p.hidden / 32);
+  const hipError_t e = launch(quant_x_kernel, dim3((unsigned)((blocks + 255) / 256)), dim3(256),
+                              0, stream, start, nullptr, p);
+  if (e != hipSuccess) return e;
+  // 32-bit offsets into the quantized activations (below 2 GiB: batches up
+  // to 262144 tokens at H 4096); the larger ones take 64-bit addresses and
+  // no LDS scales
+  const bool o32 = (int64_t)p.n_tokens * 2 * p.hidden < ((int64_t)1 << 31);
+  return by_type(p, stream, nullptr, stop, [&](int wt, int lo, int hi, hipEvent_t a, hipEvent_t b) {
+    if (wt != MOE_W_MXFP4)
+      return o32 ? gate_up_range<MOE_W_FP8E4M3_B128, 64, false, true>(p, lo, hi, stream, a, b)
+                 : gate_up_range<MOE_W_FP8E4M3_B128, 64, false, false>(p, lo, hi, stream, a, b);
+    if (!o32) return gate_up_range<MOE_W_MXFP4, 112, false, false>(p, lo, hi, stream, a, b);
+    return sc ? gate_up_range<MOE_W_MXFP4, 112, true, true>(p, lo, hi, stream, a, b)
+              : gate_up_range<MOE_W_MXFP4, 112, false, true>(p, lo, hi, stream, a, b);
   });
 }
 

@@ -107,10 +107,14 @@ moe_status plan_ffn(const moe_layer* layer, int n_tokens, FfnPlan* plan) {
   plan->h_stride = hs;
   const size_t h_bytes = align_up((size_t)(plan->slots * hs) * 2u, 256);
   const size_t o_bytes = align_up((size_t)(plan->slots * layer->hidden) * 4u, 256);
+  const size_t xq_bytes = align_up((size_t)n * layer->hidden * 2u, 256);
+  const size_t xs_bytes = align_up((size_t)n * (layer->hidden / 16), 256);
   plan->off_h_hi = 0;
   plan->off_h_lo = h_bytes;
   plan->off_obuf = 2 * h_bytes;
-  plan->total = 2 * h_bytes + o_bytes;
+  plan->off_xq = 2 * h_bytes + o_bytes;
+  plan->off_xs = plan->off_xq + xq_bytes;
+  plan->total = plan->off_xs + xs_bytes;
   return MOE_OK;
 }
 

@@ -16,6 +16,9 @@ namespace moe {
 //   obuf       : fp32 [slots][hidden]     weighted expert outputs (used when
 //                                         the batch is too large for the
 //                                         single-pass down + combine)
+//   xq         : u8 [n_tokens][2*hidden]  bf16 activations as E4M3 hi and lo
+//                                         parts (grouped-GEMM gate/up)
+//   xs         : u8 [n_tokens][hidden/16] their scale bytes
 // A slot is one (token, routed expert) pair in grouped order
 // (p in [0, n_tokens*top_k)) or, for the shared expert, n_tokens*top_k + t.
 struct FfnPlan {
@@ -24,6 +27,8 @@ struct FfnPlan {
   size_t off_h_hi;
   size_t off_h_lo;
   size_t off_obuf;
+  size_t off_xq;
+  size_t off_xs;
   size_t total;
 };
 

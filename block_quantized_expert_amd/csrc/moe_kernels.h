@@ -28,6 +28,11 @@ struct FfnParams {
   const int32_t* offsets;
   const int32_t* perm;
   const int32_t* inv_perm;
+  // bf16 activations of the grouped-GEMM path as two E4M3 parts:
+  // xq [n_tokens][hidden/128][256] (per 128 inputs 128 hi bytes, 128 lo
+  // bytes), xs [n_tokens][hidden/32][2] (their UE8M0 scale bytes)
+  uint8_t* xq;
+  uint8_t* xs;
   __bf16* h_hi;  // [slots][h_stride]
   __bf16* h_lo;
   int64_t h_stride;

@@ -69,7 +69,9 @@ def test_ffn_workspace_bytes():
     slots = n * 6 + n
     h = -(-slots * 2048 * 2 // 256) * 256
     o = -(-slots * 4096 * 4 // 256) * 256
-    assert B.lib().moe_ffn_workspace_bytes(ctypes.byref(L), n) == 2 * h + o
+    xq = n * 4096 * 2          # activations as two E4M3 parts
+    xs = n * 4096 // 16        # their scale bytes
+    assert B.lib().moe_ffn_workspace_bytes(ctypes.byref(L), n) == 2 * h + o + xq + xs
     assert B.lib().moe_ffn_workspace_bytes(ctypes.byref(L), 0) == 0
     assert B.lib().moe_ffn_workspace_bytes(ctypes.byref(_layer(hidden=100)), 8) == 0
     assert B.lib().moe_ffn_workspace_bytes(None, 8) == 0
