@@ -664,8 +664,9 @@ __device__ __forceinline__ void down_item(const FfnParams& p, const GItem& it, c
     wcol[tb] = shared ? 1.0f : p.topk_w[p.perm[it.slot0 + n]];
   }
 
-  u32x4 q0[RB][Q], q1[RB][Q], q2[RB][Q];
-  uint32_t u0[RB], u1[RB], u2[RB];
+  // weight codes of the current step and the next
+  u32x4 q0[RB][Q], q1[RB][Q];
+  uint32_t u0[RB], u1[RB];
   auto load_w = [&](int ks, u32x4 (&q)[RB][Q], uint32_t (&u)[RB]) {
     const int k = min(ks, nks - 1);
 #pragma unroll
@@ -728,7 +729,6 @@ __device__ __forceinline__ void down_item(const FfnParams& p, const GItem& it, c
   if (kSC) copy_scales();
   if (kCh) load_sc(0);
   load_w(0, q0, u0);
-  load_w(1, q1, u1);
   st.copy(p.h_hi, 2 * p.h_stride, 0, bh(0), nbt);
   st.copy(p.h_lo, 2 * p.h_stride, 0, bl(0), nbt);
   wait_vm<0>();
@@ -743,7 +743,9 @@ __device__ __forceinline__ void down_item(const FfnParams& p, const GItem& it, c
       st.copy(p.h_lo, 2 * p.h_stride, ks + 1, bl(ks + 1), nbt);
     }
     __builtin_amdgcn_sched_barrier(0);
-    load_w(ks + 2, q2, u2);
+    // the next step's weights (one step ahead: the step ends by moving them
+    // into q0, so a deeper register ring would only wait for its loads there)
+    load_w(ks + 1, q1, u1);
     __builtin_amdgcn_sched_barrier(0);
     const char* curh = bh(ks);
     const char* curl = bl(ks);
@@ -779,12 +781,8 @@ __device__ __forceinline__ void down_item(const FfnParams& p, const GItem& it, c
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-      for (int i = 0; i < Q; ++i) {
-        q0[rb][i] = q1[rb][i];
-        q1[rb][i] = q2[rb][i];
-      }
+      for (int i = 0; i < Q; ++i) q0[rb][i] = q1[rb][i];
       u0[rb] = u1[rb];
-      u1[rb] = u2[rb];
     }
   }
   wait_vm<0>();
