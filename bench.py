@@ -59,11 +59,11 @@ DEFAULTS = {  # workload: (steps, warmup, copies, pool, event_every)
 # roofline kernel is unchanged since the counters were taken are listed.
 FETCH_SCALE = 262144.0 / 131083.5
 WRITE_SCALE = 1.0
-KERNEL_TRAFFIC_KIB = {  # workload: (FETCH_SIZE, WRITE_SIZE) per step of the roofline kernel
-    "decode1": (46171.4, 82.2),         # decode_fused_kernel<8>
-    "decode32": (472960.7, 4352.3),     # gemm_gate_up_kernel<0, 112, true>
-    "prefill512": (1156782.7, 33578.0),  # gemm_gate_up_kernel<0, 112, true>
-    "hash4096": (2312333.7, 307720.7),  # gate/up: MXFP4 routed + fp8 shared launch
+KERNEL_TRAFFIC_KIB = {  # workload: (FETCH_SIZE, WRITE_SIZE) per step of the roofline stage
+    "decode1": (46171.7, 82.2),           # decode_fused_kernel<8>
+    "decode32": (474731.0, 2056.2),       # quant_x_kernel + gemm_gate_up_kernel<0, 112, true, true>
+    "prefill512": (1179494.4, 35260.2),   # quant_x_kernel + gemm_gate_up_kernel<0, 112, true, true>
+    "hash4096": (2533715.7, 329450.5),    # quant_x_kernel + MXFP4 routed and fp8 shared gate/up
 }
 
 
