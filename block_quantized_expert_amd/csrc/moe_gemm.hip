@@ -342,11 +342,12 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
   constexpr int FA = WT == MOE_W_MXFP4 ? 4 : 0;  // operand format of the weights
   // Scale bytes (SC: MXFP4, H a multiple of 512 and at most 4096):
   //  - up to five token blocks: the item's scales sit in LDS (kSC, below);
-  //  - six: 16-byte chunks of four steps in registers (kCh, below);
-  //  - otherwise (and seven blocks): one byte per row and step, loaded with
-  //    the step's codes.
+  //  - six and seven: 16-byte chunks of four steps in registers (kCh,
+  //    below): a byte load per row and step would add as many memory
+  //    requests as the weight codes themselves;
+  //  - otherwise: one byte per row and step, loaded with the step's codes.
   constexpr bool kSC = SC && WT == MOE_W_MXFP4 && NBT <= 5;
-  constexpr bool kCh = SC && WT == MOE_W_MXFP4 && NBT == 6;
+  constexpr bool kCh = SC && WT == MOE_W_MXFP4 && NBT >= 6;
   constexpr int kLoads = (kSC || kCh) ? 4 * Q : 4 * (Q + 1);  // vector loads of one step's weights
   const int g = lane >> 4, r16 = lane & 15;
   const bool shared = it.seg == p.n_experts;
