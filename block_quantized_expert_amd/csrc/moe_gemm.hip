@@ -346,8 +346,10 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
   //    below): a byte load per row and step would add as many memory
   //    requests as the weight codes themselves;
   //  - otherwise: one byte per row and step, loaded with the step's codes.
+  // fp8 (SC: H a multiple of 512): the row's one byte per step, four steps
+  // in one 4-byte load (kCh).
   constexpr bool kSC = SC && WT == MOE_W_MXFP4 && NBT <= 5;
-  constexpr bool kCh = SC && WT == MOE_W_MXFP4 && NBT >= 6;
+  constexpr bool kCh = SC && (WT == MOE_W_MXFP4 ? NBT >= 6 : true);
   constexpr int kLoads = (kSC || kCh) ? 4 * Q : 4 * (Q + 1);  // vector loads of one step's weights
   const int g = lane >> 4, r16 = lane & 15;
   const bool shared = it.seg == p.n_experts;
@@ -431,18 +433,27 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
 #pragma unroll
     for (int mat = 0; mat < 2; ++mat)
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-        scw[mat][rb] = load16(sbase[mat] + srow_w + 16 * rb * sb + 16 * cc);
+      for (int rb = 0; rb < 2; ++rb) {
+        if constexpr (WT == MOE_W_MXFP4)
+          scw[mat][rb] = load16(sbase[mat] + srow_w + 16 * rb * sb + 16 * cc);
+        else
+          scw[mat][rb][0] =
+              *reinterpret_cast<const uint32_t*>(sbase[mat] + srow_w + 16 * rb * sb + 4 * cc);
+      }
   };
   auto take_sc = [&]() {
 #pragma unroll
     for (int mat = 0; mat < 2; ++mat)
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
-        uint32_t v = 0;
+        if constexpr (WT == MOE_W_MXFP4) {
+          uint32_t v = 0;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) v |= ((scw[mat][rb][t] >> (8 * g)) & 0xFFu) << (8 * t);
-        sp[mat][rb] = v;
+          for (int t = 0; t < 4; ++t) v |= ((scw[mat][rb][t] >> (8 * g)) & 0xFFu) << (8 * t);
+          sp[mat][rb] = v;
+        } else {
+          sp[mat][rb] = scw[mat][rb][0];
+        }
       }
   };
   // scales (kSC): the item's 128 rows of each matrix are consecutive, so
@@ -917,9 +928,12 @@ hipError_t launch_gemm_gate_up(const FfnParams& p, hipStream_t stream, hipEvent_
   // no LDS scales
   const bool o32 = (int64_t)p.n_tokens * 2 * p.hidden < ((int64_t)1 << 31);
   return by_type(p, stream, nullptr, stop, [&](int wt, int lo, int hi, hipEvent_t a, hipEvent_t b) {
-    if (wt != MOE_W_MXFP4)
-      return o32 ? gate_up_range<MOE_W_FP8E4M3_B128, 64, false, true>(p, lo, hi, stream, a, b)
-                 : gate_up_range<MOE_W_FP8E4M3_B128, 64, false, false>(p, lo, hi, stream, a, b);
+    if (wt != MOE_W_MXFP4) {
+      if (!o32) return gate_up_range<MOE_W_FP8E4M3_B128, 64, false, false>(p, lo, hi, stream, a, b);
+      return p.hidden % 512 == 0
+                 ? gate_up_range<MOE_W_FP8E4M3_B128, 64, true, true>(p, lo, hi, stream, a, b)
+                 : gate_up_range<MOE_W_FP8E4M3_B128, 64, false, true>(p, lo, hi, stream, a, b);
+    }
     if (!o32) return gate_up_range<MOE_W_MXFP4, 112, false, false>(p, lo, hi, stream, a, b);
     return sc ? gate_up_range<MOE_W_MXFP4, 112, true, true>(p, lo, hi, stream, a, b)
               : gate_up_range<MOE_W_MXFP4, 112, false, true>(p, lo, hi, stream, a, b);

@@ -23,7 +23,7 @@ moe_status check_tokens_k(int n_tokens, int n_experts, int top_k) {
 moe_status check_proj(const moe_proj& p) {
   if (p.type != MOE_W_MXFP4 && p.type != MOE_W_FP8E4M3_B128) return MOE_ERR_UNSUPPORTED;
   if (p.codes == nullptr || p.scales == nullptr) return MOE_ERR_INVALID;
-  if (!aligned16(p.codes)) return MOE_ERR_INVALID;
+  if (!aligned16(p.codes) || !aligned16(p.scales)) return MOE_ERR_INVALID;
   return MOE_OK;
 }
 

@@ -93,7 +93,7 @@ typedef enum { MOE_W_MXFP4 = 0, MOE_W_FP8E4M3_B128 = 1 } moe_weight_type;
 typedef struct {
   int32_t type; /* moe_weight_type */
   const uint8_t* codes;  /* 16-byte aligned */
-  const uint8_t* scales;
+  const uint8_t* scales; /* 16-byte aligned */
 } moe_proj;
 
 typedef struct {

@@ -122,6 +122,13 @@ def test_ffn_null_layer_and_mixed_types():
     L = _layer()
     L.shared_up = B.MoeProj(0, 0, FAKE.value)
     assert _ffn(L) == B.MOE_ERR_INVALID
+    # scale bytes are read with 16-byte loads and copies
+    L = _layer()
+    L.up = B.MoeProj(0, FAKE.value, FAKE.value + 4)
+    assert _ffn(L) == B.MOE_ERR_INVALID
+    L = _layer(swtype=1)
+    L.shared_down = B.MoeProj(1, FAKE.value, FAKE.value + 1)
+    assert _ffn(L) == B.MOE_ERR_INVALID
 
 
 def test_ffn_zero_tokens_is_a_no_op():
