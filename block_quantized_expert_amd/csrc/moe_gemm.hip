@@ -636,10 +636,11 @@ __device__ __forceinline__ void down_item(const FfnParams& p, const GItem& it, c
   constexpr int Q = F::Q;
   constexpr int TB = NBT;
   constexpr int RB = kDnRows / (16 * kGWaves);  // row blocks per wavefront
-  // scale bytes as in gate/up (SC: I a multiple of 512 and at most 2048):
-  // in LDS for up to three token blocks (kSC), in 16-byte chunks for four
+  // scale bytes as in gate/up (SC: I a multiple of 512, and at most 2048
+  // for MXFP4): MXFP4 in LDS for up to three token blocks (kSC), in 16-byte
+  // chunks for four; fp8 four steps' bytes of a row in one 4-byte load
   constexpr bool kSC = SC && WT == MOE_W_MXFP4 && NBT <= 3;
-  constexpr bool kCh = SC && WT == MOE_W_MXFP4 && NBT == 4;
+  constexpr bool kCh = SC && (WT == MOE_W_MXFP4 ? NBT == 4 : true);
   constexpr int kLoads = (kSC || kCh) ? RB * Q : RB * (Q + 1);
   const int g = lane >> 4, r16 = lane & 15;
   const bool shared = it.seg == p.n_experts;
@@ -698,16 +699,23 @@ __device__ __forceinline__ void down_item(const FfnParams& p, const GItem& it, c
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const int rr = rb < nrb ? rb : 0;
-      scw[rb] = load16(sbase + srow + 16 * rr * sb + 16 * cc);
+      if constexpr (WT == MOE_W_MXFP4)
+        scw[rb] = load16(sbase + srow + 16 * rr * sb + 16 * cc);
+      else
+        scw[rb][0] = *reinterpret_cast<const uint32_t*>(sbase + srow + 16 * rr * sb + 4 * cc);
     }
   };
   auto take_sc = [&]() {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      uint32_t v = 0;
+      if constexpr (WT == MOE_W_MXFP4) {
+        uint32_t v = 0;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) v |= ((scw[rb][t] >> (8 * g)) & 0xFFu) << (8 * t);
-      sp[rb] = v;
+        for (int t = 0; t < 4; ++t) v |= ((scw[rb][t] >> (8 * g)) & 0xFFu) << (8 * t);
+        sp[rb] = v;
+      } else {
+        sp[rb] = scw[rb][0];
+      }
     }
   };
   // scales (kSC), as in gate/up: the item's rows (up to 256, fewer in the
@@ -945,7 +953,13 @@ hipError_t launch_gemm_down(const FfnParams& p, hipStream_t stream, hipEvent_t s
   const bool sc = p.inter <= 2048 && p.inter % 512 == 0 &&
                   (!p.has_shared || (p.shared_inter <= 2048 && p.shared_inter % 512 == 0));
   return by_type(p, stream, start, stop, [&](int wt, int lo, int hi, hipEvent_t a, hipEvent_t b) {
-    if (wt != MOE_W_MXFP4) return down_range<MOE_W_FP8E4M3_B128, 64, false>(p, lo, hi, stream, a, b);
+    if (wt != MOE_W_MXFP4) {
+      // the fp8 segments of this launch: the routed ones, the shared one
+      const bool sc8 = (lo >= p.n_experts || p.inter % 512 == 0) &&
+                       (hi <= p.n_experts || p.shared_inter % 512 == 0);
+      return sc8 ? down_range<MOE_W_FP8E4M3_B128, 64, true>(p, lo, hi, stream, a, b)
+                 : down_range<MOE_W_FP8E4M3_B128, 64, false>(p, lo, hi, stream, a, b);
+    }
     return sc ? down_range<MOE_W_MXFP4, 64, true>(p, lo, hi, stream, a, b)
               : down_range<MOE_W_MXFP4, 64, false>(p, lo, hi, stream, a, b);
   });
