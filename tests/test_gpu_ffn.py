@@ -103,6 +103,55 @@ def test_small_layers_full(wl):
     assert_y_close(y.cpu().numpy(), ref)
 
 
+def _extreme_activations(n, h, seed):
+    """bf16 rows of six kinds (by token index mod 6): zero, small (2^-40,
+    the expert outputs stay normal fp32), bf16-subnormal (~2^-130: h
+    underflows, the output is exactly zero on both sides), large (2^20),
+    magnitudes log-uniform over 30 binades inside every 32-input block, and
+    one nonzero per block.  The batched gate/up stores x as two E4M3 parts
+    under a per-32 scale taken from the block's largest magnitude; these
+    rows test that split at the ends of the exponent range and far below the
+    block maximum."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n, h))
+    kind = np.arange(n) % 6
+    x[kind == 0] = 0.0
+    x[kind == 1] *= 2.0 ** -40
+    x[kind == 2] *= 2.0 ** -130
+    x[kind == 3] *= 2.0 ** 20
+    m = kind == 4
+    x[m] = np.sign(x[m]) * 2.0 ** rng.uniform(-30, 0, size=x[m].shape)
+    m = kind == 5
+    keep = np.zeros((n, h), dtype=bool)
+    keep[:, ::32] = True
+    x[m & ~keep.any(1)] = 0.0
+    x[m] = np.where(keep[m], x[m], 0.0)
+    x[0, 1] = -0.0
+    return torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16)
+
+
+def test_extreme_activations_per_token():
+    # batched path (48 tokens > 16): activation quantization + grouped GEMMs
+    wl = replace(SMALL, n_tokens=48, shared="mxfp4", seed=28)
+    print("case extreme activations", flush=True)
+    layer, _, _, routing, routing_d = gpu_inputs(wl)
+    x = _extreme_activations(wl.n_tokens, wl.hidden, 29)
+    y, ids, w, g = B.forward(layer, x.to(DEV), routing_d)
+    torch.cuda.synchronize()
+    rids, rw = oracle_routing(wl, routing)
+    assert np.array_equal(ids.cpu().numpy(), rids)
+    ref = oracle_y(wl, x, rids, rw)
+    yh = y.cpu().numpy()
+    assert np.all(np.isfinite(yh))
+    for t in range(wl.n_tokens):
+        rms = float(np.sqrt(np.mean(ref[t].astype(np.float64) ** 2)))
+        err = float(np.max(np.abs(yh[t].astype(np.float64) - ref[t])))
+        if rms == 0.0:
+            assert err == 0.0, t
+        else:
+            assert err <= 2e-3 * rms, (t, err / rms)
+
+
 def test_stages_equal_forward():
     wl = replace(SMALL, n_tokens=50, seed=27)
     print("case stages", flush=True)
