@@ -1007,6 +1007,8 @@ int decode_steps(const FfnParams& p) {
 
 }  // namespace
 
+bool gate_up_writes_h3(const FfnParams& p) { return !p.x_f32 && decode_steps(p) == 0; }
+
 hipError_t launch_ffn_gate_up(const FfnParams& p, hipStream_t stream, hipEvent_t start,
                               hipEvent_t stop) {
   switch (decode_steps(p)) {
@@ -1027,7 +1029,9 @@ hipError_t launch_ffn_gate_up(const FfnParams& p, hipStream_t stream, hipEvent_t
 
 hipError_t launch_ffn_down(const FfnParams& p, hipStream_t stream, hipEvent_t start,
                            hipEvent_t stop) {
-  const int slots = small_slots(p);
+  // the small-batch down reads the bf16 pair; h in E4M3 parts goes to the
+  // grouped-GEMM down whatever the batch size
+  const int slots = gate_up_writes_h3(p) ? 0 : small_slots(p);
   if (slots > 0) {
     const bool r4 = p.w_type == MOE_W_MXFP4;
     const bool s4 = !p.has_shared || p.sw_type == MOE_W_MXFP4;

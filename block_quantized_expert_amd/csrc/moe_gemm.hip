@@ -331,6 +331,41 @@ __device__ __forceinline__ i32x8 join8(u32x4 a, u32x4 b) {
                (int)b[3]};
 }
 
+// Eight values v (two groups of four) of one 32-input block whose largest
+// magnitude is mag, as three E4M3 parts: with e the exponent of mag and
+// f = v / 2^(e-7), part 1 = f rounded to E4M3, part 2 = (f - part 1) * 16
+// rounded, part 3 = (that - part 2) * 16 rounded; v = (p1 + p2/16 + p3/256)
+// * 2^(e-7) up to 2^-12 of |v| (each rounding keeps 4 significant bits of a
+// remainder no larger than f).  part[q][grp] packs the group's four bytes
+// of part q; the return value holds the three parts' UE8M0 scale bytes
+// (e-7, e-11, e-15 biased, kept at least 8, 4, 0) in bytes 0..2.
+__device__ __forceinline__ uint32_t split_e4m3x3(const float (&v)[2][4], float mag,
+                                                uint32_t (&part)[3][2]) {
+  const int sb = min(max((int)((__float_as_uint(mag) >> 23) & 0xFF) - 7, 8), 254);
+  const float inv = __uint_as_float((uint32_t)(254 - sb) << 23);  // 2^(127 - sb)
+#pragma unroll
+  for (int grp = 0; grp < 2; ++grp) {
+    float f[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) f[r] = v[grp][r] * inv;
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], w, true);
+      part[q][grp] = (uint32_t)w;
+      if (q < 2) {
+        const auto d0 = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+        const auto d1 = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+        f[0] = (f[0] - d0[0]) * 16.0f;
+        f[1] = (f[1] - d0[1]) * 16.0f;
+        f[2] = (f[2] - d1[0]) * 16.0f;
+        f[3] = (f[3] - d1[1]) * 16.0f;
+      }
+    }
+  }
+  return (uint32_t)sb | ((uint32_t)(sb - 4) << 8) | ((uint32_t)(sb - 8) << 16);
+}
+
 // NBT = token blocks of the tile (ceil(m / 16)), a compile-time constant so
 // that a step's operand reads and MFMAs form one branch-free block.
 template <int WT, int TT, int NBT, bool SC, bool O32>
@@ -582,29 +617,39 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
   }
   wait_vm<0>();  // the reloads past the end
 
-  // SwiGLU; lane holds rows 4g .. 4g+3 of each block for token column r16
+  // SwiGLU, then h as three E4M3 parts (split_e4m3x3) under the scale of
+  // the wavefront's 32 rows, which are one 32-input block of the down
+  // projection: the lane holds rows 4g .. 4g+3 of row block rb for token
+  // column r16, and the four lanes of a token meet in two shuffles.
+  const int64_t hs = p.h_stride;
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+  for (int tb = 0; tb < TB; ++tb) {
+    float v[2][4];
+    float mag = 0.0f;
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb) {
-      const int n = tb * 16 + r16;
-      if (live && tb < nbt && n < it.m) {
-        bf16x4 hi, lo;
+    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float gv = acc[0][rb][tb][r];
-          const float h = gv / (1.0f + expf(-gv)) * acc[1][rb][tb][r];
-          __bf16 x, y;
-          split_bf16(h, x, y);
-          hi[r] = x;
-          lo[r] = y;
-        }
-        const int64_t o =
-            (int64_t)(it.slot0 + n) * p.h_stride + it.row0 + 32 * wave + 16 * rb + 4 * g;
-        *reinterpret_cast<bf16x4*>(p.h_hi + o) = hi;
-        *reinterpret_cast<bf16x4*>(p.h_lo + o) = lo;
+      for (int r = 0; r < 4; ++r) {
+        const float gv = acc[0][rb][tb][r];
+        v[rb][r] = gv / (1.0f + expf(-gv)) * acc[1][rb][tb][r];
+        mag = fmaxf(mag, fabsf(v[rb][r]));
       }
+    mag = fmaxf(mag, __shfl_xor(mag, 16));
+    mag = fmaxf(mag, __shfl_xor(mag, 32));
+    uint32_t part[3][2];
+    const uint32_t sbytes = split_e4m3x3(v, mag, part);
+    const int n = tb * 16 + r16;
+    if (live && n < it.m) {
+      uint8_t* dst = p.h3 + (int64_t)(it.slot0 + n) * 3 * hs + (it.row0 / 128) * 384 + 32 * wave + 4 * g;
+#pragma unroll
+      for (int q = 0; q < 3; ++q)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) *reinterpret_cast<uint32_t*>(dst + q * 128 + 16 * rb) = part[q][rb];
+      if (g == 0)
+        *reinterpret_cast<uint32_t*>(p.h3s + (int64_t)(it.slot0 + n) * (hs / 32) * 4 +
+                                     (it.row0 / 32 + wave) * 4) = sbytes;
     }
+  }
 }
 
 template <int WT, int TT, bool SC, bool O32>
@@ -845,6 +890,264 @@ __global__ __launch_bounds__(kGThreads, 2) void gemm_down_kernel(FfnParams p, in
   }
 }
 
+// ------------------------------------------------------ down on E4M3 parts
+//
+// The grouped-GEMM path with bf16 x stores h as three E4M3 parts per
+// element (split_e4m3x3).  The down projection feeds them to the scaled
+// instruction as its B operand with the weight codes and scale bytes as
+// stored: three 16x16x128 instructions per tile and step, where the bf16
+// pair took eight 16x16x32 ones and a decode.  An h tile is three planes of
+// TT rows x 128 bytes per step (one per part) and 16 scale bytes per row.
+constexpr int kD3Plane = 64 * 128;              // one part's rows of a step (TT = 64)
+constexpr int kD3Buf = 3 * kD3Plane;            // the three parts
+constexpr int kD3ScaleOff = kDnScaleOff + kDnRows * (2048 / 32);  // after the weight scales
+static_assert(2 * kD3Buf <= kDnScaleOff, "down h tiles");
+static_assert(kD3ScaleOff + 2 * 64 * 16 <= kGemmLds, "down LDS");
+
+// 16 bytes of a 128-byte LDS row: chunk c of row n sits at position
+// c ^ ((n >> 1) & 7), so the 16 rows that one operand read touches (two rows
+// share a 256-byte bank line) hit distinct banks.
+__device__ __forceinline__ u32x4 row128_chunk(const char* plane, int n, int c) {
+  return *reinterpret_cast<const u32x4*>(plane + n * 128 + ((c ^ ((n >> 1) & 7)) << 4));
+}
+
+template <int WT, int NBT, bool SC>
+__device__ __forceinline__ void down3_item(const FfnParams& p, const GItem& it, char* smem,
+                                           int wave, int lane) {
+  using F = Fmt<WT>;
+  constexpr int Q = F::Q;
+  constexpr int TB = NBT;
+  constexpr int TT = 64;
+  constexpr int FA = WT == MOE_W_MXFP4 ? 4 : 0;  // operand format of the weights
+  constexpr int RB = kDnRows / (16 * kGWaves);  // row blocks per wavefront
+  // scale bytes of the weights as in down_item
+  constexpr bool kSC = SC && WT == MOE_W_MXFP4 && NBT <= 3;
+  constexpr bool kCh = SC && (WT == MOE_W_MXFP4 ? NBT == 4 : true);
+  constexpr int kLoads = (kSC || kCh) ? RB * Q : RB * (Q + 1);
+  const int g = lane >> 4, r16 = lane & 15;
+  const bool shared = it.seg == p.n_experts;
+  const int kdim = shared ? p.shared_inter : p.inter;
+  const int64_t cb = F::row_bytes(kdim), sb = F::scale_row_bytes(kdim);
+  const int nks = kdim / 128;
+  constexpr int nbt = NBT;
+  const int64_t hs = p.h_stride;
+  // row blocks of this wavefront inside the matrix (the last tile may be short)
+  const int wrow0 = it.row0 + 64 * wave;
+  const int nrb = uniform(max(0, min(RB, (p.hidden - wrow0) / 16)));
+  const int64_t r0 = wrow0 + r16 < p.hidden ? wrow0 + r16 : r16;
+  const int64_t lrow = (shared ? 0 : (int64_t)it.seg * p.hidden) + r0;
+  // code bytes of a step: MXFP4 16 at 16g; fp8 16 at 16g and 16 at 64 + 16g
+  const int64_t lc = lrow * cb + 16 * g, ls = lrow * sb + F::scale_off(0, g);
+  const uint8_t* cbase = shared ? p.sdown_c : p.down_c;
+  const uint8_t* sbase = shared ? p.sdown_s : p.down_s;
+
+  // h copies: instruction i = 4j + wave (j = 0..5) fills part i / 8, rows
+  // 8 (i % 8) .. +7 (lane l: row + l / 8, position l % 8); so a wavefront's
+  // rows are 8 wave .. +7 and 32 + 8 wave .. +7 of every part.  Rows past
+  // the tile repeat row 0.
+  int64_t hsrc[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int n = 32 * e + 8 * wave + (lane >> 3);
+    const int c = (lane & 7) ^ ((n >> 1) & 7);
+    hsrc[e] = (int64_t)(it.slot0 + (n < it.m ? n : 0)) * 3 * hs + 16 * c;
+  }
+  // scale bytes: wavefront w copies rows 16w .. +15, four lanes per row
+  const int ns = 16 * wave + (lane >> 2);
+  const uint8_t* hss = p.h3s + (int64_t)(it.slot0 + (ns < it.m ? ns : 0)) * (hs / 32) * 4 + 4 * (lane & 3);
+  auto lds = [](char* q) { return (__attribute__((address_space(3))) void*)q; };
+  auto hbuf = [&](int b) { return smem + (b & 1) * kD3Buf; };
+  auto sbuf = [&](int b) { return smem + kD3ScaleOff + (b & 1) * (TT * 16); };
+  auto copy_h = [&](int ks) {
+    char* dst = hbuf(ks);
+#pragma unroll
+    for (int j = 0; j < 6; ++j) {
+      const int q = j >> 1, e = j & 1;
+      if (32 * e + 8 * wave < 16 * nbt)
+        __builtin_amdgcn_global_load_lds(p.h3 + hsrc[e] + ks * 384 + q * 128,
+                                         lds(dst + q * kD3Plane + (32 * e + 8 * wave) * 128), 16, 0,
+                                         0);
+    }
+    if (16 * wave < 16 * nbt)
+      __builtin_amdgcn_global_load_lds(hss + ks * 16, lds(sbuf(ks) + 256 * wave), 4, 0, 0);
+  };
+
+  // routing weight of each token column, fetched now, used by the epilogue
+  float wcol[TB];
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb) {
+    const int n = min(tb * 16 + r16, it.m - 1);
+    wcol[tb] = shared ? 1.0f : p.topk_w[p.perm[it.slot0 + n]];
+  }
+
+  // weight codes of the current step and the next
+  u32x4 q0[RB][Q], q1[RB][Q];
+  uint32_t u0[RB], u1[RB];
+  auto load_w = [&](int ks, u32x4 (&q)[RB][Q], uint32_t (&u)[RB]) {
+    const int k = min(ks, nks - 1);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int rr = rb < nrb ? rb : 0;
+#pragma unroll
+      for (int i = 0; i < Q; ++i)
+        q[rb][i] = load16(cbase + lc + 16 * rr * cb + F::code_off(k, 0) + 64 * i);
+      if (!kSC && !kCh) u[rb] = sbase[ls + 16 * rr * sb + F::scale_off(k, 0)];
+    }
+  };
+  u32x4 scw[RB];
+  uint32_t sp[RB];
+  const int64_t srow = ls - F::scale_off(0, g);
+  auto load_sc = [&](int c) {
+    const int cc = min(c, nks / 4 - 1);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int rr = rb < nrb ? rb : 0;
+      if constexpr (WT == MOE_W_MXFP4)
+        scw[rb] = load16(sbase + srow + 16 * rr * sb + 16 * cc);
+      else
+        scw[rb][0] = *reinterpret_cast<const uint32_t*>(sbase + srow + 16 * rr * sb + 4 * cc);
+    }
+  };
+  auto take_sc = [&]() {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      if constexpr (WT == MOE_W_MXFP4) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v |= ((scw[rb][t] >> (8 * g)) & 0xFFu) << (8 * t);
+        sp[rb] = v;
+      } else {
+        sp[rb] = scw[rb][0];
+      }
+    }
+  };
+  // weight scales (kSC): the item's rows as one contiguous block in LDS
+  char* const sscale = smem + kDnScaleOff;  // [256 rows][sb]
+  auto copy_scales = [&]() {
+    const int64_t bytes = (int64_t)min(kDnRows, p.hidden - it.row0) * sb;
+    const uint8_t* src = sbase + ((shared ? 0 : (int64_t)it.seg * p.hidden) + it.row0) * sb;
+    for (int64_t o = (int64_t)wave * 1024; o < bytes; o += kGWaves * 1024)
+      if (o + lane * 16 < bytes)
+        __builtin_amdgcn_global_load_lds(src + o + lane * 16, lds(sscale + o), 16, 0, 0);
+  };
+  auto scale_byte = [&](int rb, int ks) -> uint32_t {
+    const int rr = rb < nrb ? rb : 0;
+    return *reinterpret_cast<const uint8_t*>(sscale + (64 * wave + 16 * rr + r16) * sb + ks * 4 +
+                                             g);
+  };
+
+  f32x4 acc[RB][TB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) acc[rb][tb] = f32x4{0, 0, 0, 0};
+
+  auto step_mma = [&](int ks, const u32x4 (&qq)[RB][Q], const uint32_t (&uu)[RB]) {
+    const char* cur = hbuf(ks);
+    const char* cts = sbuf(ks);
+    uint32_t sa[RB];
+    i32x8 a[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      sa[rb] = kSC ? scale_byte(rb, ks) : kCh ? sp[rb] >> (8 * (ks & 3)) : uu[rb];
+      a[rb] = weight_operand<WT>(qq[rb]);
+    }
+    // operand u = 3 tb + part is read while operand u-1 multiplies
+    i32x8 bop[2];
+    uint32_t sbt[2];
+    auto read_op = [&](int u) {
+      const int tb = u / 3, q = u % 3;
+      const int n = tb * 16 + r16;
+      const char* plane = cur + q * kD3Plane;
+      bop[u & 1] = join8(row128_chunk(plane, n, g), row128_chunk(plane, n, g + 4));
+      if (q == 0) sbt[tb & 1] = *reinterpret_cast<const uint32_t*>(cts + n * 16 + 4 * g);
+    };
+    read_op(0);
+#pragma unroll
+    for (int u = 0; u < 3 * TB; ++u) {
+      if (u + 1 < 3 * TB) read_op(u + 1);
+      const int tb = u / 3, q = u % 3;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        if (rb < nrb) {
+          if (q == 0)
+            acc[rb][tb] = mfma_scaled<FA, 0, 0>(a[rb], bop[u & 1], acc[rb][tb], sa[rb], sbt[tb & 1]);
+          else if (q == 1)
+            acc[rb][tb] = mfma_scaled<FA, 0, 1>(a[rb], bop[u & 1], acc[rb][tb], sa[rb], sbt[tb & 1]);
+          else
+            acc[rb][tb] = mfma_scaled<FA, 0, 2>(a[rb], bop[u & 1], acc[rb][tb], sa[rb], sbt[tb & 1]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  if (kSC) copy_scales();
+  if (kCh) load_sc(0);
+  load_w(0, q0, u0);
+  copy_h(0);
+  wait_vm<0>();
+  __syncthreads();
+  for (int ks = 0; ks < nks; ++ks) {
+    if (kCh && (ks & 3) == 0) {
+      take_sc();
+      load_sc((ks >> 2) + 1);
+    }
+    if (ks + 1 < nks) copy_h(ks + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    // the next step's weights (one step ahead: the step ends by moving them
+    // into q0, so a deeper register ring would only wait for its loads there)
+    load_w(ks + 1, q1, u1);
+    __builtin_amdgcn_sched_barrier(0);
+    step_mma(ks, q0, u0);
+    step_barrier<kLoads>();
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+      for (int i = 0; i < Q; ++i) q0[rb][i] = q1[rb][i];
+      u0[rb] = u1[rb];
+    }
+  }
+  wait_vm<0>();
+
+  // routing weight of each token column, then the per-slot outputs
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb) {
+    const int n = tb * 16 + r16;
+    if (tb < nbt && n < it.m) {
+      const int64_t slot = it.slot0 + n;
+      const float w = wcol[tb];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        if (rb < nrb) {
+          *reinterpret_cast<f32x4*>(p.obuf + slot * p.hidden + wrow0 + 16 * rb + 4 * g) =
+              acc[rb][tb] * w;
+        }
+      }
+    }
+  }
+}
+
+template <int WT, bool SC>
+__global__ __launch_bounds__(kGThreads, 2) void gemm_down3_kernel(FfnParams p, int seg_lo,
+                                                                   int seg_hi) {
+  extern __shared__ __align__(16) char smem[];
+  __shared__ int s_pref[kSegMax + 1];
+  __shared__ int s_tmp[kGThreads / kWave];
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int total = item_prefix<64, kDnRows, true>(p, seg_lo, seg_hi, s_pref, s_tmp);
+  const int slots = (total + 7) & ~7;
+  for (int i = blockIdx.x; i < slots; i += gridDim.x) {
+    const int item = xcd_item(i, total);
+    if (item < 0) continue;
+    const GItem it = find_item<64, kDnRows, true>(p, seg_lo, seg_hi, s_pref, item);
+    dispatch_nbt<4>((it.m + 15) >> 4, [&](auto nb) {
+      down3_item<WT, decltype(nb)::value, SC>(p, it, smem, wave, lane);
+    });
+    __syncthreads();
+  }
+}
+
 template <typename... Params, typename... Args>
 hipError_t launch(void (*kernel)(Params...), dim3 grid, dim3 block, size_t lds,
                   hipStream_t stream, hipEvent_t start, hipEvent_t stop, Args... args) {
@@ -893,6 +1196,16 @@ hipError_t gate_up_range(const FfnParams& p, int seg_lo, int seg_hi, hipStream_t
   const int grid = grid_for(items_bound(p, seg_lo, seg_hi, TT, kGuRows, false));
   return launch(gemm_gate_up_kernel<WT, TT, SC, O32>, dim3(grid), dim3(kGThreads),
                 (size_t)kGemmLds, stream, start, stop, p, seg_lo, seg_hi);
+}
+
+template <int WT, bool SC>
+hipError_t down3_range(const FfnParams& p, int seg_lo, int seg_hi, hipStream_t stream,
+                       hipEvent_t start, hipEvent_t stop) {
+  static const hipError_t attr = allow_lds(gemm_down3_kernel<WT, SC>);
+  if (attr != hipSuccess) return attr;
+  const int grid = grid_for(items_bound(p, seg_lo, seg_hi, 64, kDnRows, true));
+  return launch(gemm_down3_kernel<WT, SC>, dim3(grid), dim3(kGThreads), (size_t)kGemmLds, stream,
+                start, stop, p, seg_lo, seg_hi);
 }
 
 template <int WT, int TT, bool SC>
@@ -952,14 +1265,23 @@ hipError_t launch_gemm_down(const FfnParams& p, hipStream_t stream, hipEvent_t s
                             hipEvent_t stop) {
   const bool sc = p.inter <= 2048 && p.inter % 512 == 0 &&
                   (!p.has_shared || (p.shared_inter <= 2048 && p.shared_inter % 512 == 0));
+  // h in three E4M3 parts (from the grouped-GEMM gate/up) or as the bf16
+  // pair (fp32 x, or the decode gate/up of a small batch with many slots)
+  const bool h3 = gate_up_writes_h3(p);
   return by_type(p, stream, start, stop, [&](int wt, int lo, int hi, hipEvent_t a, hipEvent_t b) {
     if (wt != MOE_W_MXFP4) {
       // the fp8 segments of this launch: the routed ones, the shared one
       const bool sc8 = (lo >= p.n_experts || p.inter % 512 == 0) &&
                        (hi <= p.n_experts || p.shared_inter % 512 == 0);
+      if (h3)
+        return sc8 ? down3_range<MOE_W_FP8E4M3_B128, true>(p, lo, hi, stream, a, b)
+                   : down3_range<MOE_W_FP8E4M3_B128, false>(p, lo, hi, stream, a, b);
       return sc8 ? down_range<MOE_W_FP8E4M3_B128, 64, true>(p, lo, hi, stream, a, b)
                  : down_range<MOE_W_FP8E4M3_B128, 64, false>(p, lo, hi, stream, a, b);
     }
+    if (h3)
+      return sc ? down3_range<MOE_W_MXFP4, true>(p, lo, hi, stream, a, b)
+                : down3_range<MOE_W_MXFP4, false>(p, lo, hi, stream, a, b);
     return sc ? down_range<MOE_W_MXFP4, 64, true>(p, lo, hi, stream, a, b)
               : down_range<MOE_W_MXFP4, 64, false>(p, lo, hi, stream, a, b);
   });

@@ -109,10 +109,16 @@ moe_status plan_ffn(const moe_layer* layer, int n_tokens, FfnPlan* plan) {
   const size_t o_bytes = align_up((size_t)(plan->slots * layer->hidden) * 4u, 256);
   const size_t xq_bytes = align_up((size_t)n * layer->hidden * 2u, 256);
   const size_t xs_bytes = align_up((size_t)n * (layer->hidden / 16), 256);
+  // h as three E4M3 parts + 4 scale bytes per 32 fits in the bf16 pair's
+  // place (3.125 against 4 bytes per element) except for tiny layers
+  const size_t h3_bytes = align_up((size_t)(plan->slots * hs) * 3u, 256);
+  const size_t h3s_bytes = align_up((size_t)(plan->slots * (hs / 32)) * 4u, 256);
+  const size_t h_area = 2 * h_bytes > h3_bytes + h3s_bytes ? 2 * h_bytes : h3_bytes + h3s_bytes;
   plan->off_h_hi = 0;
   plan->off_h_lo = h_bytes;
-  plan->off_obuf = 2 * h_bytes;
-  plan->off_xq = 2 * h_bytes + o_bytes;
+  plan->off_h3s = h3_bytes;
+  plan->off_obuf = h_area;
+  plan->off_xq = h_area + o_bytes;
   plan->off_xs = plan->off_xq + xq_bytes;
   plan->total = plan->off_xs + xs_bytes;
   return MOE_OK;

@@ -19,6 +19,10 @@ namespace moe {
 //   xq         : u8 [n_tokens][2*hidden]  bf16 activations as E4M3 hi and lo
 //                                         parts (grouped-GEMM gate/up)
 //   xs         : u8 [n_tokens][hidden/16] their scale bytes
+//   h3, h3s    : at off_h_hi, in place of h_hi/h_lo on the grouped-GEMM
+//                path with bf16 x: h as three E4M3 parts
+//                u8 [slots][h_stride/128][3][128] and their scale bytes
+//                u8 [slots][h_stride/32][4]
 // A slot is one (token, routed expert) pair in grouped order
 // (p in [0, n_tokens*top_k)) or, for the shared expert, n_tokens*top_k + t.
 struct FfnPlan {
@@ -29,6 +33,7 @@ struct FfnPlan {
   size_t off_obuf;
   size_t off_xq;
   size_t off_xs;
+  size_t off_h3s;
   size_t total;
 };
 

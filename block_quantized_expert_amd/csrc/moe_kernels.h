@@ -36,6 +36,12 @@ struct FfnParams {
   __bf16* h_hi;  // [slots][h_stride]
   __bf16* h_lo;
   int64_t h_stride;
+  // grouped-GEMM path with bf16 x: h as three E4M3 parts in place of the
+  // pair, h3 [slots][h_stride/128][3][128] (per 128 inputs the three parts'
+  // bytes), h3s [slots][h_stride/32][4] (their UE8M0 scale bytes s, s-4,
+  // s-8 and a zero byte)
+  uint8_t* h3;
+  uint8_t* h3s;
   float* obuf;  // [slots][hidden] weighted per-slot outputs
   float* y;     // [n_tokens][hidden]
 };
@@ -89,6 +95,9 @@ hipError_t launch_ffn_down(const FfnParams& p, hipStream_t stream, hipEvent_t st
 int fused_decode_steps(const FfnParams& p);
 hipError_t launch_decode_fused(const FusedParams& f, hipStream_t stream, hipEvent_t start,
                                hipEvent_t stop);
+// true if launch_ffn_gate_up stores h as three E4M3 parts (h3, h3s: the
+// grouped-GEMM gate/up), false if as the bf16 pair (h_hi, h_lo)
+bool gate_up_writes_h3(const FfnParams& p);
 // grouped-GEMM kernels for batches in which experts see many tokens
 hipError_t launch_gemm_gate_up(const FfnParams& p, hipStream_t stream, hipEvent_t start,
                                hipEvent_t stop);
