@@ -897,12 +897,16 @@ __global__ __launch_bounds__(kGThreads, 2) void gemm_down_kernel(FfnParams p, in
 // instruction as its B operand with the weight codes and scale bytes as
 // stored: three 16x16x128 instructions per tile and step, where the bf16
 // pair took eight 16x16x32 ones and a decode.  An h tile is three planes of
-// TT rows x 128 bytes per step (one per part) and 16 scale bytes per row.
-constexpr int kD3Plane = 64 * 128;              // one part's rows of a step (TT = 64)
-constexpr int kD3Buf = 3 * kD3Plane;            // the three parts
-constexpr int kD3ScaleOff = kDnScaleOff + kDnRows * (2048 / 32);  // after the weight scales
-static_assert(2 * kD3Buf <= kDnScaleOff, "down h tiles");
-static_assert(kD3ScaleOff + 2 * 64 * 16 <= kGemmLds, "down LDS");
+// 16 NBT rows x 128 bytes per step (one per part) and 16 scale bytes per
+// row.  LDS per workgroup: two tiles, then (up to three token blocks) the
+// item's weight scales, then the tiles' scale bytes.  Up to 64 tokens per
+// tile: 96 would fit (so that an expert with up to 96 tokens streams its
+// down weights once) but measured 10 % slower on hash4096.
+constexpr int kD3Tok = 64;
+constexpr int kD3Full = 2 * 3 * kD3Tok * 128 + 2 * kD3Tok * 16;             // full tiles
+constexpr int kD3Sc = 2 * 3 * 48 * 128 + kDnRows * (2048 / 32) + 2 * 48 * 16;  // 3 blocks + scales
+constexpr int kD3Lds = kD3Full > kD3Sc ? kD3Full : kD3Sc;
+static_assert(kD3Lds + (kSegMax + 1 + kGWaves) * 4 + 64 <= 80 * 1024, "two workgroups per CU");
 
 // 16 bytes of a 128-byte LDS row: chunk c of row n sits at position
 // c ^ ((n >> 1) & 7), so the 16 rows that one operand read touches (two rows
@@ -917,7 +921,8 @@ __device__ __forceinline__ void down3_item(const FfnParams& p, const GItem& it, 
   using F = Fmt<WT>;
   constexpr int Q = F::Q;
   constexpr int TB = NBT;
-  constexpr int TT = 64;
+  constexpr int kPlane = 16 * NBT * 128;  // one part's rows of a step
+  constexpr int kBuf = 3 * kPlane;        // the three parts
   constexpr int FA = WT == MOE_W_MXFP4 ? 4 : 0;  // operand format of the weights
   constexpr int RB = kDnRows / (16 * kGWaves);  // row blocks per wavefront
   // scale bytes of the weights as in down_item
@@ -941,35 +946,50 @@ __device__ __forceinline__ void down3_item(const FfnParams& p, const GItem& it, 
   const uint8_t* cbase = shared ? p.sdown_c : p.down_c;
   const uint8_t* sbase = shared ? p.sdown_s : p.down_s;
 
-  // h copies: instruction i = 4j + wave (j = 0..5) fills part i / 8, rows
-  // 8 (i % 8) .. +7 (lane l: row + l / 8, position l % 8); so a wavefront's
-  // rows are 8 wave .. +7 and 32 + 8 wave .. +7 of every part.  Rows past
-  // the tile repeat row 0.
-  int64_t hsrc[2];
+  // h copies: one instruction fills 8 rows of a part (lane l: row + l / 8,
+  // position l % 8); wavefront w fills the row groups w, w + 4 and w + 8 of
+  // each part (the ones below the tile), rows past the tile's tokens repeat
+  // row 0.  Scale bytes: 16 rows per instruction (four lanes per row),
+  // groups w and w + 4.
+  constexpr int kRG = (2 * NBT + 3) / 4;   // row groups of 8 per wavefront
+  constexpr int kSG = (NBT + 3) / 4;       // scale groups of 16 per wavefront
+  int64_t hsrc[kRG];
 #pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int n = 32 * e + 8 * wave + (lane >> 3);
+  for (int e = 0; e < kRG; ++e) {
+    const int n = 8 * (wave + 4 * e) + (lane >> 3);
     const int c = (lane & 7) ^ ((n >> 1) & 7);
     hsrc[e] = (int64_t)(it.slot0 + (n < it.m ? n : 0)) * 3 * hs + 16 * c;
   }
-  // scale bytes: wavefront w copies rows 16w .. +15, four lanes per row
-  const int ns = 16 * wave + (lane >> 2);
-  const uint8_t* hss = p.h3s + (int64_t)(it.slot0 + (ns < it.m ? ns : 0)) * (hs / 32) * 4 + 4 * (lane & 3);
+  const uint8_t* hss[kSG];
+#pragma unroll
+  for (int e = 0; e < kSG; ++e) {
+    const int ns = 16 * (wave + 4 * e) + (lane >> 2);
+    hss[e] = p.h3s + (int64_t)(it.slot0 + (ns < it.m ? ns : 0)) * (hs / 32) * 4 + 4 * (lane & 3);
+  }
+  // LDS: tiles, the weight scales (kSC), the tiles' scale bytes
+  constexpr int kWScOff = 2 * kBuf;
+  constexpr int kTScOff = kWScOff + (kSC ? kDnRows * (2048 / 32) : 0);
+  static_assert(kTScOff + 2 * 16 * NBT * 16 <= kD3Lds, "down LDS");
   auto lds = [](char* q) { return (__attribute__((address_space(3))) void*)q; };
-  auto hbuf = [&](int b) { return smem + (b & 1) * kD3Buf; };
-  auto sbuf = [&](int b) { return smem + kD3ScaleOff + (b & 1) * (TT * 16); };
+  auto hbuf = [&](int b) { return smem + (b & 1) * kBuf; };
+  auto sbuf = [&](int b) { return smem + kTScOff + (b & 1) * (16 * NBT * 16); };
   auto copy_h = [&](int ks) {
     char* dst = hbuf(ks);
 #pragma unroll
-    for (int j = 0; j < 6; ++j) {
-      const int q = j >> 1, e = j & 1;
-      if (32 * e + 8 * wave < 16 * nbt)
-        __builtin_amdgcn_global_load_lds(p.h3 + hsrc[e] + ks * 384 + q * 128,
-                                         lds(dst + q * kD3Plane + (32 * e + 8 * wave) * 128), 16, 0,
-                                         0);
+    for (int q = 0; q < 3; ++q)
+#pragma unroll
+      for (int e = 0; e < kRG; ++e) {
+        const int rg = wave + 4 * e;
+        if (rg < 2 * nbt)
+          __builtin_amdgcn_global_load_lds(p.h3 + hsrc[e] + ks * 384 + q * 128,
+                                           lds(dst + q * kPlane + rg * 8 * 128), 16, 0, 0);
+      }
+#pragma unroll
+    for (int e = 0; e < kSG; ++e) {
+      const int sg = wave + 4 * e;
+      if (sg < nbt)
+        __builtin_amdgcn_global_load_lds(hss[e] + ks * 16, lds(sbuf(ks) + sg * 256), 4, 0, 0);
     }
-    if (16 * wave < 16 * nbt)
-      __builtin_amdgcn_global_load_lds(hss + ks * 16, lds(sbuf(ks) + 256 * wave), 4, 0, 0);
   };
 
   // routing weight of each token column, fetched now, used by the epilogue
@@ -1022,7 +1042,7 @@ __device__ __forceinline__ void down3_item(const FfnParams& p, const GItem& it, 
     }
   };
   // weight scales (kSC): the item's rows as one contiguous block in LDS
-  char* const sscale = smem + kDnScaleOff;  // [256 rows][sb]
+  char* const sscale = smem + kWScOff;  // [256 rows][sb]
   auto copy_scales = [&]() {
     const int64_t bytes = (int64_t)min(kDnRows, p.hidden - it.row0) * sb;
     const uint8_t* src = sbase + ((shared ? 0 : (int64_t)it.seg * p.hidden) + it.row0) * sb;
@@ -1058,7 +1078,7 @@ __device__ __forceinline__ void down3_item(const FfnParams& p, const GItem& it, 
     auto read_op = [&](int u) {
       const int tb = u / 3, q = u % 3;
       const int n = tb * 16 + r16;
-      const char* plane = cur + q * kD3Plane;
+      const char* plane = cur + q * kPlane;
       bop[u & 1] = join8(row128_chunk(plane, n, g), row128_chunk(plane, n, g + 4));
       if (q == 0) sbt[tb & 1] = *reinterpret_cast<const uint32_t*>(cts + n * 16 + 4 * g);
     };
@@ -1135,13 +1155,13 @@ __global__ __launch_bounds__(kGThreads, 2) void gemm_down3_kernel(FfnParams p, i
   __shared__ int s_pref[kSegMax + 1];
   __shared__ int s_tmp[kGThreads / kWave];
   const int lane = threadIdx.x & 63, wave = wave_id();
-  const int total = item_prefix<64, kDnRows, true>(p, seg_lo, seg_hi, s_pref, s_tmp);
+  const int total = item_prefix<kD3Tok, kDnRows, true>(p, seg_lo, seg_hi, s_pref, s_tmp);
   const int slots = (total + 7) & ~7;
   for (int i = blockIdx.x; i < slots; i += gridDim.x) {
     const int item = xcd_item(i, total);
     if (item < 0) continue;
-    const GItem it = find_item<64, kDnRows, true>(p, seg_lo, seg_hi, s_pref, item);
-    dispatch_nbt<4>((it.m + 15) >> 4, [&](auto nb) {
+    const GItem it = find_item<kD3Tok, kDnRows, true>(p, seg_lo, seg_hi, s_pref, item);
+    dispatch_nbt<kD3Tok / 16>((it.m + 15) >> 4, [&](auto nb) {
       down3_item<WT, decltype(nb)::value, SC>(p, it, smem, wave, lane);
     });
     __syncthreads();
@@ -1201,10 +1221,12 @@ hipError_t gate_up_range(const FfnParams& p, int seg_lo, int seg_hi, hipStream_t
 template <int WT, bool SC>
 hipError_t down3_range(const FfnParams& p, int seg_lo, int seg_hi, hipStream_t stream,
                        hipEvent_t start, hipEvent_t stop) {
-  static const hipError_t attr = allow_lds(gemm_down3_kernel<WT, SC>);
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_down3_kernel<WT, SC>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kD3Lds);
   if (attr != hipSuccess) return attr;
-  const int grid = grid_for(items_bound(p, seg_lo, seg_hi, 64, kDnRows, true));
-  return launch(gemm_down3_kernel<WT, SC>, dim3(grid), dim3(kGThreads), (size_t)kGemmLds, stream,
+  const int grid = grid_for(items_bound(p, seg_lo, seg_hi, kD3Tok, kDnRows, true));
+  return launch(gemm_down3_kernel<WT, SC>, dim3(grid), dim3(kGThreads), (size_t)kD3Lds, stream,
                 start, stop, p, seg_lo, seg_hi);
 }
 
