@@ -117,14 +117,11 @@ __device__ __forceinline__ float routed_weight(double s, double total, float rou
   return (float)((double)routed_scale * s / total);
 }
 
-// Top-k of one token's logits with weights: lane r < k returns the expert of
-// rank r and its weight (route_select, then routed_weight).
+// Top-k of one token's keys (load_keys) with weights: lane r < k returns
+// the expert of rank r and its weight (route_select, then routed_weight).
 template <int PER>
-__device__ __forceinline__ void route_token(const float* __restrict__ row, int n_experts,
-                                            int top_k, float routed_scale, int lane,
-                                            int& out_id, float& out_w) {
-  uint32_t key[PER];
-  load_keys<PER>(row, n_experts, lane, key);
+__device__ __forceinline__ void route_keys(uint32_t (&key)[PER], int top_k, float routed_scale,
+                                           int lane, int& out_id, float& out_w) {
   uint32_t out_key;
   route_select<PER>(key, top_k, lane, out_id, out_key);
   const double s = lane < top_k ? gate_score((double)key_value(out_key)) : 0.0;
@@ -137,6 +134,16 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, int n
   double total = 0.0;
   for (int i = 0; i < top_k; ++i) total += s_of_rank(i);
   out_w = lane < top_k ? routed_weight(s, total, routed_scale) : 0.0f;
+}
+
+// route_keys of the token whose logits start at row.
+template <int PER>
+__device__ __forceinline__ void route_token(const float* __restrict__ row, int n_experts,
+                                            int top_k, float routed_scale, int lane,
+                                            int& out_id, float& out_w) {
+  uint32_t key[PER];
+  load_keys<PER>(row, n_experts, lane, key);
+  route_keys<PER>(key, top_k, routed_scale, lane, out_id, out_w);
 }
 
 }  // namespace

@@ -23,8 +23,10 @@ namespace {
 
 constexpr int kGroupThreads = 1024;
 constexpr int kGroupWaves = kGroupThreads / kWave;
-// flat indices held in LDS by the fused route+group kernel
+// flat indices held in LDS by the fused route+group kernel, and its tokens
+// (four per wavefront)
 constexpr int kFusedMaxFlat = 4096;
+constexpr int kFusedMaxTokens = 4 * kGroupWaves;
 
 // ---------------------------------------------------------------- routing
 
@@ -190,9 +192,10 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(
 }
 
 // Learned routing and grouping of a small batch by one workgroup: the
-// sixteen wavefronts route the tokens (token t by wavefront t % 16), keep
+// sixteen wavefronts route the tokens (token t by wavefront t % 16, at most
+// TPW each, all their logits requested before the first selection), keep
 // the ids in LDS, then group them.
-template <int PER>
+template <int PER, int TPW>
 __global__ __launch_bounds__(kGroupThreads) void route_group_kernel(
     const float* __restrict__ logits, int n_tokens, int n_experts, int top_k, float routed_scale,
     int32_t* __restrict__ ids, float* __restrict__ w, int32_t* __restrict__ counts,
@@ -202,15 +205,24 @@ __global__ __launch_bounds__(kGroupThreads) void route_group_kernel(
   __shared__ int32_t s_ids[kFusedMaxFlat];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  for (int t = wave; t < n_tokens; t += kGroupWaves) {
-    int id;
-    float wt;
-    route_token<PER>(logits + (size_t)t * n_experts, n_experts, top_k, routed_scale, lane, id,
-                     wt);
-    if (lane < top_k) {
-      ids[t * top_k + lane] = id;
-      w[t * top_k + lane] = wt;
-      s_ids[t * top_k + lane] = id;
+  uint32_t key[TPW][PER];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int t = min(wave + kGroupWaves * i, n_tokens - 1);  // past the end: a repeat, unused
+    load_keys<PER>(logits + (size_t)t * n_experts, n_experts, lane, key[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int t = wave + kGroupWaves * i;
+    if (t < n_tokens) {
+      int id;
+      float wt;
+      route_keys<PER>(key[i], top_k, routed_scale, lane, id, wt);
+      if (lane < top_k) {
+        ids[t * top_k + lane] = id;
+        w[t * top_k + lane] = wt;
+        s_ids[t * top_k + lane] = id;
+      }
     }
   }
   __syncthreads();
@@ -327,7 +339,10 @@ hipError_t launch_route_group(const float* logits, int n_tokens, int n_experts, 
                               float routed_scale, int32_t* ids, float* w, int32_t* counts,
                               int32_t* offsets, int32_t* perm, int32_t* inv_perm,
                               int32_t* dev_error, hipStream_t stream) {
-  if ((int64_t)n_tokens * top_k > kFusedMaxFlat) {
+  // one workgroup routes at most four tokens per wavefront; larger batches
+  // route on a wavefront per token and group in a second kernel (one
+  // workgroup routing 512 tokens took 133 us, the two kernels ~15)
+  if (n_tokens > kFusedMaxTokens || (int64_t)n_tokens * top_k > kFusedMaxFlat) {
     hipError_t e = launch_route(logits, n_tokens, n_experts, top_k, routed_scale, ids, w, stream);
     if (e != hipSuccess) return e;
     return launch_group(ids, n_tokens, top_k, n_experts, counts, offsets, perm, inv_perm,
@@ -352,20 +367,30 @@ hipError_t launch_route_group(const float* logits, int n_tokens, int n_experts, 
 #undef MOE_RGW
     return hipGetLastError();
   }
-#define MOE_RG(P)                                                                          \
-  route_group_kernel<P><<<1, kGroupThreads, 0, stream>>>(logits, n_tokens, n_experts,      \
-                                                         top_k, routed_scale, ids, w, counts, \
-                                                         offsets, perm, inv_perm, dev_error)
-  if (per <= 1)
-    MOE_RG(1);
-  else if (per <= 2)
-    MOE_RG(2);
-  else if (per <= 4)
-    MOE_RG(4);
-  else if (per <= 8)
-    MOE_RG(8);
-  else
-    MOE_RG(16);
+  const int tpw = (n_tokens + kGroupWaves - 1) / kGroupWaves;
+#define MOE_RG(P, T)                                                                          \
+  route_group_kernel<P, T><<<1, kGroupThreads, 0, stream>>>(logits, n_tokens, n_experts,      \
+                                                            top_k, routed_scale, ids, w, counts, \
+                                                            offsets, perm, inv_perm, dev_error)
+#define MOE_RG_T(P)   \
+  if (tpw <= 1)       \
+    MOE_RG(P, 1);     \
+  else if (tpw <= 2)  \
+    MOE_RG(P, 2);     \
+  else                \
+    MOE_RG(P, 4);
+  if (per <= 1) {
+    MOE_RG_T(1)
+  } else if (per <= 2) {
+    MOE_RG_T(2)
+  } else if (per <= 4) {
+    MOE_RG_T(4)
+  } else if (per <= 8) {
+    MOE_RG_T(8)
+  } else {
+    MOE_RG_T(16)
+  }
+#undef MOE_RG_T
 #undef MOE_RG
   return hipGetLastError();
 }
