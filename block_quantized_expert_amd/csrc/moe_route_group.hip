@@ -85,7 +85,7 @@ __global__ __launch_bounds__(256) void route_hash_kernel(const int32_t* __restri
 struct GroupShared {
   // s_count: histogram, later each expert's count in the current round;
   // s_next: next free position of each expert; s_wave[w][e]: count of
-  // wavefront w, then its offset inside the round (<= 1024).
+  // wavefront w, then its offset inside the round (<= 4096).
   int s_count[MOE_MAX_EXPERTS];
   int s_next[MOE_MAX_EXPERTS];
   uint16_t s_wave[kGroupWaves][MOE_MAX_EXPERTS];
@@ -135,23 +135,40 @@ __device__ void group_block(const int32_t* ids, int nk, int n_experts, int32_t* 
   }
   __syncthreads();
 
-  // 3. stable scatter, 1024 flat indices per round, in ascending order
+  // 3. stable scatter, 4096 flat indices per round in ascending order:
+  // wavefront w takes indices 256w .. +255 of the round as four batches of
+  // 64.  An index's rank inside its wavefront is the running count of its
+  // expert over the wavefront's earlier batches (s_wave, updated by the
+  // batch's last lane of each expert) plus its rank inside the batch (lanes
+  // with the same expert, from ballots of the expert's bits).
   int nbits = 0;
   while ((1 << nbits) < n_experts) ++nbits;
-  for (int base = 0; base < nk; base += kGroupThreads) {
-    const int f = base + tid;
-    const int e = f < nk ? ids[f] : -1;
-    const bool valid = e >= 0 && e < n_experts;
-    // lanes of this wavefront holding the same expert
-    uint64_t same = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = valid && ((e >> b) & 1);
-      const uint64_t m = __ballot(bit);
-      same &= bit ? m : ~m;
+  constexpr int kBatches = 4;
+  constexpr int kRound = kGroupThreads * kBatches;
+  for (int base = 0; base < nk; base += kRound) {
+    int ev[kBatches];
+#pragma unroll
+    for (int j = 0; j < kBatches; ++j) {
+      const int f = base + 256 * wave + 64 * j + lane;
+      ev[j] = f < nk ? ids[f] : -1;
     }
-    const int rank = __popcll(same & lanemask_lt(lane));
-    const bool last = valid && (same >> lane) == 1ull;
-    if (last) sh.s_wave[wave][e] = (uint16_t)(rank + 1);
+    int rank[kBatches];
+#pragma unroll
+    for (int j = 0; j < kBatches; ++j) {
+      const int e = ev[j];
+      const bool valid = e >= 0 && e < n_experts;
+      uint64_t same = __ballot(valid);
+      for (int b = 0; b < nbits; ++b) {
+        const bool bit = valid && ((e >> b) & 1);
+        const uint64_t m = __ballot(bit);
+        same &= bit ? m : ~m;
+      }
+      const int r = __popcll(same & lanemask_lt(lane));
+      const int run = valid ? (int)sh.s_wave[wave][e] : 0;  // read by every lane first
+      rank[j] = run + r;
+      const bool last = valid && (same >> lane) == 1ull;
+      if (last) sh.s_wave[wave][e] = (uint16_t)(run + r + 1);
+    }
     __syncthreads();
     // per expert: wavefront counts -> offsets inside this round
     for (int x = tid; x < n_experts; x += kGroupThreads) {
@@ -165,12 +182,17 @@ __device__ void group_block(const int32_t* ids, int nk, int n_experts, int32_t* 
       sh.s_count[x] = run;
     }
     __syncthreads();
-    if (valid) {
-      const int p = sh.s_next[e] + (int)sh.s_wave[wave][e] + rank;
-      perm[p] = f;
-      inv_perm[f] = p;
-    } else if (f < nk) {
-      inv_perm[f] = -1;
+#pragma unroll
+    for (int j = 0; j < kBatches; ++j) {
+      const int f = base + 256 * wave + 64 * j + lane;
+      const int e = ev[j];
+      if (e >= 0 && e < n_experts) {
+        const int p = sh.s_next[e] + (int)sh.s_wave[wave][e] + rank[j];
+        perm[p] = f;
+        inv_perm[f] = p;
+      } else if (f < nk) {
+        inv_perm[f] = -1;
+      }
     }
     __syncthreads();
     for (int x = tid; x < n_experts; x += kGroupThreads) {

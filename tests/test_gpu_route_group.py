@@ -172,10 +172,13 @@ def test_route_and_group_deterministic():
 
 @pytest.mark.parametrize("name,n_tokens", [("tiny", None), ("tiny", 32), ("tiny", 33),
                                            ("decode1", None), ("decode32", None),
-                                           ("prefill512", None), ("prefill512", 1000)])
+                                           ("decode32", 17), ("decode32", 64),
+                                           ("decode32", 65), ("prefill512", None),
+                                           ("prefill512", 1000)])
 def test_route_group_fused_equals_oracle(name, n_tokens):
-    # up to 64 flat entries: one wavefront; up to 4096: one workgroup;
-    # 1000 tokens x 6 takes the two-kernel path
+    # up to 64 flat entries: one wavefront; up to 64 tokens (one to four per
+    # wavefront) and 4096 entries: one workgroup; more tokens: a routing
+    # kernel and a grouping kernel
     wl = I.WORKLOADS[name]
     print("case route_group", name, n_tokens, flush=True)
     lg = I.router_logits(wl, n_tokens=n_tokens)
