@@ -60,10 +60,10 @@ DEFAULTS = {  # workload: (steps, warmup, copies, pool, event_every)
 FETCH_SCALE = 262144.0 / 131083.5
 WRITE_SCALE = 1.0
 KERNEL_TRAFFIC_KIB = {  # workload: (FETCH_SIZE, WRITE_SIZE) per step of the roofline stage
-    "decode1": (46171.7, 82.2),           # decode_fused_kernel<8>
-    "decode32": (474731.0, 2056.2),       # quant_x_kernel + gemm_gate_up_kernel<0, 112, true, true>
-    "prefill512": (1179494.4, 35260.2),   # quant_x_kernel + gemm_gate_up_kernel<0, 112, true, true>
-    "hash4096": (2533715.7, 329450.5),    # quant_x_kernel + MXFP4 routed and fp8 shared gate/up
+    "decode1": (46171.0, 82.2),           # decode_fused_kernel<8>
+    "decode32": (474928.5, 1668.5),       # quant_x_kernel + gemm_gate_up_kernel<0, 112, true, true>
+    "prefill512": (1184530.3, 27518.6),   # quant_x_kernel + gemm_gate_up_kernel<0, 112, true, true>
+    "hash4096": (2259314.5, 227773.1),    # quant_x_kernel + MXFP4 routed and fp8 shared gate/up
 }
 
 

@@ -135,26 +135,28 @@ __device__ void group_block(const int32_t* ids, int nk, int n_experts, int32_t* 
   }
   __syncthreads();
 
-  // 3. stable scatter, 4096 flat indices per round in ascending order:
-  // wavefront w takes indices 256w .. +255 of the round as four batches of
-  // 64.  An index's rank inside its wavefront is the running count of its
-  // expert over the wavefront's earlier batches (s_wave, updated by the
-  // batch's last lane of each expert) plus its rank inside the batch (lanes
-  // with the same expert, from ballots of the expert's bits).
+  // 3. stable scatter, nb * 1024 flat indices per round in ascending order
+  // (nb = 4 batches, or 1 when one round of 1024 covers them all): wavefront
+  // w takes indices 64 nb w .. +64 nb - 1 of the round as nb batches of 64.
+  // An index's rank inside its wavefront is the running count of its expert
+  // over the wavefront's earlier batches (s_wave, updated by the batch's
+  // last lane of each expert) plus its rank inside the batch (lanes with the
+  // same expert, from ballots of the expert's bits).
   int nbits = 0;
   while ((1 << nbits) < n_experts) ++nbits;
   constexpr int kBatches = 4;
-  constexpr int kRound = kGroupThreads * kBatches;
-  for (int base = 0; base < nk; base += kRound) {
+  const int nb = nk <= kGroupThreads ? 1 : kBatches;
+  for (int base = 0; base < nk; base += kGroupThreads * nb) {
     int ev[kBatches];
 #pragma unroll
     for (int j = 0; j < kBatches; ++j) {
-      const int f = base + 256 * wave + 64 * j + lane;
-      ev[j] = f < nk ? ids[f] : -1;
+      const int f = base + 64 * nb * wave + 64 * j + lane;
+      ev[j] = j < nb && f < nk ? ids[f] : -1;
     }
     int rank[kBatches];
 #pragma unroll
     for (int j = 0; j < kBatches; ++j) {
+      if (j >= nb) break;
       const int e = ev[j];
       const bool valid = e >= 0 && e < n_experts;
       uint64_t same = __ballot(valid);
@@ -184,7 +186,8 @@ __device__ void group_block(const int32_t* ids, int nk, int n_experts, int32_t* 
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < kBatches; ++j) {
-      const int f = base + 256 * wave + 64 * j + lane;
+      if (j >= nb) break;
+      const int f = base + 64 * nb * wave + 64 * j + lane;
       const int e = ev[j];
       if (e >= 0 && e < n_experts) {
         const int p = sh.s_next[e] + (int)sh.s_wave[wave][e] + rank[j];
