@@ -65,6 +65,11 @@ constexpr int kTokScaleBytes = 128 * 8;
 constexpr int kTokScaleOff = kGuScaleOff + 2 * kGuRows * (4096 / 32);
 static_assert(kTokScaleOff >= 2 * 128 * 256, "gate/up token tiles");
 static_assert(kTokScaleOff + 2 * kTokScaleBytes <= kGemmLds, "gate/up LDS");
+// gate/up with scale chunks (no LDS weight scales): the token scale bytes of
+// four steps (32 per row, up to 128 rows), two of them, after the largest
+// token tiles (112 rows x 2 buffers)
+constexpr int kTokChunkOff = 2 * 112 * 256;
+static_assert(kTokChunkOff + 2 * 128 * 32 <= kGemmLds, "gate/up LDS");
 // dynamic LDS + the static item prefix and scan words of a workgroup (plus
 // alignment): two workgroups in the 160 KiB of a CU
 static_assert(kGemmLds + (kSegMax + 1 + kGWaves) * 4 + 64 <= 80 * 1024, "two workgroups per CU");
@@ -529,11 +534,27 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
   // token tile b at smem + b * kTokB, its scales at kTokScaleOff + b * 1 KiB
   // (offsets from smem keep LDS addressing)
   auto buf = [&](int b) { return smem + (b & 1) * kTokB; };
+  // token scale bytes of step ks: per step (8 bytes a row), or with the
+  // weight-scale chunks (kCh) per four steps (32 bytes a row, one request
+  // per row instead of four), in buffer (ks / 4) & 1, row stride 32
   auto tsb = [&](int b) { return smem + kTokScaleOff + (b & 1) * kTokScaleBytes; };
-  // step ks's activations (rows and scale bytes) into buffer ks & 1
+  auto tsc = [&](int ks) -> const char* {
+    return kCh ? smem + kTokChunkOff + ((ks >> 2) & 1) * (128 * 32) + (ks & 3) * 8 : tsb(ks);
+  };
+  constexpr int kTsStride = kCh ? 32 : 8;
+  auto copy_tsc = [&](int c) {  // kCh: chunk c (steps 4c .. 4c+3), lane pairs of rows 32w ..
+    const int cc = min(c, nks / 4 - 1);
+    if (32 * wave < 16 * nbt)
+      __builtin_amdgcn_global_load_lds(
+          p.xs + (int64_t)srow * (p.hidden / 16) + cc * 32 + 16 * (lane & 1),
+          (__attribute__((address_space(3))) void*)(smem + kTokChunkOff + (c & 1) * (128 * 32) +
+                                                    1024 * wave),
+          16, 0, 0);
+  };
+  // step ks's activations (rows, and per step their scale bytes) into buffer ks & 1
   auto copy_tok = [&](int ks) {
     st.copy(p.xq, 2 * (int64_t)p.hidden, ks, buf(ks), nbt);
-    if (32 * wave < 16 * nbt)
+    if (!kCh && 32 * wave < 16 * nbt)
       __builtin_amdgcn_global_load_lds(
           xsl + ks * 8, (__attribute__((address_space(3))) void*)(tsb(ks) + 256 * wave), 4, 0, 0);
   };
@@ -541,7 +562,7 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
   // not chunked) times the token tile in LDS, hi and lo parts
   auto step_mma = [&](int ks, const u32x4 (&qq)[2][2][Q], const uint32_t (&uu)[2][2]) {
     const char* cur = buf(ks);
-    const char* cts = tsb(ks);
+    const char* cts = tsc(ks);
     uint32_t sa[2][2];
     i32x8 a[2][2];
 #pragma unroll
@@ -561,7 +582,8 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
       const char* row = cur + n * 256;
       const int c0 = (u & 1) * 8 + g;
       bop[u & 1] = join8(tile_chunk(row, c0, r16), tile_chunk(row, c0 + 4, r16));
-      if ((u & 1) == 0) sbt[(u >> 1) & 1] = *reinterpret_cast<const uint16_t*>(cts + n * 8 + 2 * g);
+      if ((u & 1) == 0)
+        sbt[(u >> 1) & 1] = *reinterpret_cast<const uint16_t*>(cts + n * kTsStride + 2 * g);
     };
     read_op(0);
 #pragma unroll
@@ -583,7 +605,10 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
     }
   };
   if (kSC) copy_scales();
-  if (kCh) load_sc(0);
+  if (kCh) {
+    load_sc(0);
+    copy_tsc(0);
+  }
   load_w(0, q0, u0);
   copy_tok(0);
   wait_vm<0>();
@@ -596,6 +621,7 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
     if (kCh && (ks & 3) == 0) {
       take_sc();
       load_sc((ks >> 2) + 1);
+      copy_tsc((ks >> 2) + 1);  // its buffer held chunk c-1, done before this step
     }
     // step ks+1's activations, then its weights (one step ahead: the step
     // ends by moving them into q0, so a deeper register ring would only
