@@ -10,7 +10,7 @@
 //   GPU coverage: routed experts in MXFP4, dense weights fp8-e4m3 + UE8M0;
 //   expert-grouped GEMM on the GPU.
 //
-// A work item is (segment, row tile, token tile of up to kTileTok slots).  A
+// A work item is (segment, row tile, token tile of up to TT slots).  A
 // segment is a routed expert (slots offsets[e] .. offsets[e+1]) or the shared
 // expert (slot N*k + t is token t).  Items of one row tile are consecutive, so
 // the workgroups that multiply the same weights with different token tiles
@@ -20,22 +20,31 @@
 //
 // Inside an item each wavefront owns whole output rows over the full
 // reduction: no partial sums cross wavefronts.  The reduction runs in steps
-// of 128.  The token operand of a step (activation rows gathered through
-// perm, or the h rows of the slots) is staged in LDS, double buffered; the
-// weight codes of step ks+1 and its token operand are in flight while step ks
-// multiplies.
+// of 128.  The token operand of a step (quantized activation rows gathered
+// through perm, or the h rows of the slots) is staged in LDS, double
+// buffered; the weight codes of step ks+1 and its token operand are in
+// flight while step ks multiplies.
 //
-// Gate/up: a workgroup owns 128 intermediate rows and up to 128 tokens;
-// wavefront w owns rows 32w .. 32w+31 of the gate and of the up matrix
-// (four 16-row blocks), so one token fragment read from LDS feeds four
-// MFMAs and one decoded weight fragment feeds up to eight token blocks.  The
-// epilogue applies SwiGLU and writes h as a bf16 hi/lo pair.
+// Gate/up (bf16 x): quant_x_kernel first writes x as two E4M3 parts with
+// UE8M0 block scales that reproduce the bf16 value.  The weights enter the
+// scaled 16x16x128 instruction as stored (E2M1 or E4M3 codes with their
+// UE8M0 bytes), so nothing is decoded in registers: two instructions per
+// tile and step, one per part.  A workgroup owns 128 intermediate rows and
+// up to 112 (MXFP4) or 64 (fp8) tokens; wavefront w owns rows 32w .. 32w+31
+// of the gate and of the up matrix (four 16-row blocks), so one token
+// fragment read from LDS feeds four instructions and one weight fragment
+// feeds up to seven token blocks.  The epilogue applies SwiGLU and writes h
+// as three E4M3 parts with their scale bytes (split_e4m3x3).
 //
 // Down: a workgroup owns 256 hidden rows and up to 64 tokens; wavefront w
-// owns rows 64w .. 64w+63 (four blocks) and multiplies them with h_hi and
-// h_lo.  The epilogue scales each token column by its routing weight (1 for
-// the shared expert) and writes the per-slot output; a separate pass sums
-// the slots of every token in a fixed order.
+// owns rows 64w .. 64w+63 (four blocks).  gemm_down3_kernel multiplies the
+// stored weight codes with the three E4M3 parts of h on the scaled
+// instruction; gemm_down_kernel serves h as a bf16 hi/lo pair (written by
+// the gate/up of fp32 x and by the small-batch decode gate/up): it decodes
+// the weights to bf16 and multiplies them with h_hi and h_lo.  Both
+// epilogues scale each token column by its routing weight (1 for the
+// shared expert) and write the per-slot output; a separate pass sums the
+// slots of every token in a fixed order.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
