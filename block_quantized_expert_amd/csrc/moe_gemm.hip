@@ -48,6 +48,8 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "moe_device.h"
 #include "moe_formats.h"
 #include "moe_kernels.h"
@@ -452,7 +454,11 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
     }
     srow = shared ? slot_s - nk : pvs / p.top_k;
   }
-  const uint8_t* xsl = p.xs + (int64_t)srow * (p.hidden / 16) + 4 * (lane & 1);
+  // the lane's bytes of its token-scale row: with O32 one 32-bit offset
+  // from the uniform base (no 64-bit lane address to keep across items)
+  using XsOff = std::conditional_t<O32, uint32_t, int64_t>;
+  const XsOff xs_row = (XsOff)srow * (XsOff)(p.hidden / 16);
+  const uint8_t* xsl = p.xs + (xs_row + 4 * (lane & 1));
 
   // weight codes: the current step and the next
   u32x4 q0[2][2][Q], q1[2][2][Q];
@@ -555,7 +561,7 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
     const int cc = min(c, nks / 4 - 1);
     if (32 * wave < 16 * nbt)
       __builtin_amdgcn_global_load_lds(
-          p.xs + (int64_t)srow * (p.hidden / 16) + cc * 32 + 16 * (lane & 1),
+          p.xs + (xs_row + (XsOff)(cc * 32 + 16 * (lane & 1))),
           (__attribute__((address_space(3))) void*)(smem + kTokChunkOff + (c & 1) * (128 * 32) +
                                                     1024 * wave),
           16, 0, 0);
