@@ -80,6 +80,28 @@ def test_sampled_full_size(name, n_tok, n_rows, with_shared):
     assert_y_close(y.cpu().numpy()[tokens][:, rows], ref)
 
 
+def test_batch_past_32bit_activation_offsets():
+    """263144 tokens at hidden 4096: the quantized activations (two bytes
+    per input) pass 2^31 bytes, so the batched gate/up kernels (MXFP4 routed,
+    fp8 shared) take their 64-bit-offset form.  Small experts keep the run
+    short; sampled tokens on both sides of the 2^31-byte mark against the
+    oracle."""
+    wl = I.Workload("past2g", 263144, 4096, 128, 4, 1, 1.5, "bf16", "learned", 119, 124,
+                    "fp8_e4m3_b128", "none", 27)
+    first_past = (1 << 31) // (2 * wl.hidden)  # first token whose row starts at 2^31
+    assert first_past < wl.n_tokens
+    print("case past2g: %d tokens, hidden %d" % (wl.n_tokens, wl.hidden), flush=True)
+    _, x, routing, y, ids, w, _ = _run(wl)
+    rids, rw = oracle_routing(wl, routing)
+    assert np.array_equal(ids.cpu().numpy(), rids)
+    tokens = sorted(set(_sample(first_past, 3, 13) + [first_past - 1, first_past,
+                                                       wl.n_tokens - 1]))
+    rows = _sample(wl.hidden, 256, 14)
+    got = y[torch.tensor(tokens, device=y.device)][:, torch.tensor(rows, device=y.device)]
+    ref = oracle_y(wl, x, rids, rw, tokens=tokens, rows=rows)
+    assert_y_close(got.cpu().numpy(), ref)
+
+
 # ------------------------------------------------------- small, several tiles
 
 SMALL = I.Workload("small", 100, 256, 128, 8, 2, 1.5, "bf16", "learned", 119, 124,
