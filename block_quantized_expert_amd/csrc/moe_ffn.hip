@@ -931,20 +931,24 @@ hipError_t allow_lds(K kernel) {
                              hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget);
 }
 
-template <int NBT, bool XF32>
+// fp32 activations: bf16 ones take the grouped GEMM or the decode kernel,
+// so only the XF32 instantiations are launched.
+template <int NBT>
 hipError_t gate_up_launch(const FfnParams& p, dim3 grid, hipStream_t stream, hipEvent_t start,
                           hipEvent_t stop) {
-  // a small tile's activation rows fit in LDS: stage them once per item
-  const int x_stride = p.hidden * (XF32 ? 4 : 2) + 16;
-  const int rows = p.n_tokens < 16 * NBT ? p.n_tokens : 16 * NBT;
-  const size_t lds = (size_t)rows * x_stride;
-  if (NBT == 1 && lds <= (size_t)kLdsBudget) {
-    static const hipError_t attr = allow_lds(gate_up_kernel<NBT, XF32, true>);
-    if (attr != hipSuccess) return attr;
-    return launch(gate_up_kernel<NBT, XF32, true>, grid, dim3(kThreads), lds, stream, start, stop,
-                  p, x_stride);
+  if constexpr (NBT == 1) {
+    // a one-block tile's activation rows fit in LDS: stage them once per item
+    const int x_stride = p.hidden * 4 + 16;
+    const int rows = p.n_tokens < 16 ? p.n_tokens : 16;
+    const size_t lds = (size_t)rows * x_stride;
+    if (lds <= (size_t)kLdsBudget) {
+      static const hipError_t attr = allow_lds(gate_up_kernel<1, true, true>);
+      if (attr != hipSuccess) return attr;
+      return launch(gate_up_kernel<1, true, true>, grid, dim3(kThreads), lds, stream, start,
+                    stop, p, x_stride);
+    }
   }
-  return launch(gate_up_kernel<NBT, XF32, false>, grid, dim3(kThreads), 0, stream, start, stop,
+  return launch(gate_up_kernel<NBT, true, false>, grid, dim3(kThreads), 0, stream, start, stop,
                 p, 0);
 }
 
@@ -954,9 +958,7 @@ hipError_t gate_up_nbt(const FfnParams& p, hipStream_t stream, hipEvent_t start,
   const int64_t shared_tiles = p.has_shared ? (p.n_tokens + TN - 1) / TN : 0;
   const int64_t items = routed_tiles_bound(p, TN) * (p.inter / 16) +
                         shared_tiles * (p.shared_inter / 16);
-  const dim3 grid(grid_for(items));
-  if (p.x_f32) return gate_up_launch<NBT, true>(p, grid, stream, start, stop);
-  return gate_up_launch<NBT, false>(p, grid, stream, start, stop);
+  return gate_up_launch<NBT>(p, dim3(grid_for(items)), stream, start, stop);
 }
 
 // Slots of a small batch; 0 when the batch takes the per-slot path.

@@ -50,6 +50,7 @@ class Workload:
     vocab: int = 129280
     min_gap: float = 1e-3  # every pair of logits of a token differs by this
     shared_inter: int = 0  # 0: same as inter
+    routed: str = "mxfp4"  # weight type of the routed experts
 
 
 WORKLOADS = {
@@ -170,25 +171,42 @@ def _mxfp4_block(wl, proj, copy, first, n_exp, device):
     return (codes.view(n_exp, rows, cols // 2), scales.view(n_exp, rows, cols // 32))
 
 
-def _fp8_matrix(wl, proj, copy, device):
-    """fp8-e4m3 codes: sign uniform, exponent field uniform in 0..10 (so
-    zeros and subnormals occur), mantissa uniform; never NaN."""
+def _fp8_block(wl, proj, copy, first, n_exp, device):
+    """fp8-e4m3 codes of matrices first .. first+n_exp-1 of a projection:
+    sign uniform, exponent field uniform in 0..10 (so zeros and subnormals
+    occur), mantissa uniform; never NaN.  One UE8M0 scale per 1x128 block."""
     rows, cols = proj_shape(wl, proj)
     pid = PROJ_IDS[proj]
-    w = hash_words(stream_key(wl.seed, copy, pid, 0), 0, rows * cols, device)
+    n = rows * cols
+    w = hash_words(stream_key(wl.seed, copy, pid, 0), first * n, n_exp * n, device)
     sign = w & 1
     mant = (w >> 1) & 7
     expf = (((w >> 8) & 0xFFFF) * 11) >> 16
-    codes = ((sign << 7) | (expf << 3) | mant).to(torch.uint8).view(rows, cols)
+    codes = ((sign << 7) | (expf << 3) | mant).to(torch.uint8).view(n_exp, rows, cols)
     nval = wl.scale_hi - wl.scale_lo + 1
-    sc = uniform_small(stream_key(wl.seed, copy, pid, 1), 0, rows * (cols // 128), nval, device)
-    scales = (sc + wl.scale_lo).to(torch.uint8).view(rows, cols // 128)
+    sb = rows * (cols // 128)
+    sc = uniform_small(stream_key(wl.seed, copy, pid, 1), first * sb, n_exp * sb, nval, device)
+    scales = (sc + wl.scale_lo).to(torch.uint8).view(n_exp, rows, cols // 128)
     return codes, scales
+
+
+def _fp8_matrix(wl, proj, copy, device):
+    c, s = _fp8_block(wl, proj, copy, 0, 1, device)
+    return c[0], s[0]
+
+
+def _routed_block(wl, proj, copy, first, n_exp, device):
+    """Codes and scales of routed experts first .. first+n_exp-1."""
+    if wl.routed == "mxfp4":
+        return _mxfp4_block(wl, proj, copy, first, n_exp, device)
+    if wl.routed == "fp8_e4m3_b128":
+        return _fp8_block(wl, proj, copy, first, n_exp, device)
+    raise ValueError(wl.routed)
 
 
 def expert_weights(wl: Workload, proj: str, experts, device="cpu", copy: int = 0):
     """{e: (codes, scales)} for the listed routed experts of ``proj``."""
-    return {int(e): tuple(t[0] for t in _mxfp4_block(wl, proj, copy, int(e), 1, device))
+    return {int(e): tuple(t[0] for t in _routed_block(wl, proj, copy, int(e), 1, device))
             for e in experts}
 
 
@@ -203,19 +221,22 @@ def make_layer(wl: Workload, device="cpu", copy: int = 0, experts=None,
     layer = {"hidden": wl.hidden, "inter": wl.inter, "n_experts": wl.n_experts}
     for proj in ("gate", "up", "down"):
         if experts is None:
-            rows, cols = proj_shape(wl, proj)
-            codes = torch.empty((wl.n_experts, rows, cols // 2), dtype=torch.uint8, device=device)
-            scales = torch.empty((wl.n_experts, rows, cols // 32), dtype=torch.uint8, device=device)
+            codes = scales = None
             for e0 in range(0, wl.n_experts, chunk):
                 n = min(chunk, wl.n_experts - e0)
-                c, s = _mxfp4_block(wl, proj, copy, e0, n, device)
+                c, s = _routed_block(wl, proj, copy, e0, n, device)
+                if codes is None:
+                    codes = torch.empty((wl.n_experts,) + tuple(c.shape[1:]), dtype=torch.uint8,
+                                        device=device)
+                    scales = torch.empty((wl.n_experts,) + tuple(s.shape[1:]),
+                                         dtype=torch.uint8, device=device)
                 codes[e0:e0 + n] = c
                 scales[e0:e0 + n] = s
         else:
             ew = expert_weights(wl, proj, experts, device, copy)
             codes = {e: v[0] for e, v in ew.items()}
             scales = {e: v[1] for e, v in ew.items()}
-        layer[proj] = {"type": "mxfp4", "codes": codes, "scales": scales}
+        layer[proj] = {"type": wl.routed, "codes": codes, "scales": scales}
     if with_shared:
         shared = {"inter": wl.shared_inter or wl.inter}
         for proj in ("shared_gate", "shared_up", "shared_down"):

@@ -115,7 +115,20 @@ SMALL = I.Workload("small", 100, 256, 128, 8, 2, 1.5, "bf16", "learned", 119, 12
     replace(SMALL, n_tokens=17, act="f32", top_k=3, seed=24),     # fp32 x, hi/lo split
     replace(SMALL, n_tokens=130, n_experts=5, top_k=5, seed=25),  # every expert, 3 tiles
     replace(SMALL, n_tokens=1, hidden=512, inter=384, seed=26),   # K steps 4 and 3
-], ids=["ragged100", "fp8shared40", "sharedinter33", "f32x17", "allexperts130", "odd_k1"])
+    replace(SMALL, routed="fp8_e4m3_b128", seed=28),             # fp8 routed, grouped GEMM
+    replace(SMALL, routed="fp8_e4m3_b128", act="f32", n_tokens=3, seed=29),   # small down
+    replace(SMALL, routed="fp8_e4m3_b128", shared="fp8_e4m3_b128", act="f32", n_tokens=3,
+            seed=30),
+    replace(SMALL, shared="fp8_e4m3_b128", act="f32", n_tokens=3, seed=31),
+    replace(SMALL, routed="fp8_e4m3_b128", act="f32", n_tokens=60, seed=32),  # bf16-pair down
+    replace(SMALL, act="f32", n_tokens=40, inter=512, seed=33),  # pair down, scale chunks
+    replace(SMALL, routed="fp8_e4m3_b128", act="f32", n_tokens=40, inter=512, seed=34),
+    replace(SMALL, n_tokens=3, hidden=1024, seed=35),            # decode gate/up, 2 steps
+    replace(SMALL, n_tokens=2, hidden=2048, seed=36),            # decode gate/up, 4 steps
+], ids=["ragged100", "fp8shared40", "sharedinter33", "f32x17", "allexperts130", "odd_k1",
+        "fp8routed100", "fp8routed_f32x3", "fp8both_f32x3", "fp8shared_f32x3",
+        "fp8routed_f32x60", "f32x40_i512", "fp8routed_f32x40_i512", "decode_h1024",
+        "decode_h2048"])
 def test_small_layers_full(wl):
     print("case small", wl, flush=True)
     _, x, routing, y, ids, w, _ = _run(wl)

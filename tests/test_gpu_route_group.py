@@ -189,3 +189,25 @@ def test_route_group_fused_equals_oracle(name, n_tokens):
     assert_w_close(w.cpu().numpy(), rw)
     for got, ref in zip(g, O.group(rids, wl.n_experts)):
         assert np.array_equal(got.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("n,e,k", [
+    (10, 16, 8), (20, 16, 8), (12, 256, 6),              # 1 and 4 experts a lane
+    (2, 100, 8), (12, 100, 8), (30, 100, 8), (60, 100, 8),     # 2 experts a lane
+    (3, 500, 6), (14, 500, 6), (25, 500, 6), (50, 500, 6),     # 8
+    (7, 1000, 8), (16, 1000, 8), (31, 1000, 8), (64, 1000, 8),  # 16
+])
+def test_route_group_fused_expert_widths(n, e, k):
+    """The fused route+group kernels at every experts-per-lane width and
+    tokens-per-wavefront count: N*k <= 64 runs on one wavefront, else one
+    workgroup takes one, two or four tokens per wavefront."""
+    print("case route_group widths", n, e, k, flush=True)
+    lg = torch.from_numpy(I.spaced_logits(np.random.default_rng(7000 + 13 * n + e), n,
+                                          np.zeros(e), 1e-3))
+    ids, w, g = B.moe_route_group(lg.to(DEV), k, 1.5)
+    torch.cuda.synchronize()
+    rids, rw = O.route_topk(lg.numpy(), k, 1.5)
+    assert np.array_equal(ids.cpu().numpy(), rids)
+    assert_w_close(w.cpu().numpy(), rw)
+    for got, ref in zip(g, O.group(rids, e)):
+        assert np.array_equal(got.cpu().numpy(), ref)

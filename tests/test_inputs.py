@@ -43,6 +43,28 @@ def test_single_expert_matches_stacked_layer():
     assert int(s.min()) == 121 and int(s.max()) == 124
 
 
+def test_fp8_routed_experts_match_stacked_layer():
+    # routed experts in fp8-e4m3 (one UE8M0 per 1x128): regenerating some
+    # alone gives the stacked bytes; matrix 0 of the shared expert's stream
+    # is the one-matrix shared generator
+    from dataclasses import replace
+    wl = replace(I.WORKLOADS["tiny"], routed="fp8_e4m3_b128")
+    full = I.make_layer(wl)
+    part = I.make_layer(wl, experts=[0, 9])
+    for proj in ("gate", "up", "down"):
+        assert full[proj]["type"] == "fp8_e4m3_b128"
+        for e in (0, 9):
+            assert torch.equal(full[proj]["codes"][e], part[proj]["codes"][e])
+            assert torch.equal(full[proj]["scales"][e], part[proj]["scales"][e])
+    assert full["gate"]["codes"].shape == (16, 128, 256)
+    assert full["gate"]["scales"].shape == (16, 128, 2)
+    assert full["down"]["codes"].shape == (16, 256, 128)
+    assert full["down"]["scales"].shape == (16, 256, 1)
+    c, sc = I._fp8_matrix(wl, "shared_up", 0, "cpu")
+    cb, sb = I._fp8_block(wl, "shared_up", 0, 0, 1, "cpu")
+    assert torch.equal(c, cb[0]) and torch.equal(sc, sb[0])
+
+
 def test_fp8_shared_codes_are_finite_and_cover_subnormals():
     wl = I.WORKLOADS["hash4096"]
     c, s = I._fp8_matrix(wl, "shared_gate", 0, "cpu")
