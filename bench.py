@@ -254,7 +254,7 @@ def cpu_baseline(wl, seconds_hint: float):
 
     n_sample = {"decode1": 1, "decode32": 2, "prefill512": 2, "hash4096": 2}.get(wl.name, 8)
     t_oracle, done, rounds = 0.0, 0, 0
-    while (t_oracle < seconds_hint or rounds == 0) and rounds < 16:
+    while (t_oracle < seconds_hint or rounds == 0) and rounds < 48:
         tokens = list(range(min(n_sample, wl.n_tokens)))
         x = I.activations_to_numpy(I.activations(wl, copy=rounds))[tokens]
         r = I.routing_to_numpy(I.routing_inputs(wl, copy=rounds))
