@@ -942,7 +942,8 @@ __global__ __launch_bounds__(kGThreads, 2) void gemm_down_kernel(FfnParams p, in
 // row.  LDS per workgroup: two tiles, then (up to three token blocks) the
 // item's weight scales, then the tiles' scale bytes.  Up to 64 tokens per
 // tile: 96 would fit (so that an expert with up to 96 tokens streams its
-// down weights once) but measured 10 % slower on hash4096.
+// down weights once) but measured 8 % slower on hash4096 and 15 % slower on
+// prefill512.
 constexpr int kD3Tok = 64;
 constexpr int kD3Full = 2 * 3 * kD3Tok * 128 + 2 * kD3Tok * 16;             // full tiles
 constexpr int kD3Sc = 2 * 3 * 48 * 128 + kDnRows * (2048 / 32) + 2 * 48 * 16;  // 3 blocks + scales
