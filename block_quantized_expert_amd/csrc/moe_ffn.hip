@@ -33,6 +33,11 @@
 // sum builds up in one accumulator in a fixed order (deterministic, no
 // per-slot outputs).  Larger batches write weighted per-slot outputs and
 // sum them in a separate combine kernel, shared first then slots 0..k-1.
+//
+// Which gate/up runs: bf16 activations of up to 16 tokens with MXFP4 experts
+// take gate_up_decode_kernel; fp32 activations take gate_up_kernel; every
+// other batch goes to the grouped GEMMs (moe_gemm.hip), which store h as
+// three E4M3 parts for their own down projection.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
