@@ -60,7 +60,7 @@ DEFAULTS = {  # workload: (steps, warmup, copies, pool, event_every)
 FETCH_SCALE = 262144.0 / 131083.5
 WRITE_SCALE = 1.0
 KERNEL_TRAFFIC_KIB = {  # workload: (FETCH_SIZE, WRITE_SIZE) per step of the roofline stage
-    "decode1": (46171.0, 82.2),           # decode_fused_kernel<8>
+    "decode1": (46176.4, 82.2),           # decode_fused_kernel<8>
     "decode32": (474862.2, 1669.1),       # quant_x_kernel + gemm_gate_up_kernel<0, 112, true, true>
     "prefill512": (1184148.4, 27735.4),   # quant_x_kernel + gemm_gate_up_kernel<0, 112, true, true>
     "hash4096": (2321829.8, 231717.5),    # quant_x_kernel + MXFP4 routed and fp8 shared gate/up
