@@ -84,7 +84,7 @@ typedef enum { MOE_W_MXFP4 = 0, MOE_W_FP8E4M3_B128 = 1 } moe_weight_type;
 #define MOE_DEVERR_SYNC 4      /* moe_forward: a wait of the single-token kernel timed
                                   out (y incomplete)                    */
 
-/* Limits of this build. */
+/* Limits of the library. */
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOP_K 8
 #define MOE_MAX_DIM 65536

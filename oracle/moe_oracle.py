@@ -24,7 +24,7 @@ What it computes, and where the pages define it (pages cited by title):
 * [cism] "Development Snapshot Validation", 4-bit quantization scheme study
   table: MXFP4 is "E2M1 + E8M0, blocks of 32" at 4.25 bits per weight.
 
-Readings taken where the pages are silent (each also listed in the design doc):
+Readings taken where the pages are silent:
 
 * E2M1 element: sign bit 3, two exponent bits (bias 1), one mantissa bit,
   i.e. the OCP MX v1.0 element; magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}.
