@@ -22,7 +22,7 @@ What it computes, and where the pages define it (pages cited by title):
   introduction: routed experts are native fp4 (MXFP4); the dense set is
   fp8-e4m3 with UE8M0 block scales.
 * [cism] "Development Snapshot Validation", 4-bit quantization scheme study
-  table: MXFP4 is "E2M1 + E8M0, blocks of 32" at 4.25 bits per weight.
+  table: MXFP4 is E2M1 elements with E8M0 scales, one per block of 32, at 4.25 bits per weight.
 
 Readings taken where the pages are silent:
 
