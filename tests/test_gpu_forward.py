@@ -64,6 +64,24 @@ def test_single_token_shapes(wl, with_shared):
     _run_and_check(wl, with_shared)
 
 
+@pytest.mark.parametrize("n_tokens", [32, 200])
+def test_batches_take_the_grouped_gemms(n_tokens):
+    """bf16 batches of more than 16 tokens through moe_forward: the
+    route+group kernel(s), then the grouped-GEMM gate/up and down and the
+    combine.  Routing exact; y on sampled tokens and rows."""
+    wl = replace(I.WORKLOADS["decode32"], n_tokens=n_tokens)
+    print("case forward batch", n_tokens, flush=True)
+    layer, x, x_d, routing, routing_d = gpu_inputs(wl, copy=5)
+    buf = B.moe_forward(layer, routing_d["logits"], x_d, wl.routed_scale)
+    torch.cuda.synchronize()
+    assert int(buf.dev_error.item()) == 0
+    ids_ref, w_ref = _check_routing(wl, routing, buf)
+    tokens = sorted(np.random.default_rng(n_tokens).choice(n_tokens, 4, replace=False).tolist())
+    rows = sorted(np.random.default_rng(n_tokens + 1).choice(wl.hidden, 512, replace=False).tolist())
+    ref = oracle_y(wl, x, ids_ref, w_ref, tokens=tokens, rows=rows, copy=5)
+    assert_y_close(buf.y.cpu().numpy()[tokens][:, rows], ref)
+
+
 @pytest.mark.parametrize("wl", [
     replace(ONE, act="f32", seed=36),              # fp32 x: separate kernels
     replace(ONE, n_tokens=3, seed=37),             # several tokens: separate kernels
