@@ -83,17 +83,22 @@ __global__ __launch_bounds__(256) void route_hash_kernel(const int32_t* __restri
 // ---------------------------------------------------------------- grouping
 
 struct GroupShared {
-  // s_count: histogram, later each expert's count in the current round;
-  // s_next: next free position of each expert; s_wave[w][e]: count of
-  // wavefront w, then its offset inside the round (<= 4096).
-  int s_count[MOE_MAX_EXPERTS];
-  int s_next[MOE_MAX_EXPERTS];
-  uint16_t s_wave[kGroupWaves][MOE_MAX_EXPERTS];
+  // s_base[w][e]: how many entries of wavefront w's segment go to expert e,
+  // then the position of the next one
+  int s_base[kGroupWaves][MOE_MAX_EXPERTS];
   int s_wave_sum[kGroupWaves];
 };
 
 // The whole grouping by one 1024-thread workgroup.  `ids` may point at
 // global memory or LDS.
+//
+// Wavefront w owns one contiguous segment of the flat indices (segments in
+// ascending order, a multiple of 64 long).  It counts its segment per
+// expert; one scan over (expert, wavefront) gives each wavefront the first
+// position of each expert; then every wavefront scatters its segment in
+// ascending order, 64 indices at a time, with no further barrier.  The rank
+// of an index inside its batch of 64 is the number of earlier lanes holding
+// the same expert, from ballots of the expert's bits.
 __device__ void group_block(const int32_t* ids, int nk, int n_experts, int32_t* __restrict__ counts,
                             int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
                             int32_t* __restrict__ inv_perm, int32_t* __restrict__ dev_error,
@@ -101,25 +106,49 @@ __device__ void group_block(const int32_t* ids, int nk, int n_experts, int32_t* 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  constexpr int kLoads = 8;  // batches of 64 requested before the first is used
 
-  for (int e = tid; e < n_experts; e += kGroupThreads) sh.s_count[e] = 0;
   for (int i = tid; i < kGroupWaves * MOE_MAX_EXPERTS; i += kGroupThreads)
-    (&sh.s_wave[0][0])[i] = 0;
+    (&sh.s_base[0][0])[i] = 0;
+  const int64_t seg = ((int64_t)nk + kGroupThreads - 1) / kGroupThreads * kWave;
+  const int lo = (int)min<int64_t>((int64_t)wave * seg, nk);
+  const int len = (int)min<int64_t>((int64_t)wave * seg + seg, nk) - lo;
+  const int32_t* sid = ids + lo;
   __syncthreads();
 
-  // 1. histogram (order-free)
+  // 1. per-wavefront histogram of its own segment
   int bad = 0;
-  for (int f = tid; f < nk; f += kGroupThreads) {
-    const int e = ids[f];
-    if (e >= 0 && e < n_experts)
-      atomicAdd(&sh.s_count[e], 1);
-    else
-      bad = 1;
+  for (int d = 0; d < len; d += kWave * kLoads) {
+    int ev[kLoads];
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      const int o = d + kWave * j + lane;
+      ev[j] = o < len ? sid[o] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      if (d + kWave * j + lane < len) {
+        const int e = ev[j];
+        if (e >= 0 && e < n_experts)
+          atomicAdd(&sh.s_base[wave][e], 1);
+        else
+          bad = 1;
+      }
+    }
   }
   __syncthreads();
 
-  // 2. exclusive scan over experts (n_experts <= 1024: one per thread)
-  const int c = tid < n_experts ? sh.s_count[tid] : 0;
+  // 2. per expert (one per thread, n_experts <= 1024): its count, the prefix
+  // over wavefronts, then the exclusive scan over experts
+  int c = 0;
+  if (tid < n_experts) {
+#pragma unroll
+    for (int w = 0; w < kGroupWaves; ++w) {
+      const int v = sh.s_base[w][tid];
+      sh.s_base[w][tid] = c;
+      c += v;
+    }
+  }
   int incl = wave_incl_scan(c);
   if (lane == kWave - 1) sh.s_wave_sum[wave] = incl;
   __syncthreads();
@@ -130,33 +159,27 @@ __device__ void group_block(const int32_t* ids, int nk, int n_experts, int32_t* 
   if (tid < n_experts) {
     counts[tid] = c;
     offsets[tid] = excl;
-    sh.s_next[tid] = excl;
+#pragma unroll
+    for (int w = 0; w < kGroupWaves; ++w) sh.s_base[w][tid] += excl;
     if (tid == n_experts - 1) offsets[n_experts] = incl;
   }
   __syncthreads();
 
-  // 3. stable scatter, nb * 1024 flat indices per round in ascending order
-  // (nb = 4 batches, or 1 when one round of 1024 covers them all): wavefront
-  // w takes indices 64 nb w .. +64 nb - 1 of the round as nb batches of 64.
-  // An index's rank inside its wavefront is the running count of its expert
-  // over the wavefront's earlier batches (s_wave, updated by the batch's
-  // last lane of each expert) plus its rank inside the batch (lanes with the
-  // same expert, from ballots of the expert's bits).
+  // 3. stable scatter of each segment; s_base[wave] is touched by this
+  // wavefront only from here on
   int nbits = 0;
   while ((1 << nbits) < n_experts) ++nbits;
-  constexpr int kBatches = 4;
-  const int nb = nk <= kGroupThreads ? 1 : kBatches;
-  for (int base = 0; base < nk; base += kGroupThreads * nb) {
-    int ev[kBatches];
+  for (int d = 0; d < len; d += kWave * kLoads) {
+    int ev[kLoads];
 #pragma unroll
-    for (int j = 0; j < kBatches; ++j) {
-      const int f = base + 64 * nb * wave + 64 * j + lane;
-      ev[j] = j < nb && f < nk ? ids[f] : -1;
+    for (int j = 0; j < kLoads; ++j) {
+      const int o = d + kWave * j + lane;
+      ev[j] = o < len ? sid[o] : -1;
     }
-    int rank[kBatches];
 #pragma unroll
-    for (int j = 0; j < kBatches; ++j) {
-      if (j >= nb) break;
+    for (int j = 0; j < kLoads; ++j) {
+      if (d + kWave * j >= len) break;
+      const int o = d + kWave * j + lane;
       const int e = ev[j];
       const bool valid = e >= 0 && e < n_experts;
       uint64_t same = __ballot(valid);
@@ -166,44 +189,16 @@ __device__ void group_block(const int32_t* ids, int nk, int n_experts, int32_t* 
         same &= bit ? m : ~m;
       }
       const int r = __popcll(same & lanemask_lt(lane));
-      const int run = valid ? (int)sh.s_wave[wave][e] : 0;  // read by every lane first
-      rank[j] = run + r;
+      const int run = valid ? sh.s_base[wave][e] : 0;  // read by every lane first
       const bool last = valid && (same >> lane) == 1ull;
-      if (last) sh.s_wave[wave][e] = (uint16_t)(run + r + 1);
-    }
-    __syncthreads();
-    // per expert: wavefront counts -> offsets inside this round
-    for (int x = tid; x < n_experts; x += kGroupThreads) {
-      int run = 0;
-#pragma unroll
-      for (int w = 0; w < kGroupWaves; ++w) {
-        const int cnt = sh.s_wave[w][x];
-        sh.s_wave[w][x] = (uint16_t)run;
-        run += cnt;
-      }
-      sh.s_count[x] = run;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kBatches; ++j) {
-      if (j >= nb) break;
-      const int f = base + 64 * nb * wave + 64 * j + lane;
-      const int e = ev[j];
-      if (e >= 0 && e < n_experts) {
-        const int p = sh.s_next[e] + (int)sh.s_wave[wave][e] + rank[j];
-        perm[p] = f;
-        inv_perm[f] = p;
-      } else if (f < nk) {
-        inv_perm[f] = -1;
+      if (last) sh.s_base[wave][e] = run + r + 1;
+      if (valid) {
+        perm[run + r] = lo + o;
+        inv_perm[lo + o] = run + r;
+      } else if (o < len) {
+        inv_perm[lo + o] = -1;
       }
     }
-    __syncthreads();
-    for (int x = tid; x < n_experts; x += kGroupThreads) {
-      sh.s_next[x] += sh.s_count[x];
-#pragma unroll
-      for (int w = 0; w < kGroupWaves; ++w) sh.s_wave[w][x] = 0;
-    }
-    __syncthreads();
   }
   if (bad && dev_error) atomicOr(dev_error, MOE_DEVERR_EXPERT_ID);
 }

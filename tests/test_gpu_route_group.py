@@ -111,7 +111,8 @@ def test_group_workloads(name):
 
 
 @pytest.mark.parametrize("n,k,e,seed", [(3000, 8, 1000, 1), (129, 8, 1024, 2), (500, 1, 1, 3),
-                                        (1, 8, 8, 4), (2049, 3, 7, 5), (4096, 6, 256, 6)])
+                                        (1, 8, 8, 4), (2049, 3, 7, 5), (4096, 6, 256, 6),
+                                        (70001, 6, 256, 7)])
 def test_group_random(n, k, e, seed):
     print("case group random", n, k, e, flush=True)
     rng = np.random.default_rng(seed)
