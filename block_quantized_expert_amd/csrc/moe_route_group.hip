@@ -27,6 +27,10 @@ constexpr int kGroupWaves = kGroupThreads / kWave;
 // (four per wavefront)
 constexpr int kFusedMaxFlat = 4096;
 constexpr int kFusedMaxTokens = 4 * kGroupWaves;
+// flat indices scattered per grouping workgroup (at least), and the most
+// workgroups
+constexpr int kGroupChunk = 1024;
+constexpr int kGroupMaxBlocks = 64;
 
 // ---------------------------------------------------------------- routing
 
@@ -86,20 +90,28 @@ struct GroupShared {
   // s_base[w][e]: how many entries of wavefront w's segment go to expert e,
   // then the position of the next one
   int s_base[kGroupWaves][MOE_MAX_EXPERTS];
+  // entries of each expert before and after the workgroup's range
+  int s_pre[MOE_MAX_EXPERTS];
+  int s_post[MOE_MAX_EXPERTS];
   int s_wave_sum[kGroupWaves];
 };
 
-// The whole grouping by one 1024-thread workgroup.  `ids` may point at
-// global memory or LDS.
+// The grouping of the flat indices [blk_lo, blk_hi) of nk by one 1024-thread
+// workgroup.  `ids` may point at global memory or LDS.  Several workgroups
+// split the indices with no memory shared between them: each one counts
+// every index outside its range per expert itself (those before it and
+// those after it apart), so it knows where each expert's entries of its
+// range start.  Only the `writer` stores counts, offsets and the error flag.
 //
-// Wavefront w owns one contiguous segment of the flat indices (segments in
+// Inside the range, wavefront w owns one contiguous segment (segments in
 // ascending order, a multiple of 64 long).  It counts its segment per
 // expert; one scan over (expert, wavefront) gives each wavefront the first
 // position of each expert; then every wavefront scatters its segment in
 // ascending order, 64 indices at a time, with no further barrier.  The rank
 // of an index inside its batch of 64 is the number of earlier lanes holding
 // the same expert, from ballots of the expert's bits.
-__device__ void group_block(const int32_t* ids, int nk, int n_experts, int32_t* __restrict__ counts,
+__device__ void group_block(const int32_t* ids, int nk, int blk_lo, int blk_hi, bool writer,
+                            int n_experts, int32_t* __restrict__ counts,
                             int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
                             int32_t* __restrict__ inv_perm, int32_t* __restrict__ dev_error,
                             GroupShared& sh) {
@@ -110,20 +122,52 @@ __device__ void group_block(const int32_t* ids, int nk, int n_experts, int32_t* 
 
   for (int i = tid; i < kGroupWaves * MOE_MAX_EXPERTS; i += kGroupThreads)
     (&sh.s_base[0][0])[i] = 0;
-  const int64_t seg = ((int64_t)nk + kGroupThreads - 1) / kGroupThreads * kWave;
-  const int lo = (int)min<int64_t>((int64_t)wave * seg, nk);
-  const int len = (int)min<int64_t>((int64_t)wave * seg + seg, nk) - lo;
+  for (int e = tid; e < n_experts; e += kGroupThreads) {
+    sh.s_pre[e] = 0;
+    sh.s_post[e] = 0;
+  }
+  const int blen = blk_hi - blk_lo;
+  const int64_t seg = ((int64_t)blen + kGroupThreads - 1) / kGroupThreads * kWave;
+  const int lo = blk_lo + (int)min<int64_t>((int64_t)wave * seg, blen);
+  const int len = blk_lo + (int)min<int64_t>((int64_t)wave * seg + seg, blen) - lo;
   const int32_t* sid = ids + lo;
+  // the first kLoads batches of the wavefront's segment, loaded by the
+  // histogram and used again by the scatter
+  int keep[kLoads];
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) keep[j] = -1;
   __syncthreads();
 
-  // 1. per-wavefront histogram of its own segment
+  // 1. histograms: the indices outside the range (any thread takes any),
+  // then each wavefront's own segment
   int bad = 0;
+  const int n_out = nk - blen;
+  for (int d = 0; d < n_out; d += kGroupThreads * kLoads) {
+    int ev[kLoads];
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      const int g = d + kGroupThreads * j + tid;
+      ev[j] = g < n_out ? ids[g < blk_lo ? g : g + blen] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      const int g = d + kGroupThreads * j + tid;
+      if (g < n_out) {
+        const int e = ev[j];
+        if (e >= 0 && e < n_experts)
+          atomicAdd(g < blk_lo ? &sh.s_pre[e] : &sh.s_post[e], 1);
+        else
+          bad = 1;
+      }
+    }
+  }
   for (int d = 0; d < len; d += kWave * kLoads) {
     int ev[kLoads];
 #pragma unroll
     for (int j = 0; j < kLoads; ++j) {
       const int o = d + kWave * j + lane;
-      ev[j] = o < len ? sid[o] : 0;
+      ev[j] = o < len ? sid[o] : -1;
+      if (d == 0) keep[j] = ev[j];
     }
 #pragma unroll
     for (int j = 0; j < kLoads; ++j) {
@@ -138,9 +182,11 @@ __device__ void group_block(const int32_t* ids, int nk, int n_experts, int32_t* 
   }
   __syncthreads();
 
-  // 2. per expert (one per thread, n_experts <= 1024): its count, the prefix
-  // over wavefronts, then the exclusive scan over experts
+  // 2. per expert (one per thread, n_experts <= 1024): the prefix of its
+  // range count over wavefronts, its total, then the exclusive scan of the
+  // totals over experts
   int c = 0;
+  int pre = 0;
   if (tid < n_experts) {
 #pragma unroll
     for (int w = 0; w < kGroupWaves; ++w) {
@@ -148,6 +194,8 @@ __device__ void group_block(const int32_t* ids, int nk, int n_experts, int32_t* 
       sh.s_base[w][tid] = c;
       c += v;
     }
+    pre = sh.s_pre[tid];
+    c += pre + sh.s_post[tid];
   }
   int incl = wave_incl_scan(c);
   if (lane == kWave - 1) sh.s_wave_sum[wave] = incl;
@@ -157,11 +205,13 @@ __device__ void group_block(const int32_t* ids, int nk, int n_experts, int32_t* 
   incl += before;
   const int excl = incl - c;
   if (tid < n_experts) {
-    counts[tid] = c;
-    offsets[tid] = excl;
+    if (writer) {
+      counts[tid] = c;
+      offsets[tid] = excl;
+      if (tid == n_experts - 1) offsets[n_experts] = incl;
+    }
 #pragma unroll
-    for (int w = 0; w < kGroupWaves; ++w) sh.s_base[w][tid] += excl;
-    if (tid == n_experts - 1) offsets[n_experts] = incl;
+    for (int w = 0; w < kGroupWaves; ++w) sh.s_base[w][tid] += excl + pre;
   }
   __syncthreads();
 
@@ -174,7 +224,7 @@ __device__ void group_block(const int32_t* ids, int nk, int n_experts, int32_t* 
 #pragma unroll
     for (int j = 0; j < kLoads; ++j) {
       const int o = d + kWave * j + lane;
-      ev[j] = o < len ? sid[o] : -1;
+      ev[j] = d == 0 ? keep[j] : (o < len ? sid[o] : -1);
     }
 #pragma unroll
     for (int j = 0; j < kLoads; ++j) {
@@ -200,15 +250,18 @@ __device__ void group_block(const int32_t* ids, int nk, int n_experts, int32_t* 
       }
     }
   }
-  if (bad && dev_error) atomicOr(dev_error, MOE_DEVERR_EXPERT_ID);
+  if (bad && writer && dev_error) atomicOr(dev_error, MOE_DEVERR_EXPERT_ID);
 }
 
 __global__ __launch_bounds__(kGroupThreads) void group_kernel(
-    const int32_t* __restrict__ ids, int nk, int n_experts, int32_t* __restrict__ counts,
+    const int32_t* __restrict__ ids, int nk, int blk, int n_experts, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
     int32_t* __restrict__ dev_error) {
   __shared__ GroupShared sh;
-  group_block(ids, nk, n_experts, counts, offsets, perm, inv_perm, dev_error, sh);
+  const int lo = (int)min<int64_t>((int64_t)blockIdx.x * blk, nk);
+  const int hi = (int)min<int64_t>((int64_t)lo + blk, nk);
+  group_block(ids, nk, lo, hi, blockIdx.x == 0, n_experts, counts, offsets, perm, inv_perm,
+              dev_error, sh);
 }
 
 // Learned routing and grouping of a small batch by one workgroup: the
@@ -246,7 +299,8 @@ __global__ __launch_bounds__(kGroupThreads) void route_group_kernel(
     }
   }
   __syncthreads();
-  group_block(s_ids, n_tokens * top_k, n_experts, counts, offsets, perm, inv_perm, dev_error, sh);
+  const int nk = n_tokens * top_k;
+  group_block(s_ids, nk, 0, nk, true, n_experts, counts, offsets, perm, inv_perm, dev_error, sh);
 }
 
 // Route and group a batch of at most 64 flat entries with one wavefront:
@@ -350,8 +404,15 @@ hipError_t launch_route_hash(const int32_t* token_ids, int n_tokens, const int32
 hipError_t launch_group(const int32_t* ids, int n_tokens, int top_k, int n_experts,
                         int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
                         int32_t* dev_error, hipStream_t stream) {
-  group_kernel<<<1, kGroupThreads, 0, stream>>>(ids, n_tokens * top_k, n_experts, counts, offsets,
-                                                perm, inv_perm, dev_error);
+  // workgroups of at least kGroupChunk indices (a multiple of 1024), at most
+  // kGroupMaxBlocks of them: each one reads all nk ids once to count them
+  const int nk = n_tokens * top_k;
+  const int want = min(kGroupMaxBlocks, max(1, (nk + kGroupChunk - 1) / kGroupChunk));
+  const int blk = max(kGroupThreads,
+                      (nk + want * kGroupThreads - 1) / (want * kGroupThreads) * kGroupThreads);
+  const int blocks = max(1, (nk + blk - 1) / blk);
+  group_kernel<<<blocks, kGroupThreads, 0, stream>>>(ids, nk, blk, n_experts, counts, offsets,
+                                                     perm, inv_perm, dev_error);
   return hipGetLastError();
 }
 
