@@ -120,9 +120,9 @@ __device__ void group_block(const int32_t* ids, int nk, int blk_lo, int blk_hi, 
   const int wave = tid >> 6;
   constexpr int kLoads = 8;  // batches of 64 requested before the first is used
 
-  for (int i = tid; i < kGroupWaves * MOE_MAX_EXPERTS; i += kGroupThreads)
-    (&sh.s_base[0][0])[i] = 0;
   for (int e = tid; e < n_experts; e += kGroupThreads) {
+#pragma unroll
+    for (int w = 0; w < kGroupWaves; ++w) sh.s_base[w][e] = 0;
     sh.s_pre[e] = 0;
     sh.s_post[e] = 0;
   }
