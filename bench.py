@@ -3,26 +3,35 @@
 
 One step = route -> group -> gate/up (+SwiGLU) -> down (+combine) over one
 batch of synthetic input, every kernel launched through the C ABI of
-libmoe.so on one HIP stream.  Default workload: the DeepSeek-V4-Flash-shaped
-layer at single-token decode (hidden 4096, 256 routed experts + 1 shared,
-intermediate 2048, top-6, MXFP4 experts, bf16 activations).
+libmoe.so on one HIP stream.
 
-Cold caches: the weights live in --copies independent layer copies (3.44 GB
+The headline line is the largest workload that fits one GPU: the hash-routed
+prefill of 4096 tokens on the DeepSeek-V4-Flash-shaped layer (hidden 4096,
+256 routed MXFP4 experts + 1 fp8-e4m3 shared, intermediate 2048, top-6).
+Its K timed steps follow W warm-up steps.  The other workloads (tiny,
+single-token decode, batched decode of 32, prefill of 512) are measured in
+the same run, each with its own step count, and reported as nested records
+under "configs" (``--workload NAME`` measures only that one as the line).
+
+Cold caches: the weights live in several independent layer copies (3.44 GB
 each) used round-robin, and every step takes a fresh batch from a seeded
 pool, so no expert is served from the 256 MB last-level cache or the L2s.
 
-Prints ONE JSON line.  `value` is tokens/s over the K timed steps
-(wall clock, synchronised on both sides).  `roofline` is for the dominant
-kernel (gate/up): algorithmic bytes per launch over its average duration
-measured with HIP events on the launch stream inside the timed region (at
-one token the whole layer is one kernel, and that kernel is the one
-reported).  The
-kernels record those events from their own dispatch packets; recording them
-costs the host several microseconds per step, so at decode sizes (where the
-host would otherwise fall behind the GPU) only every --event-every-th timed
-step carries them.
-`cpu_baseline` times the fp64 oracle on a bounded sample of the same
-workload on the host cores.
+Every record holds:
+- ``value``: tokens/s over its timed steps (wall clock, synchronised on both
+  sides) and ``ms_per_step``;
+- ``step_stats``: the timed steps split into five consecutive repetitions,
+  each timed with stream events: median, min and max of the per-step time,
+  and ``spread_over_15pct`` when (max - min) / median > 0.15;
+- ``roofline``: the kernel that runs the routed experts' gate/up (at one
+  token, the single kernel that does the whole layer), its algorithmic bytes
+  or flops per launch over its average duration from HIP events that its own
+  dispatch records (on the stream it runs on);
+- ``cpu_baseline``: the fp64 oracle on a bounded sample of the same workload
+  on the host cores.
+The line also carries ``hbm_read_ceiling``: the rate of a plain streaming
+read over 4 GiB (moe_stream_read), the measured ceiling beside the 8 TB/s
+published figure.
 """
 
 from __future__ import annotations
@@ -41,29 +50,32 @@ if ROOT not in sys.path:
 METRIC = "MoE-FFN tokens/s + % HBM peak (decode) / % MFMA peak (prefill), 1 GPU"
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
+MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8, published
+HEADLINE = "hash4096"
+NESTED = ["tiny", "decode1", "decode32", "prefill512"]
+REPS = 5
 
-DEFAULTS = {  # workload: (steps, warmup, copies, pool, event_every)
+# workload: (steps, warmup, copies, pool, event_every) when it is measured as
+# a nested record or as the line without --steps/--warmup
+DEFAULTS = {
+    "tiny": (2000, 100, 1, 8, 8),
     "decode1": (2000, 100, 8, 64, 8),
     "decode32": (400, 20, 8, 16, 1),
-    "prefill512": (50, 5, 8, 4, 1),
-    "hash4096": (20, 3, 2, 2, 1),
-    "tiny": (2000, 100, 1, 8, 8),
+    "prefill512": (100, 10, 8, 4, 1),
+    "hash4096": (20, 5, 2, 2, 1),
 }
 
 # HBM traffic of the roofline kernel per launch, from two rocprofv3 --pmc
-# passes over this script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch,
-# averaged over the timed dispatches), each scaled by what the same counter
-# reads for a plain 256 MiB device copy run in the same process
+# passes over this script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch of
+# that kernel, averaged over the timed dispatches), each scaled by what the
+# same counter reads for a plain 256 MiB device copy run in the same process
 # (--copy-mib 256): FETCH_SIZE read 131083.5 KiB for 262144 KiB read,
-# WRITE_SIZE read 262144 KiB for 262144 KiB written.  Only workloads whose
-# roofline kernel is unchanged since the counters were taken are listed.
+# WRITE_SIZE 262144 KiB for 262144 KiB written.  Only kernels unchanged since
+# their counters were taken are listed.
 FETCH_SCALE = 262144.0 / 131083.5
 WRITE_SCALE = 1.0
-KERNEL_TRAFFIC_KIB = {  # workload: (FETCH_SIZE, WRITE_SIZE) per step of the roofline stage
-    "decode1": (46176.4, 82.2),           # decode_fused_kernel<8>
-    "decode32": (474862.2, 1669.1),       # quant_x_kernel + gemm_gate_up_kernel<0, 112, true, true>
-    "prefill512": (1184148.4, 27735.4),   # quant_x_kernel + gemm_gate_up_kernel<0, 112, true, true>
-    "hash4096": (2321829.8, 231717.5),    # quant_x_kernel + MXFP4 routed and fp8 shared gate/up
+KERNEL_TRAFFIC_KIB = {  # workload: (FETCH_SIZE, WRITE_SIZE) per dispatch
+    "decode1": (46176.4, 82.2),  # decode_fused_kernel<8>
 }
 
 
@@ -82,43 +94,47 @@ def proj_bytes(wtype: str, rows: int, cols: int) -> int:
 
 
 def workload_costs(wl, counts_list):
-    """Algorithmic bytes and flops of each launch, averaged over steps.
+    """Algorithmic bytes and flops, averaged over the steps' routings.
 
-    Gate/up launch: gate and up matrices of every routed expert with at
-    least one token, plus the shared expert, plus the activations read.
-    Down launch: the down matrices of the same experts plus y written.
-    Whole path adds router input and ids/weights.  Flops: 2*3*I*H per
-    (token, expert) pair including the shared expert.  Implementation
-    traffic (h, per-slot outputs, permutation) is not counted.
+    Routed gate/up kernel: the gate and up matrices of every routed expert
+    with at least one token (plus the shared expert when it is stored like
+    the routed ones: then it runs in the same kernel) and the activations.
+    Routed down kernel: the down matrices of the same experts and y.  Whole
+    path: every expert touched + shared + x + router input + ids/weights + y.
+    Flops: 2*2*I*H per (token, expert) for gate/up, 2*I*H for down, the
+    shared expert counted with weight 1.  Implementation traffic (h,
+    per-slot outputs, quantized activations, the permutation) is not counted.
     """
     h, i = wl.hidden, wl.inter
     si = wl.shared_inter or wl.inter
     act = 4 if wl.act == "f32" else 2
-    per_routed_gu = 2 * proj_bytes("mxfp4", i, h)
-    per_routed_dn = proj_bytes("mxfp4", h, i)
+    per_gu = 2 * proj_bytes(wl.routed, i, h)
+    per_dn = proj_bytes(wl.routed, h, i)
     sh_gu = 2 * proj_bytes(wl.shared, si, h)
     sh_dn = proj_bytes(wl.shared, h, si)
-    n = wl.n_tokens
-    gu, dn, path, flops = 0.0, 0.0, 0.0, 0.0
+    same = wl.shared == wl.routed
+    n, k = wl.n_tokens, wl.top_k
+    gu = dn = path = 0.0
     for counts in counts_list:
         d = int((counts > 0).sum())
-        g = d * per_routed_gu + sh_gu + n * h * act
-        dd = d * per_routed_dn + sh_dn + n * h * 4
-        route_in = n * wl.n_experts * 4 if wl.routing == "learned" else n * 4 + n * wl.top_k * 8
-        gu += g
-        dn += dd
-        path += g + dd + route_in + n * wl.top_k * 8
-        flops += 2.0 * (3 * i * h) * (n * wl.top_k) + 2.0 * (3 * si * h) * n
-    k = len(counts_list)
-    gu_flops = 2.0 * (2 * i * h) * (n * wl.top_k) + 2.0 * (2 * si * h) * n
-    return {"gate_up_bytes": gu / k, "down_bytes": dn / k, "path_bytes": path / k,
-            "path_flops": flops / k, "gate_up_flops": gu_flops,
-            "per_routed_gate_up_bytes": per_routed_gu, "shared_gate_up_bytes": sh_gu}
+        gu += d * per_gu + (sh_gu if same else 0) + n * h * act
+        dn += d * per_dn + (sh_dn if same else 0) + n * h * 4
+        route_in = n * wl.n_experts * 4 if wl.routing == "learned" else n * 4 + n * k * 8
+        path += (d * (per_gu + per_dn) + sh_gu + sh_dn + n * h * act + n * h * 4 + route_in
+                 + n * k * 8)
+    c = len(counts_list)
+    sh_tok = n if same else 0
+    return {
+        "gate_up_bytes": gu / c, "down_bytes": dn / c, "path_bytes": path / c,
+        "gate_up_flops": 4.0 * i * h * n * k + 4.0 * si * h * sh_tok,
+        "down_flops": 2.0 * i * h * n * k + 2.0 * si * h * sh_tok,
+        "path_flops": 6.0 * i * h * n * k + 6.0 * si * h * n,
+    }
 
 
 class Runner:
     """Pre-built ctypes arguments for every (layer copy, input) pair so a
-    step costs four direct library calls."""
+    step costs a few direct library calls."""
 
     def __init__(self, wl, layers, pool, dev):
         import torch
@@ -163,10 +179,9 @@ class Runner:
                     ("moe_group", self.group_args)])
         # single-token learned routing: the whole layer is one moe_forward call
         # (one fused kernel); its outputs land in one set of buffers
-        x_type_c = B.MOE_ACT_F32 if wl.act == "f32" else B.MOE_ACT_BF16
         self.fused = (wl.routing == "learned" and
                       self.L.moe_forward_single_kernel(ctypes.byref(layers[0].c), n,
-                                                       x_type_c) == 1)
+                                                       x_type) == 1)
         self.fwd_args = {}
         if self.fused:
             self.fwd = B.ForwardBuffers(layers[0], n, dev)
@@ -187,8 +202,9 @@ class Runner:
 
     def step(self, s, ev=None):
         """One pass of the path; ``ev`` = four events that the library
-        records from the kernel dispatches themselves: gate/up start and stop,
-        down start and stop, or (single fused kernel) its start and stop."""
+        records from the kernel dispatches themselves: routed gate/up kernel
+        start and stop, routed down kernel start and stop, or (single fused
+        kernel) its start and stop."""
         c = s % len(self.layers)
         r = s % len(self.pool)
         L = self.L
@@ -284,21 +300,214 @@ def cpu_baseline(wl, seconds_hint: float):
                       % (done, wl.name, rounds, wl.hidden, t_oracle)}
 
 
+def describe(wl, copies):
+    return ("%s: %d token(s), hidden %d, %d routed experts (%s) + 1 shared (%s), "
+            "intermediate %d, top-%d, %s routing, %s activations, %d cold layer copies"
+            % (wl.name, wl.n_tokens, wl.hidden, wl.n_experts, wl.routed, wl.shared, wl.inter,
+               wl.top_k, wl.routing, wl.act, copies))
+
+
+def step_stats(rep_ms, rep_steps):
+    import numpy as np
+
+    per = np.array(rep_ms) / np.array(rep_steps) * 1e3  # us per step in each repetition
+    med = float(np.median(per))
+    return {"reps": len(per), "steps_per_rep": list(rep_steps),
+            "us_per_step_median": med, "us_per_step_min": float(per.min()),
+            "us_per_step_max": float(per.max()),
+            "spread_over_15pct": bool((per.max() - per.min()) / med > 0.15)}
+
+
+def run_workload(name, steps, warmup, copies, n_pool, every, cpu_seconds, dev):
+    """Measure one workload; returns its record (without the top-level
+    contract keys)."""
+    import numpy as np
+    import torch
+
+    from block_quantized_expert_amd import binding as B
+    from block_quantized_expert_amd import inputs as I
+
+    wl = I.WORKLOADS[name]
+    t0 = time.perf_counter()
+    layers = [B.Layer(I.make_layer(wl, device=dev, copy=c), wl.top_k) for c in range(copies)]
+    pool = make_pool(wl, n_pool, dev)
+    runner = Runner(wl, layers, pool, dev)
+    torch.cuda.synchronize()
+    print("%s setup %.1f s: %d layer copies, %d inputs" % (name, time.perf_counter() - t0,
+                                                            copies, n_pool),
+          file=sys.stderr, flush=True)
+
+    for s in range(warmup):
+        runner.step(s)
+    torch.cuda.synchronize()
+
+    # events recorded by the kernels' own dispatches on every `every`-th step
+    sampled = list(range(0, steps, every))
+    evs = [tuple(B.HipEvent() for _ in range(4)) for _ in sampled]
+    ev_handles = [None] * steps
+    for i, j in enumerate(sampled):
+        ev_handles[j] = tuple(e.handle for e in evs[i])
+    # repetition boundaries: stream events between steps
+    reps = min(REPS, steps)
+    bounds = [round(r * steps / reps) for r in range(reps + 1)]
+    rep_ev = [torch.cuda.Event(enable_timing=True) for _ in bounds]
+    stream = runner.stream
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    b = 0
+    for j in range(steps):
+        if j == bounds[b]:
+            rep_ev[b].record(stream)
+            b += 1
+        runner.step(warmup + j, ev_handles[j])
+    rep_ev[b].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+
+    rep_ms = [rep_ev[r].elapsed_time(rep_ev[r + 1]) for r in range(reps)]
+    rep_steps = [bounds[r + 1] - bounds[r] for r in range(reps)]
+    gu_ms = [e[0].elapsed_ms(e[1]) for e in evs]
+    gu_avg_s = float(np.mean(gu_ms)) / 1e3
+    dn_avg_s = None if runner.fused else float(np.mean([e[2].elapsed_ms(e[3]) for e in evs])) / 1e3
+    counts_list = routed_counts(runner, n_pool)
+    used = [counts_list[(warmup + j) % n_pool] for j in range(steps)]
+    costs = workload_costs(wl, used)
+
+    ms_per_step = elapsed / steps * 1e3
+    if runner.fused:
+        kernel_name = "decode_fused_kernel<%d> (moe_forward: route + group + FFN)" % (wl.hidden // 512)
+        k_bytes, k_flops, issue = costs["path_bytes"], costs["path_flops"], 1.0
+    else:
+        kernel_name = "routed gate/up kernel of moe_ffn_forward (+ SwiGLU)"
+        k_bytes, k_flops = costs["gate_up_bytes"], costs["gate_up_flops"]
+        # bf16 x on the grouped GEMMs: each product issued once per E4M3 part
+        # of x (two) on the scaled fp8 instruction
+        issue = 2.0 if (wl.act == "bf16" and wl.n_tokens > 16) else 1.0
+    intensity = k_flops / k_bytes
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    mfma_bound = intensity > ridge
+    gbps = k_bytes / gu_avg_s / 1e9
+    tflops = k_flops / gu_avg_s / 1e12
+    roof = {
+        "kernel": kernel_name,
+        "bound": "mfma" if mfma_bound else "hbm",
+        "achieved": tflops if mfma_bound else gbps,
+        "peak": MFMA_BF16_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBPS,
+        "unit": "TFLOP/s" if mfma_bound else "GB/s",
+        "frac": tflops / MFMA_BF16_PEAK_TFLOPS if mfma_bound else gbps / HBM_PEAK_GBPS,
+        "traffic": kernel_traffic(name),
+        "bytes_per_launch": k_bytes,
+        "flops_per_launch": k_flops,
+        "flop_per_byte": intensity,
+        "avg_launch_us": gu_avg_s * 1e6,
+        "timed_launches": len(sampled),
+        "hbm_frac": gbps / HBM_PEAK_GBPS,
+        "mfma_bf16_frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+    }
+    if issue > 1.0:
+        roof["peak_note"] = ("bf16-equivalent: algorithmic flops against the dense bf16 peak; "
+                             "the kernel issues each product %d times (once per E4M3 part of x) "
+                             "on v_mfma_scale_f32_16x16x128_f8f6f4 at the fp8 rate" % issue)
+        roof["issued_flops_per_launch"] = issue * k_flops
+        roof["issued_frac_of_fp8_peak"] = issue * tflops / MFMA_FP8_PEAK_TFLOPS
+    rec = {
+        "workload": name,
+        "config": {"workload": describe(wl, copies), "n_tokens": wl.n_tokens},
+        "value": wl.n_tokens * steps / elapsed,
+        "unit": "tokens/s",
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": ms_per_step,
+        "step_stats": step_stats(rep_ms, rep_steps),
+        "roofline": roof,
+        "path": {
+            "bytes_per_step": costs["path_bytes"],
+            "achieved_GBps": costs["path_bytes"] / (elapsed / steps) / 1e9,
+            "hbm_frac": costs["path_bytes"] / (elapsed / steps) / 1e9 / HBM_PEAK_GBPS,
+            "flops_per_step": costs["path_flops"],
+            "achieved_TFLOPs": costs["path_flops"] / (elapsed / steps) / 1e12,
+            "mfma_bf16_frac": costs["path_flops"] / (elapsed / steps) / 1e12
+                              / MFMA_BF16_PEAK_TFLOPS,
+        },
+    }
+    if dn_avg_s is not None:
+        dissue = 3.0 if issue > 1.0 else 1.0  # h as three E4M3 parts
+        rec["down_kernel"] = {
+            "kernel": "routed down kernel of moe_ffn_forward",
+            "bytes_per_launch": costs["down_bytes"],
+            "flops_per_launch": costs["down_flops"],
+            "avg_launch_us": dn_avg_s * 1e6,
+            "achieved_GBps": costs["down_bytes"] / dn_avg_s / 1e9,
+            "achieved_TFLOPs": costs["down_flops"] / dn_avg_s / 1e12,
+            "mfma_bf16_frac": costs["down_flops"] / dn_avg_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "issued_frac_of_fp8_peak": dissue * costs["down_flops"] / dn_avg_s / 1e12
+                                       / MFMA_FP8_PEAK_TFLOPS,
+        }
+    st = rec["step_stats"]
+    print("%s: %d steps %.2f us/step (reps median %.2f, min %.2f, max %.2f), roofline kernel "
+          "%.2f us (%.0f GB/s, %.0f TFLOP/s)%s" % (
+              name, steps, ms_per_step * 1e3, st["us_per_step_median"], st["us_per_step_min"],
+              st["us_per_step_max"], gu_avg_s * 1e6, gbps, tflops,
+              "" if dn_avg_s is None else ", down %.2f us" % (dn_avg_s * 1e6)),
+          file=sys.stderr, flush=True)
+    del runner, layers, pool
+    torch.cuda.empty_cache()
+    if cpu_seconds > 0:
+        rec["cpu_baseline"] = cpu_baseline(wl, cpu_seconds)
+    return rec
+
+
+def read_ceiling(dev, gib=4, reps=5):
+    """GB/s of moe_stream_read over a cold buffer of `gib` GiB (median and
+    best of `reps` runs after one warm-up)."""
+    import numpy as np
+    import torch
+
+    from block_quantized_expert_amd import binding as B
+
+    n = gib << 30
+    buf = torch.empty(n, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    s = torch.cuda.current_stream()
+    L = B.lib()
+    args = (ctypes.c_void_p(buf.data_ptr()), n, ctypes.c_void_p(sink.data_ptr()),
+            ctypes.c_void_p(s.cuda_stream))
+    if L.moe_stream_read(*args):
+        raise RuntimeError("moe_stream_read failed")
+    rates = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(s)
+        L.moe_stream_read(*args)
+        b.record(s)
+        torch.cuda.synchronize()
+        rates.append(n / (a.elapsed_time(b) / 1e3) / 1e9)
+    del buf
+    torch.cuda.empty_cache()
+    return {"kernel": "moe_stream_read (16 B per lane and load, 4 loads in flight per lane)",
+            "bytes": n, "GBps_median": float(np.median(rates)), "GBps_max": float(max(rates)),
+            "frac_of_published": float(np.median(rates)) / HBM_PEAK_GBPS}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="decode1")
+    ap.add_argument("--workload", default=None,
+                    help="measure only this workload (default: %s as the line, the others "
+                         "as nested records)" % HEADLINE)
     ap.add_argument("--copies", type=int, default=None)
     ap.add_argument("--pool", type=int, default=None)
     ap.add_argument("--event-every", type=int, default=None,
                     help="record the per-kernel events on every n-th timed step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before the warm-up, copy this many MiB once with a plain device "
                          "copy kernel (a known byte count for calibrating memory counters)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--nested-cpu-seconds", type=float, default=4.0)
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -308,35 +517,16 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     from block_quantized_expert_amd import build as _build
 
     if not os.path.exists(_build.LIB):
         _build.build()
-    from block_quantized_expert_amd import binding as B
-    from block_quantized_expert_amd import inputs as I
-
-    wl = I.WORKLOADS[args.workload]
-    d_steps, d_warm, d_copies, d_pool, d_every = DEFAULTS[wl.name]
-    steps = args.steps if args.steps is not None else d_steps
-    warmup = args.warmup if args.warmup is not None else d_warm
-    copies = args.copies if args.copies is not None else d_copies
-    n_pool = args.pool if args.pool is not None else d_pool
-    every = max(1, args.event_every if args.event_every is not None else d_every)
 
     dev = torch.device("cuda:0")
-    t0 = time.perf_counter()
-    layers = [B.Layer(I.make_layer(wl, device=dev, copy=c), wl.top_k) for c in range(copies)]
-    pool = make_pool(wl, n_pool, dev)
-    runner = Runner(wl, layers, pool, dev)
-    torch.cuda.synchronize()
-    print("setup %.1f s: %d layer copies, %d inputs" % (time.perf_counter() - t0, copies, n_pool),
-          file=sys.stderr, flush=True)
-
     if args.copy_mib > 0:
-        # one read and one write of exactly copy_mib MiB, outside the timed region
+        # one read and one write of exactly copy_mib MiB, outside the timed regions
         n = args.copy_mib << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -344,111 +534,54 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    for s in range(warmup):
-        runner.step(s)
-    torch.cuda.synchronize()
 
-    sampled = list(range(0, steps, every))
-    evs = [tuple(B.HipEvent() for _ in range(4)) for _ in sampled]
-    ev_handles = [None] * steps
-    for i, j in enumerate(sampled):
-        ev_handles[j] = tuple(e.handle for e in evs[i])
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for j in range(steps):
-        runner.step(warmup + j, ev_handles[j])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
+    line_name = args.workload or HEADLINE
+    nested = [] if args.workload else NESTED
+    cpu = not args.no_cpu_baseline
+    configs = {}
+    for name in nested:
+        st, wu, cp, po, ev = DEFAULTS[name]
+        configs[name] = run_workload(name, st, wu, cp, po, ev,
+                                     args.nested_cpu_seconds if cpu else 0.0, dev)
+    st, wu, cp, po, ev = DEFAULTS[line_name]
+    steps = args.steps if args.steps is not None else st
+    warmup = args.warmup if args.warmup is not None else wu
+    rec = run_workload(line_name, steps, warmup,
+                       args.copies if args.copies is not None else cp,
+                       args.pool if args.pool is not None else po,
+                       max(1, args.event_every if args.event_every is not None else ev),
+                       args.cpu_seconds if cpu else 0.0, dev)
 
-    gate_up_ms = [e[0].elapsed_ms(e[1]) for e in evs]
-    gu_avg_s = float(np.mean(gate_up_ms)) / 1e3
-    dn_avg_s = float("nan") if runner.fused else float(np.mean(
-        [e[2].elapsed_ms(e[3]) for e in evs])) / 1e3
-    counts_list = routed_counts(runner, n_pool)
-    used = [counts_list[(warmup + j) % n_pool] for j in range(steps)]
-    costs = workload_costs(wl, used)
-
-    ms_per_step = elapsed / steps * 1e3
-    tokens_per_s = wl.n_tokens * steps / elapsed
-    if runner.fused:
-        # one kernel does the whole layer: its roof is HBM for all the
-        # layer's bytes
-        kernel_name = "decode_fused_kernel (moe_forward: route + group + FFN)"
-        k_bytes, k_flops = costs["path_bytes"], costs["path_flops"]
-    else:
-        kernel_name = "gate/up + SwiGLU stage (moe_ffn_gate_up)"
-        k_bytes, k_flops = costs["gate_up_bytes"], costs["gate_up_flops"]
-    # HBM below the ridge point, the bf16 MFMA peak above it (the
-    # contractions run in bf16)
-    intensity = k_flops / k_bytes
-    mfma_bound = intensity > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
-    achieved = k_bytes / gu_avg_s / 1e9
-    gu_tflops = k_flops / gu_avg_s / 1e12
-    path_gbps = costs["path_bytes"] / (elapsed / steps) / 1e9
-    path_tflops = costs["path_flops"] / (elapsed / steps) / 1e12
-    traffic = kernel_traffic(wl.name)
     result = {
         "metric": METRIC,
-        "value": tokens_per_s,
+        "value": rec["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": steps,
         "warmup": warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": rec["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "mxfp4",
+        "compute": "E2M1 expert weights with UE8M0 block scales on the matrix cores "
+                   "(batched: with exact E4M3 parts of the bf16 activations on "
+                   "v_mfma_scale_f32_16x16x128_f8f6f4; one token: decoded exactly to bf16); "
+                   "fp32 accumulation",
         "data": "synthetic",
-        "config": {
-            "workload": "%s: %d token(s), hidden %d, %d routed experts + %s shared, "
-                        "intermediate %d, top-%d, %s routing, MXFP4 routed experts, %s "
-                        "activations, %d cold layer copies"
-                        % (wl.name, wl.n_tokens, wl.hidden, wl.n_experts,
-                           "1 " + wl.shared, wl.inter, wl.top_k, wl.routing, wl.act, copies),
-            "n_tokens": wl.n_tokens,
-        },
-        "roofline": {
-            "kernel": kernel_name,
-            "bound": "mfma" if mfma_bound else "hbm",
-            "achieved": gu_tflops if mfma_bound else achieved,
-            "peak": MFMA_BF16_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBPS,
-            "unit": "TFLOP/s" if mfma_bound else "GB/s",
-            "frac": gu_tflops / MFMA_BF16_PEAK_TFLOPS if mfma_bound else achieved / HBM_PEAK_GBPS,
-            "traffic": traffic,
-            "bytes_per_launch": k_bytes,
-            "flops_per_launch": k_flops,
-            "flop_per_byte": intensity,
-            "avg_launch_us": gu_avg_s * 1e6,
-            "timed_launches": len(sampled),
-        },
-        "down_kernel": None if runner.fused else {
-            "bytes_per_launch": costs["down_bytes"],
-            "avg_launch_us": dn_avg_s * 1e6,
-            "achieved_GBps": costs["down_bytes"] / dn_avg_s / 1e9,
-        },
-        "path": {
-            "bytes_per_step": costs["path_bytes"],
-            "achieved_GBps": path_gbps,
-            "hbm_frac": path_gbps / HBM_PEAK_GBPS,
-            "flops_per_step": costs["path_flops"],
-            "achieved_TFLOPs": path_tflops,
-            "mfma_bf16_frac": path_tflops / MFMA_BF16_PEAK_TFLOPS,
-        },
+        "config": rec["config"],
+        "step_stats": rec["step_stats"],
+        "roofline": rec["roofline"],
+        "path": rec["path"],
     }
-    if runner.fused:
-        print("timed %d steps in %.3f s: %.2f us/step, fused kernel %.2f us (%.0f GB/s), "
-              "path %.0f GB/s" % (steps, elapsed, ms_per_step * 1e3, gu_avg_s * 1e6, achieved,
-                                  path_gbps), file=sys.stderr, flush=True)
-    else:
-        print("timed %d steps in %.3f s: %.2f us/step, gate/up %.2f us (%.0f GB/s), down %.2f us "
-              "(%.0f GB/s), path %.0f GB/s"
-              % (steps, elapsed, ms_per_step * 1e3, gu_avg_s * 1e6, achieved, dn_avg_s * 1e6,
-                 costs["down_bytes"] / dn_avg_s / 1e9, path_gbps), file=sys.stderr, flush=True)
-    del runner, layers, pool
-    torch.cuda.empty_cache()
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    if "down_kernel" in rec:
+        result["down_kernel"] = rec["down_kernel"]
+    if "cpu_baseline" in rec:
+        result["cpu_baseline"] = rec["cpu_baseline"]
+    if not args.no_ceiling:
+        result["hbm_read_ceiling"] = read_ceiling(dev)
+    if configs:
+        result["configs"] = configs
     print(json.dumps(result), flush=True)
 
 

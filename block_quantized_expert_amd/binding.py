@@ -21,12 +21,12 @@ MOE_W_MXFP4, MOE_W_FP8E4M3_B128 = 0, 1
 MOE_DEVERR_EXPERT_ID, MOE_DEVERR_TOKEN_ID, MOE_DEVERR_SYNC = 1, 2, 4
 MOE_FORWARD_SYNC_BYTES = 8192
 
-# every symbol include/moe.h declares
+# every symbol include/*.h declare
 EXPORTED = ["moe_route", "moe_route_hash", "moe_route_group", "moe_group_workspace_bytes",
             "moe_group", "moe_ffn_workspace_bytes", "moe_ffn_forward", "moe_ffn_gate_up",
             "moe_ffn_down", "moe_ffn_forward_timed", "moe_forward_workspace_bytes",
             "moe_forward_single_kernel", "moe_forward_workspace_init", "moe_forward",
-            "moe_forward_timed", "moe_status_string"]
+            "moe_forward_timed", "moe_status_string", "moe_stream_read"]
 
 WEIGHT_TYPES = {"mxfp4": MOE_W_MXFP4, "fp8_e4m3_b128": MOE_W_FP8E4M3_B128}
 
@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
         L.moe_forward_timed.argtypes = fwd + [P, P]
         for name in ("moe_forward_workspace_init", "moe_forward", "moe_forward_timed"):
             getattr(L, name).restype = ctypes.c_int
+        L.moe_stream_read.argtypes = [P, S, P, P]
+        L.moe_stream_read.restype = ctypes.c_int
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -324,7 +326,7 @@ class ForwardBuffers:
     """Outputs and workspace of moe_forward for a batch of n tokens; the
     workspace's synchronisation words are zeroed once here."""
 
-    def __init__(self, layer: Layer, n_tokens: int, device, stream=None):
+    def __init__(self, layer: Layer, n_tokens: int, device, stream=None, workspace=True):
         n, k, e = n_tokens, layer.top_k, layer.c.n_experts
         self.n = n
         self.ids = torch.empty((n, k), dtype=torch.int32, device=device)
@@ -334,17 +336,20 @@ class ForwardBuffers:
                          torch.empty(max(n * k, 1), dtype=torch.int32, device=device),
                          torch.empty(max(n * k, 1), dtype=torch.int32, device=device))
         self.y = torch.empty((n, layer.hidden), dtype=torch.float32, device=device)
-        nbytes = max(layer.forward_workspace_bytes(n), MOE_FORWARD_SYNC_BYTES)
-        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
         self.dev_error = torch.zeros(1, dtype=torch.int32, device=device)
-        _check(lib().moe_forward_workspace_init(_ptr(self.workspace), nbytes, _stream(stream)),
-               "moe_forward_workspace_init")
+        self.workspace = None
+        if workspace:
+            nbytes = max(layer.forward_workspace_bytes(n), MOE_FORWARD_SYNC_BYTES)
+            self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+            _check(lib().moe_forward_workspace_init(_ptr(self.workspace), nbytes,
+                                                    _stream(stream)),
+                   "moe_forward_workspace_init")
 
     def args(self):
         counts, offsets, perm, inv_perm = self.grouping
         return [_ptr(self.ids), _ptr(self.w), _ptr(counts), _ptr(offsets), _ptr(perm),
-                _ptr(inv_perm), _ptr(self.y), _ptr(self.workspace), self.workspace.numel(),
-                _ptr(self.dev_error)]
+                _ptr(inv_perm), _ptr(self.y), _ptr(self.workspace),
+                0 if self.workspace is None else self.workspace.numel(), _ptr(self.dev_error)]
 
 
 def moe_forward(layer: Layer, logits, x, routed_scale=1.5, buffers: ForwardBuffers = None,
@@ -364,3 +369,4 @@ def moe_forward(layer: Layer, logits, x, routed_scale=1.5, buffers: ForwardBuffe
         _check(lib().moe_forward_timed(*common, *buffers.args(), _stream(stream), *evs),
                "moe_forward_timed")
     return buffers
+

@@ -2,6 +2,8 @@
 // validate on the host, then enqueue the kernels on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <stdlib.h>
+
 #include <atomic>
 #include <chrono>
 #include <random>
@@ -13,6 +15,10 @@
 namespace {
 
 moe_status launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE; }
+
+// Polls of the single-token kernel's grid-barrier flags before it gives up
+// (about a second).
+constexpr uint32_t kFusedSpinLimit = 1u << 20;
 
 moe::FfnParams make_params(const moe_layer* L, const void* x, int x_type, int n_tokens,
                            const float* topk_w, const int32_t* counts, const int32_t* offsets,
@@ -136,6 +142,16 @@ moe_status forward_impl(const moe_layer* layer, const float* logits, float route
     f.inv_perm = inv_perm;
     f.sync = reinterpret_cast<moe::FusedSync*>(ws);
     f.epoch = next_epoch();
+    f.wait_epoch = f.epoch;
+    f.spin_limit = kFusedSpinLimit;
+    // test hook: MOE_TEST_FUSED_GIVE_UP=<polls> makes the grid barrier wait
+    // for a value no workgroup posts and give up after that many polls, so
+    // the timeout path runs with every workgroup still exiting normally
+    if (const char* v = getenv("MOE_TEST_FUSED_GIVE_UP")) {
+      f.wait_epoch = f.epoch ^ 0x8000000000000000ull;
+      if (f.wait_epoch == 0) f.wait_epoch = 0x4000000000000000ull;
+      f.spin_limit = (uint32_t)strtoul(v, nullptr, 10);
+    }
     f.dev_error = dev_error;
     return launched(moe::launch_decode_fused(f, stream, start, stop));
   }

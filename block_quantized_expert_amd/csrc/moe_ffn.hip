@@ -1049,11 +1049,11 @@ hipError_t launch_ffn_down(const FfnParams& p, hipStream_t stream, hipEvent_t st
                                                                       stop);
   }
   // weighted per-slot outputs, then each token's sum in a fixed order
-  hipError_t e = launch_gemm_down(p, stream, start, nullptr);
+  hipError_t e = launch_gemm_down(p, stream, start, stop);
   if (e != hipSuccess) return e;
   const int64_t n = (int64_t)p.n_tokens * (p.hidden / 4);
   return launch(combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, nullptr,
-                stop, p);
+                nullptr, p);
 }
 
 }  // namespace moe

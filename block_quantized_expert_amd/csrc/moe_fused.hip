@@ -36,8 +36,9 @@
 //  3. the grid barrier (epoch flags, see arrive / wait_release); the down
 //     codes of the workgroup's first row block are requested between its
 //     arrival and its wait, so they arrive during the wait.  Every wait is
-//     bounded: on timeout the kernel reports MOE_DEVERR_SYNC and skips the
-//     rest, so every wavefront always exits.
+//     bounded: on timeout the workgroup reports MOE_DEVERR_SYNC, writes NaN
+//     into its rows of y and skips the rest, so every wavefront always
+//     exits and an incomplete y cannot pass for a result.
 //  4. down: a workgroup takes 16 hidden rows over the whole intermediate
 //     dimension; wavefront w takes the 128-wide steps w, w + 16, ... for
 //     every segment, with its slice of w_a * h staged in its own LDS rows.
@@ -64,7 +65,6 @@ constexpr int kMaxHidden = 4096;               // x staged whole in LDS
 constexpr int kMaxInter = 4096;                // down scales of a row block staged in LDS
 constexpr int kDScale = 16 * (kMaxInter / 32);  // their bytes per segment
 constexpr int kHRow = 136;                      // bf16 per staged h row (128 + 8)
-constexpr uint32_t kSpinLimit = 1u << 20;       // polls of a flag (about a second)
 
 struct FusedSmem {
   int ids[MOE_MAX_TOP_K];   // routed experts in rank order
@@ -133,7 +133,7 @@ __device__ void arrive(const FusedParams& f) {
 
 __device__ bool wait_release(const FusedParams& f, FusedSmem& sm) {
   if (threadIdx.x < kWave) {
-    const unsigned long long ep = f.epoch;
+    const unsigned long long ep = f.wait_epoch;
     const int lane = threadIdx.x;
     uint32_t spins = 0;
     int ok = 1;
@@ -149,7 +149,7 @@ __device__ bool wait_release(const FusedParams& f, FusedSmem& sm) {
       }
       if (__ballot(!mine) == 0) break;
       __builtin_amdgcn_s_sleep(2);
-      if (++spins > kSpinLimit) {
+      if (++spins > f.spin_limit) {
         ok = 0;
         break;
       }
@@ -440,7 +440,12 @@ __global__ __launch_bounds__(kFThreads) void decode_fused_kernel(FusedParams f) 
   arrive(f);
   if (pre) load_down(blockIdx.x, wave);
   if (!wait_release(f, sm)) {
+    // some workgroup never arrived (the grid was not all resident): this
+    // workgroup's rows of y are not computed; NaN there makes the failure
+    // visible in y itself, whether or not the caller passed dev_error
     if (threadIdx.x == 0 && f.dev_error) atomicOr(f.dev_error, MOE_DEVERR_SYNC);
+    for (int rb = blockIdx.x; rb < n_rb; rb += G)
+      if (threadIdx.x < 16) p.y[rb * 16 + threadIdx.x] = __builtin_nanf("");
     return;
   }
 

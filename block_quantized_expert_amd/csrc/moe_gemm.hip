@@ -1284,15 +1284,16 @@ hipError_t down_range(const FfnParams& p, int seg_lo, int seg_hi, hipStream_t st
 
 // Segments of one weight type go through one launch: everything at once when
 // the shared expert is stored like the routed ones, else the routed experts
-// and then the shared expert.
+// and then the shared expert.  start/stop go to the launch that holds the
+// routed experts.
 template <typename Range>
 hipError_t by_type(const FfnParams& p, hipStream_t stream, hipEvent_t start, hipEvent_t stop,
                    Range run) {
   const int E = p.n_experts;
   if (!p.has_shared || p.sw_type == p.w_type) return run(p.w_type, 0, E + p.has_shared, start, stop);
-  const hipError_t e = run(p.w_type, 0, E, start, nullptr);
+  const hipError_t e = run(p.w_type, 0, E, start, stop);
   if (e != hipSuccess) return e;
-  return run(p.sw_type, E, E + 1, nullptr, stop);
+  return run(p.sw_type, E, E + 1, nullptr, nullptr);
 }
 
 }  // namespace
@@ -1306,13 +1307,13 @@ hipError_t launch_gemm_gate_up(const FfnParams& p, hipStream_t stream, hipEvent_
   const bool sc = p.hidden <= 4096 && p.hidden % 512 == 0;
   const int64_t blocks = (int64_t)p.n_tokens * (p.hidden / 32);
   const hipError_t e = launch(quant_x_kernel, dim3((unsigned)((blocks + 255) / 256)), dim3(256),
-                              0, stream, start, nullptr, p);
+                              0, stream, nullptr, nullptr, p);
   if (e != hipSuccess) return e;
   // 32-bit offsets into the quantized activations (below 2 GiB: batches up
   // to 262144 tokens at H 4096); the larger ones take 64-bit addresses and
   // no LDS scales
   const bool o32 = (int64_t)p.n_tokens * 2 * p.hidden < ((int64_t)1 << 31);
-  return by_type(p, stream, nullptr, stop, [&](int wt, int lo, int hi, hipEvent_t a, hipEvent_t b) {
+  return by_type(p, stream, start, stop, [&](int wt, int lo, int hi, hipEvent_t a, hipEvent_t b) {
     if (wt != MOE_W_MXFP4) {
       if (!o32) return gate_up_range<MOE_W_FP8E4M3_B128, 64, false, false>(p, lo, hi, stream, a, b);
       return p.hidden % 512 == 0

@@ -67,7 +67,10 @@ struct FusedParams {
   int32_t* perm;
   int32_t* inv_perm;
   FusedSync* sync;
-  unsigned long long epoch;       // unique per call, never 0
+  unsigned long long epoch;       // unique per call, never 0: posted on arrival
+  unsigned long long wait_epoch;  // the value waited for: epoch (a test may ask for
+                                  // one no workgroup posts, to exercise the give-up)
+  uint32_t spin_limit;            // polls of the flags before giving up
   int32_t* dev_error;             // nullable
   int grid;                       // set by the launcher
 };

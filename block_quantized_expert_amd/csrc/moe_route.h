@@ -35,10 +35,14 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 
 // A float as an unsigned key with the same order (larger value, larger
 // key); -0 is first made +0, so the two compare equal as they do as floats.
+// Every key is at least 1: 0 marks padding lanes and experts already chosen,
+// which must stay below every live key (only the negative NaN with all
+// mantissa bits set would map to 0; it shares 1 with its neighbour NaN).
 __device__ __forceinline__ uint32_t order_key(float v) {
   uint32_t b = __float_as_uint(v);
   if (b == 0x80000000u) b = 0u;
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  const uint32_t k = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return k > 1u ? k : 1u;
 }
 
 __device__ __forceinline__ float key_value(uint32_t k) {

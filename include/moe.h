@@ -82,7 +82,7 @@ typedef enum { MOE_W_MXFP4 = 0, MOE_W_FP8E4M3_B128 = 1 } moe_weight_type;
 #define MOE_DEVERR_EXPERT_ID 1 /* an expert id outside [0, n_experts)  */
 #define MOE_DEVERR_TOKEN_ID 2  /* a token id outside [0, vocab)        */
 #define MOE_DEVERR_SYNC 4      /* moe_forward: a wait of the single-token kernel timed
-                                  out (y incomplete)                    */
+                                  out (the rows of y it owned are NaN)  */
 
 /* Limits of the library. */
 #define MOE_MAX_EXPERTS 1024
@@ -113,7 +113,8 @@ typedef struct {
  *   logits     fp32 [n_tokens][n_experts], row-major, finite.
  *   topk_ids   out int32 [n_tokens][top_k]: the top_k largest logits of the
  *              token, slot 0 the largest, ties to the lower expert index
- *              (-0 equals +0).
+ *              (-0 equals +0).  The ids of a token are always distinct
+ *              (non-finite logits give unspecified but distinct ids).
  *   topk_w     out fp32 [n_tokens][top_k]: s_i = sqrt(softplus(logit_i)),
  *              w_i = routed_scale * s_i / sum_j s_j (evaluated in fp64,
  *              rounded to fp32 once).
@@ -186,9 +187,25 @@ size_t moe_ffn_workspace_bytes(const moe_layer* layer, int n_tokens);
  *   topk_w   fp32 [n_tokens][top_k] as made by a router.
  *   counts, offsets, perm, inv_perm   as made by moe_group for the same ids.
  *   y        out fp32 [n_tokens][hidden], fully overwritten.
- *   Weights are decoded exactly to bfloat16 and multiplied on the matrix
- *   cores with fp32 accumulation; the SwiGLU output (and fp32 x) enter the
- *   matrix cores as a bf16 high + bf16 low pair.  The combine sums each
+ *   The slots' experts come from counts/offsets/perm/inv_perm; the ids
+ *   themselves are not read.
+ * Numerics (all products accumulate in fp32 on the matrix cores):
+ *   - bf16 x with more than 16 tokens, a hidden size the small-batch
+ *     kernel does not cover, or an fp8 expert (routed or shared): the
+ *     grouped GEMMs.  Weight codes and scale bytes go undecoded into the scaled
+ *     matrix instruction; x is first rewritten as two E4M3 parts under one
+ *     power-of-two scale per 32 inputs (hi + lo sum back to the bf16 value
+ *     exactly for inputs within 2^-13 of their block's largest magnitude;
+ *     smaller ones keep their bits above 2^-17 of that magnitude); the
+ *     SwiGLU output h is stored as three E4M3 parts per 32 values (h to
+ *     2^-12 of its magnitude) for the down projection.
+ *   - bf16 x with MXFP4 experts and up to 16 tokens: weights decoded
+ *     exactly to bf16 in registers, x as given, h as a bf16 high + low pair
+ *     (16 significant bits).
+ *   - fp32 x: weights decoded exactly to bf16, x and h as bf16 high + low
+ *     pairs.
+ *   Either way the error stays far inside max|err| <= 2e-3 * rms(y) of the
+ *   exact result for inputs like the pages' workloads.  The combine sums each
  *   token's terms in a fixed order (shared first, then slot 0..top_k-1), so
  *   y is deterministic.
  */
@@ -215,10 +232,14 @@ moe_status moe_ffn_down(const moe_layer* layer, const void* x, int x_type, int n
 
 /*
  * moe_ffn_forward that also records, into caller-created events (each may
- * be NULL), the start and end of the gate/up kernel and of the down kernel.
- * The times come from the kernels' own dispatches, so no extra packets are
- * queued and the stream runs as it would untimed.  For benchmarks and
- * profilers: hipEventElapsedTime(start, stop) is the kernel's duration.
+ * be NULL), the start and end of the kernel that runs the routed experts'
+ * gate/up and of the kernel that runs their down projection (the shared
+ * expert is in the same kernel when it has the routed experts' weight type;
+ * the activation quantization of batched calls, a shared expert of another
+ * type and the combine pass run outside the timed pairs).  The times come
+ * from the kernels' own dispatches, so no extra packets are queued and the
+ * stream runs as it would untimed.  For benchmarks and profilers:
+ * hipEventElapsedTime(start, stop) is the kernel's duration.
  */
 moe_status moe_ffn_forward_timed(const moe_layer* layer, const void* x, int x_type,
                                  int n_tokens, const float* topk_w, const int32_t* counts,
@@ -244,15 +265,23 @@ moe_status moe_ffn_forward_timed(const moe_layer* layer, const void* x, int x_ty
  *                 moe_forward_workspace_init before the first call.  Calls
  *                 that share a workspace must not overlap in time.
  *   dev_error     nullable; MOE_DEVERR_SYNC is set if a wait of the
- *                 single-token kernel times out (y is then incomplete).
+ *                 single-token kernel times out.
  * Single-token calls with bf16 activations, MXFP4 routed experts (and an
  * MXFP4 shared expert of the same width), n_experts <= 256, hidden in
  * {512, 1024, 2048, 4096} and inter a multiple of 128 up to 4096 run as one kernel
  * when the GPU holds at least hidden/16 of its workgroups at once (256 on
- * MI355X); that kernel's grid is exactly the workgroups the GPU holds (it waits for
- * all of them at a grid barrier, so nothing else may keep the GPU full
- * indefinitely meanwhile); every other call runs the route+group kernel and
- * the FFN kernels of moe_ffn_forward.
+ * MI355X); every other call runs the route+group kernel and the FFN kernels
+ * of moe_ffn_forward.
+ * Co-residency: the single kernel's grid is the number of its workgroups the
+ * occupancy query says fit on the GPU at once (one per compute unit), and
+ * its workgroups meet at a grid barrier, so it needs all of them resident
+ * together.  Kernels of other streams or processes that hold compute units
+ * (or their LDS) for the whole call, a GPU partitioned below its full count
+ * of compute units, or a debugger that serialises workgroups break that.
+ * The barrier's wait is bounded (about a second of polling): a workgroup
+ * that gives up sets MOE_DEVERR_SYNC in *dev_error and writes NaN into the
+ * rows of y it owns, so an incomplete y never looks like a result even when
+ * dev_error is NULL.
  */
 #define MOE_FORWARD_SYNC_BYTES 8192
 /* 1 if moe_forward runs as the single fused kernel for this layer, batch

@@ -310,16 +310,3 @@ def ffn(layer: dict, x: np.ndarray, act_type: str, ids: np.ndarray,
         y += expert_ffn(xs, wg, wu, wd)
     return y.astype(np.float32)
 
-
-def moe_layer_forward(layer: dict, x: np.ndarray, act_type: str, routing: dict,
-                      top_k: int, routed_scale: float = 1.5, tokens=None,
-                      out_rows=None, with_shared: bool = True):
-    """Whole path: route (learned or hash), then the FFN and combine."""
-    if routing["kind"] == "learned":
-        ids, w = route_topk(routing["logits"], top_k, routed_scale)
-    elif routing["kind"] == "hash":
-        ids, w = route_hash(routing["token_ids"], routing["tid2eid"], routing["tid2w"])
-    else:
-        raise ValueError("unknown routing kind")
-    y = ffn(layer, x, act_type, ids, w, tokens, out_rows, with_shared)
-    return ids, w, y

@@ -60,3 +60,52 @@ def assert_y_close(y: np.ndarray, ref: np.ndarray, tol: float = Y_TOL):
 def assert_w_close(w_gpu: np.ndarray, w_ref: np.ndarray):
     """Both sides round an fp64 value to fp32 once: at most one ulp apart."""
     assert np.all(np.abs(w_gpu - w_ref) <= np.spacing(np.abs(w_ref).astype(np.float32)))
+
+
+def host_layer(weights: dict, experts) -> dict:
+    """The listed routed experts (and the shared expert) of a device layer
+    made by ``inputs.make_layer``, copied to host NumPy for the oracle.  The
+    bytes are the generator's, as on the GPU; copying them is faster than
+    drawing them again on the CPU for layers with many experts."""
+    out = {"hidden": weights["hidden"], "inter": weights["inter"],
+           "n_experts": weights["n_experts"]}
+    for proj in ("gate", "up", "down"):
+        p = weights[proj]
+        out[proj] = {"type": p["type"],
+                     "codes": {int(e): p["codes"][int(e)].cpu().numpy() for e in experts},
+                     "scales": {int(e): p["scales"][int(e)].cpu().numpy() for e in experts}}
+    sh = weights.get("shared")
+    if sh is None:
+        out["shared"] = None
+    else:
+        out["shared"] = {"inter": sh["inter"]}
+        for proj in ("gate", "up", "down"):
+            out["shared"][proj] = {"type": sh[proj]["type"], "codes": sh[proj]["codes"].cpu().numpy(),
+                                   "scales": sh[proj]["scales"].cpu().numpy()}
+    return out
+
+
+def oracle_y_host(weights: dict, act: str, x: torch.Tensor, ids, w, tokens=None, rows=None,
+                  with_shared=True):
+    """oracle_y with the weights copied from the device layer."""
+    tok = range(ids.shape[0]) if tokens is None else tokens
+    needed = sorted({int(e) for t in tok for e in ids[t] if e >= 0})
+    layer = host_layer(weights, needed)
+    return O.ffn(layer, I.activations_to_numpy(x), act, ids, w, tokens=tokens, out_rows=rows,
+                 with_shared=with_shared)
+
+
+def block_tokens(ids: np.ndarray, n_experts: int, block: int = 16):
+    """Tokens that put a slot in every `block`-slot block of every expert's
+    group (and of the shared expert's, whose slot order is the token order):
+    the first slot of each block.  Grouped slots are in expert order, stably
+    by flat index, so this hits every token tile and every 16-token block
+    the grouped kernels form."""
+    counts, offsets, perm, _ = O.group(ids, n_experts)
+    k = ids.shape[1]
+    toks = set()
+    for e in range(n_experts):
+        for s in range(offsets[e], offsets[e + 1], block):
+            toks.add(int(perm[s]) // k)
+    toks.update(range(0, ids.shape[0], block))
+    return sorted(toks)

@@ -1,5 +1,5 @@
 """The C ABI on the host: the library loads, exports every symbol that
-include/moe.h declares, sizes workspaces, and rejects bad arguments before
+include/*.h declare, sizes workspaces, and rejects bad arguments before
 anything reaches a GPU (every call here fails validation, so no HIP call is
 made)."""
 
@@ -14,13 +14,18 @@ import pytest
 from block_quantized_expert_amd import binding as B
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "moe.h")
+INCLUDE = os.path.join(ROOT, "include")
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(moe_\w+)\s*\(", text, flags=re.M)))
+    names = set()
+    for fn in sorted(os.listdir(INCLUDE)):
+        if not fn.endswith(".h"):
+            continue
+        text = open(os.path.join(INCLUDE, fn)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"^[A-Za-z_][\w \*]*?\b(moe_\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_symbol():

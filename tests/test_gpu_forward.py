@@ -3,6 +3,7 @@ oracle, through the C ABI.  Single-token calls of the covered formats run as
 one fused kernel with a grid barrier; the other calls go through the
 separate route+group and FFN kernels."""
 
+import ctypes
 from dataclasses import replace
 
 import numpy as np
@@ -149,3 +150,33 @@ def test_timed_entry_point():
     assert 0.0 < t < 100.0
     ids_ref, w_ref = oracle_routing(wl, routing)
     assert_y_close(buf.y.cpu().numpy(), oracle_y(wl, x, ids_ref, w_ref, copy=4))
+
+
+@pytest.mark.parametrize("with_dev_error", [True, False])
+def test_barrier_give_up_writes_nan(monkeypatch, with_dev_error):
+    """The single-token kernel's grid barrier is a bounded wait.  With the
+    library's test hook the host asks it to wait for a value no workgroup
+    posts and to give up after 16 polls: every workgroup then takes the
+    give-up path and exits normally, sets MOE_DEVERR_SYNC and leaves NaN in
+    its rows of y, so an incomplete y is visible without dev_error too.  The
+    next call without the hook is correct again."""
+    wl = replace(ONE, n_experts=64, top_k=4, seed=44)
+    layer, x, x_d, routing, routing_d = gpu_inputs(wl)
+    assert B.lib().moe_forward_single_kernel(ctypes.byref(layer.c), 1, B.MOE_ACT_BF16) == 1
+    buf = B.ForwardBuffers(layer, 1, x_d.device)
+    if not with_dev_error:
+        buf.dev_error = None
+    monkeypatch.setenv("MOE_TEST_FUSED_GIVE_UP", "16")
+    B.moe_forward(layer, routing_d["logits"], x_d, wl.routed_scale, buffers=buf)
+    torch.cuda.synchronize()
+    assert torch.isnan(buf.y).all()
+    if with_dev_error:
+        assert int(buf.dev_error.item()) & B.MOE_DEVERR_SYNC
+        buf.dev_error.zero_()
+    monkeypatch.delenv("MOE_TEST_FUSED_GIVE_UP")
+    B.moe_forward(layer, routing_d["logits"], x_d, wl.routed_scale, buffers=buf)
+    torch.cuda.synchronize()
+    if with_dev_error:
+        assert int(buf.dev_error.item()) == 0
+    ids_ref, w_ref = oracle_routing(wl, routing)
+    assert_y_close(buf.y.cpu().numpy(), oracle_y(wl, x, ids_ref, w_ref))
