@@ -20,13 +20,15 @@ MOE_ACT_F32, MOE_ACT_BF16 = 0, 1
 MOE_W_MXFP4, MOE_W_FP8E4M3_B128 = 0, 1
 MOE_DEVERR_EXPERT_ID, MOE_DEVERR_TOKEN_ID, MOE_DEVERR_SYNC = 1, 2, 4
 MOE_FORWARD_SYNC_BYTES = 8192
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # every symbol include/*.h declare
 EXPORTED = ["moe_route", "moe_route_hash", "moe_route_group", "moe_group_workspace_bytes",
             "moe_group", "moe_ffn_workspace_bytes", "moe_ffn_forward", "moe_ffn_gate_up",
             "moe_ffn_down", "moe_ffn_forward_timed", "moe_forward_workspace_bytes",
             "moe_forward_single_kernel", "moe_forward_workspace_init", "moe_forward",
-            "moe_forward_timed", "moe_status_string", "moe_stream_read"]
+            "moe_forward_timed", "moe_forward_noalloc", "moe_status_string",
+            "moe_stream_read"]
 
 WEIGHT_TYPES = {"mxfp4": MOE_W_MXFP4, "fp8_e4m3_b128": MOE_W_FP8E4M3_B128}
 
@@ -86,7 +88,9 @@ def lib() -> ctypes.CDLL:
         fwd = [ctypes.POINTER(MoeLayer), P, F, P, I, I, P, P, P, P, P, P, P, P, S, P, P]
         L.moe_forward.argtypes = fwd
         L.moe_forward_timed.argtypes = fwd + [P, P]
-        for name in ("moe_forward_workspace_init", "moe_forward", "moe_forward_timed"):
+        L.moe_forward_noalloc.argtypes = fwd[:13] + [P, P]
+        for name in ("moe_forward_workspace_init", "moe_forward", "moe_forward_timed",
+                     "moe_forward_noalloc"):
             getattr(L, name).restype = ctypes.c_int
         L.moe_stream_read.argtypes = [P, S, P, P]
         L.moe_stream_read.restype = ctypes.c_int
@@ -370,3 +374,17 @@ def moe_forward(layer: Layer, logits, x, routed_scale=1.5, buffers: ForwardBuffe
                "moe_forward_timed")
     return buffers
 
+
+def moe_forward_noalloc(layer: Layer, logits, x, routed_scale=1.5, buffers: ForwardBuffers = None,
+                        stream=None):
+    """moe_forward on the library's own scratch array (no workspace).  Only
+    the output tensors of ``buffers`` are used.  Returns the buffers."""
+    n = x.shape[0]
+    if buffers is None:
+        buffers = ForwardBuffers(layer, n, x.device, stream, workspace=False)
+    x_type = MOE_ACT_BF16 if x.dtype == torch.bfloat16 else MOE_ACT_F32
+    a = buffers.args()
+    _check(lib().moe_forward_noalloc(ctypes.byref(layer.c), _ptr(logits), routed_scale, _ptr(x),
+                                     x_type, n, *a[:7], a[9], _stream(stream)),
+           "moe_forward_noalloc")
+    return buffers

@@ -6,6 +6,7 @@
 
 #include <atomic>
 #include <chrono>
+#include <mutex>
 #include <random>
 
 #include "moe.h"
@@ -168,6 +169,45 @@ moe_status forward_impl(const moe_layer* layer, const float* logits, float route
   return MOE_OK;
 }
 
+// ---------------------------------------------------------------- no-alloc
+
+// moe_forward_noalloc's workspace: one array per GPU the library runs on,
+// held until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory; its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+__global__ void zero_words_kernel(unsigned long long* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0ull;
+}
+
+// The current device's scratch address; on the first call for a device it
+// is looked up, and the barrier flags at its start are cleared on `stream`
+// with a small kernel (no memset node, so the call can be captured in a
+// graph; later calls need no clearing: every call stamps a new value).
+moe_status device_scratch(hipStream_t stream, char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return MOE_ERR_DEVICE;
+    constexpr int kWords = MOE_FORWARD_SYNC_BYTES / 8;
+    hipLaunchKernelGGL(zero_words_kernel, dim3((kWords + 255) / 256), dim3(256), 0, stream,
+                       static_cast<unsigned long long*>(ptr), kWords);
+    if (hipGetLastError() != hipSuccess) return MOE_ERR_DEVICE;
+    g_scratch[dev] = ptr;
+  }
+  *out = static_cast<char*>(g_scratch[dev]);
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -311,6 +351,28 @@ moe_status moe_forward_timed(const moe_layer* layer, const float* logits, float 
   return forward_impl(layer, logits, routed_scale, x, x_type, n_tokens, topk_ids, topk_w, counts,
                       offsets, perm, inv_perm, y, workspace, workspace_bytes, dev_error, stream,
                       start, stop);
+}
+
+moe_status moe_forward_noalloc(const moe_layer* layer, const float* logits, float routed_scale,
+                               const void* x, int x_type, int n_tokens, int32_t* topk_ids,
+                               float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                               int32_t* inv_perm, float* y, int32_t* dev_error,
+                               hipStream_t stream) {
+  // every argument is checked (the workspace against the scratch size)
+  // before the first call on a device enqueues its clearing kernel; the
+  // checks read only the workspace pointer's alignment, so an aligned
+  // stand-in serves until the device address is known
+  moe::ForwardPlan plan;
+  moe_status s = moe::check_forward(layer, logits, routed_scale, x, x_type, n_tokens, topk_ids,
+                                    topk_w, counts, offsets, perm, inv_perm, y,
+                                    reinterpret_cast<void*>(uintptr_t{256}),
+                                    MOE_NOALLOC_SCRATCH_BYTES, &plan);
+  if (s != MOE_OK) return s;
+  char* ws = nullptr;
+  if ((s = device_scratch(stream, &ws)) != MOE_OK) return s;
+  return forward_impl(layer, logits, routed_scale, x, x_type, n_tokens, topk_ids, topk_w, counts,
+                      offsets, perm, inv_perm, y, ws, MOE_NOALLOC_SCRATCH_BYTES, dev_error,
+                      stream, nullptr, nullptr);
 }
 
 const char* moe_status_string(moe_status s) {

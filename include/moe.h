@@ -306,6 +306,29 @@ moe_status moe_forward_timed(const moe_layer* layer, const float* logits, float 
                              size_t workspace_bytes, int32_t* dev_error, hipStream_t stream,
                              hipEvent_t start, hipEvent_t stop);
 
+/*
+ * moe_forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The same arguments and results as moe_forward, without the workspace: the
+ * scratch memory is an array of MOE_NOALLOC_SCRATCH_BYTES inside the library,
+ * one per GPU it runs on, held until the process ends.  Nothing is allocated
+ * by the call (the first call on a device also enqueues one small kernel that
+ * clears the array's barrier flags).
+ *   Batches whose moe_forward_workspace_bytes exceed
+ *   MOE_NOALLOC_SCRATCH_BYTES return MOE_ERR_WORKSPACE before anything is
+ *   enqueued (at hidden 4096, intermediate 2048, top-6 and a shared expert:
+ *   up to about 370 tokens).
+ *   Every call on a GPU uses that GPU's one array and leaves its contents
+ *   behind: calls on one GPU must not overlap in time (two streams, or two
+ *   host threads, running calls at once on the same device race on it).
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe_status moe_forward_noalloc(const moe_layer* layer, const float* logits, float routed_scale,
+                               const void* x, int x_type, int n_tokens, int32_t* topk_ids,
+                               float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                               int32_t* inv_perm, float* y, int32_t* dev_error,
+                               hipStream_t stream);
+
 /* A static, human-readable name of a status code. */
 const char* moe_status_string(moe_status s);
 
