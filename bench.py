@@ -26,7 +26,11 @@ Every record holds:
 - ``roofline``: the kernel that runs the routed experts' gate/up (at one
   token, the single kernel that does the whole layer), its algorithmic bytes
   or flops per launch over its average duration from HIP events that its own
-  dispatch records (on the stream it runs on);
+  dispatch records (on the stream it runs on).  Those events are taken in a
+  pass of at least 20 more steps right after the timed steps (the same
+  rotation of layer copies and inputs, so still cold): a dispatch that
+  records events leaves the GPU idle for several microseconds, which at
+  single-token decode (a ~29 us step) would inflate the timed steps;
 - ``cpu_baseline``: the fp64 oracle on a bounded sample of the same workload
   on the host cores.
 The line also carries ``hbm_read_ceiling``: the rate of a plain streaming
@@ -55,15 +59,16 @@ HEADLINE = "hash4096"
 NESTED = ["tiny", "decode1", "decode32", "prefill512"]
 REPS = 5
 
-# workload: (steps, warmup, copies, pool, event_every) when it is measured as
-# a nested record or as the line without --steps/--warmup
+# workload: (steps, warmup, copies, pool) when it is measured as a nested
+# record or as the line without --steps/--warmup
 DEFAULTS = {
-    "tiny": (2000, 100, 1, 8, 8),
-    "decode1": (2000, 100, 8, 64, 8),
-    "decode32": (400, 20, 8, 16, 1),
-    "prefill512": (100, 10, 8, 4, 1),
-    "hash4096": (20, 5, 2, 2, 1),
+    "tiny": (2000, 100, 1, 8),
+    "decode1": (2000, 100, 8, 64),
+    "decode32": (400, 20, 8, 16),
+    "prefill512": (100, 10, 8, 4),
+    "hash4096": (20, 5, 2, 2),
 }
+MIN_EVENT_SAMPLES = 20
 
 # HBM traffic of the roofline kernel per launch, from two rocprofv3 --pmc
 # passes over this script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch of
@@ -318,7 +323,7 @@ def step_stats(rep_ms, rep_steps):
             "spread_over_15pct": bool((per.max() - per.min()) / med > 0.15)}
 
 
-def run_workload(name, steps, warmup, copies, n_pool, every, cpu_seconds, dev):
+def run_workload(name, steps, warmup, copies, n_pool, cpu_seconds, dev):
     """Measure one workload; returns its record (without the top-level
     contract keys)."""
     import numpy as np
@@ -341,12 +346,6 @@ def run_workload(name, steps, warmup, copies, n_pool, every, cpu_seconds, dev):
         runner.step(s)
     torch.cuda.synchronize()
 
-    # events recorded by the kernels' own dispatches on every `every`-th step
-    sampled = list(range(0, steps, every))
-    evs = [tuple(B.HipEvent() for _ in range(4)) for _ in sampled]
-    ev_handles = [None] * steps
-    for i, j in enumerate(sampled):
-        ev_handles[j] = tuple(e.handle for e in evs[i])
     # repetition boundaries: stream events between steps
     reps = min(REPS, steps)
     bounds = [round(r * steps / reps) for r in range(reps + 1)]
@@ -359,27 +358,36 @@ def run_workload(name, steps, warmup, copies, n_pool, every, cpu_seconds, dev):
         if j == bounds[b]:
             rep_ev[b].record(stream)
             b += 1
-        runner.step(warmup + j, ev_handles[j])
+        runner.step(warmup + j)
     rep_ev[b].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
-
     rep_ms = [rep_ev[r].elapsed_time(rep_ev[r + 1]) for r in range(reps)]
     rep_steps = [bounds[r + 1] - bounds[r] for r in range(reps)]
-    gu_ms = [e[0].elapsed_ms(e[1]) for e in evs]
-    gu_avg_s = float(np.mean(gu_ms)) / 1e3
+
+    # kernel durations: events recorded by the kernels' own dispatches, on
+    # every step of a further pass that continues the same rotation
+    n_samp = max(MIN_EVENT_SAMPLES, min(steps // 4, 250))
+    evs = [tuple(B.HipEvent() for _ in range(4)) for _ in range(n_samp)]
+    first = warmup + steps
+    for i in range(n_samp):
+        runner.step(first + i, tuple(e.handle for e in evs[i]))
+    torch.cuda.synchronize()
+    gu_avg_s = float(np.mean([e[0].elapsed_ms(e[1]) for e in evs])) / 1e3
     dn_avg_s = None if runner.fused else float(np.mean([e[2].elapsed_ms(e[3]) for e in evs])) / 1e3
     counts_list = routed_counts(runner, n_pool)
     used = [counts_list[(warmup + j) % n_pool] for j in range(steps)]
+    used_samp = [counts_list[(first + i) % n_pool] for i in range(n_samp)]
     costs = workload_costs(wl, used)
+    kcosts = workload_costs(wl, used_samp)
 
     ms_per_step = elapsed / steps * 1e3
     if runner.fused:
         kernel_name = "decode_fused_kernel<%d> (moe_forward: route + group + FFN)" % (wl.hidden // 512)
-        k_bytes, k_flops, issue = costs["path_bytes"], costs["path_flops"], 1.0
+        k_bytes, k_flops, issue = kcosts["path_bytes"], kcosts["path_flops"], 1.0
     else:
         kernel_name = "routed gate/up kernel of moe_ffn_forward (+ SwiGLU)"
-        k_bytes, k_flops = costs["gate_up_bytes"], costs["gate_up_flops"]
+        k_bytes, k_flops = kcosts["gate_up_bytes"], kcosts["gate_up_flops"]
         # bf16 x on the grouped GEMMs: each product issued once per E4M3 part
         # of x (two) on the scaled fp8 instruction
         issue = 2.0 if (wl.act == "bf16" and wl.n_tokens > 16) else 1.0
@@ -400,7 +408,9 @@ def run_workload(name, steps, warmup, copies, n_pool, every, cpu_seconds, dev):
         "flops_per_launch": k_flops,
         "flop_per_byte": intensity,
         "avg_launch_us": gu_avg_s * 1e6,
-        "timed_launches": len(sampled),
+        "timed_launches": n_samp,
+        "timing": "dispatch-recorded HIP events on every step of a %d-step pass right "
+                  "after the timed steps (same rotation, cold)" % n_samp,
         "hbm_frac": gbps / HBM_PEAK_GBPS,
         "mfma_bf16_frac": tflops / MFMA_BF16_PEAK_TFLOPS,
     }
@@ -434,13 +444,13 @@ def run_workload(name, steps, warmup, copies, n_pool, every, cpu_seconds, dev):
         dissue = 3.0 if issue > 1.0 else 1.0  # h as three E4M3 parts
         rec["down_kernel"] = {
             "kernel": "routed down kernel of moe_ffn_forward",
-            "bytes_per_launch": costs["down_bytes"],
-            "flops_per_launch": costs["down_flops"],
+            "bytes_per_launch": kcosts["down_bytes"],
+            "flops_per_launch": kcosts["down_flops"],
             "avg_launch_us": dn_avg_s * 1e6,
-            "achieved_GBps": costs["down_bytes"] / dn_avg_s / 1e9,
-            "achieved_TFLOPs": costs["down_flops"] / dn_avg_s / 1e12,
-            "mfma_bf16_frac": costs["down_flops"] / dn_avg_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-            "issued_frac_of_fp8_peak": dissue * costs["down_flops"] / dn_avg_s / 1e12
+            "achieved_GBps": kcosts["down_bytes"] / dn_avg_s / 1e9,
+            "achieved_TFLOPs": kcosts["down_flops"] / dn_avg_s / 1e12,
+            "mfma_bf16_frac": kcosts["down_flops"] / dn_avg_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "issued_frac_of_fp8_peak": dissue * kcosts["down_flops"] / dn_avg_s / 1e12
                                        / MFMA_FP8_PEAK_TFLOPS,
         }
     st = rec["step_stats"]
@@ -499,8 +509,6 @@ def main():
                          "as nested records)" % HEADLINE)
     ap.add_argument("--copies", type=int, default=None)
     ap.add_argument("--pool", type=int, default=None)
-    ap.add_argument("--event-every", type=int, default=None,
-                    help="record the per-kernel events on every n-th timed step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -540,16 +548,15 @@ def main():
     cpu = not args.no_cpu_baseline
     configs = {}
     for name in nested:
-        st, wu, cp, po, ev = DEFAULTS[name]
-        configs[name] = run_workload(name, st, wu, cp, po, ev,
+        st, wu, cp, po = DEFAULTS[name]
+        configs[name] = run_workload(name, st, wu, cp, po,
                                      args.nested_cpu_seconds if cpu else 0.0, dev)
-    st, wu, cp, po, ev = DEFAULTS[line_name]
+    st, wu, cp, po = DEFAULTS[line_name]
     steps = args.steps if args.steps is not None else st
     warmup = args.warmup if args.warmup is not None else wu
     rec = run_workload(line_name, steps, warmup,
                        args.copies if args.copies is not None else cp,
                        args.pool if args.pool is not None else po,
-                       max(1, args.event_every if args.event_every is not None else ev),
                        args.cpu_seconds if cpu else 0.0, dev)
 
     result = {

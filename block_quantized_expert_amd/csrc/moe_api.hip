@@ -4,10 +4,7 @@
 
 #include <stdlib.h>
 
-#include <atomic>
-#include <chrono>
 #include <mutex>
-#include <random>
 
 #include "moe.h"
 #include "moe_host.h"
@@ -16,6 +13,21 @@
 namespace {
 
 moe_status launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE; }
+
+// Zeroes n 8-byte words: the barrier words of a forward workspace are
+// cleared by a kernel, not a memset, so the clearing can sit in a captured
+// graph too.
+__global__ void zero_words_kernel(unsigned long long* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0ull;
+}
+
+hipError_t zero_sync_words(void* p, hipStream_t stream) {
+  constexpr int kWords = MOE_FORWARD_SYNC_BYTES / 8;
+  hipLaunchKernelGGL(zero_words_kernel, dim3((kWords + 255) / 256), dim3(256), 0, stream,
+                     static_cast<unsigned long long*>(p), kWords);
+  return hipGetLastError();
+}
 
 // Polls of the single-token kernel's grid-barrier flags before it gives up
 // (about a second).
@@ -96,23 +108,6 @@ moe_status ffn_stages(int stages, const moe_layer* layer, const void* x, int x_t
 
 static_assert(sizeof(moe::FusedSync) <= MOE_FORWARD_SYNC_BYTES, "sync area of the workspace");
 
-// A value no earlier call of this process used: a counter that starts at a
-// random point of the 64-bit range (so flags left by another process do not
-// match either) and skips 0 (the value moe_forward_workspace_init writes).
-unsigned long long next_epoch() {
-  static std::atomic<unsigned long long> counter{[] {
-    std::random_device rd;
-    const unsigned long long t = (unsigned long long)
-        std::chrono::steady_clock::now().time_since_epoch().count();
-    return (((unsigned long long)rd() << 32) ^ rd() ^ (t * 0x9E3779B97F4A7C15ull)) | 1ull;
-  }()};
-  unsigned long long v;
-  do {
-    v = counter.fetch_add(1, std::memory_order_relaxed);
-  } while (v == 0);
-  return v;
-}
-
 moe_status forward_impl(const moe_layer* layer, const float* logits, float routed_scale,
                         const void* x, int x_type, int n_tokens, int32_t* topk_ids,
                         float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
@@ -142,15 +137,13 @@ moe_status forward_impl(const moe_layer* layer, const float* logits, float route
     f.perm = perm;
     f.inv_perm = inv_perm;
     f.sync = reinterpret_cast<moe::FusedSync*>(ws);
-    f.epoch = next_epoch();
-    f.wait_epoch = f.epoch;
+    f.wait_xor = 0;
     f.spin_limit = kFusedSpinLimit;
     // test hook: MOE_TEST_FUSED_GIVE_UP=<polls> makes the grid barrier wait
     // for a value no workgroup posts and give up after that many polls, so
     // the timeout path runs with every workgroup still exiting normally
     if (const char* v = getenv("MOE_TEST_FUSED_GIVE_UP")) {
-      f.wait_epoch = f.epoch ^ 0x8000000000000000ull;
-      if (f.wait_epoch == 0) f.wait_epoch = 0x4000000000000000ull;
+      f.wait_xor = 0x8000000000000000ull;
       f.spin_limit = (uint32_t)strtoul(v, nullptr, 10);
     }
     f.dev_error = dev_error;
@@ -181,11 +174,6 @@ constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void* g_scratch[kMaxDevices];
 
-__global__ void zero_words_kernel(unsigned long long* p, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0ull;
-}
-
 // The current device's scratch address; on the first call for a device it
 // is looked up, and the barrier flags at its start are cleared on `stream`
 // with a small kernel (no memset node, so the call can be captured in a
@@ -198,10 +186,7 @@ moe_status device_scratch(hipStream_t stream, char** out) {
     void* ptr = nullptr;
     if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
       return MOE_ERR_DEVICE;
-    constexpr int kWords = MOE_FORWARD_SYNC_BYTES / 8;
-    hipLaunchKernelGGL(zero_words_kernel, dim3((kWords + 255) / 256), dim3(256), 0, stream,
-                       static_cast<unsigned long long*>(ptr), kWords);
-    if (hipGetLastError() != hipSuccess) return MOE_ERR_DEVICE;
+    if (zero_sync_words(ptr, stream) != hipSuccess) return MOE_ERR_DEVICE;
     g_scratch[dev] = ptr;
   }
   *out = static_cast<char*>(g_scratch[dev]);
@@ -329,7 +314,8 @@ int moe_forward_single_kernel(const moe_layer* layer, int n_tokens, int x_type) 
 moe_status moe_forward_workspace_init(void* workspace, size_t workspace_bytes,
                                       hipStream_t stream) {
   if (workspace == nullptr || workspace_bytes < MOE_FORWARD_SYNC_BYTES) return MOE_ERR_WORKSPACE;
-  return launched(hipMemsetAsync(workspace, 0, MOE_FORWARD_SYNC_BYTES, stream));
+  if ((reinterpret_cast<uintptr_t>(workspace) & 15) != 0) return MOE_ERR_INVALID;
+  return launched(zero_sync_words(workspace, stream));
 }
 
 moe_status moe_forward(const moe_layer* layer, const float* logits, float routed_scale,

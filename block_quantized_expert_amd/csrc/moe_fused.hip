@@ -67,6 +67,7 @@ constexpr int kDScale = 16 * (kMaxInter / 32);  // their bytes per segment
 constexpr int kHRow = 136;                      // bf16 per staged h row (128 + 8)
 
 struct FusedSmem {
+  unsigned long long epoch;  // this launch's barrier value (FusedSync::launch + 1)
   int ids[MOE_MAX_TOP_K];   // routed experts in rank order
   int act[kFSlots];         // expert of segment a (n_experts: shared), ascending
   int ok;
@@ -89,10 +90,11 @@ struct FusedSmem {
   } u;
 };
 
-// Synchronisation words live in the caller's workspace and carry the call's
-// epoch (a 64-bit value the host never repeats), so nothing needs resetting
-// between calls and no word is ever read-modify-written: device-wide atomic
-// updates of one address serialise at the memory (~0.1 us each).
+// Synchronisation words live in the caller's workspace and carry the
+// launch's epoch (the workspace's launch count plus one, see FusedSync), so
+// nothing needs resetting between calls and no word is ever
+// read-modify-written: device-wide atomic updates of one address serialise
+// at the memory (~0.1 us each).
 //
 // Every word that passes between workgroups during the call (h and the
 // flags) is stored and loaded at device scope, which on this GPU writes
@@ -121,19 +123,19 @@ __device__ __forceinline__ uint64_t ld_dev8(const void* a) {
 // caller can request loads in between: arrive() stores this workgroup's
 // arrival flag once its earlier stores have completed; wait_release() has
 // wavefront 0 of every workgroup read all the flags (four per lane, requested
-// together) until each holds the call's epoch.  Reading them directly, rather
+// together) until each holds the launch's epoch.  Reading them directly, rather
 // than through one workgroup that collects them and posts a release, saves
 // two memory round trips, and these are long while the down codes stream.
 // wait_release() returns false on timeout (a bounded wait).
-__device__ void arrive(const FusedParams& f) {
+__device__ void arrive(const FusedParams& f, const FusedSmem& sm) {
   stores_done();
   __syncthreads();
-  if (threadIdx.x == 0) post(f.sync->arrive + blockIdx.x, f.epoch);
+  if (threadIdx.x == 0) post(f.sync->arrive + blockIdx.x, sm.epoch);
 }
 
 __device__ bool wait_release(const FusedParams& f, FusedSmem& sm) {
   if (threadIdx.x < kWave) {
-    const unsigned long long ep = f.wait_epoch;
+    const unsigned long long ep = sm.epoch ^ f.wait_xor;
     const int lane = threadIdx.x;
     uint32_t spins = 0;
     int ok = 1;
@@ -267,6 +269,12 @@ __global__ __launch_bounds__(kFThreads) void decode_fused_kernel(FusedParams f) 
   const int score_part = wave == 9 ? 0 : wave == 10 ? 1 : wave == 11 ? 2 : wave == 13 ? 3 : -1;
 
   // ---- 1. routing and grouping; x staged
+  if (wave == kFWaves - 1 && lane == 0) {
+    // the launch count is read before this workgroup arrives at the barrier
+    // and stored back (by workgroup 0) only after every workgroup has
+    // arrived, so all of them read the same value
+    sm.epoch = ld_dev8(&f.sync->launch) + 1ull;
+  }
   if (early) {
     // first wait for a logit of our own, so that these copies queue behind
     // the routing's loads and do not delay them
@@ -437,9 +445,13 @@ __global__ __launch_bounds__(kFThreads) void decode_fused_kernel(FusedParams f) 
   // wavefront 0 polls the flags: it requests nothing before, so that no poll
   // waits behind a load (a wavefront's loads complete in order)
   const bool pre = (int)blockIdx.x < n_rb && wave > 0 && wave < ksteps;
-  arrive(f);
+  arrive(f, sm);
   if (pre) load_down(blockIdx.x, wave);
-  if (!wait_release(f, sm)) {
+  const bool released = wait_release(f, sm);
+  // the next launch on this workspace takes the next epoch (also after a
+  // give-up: its flags must not match what this launch posted)
+  if (blockIdx.x == 0 && threadIdx.x == 0) st_dev8(&f.sync->launch, sm.epoch);
+  if (!released) {
     // some workgroup never arrived (the grid was not all resident): this
     // workgroup's rows of y are not computed; NaN there makes the failure
     // visible in y itself, whether or not the caller passed dev_error

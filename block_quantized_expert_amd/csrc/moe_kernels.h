@@ -47,9 +47,15 @@ struct FfnParams {
 };
 
 // Synchronisation words of the fused single-token decode (in the caller's
-// workspace).  Each holds the epoch of the call that last posted it.
+// workspace, zeroed once).  `launch` counts the kernel's launches on this
+// workspace: a launch reads it at its start, uses launch + 1 as its epoch
+// and stores that back once its grid barrier is over, so every launch has a
+// new epoch without the host (a launch captured in a graph and replayed
+// included).  arrive[b] holds the epoch of the launch whose workgroup b last
+// arrived.
 struct FusedSync {
-  static constexpr int kMaxGrid = 1024;  // one workgroup per compute unit
+  static constexpr int kMaxGrid = 1023;  // one workgroup per compute unit
+  unsigned long long launch;
   unsigned long long arrive[kMaxGrid];
 };
 
@@ -67,9 +73,8 @@ struct FusedParams {
   int32_t* perm;
   int32_t* inv_perm;
   FusedSync* sync;
-  unsigned long long epoch;       // unique per call, never 0: posted on arrival
-  unsigned long long wait_epoch;  // the value waited for: epoch (a test may ask for
-                                  // one no workgroup posts, to exercise the give-up)
+  unsigned long long wait_xor;    // 0; a test sets a bit so that the barrier waits for
+                                  // a value no workgroup posts (the give-up path)
   uint32_t spin_limit;            // polls of the flags before giving up
   int32_t* dev_error;             // nullable
   int grid;                       // set by the launcher

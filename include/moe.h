@@ -259,9 +259,11 @@ moe_status moe_ffn_forward_timed(const moe_layer* layer, const void* x, int x_ty
  *   x, x_type, y  as for moe_ffn_forward.
  *   workspace     caller-owned device memory of at least
  *                 moe_forward_workspace_bytes(layer, n_tokens) bytes,
- *                 16-byte aligned.  Its first MOE_FORWARD_SYNC_BYTES hold
- *                 synchronisation flags stamped with a per-call value the
- *                 library never repeats: zero them once with
+ *                 16-byte aligned.  Its first MOE_FORWARD_SYNC_BYTES hold a
+ *                 launch counter and barrier flags stamped with it; the
+ *                 single-token kernel advances the counter itself, so the
+ *                 words need no reset between calls and a call captured in a
+ *                 HIP graph may be replayed.  Zero them once with
  *                 moe_forward_workspace_init before the first call.  Calls
  *                 that share a workspace must not overlap in time.
  *   dev_error     nullable; MOE_DEVERR_SYNC is set if a wait of the

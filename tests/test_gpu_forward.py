@@ -180,3 +180,44 @@ def test_barrier_give_up_writes_nan(monkeypatch, with_dev_error):
         assert int(buf.dev_error.item()) == 0
     ids_ref, w_ref = oracle_routing(wl, routing)
     assert_y_close(buf.y.cpu().numpy(), oracle_y(wl, x, ids_ref, w_ref))
+
+
+@pytest.mark.parametrize("entry", ["moe_forward", "moe_forward_noalloc"])
+@pytest.mark.parametrize("n_tokens", [1, 20])
+def test_captured_graph_replays_match_eager(entry, n_tokens):
+    """A call captured in a HIP graph (torch's CUDAGraph) is replayed four
+    times on new inputs copied into its static buffers, with eager calls and
+    synchronisations between the replays; every replay equals the eager call
+    bitwise.  One token runs the fused kernel, whose barrier takes a new
+    epoch from the workspace's launch counter at every launch (arguments are
+    frozen in a graph); 20 tokens run the route+group and FFN kernels."""
+    wl = replace(ONE, n_tokens=n_tokens, n_experts=64, top_k=4, seed=46)
+    layer, x, x_d, routing, routing_d = gpu_inputs(wl)
+    fn = getattr(B, entry)
+    use_ws = entry == "moe_forward"
+    buf = B.ForwardBuffers(layer, n_tokens, x_d.device, workspace=use_ws)
+    x_s, l_s = x_d.clone(), routing_d["logits"].clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn(layer, l_s, x_s, wl.routed_scale, buffers=buf)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn(layer, l_s, x_s, wl.routed_scale, buffers=buf)
+    for c in range(4):
+        xc = I.activations(wl, copy=c + 1).to(x_d.device)
+        lc = I.router_logits(wl, copy=c + 1).to(x_d.device)
+        x_s.copy_(xc)
+        l_s.copy_(lc)
+        g.replay()
+        torch.cuda.synchronize()
+        ref = fn(layer, lc, xc, wl.routed_scale)
+        torch.cuda.synchronize()
+        assert int(buf.dev_error.item()) == 0
+        assert torch.equal(buf.ids, ref.ids), c
+        assert torch.equal(buf.y, ref.y), c
+        if c == 3:
+            ids_ref, w_ref = oracle_routing(wl, {"kind": "learned", "logits": lc.cpu()})
+            assert_y_close(buf.y.cpu().numpy(), oracle_y(wl, xc.cpu(), ids_ref, w_ref))
