@@ -36,12 +36,33 @@ Readings taken where the pages are silent:
   is NaN); one UE8M0 scale per 128 consecutive elements of a row.
 * Learned routing selects on the raw fp32 logits (sqrt o softplus is strictly
   increasing, so the set equals selection on scores); ties go to the lower
-  expert index; output slot i = 0 holds the largest.  Expert groups are read
-  as one group (plain top-k over all experts).
+  expert index; output slot i = 0 holds the largest.  Without expert groups
+  and bias this is plain top-k over all experts (route_topk).
+* Group-limited selection ([Kernel Guide] section 1 names "expert group top-k
+  selection" and gives no parameters; route_grouped): experts form n_group
+  contiguous groups; the selection key of expert e is s_e + b_e in fp64 with
+  an optional per-expert bias b that enters the selection only; a group's
+  score is the sum of its two largest keys (its one key for a group of one
+  expert); the topk_group groups of largest score are kept (ties to the
+  lower group index) and the top_k largest keys among their experts are
+  chosen (ties to the lower expert index); the weights use the unbiased s.
+* Tail pruning ([Kernel Guide] section 3.2 item 3 and its configuration
+  table; [RFC] section 5; prune_tail): a token keeps the routed experts whose
+  weight is at least min_w, at most keep_max of them (the largest weights,
+  ties to the lower slot) and at least one (the largest); kept weights are
+  multiplied by alpha = sqrt(sum_all w^2 / sum_kept w^2); a dropped slot
+  has expert id -1 and weight 0.  p_early = 0.025 of the RFC (weights that
+  sum to 1) is min_w = 0.025 * routed_scale here.
+* Gate-first lazy skip ([RFC] section 5; ffn(lazy_tau=...)): a routed
+  expert whose gate output g for a token has max_j |SiLU(g_j)| < lazy_tau
+  contributes nothing to that token (its up and down projections are not
+  needed).  The shared expert is never skipped.
 * Weights: s = sqrt(softplus(logit)), w = scale * s / sum(s) over the top-k,
   evaluated in fp64 and rounded to fp32 once.
 * Grouping: perm lists flat indices f = t*top_k + i stably sorted by expert
-  (ascending f inside an expert); inv_perm[perm[p]] = p.
+  (ascending f inside an expert); inv_perm[perm[p]] = p.  An id of -1 (a
+  slot dropped by tail pruning) belongs to no expert: it is not counted, not
+  in perm, and its inv_perm is -1.
 * The shared expert sees every token with weight 1 and has its own
   intermediate size.  No clamp is applied to the SwiGLU gate.
 * y is accumulated in fp64 and rounded to fp32 (round-to-nearest-even) once.
@@ -220,6 +241,90 @@ def route_hash(token_ids: np.ndarray, tid2eid: np.ndarray, tid2w: np.ndarray):
     return ids, w
 
 
+def gate_score(v: float) -> float:
+    """s = sqrt(softplus(v)) in fp64 ([Kernel Guide] section 1, SQRT_SOFTPLUS)."""
+    return math.sqrt(softplus(v))
+
+
+def route_grouped(logits: np.ndarray, top_k: int, routed_scale: float, n_group: int = 1,
+                  topk_group: int = 1, bias=None):
+    """Group-limited SQRT_SOFTPLUS router with a selection-only bias.
+
+    For each token, in fp64: s_e = sqrt(softplus(l_e)); key_e = s_e + b_e;
+    group g holds experts g*G .. g*G+G-1 (G = E / n_group) and scores the sum
+    of its two largest keys (largest first; one key if G == 1); the
+    topk_group best groups (score descending, ties to the lower group) are
+    kept; the top_k experts of those groups by key (descending, ties to the
+    lower expert) are chosen, slot 0 the largest; w_i = routed_scale * s_i /
+    sum_j s_j over the chosen (unbiased scores, summed in slot order),
+    rounded to fp32 once.
+    """
+    logits = np.asarray(logits, dtype=np.float32)
+    n_tokens, n_experts = logits.shape
+    if n_group < 1 or n_experts % n_group != 0:
+        raise ValueError("n_group must divide n_experts")
+    gsize = n_experts // n_group
+    if not 1 <= topk_group <= n_group or not 0 < top_k <= topk_group * gsize:
+        raise ValueError("bad topk_group / top_k")
+    b = [0.0] * n_experts if bias is None else [float(v) for v in np.asarray(bias, np.float32)]
+    ids = np.zeros((n_tokens, top_k), dtype=np.int32)
+    w = np.zeros((n_tokens, top_k), dtype=np.float32)
+    for t in range(n_tokens):
+        s = [gate_score(float(v)) for v in logits[t]]
+        key = [s[e] + b[e] for e in range(n_experts)]
+        gscore = []
+        for g in range(n_group):
+            members = sorted(key[g * gsize:(g + 1) * gsize], reverse=True)
+            gscore.append(members[0] + members[1] if gsize > 1 else members[0])
+        groups = sorted(range(n_group), key=lambda g: (-gscore[g], g))[:topk_group]
+        cand = [e for g in sorted(groups) for e in range(g * gsize, (g + 1) * gsize)]
+        chosen = sorted(cand, key=lambda e: (-key[e], e))[:top_k]
+        total = 0.0
+        for e in chosen:
+            total += s[e]
+        for i, e in enumerate(chosen):
+            ids[t, i] = e
+            w[t, i] = np.float32(routed_scale * s[e] / total)
+    return ids, w
+
+
+def prune_tail(ids: np.ndarray, w: np.ndarray, keep_max: int, min_w: float):
+    """Tail pruning with L2-quadrature rescaling of the kept weights.
+
+    Per token: the slots with w >= min_w are candidates; at most keep_max of
+    them are kept (the largest weights, ties to the lower slot), and at least
+    one (the slot of the largest weight).  alpha = sqrt(sum_all w^2 /
+    sum_kept w^2) from the fp32 weights in fp64; kept w becomes
+    fp32(w * alpha); dropped slots get id -1 and weight 0.  Slots keep their
+    positions.
+    """
+    ids = np.array(ids, dtype=np.int32)
+    w = np.array(w, dtype=np.float32)
+    n_tokens, top_k = ids.shape
+    if not 1 <= keep_max <= top_k:
+        raise ValueError("keep_max must be in 1..top_k")
+    for t in range(n_tokens):
+        wt = [float(v) for v in w[t]]
+        by_weight = sorted(range(top_k), key=lambda i: (-wt[i], i))
+        kept = [i for i in by_weight if wt[i] >= min_w][:keep_max]
+        if not kept:
+            kept = by_weight[:1]
+        all_sq = 0.0
+        for v in wt:
+            all_sq += v * v
+        kept_sq = 0.0
+        for i in sorted(kept):
+            kept_sq += wt[i] * wt[i]
+        alpha = math.sqrt(all_sq / kept_sq)
+        for i in range(top_k):
+            if i in kept:
+                w[t, i] = np.float32(wt[i] * alpha)
+            else:
+                ids[t, i] = -1
+                w[t, i] = 0.0
+    return ids, w
+
+
 # ----------------------------------------------------------------------------
 # Grouping (token-to-expert bucketing)
 # ----------------------------------------------------------------------------
@@ -229,19 +334,24 @@ def group(ids: np.ndarray, n_experts: int):
     """counts, exclusive offsets, stable permutation and its inverse.
 
     Two plain passes: count, then place each flat index f = t*k + i (in
-    ascending f) at the next free position of its expert.
+    ascending f) at the next free position of its expert.  Ids of -1 (slots
+    dropped by tail pruning) are skipped: perm has offsets[E] entries and
+    their inv_perm is -1.
     """
     flat = [int(v) for v in np.asarray(ids).reshape(-1)]
     counts = [0] * n_experts
     for e in flat:
-        counts[e] += 1
+        if e >= 0:
+            counts[e] += 1
     offsets = [0] * (n_experts + 1)
     for e in range(n_experts):
         offsets[e + 1] = offsets[e] + counts[e]
     fill = offsets[:n_experts]
-    perm = [0] * len(flat)
-    inv_perm = [0] * len(flat)
+    perm = [0] * offsets[n_experts]
+    inv_perm = [-1] * len(flat)
     for f, e in enumerate(flat):
+        if e < 0:
+            continue
         p = fill[e]
         perm[p] = f
         inv_perm[f] = p
@@ -271,13 +381,17 @@ def expert_ffn(xs: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray,
 
 
 def ffn(layer: dict, x: np.ndarray, act_type: str, ids: np.ndarray,
-        w: np.ndarray, tokens=None, out_rows=None, with_shared: bool = True):
+        w: np.ndarray, tokens=None, out_rows=None, with_shared: bool = True,
+        lazy_tau: float = 0.0):
     """MoE FFN output y (fp32) for ``tokens`` (default: all) and output
     features ``out_rows`` (default: all).
 
     y_t = e_shared(x_t) + sum_i w[t,i] e_{ids[t,i]}(x_t), accumulated in fp64,
     rounded to fp32 once.  Each routed expert's three matrices are decoded to
-    fp64 once; the tokens that chose it are found by scanning ``ids``.
+    fp64 once; the tokens that chose it are found by scanning ``ids``.  A slot
+    with id -1 (dropped by tail pruning) has no expert.  With lazy_tau > 0 a
+    routed expert whose gate output for a token has max_j |SiLU(g_j)| <
+    lazy_tau is left out of that token's sum (gate-first lazy skip).
     """
     hidden, inter = layer["hidden"], layer["inter"]
     ids = np.asarray(ids)
@@ -291,14 +405,19 @@ def ffn(layer: dict, x: np.ndarray, act_type: str, ids: np.ndarray,
     members = {}  # expert -> list of (row in xs, weight)
     for j, t in enumerate(tokens):
         for i in range(top_k):
-            members.setdefault(int(ids[t, i]), []).append((j, float(w[t, i])))
+            if int(ids[t, i]) >= 0:
+                members.setdefault(int(ids[t, i]), []).append((j, float(w[t, i])))
     for e in sorted(members):
         wg = decode_proj(layer["gate"], e, hidden)
         wu = decode_proj(layer["up"], e, hidden)
         wd = decode_proj(layer["down"], e, inter, out_rows)
         rows = [j for j, _ in members[e]]
         o = expert_ffn(xs[rows], wg, wu, wd)
+        if lazy_tau > 0.0:
+            gate_max = np.max(np.abs(silu(xs[rows] @ wg.T)), axis=1)
         for r, (j, wt) in enumerate(members[e]):
+            if lazy_tau > 0.0 and gate_max[r] < lazy_tau:
+                continue
             y[j] += wt * o[r]
 
     shared = layer.get("shared")
