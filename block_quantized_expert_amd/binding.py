@@ -28,7 +28,8 @@ EXPORTED = ["moe_route", "moe_route_hash", "moe_route_group", "moe_group_workspa
             "moe_ffn_down", "moe_ffn_forward_timed", "moe_forward_workspace_bytes",
             "moe_forward_single_kernel", "moe_forward_workspace_init", "moe_forward",
             "moe_forward_timed", "moe_forward_noalloc", "moe_status_string",
-            "moe_stream_read"]
+            "moe_stream_read", "moe_route_ex", "moe_route_group_ex", "moe_ffn_forward_ex",
+            "moe_forward_ex"]
 
 WEIGHT_TYPES = {"mxfp4": MOE_W_MXFP4, "fp8_e4m3_b128": MOE_W_FP8E4M3_B128}
 
@@ -41,6 +42,28 @@ class MoeError(RuntimeError):
 
 class MoeProj(ctypes.Structure):
     _fields_ = [("type", ctypes.c_int32), ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+
+
+class MoeOpts(ctypes.Structure):
+    _fields_ = [("n_group", ctypes.c_int32), ("topk_group", ctypes.c_int32),
+                ("sel_bias", ctypes.c_void_p), ("keep_max", ctypes.c_int32),
+                ("min_w", ctypes.c_float), ("lazy_tau", ctypes.c_float)]
+
+
+def make_opts(n_group=0, topk_group=0, sel_bias=None, keep_max=0, min_w=0.0, lazy_tau=0.0):
+    """A moe_opts; ``sel_bias`` is a device fp32 tensor [n_experts] or None
+    (the struct keeps a reference to it, so its memory stays valid while the
+    struct lives)."""
+    o = MoeOpts()
+    o.n_group, o.topk_group, o.keep_max = n_group, topk_group, keep_max
+    o.sel_bias = None if sel_bias is None else sel_bias.data_ptr()
+    o.min_w, o.lazy_tau = min_w, lazy_tau
+    o._sel_bias_tensor = sel_bias
+    return o
+
+
+def _opts_ref(opts):
+    return None if opts is None else ctypes.byref(opts)
 
 
 class MoeLayer(ctypes.Structure):
@@ -91,6 +114,16 @@ def lib() -> ctypes.CDLL:
         L.moe_forward_noalloc.argtypes = fwd[:13] + [P, P]
         for name in ("moe_forward_workspace_init", "moe_forward", "moe_forward_timed",
                      "moe_forward_noalloc"):
+            getattr(L, name).restype = ctypes.c_int
+        O = ctypes.POINTER(MoeOpts)
+        L.moe_route_ex.argtypes = [P, I, I, I, F, O, P, P, P]
+        L.moe_route_group_ex.argtypes = [P, I, I, I, F, O, P, P, P, P, P, P, P, P]
+        L.moe_ffn_forward_ex.argtypes = [ctypes.POINTER(MoeLayer), P, I, I, P, P, P, P, P, P, O,
+                                         P, S, P, P, P, P, P]
+        L.moe_forward_ex.argtypes = [ctypes.POINTER(MoeLayer), P, F, O, P, I, I, P, P, P, P, P,
+                                     P, P, P, S, P, P, P, P]
+        for name in ("moe_route_ex", "moe_route_group_ex", "moe_ffn_forward_ex",
+                     "moe_forward_ex"):
             getattr(L, name).restype = ctypes.c_int
         L.moe_stream_read.argtypes = [P, S, P, P]
         L.moe_stream_read.restype = ctypes.c_int
@@ -232,6 +265,32 @@ def moe_route_hash(token_ids, tid2eid, tid2w, n_experts, ids=None, w=None, dev_e
     return ids, w
 
 
+def moe_route_ex(logits, top_k, opts, routed_scale=1.5, stream=None):
+    n, e = logits.shape
+    dev = logits.device
+    ids = torch.empty((n, top_k), dtype=torch.int32, device=dev)
+    w = torch.empty((n, top_k), dtype=torch.float32, device=dev)
+    _check(lib().moe_route_ex(_ptr(logits), n, e, top_k, routed_scale, _opts_ref(opts), _ptr(ids),
+                              _ptr(w), _stream(stream)), "moe_route_ex")
+    return ids, w
+
+
+def moe_route_group_ex(logits, top_k, opts, routed_scale=1.5, dev_error=None, stream=None):
+    """Route with options and group.  Returns (ids, w, (counts, offsets, perm, inv_perm))."""
+    n, e = logits.shape
+    dev = logits.device
+    ids = torch.empty((n, top_k), dtype=torch.int32, device=dev)
+    w = torch.empty((n, top_k), dtype=torch.float32, device=dev)
+    g = (torch.empty(e, dtype=torch.int32, device=dev),
+         torch.empty(e + 1, dtype=torch.int32, device=dev),
+         torch.empty(n * top_k, dtype=torch.int32, device=dev),
+         torch.empty(n * top_k, dtype=torch.int32, device=dev))
+    _check(lib().moe_route_group_ex(_ptr(logits), n, e, top_k, routed_scale, _opts_ref(opts),
+                                    _ptr(ids), _ptr(w), *[_ptr(t) for t in g], _ptr(dev_error),
+                                    _stream(stream)), "moe_route_group_ex")
+    return ids, w, g
+
+
 def moe_group(ids, n_experts, out=None, dev_error=None, stream=None):
     """Returns (counts, offsets, perm, inv_perm)."""
     n, k = ids.shape
@@ -312,6 +371,24 @@ def moe_ffn_forward_timed(layer: Layer, x, w, grouping, events, y=None, workspac
     return y
 
 
+def moe_ffn_forward_ex(layer: Layer, x, w, grouping, opts, y=None, workspace=None, events=None,
+                       stream=None):
+    n = x.shape[0]
+    x_type = MOE_ACT_BF16 if x.dtype == torch.bfloat16 else MOE_ACT_F32
+    if y is None:
+        y = torch.empty((n, layer.hidden), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(layer.workspace_bytes(n), 1), dtype=torch.uint8,
+                                device=x.device)
+    counts, offsets, perm, inv_perm = grouping
+    evs = [None] * 4 if events is None else [None if e is None else e.handle for e in events]
+    _check(lib().moe_ffn_forward_ex(ctypes.byref(layer.c), _ptr(x), x_type, n, _ptr(w),
+                                    _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(inv_perm),
+                                    _ptr(y), _opts_ref(opts), _ptr(workspace), workspace.numel(),
+                                    _stream(stream), *evs), "moe_ffn_forward_ex")
+    return y
+
+
 def forward(layer: Layer, x, routing: dict, routed_scale=1.5, stream=None):
     """Route, group and run the FFN (all on the device).  Returns
     (y, ids, w, grouping)."""
@@ -387,4 +464,18 @@ def moe_forward_noalloc(layer: Layer, logits, x, routed_scale=1.5, buffers: Forw
     _check(lib().moe_forward_noalloc(ctypes.byref(layer.c), _ptr(logits), routed_scale, _ptr(x),
                                      x_type, n, *a[:7], a[9], _stream(stream)),
            "moe_forward_noalloc")
+    return buffers
+
+
+def moe_forward_ex(layer: Layer, logits, x, opts, routed_scale=1.5,
+                   buffers: ForwardBuffers = None, stream=None, events=None):
+    """moe_forward with a moe_opts.  Returns the ForwardBuffers."""
+    n = x.shape[0]
+    if buffers is None:
+        buffers = ForwardBuffers(layer, n, x.device, stream)
+    x_type = MOE_ACT_BF16 if x.dtype == torch.bfloat16 else MOE_ACT_F32
+    evs = [None, None] if events is None else [None if e is None else e.handle for e in events]
+    _check(lib().moe_forward_ex(ctypes.byref(layer.c), _ptr(logits), routed_scale,
+                                _opts_ref(opts), _ptr(x), x_type, n, *buffers.args(),
+                                _stream(stream), *evs), "moe_forward_ex")
     return buffers

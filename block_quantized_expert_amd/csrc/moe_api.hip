@@ -78,7 +78,18 @@ moe::FfnParams make_params(const moe_layer* L, const void* x, int x_type, int n_
   p.xq = reinterpret_cast<uint8_t*>(ws + plan.off_xq);
   p.xs = reinterpret_cast<uint8_t*>(ws + plan.off_xs);
   p.y = y;
+  p.lazy_tau = 0.0f;
+  p.gmax = reinterpret_cast<uint32_t*>(ws + plan.off_gmax);
+  p.gbuf = reinterpret_cast<float*>(ws + plan.off_gbuf);
   return p;
+}
+
+moe::RouteOpts route_opts(const moe::OptsPlan& o) {
+  return moe::RouteOpts{o.n_group, o.topk_group, o.bias, o.keep_max, o.min_w};
+}
+
+bool route_opts_active(const moe::OptsPlan& o, int top_k) {
+  return o.n_group > 1 || o.bias != nullptr || o.keep_max < top_k || o.min_w > 0.0f;
 }
 
 enum Stage { kGateUp = 1, kDown = 2, kBoth = 3 };
@@ -87,13 +98,17 @@ moe_status ffn_stages(int stages, const moe_layer* layer, const void* x, int x_t
                       int n_tokens, const float* topk_w, const int32_t* counts,
                       const int32_t* offsets, const int32_t* perm, const int32_t* inv_perm,
                       float* y, void* workspace, size_t workspace_bytes, hipStream_t stream,
-                      hipEvent_t const* events = nullptr) {
+                      hipEvent_t const* events = nullptr, const moe_opts* opts = nullptr) {
   moe::FfnPlan plan;
   moe_status s = moe::check_ffn(layer, x, x_type, n_tokens, topk_w, counts, offsets, perm,
                                 inv_perm, y, workspace, workspace_bytes, &plan);
-  if (s != MOE_OK || n_tokens == 0) return s;
-  const moe::FfnParams p = make_params(layer, x, x_type, n_tokens, topk_w, counts, offsets, perm,
-                                       inv_perm, y, workspace, plan);
+  if (s != MOE_OK) return s;
+  moe::OptsPlan o;
+  if ((s = moe::check_opts(opts, layer->n_experts, layer->top_k, &o)) != MOE_OK) return s;
+  if (n_tokens == 0) return MOE_OK;
+  moe::FfnParams p = make_params(layer, x, x_type, n_tokens, topk_w, counts, offsets, perm,
+                                 inv_perm, y, workspace, plan);
+  p.lazy_tau = o.lazy_tau;
   hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
   if (events)
     for (int i = 0; i < 4; ++i) ev[i] = events[i];
@@ -113,23 +128,32 @@ moe_status forward_impl(const moe_layer* layer, const float* logits, float route
                         float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
                         int32_t* inv_perm, float* y, void* workspace, size_t workspace_bytes,
                         int32_t* dev_error, hipStream_t stream, hipEvent_t start,
-                        hipEvent_t stop) {
+                        hipEvent_t stop, const moe_opts* opts = nullptr) {
   moe::ForwardPlan plan;
   moe_status s = moe::check_forward(layer, logits, routed_scale, x, x_type, n_tokens, topk_ids,
                                     topk_w, counts, offsets, perm, inv_perm, y, workspace,
                                     workspace_bytes, &plan);
   if (s != MOE_OK) return s;
+  moe::OptsPlan o;
+  if ((s = moe::check_opts(opts, layer->n_experts, layer->top_k, &o)) != MOE_OK) return s;
+  const moe::RouteOpts ro = route_opts(o);
   char* ws = static_cast<char*>(workspace);
   moe::FfnParams p{};
-  if (n_tokens > 0)
+  if (n_tokens > 0) {
     p = make_params(layer, x, x_type, n_tokens, topk_w, counts, offsets, perm, inv_perm, y,
                     ws + plan.off_ffn, plan.ffn);
-  const int steps = n_tokens > 0 ? moe::fused_decode_steps(p) : 0;
+    p.lazy_tau = o.lazy_tau;
+  }
+  // the lazy skip needs the gate outputs of every row before the up pass:
+  // the separate kernels
+  const int steps = n_tokens > 0 && o.lazy_tau == 0.0f ? moe::fused_decode_steps(p) : 0;
   if (steps > 0) {
     moe::FusedParams f{};
     f.p = p;
     f.logits = logits;
     f.routed_scale = routed_scale;
+    f.ropts = ro;
+    f.route_opts = route_opts_active(o, layer->top_k) ? 1 : 0;
     f.topk_ids = topk_ids;
     f.topk_w = topk_w;
     f.counts = counts;
@@ -151,8 +175,8 @@ moe_status forward_impl(const moe_layer* layer, const float* logits, float route
   }
   if (start && hipEventRecord(start, stream) != hipSuccess) return MOE_ERR_DEVICE;
   s = launched(moe::launch_route_group(logits, n_tokens, layer->n_experts, layer->top_k,
-                                       routed_scale, topk_ids, topk_w, counts, offsets, perm,
-                                       inv_perm, dev_error, stream));
+                                       routed_scale, ro, topk_ids, topk_w, counts, offsets,
+                                       perm, inv_perm, dev_error, stream));
   if (s != MOE_OK) return s;
   if (n_tokens > 0) {
     if ((s = launched(moe::launch_ffn_gate_up(p, stream, nullptr, nullptr))) != MOE_OK) return s;
@@ -197,14 +221,23 @@ moe_status device_scratch(hipStream_t stream, char** out) {
 
 extern "C" {
 
+moe_status moe_route_ex(const float* logits, int n_tokens, int n_experts, int top_k,
+                        float routed_scale, const moe_opts* opts, int32_t* topk_ids,
+                        float* topk_w, hipStream_t stream) {
+  moe_status s = moe::check_route(logits, n_tokens, n_experts, top_k, routed_scale, topk_ids,
+                                  topk_w);
+  if (s != MOE_OK) return s;
+  moe::OptsPlan o;
+  if ((s = moe::check_opts(opts, n_experts, top_k, &o)) != MOE_OK || n_tokens == 0) return s;
+  return launched(moe::launch_route(logits, n_tokens, n_experts, top_k, routed_scale,
+                                    route_opts(o), topk_ids, topk_w, stream));
+}
+
 moe_status moe_route(const float* logits, int n_tokens, int n_experts, int top_k,
                      float routed_scale, int32_t* topk_ids, float* topk_w,
                      hipStream_t stream) {
-  moe_status s = moe::check_route(logits, n_tokens, n_experts, top_k, routed_scale, topk_ids,
-                                  topk_w);
-  if (s != MOE_OK || n_tokens == 0) return s;
-  return launched(moe::launch_route(logits, n_tokens, n_experts, top_k, routed_scale, topk_ids,
-                                    topk_w, stream));
+  return moe_route_ex(logits, n_tokens, n_experts, top_k, routed_scale, nullptr, topk_ids,
+                      topk_w, stream);
 }
 
 moe_status moe_route_hash(const int32_t* token_ids, int n_tokens, const int32_t* tid2eid,
@@ -218,16 +251,26 @@ moe_status moe_route_hash(const int32_t* token_ids, int n_tokens, const int32_t*
                                          top_k, topk_ids, topk_w, dev_error, stream));
 }
 
+moe_status moe_route_group_ex(const float* logits, int n_tokens, int n_experts, int top_k,
+                              float routed_scale, const moe_opts* opts, int32_t* topk_ids,
+                              float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                              int32_t* inv_perm, int32_t* dev_error, hipStream_t stream) {
+  moe_status s = moe::check_route_group(logits, n_tokens, n_experts, top_k, routed_scale,
+                                        topk_ids, topk_w, counts, offsets, perm, inv_perm);
+  if (s != MOE_OK) return s;
+  moe::OptsPlan o;
+  if ((s = moe::check_opts(opts, n_experts, top_k, &o)) != MOE_OK) return s;
+  return launched(moe::launch_route_group(logits, n_tokens, n_experts, top_k, routed_scale,
+                                          route_opts(o), topk_ids, topk_w, counts, offsets,
+                                          perm, inv_perm, dev_error, stream));
+}
+
 moe_status moe_route_group(const float* logits, int n_tokens, int n_experts, int top_k,
                            float routed_scale, int32_t* topk_ids, float* topk_w, int32_t* counts,
                            int32_t* offsets, int32_t* perm, int32_t* inv_perm,
                            int32_t* dev_error, hipStream_t stream) {
-  moe_status s = moe::check_route_group(logits, n_tokens, n_experts, top_k, routed_scale,
-                                        topk_ids, topk_w, counts, offsets, perm, inv_perm);
-  if (s != MOE_OK) return s;
-  return launched(moe::launch_route_group(logits, n_tokens, n_experts, top_k, routed_scale,
-                                          topk_ids, topk_w, counts, offsets, perm, inv_perm,
-                                          dev_error, stream));
+  return moe_route_group_ex(logits, n_tokens, n_experts, top_k, routed_scale, nullptr, topk_ids,
+                            topk_w, counts, offsets, perm, inv_perm, dev_error, stream);
 }
 
 size_t moe_group_workspace_bytes(int n_tokens, int top_k, int n_experts) {
@@ -264,6 +307,18 @@ moe_status moe_ffn_forward(const moe_layer* layer, const void* x, int x_type, in
                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return ffn_stages(kBoth, layer, x, x_type, n_tokens, topk_w, counts, offsets, perm, inv_perm,
                     y, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_ffn_forward_ex(const moe_layer* layer, const void* x, int x_type, int n_tokens,
+                              const float* topk_w, const int32_t* counts, const int32_t* offsets,
+                              const int32_t* perm, const int32_t* inv_perm, float* y,
+                              const moe_opts* opts, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream, hipEvent_t gate_up_start,
+                              hipEvent_t gate_up_stop, hipEvent_t down_start,
+                              hipEvent_t down_stop) {
+  const hipEvent_t ev[4] = {gate_up_start, gate_up_stop, down_start, down_stop};
+  return ffn_stages(kBoth, layer, x, x_type, n_tokens, topk_w, counts, offsets, perm, inv_perm,
+                    y, workspace, workspace_bytes, stream, ev, opts);
 }
 
 moe_status moe_ffn_gate_up(const moe_layer* layer, const void* x, int x_type, int n_tokens,
@@ -337,6 +392,17 @@ moe_status moe_forward_timed(const moe_layer* layer, const float* logits, float 
   return forward_impl(layer, logits, routed_scale, x, x_type, n_tokens, topk_ids, topk_w, counts,
                       offsets, perm, inv_perm, y, workspace, workspace_bytes, dev_error, stream,
                       start, stop);
+}
+
+moe_status moe_forward_ex(const moe_layer* layer, const float* logits, float routed_scale,
+                          const moe_opts* opts, const void* x, int x_type, int n_tokens,
+                          int32_t* topk_ids, float* topk_w, int32_t* counts, int32_t* offsets,
+                          int32_t* perm, int32_t* inv_perm, float* y, void* workspace,
+                          size_t workspace_bytes, int32_t* dev_error, hipStream_t stream,
+                          hipEvent_t start, hipEvent_t stop) {
+  return forward_impl(layer, logits, routed_scale, x, x_type, n_tokens, topk_ids, topk_w, counts,
+                      offsets, perm, inv_perm, y, workspace, workspace_bytes, dev_error, stream,
+                      start, stop, opts);
 }
 
 moe_status moe_forward_noalloc(const moe_layer* layer, const float* logits, float routed_scale,

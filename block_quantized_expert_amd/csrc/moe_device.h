@@ -16,6 +16,21 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
+// Gate-first lazy skip: the largest |SiLU(g)| = |g / (1 + e^-g)| of four
+// gate values, and that maximum merged over the four lane groups (lanes l,
+// l^16, l^32, l^48: the 16 rows of a 16x16 MFMA tile's column l % 16).
+// Every lane of the wavefront must call silu_col_max.
+__device__ __forceinline__ float silu_abs_max4(f32x4 g) {
+  float m = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(g[r] / (1.0f + expf(-g[r]))));
+  return m;
+}
+__device__ __forceinline__ float silu_col_max(float m) {
+  m = fmaxf(m, __shfl_xor(m, 16));
+  return fmaxf(m, __shfl_xor(m, 32));
+}
+
 // UE8M0 byte u -> the fp32 number 2^(u-127) (u in 1..254).
 __device__ __forceinline__ float ue8m0_to_f32(uint32_t u) { return __uint_as_float(u << 23); }
 

@@ -363,6 +363,15 @@ __global__ __launch_bounds__(kThreads) void gate_up_kernel(FfnParams p, int x_st
           au[tb] += s_red[w][2 * tb + 1][lane];
         }
       }
+      if (p.lazy_tau > 0.0f && !shared) {
+        // the slots' largest |SiLU(g)| over this block's rows
+#pragma unroll
+        for (int tb = 0; tb < NBT; ++tb) {
+          const float mx = silu_col_max(silu_abs_max4(ag[tb]));
+          if (g == 0 && tb * 16 + r16 < it.m)
+            atomicMax(p.gmax + it.slot0 + tb * 16 + r16, __float_as_uint(mx));
+        }
+      }
 #pragma unroll
       for (int tb = 0; tb < NBT; ++tb) {
         const int n = tb * 16 + r16;
@@ -427,7 +436,17 @@ __device__ __forceinline__ int nth_active_expert(const FfnParams& p, int a, int 
 // its 2*S code vectors and its scale bytes (4*S contiguous bytes of each
 // row) leave as one burst, and it stages only its own quarter of the
 // activations in LDS.  The four partial sums meet in LDS for the SwiGLU.
-template <int S>
+//
+// MODE 0 runs gate and up together.  The gate-first lazy skip ("[RFC /
+// Benchmarks] Fitting 284B DeepSeek-V4-Flash in 57.61 GiB RAM", section 5)
+// splits the routed blocks over two launches: MODE 1 (routed blocks only)
+// computes g, keeps it in gbuf and merges each slot's largest |SiLU(g)| into
+// gmax; MODE 2 first reads the tile's slots from gmax and leaves at once,
+// before requesting any weight, when every one is below lazy_tau (so a
+// skipped expert's up rows are never read), else computes u and writes
+// h = SiLU(g) u, with h = 0 for the slots below the threshold; the shared
+// expert's blocks run gate and up in MODE 2.
+template <int S, int MODE>
 __global__ __launch_bounds__(kThreads) void gate_up_decode_kernel(FfnParams p, int a_bound,
                                                                   int m_max) {
   constexpr int kRow = S * 128 + 8;  // bf16 per staged token row (+8: other banks)
@@ -445,10 +464,24 @@ __global__ __launch_bounds__(kThreads) void gate_up_decode_kernel(FfnParams p, i
     e = nth_active_expert(p, a, lane);
     if (e < 0) return;  // the same on every wavefront: the block leaves whole
   } else {
+    if (MODE == 1) return;  // not launched: MODE 1 has the routed blocks only
     e = p.n_experts;
     rb = blk - routed_blocks;
   }
   const bool shared = e == p.n_experts;
+  // tokens of the tile; distinct ids per token keep m <= N (<= m_max), the
+  // clamp keeps repeated ids (outside the ABI's preconditions) inside the
+  // staged rows
+  const int m = uniform(min(shared ? p.n_tokens : p.counts[e], m_max));
+  const int slot0 = uniform(shared ? p.n_tokens * p.top_k : p.offsets[e]);
+  bool col_live = r16 < m;  // MODE 2: the column's slot passes the threshold
+  if (MODE == 2 && !shared) {
+    const float gm = __uint_as_float(p.gmax[slot0 + min(r16, m - 1)]);
+    col_live = col_live && gm >= p.lazy_tau;
+    if (__ballot(col_live) == 0) return;  // the same in every wavefront
+  }
+  const bool do_gate = MODE != 2 || shared;  // uniform
+  const bool do_up = MODE != 1;
   const int rows = shared ? p.shared_inter : p.inter;
   const int64_t cb = p.hidden / 2, sb = p.hidden / 32;
   const int64_t row = (shared ? 0 : (int64_t)e * rows) + rb * 16 + r16;
@@ -459,35 +492,38 @@ __global__ __launch_bounds__(kThreads) void gate_up_decode_kernel(FfnParams p, i
 
   // one burst: codes, then the 4*S scale bytes of each row as whole words
   u32x4 qg[S], qu[S];
-#pragma unroll
-  for (int j = 0; j < S; ++j) {
-    qg[j] = load16(gc + j * 64);
-    qu[j] = load16(uc + j * 64);
-  }
   uint32_t wg[S], wu[S];
+  if (do_gate) {
+#pragma unroll
+    for (int j = 0; j < S; ++j) qg[j] = load16(gc + j * 64);
+  }
+  if (do_up) {
+#pragma unroll
+    for (int j = 0; j < S; ++j) qu[j] = load16(uc + j * 64);
+  }
   if constexpr (S >= 4) {
 #pragma unroll
     for (int v = 0; v < S / 4; ++v) {
-      const u32x4 a4 = load16(gs + 16 * v), b4 = load16(us + 16 * v);
+      if (do_gate) {
+        const u32x4 a4 = load16(gs + 16 * v);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        wg[4 * v + i] = a4[i];
-        wu[4 * v + i] = b4[i];
+        for (int i = 0; i < 4; ++i) wg[4 * v + i] = a4[i];
+      }
+      if (do_up) {
+        const u32x4 b4 = load16(us + 16 * v);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wu[4 * v + i] = b4[i];
       }
     }
   } else {
 #pragma unroll
     for (int j = 0; j < S; ++j) {
-      wg[j] = reinterpret_cast<const uint32_t*>(gs)[j];
-      wu[j] = reinterpret_cast<const uint32_t*>(us)[j];
+      if (do_gate) wg[j] = reinterpret_cast<const uint32_t*>(gs)[j];
+      if (do_up) wu[j] = reinterpret_cast<const uint32_t*>(us)[j];
     }
   }
 
-  // tokens of the tile and this wavefront's quarter of their activations;
-  // distinct ids per token keep m <= N (<= m_max), the clamp keeps repeated
-  // ids (outside the ABI's preconditions) inside the staged rows
-  const int m = uniform(min(shared ? p.n_tokens : p.counts[e], m_max));
-  const int slot0 = uniform(shared ? p.n_tokens * p.top_k : p.offsets[e]);
+  // this wavefront's quarter of the tile's activations
   __bf16* s_xq = reinterpret_cast<__bf16*>(s_dyn) + (size_t)wave * m_max * kRow;
   for (int c = lane; c < m * 16 * S; c += kWave) {
     const int n = c / (16 * S);
@@ -511,12 +547,16 @@ __global__ __launch_bounds__(kThreads) void gate_up_decode_kernel(FfnParams p, i
 #pragma unroll
       for (int t = 0; t < 4; ++t) b[t] = as_bf16x8(u32x4{0, 0, 0, 0});
     }
-    const float sgv = ue8m0_to_f32((wg[j] >> (8 * g)) & 0xFF);
-    const float suv = ue8m0_to_f32((wu[j] >> (8 * g)) & 0xFF);
+    if (do_gate) {
+      const float sgv = ue8m0_to_f32((wg[j] >> (8 * g)) & 0xFF);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) ag = mfma_bf16(fp4x8_to_bf16(qg[j][t], sgv), b[t], ag);
+      for (int t = 0; t < 4; ++t) ag = mfma_bf16(fp4x8_to_bf16(qg[j][t], sgv), b[t], ag);
+    }
+    if (do_up) {
+      const float suv = ue8m0_to_f32((wu[j] >> (8 * g)) & 0xFF);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) au = mfma_bf16(fp4x8_to_bf16(qu[j][t], suv), b[t], au);
+      for (int t = 0; t < 4; ++t) au = mfma_bf16(fp4x8_to_bf16(qu[j][t], suv), b[t], au);
+    }
   }
 
   if (wave > 0) {
@@ -530,12 +570,24 @@ __global__ __launch_bounds__(kThreads) void gate_up_decode_kernel(FfnParams p, i
       ag += s_red[w][0][lane];
       au += s_red[w][1][lane];
     }
-    if (r16 < m) {
+    if (MODE == 1) {
+      // g of rows rb*16 + 4g .. +3 for the column's slot, and the slot's
+      // largest |SiLU(g)| over the block's 16 rows
+      const float mx = silu_col_max(silu_abs_max4(ag));
+      if (r16 < m) {
+        *reinterpret_cast<f32x4*>(p.gbuf + (int64_t)(slot0 + r16) * p.inter + rb * 16 + 4 * g) =
+            ag;
+        if (g == 0) atomicMax(p.gmax + slot0 + r16, __float_as_uint(mx));
+      }
+    } else if (r16 < m) {
+      if (MODE == 2 && !shared)
+        ag = *reinterpret_cast<const f32x4*>(p.gbuf + (int64_t)(slot0 + r16) * p.inter +
+                                             rb * 16 + 4 * g);
       bf16x4 hi, lo;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float gv = ag[r];
-        const float h = gv / (1.0f + expf(-gv)) * au[r];
+        const float h = col_live ? gv / (1.0f + expf(-gv)) * au[r] : 0.0f;
         __bf16 a, b;
         split_bf16(h, a, b);
         hi[r] = a;
@@ -551,7 +603,8 @@ __global__ __launch_bounds__(kThreads) void gate_up_decode_kernel(FfnParams p, i
 // ------------------------------------------------------- combine
 
 // y[t] = o_shared[t] + sum_i o[inv_perm[t*k + i]] (weights already applied),
-// in that fixed order; four features per thread.
+// in that fixed order, leaving out slots dropped by tail pruning or by the
+// lazy skip; four features per thread.
 __global__ __launch_bounds__(256) void combine_kernel(FfnParams p) {
   const int h4 = p.hidden / 4;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -564,7 +617,9 @@ __global__ __launch_bounds__(256) void combine_kernel(FfnParams p) {
                                           ((int64_t)p.n_tokens * p.top_k + t) * p.hidden + q);
   for (int j = 0; j < p.top_k; ++j) {
     const int pp = p.inv_perm[t * p.top_k + j];
-    if (pp >= 0) acc += *reinterpret_cast<const f32x4*>(p.obuf + (int64_t)pp * p.hidden + q);
+    // a slot the lazy skip drops contributes nothing
+    const bool live = pp >= 0 && (p.lazy_tau == 0.0f || __uint_as_float(p.gmax[pp]) >= p.lazy_tau);
+    if (live) acc += *reinterpret_cast<const f32x4*>(p.obuf + (int64_t)pp * p.hidden + q);
   }
   *reinterpret_cast<f32x4*>(p.y + t * p.hidden + q) = acc;
 }
@@ -636,6 +691,12 @@ __global__ __launch_bounds__(kSmallThreads) void down_combine_small_kernel(FfnPa
   const int fi = min(tid, nk - 1);
   const int my_slot = p.inv_perm[fi];
   const float my_w = p.topk_w[fi];
+  // lazy skip: slots whose gate stayed below the threshold are left out, and
+  // an expert none of whose slots passes is not active (its down rows are
+  // never read)
+  const bool lazy = p.lazy_tau > 0.0f;
+  const bool my_live =
+      my_slot >= 0 && (!lazy || __uint_as_float(p.gmax[my_slot]) >= p.lazy_tau);
   if (wave == 0) {
     const int nch = uniform((p.n_experts + kWave - 1) / kWave);
     int cnt[kMaxChunks], off[kMaxChunks];
@@ -652,7 +713,13 @@ __global__ __launch_bounds__(kSmallThreads) void down_combine_small_kernel(FfnPa
     int nact = 0;
 #pragma unroll
     for (int c = 0; c < kMaxChunks; ++c) {
-      const bool on = c < nch && c * kWave + lane < p.n_experts && cnt[c] > 0;
+      bool on = c < nch && c * kWave + lane < p.n_experts && cnt[c] > 0;
+      if (lazy && on) {
+        bool any = false;
+        for (int j = 0; j < cnt[c]; ++j)
+          any = any || __uint_as_float(p.gmax[off[c] + j]) >= p.lazy_tau;
+        on = any;
+      }
       const uint64_t m = __ballot(on);
       if (on) {
         const int a = nact + __popcll(m & ((1ull << lane) - 1ull));
@@ -679,7 +746,7 @@ __global__ __launch_bounds__(kSmallThreads) void down_combine_small_kernel(FfnPa
   }
   __syncthreads();
   const int A = s_nact, AR = s_nroute;
-  if (tid < nk && my_slot >= 0) {
+  if (tid < nk && my_live) {
     int lo = 0, hi = AR;  // active expert owning the slot
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
@@ -992,14 +1059,34 @@ hipError_t gate_up_decode_launch(const FfnParams& p, hipStream_t stream, hipEven
                                  hipEvent_t stop) {
   const int64_t nk = (int64_t)p.n_tokens * p.top_k;
   const int a_bound = (int)(nk < p.n_experts ? nk : p.n_experts);
-  const int blocks = a_bound * (p.inter / 16) + (p.has_shared ? p.shared_inter / 16 : 0);
+  const int routed = a_bound * (p.inter / 16);
+  const int blocks = routed + (p.has_shared ? p.shared_inter / 16 : 0);
   // every tile holds at most min(N, 16) tokens
   const int m_max = p.n_tokens < kDecodeMaxTokens ? p.n_tokens : kDecodeMaxTokens;
   const size_t lds = (size_t)kWaves * m_max * (S * 128 + 8) * 2;
-  static const hipError_t attr = allow_lds(gate_up_decode_kernel<S>);
-  if (attr != hipSuccess) return attr;
-  return launch(gate_up_decode_kernel<S>, dim3(blocks), dim3(kThreads), lds, stream, start, stop,
-                p, a_bound, m_max);
+  if (p.lazy_tau == 0.0f) {
+    static const hipError_t attr = allow_lds(gate_up_decode_kernel<S, 0>);
+    if (attr != hipSuccess) return attr;
+    return launch(gate_up_decode_kernel<S, 0>, dim3(blocks), dim3(kThreads), lds, stream, start,
+                  stop, p, a_bound, m_max);
+  }
+  // gate first: the routed gate rows, then the up rows of the experts some
+  // token keeps, and the shared expert
+  static const hipError_t attr1 = allow_lds(gate_up_decode_kernel<S, 1>);
+  static const hipError_t attr2 = allow_lds(gate_up_decode_kernel<S, 2>);
+  if (attr1 != hipSuccess) return attr1;
+  if (attr2 != hipSuccess) return attr2;
+  hipError_t e = launch(gate_up_decode_kernel<S, 1>, dim3(routed > 0 ? routed : 1),
+                        dim3(kThreads), lds, stream, start, nullptr, p, a_bound, m_max);
+  if (e != hipSuccess) return e;
+  return launch(gate_up_decode_kernel<S, 2>, dim3(blocks), dim3(kThreads), lds, stream, nullptr,
+                stop, p, a_bound, m_max);
+}
+
+// Zeroes n 32-bit words (the lazy skip's per-slot gate maxima).
+__global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t* __restrict__ v, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) v[i] = 0u;
 }
 
 // The decode kernel covers small batches of bf16 activations with MXFP4
@@ -1018,6 +1105,12 @@ bool gate_up_writes_h3(const FfnParams& p) { return !p.x_f32 && decode_steps(p) 
 
 hipError_t launch_ffn_gate_up(const FfnParams& p, hipStream_t stream, hipEvent_t start,
                               hipEvent_t stop) {
+  if (p.lazy_tau > 0.0f) {
+    const int64_t nk = (int64_t)p.n_tokens * p.top_k;
+    const hipError_t e = launch(zero_u32_kernel, dim3((unsigned)((nk + 255) / 256)), dim3(256), 0,
+                                stream, nullptr, nullptr, p.gmax, nk);
+    if (e != hipSuccess) return e;
+  }
   switch (decode_steps(p)) {
     case 1: return gate_up_decode_launch<1>(p, stream, start, stop);
     case 2: return gate_up_decode_launch<2>(p, stream, start, stop);

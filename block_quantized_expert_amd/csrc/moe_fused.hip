@@ -68,8 +68,11 @@ constexpr int kHRow = 136;                      // bf16 per staged h row (128 + 
 
 struct FusedSmem {
   unsigned long long epoch;  // this launch's barrier value (FusedSync::launch + 1)
-  int ids[MOE_MAX_TOP_K];   // routed experts in rank order
+  int ids[MOE_MAX_TOP_K];   // routed experts in rank order (-1: dropped by tail pruning)
   int act[kFSlots];         // expert of segment a (n_experts: shared), ascending
+  int nkept;                // routed segments: top_k, or the experts kept by pruning
+  float wa[kFSlots];        // routing options: the weight of segment a
+  float wslot[MOE_MAX_TOP_K];  // routing options: the weight of slot (rank) r
   int ok;
   double s[kFPer * kWave];  // sqrt(softplus(logit)) of every expert
   f32x4 gu_red[kQuads][3][2][4];  // gate/up sums of wavefronts 1-3 of a quad (token lanes)
@@ -172,20 +175,21 @@ __global__ __launch_bounds__(kFThreads) void decode_fused_kernel(FusedParams f) 
   const int slot = (quad + 3) & 3;  // quad's place in the gate/up item order
   const int g = lane >> 4, r16 = lane & 15;
   const int k = p.top_k;
-  const int nseg = k + p.has_shared;
   const int G = gridDim.x;
+  // routed segments (the kept experts), known once the routing is done
+  int kk = k, nseg = k + p.has_shared;
 
   // gate/up items: the shared expert's row blocks first, then segment a's
   const int rbr = p.inter >> 4;
   const int ns = p.has_shared ? p.shared_inter >> 4 : 0;
-  const int gu_items = ns + k * rbr;
+  int gu_items = ns + k * rbr;
   const int64_t cb = p.hidden / 2, sb = p.hidden / 32;
   u32x4 qg[S], qu[S];
   uint32_t wg[S], wu[S];
   // request the codes and scales of an item (this wavefront's quarter)
   auto issue = [&](int item) {
     const bool shared = item < ns;
-    const int a = uniform(shared ? k : (item - ns) / rbr);
+    const int a = uniform(shared ? kk : (item - ns) / rbr);
     const int rb = uniform(shared ? item : item - ns - a * rbr);
     const int e = shared ? 0 : uniform(sm.act[a]);
     const int64_t row = (shared ? 0 : (int64_t)e * p.inter) + rb * 16 + r16;
@@ -282,7 +286,46 @@ __global__ __launch_bounds__(kFThreads) void decode_fused_kernel(FusedParams f) 
     asm volatile("s_waitcnt vmcnt(0)" ::"v"(first) : "memory");
     issue_lds(blockIdx.x);
   }
-  if (wave == kRouteWave) {
+  if (f.route_opts) {
+    // groups, a selection bias or tail pruning: wavefront 0 routes with the
+    // options (the fp64 scores of its four experts per lane included) while
+    // wavefront 9 copies x into LDS
+    if (wave == kRouteWave) {
+      int id;
+      float wt;
+      route_token_opts<kFPer>(f.logits, p.n_experts, k, f.routed_scale, f.ropts, lane, id, wt);
+      const bool kept = lane < k && id >= 0;
+      const int nk = __popcll(__ballot(kept));
+      int below = 0;  // kept experts below this one: its segment
+      for (int j = 0; j < k; ++j) {
+        const int o = read_lane(id, j);
+        below += (o >= 0 && o < id) ? 1 : 0;
+      }
+      if (lane < k) {
+        sm.ids[lane] = id;
+        sm.wslot[lane] = wt;
+      }
+      if (kept) {
+        sm.act[below] = id;
+        sm.wa[below] = wt;
+      }
+      if (lane == 0) {
+        sm.nkept = nk;
+        if (p.has_shared) sm.act[nk] = p.n_experts;
+      }
+      if (blockIdx.x == 0 && lane < k) {
+        f.topk_ids[lane] = id;
+        f.inv_perm[lane] = kept ? below : -1;
+        if (kept) f.perm[below] = lane;
+      }
+    } else if (wave == 9) {
+      for (int i = 0; i < p.hidden / 512; ++i)
+        __builtin_amdgcn_global_load_lds(
+            static_cast<const __bf16*>(p.x) + i * 512 + lane * 8,
+            (__attribute__((address_space(3))) void*)(&sm.u.gu.x[i * 512]), 16, 0, 0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+  } else if (wave == kRouteWave) {
     uint32_t key[kFPer];
     load_keys<kFPer>(f.logits, p.n_experts, lane, key);
     // x goes straight from memory into LDS (lane l of copy i writes bytes
@@ -303,7 +346,10 @@ __global__ __launch_bounds__(kFThreads) void decode_fused_kernel(FusedParams f) 
       sm.ids[lane] = id;
       sm.act[below] = id;
     }
-    if (lane == 0 && p.has_shared) sm.act[k] = p.n_experts;
+    if (lane == 0) {
+      sm.nkept = k;
+      if (p.has_shared) sm.act[k] = p.n_experts;
+    }
     if (blockIdx.x == 0 && lane < k) {
       f.topk_ids[lane] = id;
       f.perm[below] = lane;
@@ -317,17 +363,20 @@ __global__ __launch_bounds__(kFThreads) void decode_fused_kernel(FusedParams f) 
     if (e < p.n_experts) sm.s[e] = gate_score((double)f.logits[e]);
   }
   __syncthreads();
+  kk = sm.nkept;
+  nseg = kk + p.has_shared;
+  gu_items = ns + kk * rbr;
   if (blockIdx.x == 0) {
     for (int e = threadIdx.x; e < p.n_experts; e += kFThreads) {
       int c = 0, off = 0;
       for (int j = 0; j < k; ++j) {
         c += sm.ids[j] == e ? 1 : 0;
-        off += sm.ids[j] < e ? 1 : 0;
+        off += (sm.ids[j] >= 0 && sm.ids[j] < e) ? 1 : 0;
       }
       f.counts[e] = c;
       f.offsets[e] = off;
     }
-    if (threadIdx.x == 0) f.offsets[p.n_experts] = k;
+    if (threadIdx.x == 0) f.offsets[p.n_experts] = kk;
   }
 
   const int ksteps = p.inter >> 7;  // 128-wide steps of the intermediate dimension
@@ -395,11 +444,18 @@ __global__ __launch_bounds__(kFThreads) void decode_fused_kernel(FusedParams f) 
         au += sm.gu_red[quad][w][1][g];
       }
       const bool shared = item < ns;
-      const int a = shared ? k : (item - ns) / rbr;
+      const int a = shared ? kk : (item - ns) / rbr;
       const int rb = shared ? item : item - ns - a * rbr;
-      double total = 0.0;
-      for (int i = 0; i < k; ++i) total += sm.s[sm.ids[i]];
-      const float wa = a == k ? 1.0f : routed_weight(sm.s[sm.act[a]], total, f.routed_scale);
+      float wa = 1.0f;
+      if (a != kk) {
+        if (f.route_opts) {
+          wa = sm.wa[a];
+        } else {
+          double total = 0.0;
+          for (int i = 0; i < k; ++i) total += sm.s[sm.ids[i]];
+          wa = routed_weight(sm.s[sm.act[a]], total, f.routed_scale);
+        }
+      }
       bf16x4 hi, lo;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -418,9 +474,13 @@ __global__ __launch_bounds__(kFThreads) void decode_fused_kernel(FusedParams f) 
   }
 
   if (blockIdx.x == 0 && wave == 0 && lane < k) {
-    double total = 0.0;
-    for (int i = 0; i < k; ++i) total += sm.s[sm.ids[i]];
-    f.topk_w[lane] = routed_weight(sm.s[sm.ids[lane]], total, f.routed_scale);
+    if (f.route_opts) {
+      f.topk_w[lane] = sm.wslot[lane];
+    } else {
+      double total = 0.0;
+      for (int i = 0; i < k; ++i) total += sm.s[sm.ids[i]];
+      f.topk_w[lane] = routed_weight(sm.s[sm.ids[lane]], total, f.routed_scale);
+    }
   }
 
   // ---- 3. grid barrier; the first row block's down codes requested meanwhile

@@ -384,7 +384,9 @@ __device__ __forceinline__ uint32_t split_e4m3x3(const float (&v)[2][4], float m
 
 // NBT = token blocks of the tile (ceil(m / 16)), a compile-time constant so
 // that a step's operand reads and MFMAs form one branch-free block.
-template <int WT, int TT, int NBT, bool SC, bool O32>
+// LAZY: the gate-first lazy skip is on (its gate maxima are merged into
+// gmax); a separate instantiation, so the plain kernels keep their registers.
+template <int WT, int TT, int NBT, bool SC, bool O32, bool LAZY>
 __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it, char* smem,
                                              int wave, int lane) {
   using F = Fmt<WT>;
@@ -663,6 +665,18 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
   // projection: the lane holds rows 4g .. 4g+3 of row block rb for token
   // column r16, and the four lanes of a token meet in two shuffles.
   const int64_t hs = p.h_stride;
+  if (LAZY && !shared) {
+    // gate-first lazy skip: each slot's largest |SiLU(g)| over the
+    // wavefront's 32 rows, merged into gmax (the combine leaves out the
+    // slots below the threshold)
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      const float mx =
+          silu_col_max(fmaxf(silu_abs_max4(acc[0][0][tb]), silu_abs_max4(acc[0][1][tb])));
+      const int n = tb * 16 + r16;
+      if (live && g == 0 && n < it.m) atomicMax(p.gmax + it.slot0 + n, __float_as_uint(mx));
+    }
+  }
 #pragma unroll
   for (int tb = 0; tb < TB; ++tb) {
     float v[2][4];
@@ -693,7 +707,7 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
   }
 }
 
-template <int WT, int TT, bool SC, bool O32>
+template <int WT, int TT, bool SC, bool O32, bool LAZY>
 __global__ __launch_bounds__(kGThreads, 2) void gemm_gate_up_kernel(FfnParams p, int seg_lo,
                                                                      int seg_hi) {
   extern __shared__ __align__(16) char smem[];
@@ -707,7 +721,7 @@ __global__ __launch_bounds__(kGThreads, 2) void gemm_gate_up_kernel(FfnParams p,
     if (item < 0) continue;
     const GItem it = find_item<TT, kGuRows, false>(p, seg_lo, seg_hi, s_pref, item);
     dispatch_nbt<TT / 16>((it.m + 15) >> 4, [&](auto nb) {
-      gate_up_item<WT, TT, decltype(nb)::value, SC, O32>(p, it, smem, wave, lane);
+      gate_up_item<WT, TT, decltype(nb)::value, SC, O32, LAZY>(p, it, smem, wave, lane);
     });
     __syncthreads();  // the LDS tiles are reused by the next item
   }
@@ -1250,14 +1264,22 @@ int grid_for(int64_t items) {
   return (int)(items < kGemmGrid ? (items > 0 ? items : 1) : kGemmGrid);
 }
 
+template <int WT, int TT, bool SC, bool O32, bool LAZY>
+hipError_t gate_up_range_as(const FfnParams& p, int seg_lo, int seg_hi, hipStream_t stream,
+                            hipEvent_t start, hipEvent_t stop) {
+  static const hipError_t attr = allow_lds(gemm_gate_up_kernel<WT, TT, SC, O32, LAZY>);
+  if (attr != hipSuccess) return attr;
+  const int grid = grid_for(items_bound(p, seg_lo, seg_hi, TT, kGuRows, false));
+  return launch(gemm_gate_up_kernel<WT, TT, SC, O32, LAZY>, dim3(grid), dim3(kGThreads),
+                (size_t)kGemmLds, stream, start, stop, p, seg_lo, seg_hi);
+}
+
 template <int WT, int TT, bool SC, bool O32>
 hipError_t gate_up_range(const FfnParams& p, int seg_lo, int seg_hi, hipStream_t stream,
                          hipEvent_t start, hipEvent_t stop) {
-  static const hipError_t attr = allow_lds(gemm_gate_up_kernel<WT, TT, SC, O32>);
-  if (attr != hipSuccess) return attr;
-  const int grid = grid_for(items_bound(p, seg_lo, seg_hi, TT, kGuRows, false));
-  return launch(gemm_gate_up_kernel<WT, TT, SC, O32>, dim3(grid), dim3(kGThreads),
-                (size_t)kGemmLds, stream, start, stop, p, seg_lo, seg_hi);
+  if (p.lazy_tau > 0.0f)
+    return gate_up_range_as<WT, TT, SC, O32, true>(p, seg_lo, seg_hi, stream, start, stop);
+  return gate_up_range_as<WT, TT, SC, O32, false>(p, seg_lo, seg_hi, stream, start, stop);
 }
 
 template <int WT, bool SC>

@@ -120,7 +120,41 @@ moe_status plan_ffn(const moe_layer* layer, int n_tokens, FfnPlan* plan) {
   plan->off_obuf = h_area;
   plan->off_xq = h_area + o_bytes;
   plan->off_xs = plan->off_xq + xq_bytes;
-  plan->total = plan->off_xs + xs_bytes;
+  const int64_t nk = n * layer->top_k;
+  const size_t gmax_bytes = align_up((size_t)nk * 4u, 256);
+  const size_t gbuf_bytes =
+      n <= kGateFirstMaxTokens ? align_up((size_t)nk * layer->inter * 4u, 256) : 0;
+  plan->off_gmax = plan->off_xs + xs_bytes;
+  plan->off_gbuf = plan->off_gmax + gmax_bytes;
+  plan->total = plan->off_gbuf + gbuf_bytes;
+  return MOE_OK;
+}
+
+moe_status check_opts(const moe_opts* opts, int n_experts, int top_k, OptsPlan* out) {
+  out->n_group = 1;
+  out->topk_group = 1;
+  out->bias = nullptr;
+  out->keep_max = top_k;
+  out->min_w = 0.0f;
+  out->lazy_tau = 0.0f;
+  if (opts == nullptr) return MOE_OK;
+  const int ng = opts->n_group == 0 ? 1 : opts->n_group;
+  if (ng < 1 || ng > 64 || n_experts % ng != 0) return MOE_ERR_INVALID;
+  const int tg = opts->topk_group == 0 ? ng : opts->topk_group;
+  if (tg < 1 || tg > ng) return MOE_ERR_INVALID;
+  if ((int64_t)tg * (n_experts / ng) < top_k) return MOE_ERR_INVALID;
+  if (opts->sel_bias != nullptr && (reinterpret_cast<uintptr_t>(opts->sel_bias) & 3u) != 0)
+    return MOE_ERR_INVALID;
+  const int km = opts->keep_max == 0 ? top_k : opts->keep_max;
+  if (km < 1 || km > top_k) return MOE_ERR_INVALID;
+  if (!isfinite(opts->min_w) || opts->min_w < 0.0f) return MOE_ERR_INVALID;
+  if (!isfinite(opts->lazy_tau) || opts->lazy_tau < 0.0f) return MOE_ERR_INVALID;
+  out->n_group = ng;
+  out->topk_group = ng == 1 ? 1 : tg;
+  out->bias = opts->sel_bias;
+  out->keep_max = km;
+  out->min_w = opts->min_w;
+  out->lazy_tau = opts->lazy_tau;
   return MOE_OK;
 }
 

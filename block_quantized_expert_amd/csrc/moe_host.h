@@ -23,6 +23,14 @@ namespace moe {
 //                path with bf16 x: h as three E4M3 parts
 //                u8 [slots][h_stride/128][3][128] and their scale bytes
 //                u8 [slots][h_stride/32][4]
+//   gmax       : u32 [n_tokens*top_k]      gate-first lazy skip: the largest
+//                                         |SiLU(g)| of each routed slot (fp32
+//                                         bits)
+//   gbuf       : fp32 [n_tokens*top_k][inter]  gate outputs kept between the
+//                                         gate and up passes of the small-batch
+//                                         lazy path (batches of up to
+//                                         kGateFirstMaxTokens tokens; else
+//                                         empty)
 // A slot is one (token, routed expert) pair in grouped order
 // (p in [0, n_tokens*top_k)) or, for the shared expert, n_tokens*top_k + t.
 struct FfnPlan {
@@ -34,8 +42,26 @@ struct FfnPlan {
   size_t off_xq;
   size_t off_xs;
   size_t off_h3s;
+  size_t off_gmax;
+  size_t off_gbuf;
   size_t total;
 };
+
+// Batches up to this many tokens keep the gate outputs for a gate-first pass.
+constexpr int kGateFirstMaxTokens = 16;
+
+// moe_opts checked and with its defaults filled in.
+struct OptsPlan {
+  int n_group;
+  int topk_group;
+  const float* bias;
+  int keep_max;
+  float min_w;
+  float lazy_tau;
+};
+// opts may be NULL (no options); the layer's n_experts and top_k, or a
+// router's, bound the group and pruning parameters.
+moe_status check_opts(const moe_opts* opts, int n_experts, int top_k, OptsPlan* out);
 
 moe_status check_route_group(const float* logits, int n_tokens, int n_experts, int top_k,
                              float routed_scale, const int32_t* ids, const float* w,

@@ -44,6 +44,26 @@ struct FfnParams {
   uint8_t* h3s;
   float* obuf;  // [slots][hidden] weighted per-slot outputs
   float* y;     // [n_tokens][hidden]
+  // gate-first lazy skip: a routed slot whose gate output has
+  // max_j |SiLU(g_j)| < lazy_tau contributes nothing (lazy_tau 0: off).
+  // gmax [n_tokens*top_k] holds that maximum per slot (fp32 bits, zeroed
+  // before the gate/up pass); gbuf [n_tokens*top_k][inter] the gate outputs
+  // of the small-batch gate-first path
+  float lazy_tau;
+  uint32_t* gmax;
+  float* gbuf;
+};
+
+// Options of the learned router beyond plain top-k (moe_opts of the C ABI,
+// checked on the host): expert groups with a selection-only bias, and tail
+// pruning of the chosen experts.  plain(top_k) asks for neither.
+struct RouteOpts {
+  int n_group;        // >= 1; 1 = one group
+  int topk_group;     // 1..n_group
+  const float* bias;  // nullable, [n_experts]
+  int keep_max;       // 1..top_k
+  float min_w;        // >= 0
+  static RouteOpts plain(int top_k) { return RouteOpts{1, 1, nullptr, top_k, 0.0f}; }
 };
 
 // Synchronisation words of the fused single-token decode (in the caller's
@@ -66,6 +86,8 @@ struct FusedParams {
   FfnParams p;
   const float* logits;
   float routed_scale;
+  RouteOpts ropts;
+  int route_opts;  // 0: plain top-k on the logits; 1: ropts applies
   int32_t* topk_ids;
   float* topk_w;
   int32_t* counts;
@@ -81,7 +103,8 @@ struct FusedParams {
 };
 
 hipError_t launch_route(const float* logits, int n_tokens, int n_experts, int top_k,
-                        float routed_scale, int32_t* ids, float* w, hipStream_t stream);
+                        float routed_scale, const RouteOpts& opts, int32_t* ids, float* w,
+                        hipStream_t stream);
 hipError_t launch_route_hash(const int32_t* token_ids, int n_tokens, const int32_t* tid2eid,
                              const float* tid2w, int vocab, int n_experts, int top_k,
                              int32_t* ids, float* w, int32_t* dev_error, hipStream_t stream);
@@ -89,9 +112,9 @@ hipError_t launch_group(const int32_t* ids, int n_tokens, int top_k, int n_exper
                         int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
                         int32_t* dev_error, hipStream_t stream);
 hipError_t launch_route_group(const float* logits, int n_tokens, int n_experts, int top_k,
-                              float routed_scale, int32_t* ids, float* w, int32_t* counts,
-                              int32_t* offsets, int32_t* perm, int32_t* inv_perm,
-                              int32_t* dev_error, hipStream_t stream);
+                              float routed_scale, const RouteOpts& opts, int32_t* ids, float* w,
+                              int32_t* counts, int32_t* offsets, int32_t* perm,
+                              int32_t* inv_perm, int32_t* dev_error, hipStream_t stream);
 // start/stop may be null; when given they record the kernel's own start and
 // end times (taken from its dispatch, no extra packets on the stream)
 hipError_t launch_ffn_gate_up(const FfnParams& p, hipStream_t stream, hipEvent_t start,

@@ -12,6 +12,7 @@
 #include <math.h>
 
 #include "moe_device.h"
+#include "moe_kernels.h"
 
 namespace moe {
 namespace {
@@ -148,6 +149,221 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, int n
   uint32_t key[PER];
   load_keys<PER>(row, n_experts, lane, key);
   route_keys<PER>(key, top_k, routed_scale, lane, out_id, out_w);
+}
+
+// ------------------------------------------------------------ routing options
+
+__device__ __forceinline__ bool opts_select_on_logits(const RouteOpts& o) {
+  return o.n_group <= 1 && o.bias == nullptr;
+}
+__device__ __forceinline__ bool opts_prune(const RouteOpts& o, int top_k) {
+  return o.keep_max < top_k || o.min_w > 0.0f;
+}
+
+// A double as an unsigned 64-bit key with the same order; -0 is made +0 and
+// every key is at least 1 (0 marks padding and removed entries).
+__device__ __forceinline__ uint64_t order_key64(double v) {
+  uint64_t b = (uint64_t)__double_as_longlong(v);
+  if (b == 0x8000000000000000ull) b = 0ull;
+  const uint64_t k = (b & 0x8000000000000000ull) ? ~b : (b | 0x8000000000000000ull);
+  return k > 1ull ? k : 1ull;
+}
+
+__device__ __forceinline__ double key_value64(uint64_t k) {
+  return __longlong_as_double(
+      (long long)((k & 0x8000000000000000ull) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k));
+}
+
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Maximum of a 64-bit value over the wavefront, in every lane.
+__device__ __forceinline__ uint64_t wave_max64(uint64_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const uint64_t o = shfl_xor64(v, m);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ double read_lane_f64(double v, int l) {
+  const long long b = __double_as_longlong(v);
+  const uint32_t lo = (uint32_t)read_lane((int)(uint32_t)b, l);
+  const uint32_t hi = (uint32_t)read_lane((int)(uint32_t)(b >> 32), l);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+__device__ __forceinline__ float read_lane_f32(float v, int l) {
+  return __int_as_float(read_lane(__float_as_int(v), l));
+}
+
+// route_select on 64-bit keys.
+template <int PER>
+__device__ __forceinline__ void route_select64(uint64_t (&key)[PER], int top_k, int lane,
+                                               int& out_id) {
+  out_id = -1;
+  for (int r = 0; r < top_k; ++r) {
+    uint64_t m = key[0];
+#pragma unroll
+    for (int j = 1; j < PER; ++j) m = key[j] > m ? key[j] : m;
+    const uint64_t top = wave_max64(m);
+    int e = -1;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const uint64_t b = __ballot(key[j] == top);
+      if (e < 0 && b != 0) e = j * kWave + __builtin_ctzll(b);
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      if (e == j * kWave + lane) key[j] = 0ull;
+    if (lane == r) out_id = e;
+  }
+}
+
+// Group-limited top-k with a selection-only bias ("Deep-Dive Mathematical &
+// Kernel Guide", section 1: SQRT_SOFTPLUS with expert group top-k selection;
+// the pages give no group parameters, so the groups are contiguous runs of
+// n_experts / n_group experts scored by the sum of their two largest keys).
+// Every expert's score s = sqrt(softplus(l)) is taken in fp64, its key is
+// s + bias; the topk_group groups of largest score are kept (ties to the
+// lower group), and the top_k largest keys among their experts are chosen
+// (ties to the lower expert).  Lane r < top_k returns the expert of rank r
+// and its weight routed_scale * s_r / sum of the chosen s (unbiased).
+template <int PER>
+__device__ void route_token_grouped(const float* __restrict__ row, int n_experts, int top_k,
+                                    float routed_scale, const RouteOpts& o, int lane,
+                                    int& out_id, float& out_w) {
+  float v[PER], bv[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) v[j] = row[min(j * kWave + lane, n_experts - 1)];
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+    bv[j] = o.bias ? o.bias[min(j * kWave + lane, n_experts - 1)] : 0.0f;
+  double s[PER];
+  uint64_t key[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const bool live = j * kWave + lane < n_experts;
+    s[j] = live ? gate_score((double)v[j]) : 0.0;
+    key[j] = live ? order_key64(s[j] + (double)bv[j]) : 0ull;
+  }
+  if (o.n_group > 1) {
+    const int gsize = n_experts / o.n_group;
+    uint64_t gkey = 0ull;  // lane g: the score key of group g
+    for (int g = 0; g < o.n_group; ++g) {
+      const int lo = g * gsize, hi = lo + gsize;
+      uint64_t m = 0ull;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int e = j * kWave + lane;
+        if (e >= lo && e < hi) m = key[j] > m ? key[j] : m;
+      }
+      const uint64_t top1 = wave_max64(m);
+      double score = key_value64(top1);
+      if (gsize > 1) {
+        // the second largest: the largest left once the lowest member
+        // holding top1 is set aside
+        int first = -1;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+          const int e = j * kWave + lane;
+          const uint64_t b = __ballot(e >= lo && e < hi && key[j] == top1);
+          if (first < 0 && b != 0) first = j * kWave + __builtin_ctzll(b);
+        }
+        uint64_t m2 = 0ull;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+          const int e = j * kWave + lane;
+          if (e >= lo && e < hi && e != first) m2 = key[j] > m2 ? key[j] : m2;
+        }
+        score = score + key_value64(wave_max64(m2));
+      }
+      if (lane == g) gkey = order_key64(score);
+    }
+    uint64_t chosen = 0ull;  // bit g: group g kept
+    for (int r = 0; r < o.topk_group; ++r) {
+      const uint64_t top = wave_max64(gkey);
+      const int g = __builtin_ctzll(__ballot(lane < o.n_group && gkey == top));
+      chosen |= 1ull << g;
+      if (lane == g) gkey = 0ull;
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int e = j * kWave + lane;
+      if (e < n_experts && !((chosen >> (e / gsize)) & 1ull)) key[j] = 0ull;
+    }
+  }
+  route_select64<PER>(key, top_k, lane, out_id);
+  // the unbiased score of the expert of each rank, from the lane that holds it
+  double my_s = 0.0;
+  for (int r = 0; r < top_k; ++r) {
+    const int e = read_lane(out_id, r);
+    const int jj = e / kWave;
+    double sv = s[0];
+#pragma unroll
+    for (int j = 1; j < PER; ++j) sv = jj == j ? s[j] : sv;
+    const double val = read_lane_f64(sv, e % kWave);
+    if (lane == r) my_s = val;
+  }
+  double total = 0.0;
+  for (int i = 0; i < top_k; ++i) total += read_lane_f64(my_s, i);
+  out_w = lane < top_k ? routed_weight(my_s, total, routed_scale) : 0.0f;
+}
+
+// Tail pruning with L2-quadrature rescaling ("Deep-Dive Mathematical &
+// Kernel Guide", section 3.2 item 3; "[RFC / Benchmarks] Fitting 284B
+// DeepSeek-V4-Flash in 57.61 GiB RAM", section 5) of one token's routed
+// experts, lane r < top_k holding slot r: the slots whose weight is not
+// below min_w are candidates, at most keep_max of them are kept (the largest
+// weights, ties to the lower slot) and at least one (the largest weight);
+// kept weights are multiplied by alpha = sqrt(sum_all w^2 / sum_kept w^2)
+// (fp64 from the fp32 weights, sums in slot order), dropped slots become
+// id -1 with weight 0.
+__device__ void prune_slots(int top_k, int keep_max, float min_w, int lane, int& id, float& w) {
+  const float wv = lane < top_k ? w : -1.0f;
+  int better = 0, cbetter = 0;
+  for (int i = 0; i < top_k; ++i) {
+    const float wi = read_lane_f32(w, i);
+    const bool beats = wi > wv || (wi == wv && i < lane);
+    better += beats ? 1 : 0;
+    cbetter += (beats && wi >= min_w) ? 1 : 0;
+  }
+  bool kept = lane < top_k && wv >= min_w && cbetter < keep_max;
+  if (__ballot(kept) == 0) kept = lane < top_k && better == 0;
+  const uint64_t km = __ballot(kept);
+  double all_sq = 0.0, kept_sq = 0.0;
+  for (int i = 0; i < top_k; ++i) {
+    const double wi = (double)read_lane_f32(w, i);
+    all_sq += wi * wi;
+    if ((km >> i) & 1ull) kept_sq += wi * wi;
+  }
+  const double alpha = sqrt(all_sq / kept_sq);
+  if (lane < top_k) {
+    if (kept) {
+      w = (float)((double)w * alpha);
+    } else {
+      id = -1;
+      w = 0.0f;
+    }
+  }
+}
+
+// One token's routing with options: plain top-k on the logits, or the
+// group-limited top-k with the selection-only bias; then tail pruning when
+// asked.  Lane r < top_k returns slot r's expert (-1 when pruned) and weight.
+template <int PER>
+__device__ void route_token_opts(const float* __restrict__ row, int n_experts, int top_k,
+                                 float routed_scale, const RouteOpts& o, int lane, int& out_id,
+                                 float& out_w) {
+  if (opts_select_on_logits(o))
+    route_token<PER>(row, n_experts, top_k, routed_scale, lane, out_id, out_w);
+  else
+    route_token_grouped<PER>(row, n_experts, top_k, routed_scale, o, lane, out_id, out_w);
+  if (opts_prune(o, top_k)) prune_slots(top_k, o.keep_max, o.min_w, lane, out_id, out_w);
 }
 
 }  // namespace

@@ -37,7 +37,7 @@ constexpr int kGroupMaxBlocks = 64;
 template <int PER>
 __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits,
                                                          int n_tokens, int n_experts, int top_k,
-                                                         float routed_scale,
+                                                         float routed_scale, RouteOpts opts,
                                                          int32_t* __restrict__ ids,
                                                          float* __restrict__ w) {
   const int lane = threadIdx.x & 63;
@@ -45,7 +45,8 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
   if (t >= n_tokens) return;  // the whole wavefront leaves together
   int id;
   float wt;
-  route_token<PER>(logits + (size_t)t * n_experts, n_experts, top_k, routed_scale, lane, id, wt);
+  route_token_opts<PER>(logits + (size_t)t * n_experts, n_experts, top_k, routed_scale, opts,
+                        lane, id, wt);
   if (lane < top_k) {
     ids[(size_t)t * top_k + lane] = id;
     w[(size_t)t * top_k + lane] = wt;
@@ -156,7 +157,7 @@ __device__ void group_block(const int32_t* ids, int nk, int blk_lo, int blk_hi, 
         const int e = ev[j];
         if (e >= 0 && e < n_experts)
           atomicAdd(g < blk_lo ? &sh.s_pre[e] : &sh.s_post[e], 1);
-        else
+        else if (e != -1)  // -1: a slot dropped by tail pruning, no expert
           bad = 1;
       }
     }
@@ -175,7 +176,7 @@ __device__ void group_block(const int32_t* ids, int nk, int blk_lo, int blk_hi, 
         const int e = ev[j];
         if (e >= 0 && e < n_experts)
           atomicAdd(&sh.s_base[wave][e], 1);
-        else
+        else if (e != -1)
           bad = 1;
       }
     }
@@ -271,18 +272,22 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(
 template <int PER, int TPW>
 __global__ __launch_bounds__(kGroupThreads) void route_group_kernel(
     const float* __restrict__ logits, int n_tokens, int n_experts, int top_k, float routed_scale,
-    int32_t* __restrict__ ids, float* __restrict__ w, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
-    int32_t* __restrict__ dev_error) {
+    RouteOpts opts, int32_t* __restrict__ ids, float* __restrict__ w,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+    int32_t* __restrict__ inv_perm, int32_t* __restrict__ dev_error) {
   __shared__ GroupShared sh;
   __shared__ int32_t s_ids[kFusedMaxFlat];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  const bool on_logits = opts_select_on_logits(opts);
+  const bool prune = opts_prune(opts, top_k);
   uint32_t key[TPW][PER];
+  if (on_logits) {
 #pragma unroll
-  for (int i = 0; i < TPW; ++i) {
-    const int t = min(wave + kGroupWaves * i, n_tokens - 1);  // past the end: a repeat, unused
-    load_keys<PER>(logits + (size_t)t * n_experts, n_experts, lane, key[i]);
+    for (int i = 0; i < TPW; ++i) {
+      const int t = min(wave + kGroupWaves * i, n_tokens - 1);  // past the end: a repeat, unused
+      load_keys<PER>(logits + (size_t)t * n_experts, n_experts, lane, key[i]);
+    }
   }
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
@@ -290,7 +295,12 @@ __global__ __launch_bounds__(kGroupThreads) void route_group_kernel(
     if (t < n_tokens) {
       int id;
       float wt;
-      route_keys<PER>(key[i], top_k, routed_scale, lane, id, wt);
+      if (on_logits)
+        route_keys<PER>(key[i], top_k, routed_scale, lane, id, wt);
+      else
+        route_token_grouped<PER>(logits + (size_t)t * n_experts, n_experts, top_k, routed_scale,
+                                 opts, lane, id, wt);
+      if (prune) prune_slots(top_k, opts.keep_max, opts.min_w, lane, id, wt);
       if (lane < top_k) {
         ids[t * top_k + lane] = id;
         w[t * top_k + lane] = wt;
@@ -309,8 +319,9 @@ __global__ __launch_bounds__(kGroupThreads) void route_group_kernel(
 template <int PER>
 __global__ __launch_bounds__(kWave) void route_group_wave_kernel(
     const float* __restrict__ logits, int n_tokens, int n_experts, int top_k, float routed_scale,
-    int32_t* __restrict__ ids, float* __restrict__ w, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm) {
+    RouteOpts opts, int32_t* __restrict__ ids, float* __restrict__ w,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+    int32_t* __restrict__ inv_perm) {
   __shared__ int s_count[MOE_MAX_EXPERTS];
   __shared__ int s_ids[kWave];
   const int lane = threadIdx.x;
@@ -318,8 +329,8 @@ __global__ __launch_bounds__(kWave) void route_group_wave_kernel(
   for (int t = 0; t < n_tokens; ++t) {
     int id;
     float wt;
-    route_token<PER>(logits + (size_t)t * n_experts, n_experts, top_k, routed_scale, lane, id,
-                     wt);
+    route_token_opts<PER>(logits + (size_t)t * n_experts, n_experts, top_k, routed_scale, opts,
+                          lane, id, wt);
     if (lane < top_k) {
       ids[t * top_k + lane] = id;
       w[t * top_k + lane] = wt;
@@ -363,6 +374,8 @@ __global__ __launch_bounds__(kWave) void route_group_wave_kernel(
     const int p = s_count[e] + __popcll(same & lanemask_lt(lane));
     perm[p] = lane;
     inv_perm[lane] = p;
+  } else if (lane < nk) {
+    inv_perm[lane] = -1;  // a slot dropped by tail pruning
   }
 }
 
@@ -371,12 +384,13 @@ int per_lane(int n_experts) { return (n_experts + kWave - 1) / kWave; }
 }  // namespace
 
 hipError_t launch_route(const float* logits, int n_tokens, int n_experts, int top_k,
-                        float routed_scale, int32_t* ids, float* w, hipStream_t stream) {
+                        float routed_scale, const RouteOpts& opts, int32_t* ids, float* w,
+                        hipStream_t stream) {
   const dim3 grid((n_tokens + 3) / 4), block(256);
   const int per = per_lane(n_experts);
 #define MOE_ROUTE(P)                                                                   \
   route_topk_kernel<P><<<grid, block, 0, stream>>>(logits, n_tokens, n_experts, top_k, \
-                                                   routed_scale, ids, w)
+                                                   routed_scale, opts, ids, w)
   if (per <= 1)
     MOE_ROUTE(1);
   else if (per <= 2)
@@ -417,14 +431,15 @@ hipError_t launch_group(const int32_t* ids, int n_tokens, int top_k, int n_exper
 }
 
 hipError_t launch_route_group(const float* logits, int n_tokens, int n_experts, int top_k,
-                              float routed_scale, int32_t* ids, float* w, int32_t* counts,
-                              int32_t* offsets, int32_t* perm, int32_t* inv_perm,
-                              int32_t* dev_error, hipStream_t stream) {
+                              float routed_scale, const RouteOpts& opts, int32_t* ids, float* w,
+                              int32_t* counts, int32_t* offsets, int32_t* perm,
+                              int32_t* inv_perm, int32_t* dev_error, hipStream_t stream) {
   // one workgroup routes at most four tokens per wavefront; larger batches
   // route on a wavefront per token and group in a second kernel (one
   // workgroup routing 512 tokens took 133 us, the two kernels ~15)
   if (n_tokens > kFusedMaxTokens || (int64_t)n_tokens * top_k > kFusedMaxFlat) {
-    hipError_t e = launch_route(logits, n_tokens, n_experts, top_k, routed_scale, ids, w, stream);
+    hipError_t e =
+        launch_route(logits, n_tokens, n_experts, top_k, routed_scale, opts, ids, w, stream);
     if (e != hipSuccess) return e;
     return launch_group(ids, n_tokens, top_k, n_experts, counts, offsets, perm, inv_perm,
                         dev_error, stream);
@@ -433,8 +448,8 @@ hipError_t launch_route_group(const float* logits, int n_tokens, int n_experts, 
   if ((int64_t)n_tokens * top_k <= kWave) {
 #define MOE_RGW(P)                                                                           \
   route_group_wave_kernel<P><<<1, kWave, 0, stream>>>(logits, n_tokens, n_experts, top_k,    \
-                                                      routed_scale, ids, w, counts, offsets, \
-                                                      perm, inv_perm)
+                                                      routed_scale, opts, ids, w, counts,    \
+                                                      offsets, perm, inv_perm)
     if (per <= 1)
       MOE_RGW(1);
     else if (per <= 2)
@@ -450,9 +465,9 @@ hipError_t launch_route_group(const float* logits, int n_tokens, int n_experts, 
   }
   const int tpw = (n_tokens + kGroupWaves - 1) / kGroupWaves;
 #define MOE_RG(P, T)                                                                          \
-  route_group_kernel<P, T><<<1, kGroupThreads, 0, stream>>>(logits, n_tokens, n_experts,      \
-                                                            top_k, routed_scale, ids, w, counts, \
-                                                            offsets, perm, inv_perm, dev_error)
+  route_group_kernel<P, T><<<1, kGroupThreads, 0, stream>>>(                                 \
+      logits, n_tokens, n_experts, top_k, routed_scale, opts, ids, w, counts, offsets, perm, \
+      inv_perm, dev_error)
 #define MOE_RG_T(P)   \
   if (tpw <= 1)       \
     MOE_RG(P, 1);     \

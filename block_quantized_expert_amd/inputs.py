@@ -270,6 +270,7 @@ def layer_to_numpy(layer: dict) -> dict:
 # ----------------------------------------------------------------------------
 
 STREAM_X, STREAM_LOGITS, STREAM_BIAS, STREAM_TOKENS, STREAM_TABLE = 1, 2, 3, 4, 5
+STREAM_SEL_BIAS = 6
 
 
 def _rng(wl: Workload, stream: int, copy: int) -> np.random.Generator:
@@ -296,6 +297,13 @@ def expert_bias(wl: Workload) -> np.ndarray:
         rank = rng.permutation(wl.n_experts) + 1
         return -1.1 * 0.3 * np.log(rank)
     raise ValueError(wl.bias)
+
+
+def selection_bias(wl: Workload, std: float = 0.5) -> torch.Tensor:
+    """A per-expert fp32 bias for selection-only use, N(0, std^2), fixed per
+    workload (input data: the router adds it to its selection keys)."""
+    b = std * _rng(wl, STREAM_SEL_BIAS, 0).standard_normal(wl.n_experts)
+    return torch.from_numpy(b.astype(np.float32))
 
 
 def spaced_logits(rng: np.random.Generator, n: int, bias: np.ndarray,

@@ -108,6 +108,57 @@ typedef struct {
 } moe_layer;
 
 /*
+ * Options beyond the plain path, taken by the *_ex entry points (a NULL
+ * pointer, or a zeroed struct, asks for none of them).  Host memory, read
+ * during the call only.
+ *
+ * Group-limited selection ("Deep-Dive Mathematical & Kernel Guide", section
+ * 1: SQRT_SOFTPLUS gating "with expert group top-k selection"; the pages
+ * give no group parameters, this is the reading taken):
+ *   n_group     experts form n_group contiguous groups of n_experts/n_group;
+ *               0 or 1: one group.  At most 64, dividing n_experts.
+ *   topk_group  a token takes its experts from the topk_group groups whose
+ *               two largest selection keys sum highest (ties to the lower
+ *               group); 0 means n_group.  topk_group * n_experts / n_group
+ *               must be at least top_k.
+ *   sel_bias    nullable device fp32 [n_experts]: the selection key of expert
+ *               e is s_e + sel_bias[e] with s = sqrt(softplus(logit)) in fp64;
+ *               the bias moves the selection only, the weights use s.
+ *   With more than one group or a bias the top_k largest keys of the kept
+ *   groups are chosen (ties to the lower expert index); without either the
+ *   selection is moe_route's (on the logits).
+ * Tail pruning with L2-quadrature rescaling (Guide section 3.2 item 3 and
+ * its configuration table; "[RFC / Benchmarks] Fitting 284B
+ * DeepSeek-V4-Flash in 57.61 GiB RAM", section 5):
+ *   keep_max    at most this many routed experts per token (the largest
+ *               weights, ties to the lower slot); 0 means top_k.
+ *   min_w       routed experts whose weight is below min_w are dropped (the
+ *               weights sum to routed_scale, so the RFC's p_early = 0.025
+ *               is min_w = 0.025 * routed_scale); at least one expert (the
+ *               largest weight) is always kept.  0: no threshold.
+ *   Kept weights are multiplied by sqrt(sum of all w^2 / sum of kept w^2)
+ *   (fp64 from the fp32 weights, rounded once); a dropped slot gets expert
+ *   id -1 and weight 0 and keeps its position.  moe_group treats id -1 as
+ *   "no expert", so the dropped experts' weights are never read.
+ * Gate-first lazy skip (RFC section 5):
+ *   lazy_tau    a routed expert whose gate output g for a token has
+ *               max_j |SiLU(g_j)| < lazy_tau contributes nothing to that
+ *               token; 0: off.  The shared expert is never skipped.  For
+ *               bf16 batches of up to 16 tokens with MXFP4 experts the gate
+ *               projection runs first and a skipped expert's up and down
+ *               weights are not read (when all of its tokens skip it); other
+ *               batches compute every expert and drop the skipped terms.
+ */
+typedef struct {
+  int32_t n_group;
+  int32_t topk_group;
+  const float* sel_bias;
+  int32_t keep_max;
+  float min_w;
+  float lazy_tau;
+} moe_opts;
+
+/*
  * Learned router ("Deep-Dive Mathematical & Kernel Guide", section 1,
  * gating_func SQRT_SOFTPLUS; section 3.2, sum of routed weights 1.5).
  *   logits     fp32 [n_tokens][n_experts], row-major, finite.
@@ -123,6 +174,13 @@ typedef struct {
 moe_status moe_route(const float* logits, int n_tokens, int n_experts, int top_k,
                      float routed_scale, int32_t* topk_ids, float* topk_w,
                      hipStream_t stream);
+
+/* moe_route with the routing options of moe_opts (groups, selection bias,
+ * tail pruning; lazy_tau is not a routing option and is ignored here).
+ * MOE_ERR_INVALID for options outside the ranges stated with moe_opts. */
+moe_status moe_route_ex(const float* logits, int n_tokens, int n_experts, int top_k,
+                        float routed_scale, const moe_opts* opts, int32_t* topk_ids,
+                        float* topk_w, hipStream_t stream);
 
 /*
  * Token-id hash router ("Deep-Dive Mathematical & Kernel Guide", section 1
@@ -152,6 +210,12 @@ moe_status moe_route_group(const float* logits, int n_tokens, int n_experts, int
                            int32_t* offsets, int32_t* perm, int32_t* inv_perm,
                            int32_t* dev_error, hipStream_t stream);
 
+/* moe_route_group with the routing options of moe_opts. */
+moe_status moe_route_group_ex(const float* logits, int n_tokens, int n_experts, int top_k,
+                              float routed_scale, const moe_opts* opts, int32_t* topk_ids,
+                              float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                              int32_t* inv_perm, int32_t* dev_error, hipStream_t stream);
+
 /* Workspace bytes moe_group needs (currently 0: it works in LDS). */
 size_t moe_group_workspace_bytes(int n_tokens, int top_k, int n_experts);
 
@@ -166,8 +230,10 @@ size_t moe_group_workspace_bytes(int n_tokens, int top_k, int n_experts);
  *             ascending f inside an expert (stable); only the first
  *             offsets[n_experts] entries are written.
  *   inv_perm  out int32 [n_tokens*top_k]: inv_perm[perm[p]] = p; -1 for an
- *             entry whose id is out of range (then MOE_DEVERR_EXPERT_ID is
- *             set in *dev_error; dev_error may be NULL).
+ *             entry whose id is -1 (a slot dropped by tail pruning: it
+ *             belongs to no expert and is not an error) or out of range (then
+ *             MOE_DEVERR_EXPERT_ID is set in *dev_error; dev_error may be
+ *             NULL).
  *   Results are deterministic (no order depends on atomics).
  */
 moe_status moe_group(const int32_t* topk_ids, int n_tokens, int top_k, int n_experts,
@@ -213,6 +279,20 @@ moe_status moe_ffn_forward(const moe_layer* layer, const void* x, int x_type, in
                            const float* topk_w, const int32_t* counts, const int32_t* offsets,
                            const int32_t* perm, const int32_t* inv_perm, float* y,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_ffn_forward with the gate-first lazy skip of moe_opts (lazy_tau; the
+ * routing options are ignored here) and, for benchmarks, the events of
+ * moe_ffn_forward_timed (each nullable).  The workspace size is
+ * moe_ffn_workspace_bytes's.
+ */
+moe_status moe_ffn_forward_ex(const moe_layer* layer, const void* x, int x_type, int n_tokens,
+                              const float* topk_w, const int32_t* counts, const int32_t* offsets,
+                              const int32_t* perm, const int32_t* inv_perm, float* y,
+                              const moe_opts* opts, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream, hipEvent_t gate_up_start,
+                              hipEvent_t gate_up_stop, hipEvent_t down_start,
+                              hipEvent_t down_stop);
 
 /*
  * The two stages of moe_ffn_forward, for callers that time or interleave
@@ -330,6 +410,20 @@ moe_status moe_forward_noalloc(const moe_layer* layer, const float* logits, floa
                                float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
                                int32_t* inv_perm, float* y, int32_t* dev_error,
                                hipStream_t stream);
+
+/*
+ * moe_forward with the options of moe_opts (routing options and the lazy
+ * skip) and start/stop events (nullable) as moe_forward_timed.  Single-token
+ * calls with group-limited selection, a selection bias or tail pruning still
+ * run as the one fused kernel (same conditions as moe_forward); a lazy skip
+ * runs the separate kernels, whose small-batch gate/up then goes gate first.
+ */
+moe_status moe_forward_ex(const moe_layer* layer, const float* logits, float routed_scale,
+                          const moe_opts* opts, const void* x, int x_type, int n_tokens,
+                          int32_t* topk_ids, float* topk_w, int32_t* counts, int32_t* offsets,
+                          int32_t* perm, int32_t* inv_perm, float* y, void* workspace,
+                          size_t workspace_bytes, int32_t* dev_error, hipStream_t stream,
+                          hipEvent_t start, hipEvent_t stop);
 
 /* A static, human-readable name of a status code. */
 const char* moe_status_string(moe_status s);

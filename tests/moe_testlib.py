@@ -86,13 +86,29 @@ def host_layer(weights: dict, experts) -> dict:
 
 
 def oracle_y_host(weights: dict, act: str, x: torch.Tensor, ids, w, tokens=None, rows=None,
-                  with_shared=True):
+                  with_shared=True, lazy_tau=0.0):
     """oracle_y with the weights copied from the device layer."""
     tok = range(ids.shape[0]) if tokens is None else tokens
     needed = sorted({int(e) for t in tok for e in ids[t] if e >= 0})
     layer = host_layer(weights, needed)
     return O.ffn(layer, I.activations_to_numpy(x), act, ids, w, tokens=tokens, out_rows=rows,
-                 with_shared=with_shared)
+                 with_shared=with_shared, lazy_tau=lazy_tau)
+
+
+def assert_w_near(w_gpu: np.ndarray, w_ref: np.ndarray, tol: float = 1e-5):
+    """Weights after options (pruning rescales): within 1e-5 absolute."""
+    assert w_gpu.shape == w_ref.shape
+    assert np.all(np.abs(w_gpu.astype(np.float64) - w_ref.astype(np.float64)) <= tol)
+
+
+def assert_grouping(grouping, ids_ref, n_experts):
+    """counts, offsets, perm, inv_perm bit-exact against the oracle's grouping."""
+    counts, offsets, perm, inv = O.group(ids_ref, n_experts)
+    g = [t.cpu().numpy() for t in grouping]
+    assert np.array_equal(g[0], counts)
+    assert np.array_equal(g[1], offsets)
+    assert np.array_equal(g[2][: offsets[-1]], perm)
+    assert np.array_equal(g[3], inv)
 
 
 def block_tokens(ids: np.ndarray, n_experts: int, block: int = 16):

@@ -76,7 +76,18 @@ def test_ffn_workspace_bytes():
     o = -(-slots * 4096 * 4 // 256) * 256
     xq = n * 4096 * 2          # activations as two E4M3 parts
     xs = n * 4096 // 16        # their scale bytes
-    assert B.lib().moe_ffn_workspace_bytes(ctypes.byref(L), n) == 2 * h + o + xq + xs
+    gmax = n * 6 * 4           # lazy skip: each routed slot's largest |SiLU(g)|
+    assert B.lib().moe_ffn_workspace_bytes(ctypes.byref(L), n) == 2 * h + o + xq + xs + gmax
+    # up to 16 tokens: also the gate outputs of the gate-first lazy pass
+    n = 16
+    slots = n * 6 + n
+    h = -(-slots * 2048 * 2 // 256) * 256
+    o = -(-slots * 4096 * 4 // 256) * 256
+    xs = -(-n * 4096 // 16 // 256) * 256
+    gmax = -(-n * 6 * 4 // 256) * 256
+    gbuf = n * 6 * 2048 * 4
+    assert B.lib().moe_ffn_workspace_bytes(ctypes.byref(L), n) == \
+        2 * h + o + n * 4096 * 2 + xs + gmax + gbuf
     assert B.lib().moe_ffn_workspace_bytes(ctypes.byref(L), 0) == 0
     assert B.lib().moe_ffn_workspace_bytes(ctypes.byref(_layer(hidden=100)), 8) == 0
     assert B.lib().moe_ffn_workspace_bytes(None, 8) == 0
@@ -252,3 +263,47 @@ def test_forward_workspace_init_rejects_small_areas():
     assert lib.moe_forward_workspace_init(None, 1 << 20, None) == B.MOE_ERR_WORKSPACE
     assert lib.moe_forward_workspace_init(FAKE, B.MOE_FORWARD_SYNC_BYTES - 1, None) == \
         B.MOE_ERR_WORKSPACE
+
+
+def test_opts_rejected_before_launch():
+    lib = B.lib()
+    P = ctypes.c_void_p
+    bad = [dict(n_group=3),                    # does not divide 256 experts
+           dict(n_group=128),                  # more than 64 groups
+           dict(n_group=8, topk_group=9),      # more groups kept than exist
+           dict(n_group=64, topk_group=1),     # 4 experts in the kept group < top-6
+           dict(n_group=-1),
+           dict(keep_max=7),                   # above top_k
+           dict(keep_max=-1),
+           dict(min_w=-0.1),
+           dict(min_w=float("nan")),
+           dict(lazy_tau=float("inf")),
+           dict(lazy_tau=-1.0)]
+    for kw in bad:
+        o = B.make_opts(**kw)
+        assert lib.moe_route_ex(FAKE, 4, 256, 6, 1.5, ctypes.byref(o), FAKE, FAKE, None) == \
+            B.MOE_ERR_INVALID, kw
+        assert lib.moe_route_group_ex(FAKE, 4, 256, 6, 1.5, ctypes.byref(o), FAKE, FAKE, FAKE,
+                                      FAKE, FAKE, FAKE, None, None) == B.MOE_ERR_INVALID, kw
+    o = B.make_opts()
+    o.sel_bias = 0x10002  # not 4-byte aligned
+    assert lib.moe_route_ex(FAKE, 4, 256, 6, 1.5, ctypes.byref(o), FAKE, FAKE, None) == \
+        B.MOE_ERR_INVALID
+    # the FFN and the whole layer check the options too
+    L = _layer()
+    o = B.make_opts(lazy_tau=-1.0)
+    assert lib.moe_ffn_forward_ex(ctypes.byref(L), FAKE, B.MOE_ACT_BF16, 4, FAKE, FAKE, FAKE,
+                                  FAKE, FAKE, FAKE, ctypes.byref(o), FAKE, 1 << 40, None, None,
+                                  None, None, None) == B.MOE_ERR_INVALID
+    o = B.make_opts(keep_max=9)
+    assert lib.moe_forward_ex(ctypes.byref(L), FAKE, 1.5, ctypes.byref(o), FAKE, B.MOE_ACT_BF16,
+                              1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None,
+                              None, None, None) == B.MOE_ERR_INVALID
+
+
+def test_opts_struct_layout_matches_c():
+    # int32 x2, pointer, int32, float x2
+    assert B.MoeOpts.sel_bias.offset == 8
+    assert B.MoeOpts.keep_max.offset == 16
+    assert B.MoeOpts.lazy_tau.offset == 24
+    assert ctypes.sizeof(B.MoeOpts) == 32
