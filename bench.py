@@ -11,7 +11,9 @@ prefill of 4096 tokens on the DeepSeek-V4-Flash-shaped layer (hidden 4096,
 Its K timed steps follow W warm-up steps.  The other workloads (tiny,
 single-token decode, batched decode of 32, prefill of 512) are measured in
 the same run, each with its own step count, and reported as nested records
-under "configs" (``--workload NAME`` measures only that one as the line).
+under "configs", together with records of the routing and FFN options
+(VARIANTS: tail pruning, group-limited top-k, the gate-first lazy skip) on
+those workloads (``--workload NAME`` measures only that one as the line).
 
 Cold caches: the weights live in several independent layer copies (3.44 GB
 each) used round-robin, and every step takes a fresh batch from a seeded
@@ -58,6 +60,24 @@ MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8, published
 HEADLINE = "hash4096"
 NESTED = ["tiny", "decode1", "decode32", "prefill512"]
 REPS = 5
+
+# Routing and FFN options (moe_opts) measured on top of a workload, as nested
+# records: name -> (workload, options).  "sel_bias" draws the per-expert
+# selection bias of the inputs module (N(0, 0.5^2)).
+VARIANTS = {
+    # tail pruning with L2 rescaling: at most 4 or 5 of the 6 routed experts
+    # ("Deep-Dive Mathematical & Kernel Guide", section 3.2 configuration table)
+    "decode1_top4": ("decode1", dict(keep_max=4)),
+    "decode1_top5": ("decode1", dict(keep_max=5)),
+    "decode32_top4": ("decode32", dict(keep_max=4)),
+    # group-limited top-k (8 groups, 4 kept) with a selection-only bias
+    "decode1_groups": ("decode1", dict(n_group=8, topk_group=4, sel_bias=True)),
+    "decode32_groups": ("decode32", dict(n_group=8, topk_group=4, sel_bias=True)),
+    # gate-first lazy skip at the RFC's threshold: the gate rows first, then the
+    # up rows of the experts some token keeps (on these inputs every expert is
+    # kept, so this is the cost of the gate-first order)
+    "decode1_lazy": ("decode1", dict(lazy_tau=1e-3)),
+}
 
 # workload: (steps, warmup, copies, pool) when it is measured as a nested
 # record or as the line without --steps/--warmup
@@ -119,7 +139,7 @@ def workload_costs(wl, counts_list):
     sh_dn = proj_bytes(wl.shared, h, si)
     same = wl.shared == wl.routed
     n, k = wl.n_tokens, wl.top_k
-    gu = dn = path = 0.0
+    gu = dn = path = slots = 0.0
     for counts in counts_list:
         d = int((counts > 0).sum())
         gu += d * per_gu + (sh_gu if same else 0) + n * h * act
@@ -127,13 +147,16 @@ def workload_costs(wl, counts_list):
         route_in = n * wl.n_experts * 4 if wl.routing == "learned" else n * 4 + n * k * 8
         path += (d * (per_gu + per_dn) + sh_gu + sh_dn + n * h * act + n * h * 4 + route_in
                  + n * k * 8)
+        slots += int(counts.sum())  # n*k, or fewer after tail pruning
     c = len(counts_list)
+    slots /= c
     sh_tok = n if same else 0
     return {
         "gate_up_bytes": gu / c, "down_bytes": dn / c, "path_bytes": path / c,
-        "gate_up_flops": 4.0 * i * h * n * k + 4.0 * si * h * sh_tok,
-        "down_flops": 2.0 * i * h * n * k + 2.0 * si * h * sh_tok,
-        "path_flops": 6.0 * i * h * n * k + 6.0 * si * h * n,
+        "gate_up_flops": 4.0 * i * h * slots + 4.0 * si * h * sh_tok,
+        "down_flops": 2.0 * i * h * slots + 2.0 * si * h * sh_tok,
+        "path_flops": 6.0 * i * h * slots + 6.0 * si * h * n,
+        "routed_slots": slots,
     }
 
 
@@ -141,7 +164,7 @@ class Runner:
     """Pre-built ctypes arguments for every (layer copy, input) pair so a
     step costs a few direct library calls."""
 
-    def __init__(self, wl, layers, pool, dev):
+    def __init__(self, wl, layers, pool, dev, opts=None):
         import torch
 
         from block_quantized_expert_amd import binding as B
@@ -151,6 +174,8 @@ class Runner:
         self.wl = wl
         self.layers = layers
         self.pool = pool
+        self.opts = opts
+        o = None if opts is None else ctypes.byref(opts)
         n, k, e = wl.n_tokens, wl.top_k, wl.n_experts
         self.ids = torch.empty((n, k), dtype=torch.int32, device=dev)
         self.w = torch.empty((n, k), dtype=torch.float32, device=dev)
@@ -173,8 +198,8 @@ class Runner:
         self.route_args = []
         for item in pool:
             if wl.routing == "learned":
-                self.route_args.append([("moe_route_group", (
-                    P(item["logits"].data_ptr()), n, e, k, ctypes.c_float(wl.routed_scale),
+                self.route_args.append([("moe_route_group_ex", (
+                    P(item["logits"].data_ptr()), n, e, k, ctypes.c_float(wl.routed_scale), o,
                     P(self.ids.data_ptr()), P(self.w.data_ptr())) + grouping + (None, s))])
             else:
                 self.route_args.append([("moe_route_hash", (
@@ -186,7 +211,8 @@ class Runner:
         # (one fused kernel); its outputs land in one set of buffers
         self.fused = (wl.routing == "learned" and
                       self.L.moe_forward_single_kernel(ctypes.byref(layers[0].c), n,
-                                                       x_type) == 1)
+                                                       x_type) == 1 and
+                      (opts is None or opts.lazy_tau == 0.0))
         self.fwd_args = {}
         if self.fused:
             self.fwd = B.ForwardBuffers(layers[0], n, dev)
@@ -194,7 +220,7 @@ class Runner:
                 for r, item in enumerate(pool):
                     self.fwd_args[(c, r)] = (
                         [ctypes.byref(layer.c), P(item["logits"].data_ptr()),
-                         ctypes.c_float(wl.routed_scale), P(item["x"].data_ptr()), x_type, n]
+                         ctypes.c_float(wl.routed_scale), o, P(item["x"].data_ptr()), x_type, n]
                         + self.fwd.args() + [s])
         self.ffn_args = {}
         for c, layer in enumerate(layers):
@@ -202,7 +228,7 @@ class Runner:
                 self.ffn_args[(c, r)] = (
                     ctypes.byref(layer.c), P(item["x"].data_ptr()), x_type, n,
                     P(self.w.data_ptr()), P(self.counts.data_ptr()), P(self.offsets.data_ptr()),
-                    P(self.perm.data_ptr()), P(self.inv.data_ptr()), P(self.y.data_ptr()),
+                    P(self.perm.data_ptr()), P(self.inv.data_ptr()), P(self.y.data_ptr()), o,
                     P(self.ws.data_ptr()), self.ws_bytes, s)
 
     def step(self, s, ev=None):
@@ -215,14 +241,14 @@ class Runner:
         L = self.L
         if self.fused:
             evs = (None, None) if ev is None else ev[:2]
-            if L.moe_forward_timed(*self.fwd_args[(c, r)], *evs):
-                raise RuntimeError("moe_forward failed in step %d" % s)
+            if L.moe_forward_ex(*self.fwd_args[(c, r)], *evs):
+                raise RuntimeError("moe_forward_ex failed in step %d" % s)
             return
         st = 0
         for name, args in self.route_args[r]:
             st |= getattr(L, name)(*args)
         evs = (None, None, None, None) if ev is None else ev
-        st |= L.moe_ffn_forward_timed(*self.ffn_args[(c, r)], *evs)
+        st |= L.moe_ffn_forward_ex(*self.ffn_args[(c, r)], *evs)
         if st:
             raise RuntimeError("a moe_* call failed in step %d" % s)
 
@@ -323,9 +349,9 @@ def step_stats(rep_ms, rep_steps):
             "spread_over_15pct": bool((per.max() - per.min()) / med > 0.15)}
 
 
-def run_workload(name, steps, warmup, copies, n_pool, cpu_seconds, dev):
-    """Measure one workload; returns its record (without the top-level
-    contract keys)."""
+def run_workload(name, steps, warmup, copies, n_pool, cpu_seconds, dev, variant=None):
+    """Measure one workload (with the options of `variant`, a key of
+    VARIANTS); returns its record (without the top-level contract keys)."""
     import numpy as np
     import torch
 
@@ -333,10 +359,19 @@ def run_workload(name, steps, warmup, copies, n_pool, cpu_seconds, dev):
     from block_quantized_expert_amd import inputs as I
 
     wl = I.WORKLOADS[name]
+    opts, opts_desc = None, None
+    if variant is not None:
+        kw = dict(VARIANTS[variant][1])
+        if kw.pop("sel_bias", False):
+            kw["sel_bias"] = I.selection_bias(wl).to(dev)
+        opts = B.make_opts(**kw)
+        opts_desc = {k: (v if k != "sel_bias" else "N(0, 0.5^2) per expert")
+                     for k, v in kw.items()}
     t0 = time.perf_counter()
     layers = [B.Layer(I.make_layer(wl, device=dev, copy=c), wl.top_k) for c in range(copies)]
     pool = make_pool(wl, n_pool, dev)
-    runner = Runner(wl, layers, pool, dev)
+    runner = Runner(wl, layers, pool, dev, opts)
+    name = variant or name
     torch.cuda.synchronize()
     print("%s setup %.1f s: %d layer copies, %d inputs" % (name, time.perf_counter() - t0,
                                                             copies, n_pool),
@@ -423,6 +458,7 @@ def run_workload(name, steps, warmup, copies, n_pool, cpu_seconds, dev):
     rec = {
         "workload": name,
         "config": {"workload": describe(wl, copies), "n_tokens": wl.n_tokens},
+        "routed_slots_per_step": costs["routed_slots"],
         "value": wl.n_tokens * steps / elapsed,
         "unit": "tokens/s",
         "steps": steps,
@@ -453,6 +489,10 @@ def run_workload(name, steps, warmup, copies, n_pool, cpu_seconds, dev):
             "issued_frac_of_fp8_peak": dissue * kcosts["down_flops"] / dn_avg_s / 1e12
                                        / MFMA_FP8_PEAK_TFLOPS,
         }
+    if opts_desc is not None:
+        rec["config"]["options"] = opts_desc
+        rec["config"]["path"] = ("single fused kernel" if runner.fused else
+                                 "route+group kernel(s), gate/up, down")
     st = rec["step_stats"]
     print("%s: %d steps %.2f us/step (reps median %.2f, min %.2f, max %.2f), roofline kernel "
           "%.2f us (%.0f GB/s, %.0f TFLOP/s)%s" % (
@@ -462,7 +502,7 @@ def run_workload(name, steps, warmup, copies, n_pool, cpu_seconds, dev):
           file=sys.stderr, flush=True)
     del runner, layers, pool
     torch.cuda.empty_cache()
-    if cpu_seconds > 0:
+    if cpu_seconds > 0 and variant is None:
         rec["cpu_baseline"] = cpu_baseline(wl, cpu_seconds)
     return rec
 
@@ -511,6 +551,8 @@ def main():
     ap.add_argument("--pool", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="leave out the nested records of the routing/FFN options")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before the warm-up, copy this many MiB once with a plain device "
                          "copy kernel (a known byte count for calibrating memory counters)")
@@ -551,13 +593,20 @@ def main():
         st, wu, cp, po = DEFAULTS[name]
         configs[name] = run_workload(name, st, wu, cp, po,
                                      args.nested_cpu_seconds if cpu else 0.0, dev)
+    if not args.workload and not args.no_variants:
+        for var, (name, _) in VARIANTS.items():
+            st, wu, cp, po = DEFAULTS[name]
+            configs[var] = run_workload(name, st, wu, cp, po, 0.0, dev, variant=var)
+    variant = None
+    if line_name in VARIANTS:  # a workload with options, measured alone
+        variant, line_name = line_name, VARIANTS[line_name][0]
     st, wu, cp, po = DEFAULTS[line_name]
     steps = args.steps if args.steps is not None else st
     warmup = args.warmup if args.warmup is not None else wu
     rec = run_workload(line_name, steps, warmup,
                        args.copies if args.copies is not None else cp,
                        args.pool if args.pool is not None else po,
-                       args.cpu_seconds if cpu else 0.0, dev)
+                       args.cpu_seconds if cpu else 0.0, dev, variant=variant)
 
     result = {
         "metric": METRIC,

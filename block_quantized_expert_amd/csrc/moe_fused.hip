@@ -75,6 +75,7 @@ struct FusedSmem {
   float wslot[MOE_MAX_TOP_K];  // routing options: the weight of slot (rank) r
   int ok;
   double s[kFPer * kWave];  // sqrt(softplus(logit)) of every expert
+  double gkeys[kFPer * kWave];  // routing options: selection keys for group scoring
   f32x4 gu_red[kQuads][3][2][4];  // gate/up sums of wavefronts 1-3 of a quad (token lanes)
   f32x4 dn_red[kFWaves][4][2];    // down sums of every wavefront (hi and lo columns)
   alignas(16) uint8_t dsc[kFSlots][kDScale];  // down scales of the row block, per segment
@@ -287,13 +288,48 @@ __global__ __launch_bounds__(kFThreads) void decode_fused_kernel(FusedParams f) 
     issue_lds(blockIdx.x);
   }
   if (f.route_opts) {
-    // groups, a selection bias or tail pruning: wavefront 0 routes with the
-    // options (the fp64 scores of its four experts per lane included) while
-    // wavefront 9 copies x into LDS
+    // groups, a selection bias or tail pruning.  Groups and a bias select on
+    // the fp64 scores: the four score wavefronts compute all of them into LDS
+    // first (one expert per lane), then wavefront 0 selects.  Pruning alone
+    // selects on the logits, as the plain path.  Wavefront 14 copies x.
+    const bool on_scores = !opts_select_on_logits(f.ropts);  // uniform
+    if (wave == 14) {
+      for (int i = 0; i < p.hidden / 512; ++i)
+        __builtin_amdgcn_global_load_lds(
+            static_cast<const __bf16*>(p.x) + i * 512 + lane * 8,
+            (__attribute__((address_space(3))) void*)(&sm.u.gu.x[i * 512]), 16, 0, 0);
+    }
+    // wavefront 0's selection bias, requested before the scores' barrier
+    float bv[kFPer];
+#pragma unroll
+    for (int j = 0; j < kFPer; ++j) bv[j] = 0.0f;
+    if (wave == kRouteWave && f.ropts.bias) {
+#pragma unroll
+      for (int j = 0; j < kFPer; ++j) bv[j] = f.ropts.bias[min(j * kWave + lane, p.n_experts - 1)];
+    }
+    if (on_scores) {
+      if (score_part >= 0) {
+        const int e = score_part * kWave + lane;
+        if (e < p.n_experts) sm.s[e] = gate_score((double)f.logits[e]);
+      }
+      __syncthreads();
+    }
     if (wave == kRouteWave) {
       int id;
       float wt;
-      route_token_opts<kFPer>(f.logits, p.n_experts, k, f.routed_scale, f.ropts, lane, id, wt);
+      if (on_scores) {
+        double sv[kFPer];
+#pragma unroll
+        for (int j = 0; j < kFPer; ++j) {
+          const int e = min(j * kWave + lane, p.n_experts - 1);
+          sv[j] = j * kWave + lane < p.n_experts ? sm.s[e] : 0.0;
+        }
+        route_select_grouped<kFPer>(sv, bv, p.n_experts, k, f.routed_scale, f.ropts, lane,
+                                    sm.gkeys, id, wt);
+      } else {
+        route_token<kFPer>(f.logits, p.n_experts, k, f.routed_scale, lane, id, wt);
+      }
+      if (opts_prune(f.ropts, k)) prune_slots(k, f.ropts.keep_max, f.ropts.min_w, lane, id, wt);
       const bool kept = lane < k && id >= 0;
       const int nk = __popcll(__ballot(kept));
       int below = 0;  // kept experts below this one: its segment
@@ -318,12 +354,8 @@ __global__ __launch_bounds__(kFThreads) void decode_fused_kernel(FusedParams f) 
         f.inv_perm[lane] = kept ? below : -1;
         if (kept) f.perm[below] = lane;
       }
-    } else if (wave == 9) {
-      for (int i = 0; i < p.hidden / 512; ++i)
-        __builtin_amdgcn_global_load_lds(
-            static_cast<const __bf16*>(p.x) + i * 512 + lane * 8,
-            (__attribute__((address_space(3))) void*)(&sm.u.gu.x[i * 512]), 16, 0, 0);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else if (wave == 14) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the copies of x have landed
     }
   } else if (wave == kRouteWave) {
     uint32_t key[kFPer];

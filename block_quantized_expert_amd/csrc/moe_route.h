@@ -174,20 +174,32 @@ __device__ __forceinline__ double key_value64(uint64_t k) {
       (long long)((k & 0x8000000000000000ull) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k));
 }
 
-__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
-  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m);
-  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m);
-  return ((uint64_t)hi << 32) | lo;
+// One DPP step of a 64-bit max-scan: both halves move with the same control
+// (lanes without a source read 0, below every key), then the larger wins.
+template <int CTRL, int ROW_MASK, bool BOUND>
+__device__ __forceinline__ uint64_t dpp_max64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, ROW_MASK,
+                                                            0xF, BOUND);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL,
+                                                            ROW_MASK, 0xF, BOUND);
+  const uint64_t o = ((uint64_t)hi << 32) | lo;
+  return o > v ? o : v;
 }
 
-// Maximum of a 64-bit value over the wavefront, in every lane.
+// Maximum of a 64-bit value over the wavefront, in every lane: the max-scan
+// of wave_max on both halves (row shifts, then row broadcasts; lane 63 ends
+// with the maximum), read back from lane 63.  DPP moves stay inside the
+// register file; cross-lane shuffles through LDS cost tens of cycles each.
 __device__ __forceinline__ uint64_t wave_max64(uint64_t v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const uint64_t o = shfl_xor64(v, m);
-    v = o > v ? o : v;
-  }
-  return v;
+  v = dpp_max64<0x111, 0xF, true>(v);   // row_shr:1
+  v = dpp_max64<0x112, 0xF, true>(v);   // row_shr:2
+  v = dpp_max64<0x114, 0xF, true>(v);   // row_shr:4
+  v = dpp_max64<0x118, 0xF, true>(v);   // row_shr:8
+  v = dpp_max64<0x142, 0xA, false>(v);  // row_bcast:15
+  v = dpp_max64<0x143, 0xC, false>(v);  // row_bcast:31
+  const uint32_t lo = (uint32_t)read_lane((int)(uint32_t)v, 63);
+  const uint32_t hi = (uint32_t)read_lane((int)(uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 __device__ __forceinline__ double read_lane_f64(double v, int l) {
@@ -233,56 +245,64 @@ __device__ __forceinline__ void route_select64(uint64_t (&key)[PER], int top_k, 
 // lower group), and the top_k largest keys among their experts are chosen
 // (ties to the lower expert).  Lane r < top_k returns the expert of rank r
 // and its weight routed_scale * s_r / sum of the chosen s (unbiased).
+// The selection itself, from the scores s (lane l holds experts j*64 + l)
+// and the selection bias bv of the same experts.  kbuf: this wavefront's LDS
+// room for n_experts doubles (used when there are groups): the keys go there
+// and lane g scans the members of group g for its two largest, so every group
+// is scored at once (one full-wavefront reduction per group cost ~0.7 us
+// each at eight groups).
 template <int PER>
-__device__ void route_token_grouped(const float* __restrict__ row, int n_experts, int top_k,
-                                    float routed_scale, const RouteOpts& o, int lane,
-                                    int& out_id, float& out_w) {
-  float v[PER], bv[PER];
-#pragma unroll
-  for (int j = 0; j < PER; ++j) v[j] = row[min(j * kWave + lane, n_experts - 1)];
-#pragma unroll
-  for (int j = 0; j < PER; ++j)
-    bv[j] = o.bias ? o.bias[min(j * kWave + lane, n_experts - 1)] : 0.0f;
-  double s[PER];
+__device__ void route_select_grouped(const double (&s)[PER], const float (&bv)[PER],
+                                     int n_experts, int top_k, float routed_scale,
+                                     const RouteOpts& o, int lane, double* kbuf, int& out_id,
+                                     float& out_w) {
   uint64_t key[PER];
+  double kv[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const bool live = j * kWave + lane < n_experts;
-    s[j] = live ? gate_score((double)v[j]) : 0.0;
-    key[j] = live ? order_key64(s[j] + (double)bv[j]) : 0ull;
+    kv[j] = s[j] + (double)bv[j];
+    key[j] = live ? order_key64(kv[j]) : 0ull;
   }
   if (o.n_group > 1) {
     const int gsize = n_experts / o.n_group;
-    uint64_t gkey = 0ull;  // lane g: the score key of group g
-    for (int g = 0; g < o.n_group; ++g) {
-      const int lo = g * gsize, hi = lo + gsize;
-      uint64_t m = 0ull;
 #pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const int e = j * kWave + lane;
-        if (e >= lo && e < hi) m = key[j] > m ? key[j] : m;
-      }
-      const uint64_t top1 = wave_max64(m);
-      double score = key_value64(top1);
-      if (gsize > 1) {
-        // the second largest: the largest left once the lowest member
-        // holding top1 is set aside
-        int first = -1;
+    for (int j = 0; j < PER; ++j)
+      if (j * kWave + lane < n_experts) kbuf[j * kWave + lane] = kv[j];
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wavefront's keys are in LDS
+    __builtin_amdgcn_wave_barrier();
+    // lane g: the two largest keys of group g (equal ones both count), their
+    // sum largest first
+    uint64_t gkey = 0ull;
+    if (lane < o.n_group) {
+      const double* kg = kbuf + lane * gsize;
+      double t1 = -INFINITY, t2 = -INFINITY;
+      // eight loads in flight at a time; the comparisons follow in order
+      int i = 0;
+      for (; i + 8 <= gsize; i += 8) {
+        double v[8];
 #pragma unroll
-        for (int j = 0; j < PER; ++j) {
-          const int e = j * kWave + lane;
-          const uint64_t b = __ballot(e >= lo && e < hi && key[j] == top1);
-          if (first < 0 && b != 0) first = j * kWave + __builtin_ctzll(b);
+        for (int u = 0; u < 8; ++u) v[u] = kg[i + u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (v[u] > t1) {
+            t2 = t1;
+            t1 = v[u];
+          } else if (v[u] > t2) {
+            t2 = v[u];
+          }
         }
-        uint64_t m2 = 0ull;
-#pragma unroll
-        for (int j = 0; j < PER; ++j) {
-          const int e = j * kWave + lane;
-          if (e >= lo && e < hi && e != first) m2 = key[j] > m2 ? key[j] : m2;
-        }
-        score = score + key_value64(wave_max64(m2));
       }
-      if (lane == g) gkey = order_key64(score);
+      for (; i < gsize; ++i) {
+        const double v = kg[i];
+        if (v > t1) {
+          t2 = t1;
+          t1 = v;
+        } else if (v > t2) {
+          t2 = v;
+        }
+      }
+      gkey = order_key64(gsize > 1 ? t1 + t2 : t1);
     }
     uint64_t chosen = 0ull;  // bit g: group g kept
     for (int r = 0; r < o.topk_group; ++r) {
@@ -312,6 +332,26 @@ __device__ void route_token_grouped(const float* __restrict__ row, int n_experts
   double total = 0.0;
   for (int i = 0; i < top_k; ++i) total += read_lane_f64(my_s, i);
   out_w = lane < top_k ? routed_weight(my_s, total, routed_scale) : 0.0f;
+}
+
+// route_select_grouped of the token whose logits start at row, its scores
+// computed here.
+template <int PER>
+__device__ void route_token_grouped(const float* __restrict__ row, int n_experts, int top_k,
+                                    float routed_scale, const RouteOpts& o, int lane,
+                                    double* kbuf, int& out_id, float& out_w) {
+  float v[PER], bv[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) v[j] = row[min(j * kWave + lane, n_experts - 1)];
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+    bv[j] = o.bias ? o.bias[min(j * kWave + lane, n_experts - 1)] : 0.0f;
+  double s[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+    s[j] = j * kWave + lane < n_experts ? gate_score((double)v[j]) : 0.0;
+  route_select_grouped<PER>(s, bv, n_experts, top_k, routed_scale, o, lane, kbuf, out_id,
+                            out_w);
 }
 
 // Tail pruning with L2-quadrature rescaling ("Deep-Dive Mathematical &
@@ -357,12 +397,12 @@ __device__ void prune_slots(int top_k, int keep_max, float min_w, int lane, int&
 // asked.  Lane r < top_k returns slot r's expert (-1 when pruned) and weight.
 template <int PER>
 __device__ void route_token_opts(const float* __restrict__ row, int n_experts, int top_k,
-                                 float routed_scale, const RouteOpts& o, int lane, int& out_id,
-                                 float& out_w) {
+                                 float routed_scale, const RouteOpts& o, int lane, double* kbuf,
+                                 int& out_id, float& out_w) {
   if (opts_select_on_logits(o))
     route_token<PER>(row, n_experts, top_k, routed_scale, lane, out_id, out_w);
   else
-    route_token_grouped<PER>(row, n_experts, top_k, routed_scale, o, lane, out_id, out_w);
+    route_token_grouped<PER>(row, n_experts, top_k, routed_scale, o, lane, kbuf, out_id, out_w);
   if (opts_prune(o, top_k)) prune_slots(top_k, o.keep_max, o.min_w, lane, out_id, out_w);
 }
 

@@ -31,6 +31,8 @@ constexpr int kFusedMaxTokens = 4 * kGroupWaves;
 // workgroups
 constexpr int kGroupChunk = 1024;
 constexpr int kGroupMaxBlocks = 64;
+static_assert(kGroupWaves * 8 * kWave * sizeof(double) <= kGroupWaves * MOE_MAX_EXPERTS * sizeof(int),
+              "group keys of 512 experts per wavefront fit in the grouping's counts");
 
 // ---------------------------------------------------------------- routing
 
@@ -40,13 +42,14 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
                                                          float routed_scale, RouteOpts opts,
                                                          int32_t* __restrict__ ids,
                                                          float* __restrict__ w) {
+  __shared__ double s_kb[4][PER * kWave];  // each wavefront's keys for group scoring
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= n_tokens) return;  // the whole wavefront leaves together
   int id;
   float wt;
   route_token_opts<PER>(logits + (size_t)t * n_experts, n_experts, top_k, routed_scale, opts,
-                        lane, id, wt);
+                        lane, s_kb[threadIdx.x >> 6], id, wt);
   if (lane < top_k) {
     ids[(size_t)t * top_k + lane] = id;
     w[(size_t)t * top_k + lane] = wt;
@@ -297,9 +300,11 @@ __global__ __launch_bounds__(kGroupThreads) void route_group_kernel(
       float wt;
       if (on_logits)
         route_keys<PER>(key[i], top_k, routed_scale, lane, id, wt);
-      else
+      else  // group keys in the grouping's LDS, which is not in use yet
         route_token_grouped<PER>(logits + (size_t)t * n_experts, n_experts, top_k, routed_scale,
-                                 opts, lane, id, wt);
+                                 opts, lane,
+                                 reinterpret_cast<double*>(&sh.s_base[0][0]) + wave * PER * kWave,
+                                 id, wt);
       if (prune) prune_slots(top_k, opts.keep_max, opts.min_w, lane, id, wt);
       if (lane < top_k) {
         ids[t * top_k + lane] = id;
@@ -324,13 +329,14 @@ __global__ __launch_bounds__(kWave) void route_group_wave_kernel(
     int32_t* __restrict__ inv_perm) {
   __shared__ int s_count[MOE_MAX_EXPERTS];
   __shared__ int s_ids[kWave];
+  __shared__ double s_kb[PER * kWave];  // keys for group scoring
   const int lane = threadIdx.x;
   for (int e = lane; e < n_experts; e += kWave) s_count[e] = 0;
   for (int t = 0; t < n_tokens; ++t) {
     int id;
     float wt;
     route_token_opts<PER>(logits + (size_t)t * n_experts, n_experts, top_k, routed_scale, opts,
-                          lane, id, wt);
+                          lane, s_kb, id, wt);
     if (lane < top_k) {
       ids[t * top_k + lane] = id;
       w[t * top_k + lane] = wt;
@@ -437,7 +443,11 @@ hipError_t launch_route_group(const float* logits, int n_tokens, int n_experts, 
   // one workgroup routes at most four tokens per wavefront; larger batches
   // route on a wavefront per token and group in a second kernel (one
   // workgroup routing 512 tokens took 133 us, the two kernels ~15)
-  if (n_tokens > kFusedMaxTokens || (int64_t)n_tokens * top_k > kFusedMaxFlat) {
+  // the single-workgroup route+group keeps each wavefront's group keys in the
+  // grouping's LDS, room for 512 experts per wavefront
+  const bool grouped_wide = opts.n_group > 1 && n_experts > 512;
+  if (n_tokens > kFusedMaxTokens || (int64_t)n_tokens * top_k > kFusedMaxFlat ||
+      (grouped_wide && (int64_t)n_tokens * top_k > kWave)) {
     hipError_t e =
         launch_route(logits, n_tokens, n_experts, top_k, routed_scale, opts, ids, w, stream);
     if (e != hipSuccess) return e;
