@@ -81,6 +81,7 @@ moe::FfnParams make_params(const moe_layer* L, const void* x, int x_type, int n_
   p.lazy_tau = 0.0f;
   p.gmax = reinterpret_cast<uint32_t*>(ws + plan.off_gmax);
   p.gbuf = reinterpret_cast<float*>(ws + plan.off_gbuf);
+  p.qctr = reinterpret_cast<uint32_t*>(ws + plan.off_qctr);
   return p;
 }
 

@@ -326,6 +326,8 @@ __global__ __launch_bounds__(kThreads) void gate_up_kernel(FfnParams p, int x_st
   __shared__ int s_pref[kMaxSeg + 1];
   __shared__ int s_tmp[kWaves];
   __shared__ f32x4 s_red[kWaves - 1][2 * NBT][kWave];
+  // the grouped down's queue counters start this call at 0
+  if (blockIdx.x == 0 && threadIdx.x < kQueueWords) p.qctr[threadIdx.x] = 0u;
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int g = lane >> 4, r16 = lane & 15;
 
@@ -452,6 +454,8 @@ __global__ __launch_bounds__(kThreads) void gate_up_decode_kernel(FfnParams p, i
   constexpr int kRow = S * 128 + 8;  // bf16 per staged token row (+8: other banks)
   extern __shared__ __align__(16) char s_dyn[];
   __shared__ f32x4 s_red[kWaves - 1][2][kWave];
+  // the grouped down's queue counters start this call at 0
+  if (blockIdx.x == 0 && threadIdx.x < kQueueWords) p.qctr[threadIdx.x] = 0u;
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int g = lane >> 4, r16 = lane & 15;
   const int rb_r = p.inter >> 4;

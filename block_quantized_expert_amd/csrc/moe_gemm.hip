@@ -234,15 +234,74 @@ __device__ __forceinline__ void step_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
-// Workgroups are dealt to the eight XCDs round-robin (workgroup b runs on
-// XCD b % 8), and each XCD has its own L2.  The item order is cut into eight
-// contiguous chunks, one per XCD: the row tiles of one expert (which share
-// its token rows) and the token tiles of one row tile (which share its
-// weights) then meet in the same L2.  Returns -1 for the padding indices.
-__device__ __forceinline__ int xcd_item(int i, int total) {
-  const int per = (total + 7) >> 3;
-  const int l = (i & 7) * per + (i >> 3);
-  return l < total ? l : -1;
+// Dynamic item queue of one launch.  Workgroups are dealt to the eight XCDs
+// round-robin (workgroup b runs on XCD b % 8), and each XCD has its own L2.
+// The item order is cut into eight contiguous chunks, one per XCD, each with
+// a counter in the workspace: the row tiles of one expert (which share its
+// token rows) and the token tiles of one row tile (which share its weights)
+// then meet in the same L2.  A workgroup takes tickets from its own XCD's
+// counter while that chunk lasts, then from the other chunks in turn, so
+// workgroups that run out of their own items take over the rest instead of
+// idling (a static assignment left the busiest workgroup 1.14 (gate/up) and
+// 1.25 (down) times the mean work on a hash-routed batch of 4096 tokens).
+// Every workgroup takes exactly one ticket past the end of every chunk, so
+// the holder of the last one (chunk items + grid - 1) resets that counter to
+// 0 for the next launch; the gate/up pass of each call also zeroes them (a
+// fresh workspace).  The next ticket is asked for once the current item's
+// reduction is done, so the atomic's latency hides under its epilogue.
+struct ItemQueue {
+  uint32_t* ctr;  // [8]
+  int total;
+};
+
+// Queue state kept in LDS by thread 0 between items, so that none of it is
+// held in registers across an item.
+struct QueueLds {
+  int item;    // the workgroup's next item, -1 when the queue is done
+  int chunks;  // chunks exhausted so far; the current one is (blockIdx.x + chunks) & 7
+};
+
+// Thread 0: turns ticket tk of the current chunk into the next item, moving
+// on to the following chunks (one more ticket each) while the ticket is past
+// the end of its chunk; the last ticket past a chunk's end resets its counter.
+__device__ __noinline__ void queue_advance(const ItemQueue& qu, QueueLds* s, int tk) {
+  const int per = (qu.total + 7) >> 3;
+  int c = s->chunks;
+  for (;;) {
+    const int q = (blockIdx.x + c) & 7;
+    const int nq = max(0, min(per, qu.total - q * per));
+    if (tk < nq) {
+      s->item = q * per + tk;
+      break;
+    }
+    if (tk == nq + (int)gridDim.x - 1) atomicExch(qu.ctr + q, 0u);
+    if (++c == 8) {
+      s->item = -1;
+      break;
+    }
+    tk = (int)atomicAdd(qu.ctr + ((blockIdx.x + c) & 7), 1u);
+  }
+  s->chunks = c;
+}
+
+// body(item, take): take() asks for the next ticket (thread 0 only; called
+// once, after the item's reduction, so the atomic overlaps its epilogue).
+template <typename Body>
+__device__ __forceinline__ void run_queue(const ItemQueue& qu, QueueLds* s, Body&& body) {
+  if (threadIdx.x == 0) {
+    s->chunks = 0;
+    queue_advance(qu, s, (int)atomicAdd(qu.ctr + (blockIdx.x & 7), 1u));
+  }
+  __syncthreads();
+  for (int item = s->item; item >= 0; item = s->item) {
+    int tk = 0;
+    body(item, [&]() {
+      if (threadIdx.x == 0) tk = (int)atomicAdd(qu.ctr + ((blockIdx.x + s->chunks) & 7), 1u);
+    });
+    __syncthreads();  // every thread has read s->item; the LDS tiles are free
+    if (threadIdx.x == 0) queue_advance(qu, s, tk);
+    __syncthreads();
+  }
 }
 
 // Calls f(std::integral_constant<int, n>) for the runtime n in 1..MAX.
@@ -277,6 +336,9 @@ __device__ __forceinline__ void dispatch_nbt(int n, Fn&& f) {
 // then the 128 lo bytes, in input order; xs [token][hidden/32][2 bytes] = the
 // hi and lo scale bytes of each block.  One thread per block.
 __global__ __launch_bounds__(256) void quant_x_kernel(FfnParams p) {
+  // the grouped GEMMs' queue counters start this call at 0 (they reset
+  // themselves at the end of each launch; this covers a fresh workspace)
+  if (blockIdx.x == 0 && threadIdx.x < kQueueWords) p.qctr[threadIdx.x] = 0u;
   const int nb = p.hidden / 32;
   const int64_t blk = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (blk >= (int64_t)p.n_tokens * nb) return;
@@ -386,9 +448,9 @@ __device__ __forceinline__ uint32_t split_e4m3x3(const float (&v)[2][4], float m
 // that a step's operand reads and MFMAs form one branch-free block.
 // LAZY: the gate-first lazy skip is on (its gate maxima are merged into
 // gmax); a separate instantiation, so the plain kernels keep their registers.
-template <int WT, int TT, int NBT, bool SC, bool O32, bool LAZY>
+template <int WT, int TT, int NBT, bool SC, bool O32, bool LAZY, typename Take>
 __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it, char* smem,
-                                             int wave, int lane) {
+                                             int wave, int lane, Take&& take) {
   using F = Fmt<WT>;
   constexpr int Q = F::Q;
   constexpr int TB = NBT;
@@ -659,6 +721,7 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
       }
   }
   wait_vm<0>();  // the reloads past the end
+  take();        // the next item's ticket, in flight during the epilogue
 
   // SwiGLU, then h as three E4M3 parts (split_e4m3x3) under the scale of
   // the wavefront's 32 rows, which are one 32-input block of the down
@@ -709,29 +772,27 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
 
 template <int WT, int TT, bool SC, bool O32, bool LAZY>
 __global__ __launch_bounds__(kGThreads, 2) void gemm_gate_up_kernel(FfnParams p, int seg_lo,
-                                                                     int seg_hi) {
+                                                                     int seg_hi,
+                                                                     uint32_t* qctr) {
   extern __shared__ __align__(16) char smem[];
   __shared__ int s_pref[kSegMax + 1];
   __shared__ int s_tmp[kGThreads / kWave];
+  __shared__ QueueLds s_q;
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int total = item_prefix<TT, kGuRows, false>(p, seg_lo, seg_hi, s_pref, s_tmp);
-  const int slots = (total + 7) & ~7;
-  for (int i = blockIdx.x; i < slots; i += gridDim.x) {
-    const int item = xcd_item(i, total);
-    if (item < 0) continue;
+  run_queue(ItemQueue{qctr, total}, &s_q, [&](int item, auto&& take) {
     const GItem it = find_item<TT, kGuRows, false>(p, seg_lo, seg_hi, s_pref, item);
     dispatch_nbt<TT / 16>((it.m + 15) >> 4, [&](auto nb) {
-      gate_up_item<WT, TT, decltype(nb)::value, SC, O32, LAZY>(p, it, smem, wave, lane);
+      gate_up_item<WT, TT, decltype(nb)::value, SC, O32, LAZY>(p, it, smem, wave, lane, take);
     });
-    __syncthreads();  // the LDS tiles are reused by the next item
-  }
+  });
 }
 
 // ------------------------------------------------------------- down
 
-template <int WT, int TT, int NBT, bool SC>
+template <int WT, int TT, int NBT, bool SC, typename Take>
 __device__ __forceinline__ void down_item(const FfnParams& p, const GItem& it, char* smem,
-                                          int wave, int lane) {
+                                          int wave, int lane, Take&& take) {
   using F = Fmt<WT>;
   constexpr int Q = F::Q;
   constexpr int TB = NBT;
@@ -906,6 +967,7 @@ __device__ __forceinline__ void down_item(const FfnParams& p, const GItem& it, c
     }
   }
   wait_vm<0>();
+  take();  // the next item's ticket, in flight during the epilogue
 
   // routing weight of each token column, then the per-slot outputs
 #pragma unroll
@@ -927,22 +989,19 @@ __device__ __forceinline__ void down_item(const FfnParams& p, const GItem& it, c
 
 template <int WT, int TT, bool SC>
 __global__ __launch_bounds__(kGThreads, 2) void gemm_down_kernel(FfnParams p, int seg_lo,
-                                                                  int seg_hi) {
+                                                                  int seg_hi, uint32_t* qctr) {
   extern __shared__ __align__(16) char smem[];
   __shared__ int s_pref[kSegMax + 1];
   __shared__ int s_tmp[kGThreads / kWave];
+  __shared__ QueueLds s_q;
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int total = item_prefix<TT, kDnRows, true>(p, seg_lo, seg_hi, s_pref, s_tmp);
-  const int slots = (total + 7) & ~7;
-  for (int i = blockIdx.x; i < slots; i += gridDim.x) {
-    const int item = xcd_item(i, total);
-    if (item < 0) continue;
+  run_queue(ItemQueue{qctr, total}, &s_q, [&](int item, auto&& take) {
     const GItem it = find_item<TT, kDnRows, true>(p, seg_lo, seg_hi, s_pref, item);
     dispatch_nbt<TT / 16>((it.m + 15) >> 4, [&](auto nb) {
-      down_item<WT, TT, decltype(nb)::value, SC>(p, it, smem, wave, lane);
+      down_item<WT, TT, decltype(nb)::value, SC>(p, it, smem, wave, lane, take);
     });
-    __syncthreads();
-  }
+  });
 }
 
 // ------------------------------------------------------ down on E4M3 parts
@@ -971,9 +1030,9 @@ __device__ __forceinline__ u32x4 row128_chunk(const char* plane, int n, int c) {
   return *reinterpret_cast<const u32x4*>(plane + n * 128 + ((c ^ ((n >> 1) & 7)) << 4));
 }
 
-template <int WT, int NBT, bool SC>
+template <int WT, int NBT, bool SC, typename Take>
 __device__ __forceinline__ void down3_item(const FfnParams& p, const GItem& it, char* smem,
-                                           int wave, int lane) {
+                                           int wave, int lane, Take&& take) {
   using F = Fmt<WT>;
   constexpr int Q = F::Q;
   constexpr int TB = NBT;
@@ -1185,6 +1244,7 @@ __device__ __forceinline__ void down3_item(const FfnParams& p, const GItem& it, 
     }
   }
   wait_vm<0>();
+  take();  // the next item's ticket, in flight during the epilogue
 
   // routing weight of each token column, then the per-slot outputs
 #pragma unroll
@@ -1206,22 +1266,19 @@ __device__ __forceinline__ void down3_item(const FfnParams& p, const GItem& it, 
 
 template <int WT, bool SC>
 __global__ __launch_bounds__(kGThreads, 2) void gemm_down3_kernel(FfnParams p, int seg_lo,
-                                                                   int seg_hi) {
+                                                                   int seg_hi, uint32_t* qctr) {
   extern __shared__ __align__(16) char smem[];
   __shared__ int s_pref[kSegMax + 1];
   __shared__ int s_tmp[kGThreads / kWave];
   const int lane = threadIdx.x & 63, wave = wave_id();
+  __shared__ QueueLds s_q;
   const int total = item_prefix<kD3Tok, kDnRows, true>(p, seg_lo, seg_hi, s_pref, s_tmp);
-  const int slots = (total + 7) & ~7;
-  for (int i = blockIdx.x; i < slots; i += gridDim.x) {
-    const int item = xcd_item(i, total);
-    if (item < 0) continue;
+  run_queue(ItemQueue{qctr, total}, &s_q, [&](int item, auto&& take) {
     const GItem it = find_item<kD3Tok, kDnRows, true>(p, seg_lo, seg_hi, s_pref, item);
     dispatch_nbt<kD3Tok / 16>((it.m + 15) >> 4, [&](auto nb) {
-      down3_item<WT, decltype(nb)::value, SC>(p, it, smem, wave, lane);
+      down3_item<WT, decltype(nb)::value, SC>(p, it, smem, wave, lane, take);
     });
-    __syncthreads();
-  }
+  });
 }
 
 template <typename... Params, typename... Args>
@@ -1260,6 +1317,13 @@ int64_t items_bound(const FfnParams& p, int seg_lo, int seg_hi, int tt, int rt, 
 
 constexpr int kGemmGrid = 256 * 2;  // 256 CUs, two workgroups each
 
+// The eight queue counters of a launch: gate/up of the routed experts (with
+// the shared one when it shares the launch), gate/up of a shared expert of
+// another type, then the same two for the down projection.
+uint32_t* queue_counters(const FfnParams& p, int seg_lo, bool down) {
+  return p.qctr + 8 * ((down ? 2 : 0) + (seg_lo >= p.n_experts ? 1 : 0));
+}
+
 int grid_for(int64_t items) {
   return (int)(items < kGemmGrid ? (items > 0 ? items : 1) : kGemmGrid);
 }
@@ -1271,7 +1335,8 @@ hipError_t gate_up_range_as(const FfnParams& p, int seg_lo, int seg_hi, hipStrea
   if (attr != hipSuccess) return attr;
   const int grid = grid_for(items_bound(p, seg_lo, seg_hi, TT, kGuRows, false));
   return launch(gemm_gate_up_kernel<WT, TT, SC, O32, LAZY>, dim3(grid), dim3(kGThreads),
-                (size_t)kGemmLds, stream, start, stop, p, seg_lo, seg_hi);
+                (size_t)kGemmLds, stream, start, stop, p, seg_lo, seg_hi,
+                queue_counters(p, seg_lo, false));
 }
 
 template <int WT, int TT, bool SC, bool O32>
@@ -1291,7 +1356,7 @@ hipError_t down3_range(const FfnParams& p, int seg_lo, int seg_hi, hipStream_t s
   if (attr != hipSuccess) return attr;
   const int grid = grid_for(items_bound(p, seg_lo, seg_hi, kD3Tok, kDnRows, true));
   return launch(gemm_down3_kernel<WT, SC>, dim3(grid), dim3(kGThreads), (size_t)kD3Lds, stream,
-                start, stop, p, seg_lo, seg_hi);
+                start, stop, p, seg_lo, seg_hi, queue_counters(p, seg_lo, true));
 }
 
 template <int WT, int TT, bool SC>
@@ -1301,7 +1366,7 @@ hipError_t down_range(const FfnParams& p, int seg_lo, int seg_hi, hipStream_t st
   if (attr != hipSuccess) return attr;
   const int grid = grid_for(items_bound(p, seg_lo, seg_hi, TT, kDnRows, true));
   return launch(gemm_down_kernel<WT, TT, SC>, dim3(grid), dim3(kGThreads), (size_t)kGemmLds,
-                stream, start, stop, p, seg_lo, seg_hi);
+                stream, start, stop, p, seg_lo, seg_hi, queue_counters(p, seg_lo, true));
 }
 
 // Segments of one weight type go through one launch: everything at once when

@@ -125,7 +125,8 @@ moe_status plan_ffn(const moe_layer* layer, int n_tokens, FfnPlan* plan) {
   const size_t gbuf_bytes =
       n <= kGateFirstMaxTokens ? align_up((size_t)nk * layer->inter * 4u, 256) : 0;
   plan->off_gmax = plan->off_xs + xs_bytes;
-  plan->off_gbuf = plan->off_gmax + gmax_bytes;
+  plan->off_qctr = plan->off_gmax + gmax_bytes;
+  plan->off_gbuf = plan->off_qctr + (n > 0 ? 256 : 0);
   plan->total = plan->off_gbuf + gbuf_bytes;
   return MOE_OK;
 }

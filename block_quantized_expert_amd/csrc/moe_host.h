@@ -26,6 +26,8 @@ namespace moe {
 //   gmax       : u32 [n_tokens*top_k]      gate-first lazy skip: the largest
 //                                         |SiLU(g)| of each routed slot (fp32
 //                                         bits)
+//   qctr       : u32 [32]                  the grouped GEMMs' item-queue
+//                                         counters (256 bytes)
 //   gbuf       : fp32 [n_tokens*top_k][inter]  gate outputs kept between the
 //                                         gate and up passes of the small-batch
 //                                         lazy path (batches of up to
@@ -44,6 +46,7 @@ struct FfnPlan {
   size_t off_h3s;
   size_t off_gmax;
   size_t off_gbuf;
+  size_t off_qctr;
   size_t total;
 };
 

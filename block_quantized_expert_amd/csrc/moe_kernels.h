@@ -52,7 +52,11 @@ struct FfnParams {
   float lazy_tau;
   uint32_t* gmax;
   float* gbuf;
+  // the grouped GEMMs' item-queue counters, kQueueWords of them
+  uint32_t* qctr;
 };
+
+constexpr int kQueueWords = 32;  // 4 launches x 8 XCD chunks
 
 // Options of the learned router beyond plain top-k (moe_opts of the C ABI,
 // checked on the host): expert groups with a selection-only bias, and tail

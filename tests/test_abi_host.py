@@ -77,7 +77,9 @@ def test_ffn_workspace_bytes():
     xq = n * 4096 * 2          # activations as two E4M3 parts
     xs = n * 4096 // 16        # their scale bytes
     gmax = n * 6 * 4           # lazy skip: each routed slot's largest |SiLU(g)|
-    assert B.lib().moe_ffn_workspace_bytes(ctypes.byref(L), n) == 2 * h + o + xq + xs + gmax
+    qctr = 256                 # item-queue counters of the grouped GEMMs
+    assert B.lib().moe_ffn_workspace_bytes(ctypes.byref(L), n) == \
+        2 * h + o + xq + xs + gmax + qctr
     # up to 16 tokens: also the gate outputs of the gate-first lazy pass
     n = 16
     slots = n * 6 + n
@@ -87,7 +89,7 @@ def test_ffn_workspace_bytes():
     gmax = -(-n * 6 * 4 // 256) * 256
     gbuf = n * 6 * 2048 * 4
     assert B.lib().moe_ffn_workspace_bytes(ctypes.byref(L), n) == \
-        2 * h + o + n * 4096 * 2 + xs + gmax + gbuf
+        2 * h + o + n * 4096 * 2 + xs + gmax + 256 + gbuf
     assert B.lib().moe_ffn_workspace_bytes(ctypes.byref(L), 0) == 0
     assert B.lib().moe_ffn_workspace_bytes(ctypes.byref(_layer(hidden=100)), 8) == 0
     assert B.lib().moe_ffn_workspace_bytes(None, 8) == 0
