@@ -57,17 +57,23 @@
 namespace moe {
 namespace {
 
-constexpr int kGThreads = 256;  // four wavefronts, two workgroups per CU
-constexpr int kGWaves = kGThreads / kWave;
+// Two workgroups of four wavefronts per CU (two wavefronts per SIMD, 256
+// registers each).  One workgroup of eight (kGWaves = 8: a token tile staged
+// once per CU for 256 gate/up or 512 down rows) measured no faster on the
+// 4096-token batch and 5-13 % slower on 32 and 512 tokens: a CU then has no
+// second workgroup whose steps cover an item's prologue and epilogue.
+constexpr int kGWaves = 4;
+constexpr int kGPerCU = 8 / kGWaves;  // workgroups per CU
+constexpr int kGThreads = kGWaves * kWave;
 constexpr int kGuRows = 32 * kGWaves;  // intermediate rows per gate/up item
 constexpr int kDnRows = 64 * kGWaves;  // hidden rows per down item
 constexpr int kSegMax = MOE_MAX_EXPERTS + 1;
-// dynamic LDS of either kernel; with the static item prefix (4 KiB) two
-// workgroups must fit the 160 KiB of a CU
-constexpr int kGemmLds = 74 * 1024;
+// dynamic LDS of either kernel; with the static item prefix (4 KiB) the
+// workgroups of a CU must fit its 160 KiB
+constexpr int kGemmLds = kGWaves == 8 ? 106 * 1024 : 74 * 1024;
 // scale blocks in LDS: after two token tiles of up to five blocks (gate/up,
-// 128 rows x H/32 bytes per matrix, H <= 4096) or two h_hi/h_lo pairs of up
-// to three blocks (down, 256 rows x I/32 bytes, I <= 2048)
+// kGuRows rows x H/32 bytes per matrix, H <= 4096) or two h_hi/h_lo pairs
+// of up to three blocks (down, kDnRows rows x I/32 bytes, I <= 2048)
 constexpr int kGuScaleOff = 2 * 16 * 5 * 256;
 constexpr int kDnScaleOff = 2 * 2 * 16 * 3 * 256;
 // gate/up: the scale bytes of two token tiles (8 per row and step, up to 128
@@ -82,8 +88,9 @@ static_assert(kTokScaleOff + 2 * kTokScaleBytes <= kGemmLds, "gate/up LDS");
 constexpr int kTokChunkOff = 2 * 112 * 256;
 static_assert(kTokChunkOff + 2 * 128 * 32 <= kGemmLds, "gate/up LDS");
 // dynamic LDS + the static item prefix and scan words of a workgroup (plus
-// alignment): two workgroups in the 160 KiB of a CU
-static_assert(kGemmLds + (kSegMax + 1 + kGWaves) * 4 + 64 <= 80 * 1024, "two workgroups per CU");
+// alignment): kGPerCU workgroups in the 160 KiB of a CU
+static_assert(kGemmLds + (kSegMax + 1 + kGWaves) * 4 + 64 <= 160 * 1024 / kGPerCU,
+              "workgroups per CU");
 static_assert(kDnScaleOff + kDnRows * (2048 / 32) <= kGemmLds, "down LDS");
 
 struct GItem {
@@ -575,15 +582,15 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
         }
       }
   };
-  // scales (kSC): the item's 128 rows of each matrix are consecutive, so
-  // their scale bytes are one contiguous block (128 * H/32 bytes), copied
+  // scales (kSC): the item's kGuRows rows of each matrix are consecutive, so
+  // their scale bytes are one contiguous block (kGuRows * H/32 bytes), copied
   // into LDS at the start of the item (1 KiB per copy instruction) and read
   // from there at every step.  Loaded from memory per step (one byte per
   // row) they doubled the weight stream's requests; loaded per four steps
   // (16 bytes) the lines left the L2 between loads and were fetched up to
   // eight times each.
   constexpr int kTokB = kSC ? 16 * NBT * 256 : TT * 256;  // bytes of one token tile
-  char* const sscale = smem + kGuScaleOff;                // [mat][128 rows][sb]
+  char* const sscale = smem + kGuScaleOff;                // [mat][kGuRows][sb]
   auto copy_scales = [&]() {
     const int64_t bytes = (int64_t)kGuRows * sb;  // per matrix
     const int64_t row0 = (shared ? 0 : (int64_t)it.seg * rows) + it.row0;
@@ -758,7 +765,8 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
     const uint32_t sbytes = split_e4m3x3(v, mag, part);
     const int n = tb * 16 + r16;
     if (live && n < it.m) {
-      uint8_t* dst = p.h3 + (int64_t)(it.slot0 + n) * 3 * hs + (it.row0 / 128) * 384 + 32 * wave + 4 * g;
+      const int hrow = it.row0 + 32 * wave;  // h3 keeps 128-row blocks of three parts
+      uint8_t* dst = p.h3 + (int64_t)(it.slot0 + n) * 3 * hs + (hrow >> 7) * 384 + (hrow & 127) + 4 * g;
 #pragma unroll
       for (int q = 0; q < 3; ++q)
 #pragma unroll
@@ -771,7 +779,7 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
 }
 
 template <int WT, int TT, bool SC, bool O32, bool LAZY>
-__global__ __launch_bounds__(kGThreads, 2) void gemm_gate_up_kernel(FfnParams p, int seg_lo,
+__global__ __launch_bounds__(kGThreads, kGPerCU) void gemm_gate_up_kernel(FfnParams p, int seg_lo,
                                                                      int seg_hi,
                                                                      uint32_t* qctr) {
   extern __shared__ __align__(16) char smem[];
@@ -879,10 +887,10 @@ __device__ __forceinline__ void down_item(const FfnParams& p, const GItem& it, c
       }
     }
   };
-  // scales (kSC), as in gate/up: the item's rows (up to 256, fewer in the
+  // scales (kSC), as in gate/up: the item's rows (up to kDnRows, fewer in the
   // last tile of the matrix) as one contiguous block in LDS
   constexpr int kTokB = kSC ? 16 * NBT * 256 : TT * 256;  // bytes of one h tile
-  char* const sscale = smem + kDnScaleOff;                // [256 rows][sb]
+  char* const sscale = smem + kDnScaleOff;                // [kDnRows][sb]
   auto copy_scales = [&]() {
     const int64_t bytes = (int64_t)min(kDnRows, p.hidden - it.row0) * sb;
     const uint8_t* src = sbase + ((shared ? 0 : (int64_t)it.seg * p.hidden) + it.row0) * sb;
@@ -988,7 +996,7 @@ __device__ __forceinline__ void down_item(const FfnParams& p, const GItem& it, c
 }
 
 template <int WT, int TT, bool SC>
-__global__ __launch_bounds__(kGThreads, 2) void gemm_down_kernel(FfnParams p, int seg_lo,
+__global__ __launch_bounds__(kGThreads, kGPerCU) void gemm_down_kernel(FfnParams p, int seg_lo,
                                                                   int seg_hi, uint32_t* qctr) {
   extern __shared__ __align__(16) char smem[];
   __shared__ int s_pref[kSegMax + 1];
@@ -1021,7 +1029,7 @@ constexpr int kD3Tok = 64;
 constexpr int kD3Full = 2 * 3 * kD3Tok * 128 + 2 * kD3Tok * 16;             // full tiles
 constexpr int kD3Sc = 2 * 3 * 48 * 128 + kDnRows * (2048 / 32) + 2 * 48 * 16;  // 3 blocks + scales
 constexpr int kD3Lds = kD3Full > kD3Sc ? kD3Full : kD3Sc;
-static_assert(kD3Lds + (kSegMax + 1 + kGWaves) * 4 + 64 <= 80 * 1024, "two workgroups per CU");
+static_assert(kD3Lds <= kGemmLds, "down LDS");
 
 // 16 bytes of a 128-byte LDS row: chunk c of row n sits at position
 // c ^ ((n >> 1) & 7), so the 16 rows that one operand read touches (two rows
@@ -1062,23 +1070,23 @@ __device__ __forceinline__ void down3_item(const FfnParams& p, const GItem& it, 
   const uint8_t* sbase = shared ? p.sdown_s : p.down_s;
 
   // h copies: one instruction fills 8 rows of a part (lane l: row + l / 8,
-  // position l % 8); wavefront w fills the row groups w, w + 4 and w + 8 of
-  // each part (the ones below the tile), rows past the tile's tokens repeat
-  // row 0.  Scale bytes: 16 rows per instruction (four lanes per row),
-  // groups w and w + 4.
-  constexpr int kRG = (2 * NBT + 3) / 4;   // row groups of 8 per wavefront
-  constexpr int kSG = (NBT + 3) / 4;       // scale groups of 16 per wavefront
+  // position l % 8); wavefront w fills the row groups w, w + W, ... of each
+  // part (W wavefronts; the groups below the tile), rows past the tile's
+  // tokens repeat row 0.  Scale bytes: 16 rows per instruction (four lanes
+  // per row), groups w, w + W, ...
+  constexpr int kRG = (2 * NBT + kGWaves - 1) / kGWaves;  // row groups of 8 per wavefront
+  constexpr int kSG = (NBT + kGWaves - 1) / kGWaves;      // scale groups of 16 per wavefront
   int64_t hsrc[kRG];
 #pragma unroll
   for (int e = 0; e < kRG; ++e) {
-    const int n = 8 * (wave + 4 * e) + (lane >> 3);
+    const int n = 8 * (wave + kGWaves * e) + (lane >> 3);
     const int c = (lane & 7) ^ ((n >> 1) & 7);
     hsrc[e] = (int64_t)(it.slot0 + (n < it.m ? n : 0)) * 3 * hs + 16 * c;
   }
   const uint8_t* hss[kSG];
 #pragma unroll
   for (int e = 0; e < kSG; ++e) {
-    const int ns = 16 * (wave + 4 * e) + (lane >> 2);
+    const int ns = 16 * (wave + kGWaves * e) + (lane >> 2);
     hss[e] = p.h3s + (int64_t)(it.slot0 + (ns < it.m ? ns : 0)) * (hs / 32) * 4 + 4 * (lane & 3);
   }
   // LDS: tiles, the weight scales (kSC), the tiles' scale bytes
@@ -1094,14 +1102,14 @@ __device__ __forceinline__ void down3_item(const FfnParams& p, const GItem& it, 
     for (int q = 0; q < 3; ++q)
 #pragma unroll
       for (int e = 0; e < kRG; ++e) {
-        const int rg = wave + 4 * e;
+        const int rg = wave + kGWaves * e;
         if (rg < 2 * nbt)
           __builtin_amdgcn_global_load_lds(p.h3 + hsrc[e] + ks * 384 + q * 128,
                                            lds(dst + q * kPlane + rg * 8 * 128), 16, 0, 0);
       }
 #pragma unroll
     for (int e = 0; e < kSG; ++e) {
-      const int sg = wave + 4 * e;
+      const int sg = wave + kGWaves * e;
       if (sg < nbt)
         __builtin_amdgcn_global_load_lds(hss[e] + ks * 16, lds(sbuf(ks) + sg * 256), 4, 0, 0);
     }
@@ -1157,7 +1165,7 @@ __device__ __forceinline__ void down3_item(const FfnParams& p, const GItem& it, 
     }
   };
   // weight scales (kSC): the item's rows as one contiguous block in LDS
-  char* const sscale = smem + kWScOff;  // [256 rows][sb]
+  char* const sscale = smem + kWScOff;  // [kDnRows][sb]
   auto copy_scales = [&]() {
     const int64_t bytes = (int64_t)min(kDnRows, p.hidden - it.row0) * sb;
     const uint8_t* src = sbase + ((shared ? 0 : (int64_t)it.seg * p.hidden) + it.row0) * sb;
@@ -1265,7 +1273,7 @@ __device__ __forceinline__ void down3_item(const FfnParams& p, const GItem& it, 
 }
 
 template <int WT, bool SC>
-__global__ __launch_bounds__(kGThreads, 2) void gemm_down3_kernel(FfnParams p, int seg_lo,
+__global__ __launch_bounds__(kGThreads, kGPerCU) void gemm_down3_kernel(FfnParams p, int seg_lo,
                                                                    int seg_hi, uint32_t* qctr) {
   extern __shared__ __align__(16) char smem[];
   __shared__ int s_pref[kSegMax + 1];
@@ -1315,7 +1323,7 @@ int64_t items_bound(const FfnParams& p, int seg_lo, int seg_hi, int tt, int rt, 
   return items;
 }
 
-constexpr int kGemmGrid = 256 * 2;  // 256 CUs, two workgroups each
+constexpr int kGemmGrid = 256 * kGPerCU;  // 256 CUs
 
 // The eight queue counters of a launch: gate/up of the routed experts (with
 // the shared one when it shares the launch), gate/up of a shared expert of
