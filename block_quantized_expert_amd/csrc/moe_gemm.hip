@@ -241,36 +241,47 @@ __device__ __forceinline__ void step_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
-// Dynamic item queue of one launch.  Workgroups are dealt to the eight XCDs
+// Item schedule of one launch.  Workgroups are dealt to the eight XCDs
 // round-robin (workgroup b runs on XCD b % 8), and each XCD has its own L2.
-// The item order is cut into eight contiguous chunks, one per XCD, each with
-// a counter in the workspace: the row tiles of one expert (which share its
-// token rows) and the token tiles of one row tile (which share its weights)
-// then meet in the same L2.  A workgroup takes tickets from its own XCD's
-// counter while that chunk lasts, then from the other chunks in turn, so
-// workgroups that run out of their own items take over the rest instead of
-// idling (a static assignment left the busiest workgroup 1.14 (gate/up) and
-// 1.25 (down) times the mean work on a hash-routed batch of 4096 tokens).
-// Every workgroup takes exactly one ticket past the end of every chunk, so
-// the holder of the last one (chunk items + grid - 1) resets that counter to
-// 0 for the next launch; the gate/up pass of each call also zeroes them (a
-// fresh workspace).  The next ticket is asked for once the current item's
-// reduction is done, so the atomic's latency hides under its epilogue.
+// The item order is cut into eight contiguous chunks, one per XCD: the row
+// tiles of one expert (which share its token rows) and the token tiles of
+// one row tile (which share its weights) then meet in the same L2.
+//  - static: workgroup b takes items b / 8, b / 8 + grid / 8, ... of chunk
+//    b % 8;
+//  - dynamic: each chunk has a counter in the workspace; a workgroup takes
+//    tickets from its own XCD's counter while that chunk lasts, then from
+//    the other chunks in turn, so workgroups that run out of their own items
+//    take over the rest instead of idling.  Every workgroup takes exactly one
+//    ticket past the end of every chunk, so the holder of the last one
+//    (chunk items + grid - 1) resets that counter to 0 for the next launch;
+//    the gate/up pass of each call also zeroes them (a fresh workspace).
+//    The next ticket is asked for once the current item's reduction is
+//    done, so the atomic's latency hides under its epilogue.
+// Tickets on one counter serialise (about 0.1 us each), so the dynamic
+// schedule pays only for long items of uneven length: on a hash-routed
+// batch of 4096 tokens (about 96 per expert) it took the routed gate/up
+// from 873 to 829 us and the down from 775 to 640 us (a static schedule
+// left the busiest workgroup 1.14 and 1.25 times the mean work); on 32 and
+// 512 tokens (one-token items by the thousand) it was 10-20 % slower.
 struct ItemQueue {
   uint32_t* ctr;  // [8]
   int total;
+  bool dynamic;
 };
 
-// Queue state kept in LDS by thread 0 between items, so that none of it is
-// held in registers across an item.
+// Schedule state kept in LDS by thread 0 between items, so that none of it
+// is held in registers across an item.
 struct QueueLds {
-  int item;    // the workgroup's next item, -1 when the queue is done
-  int chunks;  // chunks exhausted so far; the current one is (blockIdx.x + chunks) & 7
+  int item;    // the workgroup's next item, -1 when it has none left
+  int chunks;  // dynamic: chunks exhausted so far, the current one is
+               // (blockIdx.x + chunks) & 7; static: the workgroup's index
+               // into the dealt order
 };
 
-// Thread 0: turns ticket tk of the current chunk into the next item, moving
-// on to the following chunks (one more ticket each) while the ticket is past
-// the end of its chunk; the last ticket past a chunk's end resets its counter.
+// Thread 0, dynamic schedule: turns ticket tk of the current chunk into the
+// next item, moving on to the following chunks (one more ticket each) while
+// the ticket is past the end of its chunk; the last ticket past a chunk's
+// end resets its counter.
 __device__ __noinline__ void queue_advance(const ItemQueue& qu, QueueLds* s, int tk) {
   const int per = (qu.total + 7) >> 3;
   int c = s->chunks;
@@ -291,22 +302,49 @@ __device__ __noinline__ void queue_advance(const ItemQueue& qu, QueueLds* s, int
   s->chunks = c;
 }
 
-// body(item, take): take() asks for the next ticket (thread 0 only; called
-// once, after the item's reduction, so the atomic overlaps its epilogue).
+// Thread 0, static schedule: the next item of the dealt order from index i
+// (i, i + grid, ...: chunk i % 8, position i / 8), skipping the padding of
+// short chunks.
+__device__ __forceinline__ void static_advance(const ItemQueue& qu, QueueLds* s, int i) {
+  const int per = (qu.total + 7) >> 3;
+  for (; i < 8 * per; i += gridDim.x) {
+    const int item = (i & 7) * per + (i >> 3);
+    if (item < qu.total) {
+      s->item = item;
+      s->chunks = i;
+      return;
+    }
+  }
+  s->item = -1;
+}
+
+// body(item, take): take() asks for the next ticket (dynamic: thread 0;
+// called once per item, after its reduction, so the atomic overlaps the
+// epilogue; static: nothing).
 template <typename Body>
 __device__ __forceinline__ void run_queue(const ItemQueue& qu, QueueLds* s, Body&& body) {
   if (threadIdx.x == 0) {
-    s->chunks = 0;
-    queue_advance(qu, s, (int)atomicAdd(qu.ctr + (blockIdx.x & 7), 1u));
+    if (qu.dynamic) {
+      s->chunks = 0;
+      queue_advance(qu, s, (int)atomicAdd(qu.ctr + (blockIdx.x & 7), 1u));
+    } else {
+      static_advance(qu, s, blockIdx.x);
+    }
   }
   __syncthreads();
   for (int item = s->item; item >= 0; item = s->item) {
     int tk = 0;
     body(item, [&]() {
-      if (threadIdx.x == 0) tk = (int)atomicAdd(qu.ctr + ((blockIdx.x + s->chunks) & 7), 1u);
+      if (qu.dynamic && threadIdx.x == 0)
+        tk = (int)atomicAdd(qu.ctr + ((blockIdx.x + s->chunks) & 7), 1u);
     });
     __syncthreads();  // every thread has read s->item; the LDS tiles are free
-    if (threadIdx.x == 0) queue_advance(qu, s, tk);
+    if (threadIdx.x == 0) {
+      if (qu.dynamic)
+        queue_advance(qu, s, tk);
+      else
+        static_advance(qu, s, s->chunks + gridDim.x);
+    }
     __syncthreads();
   }
 }
@@ -406,9 +444,21 @@ __device__ __forceinline__ i32x8 weight_operand(const u32x4 (&q)[Fmt<WT>::Q]) {
                  (int)q[1][0], (int)q[1][1], (int)q[1][2], (int)q[1][3]};
 }
 
-// 16 bytes of an LDS tile row: chunk c of row n sits at position c ^ (n & 15).
-__device__ __forceinline__ u32x4 tile_chunk(const char* row, int c, int r16) {
-  return *reinterpret_cast<const u32x4*>(row + ((c ^ r16) << 4));
+// LDS-typed views (32-bit addresses) of the shared-memory tiles.
+using lds_cptr = const __attribute__((address_space(3))) char*;
+typedef const __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef const __attribute__((address_space(3))) uint16_t lds_u16;
+typedef const __attribute__((address_space(3))) uint32_t lds_u32;
+__device__ __forceinline__ lds_cptr to_lds(const char* p) {
+  return (lds_cptr)p;  // an address-space cast: the tiles live in LDS
+}
+
+// Hides a value's origin from the optimiser (an empty register constraint,
+// no instruction), so that constant offsets added to it afterwards stay
+// immediates instead of being folded into hoisted per-offset registers.
+template <typename T>
+__device__ __forceinline__ void opaque(T& v) {
+  asm volatile("" : "+v"(v));
 }
 
 __device__ __forceinline__ i32x8 join8(u32x4 a, u32x4 b) {
@@ -661,30 +711,49 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
     // operand u = 2 tb + part (part 0: hi bytes, chunks g and 4+g; part 1:
     // lo bytes, chunks 8+g and 12+g) is read while operand u-1 multiplies,
     // so two 8-register operands are live at a time
-    i32x8 bop[2];
+    // The lane's four chunk addresses in token block 0 and its scale bytes'
+    // address, once per step; block tb lies tb * 4096 (scales tb * 16 *
+    // kTsStride) bytes further, which the LDS reads take as their immediate
+    // offset.  (Written as one expression per read, the compiler hoists a
+    // separate loop-invariant register per token block and part.)
+    lds_cptr pc[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      pc[c] = to_lds(cur) + r16 * 256 + (((4 * c + g) ^ r16) << 4);
+      opaque(pc[c]);
+    }
+    lds_cptr ps = to_lds(cts) + r16 * kTsStride + 2 * g;
+    opaque(ps);
+    // operand u is read kAhead operands before it multiplies (a ring of
+    // kAhead + 1 eight-register operands), so the LDS latency is covered by
+    // 4 * kAhead instructions
+    constexpr int kAhead = 1;
+    i32x8 bop[kAhead + 1];
     uint32_t sbt[2];
     auto read_op = [&](int u) {
-      const int n = (u >> 1) * 16 + r16;
-      const char* row = cur + n * 256;
-      const int c0 = (u & 1) * 8 + g;
-      bop[u & 1] = join8(tile_chunk(row, c0, r16), tile_chunk(row, c0 + 4, r16));
-      if ((u & 1) == 0)
-        sbt[(u >> 1) & 1] = *reinterpret_cast<const uint16_t*>(cts + n * kTsStride + 2 * g);
+      const int tb = u >> 1, part = u & 1;
+      bop[u % (kAhead + 1)] =
+          join8(*reinterpret_cast<const lds_u32x4*>(pc[2 * part] + tb * 4096),
+                *reinterpret_cast<const lds_u32x4*>(pc[2 * part + 1] + tb * 4096));
+      if (part == 0)
+        sbt[tb & 1] = *reinterpret_cast<const lds_u16*>(ps + tb * 16 * kTsStride);
     };
-    read_op(0);
+#pragma unroll
+    for (int u = 0; u < kAhead && u < 2 * TB; ++u) read_op(u);
 #pragma unroll
     for (int u = 0; u < 2 * TB; ++u) {
-      if (u + 1 < 2 * TB) read_op(u + 1);
+      if (u + kAhead < 2 * TB) read_op(u + kAhead);
       const int tb = u >> 1;
+      const i32x8& b = bop[u % (kAhead + 1)];
 #pragma unroll
       for (int mat = 0; mat < 2; ++mat)
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
           if ((u & 1) == 0)
-            acc[mat][rb][tb] = mfma_scaled<FA, 0, 0>(a[mat][rb], bop[0], acc[mat][rb][tb],
+            acc[mat][rb][tb] = mfma_scaled<FA, 0, 0>(a[mat][rb], b, acc[mat][rb][tb],
                                                      sa[mat][rb], sbt[tb & 1]);
           else
-            acc[mat][rb][tb] = mfma_scaled<FA, 0, 1>(a[mat][rb], bop[1], acc[mat][rb][tb],
+            acc[mat][rb][tb] = mfma_scaled<FA, 0, 1>(a[mat][rb], b, acc[mat][rb][tb],
                                                      sa[mat][rb], sbt[tb & 1]);
         }
       __builtin_amdgcn_sched_barrier(0);
@@ -788,7 +857,7 @@ __global__ __launch_bounds__(kGThreads, kGPerCU) void gemm_gate_up_kernel(FfnPar
   __shared__ QueueLds s_q;
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int total = item_prefix<TT, kGuRows, false>(p, seg_lo, seg_hi, s_pref, s_tmp);
-  run_queue(ItemQueue{qctr, total}, &s_q, [&](int item, auto&& take) {
+  run_queue(ItemQueue{qctr, total, qctr != nullptr}, &s_q, [&](int item, auto&& take) {
     const GItem it = find_item<TT, kGuRows, false>(p, seg_lo, seg_hi, s_pref, item);
     dispatch_nbt<TT / 16>((it.m + 15) >> 4, [&](auto nb) {
       gate_up_item<WT, TT, decltype(nb)::value, SC, O32, LAZY>(p, it, smem, wave, lane, take);
@@ -1004,7 +1073,7 @@ __global__ __launch_bounds__(kGThreads, kGPerCU) void gemm_down_kernel(FfnParams
   __shared__ QueueLds s_q;
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int total = item_prefix<TT, kDnRows, true>(p, seg_lo, seg_hi, s_pref, s_tmp);
-  run_queue(ItemQueue{qctr, total}, &s_q, [&](int item, auto&& take) {
+  run_queue(ItemQueue{qctr, total, qctr != nullptr}, &s_q, [&](int item, auto&& take) {
     const GItem it = find_item<TT, kDnRows, true>(p, seg_lo, seg_hi, s_pref, item);
     dispatch_nbt<TT / 16>((it.m + 15) >> 4, [&](auto nb) {
       down_item<WT, TT, decltype(nb)::value, SC>(p, it, smem, wave, lane, take);
@@ -1031,12 +1100,9 @@ constexpr int kD3Sc = 2 * 3 * 48 * 128 + kDnRows * (2048 / 32) + 2 * 48 * 16;  /
 constexpr int kD3Lds = kD3Full > kD3Sc ? kD3Full : kD3Sc;
 static_assert(kD3Lds <= kGemmLds, "down LDS");
 
-// 16 bytes of a 128-byte LDS row: chunk c of row n sits at position
-// c ^ ((n >> 1) & 7), so the 16 rows that one operand read touches (two rows
-// share a 256-byte bank line) hit distinct banks.
-__device__ __forceinline__ u32x4 row128_chunk(const char* plane, int n, int c) {
-  return *reinterpret_cast<const u32x4*>(plane + n * 128 + ((c ^ ((n >> 1) & 7)) << 4));
-}
+// An h plane in LDS has rows of 128 bytes: chunk c of row n sits at
+// position c ^ ((n >> 1) & 7), so the 16 rows that one operand read touches
+// (two rows share a 256-byte bank line) hit distinct banks.
 
 template <int WT, int NBT, bool SC, typename Take>
 __device__ __forceinline__ void down3_item(const FfnParams& p, const GItem& it, char* smem,
@@ -1195,30 +1261,45 @@ __device__ __forceinline__ void down3_item(const FfnParams& p, const GItem& it, 
       sa[rb] = kSC ? scale_byte(rb, ks) : kCh ? sp[rb] >> (8 * (ks & 3)) : uu[rb];
       a[rb] = weight_operand<WT>(qq[rb]);
     }
-    // operand u = 3 tb + part is read while operand u-1 multiplies
-    i32x8 bop[2];
+    // operand u = 3 tb + part (h part q = u % 3).  The lane's two chunk addresses in token block 0 of part 0 and its scale
+    // bytes' address are formed once per step (the swizzle depends on the
+    // row within the block only); part q and block tb lie q * kPlane +
+    // tb * 2048 (scales tb * 256) bytes further: immediate offsets.
+    lds_cptr pc[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      pc[c] = to_lds(cur) + r16 * 128 + (((4 * c + g) ^ ((r16 >> 1) & 7)) << 4);
+      opaque(pc[c]);
+    }
+    lds_cptr ps = to_lds(cts) + r16 * 16 + 4 * g;
+    opaque(ps);
+    // a ring of kAhead + 1 operands: operand u is read kAhead before use
+    constexpr int kAhead = 1;
+    i32x8 bop[kAhead + 1];
     uint32_t sbt[2];
     auto read_op = [&](int u) {
       const int tb = u / 3, q = u % 3;
-      const int n = tb * 16 + r16;
-      const char* plane = cur + q * kPlane;
-      bop[u & 1] = join8(row128_chunk(plane, n, g), row128_chunk(plane, n, g + 4));
-      if (q == 0) sbt[tb & 1] = *reinterpret_cast<const uint32_t*>(cts + n * 16 + 4 * g);
+      const int off = q * kPlane + tb * 2048;
+      bop[u % (kAhead + 1)] = join8(*reinterpret_cast<const lds_u32x4*>(pc[0] + off),
+                                    *reinterpret_cast<const lds_u32x4*>(pc[1] + off));
+      if (q == 0) sbt[tb & 1] = *reinterpret_cast<const lds_u32*>(ps + tb * 256);
     };
-    read_op(0);
+#pragma unroll
+    for (int u = 0; u < kAhead && u < 3 * TB; ++u) read_op(u);
 #pragma unroll
     for (int u = 0; u < 3 * TB; ++u) {
-      if (u + 1 < 3 * TB) read_op(u + 1);
+      if (u + kAhead < 3 * TB) read_op(u + kAhead);
       const int tb = u / 3, q = u % 3;
+      const i32x8& b = bop[u % (kAhead + 1)];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         if (rb < nrb) {
           if (q == 0)
-            acc[rb][tb] = mfma_scaled<FA, 0, 0>(a[rb], bop[u & 1], acc[rb][tb], sa[rb], sbt[tb & 1]);
+            acc[rb][tb] = mfma_scaled<FA, 0, 0>(a[rb], b, acc[rb][tb], sa[rb], sbt[tb & 1]);
           else if (q == 1)
-            acc[rb][tb] = mfma_scaled<FA, 0, 1>(a[rb], bop[u & 1], acc[rb][tb], sa[rb], sbt[tb & 1]);
+            acc[rb][tb] = mfma_scaled<FA, 0, 1>(a[rb], b, acc[rb][tb], sa[rb], sbt[tb & 1]);
           else
-            acc[rb][tb] = mfma_scaled<FA, 0, 2>(a[rb], bop[u & 1], acc[rb][tb], sa[rb], sbt[tb & 1]);
+            acc[rb][tb] = mfma_scaled<FA, 0, 2>(a[rb], b, acc[rb][tb], sa[rb], sbt[tb & 1]);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -1281,7 +1362,7 @@ __global__ __launch_bounds__(kGThreads, kGPerCU) void gemm_down3_kernel(FfnParam
   const int lane = threadIdx.x & 63, wave = wave_id();
   __shared__ QueueLds s_q;
   const int total = item_prefix<kD3Tok, kDnRows, true>(p, seg_lo, seg_hi, s_pref, s_tmp);
-  run_queue(ItemQueue{qctr, total}, &s_q, [&](int item, auto&& take) {
+  run_queue(ItemQueue{qctr, total, qctr != nullptr}, &s_q, [&](int item, auto&& take) {
     const GItem it = find_item<kD3Tok, kDnRows, true>(p, seg_lo, seg_hi, s_pref, item);
     dispatch_nbt<kD3Tok / 16>((it.m + 15) >> 4, [&](auto nb) {
       down3_item<WT, decltype(nb)::value, SC>(p, it, smem, wave, lane, take);
@@ -1325,11 +1406,17 @@ int64_t items_bound(const FfnParams& p, int seg_lo, int seg_hi, int tt, int rt, 
 
 constexpr int kGemmGrid = 256 * kGPerCU;  // 256 CUs
 
-// The eight queue counters of a launch: gate/up of the routed experts (with
-// the shared one when it shares the launch), gate/up of a shared expert of
-// another type, then the same two for the down projection.
+// The eight queue counters of a launch with the dynamic schedule, or null
+// for the static one.  Dynamic: launches with the routed experts when they
+// average at least 32 slots each (long items of uneven length); a launch of
+// the shared expert alone has items of one size.  Counters: gate/up of the
+// routed experts (with the shared one when it shares the launch), gate/up of
+// a shared expert of another type, then the same two for the down
+// projection.
 uint32_t* queue_counters(const FfnParams& p, int seg_lo, bool down) {
-  return p.qctr + 8 * ((down ? 2 : 0) + (seg_lo >= p.n_experts ? 1 : 0));
+  const bool shared_only = seg_lo >= p.n_experts;
+  if (shared_only || (int64_t)p.n_tokens * p.top_k < 32 * (int64_t)p.n_experts) return nullptr;
+  return p.qctr + 8 * ((down ? 2 : 0) + (shared_only ? 1 : 0));
 }
 
 int grid_for(int64_t items) {
