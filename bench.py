@@ -58,6 +58,7 @@ HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
 MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8, published
 HEADLINE = "hash4096"
+PACK = True  # --no-pack: the batched GEMMs read the row-major weights
 NESTED = ["tiny", "decode1", "decode32", "prefill512"]
 REPS = 5
 
@@ -101,16 +102,16 @@ MIN_EVENT_SAMPLES = 20
 # counters were taken are listed.
 FETCH_SCALE = 262144.0 / 131093.3
 WRITE_SCALE = 1.0
-KERNEL_TRAFFIC_KIB = {  # workload: (FETCH_SIZE, WRITE_SIZE) per dispatch
-    "decode1": (46204.5, 82.2),        # decode_fused_kernel<8>
-    "decode32": (475411.1, 5502.4),    # gemm_gate_up_kernel<0, 112, true, true, false>
-    "prefill512": (1180630.5, 27385.2),  # gemm_gate_up_kernel<0, 112, true, true, false>
-    "hash4096": (2131057.8, 176253.2),   # gemm_gate_up_kernel<0, 112, true, true, false>
+KERNEL_TRAFFIC_KIB = {  # (workload, packed copy used): (FETCH_SIZE, WRITE_SIZE) per dispatch
+    ("decode1", False): (46204.5, 82.2),        # decode_fused_kernel<8>
+    ("decode32", False): (475411.1, 5502.4),    # gemm_gate_up_kernel<0, 112, true, true, false, false>
+    ("prefill512", False): (1180630.5, 27385.2),
+    ("hash4096", False): (2131057.8, 176253.2),
 }
 
 
-def kernel_traffic(name):
-    kib = KERNEL_TRAFFIC_KIB.get(name)
+def kernel_traffic(name, packed):
+    kib = KERNEL_TRAFFIC_KIB.get((name, packed))
     if kib is None:
         return None
     return (kib[0] * FETCH_SCALE + kib[1] * WRITE_SCALE) * 1024.0
@@ -374,6 +375,9 @@ def run_workload(name, steps, warmup, copies, n_pool, cpu_seconds, dev, variant=
                      for k, v in kw.items()}
     t0 = time.perf_counter()
     layers = [B.Layer(I.make_layer(wl, device=dev, copy=c), wl.top_k) for c in range(copies)]
+    # the packed copy of the MXFP4 matrices (moe_pack_experts, once per layer
+    # like loading the weights): read by the batched gate/up and down only
+    packed = PACK and wl.n_tokens > 16 and wl.act == "bf16" and all(l.pack() for l in layers)
     pool = make_pool(wl, n_pool, dev)
     runner = Runner(wl, layers, pool, dev, opts)
     name = variant or name
@@ -443,7 +447,7 @@ def run_workload(name, steps, warmup, copies, n_pool, cpu_seconds, dev, variant=
         "peak": MFMA_BF16_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBPS,
         "unit": "TFLOP/s" if mfma_bound else "GB/s",
         "frac": tflops / MFMA_BF16_PEAK_TFLOPS if mfma_bound else gbps / HBM_PEAK_GBPS,
-        "traffic": kernel_traffic(name),
+        "traffic": kernel_traffic(name, packed),
         "bytes_per_launch": k_bytes,
         "flops_per_launch": k_flops,
         "flop_per_byte": intensity,
@@ -462,7 +466,8 @@ def run_workload(name, steps, warmup, copies, n_pool, cpu_seconds, dev, variant=
         roof["issued_frac_of_fp8_peak"] = issue * tflops / MFMA_FP8_PEAK_TFLOPS
     rec = {
         "workload": name,
-        "config": {"workload": describe(wl, copies), "n_tokens": wl.n_tokens},
+        "config": {"workload": describe(wl, copies), "n_tokens": wl.n_tokens,
+                   "packed_experts": packed},
         "routed_slots_per_step": costs["routed_slots"],
         "value": wl.n_tokens * steps / elapsed,
         "unit": "tokens/s",
@@ -556,6 +561,8 @@ def main():
     ap.add_argument("--pool", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
+    ap.add_argument("--no-pack", action="store_true",
+                    help="batched workloads without the packed copy of the weights")
     ap.add_argument("--no-variants", action="store_true",
                     help="leave out the nested records of the routing/FFN options")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -564,6 +571,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--nested-cpu-seconds", type=float, default=4.0)
     args = ap.parse_args()
+    global PACK
+    PACK = not args.no_pack
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

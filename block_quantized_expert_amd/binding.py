@@ -29,7 +29,7 @@ EXPORTED = ["moe_route", "moe_route_hash", "moe_route_group", "moe_group_workspa
             "moe_forward_single_kernel", "moe_forward_workspace_init", "moe_forward",
             "moe_forward_timed", "moe_forward_noalloc", "moe_status_string",
             "moe_stream_read", "moe_route_ex", "moe_route_group_ex", "moe_ffn_forward_ex",
-            "moe_forward_ex"]
+            "moe_forward_ex", "moe_packed_experts_bytes", "moe_pack_experts"]
 
 WEIGHT_TYPES = {"mxfp4": MOE_W_MXFP4, "fp8_e4m3_b128": MOE_W_FP8E4M3_B128}
 
@@ -71,7 +71,8 @@ class MoeLayer(ctypes.Structure):
                 ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("gate", MoeProj), ("up", MoeProj), ("down", MoeProj),
                 ("has_shared", ctypes.c_int32), ("shared_inter", ctypes.c_int32),
-                ("shared_gate", MoeProj), ("shared_up", MoeProj), ("shared_down", MoeProj)]
+                ("shared_gate", MoeProj), ("shared_up", MoeProj), ("shared_down", MoeProj),
+                ("packed_experts", ctypes.c_void_p)]
 
 
 _lib = None
@@ -126,6 +127,9 @@ def lib() -> ctypes.CDLL:
                      "moe_forward_ex"):
             getattr(L, name).restype = ctypes.c_int
         L.moe_stream_read.argtypes = [P, S, P, P]
+        L.moe_packed_experts_bytes.argtypes = [ctypes.POINTER(MoeLayer)]
+        L.moe_packed_experts_bytes.restype = S
+        L.moe_pack_experts.argtypes = [ctypes.POINTER(MoeLayer), P, S, P]
         L.moe_stream_read.restype = ctypes.c_int
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
@@ -232,6 +236,31 @@ class Layer:
 
     def workspace_bytes(self, n_tokens: int) -> int:
         return lib().moe_ffn_workspace_bytes(ctypes.byref(self.c), n_tokens)
+
+    def packed_bytes(self) -> int:
+        return lib().moe_packed_experts_bytes(ctypes.byref(self.c))
+
+    def pack(self, stream=None) -> bool:
+        """Writes the packed copy of the MXFP4 matrices (moe_pack_experts) into
+        a new device buffer and points the layer at it; False when the layer
+        cannot be packed.  ``unpack()`` drops it again."""
+        n = self.packed_bytes()
+        if n == 0:
+            return False
+        dev = self.weights["gate"]["codes"].device
+        buf = torch.empty(n + 256, dtype=torch.uint8, device=dev)
+        off = (-buf.data_ptr()) % 256
+        view = buf[off:off + n]
+        st = lib().moe_pack_experts(ctypes.byref(self.c), ctypes.c_void_p(view.data_ptr()),
+                                    ctypes.c_size_t(n), _stream(stream))
+        _check(st, "moe_pack_experts")
+        self._packed = buf
+        self.c.packed_experts = view.data_ptr()
+        return True
+
+    def unpack(self):
+        self.c.packed_experts = None
+        self._packed = None
 
     def forward_workspace_bytes(self, n_tokens: int) -> int:
         return lib().moe_forward_workspace_bytes(ctypes.byref(self.c), n_tokens)

@@ -19,7 +19,7 @@ HIPCC = os.path.join(ROCM, "bin", "hipcc")
 ARCH = "gfx950"
 
 HIP_SOURCES = ["moe_api.hip", "moe_route_group.hip", "moe_ffn.hip", "moe_gemm.hip", "moe_fused.hip",
-               "moe_probe.hip"]
+               "moe_pack.hip", "moe_probe.hip"]
 HOST_SOURCES = ["moe_host.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I" + INCLUDE, "-I" + CSRC]

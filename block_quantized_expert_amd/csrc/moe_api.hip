@@ -82,6 +82,15 @@ moe::FfnParams make_params(const moe_layer* L, const void* x, int x_type, int n_
   p.gmax = reinterpret_cast<uint32_t*>(ws + plan.off_gmax);
   p.gbuf = reinterpret_cast<float*>(ws + plan.off_gbuf);
   p.qctr = reinterpret_cast<uint32_t*>(ws + plan.off_qctr);
+  moe::PackPlan pk;
+  if (L->packed_experts != nullptr && moe::plan_pack(L, &pk) == MOE_OK) {
+    const uint8_t* base = static_cast<const uint8_t*>(L->packed_experts);
+    for (int m = 0; m < 6; ++m) {
+      p.pk_c[m] = pk.codes[m] >= 0 ? base + pk.codes[m] : nullptr;
+      p.pk_s[m] = pk.scales[m] >= 0 ? base + pk.scales[m] : nullptr;
+    }
+    p.packed = true;
+  }
   return p;
 }
 

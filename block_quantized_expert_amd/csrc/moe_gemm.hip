@@ -505,7 +505,7 @@ __device__ __forceinline__ uint32_t split_e4m3x3(const float (&v)[2][4], float m
 // that a step's operand reads and MFMAs form one branch-free block.
 // LAZY: the gate-first lazy skip is on (its gate maxima are merged into
 // gmax); a separate instantiation, so the plain kernels keep their registers.
-template <int WT, int TT, int NBT, bool SC, bool O32, bool LAZY, typename Take>
+template <int WT, int TT, int NBT, bool SC, bool O32, bool LAZY, bool PK, typename Take>
 __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it, char* smem,
                                              int wave, int lane, Take&& take) {
   using F = Fmt<WT>;
@@ -520,8 +520,12 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
   //  - otherwise: one byte per row and step, loaded with the step's codes.
   // fp8 (SC: H a multiple of 512): the row's one byte per step, four steps
   // in one 4-byte load (kCh).
-  constexpr bool kSC = SC && WT == MOE_W_MXFP4 && NBT <= 5;
-  constexpr bool kCh = SC && (WT == MOE_W_MXFP4 ? NBT >= 6 : true);
+  // PK (MXFP4 with SC): the packed copy, codes one KiB per step and row
+  // block, a lane's scale bytes of four steps one word (as the chunks
+  // below, without the byte gathering)
+  constexpr bool kPK = PK && WT == MOE_W_MXFP4 && SC;
+  constexpr bool kSC = SC && WT == MOE_W_MXFP4 && NBT <= 5 && !kPK;
+  constexpr bool kCh = SC && (WT == MOE_W_MXFP4 ? NBT >= 6 || kPK : true);
   constexpr int kLoads = (kSC || kCh) ? 4 * Q : 4 * (Q + 1);  // vector loads of one step's weights
   const int g = lane >> 4, r16 = lane & 15;
   const bool shared = it.seg == p.n_experts;
@@ -538,8 +542,9 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
   const int wrow = it.row0 + 32 * wave;
   const bool live = wrow < rows;
   const int64_t lrow = (shared ? 0 : (int64_t)it.seg * rows) + (live ? wrow : it.row0) + r16;
-  // code bytes of a step: MXFP4 16 at 16g; fp8 16 at 16g and 16 at 64 + 16g
-  const int64_t lc = lrow * cb + 16 * g, ls = lrow * sb + F::scale_off(0, g);
+  // the lane's scale bytes (its code bytes of a step: MXFP4 16 at 16g; fp8
+  // 16 at 16g and 16 at 64 + 16g, addressed from the wavefront base below)
+  const int64_t ls = lrow * sb + F::scale_off(0, g);
   const uint8_t* cbase[2] = {shared ? p.sgate_c : p.gate_c, shared ? p.sup_c : p.up_c};
   const uint8_t* sbase[2] = {shared ? p.sgate_s : p.gate_s, shared ? p.sup_s : p.up_s};
   // the wavefront's first row as a uniform base, the lane's rows as a 32-bit
@@ -547,6 +552,17 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
   const int64_t wrow_g = (shared ? 0 : (int64_t)it.seg * rows) + (live ? wrow : it.row0);
   const uint8_t* cwave[2] = {cbase[0] + wrow_g * cb, cbase[1] + wrow_g * cb};
   const uint32_t lco = (uint32_t)(r16 * cb) + 16 * g;
+  // packed: the wavefront's first row block (rows wrow_g .. +31 are blocks
+  // wrow_g / 16 and the next) in both matrices
+  const uint8_t* pkc[2] = {nullptr, nullptr};
+  const uint8_t* pks[2] = {nullptr, nullptr};
+  if constexpr (kPK) {
+#pragma unroll
+    for (int mat = 0; mat < 2; ++mat) {
+      pkc[mat] = p.pk_c[(shared ? 3 : 0) + mat] + (wrow_g / 16) * nks * 1024;
+      pks[mat] = p.pk_s[(shared ? 3 : 0) + mat] + (wrow_g / 16) * (nks / 4) * 256;
+    }
+  }
 
   // Token rows of this lane's copies (rows past the tile repeat row 0): the
   // 256-byte step rows of xq through Stage, and one 4-byte half of a row's
@@ -591,8 +607,12 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
-        for (int i = 0; i < Q; ++i)
-          q[mat][rb][i] = load16(cwave[mat] + (lco + (uint32_t)(16 * rb * cb + F::code_off(k, 0) + 64 * i)));
+        for (int i = 0; i < Q; ++i) {
+          if constexpr (kPK)
+            q[mat][rb][i] = load16(pkc[mat] + (uint32_t)((rb * nks + k) * 1024 + lane * 16));
+          else
+            q[mat][rb][i] = load16(cwave[mat] + (lco + (uint32_t)(16 * rb * cb + F::code_off(k, 0) + 64 * i)));
+        }
         if (!kSC && !kCh) u[mat][rb] = sbase[mat][ls + 16 * rb * sb + F::scale_off(k, 0)];
       }
   };
@@ -602,7 +622,7 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
   // leave the L2 between two loads, so this costs re-fetches that the LDS
   // copy avoids; it is the fallback where that copy does not fit.)
   u32x4 scw[2][2];
-  uint32_t sp[2][2];
+  uint32_t sp[2][2], spn[2][2];
   const int64_t srow_w = ls - F::scale_off(0, g);
   auto load_sc = [&](int c) {
     const int cc = min(c, nks / 4 - 1);
@@ -610,7 +630,10 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
     for (int mat = 0; mat < 2; ++mat)
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
-        if constexpr (WT == MOE_W_MXFP4)
+        if constexpr (kPK)
+          spn[mat][rb] = *reinterpret_cast<const uint32_t*>(
+              pks[mat] + (uint32_t)((rb * (nks / 4) + cc) * 256 + lane * 4));
+        else if constexpr (WT == MOE_W_MXFP4)
           scw[mat][rb] = load16(sbase[mat] + srow_w + 16 * rb * sb + 16 * cc);
         else
           scw[mat][rb][0] =
@@ -622,7 +645,9 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
     for (int mat = 0; mat < 2; ++mat)
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
-        if constexpr (WT == MOE_W_MXFP4) {
+        if constexpr (kPK) {
+          sp[mat][rb] = spn[mat][rb];
+        } else if constexpr (WT == MOE_W_MXFP4) {
           uint32_t v = 0;
 #pragma unroll
           for (int t = 0; t < 4; ++t) v |= ((scw[mat][rb][t] >> (8 * g)) & 0xFFu) << (8 * t);
@@ -847,7 +872,7 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
   }
 }
 
-template <int WT, int TT, bool SC, bool O32, bool LAZY>
+template <int WT, int TT, bool SC, bool O32, bool LAZY, bool PK>
 __global__ __launch_bounds__(kGThreads, kGPerCU) void gemm_gate_up_kernel(FfnParams p, int seg_lo,
                                                                      int seg_hi,
                                                                      uint32_t* qctr) {
@@ -860,7 +885,7 @@ __global__ __launch_bounds__(kGThreads, kGPerCU) void gemm_gate_up_kernel(FfnPar
   run_queue(ItemQueue{qctr, total, qctr != nullptr}, &s_q, [&](int item, auto&& take) {
     const GItem it = find_item<TT, kGuRows, false>(p, seg_lo, seg_hi, s_pref, item);
     dispatch_nbt<TT / 16>((it.m + 15) >> 4, [&](auto nb) {
-      gate_up_item<WT, TT, decltype(nb)::value, SC, O32, LAZY>(p, it, smem, wave, lane, take);
+      gate_up_item<WT, TT, decltype(nb)::value, SC, O32, LAZY, PK>(p, it, smem, wave, lane, take);
     });
   });
 }
@@ -1104,7 +1129,7 @@ static_assert(kD3Lds <= kGemmLds, "down LDS");
 // position c ^ ((n >> 1) & 7), so the 16 rows that one operand read touches
 // (two rows share a 256-byte bank line) hit distinct banks.
 
-template <int WT, int NBT, bool SC, typename Take>
+template <int WT, int NBT, bool SC, bool PK, typename Take>
 __device__ __forceinline__ void down3_item(const FfnParams& p, const GItem& it, char* smem,
                                            int wave, int lane, Take&& take) {
   using F = Fmt<WT>;
@@ -1114,9 +1139,11 @@ __device__ __forceinline__ void down3_item(const FfnParams& p, const GItem& it, 
   constexpr int kBuf = 3 * kPlane;        // the three parts
   constexpr int FA = WT == MOE_W_MXFP4 ? 4 : 0;  // operand format of the weights
   constexpr int RB = kDnRows / (16 * kGWaves);  // row blocks per wavefront
-  // scale bytes of the weights as in down_item
-  constexpr bool kSC = SC && WT == MOE_W_MXFP4 && NBT <= 3;
-  constexpr bool kCh = SC && (WT == MOE_W_MXFP4 ? NBT == 4 : true);
+  // scale bytes of the weights as in down_item; PK: the packed copy, as in
+  // gate/up
+  constexpr bool kPK = PK && WT == MOE_W_MXFP4 && SC;
+  constexpr bool kSC = SC && WT == MOE_W_MXFP4 && NBT <= 3 && !kPK;
+  constexpr bool kCh = SC && (WT == MOE_W_MXFP4 ? NBT == 4 || kPK : true);
   constexpr int kLoads = (kSC || kCh) ? RB * Q : RB * (Q + 1);
   const int g = lane >> 4, r16 = lane & 15;
   const bool shared = it.seg == p.n_experts;
@@ -1134,6 +1161,15 @@ __device__ __forceinline__ void down3_item(const FfnParams& p, const GItem& it, 
   const int64_t lc = lrow * cb + 16 * g, ls = lrow * sb + F::scale_off(0, g);
   const uint8_t* cbase = shared ? p.sdown_c : p.down_c;
   const uint8_t* sbase = shared ? p.sdown_s : p.down_s;
+  // packed: the wavefront's first row block (its 64 rows are four blocks;
+  // a wavefront past the matrix end reads block 0 and multiplies nothing)
+  const uint8_t* pkc = nullptr;
+  const uint8_t* pks = nullptr;
+  if constexpr (kPK) {
+    const int64_t blk = ((shared ? 0 : (int64_t)it.seg * p.hidden) + (nrb > 0 ? wrow0 : 0)) / 16;
+    pkc = p.pk_c[shared ? 5 : 2] + blk * nks * 1024;
+    pks = p.pk_s[shared ? 5 : 2] + blk * (nks / 4) * 256;
+  }
 
   // h copies: one instruction fills 8 rows of a part (lane l: row + l / 8,
   // position l % 8); wavefront w fills the row groups w, w + W, ... of each
@@ -1198,20 +1234,27 @@ __device__ __forceinline__ void down3_item(const FfnParams& p, const GItem& it, 
     for (int rb = 0; rb < RB; ++rb) {
       const int rr = rb < nrb ? rb : 0;
 #pragma unroll
-      for (int i = 0; i < Q; ++i)
-        q[rb][i] = load16(cbase + lc + 16 * rr * cb + F::code_off(k, 0) + 64 * i);
+      for (int i = 0; i < Q; ++i) {
+        if constexpr (kPK)
+          q[rb][i] = load16(pkc + (uint32_t)((rr * nks + k) * 1024 + lane * 16));
+        else
+          q[rb][i] = load16(cbase + lc + 16 * rr * cb + F::code_off(k, 0) + 64 * i);
+      }
       if (!kSC && !kCh) u[rb] = sbase[ls + 16 * rr * sb + F::scale_off(k, 0)];
     }
   };
   u32x4 scw[RB];
-  uint32_t sp[RB];
+  uint32_t sp[RB], spn[RB];
   const int64_t srow = ls - F::scale_off(0, g);
   auto load_sc = [&](int c) {
     const int cc = min(c, nks / 4 - 1);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const int rr = rb < nrb ? rb : 0;
-      if constexpr (WT == MOE_W_MXFP4)
+      if constexpr (kPK)
+        spn[rb] = *reinterpret_cast<const uint32_t*>(
+            pks + (uint32_t)((rr * (nks / 4) + cc) * 256 + lane * 4));
+      else if constexpr (WT == MOE_W_MXFP4)
         scw[rb] = load16(sbase + srow + 16 * rr * sb + 16 * cc);
       else
         scw[rb][0] = *reinterpret_cast<const uint32_t*>(sbase + srow + 16 * rr * sb + 4 * cc);
@@ -1220,7 +1263,9 @@ __device__ __forceinline__ void down3_item(const FfnParams& p, const GItem& it, 
   auto take_sc = [&]() {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      if constexpr (WT == MOE_W_MXFP4) {
+      if constexpr (kPK) {
+        sp[rb] = spn[rb];
+      } else if constexpr (WT == MOE_W_MXFP4) {
         uint32_t v = 0;
 #pragma unroll
         for (int t = 0; t < 4; ++t) v |= ((scw[rb][t] >> (8 * g)) & 0xFFu) << (8 * t);
@@ -1353,7 +1398,7 @@ __device__ __forceinline__ void down3_item(const FfnParams& p, const GItem& it, 
   }
 }
 
-template <int WT, bool SC>
+template <int WT, bool SC, bool PK>
 __global__ __launch_bounds__(kGThreads, kGPerCU) void gemm_down3_kernel(FfnParams p, int seg_lo,
                                                                    int seg_hi, uint32_t* qctr) {
   extern __shared__ __align__(16) char smem[];
@@ -1365,7 +1410,7 @@ __global__ __launch_bounds__(kGThreads, kGPerCU) void gemm_down3_kernel(FfnParam
   run_queue(ItemQueue{qctr, total, qctr != nullptr}, &s_q, [&](int item, auto&& take) {
     const GItem it = find_item<kD3Tok, kDnRows, true>(p, seg_lo, seg_hi, s_pref, item);
     dispatch_nbt<kD3Tok / 16>((it.m + 15) >> 4, [&](auto nb) {
-      down3_item<WT, decltype(nb)::value, SC>(p, it, smem, wave, lane, take);
+      down3_item<WT, decltype(nb)::value, SC, PK>(p, it, smem, wave, lane, take);
     });
   });
 }
@@ -1423,35 +1468,35 @@ int grid_for(int64_t items) {
   return (int)(items < kGemmGrid ? (items > 0 ? items : 1) : kGemmGrid);
 }
 
-template <int WT, int TT, bool SC, bool O32, bool LAZY>
+template <int WT, int TT, bool SC, bool O32, bool LAZY, bool PK>
 hipError_t gate_up_range_as(const FfnParams& p, int seg_lo, int seg_hi, hipStream_t stream,
                             hipEvent_t start, hipEvent_t stop) {
-  static const hipError_t attr = allow_lds(gemm_gate_up_kernel<WT, TT, SC, O32, LAZY>);
+  static const hipError_t attr = allow_lds(gemm_gate_up_kernel<WT, TT, SC, O32, LAZY, PK>);
   if (attr != hipSuccess) return attr;
   const int grid = grid_for(items_bound(p, seg_lo, seg_hi, TT, kGuRows, false));
-  return launch(gemm_gate_up_kernel<WT, TT, SC, O32, LAZY>, dim3(grid), dim3(kGThreads),
+  return launch(gemm_gate_up_kernel<WT, TT, SC, O32, LAZY, PK>, dim3(grid), dim3(kGThreads),
                 (size_t)kGemmLds, stream, start, stop, p, seg_lo, seg_hi,
                 queue_counters(p, seg_lo, false));
 }
 
-template <int WT, int TT, bool SC, bool O32>
+template <int WT, int TT, bool SC, bool O32, bool PK = false>
 hipError_t gate_up_range(const FfnParams& p, int seg_lo, int seg_hi, hipStream_t stream,
                          hipEvent_t start, hipEvent_t stop) {
   if (p.lazy_tau > 0.0f)
-    return gate_up_range_as<WT, TT, SC, O32, true>(p, seg_lo, seg_hi, stream, start, stop);
-  return gate_up_range_as<WT, TT, SC, O32, false>(p, seg_lo, seg_hi, stream, start, stop);
+    return gate_up_range_as<WT, TT, SC, O32, true, PK>(p, seg_lo, seg_hi, stream, start, stop);
+  return gate_up_range_as<WT, TT, SC, O32, false, PK>(p, seg_lo, seg_hi, stream, start, stop);
 }
 
-template <int WT, bool SC>
+template <int WT, bool SC, bool PK = false>
 hipError_t down3_range(const FfnParams& p, int seg_lo, int seg_hi, hipStream_t stream,
                        hipEvent_t start, hipEvent_t stop) {
   static const hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_down3_kernel<WT, SC>),
+      hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_down3_kernel<WT, SC, PK>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, kD3Lds);
   if (attr != hipSuccess) return attr;
   const int grid = grid_for(items_bound(p, seg_lo, seg_hi, kD3Tok, kDnRows, true));
-  return launch(gemm_down3_kernel<WT, SC>, dim3(grid), dim3(kGThreads), (size_t)kD3Lds, stream,
-                start, stop, p, seg_lo, seg_hi, queue_counters(p, seg_lo, true));
+  return launch(gemm_down3_kernel<WT, SC, PK>, dim3(grid), dim3(kGThreads), (size_t)kD3Lds,
+                stream, start, stop, p, seg_lo, seg_hi, queue_counters(p, seg_lo, true));
 }
 
 template <int WT, int TT, bool SC>
@@ -1503,6 +1548,10 @@ hipError_t launch_gemm_gate_up(const FfnParams& p, hipStream_t stream, hipEvent_
                  : gate_up_range<MOE_W_FP8E4M3_B128, 64, false, true>(p, lo, hi, stream, a, b);
     }
     if (!o32) return gate_up_range<MOE_W_MXFP4, 112, false, false>(p, lo, hi, stream, a, b);
+    // the packed copy (its shapes are multiples of 512, and every MXFP4
+    // matrix of the launch is in it) needs no LDS scale block, so no bound
+    // on H
+    if (p.packed) return gate_up_range<MOE_W_MXFP4, 112, true, true, true>(p, lo, hi, stream, a, b);
     return sc ? gate_up_range<MOE_W_MXFP4, 112, true, true>(p, lo, hi, stream, a, b)
               : gate_up_range<MOE_W_MXFP4, 112, false, true>(p, lo, hi, stream, a, b);
   });
@@ -1526,6 +1575,7 @@ hipError_t launch_gemm_down(const FfnParams& p, hipStream_t stream, hipEvent_t s
       return sc8 ? down_range<MOE_W_FP8E4M3_B128, 64, true>(p, lo, hi, stream, a, b)
                  : down_range<MOE_W_FP8E4M3_B128, 64, false>(p, lo, hi, stream, a, b);
     }
+    if (h3 && p.packed) return down3_range<MOE_W_MXFP4, true, true>(p, lo, hi, stream, a, b);
     if (h3)
       return sc ? down3_range<MOE_W_MXFP4, true>(p, lo, hi, stream, a, b)
                 : down3_range<MOE_W_MXFP4, false>(p, lo, hi, stream, a, b);

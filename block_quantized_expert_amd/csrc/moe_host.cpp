@@ -94,6 +94,38 @@ moe_status check_layer(const moe_layer* layer) {
         layer->shared_down.type != layer->shared_gate.type)
       return MOE_ERR_UNSUPPORTED;
   }
+  if (layer->packed_experts != nullptr) {
+    if (reinterpret_cast<uintptr_t>(layer->packed_experts) % 256 != 0) return MOE_ERR_INVALID;
+    PackPlan pk;
+    if ((s = plan_pack(layer, &pk)) != MOE_OK) return s;
+  }
+  return MOE_OK;
+}
+
+moe_status plan_pack(const moe_layer* layer, PackPlan* plan) {
+  if (layer->gate.type != MOE_W_MXFP4) return MOE_ERR_UNSUPPORTED;
+  if (layer->hidden % 512 != 0 || layer->inter % 512 != 0) return MOE_ERR_UNSUPPORTED;
+  const bool sh = layer->has_shared && layer->shared_gate.type == MOE_W_MXFP4;
+  if (sh && layer->shared_inter % 512 != 0) return MOE_ERR_UNSUPPORTED;
+  const int64_t E = layer->n_experts, H = layer->hidden, I = layer->inter;
+  const int64_t SI = sh ? layer->shared_inter : 0;
+  const int64_t rows[6] = {E * I, E * I, E * H, SI, SI, sh ? H : 0};
+  const int32_t cols[6] = {(int32_t)H, (int32_t)H, (int32_t)I, (int32_t)H, (int32_t)H,
+                           (int32_t)SI};
+  size_t off = 0;
+  for (int m = 0; m < 6; ++m) {
+    plan->rows[m] = rows[m];
+    plan->cols[m] = cols[m];
+    if (rows[m] == 0) {
+      plan->codes[m] = plan->scales[m] = -1;
+      continue;
+    }
+    plan->codes[m] = (int64_t)off;
+    off += align_up((size_t)rows[m] * (size_t)(cols[m] / 2), 256);
+    plan->scales[m] = (int64_t)off;
+    off += align_up((size_t)rows[m] * (size_t)(cols[m] / 32), 256);
+  }
+  plan->total = off;
   return MOE_OK;
 }
 

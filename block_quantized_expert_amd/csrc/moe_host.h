@@ -79,6 +79,21 @@ moe_status check_group(const int32_t* ids, int n_tokens, int top_k, int n_expert
                        const int32_t* counts, const int32_t* offsets, const int32_t* perm,
                        const int32_t* inv_perm);
 moe_status check_layer(const moe_layer* layer);
+
+// Layout of a packed copy (moe_pack_experts): per matrix (gate, up, down,
+// shared gate, shared up, shared down) the byte offset of its codes and of
+// its scales, or -1 for a matrix that is not packed (no shared expert, or
+// a shared expert that is not MXFP4); rows and inputs of each matrix.
+struct PackPlan {
+  int64_t codes[6];
+  int64_t scales[6];
+  int64_t rows[6];
+  int32_t cols[6];
+  size_t total;
+};
+// MOE_OK with the plan for a layer that passed check_layer and can be
+// packed; MOE_ERR_UNSUPPORTED otherwise.
+moe_status plan_pack(const moe_layer* layer, PackPlan* plan);
 // Fills `plan` for a valid layer; the layer must have passed check_layer.
 moe_status plan_ffn(const moe_layer* layer, int n_tokens, FfnPlan* plan);
 // Byte layout of the moe_forward workspace.

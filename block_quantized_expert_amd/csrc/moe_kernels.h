@@ -54,6 +54,11 @@ struct FfnParams {
   float* gbuf;
   // the grouped GEMMs' item-queue counters, kQueueWords of them
   uint32_t* qctr;
+  // packed copy of the MXFP4 matrices (moe_pack_experts), indexed gate, up,
+  // down, shared gate, shared up, shared down; null when not packed
+  const uint8_t* pk_c[6];
+  const uint8_t* pk_s[6];
+  bool packed;
 };
 
 constexpr int kQueueWords = 32;  // 4 launches x 8 XCD chunks

@@ -105,6 +105,11 @@ typedef struct {
   int32_t has_shared;      /* 0 or 1: one shared expert, weight 1        */
   int32_t shared_inter;    /* multiple of 128 when has_shared            */
   moe_proj shared_gate, shared_up, shared_down; /* one matrix each       */
+  /* Optional (NULL: unused): the layer's MXFP4 weights as written by
+   * moe_pack_experts, 256-byte aligned.  The batched gate/up and down read
+   * them from there; every other path reads the arrays above, which stay
+   * required and must hold the same weights. */
+  const void* packed_experts;
 } moe_layer;
 
 /*
@@ -243,6 +248,39 @@ moe_status moe_group(const int32_t* topk_ids, int n_tokens, int top_k, int n_exp
 
 /* Workspace bytes moe_ffn_forward (and its two stages) need for n_tokens. */
 size_t moe_ffn_workspace_bytes(const moe_layer* layer, int n_tokens);
+
+/*
+ * A second copy of a layer's MXFP4 weights in the order the batched gate/up
+ * and down read them (the same codes and UE8M0 scale bytes, "DeepSeek V4
+ * target engine (CPU + optional CUDA tier)": MXFP4 experts; the layout
+ * itself is this library's, for this GPU's matrix instructions).  In the
+ * row-major arrays a 128-input step of 16 rows touches 64 bytes of each of
+ * 16 rows; packed, it is one contiguous KiB, and the scale bytes of four
+ * steps of a lane are one 32-bit word.
+ *
+ * moe_packed_experts_bytes: bytes of the copy for `layer` (the routed gate,
+ *   up and down matrices, and the shared expert's three when it is MXFP4
+ *   too), or 0 when the layer cannot be packed: routed experts not MXFP4,
+ *   or hidden, inter (or shared_inter, for an MXFP4 shared expert) not a
+ *   multiple of 512.
+ * moe_pack_experts: writes the copy into `packed` (device, 256-byte
+ *   aligned, at least moe_packed_experts_bytes(layer) bytes; the caller owns
+ *   it), asynchronously on `stream`, reading the layer's arrays.  Returns
+ *   MOE_ERR_UNSUPPORTED for a layer that cannot be packed, MOE_ERR_INVALID
+ *   for a NULL or misaligned buffer or a short size.  Set
+ *   layer->packed_experts = packed afterwards to use it; results are bitwise
+ *   equal with and without it.
+ * Layout, for each packed matrix of R rows x C inputs (R/16 row blocks of
+ * 16 rows, S = C/128 steps): codes, block b step s at byte (b*S + s)*1024,
+ * lane l = 16*g + r holding the 16 code bytes of row 16b + r, inputs
+ * 128s + 32g .. +31; then the scales, block b and steps 4c .. 4c+3 at byte
+ * (b*S/4 + c)*256, lane l holding in byte t the scale of row 16b + r, inputs
+ * 128(4c+t) + 32g .. +31.  Matrices in the order gate, up, down, shared
+ * gate, shared up, shared down, each section 256-byte aligned.
+ */
+size_t moe_packed_experts_bytes(const moe_layer* layer);
+moe_status moe_pack_experts(const moe_layer* layer, void* packed, size_t packed_bytes,
+                            hipStream_t stream);
 
 /*
  * Expert FFN and combine ("Deep-Dive Mathematical & Kernel Guide", section 4

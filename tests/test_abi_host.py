@@ -48,7 +48,8 @@ def test_struct_layout_matches_c():
     assert ctypes.sizeof(B.MoeProj) == 24
     assert B.MoeLayer.gate.offset == 16
     assert B.MoeLayer.has_shared.offset == 88
-    assert ctypes.sizeof(B.MoeLayer) == 168
+    assert B.MoeLayer.packed_experts.offset == 168
+    assert ctypes.sizeof(B.MoeLayer) == 176
 
 
 FAKE = ctypes.c_void_p(0x10000)  # 16-byte aligned, never dereferenced
@@ -309,3 +310,51 @@ def test_opts_struct_layout_matches_c():
     assert B.MoeOpts.keep_max.offset == 16
     assert B.MoeOpts.lazy_tau.offset == 24
     assert ctypes.sizeof(B.MoeOpts) == 32
+
+
+def _pack_bytes_expected(E, H, I, SI=None):
+    """The packed layout of include/moe.h, summed section by section."""
+    def up(v):
+        return -(-v // 256) * 256
+    mats = [(E * I, H), (E * I, H), (E * H, I)]
+    if SI is not None:
+        mats += [(SI, H), (SI, H), (H, SI)]
+    return sum(up(r * c // 2) + up(r * c // 32) for r, c in mats)
+
+
+def test_packed_experts_bytes():
+    lib = B.lib()
+    # routed and shared MXFP4: all six matrices
+    L = _layer()
+    assert lib.moe_packed_experts_bytes(ctypes.byref(L)) == _pack_bytes_expected(256, 4096, 2048, 2048)
+    # an fp8 shared expert is not packed (its own launch reads it row-major)
+    L = _layer(swtype=1)
+    assert lib.moe_packed_experts_bytes(ctypes.byref(L)) == _pack_bytes_expected(256, 4096, 2048)
+    L = _layer(shared=False, e=8, hidden=1024, inter=512)
+    assert lib.moe_packed_experts_bytes(ctypes.byref(L)) == _pack_bytes_expected(8, 1024, 512)
+    # cannot be packed: fp8 routed experts, H or I not a multiple of 512
+    assert lib.moe_packed_experts_bytes(ctypes.byref(_layer(wtype=1, swtype=1))) == 0
+    assert lib.moe_packed_experts_bytes(ctypes.byref(_layer(hidden=640))) == 0
+    assert lib.moe_packed_experts_bytes(ctypes.byref(_layer(inter=384))) == 0
+    assert lib.moe_packed_experts_bytes(None) == 0
+
+
+def test_pack_experts_rejects_bad_arguments():
+    """Host-side checks only: every call here returns before any launch."""
+    lib = B.lib()
+    L = _layer(shared=False, e=8, hidden=1024, inter=512)
+    n = lib.moe_packed_experts_bytes(ctypes.byref(L))
+    aligned = ctypes.c_void_p(0x100000)
+    assert lib.moe_pack_experts(ctypes.byref(L), None, n, None) == B.MOE_ERR_INVALID
+    assert lib.moe_pack_experts(ctypes.byref(L), ctypes.c_void_p(0x100010), n, None) == B.MOE_ERR_INVALID
+    assert lib.moe_pack_experts(ctypes.byref(L), aligned, n - 1, None) == B.MOE_ERR_INVALID
+    assert lib.moe_pack_experts(None, aligned, n, None) == B.MOE_ERR_INVALID
+    fp8 = _layer(wtype=1, swtype=1, shared=False)
+    assert lib.moe_pack_experts(ctypes.byref(fp8), aligned, 1 << 40, None) == B.MOE_ERR_UNSUPPORTED
+    # a layer that names a packed copy must be packable and the copy aligned
+    L.packed_experts = 0x100000
+    assert lib.moe_ffn_workspace_bytes(ctypes.byref(L), 8) > 0
+    L.packed_experts = 0x100010
+    assert lib.moe_ffn_workspace_bytes(ctypes.byref(L), 8) == 0
+    fp8.packed_experts = 0x100000
+    assert lib.moe_ffn_workspace_bytes(ctypes.byref(fp8), 8) == 0

@@ -1,0 +1,147 @@
+"""The packed copy of a layer's MXFP4 matrices (moe_pack_experts).
+
+- Its bytes against the layout include/moe.h states, restated here with
+  numpy reshapes of the row-major arrays.
+- Every batched output computed with the copy is bitwise equal to the one
+  computed without it: the same code and scale bytes reach the matrix
+  instruction in the same order, only their addresses differ.  Checked on
+  every tile size of the grouped GEMMs (the layers of the tile-parity test),
+  with an fp8 shared expert (its own launch, not packed), with the lazy skip
+  and with pruning, and on the full-size batched workloads; the outputs
+  without the copy are compared with the oracle by the other GPU tests.
+- The single-token fused kernel and the small-batch kernels ignore the copy.
+"""
+
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from block_quantized_expert_amd import binding as B
+from block_quantized_expert_amd import inputs as I
+from moe_testlib import assert_y_close, gpu_inputs, oracle_y_host
+from oracle import moe_oracle as O
+from test_gpu_parity_tiles import COUNTS, RAGGED, _table
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+    yield
+    torch.cuda.empty_cache()
+
+
+def _np_pack(codes, scales, rows, cols):
+    """Codes: row block b, step s, lane 16 g + r -> the 16 bytes 64 s + 16 g ..
+    of row 16 b + r.  Scales: block b, chunk c, lane 16 g + r, byte t -> scale
+    byte 4 (4 c + t) + g of row 16 b + r."""
+    s = cols // 128
+    pc = codes.reshape(rows // 16, 16, s, 4, 16).transpose(0, 2, 3, 1, 4)
+    ps = scales.reshape(rows // 16, 16, s // 4, 4, 4).transpose(0, 2, 4, 1, 3)
+    return np.ascontiguousarray(pc).reshape(-1), np.ascontiguousarray(ps).reshape(-1)
+
+
+def _up(v):
+    return -(-v // 256) * 256
+
+
+def test_packed_bytes_follow_the_stated_layout():
+    wl = replace(RAGGED, n_experts=4, top_k=2, shared_inter=1024, seed=7)
+    print("case pack layout", flush=True)
+    weights = I.make_layer(wl, device=DEV)
+    layer = B.Layer(weights, wl.top_k)
+    assert layer.pack()
+    torch.cuda.synchronize()
+    got = layer._packed.cpu().numpy()
+    got = got[(-layer._packed.data_ptr()) % 256:]
+    E, H, Iw, SI = wl.n_experts, wl.hidden, wl.inter, 1024
+    sh = weights["shared"]
+    mats = [(weights["gate"], E * Iw, H), (weights["up"], E * Iw, H), (weights["down"], E * H, Iw),
+            (sh["gate"], SI, H), (sh["up"], SI, H), (sh["down"], H, SI)]
+    off = 0
+    for m, rows, cols in mats:
+        codes = m["codes"].cpu().numpy().reshape(rows, cols // 2)
+        scales = m["scales"].cpu().numpy().reshape(rows, cols // 32)
+        pc, ps = _np_pack(codes, scales, rows, cols)
+        assert np.array_equal(got[off:off + pc.size], pc)
+        off += _up(pc.size)
+        assert np.array_equal(got[off:off + ps.size], ps)
+        off += _up(ps.size)
+    assert off == layer.packed_bytes()
+
+
+def _hash_ffn(layer, wl, x_d, opts=None):
+    pairs, wts = _table(COUNTS, wl.seed)
+    tok = torch.arange(wl.n_tokens, dtype=torch.int32, device=DEV)
+    ids, w = B.moe_route_hash(tok, torch.from_numpy(pairs).to(DEV), torch.from_numpy(wts).to(DEV),
+                              wl.n_experts)
+    grouping = B.moe_group(ids, wl.n_experts)
+    if opts is None:
+        y = B.moe_ffn_forward(layer, x_d, w, grouping)
+    else:
+        y = B.moe_ffn_forward_ex(layer, x_d, w, grouping, opts)
+    torch.cuda.synchronize()
+    return y, pairs, wts
+
+
+@pytest.mark.parametrize("wl,lazy", [
+    (RAGGED, 0.0),
+    (replace(RAGGED, shared="fp8_e4m3_b128", seed=42), 0.0),
+    (RAGGED, 1e-3),
+], ids=["mxfp4_shared", "fp8_shared", "lazy"])
+def test_every_tile_size_bitwise_with_the_copy(wl, lazy):
+    print("case pack tiles %s lazy %g" % (wl.shared, lazy), flush=True)
+    layer = B.Layer(I.make_layer(wl, device=DEV), wl.top_k)
+    x = I.activations(wl)
+    x_d = x.to(DEV)
+    opts = B.make_opts(lazy_tau=lazy) if lazy > 0 else None
+    y0, pairs, wts = _hash_ffn(layer, wl, x_d, opts)
+    assert layer.pack()
+    y1, _, _ = _hash_ffn(layer, wl, x_d, opts)
+    assert torch.equal(y0, y1)
+    if lazy == 0.0:
+        rids, rw = O.route_hash(np.arange(wl.n_tokens), pairs, wts)
+        assert_y_close(y1.cpu().numpy(), oracle_y_host(layer.weights, wl.act, x, rids, rw))
+
+
+@pytest.mark.parametrize("name", ["decode32", "prefill512", "hash4096"])
+def test_full_size_batches_bitwise_with_the_copy(name):
+    wl = I.WORKLOADS[name]
+    print("case pack %s" % name, flush=True)
+    layer, x, x_d, routing, routing_d = gpu_inputs(wl)
+    y0, ids0, _, _ = B.forward(layer, x_d, routing_d, wl.routed_scale)
+    torch.cuda.synchronize()
+    assert layer.pack()
+    y1, ids1, _, _ = B.forward(layer, x_d, routing_d, wl.routed_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(ids0, ids1)
+    assert torch.equal(y0, y1)
+
+
+def test_pruned_batch_and_decode_paths_with_the_copy():
+    """moe_forward on a packed layer: a 32-token batch with tail pruning (the
+    grouped GEMMs with dropped slots), 8 tokens (small-batch kernels) and one
+    token (fused kernel), each bitwise equal to the unpacked layer."""
+    wl = I.WORKLOADS["decode32"]
+    layer, x, x_d, routing, routing_d = gpu_inputs(wl)
+    logits = routing_d["logits"]
+    cases = [(32, B.make_opts(keep_max=4)), (8, None), (1, None)]
+    before = []
+    for n, opts in cases:
+        buf = B.moe_forward_ex(layer, logits[:n].contiguous(), x_d[:n].contiguous(),
+                               opts if opts is not None else B.make_opts(), wl.routed_scale)
+        torch.cuda.synchronize()
+        before.append(buf.y.clone())
+    assert layer.pack()
+    for (n, opts), y0 in zip(cases, before):
+        print("case pack moe_forward n=%d" % n, flush=True)
+        buf = B.moe_forward_ex(layer, logits[:n].contiguous(), x_d[:n].contiguous(),
+                               opts if opts is not None else B.make_opts(), wl.routed_scale)
+        torch.cuda.synchronize()
+        assert torch.equal(y0, buf.y)
