@@ -376,10 +376,12 @@ def run_workload(name, steps, warmup, copies, n_pool, cpu_seconds, dev, variant=
     t0 = time.perf_counter()
     layers = [B.Layer(I.make_layer(wl, device=dev, copy=c), wl.top_k) for c in range(copies)]
     # the packed copy of the MXFP4 matrices (moe_pack_experts, once per layer
-    # like loading the weights): read by the batched gate/up and down only
-    packed = PACK and wl.n_tokens > 16 and wl.act == "bf16" and all(l.pack() for l in layers)
+    # like loading the weights): read by the batched gate/up and down and by
+    # the single-token fused kernel
     pool = make_pool(wl, n_pool, dev)
     runner = Runner(wl, layers, pool, dev, opts)
+    packed = (PACK and wl.act == "bf16" and (wl.n_tokens > 16 or runner.fused)
+              and all(l.pack() for l in layers))
     name = variant or name
     torch.cuda.synchronize()
     print("%s setup %.1f s: %d layer copies, %d inputs" % (name, time.perf_counter() - t0,

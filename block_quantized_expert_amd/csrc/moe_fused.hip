@@ -167,8 +167,13 @@ __device__ bool wait_release(const FusedParams& f, FusedSmem& sm) {
 }
 
 // S = hidden / 512: reduction steps of 128 per wavefront quarter in gate/up.
-template <int S>
+// PK (S a multiple of 4): the layer's packed copy (moe_pack_experts), where a
+// wavefront's step of a 16-row block is one contiguous KiB in its lanes'
+// order and a lane's scale bytes of four steps one word; the lanes hold the
+// same bytes as with the row-major arrays.
+template <int S, bool PK>
 __global__ __launch_bounds__(kFThreads) void decode_fused_kernel(FusedParams f) {
+  static_assert(!PK || S % 4 == 0, "packed scale words cover four steps");
   const FfnParams& p = f.p;
   __shared__ FusedSmem sm;
   const int lane = threadIdx.x & 63, wave = wave_id();
@@ -188,11 +193,32 @@ __global__ __launch_bounds__(kFThreads) void decode_fused_kernel(FusedParams f) 
   u32x4 qg[S], qu[S];
   uint32_t wg[S], wu[S];
   // request the codes and scales of an item (this wavefront's quarter)
+  const int nks = p.hidden >> 7;
   auto issue = [&](int item) {
     const bool shared = item < ns;
     const int a = uniform(shared ? kk : (item - ns) / rbr);
     const int rb = uniform(shared ? item : item - ns - a * rbr);
     const int e = shared ? 0 : uniform(sm.act[a]);
+    if constexpr (PK) {
+      // row block blk, steps wq S .. wq S + S - 1: S consecutive KiB; the
+      // scale words of its S / 4 chunks
+      const int64_t blk = (shared ? 0 : (int64_t)e * rbr) + rb;
+      const uint8_t* gc = p.pk_c[shared ? 3 : 0] + (blk * nks + wq * S) * 1024 + lane * 16;
+      const uint8_t* uc = p.pk_c[shared ? 4 : 1] + (blk * nks + wq * S) * 1024 + lane * 16;
+      const uint8_t* gs = p.pk_s[shared ? 3 : 0] + (blk * (nks / 4) + wq * S / 4) * 256 + lane * 4;
+      const uint8_t* us = p.pk_s[shared ? 4 : 1] + (blk * (nks / 4) + wq * S / 4) * 256 + lane * 4;
+#pragma unroll
+      for (int j = 0; j < S; ++j) {
+        qg[j] = load16(gc + j * 1024);
+        qu[j] = load16(uc + j * 1024);
+      }
+#pragma unroll
+      for (int v = 0; v < S / 4; ++v) {
+        wg[v] = *reinterpret_cast<const uint32_t*>(gs + v * 256);
+        wu[v] = *reinterpret_cast<const uint32_t*>(us + v * 256);
+      }
+      return;
+    }
     const int64_t row = (shared ? 0 : (int64_t)e * p.inter) + rb * 16 + r16;
     const uint8_t* gc = (shared ? p.sgate_c : p.gate_c) + row * cb + wq * S * 64 + g * 16;
     const uint8_t* uc = (shared ? p.sup_c : p.up_c) + row * cb + wq * S * 64 + g * 16;
@@ -225,6 +251,29 @@ __global__ __launch_bounds__(kFThreads) void decode_fused_kernel(FusedParams f) 
   // copy a shared-expert item's codes and scales (this wavefront's quarter)
   // into LDS: the same bytes issue() would load, lane l's 16 at 16l
   auto issue_lds = [&](int item) {
+    if constexpr (PK) {
+      // the codes into LDS; the S / 4 scale words straight into registers
+      // (fetch_lds waits for them with the copies)
+      const uint8_t* gc = p.pk_c[3] + ((int64_t)item * nks + wq * S) * 1024 + lane * 16;
+      const uint8_t* uc = p.pk_c[4] + ((int64_t)item * nks + wq * S) * 1024 + lane * 16;
+#pragma unroll
+      for (int j = 0; j < S; ++j) {
+        __builtin_amdgcn_global_load_lds(
+            gc + j * 1024, (__attribute__((address_space(3))) void*)(&sm.u.gu.pre[wq][2 * j][0]),
+            16, 0, 0);
+        __builtin_amdgcn_global_load_lds(
+            uc + j * 1024,
+            (__attribute__((address_space(3))) void*)(&sm.u.gu.pre[wq][2 * j + 1][0]), 16, 0, 0);
+      }
+      const uint8_t* gs = p.pk_s[3] + ((int64_t)item * (nks / 4) + wq * S / 4) * 256 + lane * 4;
+      const uint8_t* us = p.pk_s[4] + ((int64_t)item * (nks / 4) + wq * S / 4) * 256 + lane * 4;
+#pragma unroll
+      for (int v = 0; v < S / 4; ++v) {
+        wg[v] = *reinterpret_cast<const uint32_t*>(gs + v * 256);
+        wu[v] = *reinterpret_cast<const uint32_t*>(us + v * 256);
+      }
+      return;
+    }
     const int64_t row = (int64_t)item * 16 + r16;
     const uint8_t* gc = p.sgate_c + row * cb + wq * S * 64 + g * 16;
     const uint8_t* uc = p.sup_c + row * cb + wq * S * 64 + g * 16;
@@ -252,6 +301,7 @@ __global__ __launch_bounds__(kFThreads) void decode_fused_kernel(FusedParams f) 
       qg[j] = sm.u.gu.pre[wq][2 * j][lane];
       qu[j] = sm.u.gu.pre[wq][2 * j + 1][lane];
     }
+    if constexpr (PK) return;  // the scale words are in registers
 #pragma unroll
     for (int v = 0; v < S / 4; ++v) {
       const u32x4 a4 = sm.u.gu.pre[wq][2 * S + 2 * v][lane];
@@ -425,8 +475,10 @@ __global__ __launch_bounds__(kFThreads) void decode_fused_kernel(FusedParams f) 
     for (int a = 0; a < nseg; ++a) {
       const int e = uniform(sm.act[a]);
       const bool shared = e == p.n_experts;
-      const uint8_t* src = (shared ? p.sdown_s : p.down_s) +
-                           ((shared ? 0 : (int64_t)e * p.hidden) + (int64_t)blockIdx.x * 16) * dsb;
+      // packed: the row block's scale words, the same number of bytes
+      const int64_t blk = (shared ? 0 : (int64_t)e * n_rb) + blockIdx.x;
+      const uint8_t* src = PK ? p.pk_s[shared ? 5 : 2] + blk * (ksteps / 4) * 256
+                              : (shared ? p.sdown_s : p.down_s) + blk * 16 * dsb;
       for (int i = 0; i * 1024 < bytes; ++i)
         if (i * 1024 + lane * 16 < bytes)
           __builtin_amdgcn_global_load_lds(
@@ -456,8 +508,12 @@ __global__ __launch_bounds__(kFThreads) void decode_fused_kernel(FusedParams f) 
           b[t] = as_bf16x8(r16 == 0 ? *reinterpret_cast<const u32x4*>(
                                           &sm.u.gu.x[(wq * S + j) * 128 + g * 32 + 8 * t])
                                     : u32x4{0, 0, 0, 0});
-        const float sgv = ue8m0_to_f32((wg[j] >> (8 * g)) & 0xFF);
-        const float suv = ue8m0_to_f32((wu[j] >> (8 * g)) & 0xFF);
+        // the step's scale byte of the lane's 32-input block: byte g of the
+        // row's word for the step, or byte j % 4 of the packed word
+        const float sgv = ue8m0_to_f32(PK ? (wg[j >> 2] >> (8 * (j & 3))) & 0xFF
+                                          : (wg[j] >> (8 * g)) & 0xFF);
+        const float suv = ue8m0_to_f32(PK ? (wu[j >> 2] >> (8 * (j & 3))) & 0xFF
+                                          : (wu[j] >> (8 * g)) & 0xFF);
 #pragma unroll
         for (int t = 0; t < 4; ++t) ag = mfma_bf16(fp4x8_to_bf16(qg[j][t], sgv), b[t], ag);
 #pragma unroll
@@ -527,10 +583,14 @@ __global__ __launch_bounds__(kFThreads) void decode_fused_kernel(FusedParams f) 
       const int e = uniform(sm.act[aa]);
       const bool shared = e == p.n_experts;
       const int64_t row = (shared ? 0 : (int64_t)e * p.hidden) + rb * 16 + r16;
-      const uint8_t* c = (shared ? p.sdown_c : p.down_c) + row * dcb + ks * 64 + g * 16;
+      const int64_t blk = (shared ? 0 : (int64_t)e * n_rb) + rb;
+      const uint8_t* c = PK ? p.pk_c[shared ? 5 : 2] + (blk * ksteps + ks) * 1024 + lane * 16
+                            : (shared ? p.sdown_c : p.down_c) + row * dcb + ks * 64 + g * 16;
       if (a < nseg) {
         dq[a] = load16(c);
-        ds[a] = sm.dsc[a][r16 * dsb + ks * 4 + g];  // copied into LDS above
+        // copied into LDS above
+        ds[a] = PK ? sm.dsc[a][(ks >> 2) * 256 + lane * 4 + (ks & 3)]
+                   : sm.dsc[a][r16 * dsb + ks * 4 + g];
       }
     }
   };
@@ -630,7 +690,7 @@ hipError_t launch(void (*kernel)(Params...), dim3 grid, dim3 block, size_t lds,
 
 // Workgroups of the kernel that fit on the device at once; every one of them
 // must be resident for the grid barrier.
-template <int S>
+template <int S, bool PK>
 hipError_t resident_grid(int* grid) {
   static int cached = 0;
   static hipError_t status = hipSuccess;
@@ -641,22 +701,23 @@ hipError_t resident_grid(int* grid) {
       status = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (status == hipSuccess)
       status = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, reinterpret_cast<const void*>(decode_fused_kernel<S>), kFThreads, 0);
+          &per_cu, reinterpret_cast<const void*>(decode_fused_kernel<S, PK>), kFThreads, 0);
     if (status == hipSuccess) cached = per_cu * cus;
   }
   *grid = cached;
   return status;
 }
 
-template <int S>
+template <int S, bool PK>
 hipError_t fused_launch(FusedParams f, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   int grid = 0;
-  const hipError_t e = resident_grid<S>(&grid);
+  const hipError_t e = resident_grid<S, PK>(&grid);
   if (e != hipSuccess) return e;
   if (grid < 1) return hipErrorInvalidConfiguration;
   if (grid > FusedSync::kMaxGrid) grid = FusedSync::kMaxGrid;  // still all resident
   f.grid = grid;
-  return launch(decode_fused_kernel<S>, dim3(grid), dim3(kFThreads), 0, stream, start, stop, f);
+  return launch(decode_fused_kernel<S, PK>, dim3(grid), dim3(kFThreads), 0, stream, start, stop,
+                f);
 }
 
 }  // namespace
@@ -670,11 +731,14 @@ int fused_decode_steps(const FfnParams& p) {
   const int s = p.hidden / 512;
   int grid = 0;
   hipError_t e = hipErrorInvalidValue;
+  // the packed copy when the layer has one (it exists only for shapes that
+  // are multiples of 512, so S is 4 or 8 here)
+  const bool pk = p.packed && s % 4 == 0;
   switch (s) {
-    case 1: e = resident_grid<1>(&grid); break;
-    case 2: e = resident_grid<2>(&grid); break;
-    case 4: e = resident_grid<4>(&grid); break;
-    case 8: e = resident_grid<8>(&grid); break;
+    case 1: e = resident_grid<1, false>(&grid); break;
+    case 2: e = resident_grid<2, false>(&grid); break;
+    case 4: e = pk ? resident_grid<4, true>(&grid) : resident_grid<4, false>(&grid); break;
+    case 8: e = pk ? resident_grid<8, true>(&grid) : resident_grid<8, false>(&grid); break;
     default: return 0;
   }
   // every workgroup takes at most one row block of the down projection (a
@@ -685,11 +749,14 @@ int fused_decode_steps(const FfnParams& p) {
 
 hipError_t launch_decode_fused(const FusedParams& f, hipStream_t stream, hipEvent_t start,
                                hipEvent_t stop) {
+  const bool pk = f.p.packed;
   switch (fused_decode_steps(f.p)) {
-    case 1: return fused_launch<1>(f, stream, start, stop);
-    case 2: return fused_launch<2>(f, stream, start, stop);
-    case 4: return fused_launch<4>(f, stream, start, stop);
-    case 8: return fused_launch<8>(f, stream, start, stop);
+    case 1: return fused_launch<1, false>(f, stream, start, stop);
+    case 2: return fused_launch<2, false>(f, stream, start, stop);
+    case 4: return pk ? fused_launch<4, true>(f, stream, start, stop)
+                      : fused_launch<4, false>(f, stream, start, stop);
+    case 8: return pk ? fused_launch<8, true>(f, stream, start, stop)
+                      : fused_launch<8, false>(f, stream, start, stop);
     default: return hipErrorInvalidValue;
   }
 }
