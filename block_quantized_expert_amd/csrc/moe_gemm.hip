@@ -520,10 +520,10 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
   //  - otherwise: one byte per row and step, loaded with the step's codes.
   // fp8 (SC: H a multiple of 512): the row's one byte per step, four steps
   // in one 4-byte load (kCh).
-  // PK (MXFP4 with SC): the packed copy, codes one KiB per step and row
-  // block, a lane's scale bytes of four steps one word (as the chunks
-  // below, without the byte gathering)
-  constexpr bool kPK = PK && WT == MOE_W_MXFP4 && SC;
+  // PK (with SC): the packed copy, codes Q KiB per step and row block, a
+  // lane's scale bytes of four steps one word (as the chunks below, without
+  // the byte gathering)
+  constexpr bool kPK = PK && SC;
   constexpr bool kSC = SC && WT == MOE_W_MXFP4 && NBT <= 5 && !kPK;
   constexpr bool kCh = SC && (WT == MOE_W_MXFP4 ? NBT >= 6 || kPK : true);
   constexpr int kLoads = (kSC || kCh) ? 4 * Q : 4 * (Q + 1);  // vector loads of one step's weights
@@ -559,7 +559,7 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
   if constexpr (kPK) {
 #pragma unroll
     for (int mat = 0; mat < 2; ++mat) {
-      pkc[mat] = p.pk_c[(shared ? 3 : 0) + mat] + (wrow_g / 16) * nks * 1024;
+      pkc[mat] = p.pk_c[(shared ? 3 : 0) + mat] + (wrow_g / 16) * nks * 1024 * Q;
       pks[mat] = p.pk_s[(shared ? 3 : 0) + mat] + (wrow_g / 16) * (nks / 4) * 256;
     }
   }
@@ -609,7 +609,8 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
 #pragma unroll
         for (int i = 0; i < Q; ++i) {
           if constexpr (kPK)
-            q[mat][rb][i] = load16(pkc[mat] + (uint32_t)((rb * nks + k) * 1024 + lane * 16));
+            q[mat][rb][i] =
+                load16(pkc[mat] + (uint32_t)(((rb * nks + k) * Q + i) * 1024 + lane * 16));
           else
             q[mat][rb][i] = load16(cwave[mat] + (lco + (uint32_t)(16 * rb * cb + F::code_off(k, 0) + 64 * i)));
         }
@@ -1141,7 +1142,7 @@ __device__ __forceinline__ void down3_item(const FfnParams& p, const GItem& it, 
   constexpr int RB = kDnRows / (16 * kGWaves);  // row blocks per wavefront
   // scale bytes of the weights as in down_item; PK: the packed copy, as in
   // gate/up
-  constexpr bool kPK = PK && WT == MOE_W_MXFP4 && SC;
+  constexpr bool kPK = PK && SC;
   constexpr bool kSC = SC && WT == MOE_W_MXFP4 && NBT <= 3 && !kPK;
   constexpr bool kCh = SC && (WT == MOE_W_MXFP4 ? NBT == 4 || kPK : true);
   constexpr int kLoads = (kSC || kCh) ? RB * Q : RB * (Q + 1);
@@ -1167,7 +1168,7 @@ __device__ __forceinline__ void down3_item(const FfnParams& p, const GItem& it, 
   const uint8_t* pks = nullptr;
   if constexpr (kPK) {
     const int64_t blk = ((shared ? 0 : (int64_t)it.seg * p.hidden) + (nrb > 0 ? wrow0 : 0)) / 16;
-    pkc = p.pk_c[shared ? 5 : 2] + blk * nks * 1024;
+    pkc = p.pk_c[shared ? 5 : 2] + blk * nks * 1024 * Q;
     pks = p.pk_s[shared ? 5 : 2] + blk * (nks / 4) * 256;
   }
 
@@ -1236,7 +1237,7 @@ __device__ __forceinline__ void down3_item(const FfnParams& p, const GItem& it, 
 #pragma unroll
       for (int i = 0; i < Q; ++i) {
         if constexpr (kPK)
-          q[rb][i] = load16(pkc + (uint32_t)((rr * nks + k) * 1024 + lane * 16));
+          q[rb][i] = load16(pkc + (uint32_t)(((rr * nks + k) * Q + i) * 1024 + lane * 16));
         else
           q[rb][i] = load16(cbase + lc + 16 * rr * cb + F::code_off(k, 0) + 64 * i);
       }
@@ -1543,6 +1544,10 @@ hipError_t launch_gemm_gate_up(const FfnParams& p, hipStream_t stream, hipEvent_
   return by_type(p, stream, start, stop, [&](int wt, int lo, int hi, hipEvent_t a, hipEvent_t b) {
     if (wt != MOE_W_MXFP4) {
       if (!o32) return gate_up_range<MOE_W_FP8E4M3_B128, 64, false, false>(p, lo, hi, stream, a, b);
+      // packed fp8: only a shared expert (routed experts are packed only as
+      // MXFP4), in a launch of its own
+      if (p.packed && lo >= p.n_experts)
+        return gate_up_range<MOE_W_FP8E4M3_B128, 64, true, true, true>(p, lo, hi, stream, a, b);
       return p.hidden % 512 == 0
                  ? gate_up_range<MOE_W_FP8E4M3_B128, 64, true, true>(p, lo, hi, stream, a, b)
                  : gate_up_range<MOE_W_FP8E4M3_B128, 64, false, true>(p, lo, hi, stream, a, b);
@@ -1569,6 +1574,8 @@ hipError_t launch_gemm_down(const FfnParams& p, hipStream_t stream, hipEvent_t s
       // the fp8 segments of this launch: the routed ones, the shared one
       const bool sc8 = (lo >= p.n_experts || p.inter % 512 == 0) &&
                        (hi <= p.n_experts || p.shared_inter % 512 == 0);
+      if (h3 && p.packed && lo >= p.n_experts)
+        return down3_range<MOE_W_FP8E4M3_B128, true, true>(p, lo, hi, stream, a, b);
       if (h3)
         return sc8 ? down3_range<MOE_W_FP8E4M3_B128, true>(p, lo, hi, stream, a, b)
                    : down3_range<MOE_W_FP8E4M3_B128, false>(p, lo, hi, stream, a, b);

@@ -105,23 +105,31 @@ moe_status check_layer(const moe_layer* layer) {
 moe_status plan_pack(const moe_layer* layer, PackPlan* plan) {
   if (layer->gate.type != MOE_W_MXFP4) return MOE_ERR_UNSUPPORTED;
   if (layer->hidden % 512 != 0 || layer->inter % 512 != 0) return MOE_ERR_UNSUPPORTED;
-  const bool sh = layer->has_shared && layer->shared_gate.type == MOE_W_MXFP4;
+  const bool sh = layer->has_shared != 0;
   if (sh && layer->shared_inter % 512 != 0) return MOE_ERR_UNSUPPORTED;
   const int64_t E = layer->n_experts, H = layer->hidden, I = layer->inter;
   const int64_t SI = sh ? layer->shared_inter : 0;
   const int64_t rows[6] = {E * I, E * I, E * H, SI, SI, sh ? H : 0};
   const int32_t cols[6] = {(int32_t)H, (int32_t)H, (int32_t)I, (int32_t)H, (int32_t)H,
                            (int32_t)SI};
+  const int32_t st = sh ? layer->shared_gate.type : MOE_W_MXFP4;
+  const int32_t type[6] = {MOE_W_MXFP4, MOE_W_MXFP4, MOE_W_MXFP4, st, st, st};
   size_t off = 0;
   for (int m = 0; m < 6; ++m) {
     plan->rows[m] = rows[m];
     plan->cols[m] = cols[m];
+    plan->type[m] = type[m];
     if (rows[m] == 0) {
       plan->codes[m] = plan->scales[m] = -1;
       continue;
     }
+    // codes: half a byte per input (MXFP4) or a byte (fp8); scale words: one
+    // per lane, four steps and 16-row block, rows * cols / 32 bytes for both
+    // (fp8 has a scale byte per 128 inputs of a row, and the four lanes of a
+    // row hold the same word)
+    const bool fp4 = type[m] == MOE_W_MXFP4;
     plan->codes[m] = (int64_t)off;
-    off += align_up((size_t)rows[m] * (size_t)(cols[m] / 2), 256);
+    off += align_up((size_t)rows[m] * (size_t)(fp4 ? cols[m] / 2 : cols[m]), 256);
     plan->scales[m] = (int64_t)off;
     off += align_up((size_t)rows[m] * (size_t)(cols[m] / 32), 256);
   }

@@ -82,13 +82,14 @@ moe_status check_layer(const moe_layer* layer);
 
 // Layout of a packed copy (moe_pack_experts): per matrix (gate, up, down,
 // shared gate, shared up, shared down) the byte offset of its codes and of
-// its scales, or -1 for a matrix that is not packed (no shared expert, or
-// a shared expert that is not MXFP4); rows and inputs of each matrix.
+// its scales, or -1 for a matrix that is not packed (no shared expert);
+// rows, inputs and weight type of each matrix.
 struct PackPlan {
   int64_t codes[6];
   int64_t scales[6];
   int64_t rows[6];
   int32_t cols[6];
+  int32_t type[6];
   size_t total;
 };
 // MOE_OK with the plan for a layer that passed check_layer and can be

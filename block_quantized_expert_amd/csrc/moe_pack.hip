@@ -1,8 +1,8 @@
-// Packed copy of a layer's MXFP4 matrices for the batched gate/up and down
+// Packed copy of a layer's expert matrices for the batched gate/up and down
 // (declared in include/moe.h): the same code and scale bytes, reordered so
-// that one 128-input step of a 16-row block is one contiguous KiB in the
-// matrix instruction's lane order, and a lane's scale bytes of four steps
-// are one 32-bit word.
+// that one 128-input step of a 16-row block is one contiguous KiB (two for
+// fp8) in the matrix instruction's lane order, and a lane's scale bytes of
+// four steps are one 32-bit word.
 //
 // "DeepSeek V4 target engine (CPU + optional CUDA tier)", introduction and
 // GPU coverage: routed experts in MXFP4 (E2M1 codes, one UE8M0 scale per 32
@@ -54,6 +54,39 @@ __global__ __launch_bounds__(kPackThreads) void pack_scales_kernel(const uint8_t
   }
 }
 
+// fp8 codes: unit u (16 bytes) is block b, step s, half h, lane l = 16 g + r:
+// row 16 b + r, bytes 128 s + 64 h + 16 g .. +15 (the two 16-byte groups an
+// E4M3 operand lane holds), at ((b S + s) 2 + h) KiB + 16 l.
+__global__ __launch_bounds__(kPackThreads) void pack_codes_fp8_kernel(
+    const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int64_t units, int cols) {
+  const int64_t steps = cols / 128, per_block = steps * 128;
+  for (int64_t u = (int64_t)blockIdx.x * kPackThreads + threadIdx.x; u < units;
+       u += (int64_t)gridDim.x * kPackThreads) {
+    const int64_t b = u / per_block, rem = u - b * per_block;
+    const int64_t s = rem >> 7;
+    const int h = (int)((rem >> 6) & 1), l = (int)(rem & 63), g = l >> 4, r = l & 15;
+    const int64_t off = (16 * b + r) * cols + 128 * s + 64 * h + 16 * g;
+    *reinterpret_cast<u32x4*>(dst + 16 * u) = *reinterpret_cast<const u32x4*>(src + off);
+  }
+}
+
+// fp8 scales (one byte per 128 inputs of a row): unit u (4 bytes) is block
+// b, chunk c, lane l = 16 g + r: byte t is row 16 b + r's scale of step
+// 4c + t (the four lanes of a row hold the same word).
+__global__ __launch_bounds__(kPackThreads) void pack_scales_fp8_kernel(
+    const uint8_t* __restrict__ src, uint32_t* __restrict__ dst, int64_t units, int cols) {
+  const int64_t chunks = cols / 512, per_block = chunks * 64, row_bytes = cols / 128;
+  for (int64_t u = (int64_t)blockIdx.x * kPackThreads + threadIdx.x; u < units;
+       u += (int64_t)gridDim.x * kPackThreads) {
+    const int64_t b = u / per_block, rem = u - b * per_block;
+    const int64_t c = rem >> 6;
+    const int r = (int)(rem & 15);
+    const uint8_t* row = src + (16 * b + r) * row_bytes + 4 * c;
+    dst[u] = (uint32_t)row[0] | ((uint32_t)row[1] << 8) | ((uint32_t)row[2] << 16) |
+             ((uint32_t)row[3] << 24);
+  }
+}
+
 unsigned pack_grid(int64_t units) {
   const int64_t blocks = (units + kPackThreads - 1) / kPackThreads;
   return (unsigned)(blocks < kPackMaxBlocks ? blocks : kPackMaxBlocks);
@@ -89,14 +122,18 @@ extern "C" moe_status moe_pack_experts(const moe_layer* layer, void* packed, siz
   for (int m = 0; m < 6; ++m) {
     if (pk.codes[m] < 0) continue;
     const int cols = pk.cols[m];
-    const int64_t code_units = pk.rows[m] * (cols / 2) / 16;
-    const int64_t scale_units = pk.rows[m] * (cols / 32) / 4;
-    hipLaunchKernelGGL(moe::pack_codes_kernel, dim3(moe::pack_grid(code_units)),
-                       dim3(moe::kPackThreads), 0, stream, src[m]->codes, base + pk.codes[m],
-                       code_units, cols);
-    hipLaunchKernelGGL(moe::pack_scales_kernel, dim3(moe::pack_grid(scale_units)),
-                       dim3(moe::kPackThreads), 0, stream, src[m]->scales,
-                       reinterpret_cast<uint32_t*>(base + pk.scales[m]), scale_units, cols);
+    // 16-byte code units (rows x cols/2 bytes MXFP4, rows x cols fp8) and
+    // 4-byte scale words (64 lanes x cols/512 per 16-row block, both types)
+    const bool fp4 = pk.type[m] == MOE_W_MXFP4;
+    const int64_t code_units = pk.rows[m] * (fp4 ? cols / 2 : cols) / 16;
+    const int64_t scale_units = pk.rows[m] / 16 * 64 * (cols / 512);
+    hipLaunchKernelGGL(fp4 ? moe::pack_codes_kernel : moe::pack_codes_fp8_kernel,
+                       dim3(moe::pack_grid(code_units)), dim3(moe::kPackThreads), 0, stream,
+                       src[m]->codes, base + pk.codes[m], code_units, cols);
+    hipLaunchKernelGGL(fp4 ? moe::pack_scales_kernel : moe::pack_scales_fp8_kernel,
+                       dim3(moe::pack_grid(scale_units)), dim3(moe::kPackThreads), 0, stream,
+                       src[m]->scales, reinterpret_cast<uint32_t*>(base + pk.scales[m]),
+                       scale_units, cols);
     if (hipGetLastError() != hipSuccess) return MOE_ERR_DEVICE;
   }
   return MOE_OK;

@@ -105,7 +105,7 @@ typedef struct {
   int32_t has_shared;      /* 0 or 1: one shared expert, weight 1        */
   int32_t shared_inter;    /* multiple of 128 when has_shared            */
   moe_proj shared_gate, shared_up, shared_down; /* one matrix each       */
-  /* Optional (NULL: unused): the layer's MXFP4 weights as written by
+  /* Optional (NULL: unused): the layer's weights as written by
    * moe_pack_experts, 256-byte aligned.  The batched gate/up and down read
    * them from there; every other path reads the arrays above, which stay
    * required and must hold the same weights. */
@@ -250,19 +250,19 @@ moe_status moe_group(const int32_t* topk_ids, int n_tokens, int top_k, int n_exp
 size_t moe_ffn_workspace_bytes(const moe_layer* layer, int n_tokens);
 
 /*
- * A second copy of a layer's MXFP4 weights in the order the batched gate/up
- * and down read them (the same codes and UE8M0 scale bytes, "DeepSeek V4
- * target engine (CPU + optional CUDA tier)": MXFP4 experts; the layout
- * itself is this library's, for this GPU's matrix instructions).  In the
- * row-major arrays a 128-input step of 16 rows touches 64 bytes of each of
- * 16 rows; packed, it is one contiguous KiB, and the scale bytes of four
- * steps of a lane are one 32-bit word.
+ * A second copy of a layer's expert weights in the order the batched gate/up
+ * and down (and the single-token kernel) read them: the same codes and UE8M0
+ * scale bytes ("DeepSeek V4 target engine (CPU + optional CUDA tier)": MXFP4
+ * routed experts, fp8-e4m3 + UE8M0 dense weights; the layout itself is this
+ * library's, for this GPU's matrix instructions).  In the row-major arrays
+ * a 128-input step of 16 rows touches 64 (MXFP4) or 128 (fp8) bytes of each
+ * of 16 rows; packed, it is one (two) contiguous KiB, and the scale bytes of
+ * four steps of a lane are one 32-bit word.
  *
  * moe_packed_experts_bytes: bytes of the copy for `layer` (the routed gate,
- *   up and down matrices, and the shared expert's three when it is MXFP4
- *   too), or 0 when the layer cannot be packed: routed experts not MXFP4,
- *   or hidden, inter (or shared_inter, for an MXFP4 shared expert) not a
- *   multiple of 512.
+ *   up and down matrices and the shared expert's three), or 0 when the layer
+ *   cannot be packed: routed experts not MXFP4, or hidden, inter (or
+ *   shared_inter) not a multiple of 512.
  * moe_pack_experts: writes the copy into `packed` (device, 256-byte
  *   aligned, at least moe_packed_experts_bytes(layer) bytes; the caller owns
  *   it), asynchronously on `stream`, reading the layer's arrays.  Returns
@@ -270,13 +270,19 @@ size_t moe_ffn_workspace_bytes(const moe_layer* layer, int n_tokens);
  *   for a NULL or misaligned buffer or a short size.  Set
  *   layer->packed_experts = packed afterwards to use it; results are bitwise
  *   equal with and without it.
- * Layout, for each packed matrix of R rows x C inputs (R/16 row blocks of
- * 16 rows, S = C/128 steps): codes, block b step s at byte (b*S + s)*1024,
- * lane l = 16*g + r holding the 16 code bytes of row 16b + r, inputs
- * 128s + 32g .. +31; then the scales, block b and steps 4c .. 4c+3 at byte
- * (b*S/4 + c)*256, lane l holding in byte t the scale of row 16b + r, inputs
- * 128(4c+t) + 32g .. +31.  Matrices in the order gate, up, down, shared
- * gate, shared up, shared down, each section 256-byte aligned.
+ * Layout, for each matrix of R rows x C inputs (R/16 row blocks of 16 rows,
+ * S = C/128 steps, lane l = 16*g + r):
+ *   MXFP4 codes: block b step s at byte (b*S + s)*1024, lane l holding the
+ *     16 code bytes of row 16b + r, inputs 128s + 32g .. +31;
+ *   fp8 codes: block b step s half h at byte ((b*S + s)*2 + h)*1024, lane l
+ *     holding row 16b + r, inputs 128s + 64h + 16g .. +15;
+ *   scales (both): block b, steps 4c .. 4c+3 at byte (b*S/4 + c)*256, lane l
+ *     holding in byte t the scale of row 16b + r for step 4c+t (MXFP4: of
+ *     its inputs 128(4c+t) + 32g .. +31; fp8: the row's one scale of the
+ *     step).
+ * Matrices in the order gate, up, down, shared gate, shared up, shared down,
+ * codes then scales, each section 256-byte aligned; scales take R*C/32 bytes
+ * in both formats.
  */
 size_t moe_packed_experts_bytes(const moe_layer* layer);
 moe_status moe_pack_experts(const moe_layer* layer, void* packed, size_t packed_bytes,

@@ -312,14 +312,17 @@ def test_opts_struct_layout_matches_c():
     assert ctypes.sizeof(B.MoeOpts) == 32
 
 
-def _pack_bytes_expected(E, H, I, SI=None):
-    """The packed layout of include/moe.h, summed section by section."""
+def _pack_bytes_expected(E, H, I, SI=None, shared_fp8=False):
+    """The packed layout of include/moe.h, summed section by section: codes
+    (half a byte per input MXFP4, a byte fp8), then R*C/32 bytes of scale
+    words."""
     def up(v):
         return -(-v // 256) * 256
-    mats = [(E * I, H), (E * I, H), (E * H, I)]
+    mats = [(E * I, H, 2), (E * I, H, 2), (E * H, I, 2)]
     if SI is not None:
-        mats += [(SI, H), (SI, H), (H, SI)]
-    return sum(up(r * c // 2) + up(r * c // 32) for r, c in mats)
+        d = 1 if shared_fp8 else 2
+        mats += [(SI, H, d), (SI, H, d), (H, SI, d)]
+    return sum(up(r * c // d) + up(r * c // 32) for r, c, d in mats)
 
 
 def test_packed_experts_bytes():
@@ -327,9 +330,10 @@ def test_packed_experts_bytes():
     # routed and shared MXFP4: all six matrices
     L = _layer()
     assert lib.moe_packed_experts_bytes(ctypes.byref(L)) == _pack_bytes_expected(256, 4096, 2048, 2048)
-    # an fp8 shared expert is not packed (its own launch reads it row-major)
+    # an fp8 shared expert: a byte per input
     L = _layer(swtype=1)
-    assert lib.moe_packed_experts_bytes(ctypes.byref(L)) == _pack_bytes_expected(256, 4096, 2048)
+    assert lib.moe_packed_experts_bytes(ctypes.byref(L)) == \
+        _pack_bytes_expected(256, 4096, 2048, 2048, shared_fp8=True)
     L = _layer(shared=False, e=8, hidden=1024, inter=512)
     assert lib.moe_packed_experts_bytes(ctypes.byref(L)) == _pack_bytes_expected(8, 1024, 512)
     # cannot be packed: fp8 routed experts, H or I not a multiple of 512

@@ -1,15 +1,16 @@
-"""The packed copy of a layer's MXFP4 matrices (moe_pack_experts).
+"""The packed copy of a layer's expert matrices (moe_pack_experts).
 
 - Its bytes against the layout include/moe.h states, restated here with
-  numpy reshapes of the row-major arrays.
-- Every batched output computed with the copy is bitwise equal to the one
-  computed without it: the same code and scale bytes reach the matrix
-  instruction in the same order, only their addresses differ.  Checked on
-  every tile size of the grouped GEMMs (the layers of the tile-parity test),
-  with an fp8 shared expert (its own launch, not packed), with the lazy skip
-  and with pruning, and on the full-size batched workloads; the outputs
-  without the copy are compared with the oracle by the other GPU tests.
-- The single-token fused kernel and the small-batch kernels ignore the copy.
+  numpy reshapes of the row-major arrays (MXFP4 and fp8 shared experts).
+- Every output computed with the copy is bitwise equal to the one computed
+  without it: the same code and scale bytes reach the matrix instruction in
+  the same order, only their addresses differ.  Checked on every tile size
+  of the grouped GEMMs (the layers of the tile-parity test), with an fp8
+  shared expert (its own launch, packed in its format), with the lazy skip
+  and with pruning, on the full-size batched workloads, and through
+  moe_forward for one token (the fused kernel reads the copy) and eight (the
+  small-batch kernels ignore it); the outputs without the copy are compared
+  with the oracle by the other GPU tests.
 """
 
 from dataclasses import replace
@@ -37,13 +38,21 @@ def _gpu():
     torch.cuda.empty_cache()
 
 
-def _np_pack(codes, scales, rows, cols):
-    """Codes: row block b, step s, lane 16 g + r -> the 16 bytes 64 s + 16 g ..
-    of row 16 b + r.  Scales: block b, chunk c, lane 16 g + r, byte t -> scale
-    byte 4 (4 c + t) + g of row 16 b + r."""
+def _np_pack(codes, scales, rows, cols, fp8=False):
+    """MXFP4 codes: row block b, step s, lane 16 g + r -> the 16 bytes
+    64 s + 16 g .. of row 16 b + r; scales: block b, chunk c, lane 16 g + r,
+    byte t -> scale byte 4 (4 c + t) + g of row 16 b + r.  fp8 codes: block b,
+    step s, half h, lane 16 g + r -> bytes 128 s + 64 h + 16 g .. of row
+    16 b + r; scales: byte t -> the row's scale of step 4 c + t (the same
+    word on the row's four lanes)."""
     s = cols // 128
-    pc = codes.reshape(rows // 16, 16, s, 4, 16).transpose(0, 2, 3, 1, 4)
-    ps = scales.reshape(rows // 16, 16, s // 4, 4, 4).transpose(0, 2, 4, 1, 3)
+    if fp8:
+        pc = codes.reshape(rows // 16, 16, s, 2, 4, 16).transpose(0, 2, 3, 4, 1, 5)
+        sc = scales.reshape(rows // 16, 16, s // 4, 4).transpose(0, 2, 1, 3)  # [b][c][r][t]
+        ps = np.broadcast_to(sc[:, :, None], (rows // 16, s // 4, 4, 16, 4))
+    else:
+        pc = codes.reshape(rows // 16, 16, s, 4, 16).transpose(0, 2, 3, 1, 4)
+        ps = scales.reshape(rows // 16, 16, s // 4, 4, 4).transpose(0, 2, 4, 1, 3)
     return np.ascontiguousarray(pc).reshape(-1), np.ascontiguousarray(ps).reshape(-1)
 
 
@@ -51,9 +60,10 @@ def _up(v):
     return -(-v // 256) * 256
 
 
-def test_packed_bytes_follow_the_stated_layout():
-    wl = replace(RAGGED, n_experts=4, top_k=2, shared_inter=1024, seed=7)
-    print("case pack layout", flush=True)
+@pytest.mark.parametrize("shared", ["mxfp4", "fp8_e4m3_b128"])
+def test_packed_bytes_follow_the_stated_layout(shared):
+    wl = replace(RAGGED, n_experts=4, top_k=2, shared_inter=1024, seed=7, shared=shared)
+    print("case pack layout %s" % shared, flush=True)
     weights = I.make_layer(wl, device=DEV)
     layer = B.Layer(weights, wl.top_k)
     assert layer.pack()
@@ -62,13 +72,15 @@ def test_packed_bytes_follow_the_stated_layout():
     got = got[(-layer._packed.data_ptr()) % 256:]
     E, H, Iw, SI = wl.n_experts, wl.hidden, wl.inter, 1024
     sh = weights["shared"]
-    mats = [(weights["gate"], E * Iw, H), (weights["up"], E * Iw, H), (weights["down"], E * H, Iw),
-            (sh["gate"], SI, H), (sh["up"], SI, H), (sh["down"], H, SI)]
+    f8 = shared != "mxfp4"
+    mats = [(weights["gate"], E * Iw, H, False), (weights["up"], E * Iw, H, False),
+            (weights["down"], E * H, Iw, False),
+            (sh["gate"], SI, H, f8), (sh["up"], SI, H, f8), (sh["down"], H, SI, f8)]
     off = 0
-    for m, rows, cols in mats:
-        codes = m["codes"].cpu().numpy().reshape(rows, cols // 2)
-        scales = m["scales"].cpu().numpy().reshape(rows, cols // 32)
-        pc, ps = _np_pack(codes, scales, rows, cols)
+    for m, rows, cols, fp8 in mats:
+        codes = m["codes"].cpu().numpy().reshape(rows, cols if fp8 else cols // 2)
+        scales = m["scales"].cpu().numpy().reshape(rows, cols // (128 if fp8 else 32))
+        pc, ps = _np_pack(codes, scales, rows, cols, fp8)
         assert np.array_equal(got[off:off + pc.size], pc)
         off += _up(pc.size)
         assert np.array_equal(got[off:off + ps.size], ps)
