@@ -606,9 +606,9 @@ __global__ __launch_bounds__(kThreads) void gate_up_decode_kernel(FfnParams p, i
 
 // ------------------------------------------------------- combine
 
-// y[t] = o_shared[t] + sum_i o[inv_perm[t*k + i]] (weights already applied),
-// in that fixed order, leaving out slots dropped by tail pruning or by the
-// lazy skip; four features per thread.
+// y[t] = o_shared[t] + sum_i w[t*k + i] * o[inv_perm[t*k + i]], in that
+// fixed order, leaving out slots dropped by tail pruning or by the lazy
+// skip; four features per thread.
 __global__ __launch_bounds__(256) void combine_kernel(FfnParams p) {
   const int h4 = p.hidden / 4;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -623,7 +623,9 @@ __global__ __launch_bounds__(256) void combine_kernel(FfnParams p) {
     const int pp = p.inv_perm[t * p.top_k + j];
     // a slot the lazy skip drops contributes nothing
     const bool live = pp >= 0 && (p.lazy_tau == 0.0f || __uint_as_float(p.gmax[pp]) >= p.lazy_tau);
-    if (live) acc += *reinterpret_cast<const f32x4*>(p.obuf + (int64_t)pp * p.hidden + q);
+    if (live)
+      acc += p.topk_w[t * p.top_k + j] *
+             *reinterpret_cast<const f32x4*>(p.obuf + (int64_t)pp * p.hidden + q);
   }
   *reinterpret_cast<f32x4*>(p.y + t * p.hidden + q) = acc;
 }

@@ -851,7 +851,11 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float gv = acc[0][rb][tb][r];
-        v[rb][r] = gv / (1.0f + expf(-gv)) * acc[1][rb][tb][r];
+        // SiLU with the hardware exponential and reciprocal (a few ulp,
+        // far below the 2^-12 that the three-part split keeps): the
+        // range-reduced expf and the IEEE division cost about 20
+        // instructions per element, most of this epilogue
+        v[rb][r] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * acc[1][rb][tb][r];
         mag = fmaxf(mag, fabsf(v[rb][r]));
       }
     mag = fmaxf(mag, __shfl_xor(mag, 16));
@@ -916,8 +920,10 @@ __device__ __forceinline__ void down_item(const FfnParams& p, const GItem& it, c
   const int wrow0 = it.row0 + 64 * wave;
   const int nrb = uniform(max(0, min(RB, (p.hidden - wrow0) / 16)));
 
-  // the lane's row in block 0 (blocks past the matrix end reuse it and are
-  // not multiplied)
+  // the lane's row in block 0.  Blocks past the matrix end (only in a short
+  // last row tile) reuse block 0's operands and are multiplied like the
+  // others, but not stored: a test around each MFMA would make every one a
+  // branch target with a full LDS wait in front of it.
   const int64_t r0 = wrow0 + r16 < p.hidden ? wrow0 + r16 : r16;
   const int64_t lrow = (shared ? 0 : (int64_t)it.seg * p.hidden) + r0;
   const int64_t lc = lrow * cb + F::code_off(0, g), ls = lrow * sb + F::scale_off(0, g);
@@ -931,14 +937,6 @@ __device__ __forceinline__ void down_item(const FfnParams& p, const GItem& it, c
   for (int i = 0; i < Stage<TT>::kPer; ++i) {
     const int n = Stage<TT>::row_of(i, wave, lane);
     st.row[i] = it.slot0 + (n < it.m ? n : 0);
-  }
-
-  // routing weight of each token column, fetched now, used by the epilogue
-  float wcol[TB];
-#pragma unroll
-  for (int tb = 0; tb < TB; ++tb) {
-    const int n = min(tb * 16 + r16, it.m - 1);
-    wcol[tb] = shared ? 1.0f : p.topk_w[p.perm[it.slot0 + n]];
   }
 
   // weight codes of the current step and the next
@@ -1053,10 +1051,8 @@ __device__ __forceinline__ void down_item(const FfnParams& p, const GItem& it, c
         const bf16x8 fl = token_frag(curl, tb, j, g, r16);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-          if (rb < nrb) {
-            acc[rb][tb] = mfma_bf16(a[j & 1][rb], fh, acc[rb][tb]);
-            acc[rb][tb] = mfma_bf16(a[j & 1][rb], fl, acc[rb][tb]);
-          }
+          acc[rb][tb] = mfma_bf16(a[j & 1][rb], fh, acc[rb][tb]);
+          acc[rb][tb] = mfma_bf16(a[j & 1][rb], fl, acc[rb][tb]);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -1072,19 +1068,18 @@ __device__ __forceinline__ void down_item(const FfnParams& p, const GItem& it, c
   wait_vm<0>();
   take();  // the next item's ticket, in flight during the epilogue
 
-  // routing weight of each token column, then the per-slot outputs
+  // the per-slot outputs, unweighted: the combine applies the routing
+  // weights (so no item waits for them to arrive before its first step)
 #pragma unroll
   for (int tb = 0; tb < TB; ++tb) {
     const int n = tb * 16 + r16;
     if (tb < nbt && n < it.m) {
       const int64_t slot = it.slot0 + n;
-      const float w = wcol[tb];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        if (rb < nrb) {
+        if (rb < nrb)
           *reinterpret_cast<f32x4*>(p.obuf + slot * p.hidden + wrow0 + 16 * rb + 4 * g) =
-              acc[rb][tb] * w;
-        }
+              acc[rb][tb];
       }
     }
   }
@@ -1153,7 +1148,9 @@ __device__ __forceinline__ void down3_item(const FfnParams& p, const GItem& it, 
   const int nks = kdim / 128;
   constexpr int nbt = NBT;
   const int64_t hs = p.h_stride;
-  // row blocks of this wavefront inside the matrix (the last tile may be short)
+  // row blocks of this wavefront inside the matrix (the last tile may be
+  // short; blocks past the end reuse block 0's operands, are multiplied and
+  // not stored, as in down_item)
   const int wrow0 = it.row0 + 64 * wave;
   const int nrb = uniform(max(0, min(RB, (p.hidden - wrow0) / 16)));
   const int64_t r0 = wrow0 + r16 < p.hidden ? wrow0 + r16 : r16;
@@ -1217,14 +1214,6 @@ __device__ __forceinline__ void down3_item(const FfnParams& p, const GItem& it, 
         __builtin_amdgcn_global_load_lds(hss[e] + ks * 16, lds(sbuf(ks) + sg * 256), 4, 0, 0);
     }
   };
-
-  // routing weight of each token column, fetched now, used by the epilogue
-  float wcol[TB];
-#pragma unroll
-  for (int tb = 0; tb < TB; ++tb) {
-    const int n = min(tb * 16 + r16, it.m - 1);
-    wcol[tb] = shared ? 1.0f : p.topk_w[p.perm[it.slot0 + n]];
-  }
 
   // weight codes of the current step and the next
   u32x4 q0[RB][Q], q1[RB][Q];
@@ -1319,8 +1308,12 @@ __device__ __forceinline__ void down3_item(const FfnParams& p, const GItem& it, 
     }
     lds_cptr ps = to_lds(cts) + r16 * 16 + 4 * g;
     opaque(ps);
-    // a ring of kAhead + 1 operands: operand u is read kAhead before use
-    constexpr int kAhead = 1;
+    // a ring of kAhead + 1 operands: operand u is read kAhead before use.
+    // With one ahead, the three parts per token block (an odd count against
+    // a ring of two) led the register allocator to move accumulators
+    // through the operand registers, so most reads waited behind the MFMAs
+    // before them; with two ahead every operand keeps its own registers.
+    constexpr int kAhead = 2;
     i32x8 bop[kAhead + 1];
     uint32_t sbt[2];
     auto read_op = [&](int u) {
@@ -1339,14 +1332,12 @@ __device__ __forceinline__ void down3_item(const FfnParams& p, const GItem& it, 
       const i32x8& b = bop[u % (kAhead + 1)];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        if (rb < nrb) {
-          if (q == 0)
-            acc[rb][tb] = mfma_scaled<FA, 0, 0>(a[rb], b, acc[rb][tb], sa[rb], sbt[tb & 1]);
-          else if (q == 1)
-            acc[rb][tb] = mfma_scaled<FA, 0, 1>(a[rb], b, acc[rb][tb], sa[rb], sbt[tb & 1]);
-          else
-            acc[rb][tb] = mfma_scaled<FA, 0, 2>(a[rb], b, acc[rb][tb], sa[rb], sbt[tb & 1]);
-        }
+        if (q == 0)
+          acc[rb][tb] = mfma_scaled<FA, 0, 0>(a[rb], b, acc[rb][tb], sa[rb], sbt[tb & 1]);
+        else if (q == 1)
+          acc[rb][tb] = mfma_scaled<FA, 0, 1>(a[rb], b, acc[rb][tb], sa[rb], sbt[tb & 1]);
+        else
+          acc[rb][tb] = mfma_scaled<FA, 0, 2>(a[rb], b, acc[rb][tb], sa[rb], sbt[tb & 1]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1381,19 +1372,18 @@ __device__ __forceinline__ void down3_item(const FfnParams& p, const GItem& it, 
   wait_vm<0>();
   take();  // the next item's ticket, in flight during the epilogue
 
-  // routing weight of each token column, then the per-slot outputs
+  // the per-slot outputs, unweighted: the combine applies the routing
+  // weights (so no item waits for them to arrive before its first step)
 #pragma unroll
   for (int tb = 0; tb < TB; ++tb) {
     const int n = tb * 16 + r16;
     if (tb < nbt && n < it.m) {
       const int64_t slot = it.slot0 + n;
-      const float w = wcol[tb];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        if (rb < nrb) {
+        if (rb < nrb)
           *reinterpret_cast<f32x4*>(p.obuf + slot * p.hidden + wrow0 + 16 * rb + 4 * g) =
-              acc[rb][tb] * w;
-        }
+              acc[rb][tb];
       }
     }
   }

@@ -42,7 +42,7 @@ struct FfnParams {
   // s-8 and a zero byte)
   uint8_t* h3;
   uint8_t* h3s;
-  float* obuf;  // [slots][hidden] weighted per-slot outputs
+  float* obuf;  // [slots][hidden] per-slot outputs (the combine weights them)
   float* y;     // [n_tokens][hidden]
   // gate-first lazy skip: a routed slot whose gate output has
   // max_j |SiLU(g_j)| < lazy_tau contributes nothing (lazy_tau 0: off).
