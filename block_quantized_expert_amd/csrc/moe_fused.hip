@@ -207,10 +207,11 @@ __global__ __launch_bounds__(kFThreads) void decode_fused_kernel(FusedParams f) 
       const uint8_t* uc = p.pk_c[shared ? 4 : 1] + (blk * nks + wq * S) * 1024 + lane * 16;
       const uint8_t* gs = p.pk_s[shared ? 3 : 0] + (blk * (nks / 4) + wq * S / 4) * 256 + lane * 4;
       const uint8_t* us = p.pk_s[shared ? 4 : 1] + (blk * (nks / 4) + wq * S / 4) * 256 + lane * 4;
+      // every line of the packed copy is read whole, once: past the caches
 #pragma unroll
       for (int j = 0; j < S; ++j) {
-        qg[j] = load16(gc + j * 1024);
-        qu[j] = load16(uc + j * 1024);
+        qg[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(gc + j * 1024));
+        qu[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(uc + j * 1024));
       }
 #pragma unroll
       for (int v = 0; v < S / 4; ++v) {
@@ -587,7 +588,10 @@ __global__ __launch_bounds__(kFThreads) void decode_fused_kernel(FusedParams f) 
       const uint8_t* c = PK ? p.pk_c[shared ? 5 : 2] + (blk * ksteps + ks) * 1024 + lane * 16
                             : (shared ? p.sdown_c : p.down_c) + row * dcb + ks * 64 + g * 16;
       if (a < nseg) {
-        dq[a] = load16(c);
+        if constexpr (PK)  // whole lines, read once
+          dq[a] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(c));
+        else
+          dq[a] = load16(c);
         // copied into LDS above
         ds[a] = PK ? sm.dsc[a][(ks >> 2) * 256 + lane * 4 + (ks & 3)]
                    : sm.dsc[a][r16 * dsb + ks * 4 + g];

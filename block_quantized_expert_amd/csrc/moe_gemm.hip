@@ -608,9 +608,9 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
       for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
         for (int i = 0; i < Q; ++i) {
-          if constexpr (kPK)
-            q[mat][rb][i] =
-                load16(pkc[mat] + (uint32_t)(((rb * nks + k) * Q + i) * 1024 + lane * 16));
+          if constexpr (kPK)  // each line is read whole, once: past the caches
+            q[mat][rb][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+                pkc[mat] + (uint32_t)(((rb * nks + k) * Q + i) * 1024 + lane * 16)));
           else
             q[mat][rb][i] = load16(cwave[mat] + (lco + (uint32_t)(16 * rb * cb + F::code_off(k, 0) + 64 * i)));
         }
