@@ -602,18 +602,34 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
   uint32_t u0[2][2], u1[2][2];
   auto load_w = [&](int ks, u32x4 (&q)[2][2][Q], uint32_t (&u)[2][2]) {
     const int k = min(ks, nks - 1);  // past the end: reload the last step
+    if constexpr (kPK) {
+      // MXFP4 packed lines (routed experts, and a shared expert of the same
+      // format) are read whole, once per token tile: past the caches, which
+      // then keep the activation rows and scale words.  Packed fp8 codes
+      // are only ever a shared expert's, read by every token tile of the
+      // batch: cached.
+#pragma unroll
+      for (int mat = 0; mat < 2; ++mat)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int i = 0; i < Q; ++i) {
+            const u32x4* a = reinterpret_cast<const u32x4*>(
+                pkc[mat] + (uint32_t)(((rb * nks + k) * Q + i) * 1024 + lane * 16));
+            if constexpr (WT == MOE_W_MXFP4)
+              q[mat][rb][i] = __builtin_nontemporal_load(a);
+            else
+              q[mat][rb][i] = load16(a);
+          }
+      return;
+    }
 #pragma unroll
     for (int mat = 0; mat < 2; ++mat)
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
-        for (int i = 0; i < Q; ++i) {
-          if constexpr (kPK)  // each line is read whole, once: past the caches
-            q[mat][rb][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-                pkc[mat] + (uint32_t)(((rb * nks + k) * Q + i) * 1024 + lane * 16)));
-          else
-            q[mat][rb][i] = load16(cwave[mat] + (lco + (uint32_t)(16 * rb * cb + F::code_off(k, 0) + 64 * i)));
-        }
+        for (int i = 0; i < Q; ++i)
+          q[mat][rb][i] = load16(cwave[mat] + (lco + (uint32_t)(16 * rb * cb + F::code_off(k, 0) + 64 * i)));
         if (!kSC && !kCh) u[mat][rb] = sbase[mat][ls + 16 * rb * sb + F::scale_off(k, 0)];
       }
   };
