@@ -72,7 +72,7 @@ moe::FfnParams make_params(const moe_layer* L, const void* x, int x_type, int n_
   p.h_hi = reinterpret_cast<__bf16*>(ws + plan.off_h_hi);
   p.h_lo = reinterpret_cast<__bf16*>(ws + plan.off_h_lo);
   p.h_stride = plan.h_stride;
-  p.obuf = reinterpret_cast<float*>(ws + plan.off_obuf);
+  p.obuf = reinterpret_cast<uint32_t*>(ws + plan.off_obuf);
   p.h3 = reinterpret_cast<uint8_t*>(ws + plan.off_h_hi);
   p.h3s = reinterpret_cast<uint8_t*>(ws + plan.off_h3s);
   p.xq = reinterpret_cast<uint8_t*>(ws + plan.off_xq);

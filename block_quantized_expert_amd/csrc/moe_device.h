@@ -93,6 +93,27 @@ __device__ __forceinline__ u32x4 load16(const void* p) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Four floats kept to their top three bytes (sign, exponent and 15 stored
+// mantissa bits, rounded to nearest; infinities and NaNs kept) and packed
+// little-endian into three 32-bit words at w (4-byte aligned): the per-slot
+// expert outputs between the down projection and the combine, 2^-16 of
+// each value.
+__device__ __forceinline__ uint32_t f24_bits(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return ((u & 0x7F800000u) == 0x7F800000u ? u : u + 0x80u) >> 8;
+}
+__device__ __forceinline__ void store_f24x4(uint32_t* w, f32x4 v) {
+  const uint32_t a = f24_bits(v[0]), b = f24_bits(v[1]), c = f24_bits(v[2]), d = f24_bits(v[3]);
+  w[0] = a | (b << 24);
+  w[1] = (b >> 8) | (c << 16);
+  w[2] = (c >> 16) | (d << 8);
+}
+__device__ __forceinline__ f32x4 load_f24x4(const uint32_t* w) {
+  const uint32_t w0 = w[0], w1 = w[1], w2 = w[2];
+  return f32x4{__uint_as_float(w0 << 8), __uint_as_float(((w0 >> 24) | (w1 << 8)) << 8),
+               __uint_as_float(((w1 >> 16) | (w2 << 16)) << 8), __uint_as_float(w2 & 0xFFFFFF00u)};
+}
+
 // v = hi + lo with hi = bf16(v) and lo = bf16(v - hi), both round to
 // nearest even; hi + lo carries 16 significant bits of v.
 __device__ __forceinline__ void split_bf16(float v, __bf16& hi, __bf16& lo) {

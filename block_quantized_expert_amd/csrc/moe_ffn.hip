@@ -608,24 +608,22 @@ __global__ __launch_bounds__(kThreads) void gate_up_decode_kernel(FfnParams p, i
 
 // y[t] = o_shared[t] + sum_i w[t*k + i] * o[inv_perm[t*k + i]], in that
 // fixed order, leaving out slots dropped by tail pruning or by the lazy
-// skip; four features per thread.
+// skip; four features (three words of 24-bit floats per slot) per thread.
 __global__ __launch_bounds__(256) void combine_kernel(FfnParams p) {
   const int h4 = p.hidden / 4;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (int64_t)p.n_tokens * h4) return;
   const int64_t t = i / h4;
   const int64_t q = (i - t * h4) * 4;
+  // slot s's four features at word (s * hidden + q) / 4 * 3
+  auto slot_out = [&](int64_t s) { return load_f24x4(p.obuf + (s * p.hidden + q) / 4 * 3); };
   f32x4 acc = f32x4{0, 0, 0, 0};
-  if (p.has_shared)
-    acc = *reinterpret_cast<const f32x4*>(p.obuf +
-                                          ((int64_t)p.n_tokens * p.top_k + t) * p.hidden + q);
+  if (p.has_shared) acc = slot_out((int64_t)p.n_tokens * p.top_k + t);
   for (int j = 0; j < p.top_k; ++j) {
     const int pp = p.inv_perm[t * p.top_k + j];
     // a slot the lazy skip drops contributes nothing
     const bool live = pp >= 0 && (p.lazy_tau == 0.0f || __uint_as_float(p.gmax[pp]) >= p.lazy_tau);
-    if (live)
-      acc += p.topk_w[t * p.top_k + j] *
-             *reinterpret_cast<const f32x4*>(p.obuf + (int64_t)pp * p.hidden + q);
+    if (live) acc += p.topk_w[t * p.top_k + j] * slot_out(pp);
   }
   *reinterpret_cast<f32x4*>(p.y + t * p.hidden + q) = acc;
 }

@@ -1094,8 +1094,7 @@ __device__ __forceinline__ void down_item(const FfnParams& p, const GItem& it, c
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         if (rb < nrb)
-          *reinterpret_cast<f32x4*>(p.obuf + slot * p.hidden + wrow0 + 16 * rb + 4 * g) =
-              acc[rb][tb];
+          store_f24x4(p.obuf + (slot * p.hidden + wrow0 + 16 * rb + 4 * g) / 4 * 3, acc[rb][tb]);
       }
     }
   }
@@ -1398,8 +1397,7 @@ __device__ __forceinline__ void down3_item(const FfnParams& p, const GItem& it, 
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         if (rb < nrb)
-          *reinterpret_cast<f32x4*>(p.obuf + slot * p.hidden + wrow0 + 16 * rb + 4 * g) =
-              acc[rb][tb];
+          store_f24x4(p.obuf + (slot * p.hidden + wrow0 + 16 * rb + 4 * g) / 4 * 3, acc[rb][tb]);
       }
     }
   }

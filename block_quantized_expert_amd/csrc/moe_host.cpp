@@ -146,7 +146,8 @@ moe_status plan_ffn(const moe_layer* layer, int n_tokens, FfnPlan* plan) {
   if (layer->has_shared && layer->shared_inter > hs) hs = layer->shared_inter;
   plan->h_stride = hs;
   const size_t h_bytes = align_up((size_t)(plan->slots * hs) * 2u, 256);
-  const size_t o_bytes = align_up((size_t)(plan->slots * layer->hidden) * 4u, 256);
+  // per-slot outputs as 24-bit floats (three bytes a feature)
+  const size_t o_bytes = align_up((size_t)(plan->slots * layer->hidden) * 3u, 256);
   const size_t xq_bytes = align_up((size_t)n * layer->hidden * 2u, 256);
   const size_t xs_bytes = align_up((size_t)n * (layer->hidden / 16), 256);
   // h as three E4M3 parts + 4 scale bytes per 32 fits in the bf16 pair's

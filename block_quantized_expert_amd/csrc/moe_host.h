@@ -13,10 +13,10 @@ namespace moe {
 // Byte layout of the moe_ffn workspace.
 //   h_hi, h_lo : bf16 [slots][h_stride]   SwiGLU output split into a bf16
 //                                         high part and a bf16 low part
-//   obuf       : fp32 [slots][hidden]     expert outputs before the routing
-//                                         weight (used when the batch is too
-//                                         large for the single-pass down +
-//                                         combine)
+//   obuf       : [slots][hidden] x 3 B    expert outputs before the routing
+//                                         weight, 24-bit floats (used when the
+//                                         batch is too large for the
+//                                         single-pass down + combine)
 //   xq         : u8 [n_tokens][2*hidden]  bf16 activations as E4M3 hi and lo
 //                                         parts (grouped-GEMM gate/up)
 //   xs         : u8 [n_tokens][hidden/16] their scale bytes

@@ -42,7 +42,9 @@ struct FfnParams {
   // s-8 and a zero byte)
   uint8_t* h3;
   uint8_t* h3s;
-  float* obuf;  // [slots][hidden] per-slot outputs (the combine weights them)
+  // [slots][hidden / 4][3 words] per-slot outputs, four features as 24-bit
+  // floats in three words (store_f24x4); the combine weights them
+  uint32_t* obuf;
   float* y;     // [n_tokens][hidden]
   // gate-first lazy skip: a routed slot whose gate output has
   // max_j |SiLU(g_j)| < lazy_tau contributes nothing (lazy_tau 0: off).

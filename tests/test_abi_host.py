@@ -74,7 +74,7 @@ def test_ffn_workspace_bytes():
     n = 4096
     slots = n * 6 + n
     h = -(-slots * 2048 * 2 // 256) * 256
-    o = -(-slots * 4096 * 4 // 256) * 256
+    o = -(-slots * 4096 * 3 // 256) * 256  # per-slot outputs, 24-bit floats
     xq = n * 4096 * 2          # activations as two E4M3 parts
     xs = n * 4096 // 16        # their scale bytes
     gmax = n * 6 * 4           # lazy skip: each routed slot's largest |SiLU(g)|
@@ -85,7 +85,7 @@ def test_ffn_workspace_bytes():
     n = 16
     slots = n * 6 + n
     h = -(-slots * 2048 * 2 // 256) * 256
-    o = -(-slots * 4096 * 4 // 256) * 256
+    o = -(-slots * 4096 * 3 // 256) * 256  # per-slot outputs, 24-bit floats
     xs = -(-n * 4096 // 16 // 256) * 256
     gmax = -(-n * 6 * 4 // 256) * 256
     gbuf = n * 6 * 2048 * 4
