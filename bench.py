@@ -107,10 +107,10 @@ KERNEL_TRAFFIC_KIB = {  # (workload, packed copy used): (FETCH_SIZE, WRITE_SIZE)
     ("decode32", False): (475411.1, 5502.4),    # gemm_gate_up_kernel<0, 112, true, true, false, false>
     ("prefill512", False): (1180630.5, 27385.2),
     ("hash4096", False): (2131057.8, 176253.2),
-    ("decode1", True): (46193.2, 82.2),         # decode_fused_kernel<8, true>
-    ("decode32", True): (473952.6, 3448.8),     # gemm_gate_up_kernel<0, 112, true, true, false, true>
-    ("prefill512", True): (1155345.0, 24776.9),
-    ("hash4096", True): (1399765.1, 160707.3),
+    ("decode1", True): (46192.6, 82.2),         # decode_fused_kernel<8, true>
+    ("decode32", True): (479001.2, 3448.9),     # gemm_gate_up_kernel<0, 112, true, true, false, true>
+    ("prefill512", True): (1168735.0, 24634.7),
+    ("hash4096", True): (1324066.2, 159491.2),
 }
 
 
