@@ -37,7 +37,9 @@ Every record holds:
   on the host cores.
 The line also carries ``hbm_read_ceiling``: the rate of a plain streaming
 read over 4 GiB (moe_stream_read), the measured ceiling beside the 8 TB/s
-published figure.
+published figure; and ``mfma_issue_ceiling``: the rate at which independent
+scaled matrix instructions issue (moe_mfma_rate), for the instruction the
+grouped GEMMs use and for the 32x32x64 shape with E2M1 x E2M3 operands.
 """
 
 from __future__ import annotations
@@ -555,6 +557,41 @@ def read_ceiling(dev, gib=4, reps=5):
             "frac_of_published": float(np.median(rates)) / HBM_PEAK_GBPS}
 
 
+def mfma_ceiling(dev, iters=8000, reps=5):
+    """TFLOP/s that moe_mfma_rate issues (median and best of `reps` runs of
+    a few milliseconds after one warm-up) for the instruction the grouped
+    GEMMs use (16x16x128, E2M1 weights x E4M3 activations) and for the
+    32x32x64 shape with E2M1 x E2M3 operands."""
+    import numpy as np
+    import torch
+
+    from block_quantized_expert_amd import binding as B
+
+    L = B.lib()
+    n = L.moe_mfma_rate_out_floats()
+    out = torch.empty(max(int(n), 1), dtype=torch.float32, device=dev)
+    s = torch.cuda.current_stream()
+    waves = n // 64
+    res = {}
+    for label, shape, fa, fb in (("16x16x128 E2M1 x E4M3 (the kernels' instruction)", 16, 4, 0),
+                                 ("32x32x64 E2M1 x E2M3", 32, 4, 2)):
+        args = (shape, fa, fb, iters, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(s.cuda_stream))
+        if L.moe_mfma_rate(*args):
+            raise RuntimeError("moe_mfma_rate failed")
+        flops = waves * iters * (8 * 2 * 16 * 16 * 128 if shape == 16 else 4 * 2 * 32 * 32 * 64)
+        rates = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(s)
+            L.moe_mfma_rate(*args)
+            b.record(s)
+            torch.cuda.synchronize()
+            rates.append(flops / (a.elapsed_time(b) / 1e3) / 1e12)
+        res[label] = {"median": float(np.median(rates)), "max": float(max(rates))}
+    return {"kernel": "moe_mfma_rate (independent scaled MFMAs, operands in registers)",
+            "TFLOPs": res, "fp8_peak_TFLOPs": 5000.0}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -656,6 +693,7 @@ def main():
         result["cpu_baseline"] = rec["cpu_baseline"]
     if not args.no_ceiling:
         result["hbm_read_ceiling"] = read_ceiling(dev)
+        result["mfma_issue_ceiling"] = mfma_ceiling(dev)
     if configs:
         result["configs"] = configs
     print(json.dumps(result), flush=True)

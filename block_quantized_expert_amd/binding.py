@@ -28,7 +28,7 @@ EXPORTED = ["moe_route", "moe_route_hash", "moe_route_group", "moe_group_workspa
             "moe_ffn_down", "moe_ffn_forward_timed", "moe_forward_workspace_bytes",
             "moe_forward_single_kernel", "moe_forward_workspace_init", "moe_forward",
             "moe_forward_timed", "moe_forward_noalloc", "moe_status_string",
-            "moe_stream_read", "moe_route_ex", "moe_route_group_ex", "moe_ffn_forward_ex",
+            "moe_stream_read", "moe_mfma_rate", "moe_mfma_rate_out_floats", "moe_route_ex", "moe_route_group_ex", "moe_ffn_forward_ex",
             "moe_forward_ex", "moe_packed_experts_bytes", "moe_pack_experts"]
 
 WEIGHT_TYPES = {"mxfp4": MOE_W_MXFP4, "fp8_e4m3_b128": MOE_W_FP8E4M3_B128}
@@ -127,6 +127,10 @@ def lib() -> ctypes.CDLL:
                      "moe_forward_ex"):
             getattr(L, name).restype = ctypes.c_int
         L.moe_stream_read.argtypes = [P, S, P, P]
+        L.moe_mfma_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P]
+        L.moe_mfma_rate.restype = ctypes.c_int
+        L.moe_mfma_rate_out_floats.argtypes = []
+        L.moe_mfma_rate_out_floats.restype = S
         L.moe_packed_experts_bytes.argtypes = [ctypes.POINTER(MoeLayer)]
         L.moe_packed_experts_bytes.restype = S
         L.moe_pack_experts.argtypes = [ctypes.POINTER(MoeLayer), P, S, P]

@@ -362,3 +362,14 @@ def test_pack_experts_rejects_bad_arguments():
     assert lib.moe_ffn_workspace_bytes(ctypes.byref(L), 8) == 0
     fp8.packed_experts = 0x100000
     assert lib.moe_ffn_workspace_bytes(ctypes.byref(fp8), 8) == 0
+
+
+def test_mfma_rate_rejects_bad_arguments():
+    """moe_mfma_rate checks its arguments before touching the device."""
+    L = B.lib()
+    invalid = 1  # MOE_ERR_INVALID
+    assert L.moe_mfma_rate(8, 0, 0, 1, None, None) == invalid       # no such shape
+    assert L.moe_mfma_rate(16, 1, 0, 1, None, None) == invalid      # E5M2 is not offered
+    assert L.moe_mfma_rate(32, 0, 3, 1, None, None) == invalid
+    assert L.moe_mfma_rate(16, 0, 0, 0, None, None) == invalid      # no rounds
+    assert L.moe_mfma_rate(16, 4, 0, 1, None, None) == invalid      # null output
