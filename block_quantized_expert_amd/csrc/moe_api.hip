@@ -82,6 +82,11 @@ moe::FfnParams make_params(const moe_layer* L, const void* x, int x_type, int n_
   p.gmax = reinterpret_cast<uint32_t*>(ws + plan.off_gmax);
   p.gbuf = reinterpret_cast<float*>(ws + plan.off_gbuf);
   p.qctr = reinterpret_cast<uint32_t*>(ws + plan.off_qctr);
+  p.n_slots = plan.slots;
+  if (plan.off_h6s > plan.off_h6) {
+    p.h6 = reinterpret_cast<uint8_t*>(ws + plan.off_h6);
+    p.h6s = reinterpret_cast<uint32_t*>(ws + plan.off_h6s);
+  }
   moe::PackPlan pk;
   if (L->packed_experts != nullptr && moe::plan_pack(L, &pk) == MOE_OK) {
     const uint8_t* base = static_cast<const uint8_t*>(L->packed_experts);

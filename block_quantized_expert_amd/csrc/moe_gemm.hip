@@ -87,6 +87,12 @@ static_assert(kTokScaleOff + 2 * kTokScaleBytes <= kGemmLds, "gate/up LDS");
 // token tiles (112 rows x 2 buffers)
 constexpr int kTokChunkOff = 2 * 112 * 256;
 static_assert(kTokChunkOff + 2 * 128 * 32 <= kGemmLds, "gate/up LDS");
+// gate/up epilogue for E2M3 parts: each wavefront's h values staged as
+// [112 tokens][36 floats] (32 rows, the stride padded so that a row of 16
+// tokens falls on distinct banks)
+constexpr int kH6Row = 36;
+constexpr int kH6Wave = 112 * kH6Row * 4;
+static_assert(kGWaves * kH6Wave <= kGemmLds, "gate/up LDS");
 // dynamic LDS + the static item prefix and scan words of a workgroup (plus
 // alignment): kGPerCU workgroups in the 160 KiB of a CU
 static_assert(kGemmLds + (kSegMax + 1 + kGWaves) * 4 + 64 <= 160 * 1024 / kGPerCU,
@@ -444,11 +450,17 @@ __device__ __forceinline__ i32x8 weight_operand(const u32x4 (&q)[Fmt<WT>::Q]) {
                  (int)q[1][0], (int)q[1][1], (int)q[1][2], (int)q[1][3]};
 }
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x32 __attribute__((ext_vector_type(32)));
+typedef uint32_t u32x6 __attribute__((ext_vector_type(6)));
+
 // LDS-typed views (32-bit addresses) of the shared-memory tiles.
 using lds_cptr = const __attribute__((address_space(3))) char*;
 typedef const __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef const __attribute__((address_space(3))) uint16_t lds_u16;
 typedef const __attribute__((address_space(3))) uint32_t lds_u32;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef const __attribute__((address_space(3))) u32x2 lds_u32x2;
 __device__ __forceinline__ lds_cptr to_lds(const char* p) {
   return (lds_cptr)p;  // an address-space cast: the tiles live in LDS
 }
@@ -505,7 +517,8 @@ __device__ __forceinline__ uint32_t split_e4m3x3(const float (&v)[2][4], float m
 // that a step's operand reads and MFMAs form one branch-free block.
 // LAZY: the gate-first lazy skip is on (its gate maxima are merged into
 // gmax); a separate instantiation, so the plain kernels keep their registers.
-template <int WT, int TT, int NBT, bool SC, bool O32, bool LAZY, bool PK, typename Take>
+template <int WT, int TT, int NBT, bool SC, bool O32, bool LAZY, bool PK, bool H6,
+          typename Take>
 __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it, char* smem,
                                              int wave, int lane, Take&& take) {
   using F = Fmt<WT>;
@@ -524,6 +537,9 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
   // lane's scale bytes of four steps one word (as the chunks below, without
   // the byte gathering)
   constexpr bool kPK = PK && SC;
+  // H6 (packed MXFP4 batches with many tokens per expert): the down runs
+  // on E2M3 parts of h (h6)
+  constexpr bool kH6 = kPK && H6 && WT == MOE_W_MXFP4;
   constexpr bool kSC = SC && WT == MOE_W_MXFP4 && NBT <= 5 && !kPK;
   constexpr bool kCh = SC && (WT == MOE_W_MXFP4 ? NBT >= 6 || kPK : true);
   constexpr int kLoads = (kSC || kCh) ? 4 * Q : 4 * (Q + 1);  // vector loads of one step's weights
@@ -858,6 +874,76 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
       if (live && g == 0 && n < it.m) atomicMax(p.gmax + it.slot0 + n, __float_as_uint(mx));
     }
   }
+  if constexpr (kH6) {
+    // h as three E2M3 parts for the 32x32x64 down (packed MXFP4 layers):
+    // the wavefront's 32 rows of a token are one block of the down's
+    // reduction, so each lane first gathers a token's 32 values (through
+    // LDS, the token tiles being free once every wavefront is past its last
+    // step) and then converts them with the block conversion instructions:
+    // part q under the scale 2^(e_q - 2) of the largest magnitude 2^e_q of
+    // what the parts before left (2^(e_q - 1) when that would exceed 7.5),
+    // so each part uses the whole E2M3 range.
+    __syncthreads();
+    float* const stage = reinterpret_cast<float*>(smem + wave * kH6Wave);  // [TT][kH6Row]
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        f32x4 hv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float gv = acc[0][rb][tb][r];
+          hv[r] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * acc[1][rb][tb][r];
+        }
+        *reinterpret_cast<f32x4*>(stage + (tb * 16 + r16) * kH6Row + rb * 16 + 4 * g) = hv;
+      }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // this wavefront's LDS writes are done (lgkmcnt 0)
+    __builtin_amdgcn_wave_barrier();
+    const int kb = it.row0 / 32 + wave;  // the down's 32-value block of these rows
+    if (live) {
+      for (int t = lane; t < it.m; t += kWave) {
+        float f[32];
+        const float* src = stage + t * kH6Row;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const f32x4 v4 = *reinterpret_cast<const f32x4*>(src + 4 * i);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) f[4 * i + j] = v4[j];
+        }
+        const int64_t slot = it.slot0 + t;
+        uint2* dst = reinterpret_cast<uint2*>(p.h6 + ((int64_t)kb * p.n_slots + slot) * 72);
+        uint32_t sw = 0;
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+          float mag = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 32; ++i) mag = fmaxf(mag, fabsf(f[i]));
+          // biased exponent of the scale: e - 2, or e - 1 above 7.5 * 2^(e-2)
+          int sb = (int)((__float_as_uint(mag) >> 23) & 0xFF) - 2;
+          if (mag > 7.5f * __uint_as_float((uint32_t)max(sb, 1) << 23)) sb += 1;
+          sb = min(max(sb, 1), 254);
+          const float sc = __uint_as_float((uint32_t)sb << 23);
+          // the conversion interleaves its two sources: value 2j from the
+          // first, 2j+1 from the second
+          f32x16 ev, od;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            ev[j] = f[2 * j];
+            od[j] = f[2 * j + 1];
+          }
+          const u32x6 w = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, sc);
+          const f32x32 back = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(w, sc);
+#pragma unroll
+          for (int i = 0; i < 32; ++i) f[i] -= back[i];
+#pragma unroll
+          for (int i = 0; i < 3; ++i) dst[3 * q + i] = uint2{w[2 * i], w[2 * i + 1]};
+          sw |= (uint32_t)sb << (8 * q);
+        }
+        p.h6s[(int64_t)kb * p.n_slots + slot] = sw;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int tb = 0; tb < TB; ++tb) {
     float v[2][4];
@@ -893,7 +979,7 @@ __device__ __forceinline__ void gate_up_item(const FfnParams& p, const GItem& it
   }
 }
 
-template <int WT, int TT, bool SC, bool O32, bool LAZY, bool PK>
+template <int WT, int TT, bool SC, bool O32, bool LAZY, bool PK, bool H6>
 __global__ __launch_bounds__(kGThreads, kGPerCU) void gemm_gate_up_kernel(FfnParams p, int seg_lo,
                                                                      int seg_hi,
                                                                      uint32_t* qctr) {
@@ -906,7 +992,8 @@ __global__ __launch_bounds__(kGThreads, kGPerCU) void gemm_gate_up_kernel(FfnPar
   run_queue(ItemQueue{qctr, total, qctr != nullptr}, &s_q, [&](int item, auto&& take) {
     const GItem it = find_item<TT, kGuRows, false>(p, seg_lo, seg_hi, s_pref, item);
     dispatch_nbt<TT / 16>((it.m + 15) >> 4, [&](auto nb) {
-      gate_up_item<WT, TT, decltype(nb)::value, SC, O32, LAZY, PK>(p, it, smem, wave, lane, take);
+      gate_up_item<WT, TT, decltype(nb)::value, SC, O32, LAZY, PK, H6>(p, it, smem, wave, lane,
+                                                                    take);
     });
   });
 }
@@ -1420,6 +1507,241 @@ __global__ __launch_bounds__(kGThreads, kGPerCU) void gemm_down3_kernel(FfnParam
   });
 }
 
+// ------------------------------------------------- down on E2M3 parts of h
+//
+// With the packed copy, the MXFP4 down multiplies h as three E2M3 parts
+// (h6, written by the gate/up epilogue) on v_mfma_scale_f32_32x32x64_f8f6f4,
+// which issues E2M1 x E2M3 at about twice the rate of any 16x16x128 form:
+// 3 x 1/2 of the matrix time of one E4M3 product instead of 3 x 1.  A
+// workgroup owns 256 hidden rows and up to 64 tokens (two 32-token blocks);
+// wavefront w owns rows 64w .. 64w+63 (two 32-row blocks).  Per step of 128
+// inputs a 32-row block is two instructions of 64 inputs per token block and
+// part.
+//  - A (weights): lane l holds row l % 32 and inputs 32 (l / 32) .. +31 of
+//    the 64, i.e. the 16 bytes of lane 16 g + (l % 16) of the packed copy's
+//    16-row block (l % 32) / 16, g = l / 32 (first 64 inputs) or 2 + l / 32;
+//    its scale word is that lane's too.
+//  - B (h): lane l holds token l % 32 and the same 32 inputs: 24 bytes of
+//    one part; the step's four blocks of 32 inputs are copied into LDS as
+//    planes [64 tokens][72 bytes] (a token's three parts), whose 72-byte
+//    stride puts the 32 tokens of a read on distinct banks.  The LDS copy
+//    instruction writes 16 bytes per lane (its 12-byte form also advances
+//    16 bytes per lane), so the 4.5 KiB of a plane take five of them and the
+//    plane is padded to 5 KiB.
+//  - D: lane l holds token l % 32 and rows 8 j + 4 (l / 32) + 0..3.
+// one block of 32 inputs: 64 tokens x 72 bytes, padded to whole copies of
+// 1 KiB (16 bytes per lane)
+constexpr int kD6Plane = (kD3Tok * 72 + 1023) / 1024 * 1024;
+constexpr int kD6Buf = 4 * kD6Plane;             // a step (20 KiB)
+constexpr int kD6ScOff = 2 * kD6Buf;
+constexpr int kD6ScBuf = 4 * kD3Tok * 4;          // a step's scale words
+constexpr int kD6Lds = kD6ScOff + 2 * kD6ScBuf;
+static_assert(kD6Lds <= kGemmLds, "down LDS");
+
+template <int SB>
+__device__ __forceinline__ f32x16 mfma32_e2m1_e2m3(i32x8 a, i32x8 b, f32x16 c, uint32_t sa,
+                                                    uint32_t sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 2, 0, (int)sa, SB, (int)sb);
+}
+
+// NB = 32-token blocks of the tile (ceil(m / 32)).
+template <int NB, typename Take>
+__device__ __forceinline__ void down6_item(const FfnParams& p, const GItem& it, char* smem,
+                                           int wave, int lane, Take&& take) {
+  constexpr int RB = 2;           // 32-row blocks per wavefront
+  constexpr int kLoads = 2 * RB;  // vector loads of one step's weights
+  const int hi = lane >> 5, l32 = lane & 31;
+  const int b16 = (lane >> 4) & 1, r16 = lane & 15;
+  const bool shared = it.seg == p.n_experts;
+  const int kdim = shared ? p.shared_inter : p.inter;
+  const int nks = kdim / 128;
+  const int wrow0 = it.row0 + 64 * wave;
+  // 16-row blocks of this wavefront inside the matrix (the last tile may be
+  // short: blocks past the end reuse block 0's codes and are not stored)
+  const int nrb16 = uniform(max(0, min(4, (p.hidden - wrow0) / 16)));
+  const int64_t blk0 = ((shared ? 0 : (int64_t)it.seg * p.hidden) + (nrb16 > 0 ? wrow0 : 0)) / 16;
+  const uint8_t* pkc = p.pk_c[shared ? 5 : 2] + blk0 * nks * 1024;
+  const uint8_t* pks = p.pk_s[shared ? 5 : 2] + blk0 * (nks / 4) * 256;
+  // the lane's code unit (step 0) and scale word (chunk 0) for 32-row block
+  // rb and input half s of a step
+  uint32_t aoff[RB][2], soff[RB][2];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int bb = 2 * rb + b16;
+    const int blk = bb < nrb16 ? bb : 0;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int unit = 16 * (hi + 2 * s) + r16;
+      aoff[rb][s] = (uint32_t)(blk * nks * 1024 + unit * 16);
+      soff[rb][s] = (uint32_t)(blk * (nks / 4) * 256 + unit * 4);
+    }
+  }
+  auto lds = [](char* q) { return (__attribute__((address_space(3))) void*)q; };
+  // step ks into buffer b: wavefront w copies block 4 ks + w of the tile's
+  // m tokens (72 contiguous bytes each in h6, 16 bytes per lane and
+  // instruction, whole KiB into the padded plane) and their scale words.
+  // A lane whose 16 bytes start past the m tokens re-reads the tile's first
+  // 16 (its LDS bytes only feed token columns never stored); the lane that
+  // straddles the end reads up to 8 bytes past it, which h6 always holds
+  // (the next slot's record, or the 16 bytes of padding after the last).
+  // No lane branches.
+  auto copy_h = [&](int ks, int b) {
+    const int64_t kb = 4 * ks + wave;
+    const uint8_t* src = p.h6 + (kb * p.n_slots + it.slot0) * 72;
+    char* dst = smem + b * kD6Buf + wave * kD6Plane;
+    const int nbytes = it.m * 72;
+#pragma unroll
+    for (int c = 0; c < kD6Plane / 1024; ++c) {
+      const int o = 1024 * c + 16 * lane;
+      __builtin_amdgcn_global_load_lds(src + (o < nbytes ? o : 0), lds(dst + 1024 * c), 16, 0, 0);
+    }
+    __builtin_amdgcn_global_load_lds(p.h6s + kb * p.n_slots + it.slot0 + (lane < it.m ? lane : 0),
+                                     lds(smem + kD6ScOff + b * kD6ScBuf + wave * 256), 4, 0, 0);
+  };
+  u32x4 q0[RB][2], q1[RB][2];
+  auto load_w = [&](int ks, u32x4 (&q)[RB][2]) {
+    const uint32_t k = (uint32_t)min(ks, nks - 1);  // past the end: reload the last step
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) q[rb][s] = load16(pkc + (aoff[rb][s] + k * 1024));
+  };
+  uint32_t sp[RB][2], spn[RB][2];
+  auto load_sc = [&](int c) {
+    const uint32_t cc = (uint32_t)min(c, nks / 4 - 1);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        spn[rb][s] = *reinterpret_cast<const uint32_t*>(pks + (soff[rb][s] + cc * 256));
+  };
+
+  f32x16 acc[RB][NB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int tb = 0; tb < NB; ++tb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[rb][tb][e] = 0.0f;
+
+  auto step_mma = [&](int ks) {
+    const char* cur = smem + (ks & 1) * kD6Buf;
+    const char* cts = smem + kD6ScOff + (ks & 1) * kD6ScBuf;
+    i32x8 a[RB][2];
+    uint32_t sa[RB][2];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        a[rb][s] = i32x8{(int)q0[rb][s][0], (int)q0[rb][s][1], (int)q0[rb][s][2],
+                         (int)q0[rb][s][3], 0, 0, 0, 0};
+        sa[rb][s] = sp[rb][s] >> (8 * (ks & 3));
+      }
+    // operand u = 3 (2 tb + s) + q: token 32 tb + l32, block 2 s + hi of the
+    // step, part q, at plane (2 s + hi) + token * 72 + q * 24
+    lds_cptr pb = to_lds(cur) + hi * kD6Plane + l32 * 72;
+    opaque(pb);
+    lds_cptr ps = to_lds(cts) + hi * 256 + l32 * 4;
+    opaque(ps);
+    constexpr int kOps = 6 * NB;
+    constexpr int kAhead = 2;
+    i32x8 bop[kAhead + 1];
+    uint32_t sbt[2];
+    auto read_op = [&](int u) {
+      const int q = u % 3, s = (u / 3) & 1, tb = u / 6;
+      const int off = 2 * s * kD6Plane + tb * 32 * 72 + q * 24;
+      const u32x2 w0 = *reinterpret_cast<const lds_u32x2*>(pb + off);
+      const u32x2 w1 = *reinterpret_cast<const lds_u32x2*>(pb + off + 8);
+      const u32x2 w2 = *reinterpret_cast<const lds_u32x2*>(pb + off + 16);
+      bop[u % (kAhead + 1)] = i32x8{(int)w0.x, (int)w0.y, (int)w1.x, (int)w1.y,
+                                    (int)w2.x, (int)w2.y, 0, 0};
+      if (q == 0) sbt[(u / 3) & 1] = *reinterpret_cast<const lds_u32*>(ps + 2 * s * 256 + tb * 128);
+    };
+#pragma unroll
+    for (int u = 0; u < kAhead && u < kOps; ++u) read_op(u);
+#pragma unroll
+    for (int u = 0; u < kOps; ++u) {
+      if (u + kAhead < kOps) read_op(u + kAhead);
+      const int q = u % 3, s = (u / 3) & 1, tb = u / 6;
+      const i32x8& b = bop[u % (kAhead + 1)];
+      const uint32_t sb = sbt[(u / 3) & 1];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        if (q == 0)
+          acc[rb][tb] = mfma32_e2m1_e2m3<0>(a[rb][s], b, acc[rb][tb], sa[rb][s], sb);
+        else if (q == 1)
+          acc[rb][tb] = mfma32_e2m1_e2m3<1>(a[rb][s], b, acc[rb][tb], sa[rb][s], sb);
+        else
+          acc[rb][tb] = mfma32_e2m1_e2m3<2>(a[rb][s], b, acc[rb][tb], sa[rb][s], sb);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  load_sc(0);
+  load_w(0, q0);
+  copy_h(0, 0);
+  wait_vm<0>();
+  __syncthreads();
+  for (int ks = 0; ks < nks; ++ks) {
+    if ((ks & 3) == 0) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) sp[rb][s] = spn[rb][s];
+      load_sc((ks >> 2) + 1);
+    }
+    if (ks + 1 < nks) copy_h(ks + 1, (ks + 1) & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(ks + 1, q1);
+    __builtin_amdgcn_sched_barrier(0);
+    step_mma(ks);
+    step_barrier<kLoads>();  // the copies have landed (the weights in flight)
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) q0[rb][s] = q1[rb][s];
+  }
+  wait_vm<0>();
+  take();  // the next item's ticket, in flight during the epilogue
+
+  // the per-slot outputs, unweighted (the combine applies the routing
+  // weights): rows 8 j + 4 hi .. +3 of each 32-row block
+#pragma unroll
+  for (int tb = 0; tb < NB; ++tb) {
+    const int n = tb * 32 + l32;
+    if (n < it.m) {
+      const int64_t slot = it.slot0 + n;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int row = 32 * rb + 8 * j + 4 * hi;
+          if (row / 16 < nrb16)
+            store_f24x4(p.obuf + (slot * p.hidden + wrow0 + row) / 4 * 3,
+                        f32x4{acc[rb][tb][4 * j], acc[rb][tb][4 * j + 1], acc[rb][tb][4 * j + 2],
+                              acc[rb][tb][4 * j + 3]});
+        }
+    }
+  }
+}
+
+__global__ __launch_bounds__(kGThreads, kGPerCU) void gemm_down6_kernel(FfnParams p, int seg_lo,
+                                                                   int seg_hi, uint32_t* qctr) {
+  extern __shared__ __align__(16) char smem[];
+  __shared__ int s_pref[kSegMax + 1];
+  __shared__ int s_tmp[kGThreads / kWave];
+  __shared__ QueueLds s_q;
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int total = item_prefix<kD3Tok, kDnRows, true>(p, seg_lo, seg_hi, s_pref, s_tmp);
+  run_queue(ItemQueue{qctr, total, qctr != nullptr}, &s_q, [&](int item, auto&& take) {
+    const GItem it = find_item<kD3Tok, kDnRows, true>(p, seg_lo, seg_hi, s_pref, item);
+    dispatch_nbt<2>((it.m + 31) >> 5, [&](auto nb) {
+      down6_item<decltype(nb)::value>(p, it, smem, wave, lane, take);
+    });
+  });
+}
+
 template <typename... Params, typename... Args>
 hipError_t launch(void (*kernel)(Params...), dim3 grid, dim3 block, size_t lds,
                   hipStream_t stream, hipEvent_t start, hipEvent_t stop, Args... args) {
@@ -1473,23 +1795,34 @@ int grid_for(int64_t items) {
   return (int)(items < kGemmGrid ? (items > 0 ? items : 1) : kGemmGrid);
 }
 
-template <int WT, int TT, bool SC, bool O32, bool LAZY, bool PK>
+template <int WT, int TT, bool SC, bool O32, bool LAZY, bool PK, bool H6>
 hipError_t gate_up_range_as(const FfnParams& p, int seg_lo, int seg_hi, hipStream_t stream,
                             hipEvent_t start, hipEvent_t stop) {
-  static const hipError_t attr = allow_lds(gemm_gate_up_kernel<WT, TT, SC, O32, LAZY, PK>);
+  static const hipError_t attr = allow_lds(gemm_gate_up_kernel<WT, TT, SC, O32, LAZY, PK, H6>);
   if (attr != hipSuccess) return attr;
   const int grid = grid_for(items_bound(p, seg_lo, seg_hi, TT, kGuRows, false));
-  return launch(gemm_gate_up_kernel<WT, TT, SC, O32, LAZY, PK>, dim3(grid), dim3(kGThreads),
+  return launch(gemm_gate_up_kernel<WT, TT, SC, O32, LAZY, PK, H6>, dim3(grid), dim3(kGThreads),
                 (size_t)kGemmLds, stream, start, stop, p, seg_lo, seg_hi,
                 queue_counters(p, seg_lo, false));
 }
 
-template <int WT, int TT, bool SC, bool O32, bool PK = false>
+template <int WT, int TT, bool SC, bool O32, bool PK = false, bool H6 = false>
 hipError_t gate_up_range(const FfnParams& p, int seg_lo, int seg_hi, hipStream_t stream,
                          hipEvent_t start, hipEvent_t stop) {
   if (p.lazy_tau > 0.0f)
-    return gate_up_range_as<WT, TT, SC, O32, true, PK>(p, seg_lo, seg_hi, stream, start, stop);
-  return gate_up_range_as<WT, TT, SC, O32, false, PK>(p, seg_lo, seg_hi, stream, start, stop);
+    return gate_up_range_as<WT, TT, SC, O32, true, PK, H6>(p, seg_lo, seg_hi, stream, start, stop);
+  return gate_up_range_as<WT, TT, SC, O32, false, PK, H6>(p, seg_lo, seg_hi, stream, start, stop);
+}
+
+hipError_t down6_range(const FfnParams& p, int seg_lo, int seg_hi, hipStream_t stream,
+                       hipEvent_t start, hipEvent_t stop) {
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_down6_kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kD6Lds);
+  if (attr != hipSuccess) return attr;
+  const int grid = grid_for(items_bound(p, seg_lo, seg_hi, kD3Tok, kDnRows, true));
+  return launch(gemm_down6_kernel, dim3(grid), dim3(kGThreads), (size_t)kD6Lds, stream, start,
+                stop, p, seg_lo, seg_hi, queue_counters(p, seg_lo, true));
 }
 
 template <int WT, bool SC, bool PK = false>
@@ -1534,6 +1867,26 @@ hipError_t by_type(const FfnParams& p, hipStream_t stream, hipEvent_t start, hip
 // (gate/up), I <= 2048 (down); scale chunks need 16-byte scale rows and
 // whole chunks of four steps: a reduction dimension that is a multiple of
 // 512.
+// 32-bit offsets into the quantized activations (below 2 GiB: batches up
+// to 262144 tokens at H 4096); the larger ones take 64-bit addresses and
+// no LDS scales
+static bool x_offsets_32(const FfnParams& p) {
+  return (int64_t)p.n_tokens * 2 * p.hidden < ((int64_t)1 << 31);
+}
+
+// The MXFP4 gate/up of the packed copy writes h as three E2M3 parts (h6)
+// for the down to multiply on the 32x32x64 instruction when the batch
+// averages at least 16 slots per routed expert; every other grouped-GEMM
+// gate/up writes the E4M3 parts (h3).  The 32x32 tiles pay off only when
+// the down's items hold more than 16 tokens: with fewer, most of each
+// 32-token block is padding and the 16x16x128 form multiplies less (on
+// the 6-of-256 layer: equal at 12 slots per expert, the 16x16 form 6 %
+// faster at 0.75).
+static bool gate_up_writes_h6(const FfnParams& p) {
+  return p.packed && gate_up_writes_h3(p) && x_offsets_32(p) &&
+         (int64_t)p.n_tokens * p.top_k >= 16 * (int64_t)p.n_experts;
+}
+
 hipError_t launch_gemm_gate_up(const FfnParams& p, hipStream_t stream, hipEvent_t start,
                                hipEvent_t stop) {
   const bool sc = p.hidden <= 4096 && p.hidden % 512 == 0;
@@ -1541,10 +1894,9 @@ hipError_t launch_gemm_gate_up(const FfnParams& p, hipStream_t stream, hipEvent_
   const hipError_t e = launch(quant_x_kernel, dim3((unsigned)((blocks + 255) / 256)), dim3(256),
                               0, stream, nullptr, nullptr, p);
   if (e != hipSuccess) return e;
-  // 32-bit offsets into the quantized activations (below 2 GiB: batches up
-  // to 262144 tokens at H 4096); the larger ones take 64-bit addresses and
-  // no LDS scales
-  const bool o32 = (int64_t)p.n_tokens * 2 * p.hidden < ((int64_t)1 << 31);
+  const bool o32 = x_offsets_32(p);
+  const bool h6 = gate_up_writes_h6(p);
+  if (h6 && (p.h6 == nullptr || p.h6s == nullptr)) return hipErrorInvalidValue;
   return by_type(p, stream, start, stop, [&](int wt, int lo, int hi, hipEvent_t a, hipEvent_t b) {
     if (wt != MOE_W_MXFP4) {
       if (!o32) return gate_up_range<MOE_W_FP8E4M3_B128, 64, false, false>(p, lo, hi, stream, a, b);
@@ -1559,7 +1911,9 @@ hipError_t launch_gemm_gate_up(const FfnParams& p, hipStream_t stream, hipEvent_
     if (!o32) return gate_up_range<MOE_W_MXFP4, 112, false, false>(p, lo, hi, stream, a, b);
     // the packed copy (its shapes are multiples of 512, and every MXFP4
     // matrix of the launch is in it) needs no LDS scale block, so no bound
-    // on H
+    // on H; it writes h6
+    if (p.packed && h6)
+      return gate_up_range<MOE_W_MXFP4, 112, true, true, true, true>(p, lo, hi, stream, a, b);
     if (p.packed) return gate_up_range<MOE_W_MXFP4, 112, true, true, true>(p, lo, hi, stream, a, b);
     return sc ? gate_up_range<MOE_W_MXFP4, 112, true, true>(p, lo, hi, stream, a, b)
               : gate_up_range<MOE_W_MXFP4, 112, false, true>(p, lo, hi, stream, a, b);
@@ -1573,6 +1927,8 @@ hipError_t launch_gemm_down(const FfnParams& p, hipStream_t stream, hipEvent_t s
   // h in three E4M3 parts (from the grouped-GEMM gate/up) or as the bf16
   // pair (fp32 x, or the decode gate/up of a small batch with many slots)
   const bool h3 = gate_up_writes_h3(p);
+  const bool h6 = gate_up_writes_h6(p);
+  if (h6 && (p.h6 == nullptr || p.h6s == nullptr)) return hipErrorInvalidValue;
   return by_type(p, stream, start, stop, [&](int wt, int lo, int hi, hipEvent_t a, hipEvent_t b) {
     if (wt != MOE_W_MXFP4) {
       // the fp8 segments of this launch: the routed ones, the shared one
@@ -1586,6 +1942,7 @@ hipError_t launch_gemm_down(const FfnParams& p, hipStream_t stream, hipEvent_t s
       return sc8 ? down_range<MOE_W_FP8E4M3_B128, 64, true>(p, lo, hi, stream, a, b)
                  : down_range<MOE_W_FP8E4M3_B128, 64, false>(p, lo, hi, stream, a, b);
     }
+    if (h6) return down6_range(p, lo, hi, stream, a, b);
     if (h3 && p.packed) return down3_range<MOE_W_MXFP4, true, true>(p, lo, hi, stream, a, b);
     if (h3)
       return sc ? down3_range<MOE_W_MXFP4, true>(p, lo, hi, stream, a, b)

@@ -168,7 +168,18 @@ moe_status plan_ffn(const moe_layer* layer, int n_tokens, FfnPlan* plan) {
   plan->off_gmax = plan->off_xs + xs_bytes;
   plan->off_qctr = plan->off_gmax + gmax_bytes;
   plan->off_gbuf = plan->off_qctr + (n > 0 ? 256 : 0);
-  plan->total = plan->off_gbuf + gbuf_bytes;
+  // h as three E2M3 parts (24 bytes a part per 32 values) for the packed
+  // MXFP4 down of batches with at least 16 slots per routed expert, with a
+  // scale word per 32 values; 16 bytes of padding after the last record
+  // (the down's 16-byte copies may read 8 bytes past a tile)
+  const bool h6 = layer->gate.type == MOE_W_MXFP4 && plan->slots > 0 &&
+                  n * layer->top_k >= 16 * (int64_t)layer->n_experts;
+  const size_t h6_bytes =
+      h6 ? align_up((size_t)(plan->slots * (hs / 32)) * 72u + 16u, 256) : 0;
+  const size_t h6s_bytes = h6 ? align_up((size_t)(plan->slots * (hs / 32)) * 4u, 256) : 0;
+  plan->off_h6 = plan->off_gbuf + gbuf_bytes;
+  plan->off_h6s = plan->off_h6 + h6_bytes;
+  plan->total = plan->off_h6s + h6s_bytes;
   return MOE_OK;
 }
 

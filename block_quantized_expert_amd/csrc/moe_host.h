@@ -34,6 +34,11 @@ namespace moe {
 //                                         lazy path (batches of up to
 //                                         kGateFirstMaxTokens tokens; else
 //                                         empty)
+//   h6, h6s    : MXFP4 layers, batches of at least 16 slots per routed
+//                expert: h as three E2M3 parts for the down of a layer
+//                with the packed copy, u8 [h_stride/32][slots][3][24] (+16
+//                bytes of padding) and their scale words u32
+//                [h_stride/32][slots]
 // A slot is one (token, routed expert) pair in grouped order
 // (p in [0, n_tokens*top_k)) or, for the shared expert, n_tokens*top_k + t.
 struct FfnPlan {
@@ -48,6 +53,8 @@ struct FfnPlan {
   size_t off_gmax;
   size_t off_gbuf;
   size_t off_qctr;
+  size_t off_h6;   // 0 bytes unless the routed experts are MXFP4 and the batch large
+  size_t off_h6s;
   size_t total;
 };
 

@@ -42,6 +42,15 @@ struct FfnParams {
   // s-8 and a zero byte)
   uint8_t* h3;
   uint8_t* h3s;
+  // packed MXFP4 batches: h as three E2M3 parts for the 32x32x64 down,
+  // 32-row-block major: h6 [h_stride/32][slots][3 parts][24 B] (part q of
+  // the 32 values of block kb of a slot, 6 bits each, value i at bits
+  // 6i .. 6i+5), h6s [h_stride/32][slots] (the parts' UE8M0 scale bytes in
+  // bytes 0..2), 16 bytes of padding after h6; null unless the routed
+  // experts are MXFP4 and the batch has at least 16 slots per expert
+  uint8_t* h6;
+  uint32_t* h6s;
+  int64_t n_slots;  // N*k + N with a shared expert
   // [slots][hidden / 4][3 words] per-slot outputs, four features as 24-bit
   // floats in three words (store_f24x4); the combine weights them
   uint32_t* obuf;

@@ -10,7 +10,7 @@ from block_quantized_expert_amd import binding as B
 from block_quantized_expert_amd import inputs as I
 from oracle import moe_oracle as O
 
-# spec tolerance for fp32 outputs from bf16 (or fp32) activations
+# tolerance on max|y - y_ref| / rms(y_ref) for fp32 outputs from bf16 (or fp32) activations
 Y_TOL = 2e-3
 
 

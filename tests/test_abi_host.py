@@ -79,8 +79,9 @@ def test_ffn_workspace_bytes():
     xs = n * 4096 // 16        # their scale bytes
     gmax = n * 6 * 4           # lazy skip: each routed slot's largest |SiLU(g)|
     qctr = 256                 # item-queue counters of the grouped GEMMs
+    h6 = slots * 64 * 72 + 256 + slots * 64 * 4  # h in E2M3 parts (+ padding) for the packed down
     assert B.lib().moe_ffn_workspace_bytes(ctypes.byref(L), n) == \
-        2 * h + o + xq + xs + gmax + qctr
+        2 * h + o + xq + xs + gmax + qctr + h6
     # up to 16 tokens: also the gate outputs of the gate-first lazy pass
     n = 16
     slots = n * 6 + n
@@ -89,8 +90,21 @@ def test_ffn_workspace_bytes():
     xs = -(-n * 4096 // 16 // 256) * 256
     gmax = -(-n * 6 * 4 // 256) * 256
     gbuf = n * 6 * 2048 * 4
+    # (16 tokens x 6 slots: too few per expert for the E2M3 parts)
     assert B.lib().moe_ffn_workspace_bytes(ctypes.byref(L), n) == \
         2 * h + o + n * 4096 * 2 + xs + gmax + 256 + gbuf
+    # the E2M3 parts from 16 slots per routed expert on
+    L16 = _layer(e=16, k=2)
+    for n, with_h6 in ((127, False), (128, True)):
+        slots = n * 2 + n
+        h6 = -(-(slots * 64 * 72 + 16) // 256) * 256 + -(-slots * 64 * 4 // 256) * 256
+        plain = B.lib().moe_ffn_workspace_bytes(ctypes.byref(L16), n)
+        assert plain > 0
+        L16.gate = B.MoeProj(1, FAKE.value, FAKE.value)  # fp8 routed experts: no E2M3 parts
+        L16.up = L16.down = L16.gate
+        fp8 = B.lib().moe_ffn_workspace_bytes(ctypes.byref(L16), n)
+        L16 = _layer(e=16, k=2)
+        assert plain - fp8 == (h6 if with_h6 else 0)
     assert B.lib().moe_ffn_workspace_bytes(ctypes.byref(L), 0) == 0
     assert B.lib().moe_ffn_workspace_bytes(ctypes.byref(_layer(hidden=100)), 8) == 0
     assert B.lib().moe_ffn_workspace_bytes(None, 8) == 0

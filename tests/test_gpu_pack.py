@@ -2,15 +2,17 @@
 
 - Its bytes against the layout include/moe.h states, restated here with
   numpy reshapes of the row-major arrays (MXFP4 and fp8 shared experts).
-- Every output computed with the copy is bitwise equal to the one computed
-  without it: the same code and scale bytes reach the matrix instruction in
-  the same order, only their addresses differ.  Checked on every tile size
-  of the grouped GEMMs (the layers of the tile-parity test), with an fp8
-  shared expert (its own launch, packed in its format), with the lazy skip
-  and with pruning, on the full-size batched workloads, and through
-  moe_forward for one token (the fused kernel reads the copy) and eight (the
-  small-batch kernels ignore it); the outputs without the copy are compared
-  with the oracle by the other GPU tests.
+- Batched calls with the copy: the MXFP4 grouped GEMMs then carry h into the
+  down projection as three E2M3 parts (the 32x32x64 form) instead of three
+  E4M3 parts, so their outputs are compared with the oracle, on every tile
+  size of the grouped GEMMs (the layers of the tile-parity test), with an
+  fp8 shared expert (its own launch, packed in its format), with the lazy
+  skip, with pruning, and on sampled tokens and rows of the full-size
+  batched workloads, whose routing stays bitwise equal.
+- One token (the fused kernel reads the copy) and eight (the small-batch
+  kernels ignore it) through moe_forward: bitwise equal to the unpacked
+  layer, the same code and scale bytes reaching the matrix instruction in
+  the same order.
 """
 
 from dataclasses import replace
@@ -21,7 +23,7 @@ import torch
 
 from block_quantized_expert_amd import binding as B
 from block_quantized_expert_amd import inputs as I
-from moe_testlib import assert_y_close, gpu_inputs, oracle_y_host
+from moe_testlib import assert_y_close, gpu_inputs, oracle_routing, oracle_y, oracle_y_host
 from oracle import moe_oracle as O
 from test_gpu_parity_tiles import COUNTS, RAGGED, _table
 
@@ -107,53 +109,77 @@ def _hash_ffn(layer, wl, x_d, opts=None):
     (replace(RAGGED, shared="fp8_e4m3_b128", seed=42), 0.0),
     (RAGGED, 1e-3),
 ], ids=["mxfp4_shared", "fp8_shared", "lazy"])
-def test_every_tile_size_bitwise_with_the_copy(wl, lazy):
+def test_every_tile_size_with_the_copy(wl, lazy):
     print("case pack tiles %s lazy %g" % (wl.shared, lazy), flush=True)
     layer = B.Layer(I.make_layer(wl, device=DEV), wl.top_k)
     x = I.activations(wl)
     x_d = x.to(DEV)
     opts = B.make_opts(lazy_tau=lazy) if lazy > 0 else None
-    y0, pairs, wts = _hash_ffn(layer, wl, x_d, opts)
     assert layer.pack()
-    y1, _, _ = _hash_ffn(layer, wl, x_d, opts)
-    assert torch.equal(y0, y1)
-    if lazy == 0.0:
-        rids, rw = O.route_hash(np.arange(wl.n_tokens), pairs, wts)
-        assert_y_close(y1.cpu().numpy(), oracle_y_host(layer.weights, wl.act, x, rids, rw))
+    y, pairs, wts = _hash_ffn(layer, wl, x_d, opts)
+    rids, rw = O.route_hash(np.arange(wl.n_tokens), pairs, wts)
+    assert_y_close(y.cpu().numpy(),
+                   oracle_y_host(layer.weights, wl.act, x, rids, rw, lazy_tau=lazy))
 
 
-@pytest.mark.parametrize("name", ["decode32", "prefill512", "hash4096"])
-def test_full_size_batches_bitwise_with_the_copy(name):
+def _sample(n, k, seed):
+    return sorted(np.random.default_rng(seed).choice(n, size=min(n, k), replace=False).tolist())
+
+
+@pytest.mark.parametrize("name,n_tok,n_rows", [
+    ("decode32", 8, 1024),
+    ("prefill512", 6, 512),
+    ("hash4096", 6, 512),
+])
+def test_full_size_batches_with_the_copy(name, n_tok, n_rows):
+    """The launch configuration the benchmark times (packed layer, full
+    batch): routing bitwise equal to the unpacked layer's and to the
+    oracle's, y against the oracle on sampled tokens and rows."""
     wl = I.WORKLOADS[name]
     print("case pack %s" % name, flush=True)
     layer, x, x_d, routing, routing_d = gpu_inputs(wl)
-    y0, ids0, _, _ = B.forward(layer, x_d, routing_d, wl.routed_scale)
+    _, ids0, _, _ = B.forward(layer, x_d, routing_d, wl.routed_scale)
     torch.cuda.synchronize()
     assert layer.pack()
     y1, ids1, _, _ = B.forward(layer, x_d, routing_d, wl.routed_scale)
     torch.cuda.synchronize()
     assert torch.equal(ids0, ids1)
-    assert torch.equal(y0, y1)
+    rids, rw = oracle_routing(wl, routing)
+    assert np.array_equal(ids1.cpu().numpy(), rids)
+    tokens = _sample(wl.n_tokens, n_tok, 21)
+    rows = _sample(wl.hidden, n_rows, 22)
+    ref = oracle_y(wl, x, rids, rw, tokens=tokens, rows=rows)
+    assert_y_close(y1.cpu().numpy()[tokens][:, rows], ref)
 
 
 def test_pruned_batch_and_decode_paths_with_the_copy():
     """moe_forward on a packed layer: a 32-token batch with tail pruning (the
-    grouped GEMMs with dropped slots), 8 tokens (small-batch kernels) and one
-    token (fused kernel), each bitwise equal to the unpacked layer."""
+    grouped GEMMs with dropped slots) against the oracle; 8 tokens
+    (small-batch kernels) and one token (fused kernel) bitwise equal to the
+    unpacked layer."""
     wl = I.WORKLOADS["decode32"]
     layer, x, x_d, routing, routing_d = gpu_inputs(wl)
     logits = routing_d["logits"]
-    cases = [(32, B.make_opts(keep_max=4)), (8, None), (1, None)]
+    cases = [(8, None), (1, None)]
     before = []
     for n, opts in cases:
         buf = B.moe_forward_ex(layer, logits[:n].contiguous(), x_d[:n].contiguous(),
-                               opts if opts is not None else B.make_opts(), wl.routed_scale)
+                               B.make_opts(), wl.routed_scale)
         torch.cuda.synchronize()
         before.append(buf.y.clone())
     assert layer.pack()
     for (n, opts), y0 in zip(cases, before):
         print("case pack moe_forward n=%d" % n, flush=True)
         buf = B.moe_forward_ex(layer, logits[:n].contiguous(), x_d[:n].contiguous(),
-                               opts if opts is not None else B.make_opts(), wl.routed_scale)
+                               B.make_opts(), wl.routed_scale)
         torch.cuda.synchronize()
         assert torch.equal(y0, buf.y)
+    print("case pack moe_forward n=32 pruned", flush=True)
+    keep = 4
+    buf = B.moe_forward_ex(layer, logits, x_d, B.make_opts(keep_max=keep), wl.routed_scale)
+    torch.cuda.synchronize()
+    lg = I.routing_to_numpy(routing)["logits"]
+    ids_ref, w_ref = O.route_topk(lg, wl.top_k, wl.routed_scale)
+    ids_ref, w_ref = O.prune_tail(ids_ref, w_ref, keep, np.float32(0.0))
+    assert np.array_equal(buf.ids.cpu().numpy(), ids_ref)
+    assert_y_close(buf.y.cpu().numpy(), oracle_y_host(layer.weights, wl.act, x, ids_ref, w_ref))
