@@ -371,6 +371,15 @@ __device__ __forceinline__ void dispatch_nbt(int n, Fn&& f) {
   }
 }
 
+// Calls f(IntC<k>) for k = K0 .. K1-1 in order, as straight-line code.
+template <int K0, int K1, typename Fn>
+__device__ __forceinline__ void static_for(Fn&& f) {
+  if constexpr (K0 < K1) {
+    f(IntC<K0>{});
+    static_for<K0 + 1, K1>(f);
+  }
+}
+
 // ------------------------------------------------------------- gate/up
 
 // The activations enter the matrix cores as E4M3 with one UE8M0 scale per 32
@@ -1533,9 +1542,10 @@ __global__ __launch_bounds__(kGThreads, kGPerCU) void gemm_down3_kernel(FfnParam
 // 1 KiB (16 bytes per lane)
 constexpr int kD6Plane = (kD3Tok * 72 + 1023) / 1024 * 1024;
 constexpr int kD6Buf = 4 * kD6Plane;             // a step (20 KiB)
-constexpr int kD6ScOff = 2 * kD6Buf;
+constexpr int kD6Ring = 3;                       // steps in LDS: the current and two ahead
+constexpr int kD6ScOff = kD6Ring * kD6Buf;
 constexpr int kD6ScBuf = 4 * kD3Tok * 4;          // a step's scale words
-constexpr int kD6Lds = kD6ScOff + 2 * kD6ScBuf;
+constexpr int kD6Lds = kD6ScOff + kD6Ring * kD6ScBuf;
 static_assert(kD6Lds <= kGemmLds, "down LDS");
 
 template <int SB>
@@ -1549,7 +1559,7 @@ template <int NB, typename Take>
 __device__ __forceinline__ void down6_item(const FfnParams& p, const GItem& it, char* smem,
                                            int wave, int lane, Take&& take) {
   constexpr int RB = 2;           // 32-row blocks per wavefront
-  constexpr int kLoads = 2 * RB;  // vector loads of one step's weights
+  constexpr int kLoads = 4 * RB;  // loads of one step's weight codes and scale words
   const int hi = lane >> 5, l32 = lane & 31;
   const int b16 = (lane >> 4) & 1, r16 = lane & 15;
   const bool shared = it.seg == p.n_experts;
@@ -1598,22 +1608,21 @@ __device__ __forceinline__ void down6_item(const FfnParams& p, const GItem& it, 
     __builtin_amdgcn_global_load_lds(p.h6s + kb * p.n_slots + it.slot0 + (lane < it.m ? lane : 0),
                                      lds(smem + kD6ScOff + b * kD6ScBuf + wave * 256), 4, 0, 0);
   };
-  u32x4 q0[RB][2], q1[RB][2];
-  auto load_w = [&](int ks, u32x4 (&q)[RB][2]) {
+  // weight codes and scale words of three steps in registers (the current
+  // one and two ahead), indexed by ks % 3 in a loop unrolled by three; a
+  // step loads its chunk's scale word again (four steps share it: cache
+  // hits), so that nothing is carried from chunk to chunk
+  u32x4 qb[kD6Ring][RB][2];
+  uint32_t swb[kD6Ring][RB][2];
+  auto load_w = [&](int ks, u32x4 (&q)[RB][2], uint32_t (&w)[RB][2]) {
     const uint32_t k = (uint32_t)min(ks, nks - 1);  // past the end: reload the last step
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int s = 0; s < 2; ++s) q[rb][s] = load16(pkc + (aoff[rb][s] + k * 1024));
-  };
-  uint32_t sp[RB][2], spn[RB][2];
-  auto load_sc = [&](int c) {
-    const uint32_t cc = (uint32_t)min(c, nks / 4 - 1);
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-        spn[rb][s] = *reinterpret_cast<const uint32_t*>(pks + (soff[rb][s] + cc * 256));
+      for (int s = 0; s < 2; ++s) {
+        q[rb][s] = load16(pkc + (aoff[rb][s] + k * 1024));
+        w[rb][s] = *reinterpret_cast<const uint32_t*>(pks + (soff[rb][s] + (k >> 2) * 256));
+      }
   };
 
   f32x16 acc[RB][NB];
@@ -1624,21 +1633,24 @@ __device__ __forceinline__ void down6_item(const FfnParams& p, const GItem& it, 
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[rb][tb][e] = 0.0f;
 
-  auto step_mma = [&](int ks) {
-    const char* cur = smem + (ks & 1) * kD6Buf;
-    const char* cts = smem + kD6ScOff + (ks & 1) * kD6ScBuf;
+  auto step_mma = [&](int ks, int buf, const u32x4 (&q)[RB][2], const uint32_t (&w)[RB][2]) {
+    const char* cur = smem + buf * kD6Buf;
+    const char* cts = smem + kD6ScOff + buf * kD6ScBuf;
     i32x8 a[RB][2];
     uint32_t sa[RB][2];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        a[rb][s] = i32x8{(int)q0[rb][s][0], (int)q0[rb][s][1], (int)q0[rb][s][2],
-                         (int)q0[rb][s][3], 0, 0, 0, 0};
-        sa[rb][s] = sp[rb][s] >> (8 * (ks & 3));
+        a[rb][s] = i32x8{(int)q[rb][s][0], (int)q[rb][s][1], (int)q[rb][s][2], (int)q[rb][s][3],
+                         0, 0, 0, 0};
+        sa[rb][s] = w[rb][s] >> (8 * (ks & 3));
       }
-    // operand u = 3 (2 tb + s) + q: token 32 tb + l32, block 2 s + hi of the
-    // step, part q, at plane (2 s + hi) + token * 72 + q * 24
+    // operand u = (3 s + q) NB + tb: token 32 tb + l32, block 2 s + hi of
+    // the step, part q, at plane (2 s + hi) + token * 72 + q * 24.  Token
+    // blocks innermost, so that consecutive instructions go to NB x RB
+    // different accumulators (a 32x32 product waits for the one before on
+    // its accumulator).
     lds_cptr pb = to_lds(cur) + hi * kD6Plane + l32 * 72;
     opaque(pb);
     lds_cptr ps = to_lds(cts) + hi * 256 + l32 * 4;
@@ -1646,25 +1658,27 @@ __device__ __forceinline__ void down6_item(const FfnParams& p, const GItem& it, 
     constexpr int kOps = 6 * NB;
     constexpr int kAhead = 2;
     i32x8 bop[kAhead + 1];
-    uint32_t sbt[2];
+    uint32_t sbt[2][NB];
     auto read_op = [&](int u) {
-      const int q = u % 3, s = (u / 3) & 1, tb = u / 6;
+      const int tb = u % NB, q = (u / NB) % 3, s = u / (3 * NB);
       const int off = 2 * s * kD6Plane + tb * 32 * 72 + q * 24;
+      // (vector-typed LDS reads: the compiler then leaves the LDS copies in
+      // flight; its wait for them is the end-of-step barrier's)
       const u32x2 w0 = *reinterpret_cast<const lds_u32x2*>(pb + off);
       const u32x2 w1 = *reinterpret_cast<const lds_u32x2*>(pb + off + 8);
       const u32x2 w2 = *reinterpret_cast<const lds_u32x2*>(pb + off + 16);
       bop[u % (kAhead + 1)] = i32x8{(int)w0.x, (int)w0.y, (int)w1.x, (int)w1.y,
                                     (int)w2.x, (int)w2.y, 0, 0};
-      if (q == 0) sbt[(u / 3) & 1] = *reinterpret_cast<const lds_u32*>(ps + 2 * s * 256 + tb * 128);
+      if (q == 0) sbt[s][tb] = *reinterpret_cast<const lds_u32*>(ps + 2 * s * 256 + tb * 128);
     };
 #pragma unroll
     for (int u = 0; u < kAhead && u < kOps; ++u) read_op(u);
 #pragma unroll
     for (int u = 0; u < kOps; ++u) {
       if (u + kAhead < kOps) read_op(u + kAhead);
-      const int q = u % 3, s = (u / 3) & 1, tb = u / 6;
+      const int tb = u % NB, q = (u / NB) % 3, s = u / (3 * NB);
       const i32x8& b = bop[u % (kAhead + 1)];
-      const uint32_t sb = sbt[(u / 3) & 1];
+      const uint32_t sb = sbt[s][tb];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         if (q == 0)
@@ -1677,36 +1691,57 @@ __device__ __forceinline__ void down6_item(const FfnParams& p, const GItem& it, 
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  // step ks (buffers B = ks % 3): first step ks+2's copies and weights
+  // (the last steps' copies clamped to a step that exists), then the step's
+  // products; at its end step ks+1's copies (issued a step earlier, and
+  // followed by at least kLoads + kCopies later requests: step ks+1's
+  // weights, which the last steps still load, and step ks+2's copies) have
+  // landed, and the workgroup barrier frees buffer B for the copies of
+  // step ks+3.  (The weight loads of steps past the end are dropped by the
+  // compiler as unused; the count stays a lower bound.)
+  constexpr int kCopies = kD6Plane / 1024 + 1;
+  auto step = [&](auto B, int ks) {
+    constexpr int b = decltype(B)::value;
+    copy_h(min(ks + 2, nks - 1), (b + 2) % kD6Ring);
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(ks + 2, qb[(b + 2) % kD6Ring], swb[(b + 2) % kD6Ring]);
+    __builtin_amdgcn_sched_barrier(0);
+    step_mma(ks, b, qb[b], swb[b]);
+    step_barrier<kCopies + kLoads>();
+  };
 
-  load_sc(0);
-  load_w(0, q0);
+  load_w(0, qb[0], swb[0]);
   copy_h(0, 0);
-  wait_vm<0>();
-  __syncthreads();
-  for (int ks = 0; ks < nks; ++ks) {
-    if ((ks & 3) == 0) {
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) sp[rb][s] = spn[rb][s];
-      load_sc((ks >> 2) + 1);
+  load_w(1, qb[1], swb[1]);
+  copy_h(1, 1);  // (a reduction has at least four steps)
+  step_barrier<kCopies + kLoads>();  // step 0's copies landed, step 1's in flight
+  // The steps as straight-line code, four at a time (the reduction is 4, 8,
+  // 12 or 16 steps), nested so that no join follows a step: in a loop, the
+  // compiler's wait analysis, merging the entry and the back edge, took the
+  // registers loaded two steps earlier for loads still in flight and,
+  // with LDS copies pending, waited for every load (the ones just issued
+  // too).  Here it knows them complete from the end-of-step waits.
+  auto four = [&](auto C) {
+    static_for<4 * decltype(C)::value, 4 * decltype(C)::value + 4>([&](auto K) {
+      constexpr int k = decltype(K)::value;
+      step(IntC<k % kD6Ring>{}, k);
+    });
+  };
+  four(IntC<0>{});
+  if (nks > 4) {
+    four(IntC<1>{});
+    if (nks > 8) {
+      four(IntC<2>{});
+      if (nks > 12) four(IntC<3>{});
     }
-    if (ks + 1 < nks) copy_h(ks + 1, (ks + 1) & 1);
-    __builtin_amdgcn_sched_barrier(0);
-    load_w(ks + 1, q1);
-    __builtin_amdgcn_sched_barrier(0);
-    step_mma(ks);
-    step_barrier<kLoads>();  // the copies have landed (the weights in flight)
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int s = 0; s < 2; ++s) q0[rb][s] = q1[rb][s];
   }
   wait_vm<0>();
   take();  // the next item's ticket, in flight during the epilogue
 
   // the per-slot outputs, unweighted (the combine applies the routing
-  // weights): rows 8 j + 4 hi .. +3 of each 32-row block
+  // weights): rows 8 j + 4 hi .. +3 of each 32-row block.  (Staged through
+  // LDS so that twelve lanes write a token's 192 contiguous bytes, the
+  // stores measured slower: their cost is the bytes.)
 #pragma unroll
   for (int tb = 0; tb < NB; ++tb) {
     const int n = tb * 32 + l32;
@@ -1881,10 +1916,12 @@ static bool x_offsets_32(const FfnParams& p) {
 // the down's items hold more than 16 tokens: with fewer, most of each
 // 32-token block is padding and the 16x16x128 form multiplies less (on
 // the 6-of-256 layer: equal at 12 slots per expert, the 16x16 form 6 %
-// faster at 0.75).
+// faster at 0.75).  The down keeps a whole reduction's weight scales in
+// registers: intermediate sizes up to 2048.
 static bool gate_up_writes_h6(const FfnParams& p) {
   return p.packed && gate_up_writes_h3(p) && x_offsets_32(p) &&
-         (int64_t)p.n_tokens * p.top_k >= 16 * (int64_t)p.n_experts;
+         (int64_t)p.n_tokens * p.top_k >= 16 * (int64_t)p.n_experts && p.inter <= 2048 &&
+         (!p.has_shared || p.shared_inter <= 2048);
 }
 
 hipError_t launch_gemm_gate_up(const FfnParams& p, hipStream_t stream, hipEvent_t start,

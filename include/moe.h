@@ -308,7 +308,13 @@ moe_status moe_pack_experts(const moe_layer* layer, void* packed, size_t packed_
  *     exactly for inputs within 2^-13 of their block's largest magnitude;
  *     smaller ones keep their bits above 2^-17 of that magnitude); the
  *     SwiGLU output h is stored as three E4M3 parts per 32 values (h to
- *     2^-12 of its magnitude) for the down projection.
+ *     2^-12 of its magnitude) for the down projection.  With the packed
+ *     copy (moe_pack_experts) of MXFP4 experts, batches of at least 16
+ *     slots per routed expert and intermediate sizes up to 2048 store h
+ *     instead as three E2M3 parts per 32 values, each part under its own
+ *     power-of-two scale (h to 2^-12 of its block's largest magnitude), and
+ *     the down projection multiplies them on the 32x32x64 form of the
+ *     instruction.
  *   - bf16 x with MXFP4 experts and up to 16 tokens: weights decoded
  *     exactly to bf16 in registers, x as given, h as a bf16 high + low pair
  *     (16 significant bits).
