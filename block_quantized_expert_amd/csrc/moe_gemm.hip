@@ -1545,7 +1545,11 @@ constexpr int kD6Buf = 4 * kD6Plane;             // a step (20 KiB)
 constexpr int kD6Ring = 3;                       // steps in LDS: the current and two ahead
 constexpr int kD6ScOff = kD6Ring * kD6Buf;
 constexpr int kD6ScBuf = 4 * kD3Tok * 4;          // a step's scale words
-constexpr int kD6Lds = kD6ScOff + kD6Ring * kD6ScBuf;
+// the weights' scale words of a chunk of four steps, per wavefront its four
+// 16-row blocks x 256 bytes, two chunks
+constexpr int kD6WsOff = kD6ScOff + kD6Ring * kD6ScBuf;
+constexpr int kD6WsBuf = 4 * 4 * 256;
+constexpr int kD6Lds = kD6WsOff + 2 * kD6WsBuf;
 static_assert(kD6Lds <= kGemmLds, "down LDS");
 
 template <int SB>
@@ -1559,7 +1563,7 @@ template <int NB, typename Take>
 __device__ __forceinline__ void down6_item(const FfnParams& p, const GItem& it, char* smem,
                                            int wave, int lane, Take&& take) {
   constexpr int RB = 2;           // 32-row blocks per wavefront
-  constexpr int kLoads = 4 * RB;  // loads of one step's weight codes and scale words
+  constexpr int kLoads = 2 * RB;  // loads of one step's weight codes
   const int hi = lane >> 5, l32 = lane & 31;
   const int b16 = (lane >> 4) & 1, r16 = lane & 15;
   const bool shared = it.seg == p.n_experts;
@@ -1572,8 +1576,8 @@ __device__ __forceinline__ void down6_item(const FfnParams& p, const GItem& it, 
   const int64_t blk0 = ((shared ? 0 : (int64_t)it.seg * p.hidden) + (nrb16 > 0 ? wrow0 : 0)) / 16;
   const uint8_t* pkc = p.pk_c[shared ? 5 : 2] + blk0 * nks * 1024;
   const uint8_t* pks = p.pk_s[shared ? 5 : 2] + blk0 * (nks / 4) * 256;
-  // the lane's code unit (step 0) and scale word (chunk 0) for 32-row block
-  // rb and input half s of a step
+  // the lane's code unit (step 0) for 32-row block rb and input half s of a
+  // step, and its scale word in the wavefront's chunk of scales in LDS
   uint32_t aoff[RB][2], soff[RB][2];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
@@ -1583,7 +1587,7 @@ __device__ __forceinline__ void down6_item(const FfnParams& p, const GItem& it, 
     for (int s = 0; s < 2; ++s) {
       const int unit = 16 * (hi + 2 * s) + r16;
       aoff[rb][s] = (uint32_t)(blk * nks * 1024 + unit * 16);
-      soff[rb][s] = (uint32_t)(blk * (nks / 4) * 256 + unit * 4);
+      soff[rb][s] = (uint32_t)(bb * 256 + unit * 4);
     }
   }
   auto lds = [](char* q) { return (__attribute__((address_space(3))) void*)q; };
@@ -1608,21 +1612,27 @@ __device__ __forceinline__ void down6_item(const FfnParams& p, const GItem& it, 
     __builtin_amdgcn_global_load_lds(p.h6s + kb * p.n_slots + it.slot0 + (lane < it.m ? lane : 0),
                                      lds(smem + kD6ScOff + b * kD6ScBuf + wave * 256), 4, 0, 0);
   };
-  // weight codes and scale words of three steps in registers (the current
-  // one and two ahead), indexed by ks % 3 in a loop unrolled by three; a
-  // step loads its chunk's scale word again (four steps share it: cache
-  // hits), so that nothing is carried from chunk to chunk
+  // weight codes of three steps in registers (the current one and two
+  // ahead)
   u32x4 qb[kD6Ring][RB][2];
-  uint32_t swb[kD6Ring][RB][2];
-  auto load_w = [&](int ks, u32x4 (&q)[RB][2], uint32_t (&w)[RB][2]) {
+  auto load_w = [&](int ks, u32x4 (&q)[RB][2]) {
     const uint32_t k = (uint32_t)min(ks, nks - 1);  // past the end: reload the last step
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        q[rb][s] = load16(pkc + (aoff[rb][s] + k * 1024));
-        w[rb][s] = *reinterpret_cast<const uint32_t*>(pks + (soff[rb][s] + (k >> 2) * 256));
-      }
+      for (int s = 0; s < 2; ++s) q[rb][s] = load16(pkc + (aoff[rb][s] + k * 1024));
+  };
+  // the weights' scale words of chunk c (steps 4c .. 4c+3) into LDS buffer
+  // c % 2: one 16-byte copy per lane, lane l taking bytes 16 (l % 16) .. of
+  // 16-row block l / 16 of the wavefront (block 0 for blocks past the
+  // matrix end); a lane's words are then read per step from LDS (they were
+  // four requests per step)
+  auto copy_ws = [&](int c) {
+    const int bb = lane >> 4;
+    const int blk = bb < nrb16 ? bb : 0;
+    const uint8_t* src = pks + (blk * (nks / 4) + min(c, nks / 4 - 1)) * 256 + (lane & 15) * 16;
+    __builtin_amdgcn_global_load_lds(src, lds(smem + kD6WsOff + (c & 1) * kD6WsBuf + wave * 1024),
+                                     16, 0, 0);
   };
 
   f32x16 acc[RB][NB];
@@ -1633,9 +1643,10 @@ __device__ __forceinline__ void down6_item(const FfnParams& p, const GItem& it, 
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[rb][tb][e] = 0.0f;
 
-  auto step_mma = [&](int ks, int buf, const u32x4 (&q)[RB][2], const uint32_t (&w)[RB][2]) {
+  auto step_mma = [&](int ks, int buf, const u32x4 (&q)[RB][2]) {
     const char* cur = smem + buf * kD6Buf;
     const char* cts = smem + kD6ScOff + buf * kD6ScBuf;
+    const char* cws = smem + kD6WsOff + ((ks >> 2) & 1) * kD6WsBuf + wave * 1024;
     i32x8 a[RB][2];
     uint32_t sa[RB][2];
 #pragma unroll
@@ -1644,7 +1655,7 @@ __device__ __forceinline__ void down6_item(const FfnParams& p, const GItem& it, 
       for (int s = 0; s < 2; ++s) {
         a[rb][s] = i32x8{(int)q[rb][s][0], (int)q[rb][s][1], (int)q[rb][s][2], (int)q[rb][s][3],
                          0, 0, 0, 0};
-        sa[rb][s] = w[rb][s] >> (8 * (ks & 3));
+        sa[rb][s] = *reinterpret_cast<const lds_u32*>(to_lds(cws) + soff[rb][s]) >> (8 * (ks & 3));
       }
     // operand u = (3 s + q) NB + tb: token 32 tb + l32, block 2 s + hi of
     // the step, part q, at plane (2 s + hi) + token * 72 + q * 24.  Token
@@ -1691,30 +1702,34 @@ __device__ __forceinline__ void down6_item(const FfnParams& p, const GItem& it, 
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // step ks (buffers B = ks % 3): first step ks+2's copies and weights
-  // (the last steps' copies clamped to a step that exists), then the step's
-  // products; at its end step ks+1's copies (issued a step earlier, and
-  // followed by at least kLoads + kCopies later requests: step ks+1's
-  // weights, which the last steps still load, and step ks+2's copies) have
-  // landed, and the workgroup barrier frees buffer B for the copies of
-  // step ks+3.  (The weight loads of steps past the end are dropped by the
-  // compiler as unused; the count stays a lower bound.)
+  // step ks (buffers B = ks % 3): at the start of a chunk the next chunk's
+  // scale words, then step ks+2's copies and weights (the last steps'
+  // copies clamped to a step that exists), then the step's products.  At
+  // its end at most the kCopies + kLoads requests just issued remain in
+  // flight: step ks+1's copies (issued a step earlier and followed by step
+  // ks+1's weights and step ks+2's copies, at least that many requests;
+  // the compiler drops the unused weight loads of steps past the end) and
+  // the scale words have landed; the workgroup barrier frees buffer B for
+  // the copies of step ks+3 and, at the end of a chunk, the scale buffer
+  // for the chunk after next.
   constexpr int kCopies = kD6Plane / 1024 + 1;
-  auto step = [&](auto B, int ks) {
-    constexpr int b = decltype(B)::value;
+  auto step = [&](auto B, auto K) {
+    constexpr int b = decltype(B)::value, ks = decltype(K)::value;
+    if constexpr (ks % 4 == 0) copy_ws(ks / 4 + 1);
     copy_h(min(ks + 2, nks - 1), (b + 2) % kD6Ring);
     __builtin_amdgcn_sched_barrier(0);
-    load_w(ks + 2, qb[(b + 2) % kD6Ring], swb[(b + 2) % kD6Ring]);
+    load_w(ks + 2, qb[(b + 2) % kD6Ring]);
     __builtin_amdgcn_sched_barrier(0);
-    step_mma(ks, b, qb[b], swb[b]);
+    step_mma(ks, b, qb[b]);
     step_barrier<kCopies + kLoads>();
   };
 
-  load_w(0, qb[0], swb[0]);
+  copy_ws(0);
+  load_w(0, qb[0]);
   copy_h(0, 0);
-  load_w(1, qb[1], swb[1]);
+  load_w(1, qb[1]);
   copy_h(1, 1);  // (a reduction has at least four steps)
-  step_barrier<kCopies + kLoads>();  // step 0's copies landed, step 1's in flight
+  step_barrier<kCopies + kLoads>();  // chunk 0's scales and step 0's copies landed
   // The steps as straight-line code, four at a time (the reduction is 4, 8,
   // 12 or 16 steps), nested so that no join follows a step: in a loop, the
   // compiler's wait analysis, merging the entry and the back edge, took the
@@ -1724,7 +1739,7 @@ __device__ __forceinline__ void down6_item(const FfnParams& p, const GItem& it, 
   auto four = [&](auto C) {
     static_for<4 * decltype(C)::value, 4 * decltype(C)::value + 4>([&](auto K) {
       constexpr int k = decltype(K)::value;
-      step(IntC<k % kD6Ring>{}, k);
+      step(IntC<k % kD6Ring>{}, K);
     });
   };
   four(IntC<0>{});
