@@ -106,13 +106,13 @@ FETCH_SCALE = 262144.0 / 131093.3
 WRITE_SCALE = 1.0
 KERNEL_TRAFFIC_KIB = {  # (workload, packed copy used): (FETCH_SIZE, WRITE_SIZE) per dispatch
     ("decode1", False): (46204.5, 82.2),        # decode_fused_kernel<8, false>
-    ("decode32", False): (475411.1, 5502.4),    # gemm_gate_up_kernel<0, 112, true, true, false, false>
+    ("decode32", False): (475411.1, 5502.4),    # gemm_gate_up_kernel<0, 112, true, true, false, false, false>
     ("prefill512", False): (1180630.5, 27385.2),
     ("hash4096", False): (2131057.8, 176253.2),
-    ("decode1", True): (46192.6, 82.2),         # decode_fused_kernel<8, true>
-    ("decode32", True): (479001.2, 3448.9),     # gemm_gate_up_kernel<0, 112, true, true, false, true>
-    ("prefill512", True): (1168735.0, 24634.7),
-    ("hash4096", True): (1324066.2, 159491.2),
+    ("decode1", True): (46191.4, 82.2),         # decode_fused_kernel<8, true>
+    ("decode32", True): (478980.2, 3448.8),     # gemm_gate_up_kernel<0, 112, true, true, false, true, false>
+    ("prefill512", True): (1168681.3, 24638.4),
+    ("hash4096", True): (1313048.1, 120447.0),  # gemm_gate_up_kernel<0, 112, true, true, false, true, true>
 }
 
 
@@ -678,9 +678,11 @@ def main():
         "vs_baseline": None,
         "dtype": "mxfp4",
         "compute": "E2M1 expert weights with UE8M0 block scales on the matrix cores "
-                   "(batched: with exact E4M3 parts of the bf16 activations on "
-                   "v_mfma_scale_f32_16x16x128_f8f6f4; one token: decoded exactly to bf16); "
-                   "fp32 accumulation",
+                   "(batched: gate/up with exact E4M3 parts of the bf16 activations on "
+                   "v_mfma_scale_f32_16x16x128_f8f6f4, down with h as three E4M3 parts on "
+                   "the same instruction or, packed with >= 16 slots per expert, as three "
+                   "E2M3 parts on v_mfma_scale_f32_32x32x64_f8f6f4; one token: decoded "
+                   "exactly to bf16); fp32 accumulation",
         "data": "synthetic",
         "config": rec["config"],
         "step_stats": rec["step_stats"],
