@@ -1,0 +1,61 @@
+"""The E2M3 down projection (packed MXFP4 layers, batches of at least 16
+routed slots per expert): every output against the oracle on layers whose
+reductions take 4, 8, 12 and 16 steps of 128 (each a different stretch of
+the kernel's straight-line steps and of its ring of buffers), with a shared
+MXFP4 expert of the same or of a different width in the same launch, and
+with the gate-first lazy skip."""
+
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from block_quantized_expert_amd import binding as B
+from block_quantized_expert_amd import inputs as I
+from moe_testlib import assert_y_close, oracle_y_host
+from oracle import moe_oracle as O
+from test_gpu_parity_tiles import COUNTS, RAGGED, _table
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+    yield
+    torch.cuda.empty_cache()
+
+
+BASE = replace(RAGGED, hidden=512, seed=61)
+
+
+@pytest.mark.parametrize("inter,shared_inter,lazy", [
+    (512, 0, 0.0),      # 4 steps
+    (1024, 0, 0.0),     # 8
+    (1536, 0, 0.0),     # 12
+    (2048, 0, 0.0),     # 16
+    (512, 1536, 0.0),   # routed 4 steps, shared 12, one launch
+    (1536, 512, 1e-3),  # routed 12, shared 4, lazy skip
+], ids=["I512", "I1024", "I1536", "I2048", "I512_S1536", "I1536_S512_lazy"])
+def test_e2m3_down_against_the_oracle(inter, shared_inter, lazy):
+    wl = replace(BASE, inter=inter, shared_inter=shared_inter)
+    print("case e2m3 down I=%d SI=%d lazy=%g" % (inter, shared_inter, lazy), flush=True)
+    layer = B.Layer(I.make_layer(wl, device=DEV), wl.top_k)
+    assert layer.pack()
+    x = I.activations(wl)
+    pairs, wts = _table(COUNTS, wl.seed)
+    assert pairs.shape[0] * wl.top_k >= 16 * wl.n_experts  # the E2M3 path's batch size
+    tok = torch.arange(wl.n_tokens, dtype=torch.int32, device=DEV)
+    ids, w = B.moe_route_hash(tok, torch.from_numpy(pairs).to(DEV),
+                              torch.from_numpy(wts).to(DEV), wl.n_experts)
+    grouping = B.moe_group(ids, wl.n_experts)
+    opts = B.make_opts(lazy_tau=lazy) if lazy > 0 else B.make_opts()
+    y = B.moe_ffn_forward_ex(layer, x.to(DEV), w, grouping, opts)
+    torch.cuda.synchronize()
+    rids, rw = O.route_hash(np.arange(wl.n_tokens), pairs, wts)
+    assert_y_close(y.cpu().numpy(),
+                   oracle_y_host(layer.weights, wl.act, x, rids, rw, lazy_tau=lazy))
