@@ -2,8 +2,8 @@
 routed slots per expert): every output against the oracle on layers whose
 reductions take 4, 8, 12 and 16 steps of 128 (each a different stretch of
 the kernel's straight-line steps and of its ring of buffers), with a shared
-MXFP4 expert of the same or of a different width in the same launch, and
-with the gate-first lazy skip."""
+MXFP4 expert of the same or of a different width in the same launch, with
+the gate-first lazy skip, and with tail-pruned slots."""
 
 from dataclasses import replace
 
@@ -59,3 +59,23 @@ def test_e2m3_down_against_the_oracle(inter, shared_inter, lazy):
     rids, rw = O.route_hash(np.arange(wl.n_tokens), pairs, wts)
     assert_y_close(y.cpu().numpy(),
                    oracle_y_host(layer.weights, wl.act, x, rids, rw, lazy_tau=lazy))
+
+
+def test_e2m3_down_with_pruned_slots():
+    """Learned routing with tail pruning (keep_max 1 of 2) on a packed layer
+    whose batch takes the E2M3 path: the dropped slots leave the grouping,
+    the kept ones are rescaled; ids and y against the oracle."""
+    wl = replace(BASE, routing="learned", seed=63)
+    print("case e2m3 down pruned", flush=True)
+    layer = B.Layer(I.make_layer(wl, device=DEV), wl.top_k)
+    assert layer.pack()
+    x = I.activations(wl)
+    rng = np.random.default_rng(64)
+    lg = I.spaced_logits(rng, wl.n_tokens, 0.5 * rng.standard_normal(wl.n_experts), 1e-3)
+    buf = B.moe_forward_ex(layer, torch.from_numpy(lg).to(DEV), x.to(DEV),
+                           B.make_opts(keep_max=1), wl.routed_scale)
+    torch.cuda.synchronize()
+    ids_ref, w_ref = O.route_topk(lg, wl.top_k, wl.routed_scale)
+    ids_ref, w_ref = O.prune_tail(ids_ref, w_ref, 1, np.float32(0.0))
+    assert np.array_equal(buf.ids.cpu().numpy(), ids_ref)
+    assert_y_close(buf.y.cpu().numpy(), oracle_y_host(layer.weights, wl.act, x, ids_ref, w_ref))
