@@ -268,8 +268,11 @@ size_t moe_ffn_workspace_bytes(const moe_layer* layer, int n_tokens);
  *   it), asynchronously on `stream`, reading the layer's arrays.  Returns
  *   MOE_ERR_UNSUPPORTED for a layer that cannot be packed, MOE_ERR_INVALID
  *   for a NULL or misaligned buffer or a short size.  Set
- *   layer->packed_experts = packed afterwards to use it; results are bitwise
- *   equal with and without it.
+ *   layer->packed_experts = packed afterwards to use it.  Results are
+ *   bitwise equal with and without it, except for the batches of
+ *   moe_ffn_forward that then take the E2M3 parts of h (see its numerics:
+ *   at least 16 routed slots per expert, bf16 x, intermediate sizes up to
+ *   2048), whose y stays within the same tolerance of the exact result.
  * Layout, for each matrix of R rows x C inputs (R/16 row blocks of 16 rows,
  * S = C/128 steps, lane l = 16*g + r):
  *   MXFP4 codes: block b step s at byte (b*S + s)*1024, lane l holding the
