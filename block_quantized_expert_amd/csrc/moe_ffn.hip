@@ -609,24 +609,47 @@ __global__ __launch_bounds__(kThreads) void gate_up_decode_kernel(FfnParams p, i
 // y[t] = o_shared[t] + sum_i w[t*k + i] * o[inv_perm[t*k + i]], in that
 // fixed order, leaving out slots dropped by tail pruning or by the lazy
 // skip; four features (three words of 24-bit floats per slot) per thread.
+// UNIFORM (hidden a multiple of 256): a wavefront's 256 features lie in one
+// token, whose slots and weights are then read once per wavefront through
+// the scalar cache instead of by every lane.  K = top_k: the token's slot
+// indices and weights, then all its output loads, are issued with no branch
+// between them (a dropped slot loads slot 0's outputs and is not added).
+template <bool UNIFORM, int K>
 __global__ __launch_bounds__(256) void combine_kernel(FfnParams p) {
   const int h4 = p.hidden / 4;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (int64_t)p.n_tokens * h4) return;
-  const int64_t t = i / h4;
+  const int64_t t = UNIFORM ? (int64_t)__builtin_amdgcn_readfirstlane((int)(i / h4)) : i / h4;
   const int64_t q = (i - t * h4) * 4;
   // slot s's four features at word (s * hidden + q) / 4 * 3
   auto slot_out = [&](int64_t s) { return load_f24x4(p.obuf + (s * p.hidden + q) / 4 * 3); };
-  f32x4 acc = f32x4{0, 0, 0, 0};
-  if (p.has_shared) acc = slot_out((int64_t)p.n_tokens * p.top_k + t);
-  for (int j = 0; j < p.top_k; ++j) {
-    const int pp = p.inv_perm[t * p.top_k + j];
+  int pp[K];
+  float wj[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    pp[j] = p.inv_perm[t * K + j];
+    wj[j] = p.topk_w[t * K + j];
+  }
+  if (p.lazy_tau != 0.0f) {
     // a slot the lazy skip drops contributes nothing
-    const bool live = pp >= 0 && (p.lazy_tau == 0.0f || __uint_as_float(p.gmax[pp]) >= p.lazy_tau);
-    if (live) acc += p.topk_w[t * p.top_k + j] * slot_out(pp);
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+      if (pp[j] >= 0 && __uint_as_float(p.gmax[pp[j]]) < p.lazy_tau) pp[j] = -1;
+  }
+  f32x4 o[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) o[j] = slot_out(pp[j] >= 0 ? pp[j] : 0);
+  // the sum in the fixed order: shared, then slot 0 .. top_k-1
+  f32x4 acc = f32x4{0, 0, 0, 0};
+  if (p.has_shared) acc = slot_out((int64_t)p.n_tokens * K + t);
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const f32x4 a = acc + wj[j] * o[j];
+    acc = pp[j] >= 0 ? a : acc;
   }
   *reinterpret_cast<f32x4*>(p.y + t * p.hidden + q) = acc;
 }
+
 
 // ------------------------------------------------------- down + combine, small batch
 
@@ -1131,6 +1154,22 @@ hipError_t launch_ffn_gate_up(const FfnParams& p, hipStream_t stream, hipEvent_t
   }
 }
 
+template <bool UNIFORM>
+hipError_t combine_launch(const FfnParams& p, hipStream_t stream) {
+  const int64_t n = (int64_t)p.n_tokens * (p.hidden / 4);
+  const dim3 grid((unsigned)((n + 255) / 256)), block(256);
+  switch (p.top_k) {
+    case 1: return launch(combine_kernel<UNIFORM, 1>, grid, block, 0, stream, nullptr, nullptr, p);
+    case 2: return launch(combine_kernel<UNIFORM, 2>, grid, block, 0, stream, nullptr, nullptr, p);
+    case 3: return launch(combine_kernel<UNIFORM, 3>, grid, block, 0, stream, nullptr, nullptr, p);
+    case 4: return launch(combine_kernel<UNIFORM, 4>, grid, block, 0, stream, nullptr, nullptr, p);
+    case 5: return launch(combine_kernel<UNIFORM, 5>, grid, block, 0, stream, nullptr, nullptr, p);
+    case 6: return launch(combine_kernel<UNIFORM, 6>, grid, block, 0, stream, nullptr, nullptr, p);
+    case 7: return launch(combine_kernel<UNIFORM, 7>, grid, block, 0, stream, nullptr, nullptr, p);
+    default: return launch(combine_kernel<UNIFORM, 8>, grid, block, 0, stream, nullptr, nullptr, p);
+  }
+}
+
 hipError_t launch_ffn_down(const FfnParams& p, hipStream_t stream, hipEvent_t start,
                            hipEvent_t stop) {
   // the small-batch down reads the bf16 pair; h in E4M3 parts goes to the
@@ -1148,9 +1187,7 @@ hipError_t launch_ffn_down(const FfnParams& p, hipStream_t stream, hipEvent_t st
   // weighted per-slot outputs, then each token's sum in a fixed order
   hipError_t e = launch_gemm_down(p, stream, start, stop);
   if (e != hipSuccess) return e;
-  const int64_t n = (int64_t)p.n_tokens * (p.hidden / 4);
-  return launch(combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, nullptr,
-                nullptr, p);
+  return p.hidden % 256 == 0 ? combine_launch<true>(p, stream) : combine_launch<false>(p, stream);
 }
 
 }  // namespace moe
