@@ -1931,8 +1931,8 @@ static bool x_offsets_32(const FfnParams& p) {
 // the down's items hold more than 16 tokens: with fewer, most of each
 // 32-token block is padding and the 16x16x128 form multiplies less (on
 // the 6-of-256 layer: equal at 12 slots per expert, the 16x16 form 6 %
-// faster at 0.75).  The down keeps a whole reduction's weight scales in
-// registers: intermediate sizes up to 2048.
+// faster at 0.75).  The down's reduction is straight-line code of up to
+// 16 steps: intermediate sizes up to 2048.
 static bool gate_up_writes_h6(const FfnParams& p) {
   return p.packed && gate_up_writes_h3(p) && x_offsets_32(p) &&
          (int64_t)p.n_tokens * p.top_k >= 16 * (int64_t)p.n_experts && p.inter <= 2048 &&
