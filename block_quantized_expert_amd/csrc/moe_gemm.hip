@@ -1776,6 +1776,9 @@ __device__ __forceinline__ void down6_item(const FfnParams& p, const GItem& it, 
   }
 }
 
+// MIX: the launch also takes an fp8 shared expert (h in E4M3 parts, its
+// packed copy), whose items then fill the routed items' tail.
+template <bool MIX>
 __global__ __launch_bounds__(kGThreads, kGPerCU) void gemm_down6_kernel(FfnParams p, int seg_lo,
                                                                    int seg_hi, uint32_t* qctr) {
   extern __shared__ __align__(16) char smem[];
@@ -1786,6 +1789,13 @@ __global__ __launch_bounds__(kGThreads, kGPerCU) void gemm_down6_kernel(FfnParam
   const int total = item_prefix<kD3Tok, kDnRows, true>(p, seg_lo, seg_hi, s_pref, s_tmp);
   run_queue(ItemQueue{qctr, total, qctr != nullptr}, &s_q, [&](int item, auto&& take) {
     const GItem it = find_item<kD3Tok, kDnRows, true>(p, seg_lo, seg_hi, s_pref, item);
+    if (MIX && it.seg == p.n_experts) {
+      dispatch_nbt<kD3Tok / 16>((it.m + 15) >> 4, [&](auto nb) {
+        down3_item<MOE_W_FP8E4M3_B128, decltype(nb)::value, true, true>(p, it, smem, wave, lane,
+                                                                       take);
+      });
+      return;
+    }
     dispatch_nbt<2>((it.m + 31) >> 5, [&](auto nb) {
       down6_item<decltype(nb)::value>(p, it, smem, wave, lane, take);
     });
@@ -1864,14 +1874,16 @@ hipError_t gate_up_range(const FfnParams& p, int seg_lo, int seg_hi, hipStream_t
   return gate_up_range_as<WT, TT, SC, O32, false, PK, H6>(p, seg_lo, seg_hi, stream, start, stop);
 }
 
+template <bool MIX>
 hipError_t down6_range(const FfnParams& p, int seg_lo, int seg_hi, hipStream_t stream,
                        hipEvent_t start, hipEvent_t stop) {
+  constexpr int lds = MIX && kD3Lds > kD6Lds ? kD3Lds : kD6Lds;
   static const hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_down6_kernel),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, kD6Lds);
+      hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_down6_kernel<MIX>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
   const int grid = grid_for(items_bound(p, seg_lo, seg_hi, kD3Tok, kDnRows, true));
-  return launch(gemm_down6_kernel, dim3(grid), dim3(kGThreads), (size_t)kD6Lds, stream, start,
+  return launch(gemm_down6_kernel<MIX>, dim3(grid), dim3(kGThreads), (size_t)lds, stream, start,
                 stop, p, seg_lo, seg_hi, queue_counters(p, seg_lo, true));
 }
 
@@ -1981,6 +1993,10 @@ hipError_t launch_gemm_down(const FfnParams& p, hipStream_t stream, hipEvent_t s
   const bool h3 = gate_up_writes_h3(p);
   const bool h6 = gate_up_writes_h6(p);
   if (h6 && (p.h6 == nullptr || p.h6s == nullptr)) return hipErrorInvalidValue;
+  // The E2M3 routed down and the packed fp8 shared expert's down in one
+  // launch: the shared items, queued last, fill the routed items' tail.
+  if (h6 && p.w_type == MOE_W_MXFP4 && p.has_shared && p.sw_type == MOE_W_FP8E4M3_B128)
+    return down6_range<true>(p, 0, p.n_experts + 1, stream, start, stop);
   return by_type(p, stream, start, stop, [&](int wt, int lo, int hi, hipEvent_t a, hipEvent_t b) {
     if (wt != MOE_W_MXFP4) {
       // the fp8 segments of this launch: the routed ones, the shared one
@@ -1994,7 +2010,7 @@ hipError_t launch_gemm_down(const FfnParams& p, hipStream_t stream, hipEvent_t s
       return sc8 ? down_range<MOE_W_FP8E4M3_B128, 64, true>(p, lo, hi, stream, a, b)
                  : down_range<MOE_W_FP8E4M3_B128, 64, false>(p, lo, hi, stream, a, b);
     }
-    if (h6) return down6_range(p, lo, hi, stream, a, b);
+    if (h6) return down6_range<false>(p, lo, hi, stream, a, b);
     if (h3 && p.packed) return down3_range<MOE_W_MXFP4, true, true>(p, lo, hi, stream, a, b);
     if (h3)
       return sc ? down3_range<MOE_W_MXFP4, true>(p, lo, hi, stream, a, b)

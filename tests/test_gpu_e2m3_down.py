@@ -3,7 +3,8 @@ routed slots per expert): every output against the oracle on layers whose
 reductions take 4, 8, 12 and 16 steps of 128 (each a different stretch of
 the kernel's straight-line steps and of its ring of buffers), with a shared
 MXFP4 expert of the same or of a different width in the same launch, with
-the gate-first lazy skip, and with tail-pruned slots."""
+an fp8 shared expert whose E4M3-part down shares the routed down's launch,
+with the gate-first lazy skip, and with tail-pruned slots."""
 
 from dataclasses import replace
 
@@ -33,17 +34,21 @@ def _gpu():
 BASE = replace(RAGGED, hidden=512, seed=61)
 
 
-@pytest.mark.parametrize("inter,shared_inter,lazy", [
-    (512, 0, 0.0),      # 4 steps
-    (1024, 0, 0.0),     # 8
-    (1536, 0, 0.0),     # 12
-    (2048, 0, 0.0),     # 16
-    (512, 1536, 0.0),   # routed 4 steps, shared 12, one launch
-    (1536, 512, 1e-3),  # routed 12, shared 4, lazy skip
-], ids=["I512", "I1024", "I1536", "I2048", "I512_S1536", "I1536_S512_lazy"])
-def test_e2m3_down_against_the_oracle(inter, shared_inter, lazy):
-    wl = replace(BASE, inter=inter, shared_inter=shared_inter)
-    print("case e2m3 down I=%d SI=%d lazy=%g" % (inter, shared_inter, lazy), flush=True)
+@pytest.mark.parametrize("inter,shared_inter,shared,lazy", [
+    (512, 0, "mxfp4", 0.0),              # 4 steps
+    (1024, 0, "mxfp4", 0.0),             # 8
+    (1536, 0, "mxfp4", 0.0),             # 12
+    (2048, 0, "mxfp4", 0.0),             # 16
+    (512, 1536, "mxfp4", 0.0),           # routed 4 steps, shared 12, one launch
+    (1536, 512, "mxfp4", 1e-3),          # routed 12, shared 4, lazy skip
+    (512, 1536, "fp8_e4m3_b128", 0.0),   # fp8 shared down in the routed launch
+    (2048, 512, "fp8_e4m3_b128", 1e-3),  # the same, routed 16 steps, lazy skip
+], ids=["I512", "I1024", "I1536", "I2048", "I512_S1536", "I1536_S512_lazy",
+        "I512_S1536_fp8", "I2048_S512_fp8_lazy"])
+def test_e2m3_down_against_the_oracle(inter, shared_inter, shared, lazy):
+    wl = replace(BASE, inter=inter, shared_inter=shared_inter, shared=shared)
+    print("case e2m3 down I=%d SI=%d %s lazy=%g" % (inter, shared_inter, shared, lazy),
+          flush=True)
     layer = B.Layer(I.make_layer(wl, device=DEV), wl.top_k)
     assert layer.pack()
     x = I.activations(wl)
