@@ -112,7 +112,6 @@ KERNEL_TRAFFIC_KIB = {  # (workload, packed copy used): (FETCH_SIZE, WRITE_SIZE)
     ("decode1", True): (46191.4, 82.2),         # decode_fused_kernel<8, true>
     ("decode32", True): (478980.2, 3448.8),     # gemm_gate_up_kernel<0, 112, true, true, false, true, false>
     ("prefill512", True): (1168681.3, 24638.4),
-    ("hash4096", True): (1313048.1, 120447.0),  # gemm_gate_up_kernel<0, 112, true, true, false, true, true>
 }
 
 
@@ -130,12 +129,26 @@ def proj_bytes(wtype: str, rows: int, cols: int) -> int:
     return rows * cols + rows * cols // 128
 
 
-def workload_costs(wl, counts_list):
+def shared_in_routed_launch(wl, packed):
+    """Whether the shared expert's gate/up and down run in the routed
+    experts' launches: when it is stored like them, and for an fp8 shared
+    expert next to packed MXFP4 routed experts on the E2M3 down path (at
+    least 16 routed slots per expert, intermediate sizes up to 2048)."""
+    if wl.shared == wl.routed:
+        return True
+    si = wl.shared_inter or wl.inter
+    return (packed and wl.routed == "mxfp4" and wl.shared == "fp8_e4m3_b128"
+            and wl.n_tokens * wl.top_k >= 16 * wl.n_experts
+            and wl.inter <= 2048 and si <= 2048)
+
+
+def workload_costs(wl, counts_list, same=None):
     """Algorithmic bytes and flops, averaged over the steps' routings.
 
     Routed gate/up kernel: the gate and up matrices of every routed expert
-    with at least one token (plus the shared expert when it is stored like
-    the routed ones: then it runs in the same kernel) and the activations.
+    with at least one token (plus the shared expert when it runs in the same
+    launch: ``same``, by default when it is stored like the routed ones) and
+    the activations.
     Routed down kernel: the down matrices of the same experts and y.  Whole
     path: every expert touched + shared + x + router input + ids/weights + y.
     Flops: 2*2*I*H per (token, expert) for gate/up, 2*I*H for down, the
@@ -149,7 +162,8 @@ def workload_costs(wl, counts_list):
     per_dn = proj_bytes(wl.routed, h, i)
     sh_gu = 2 * proj_bytes(wl.shared, si, h)
     sh_dn = proj_bytes(wl.shared, h, si)
-    same = wl.shared == wl.routed
+    if same is None:
+        same = wl.shared == wl.routed
     n, k = wl.n_tokens, wl.top_k
     gu = dn = path = slots = 0.0
     for counts in counts_list:
@@ -430,15 +444,17 @@ def run_workload(name, steps, warmup, copies, n_pool, cpu_seconds, dev, variant=
     counts_list = routed_counts(runner, n_pool)
     used = [counts_list[(warmup + j) % n_pool] for j in range(steps)]
     used_samp = [counts_list[(first + i) % n_pool] for i in range(n_samp)]
-    costs = workload_costs(wl, used)
-    kcosts = workload_costs(wl, used_samp)
+    same = shared_in_routed_launch(wl, packed)
+    costs = workload_costs(wl, used, same)
+    kcosts = workload_costs(wl, used_samp, same)
 
     ms_per_step = elapsed / steps * 1e3
     if runner.fused:
         kernel_name = "decode_fused_kernel<%d> (moe_forward: route + group + FFN)" % (wl.hidden // 512)
         k_bytes, k_flops, issue = kcosts["path_bytes"], kcosts["path_flops"], 1.0
     else:
-        kernel_name = "routed gate/up kernel of moe_ffn_forward (+ SwiGLU)"
+        kernel_name = ("routed gate/up kernel of moe_ffn_forward (+ SwiGLU)"
+                       + (", with the shared expert's items" if same else ""))
         k_bytes, k_flops = kcosts["gate_up_bytes"], kcosts["gate_up_flops"]
         # bf16 x on the grouped GEMMs: each product issued once per E4M3 part
         # of x (two) on the scaled fp8 instruction

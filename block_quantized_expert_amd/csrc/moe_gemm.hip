@@ -1007,6 +1007,44 @@ __global__ __launch_bounds__(kGThreads, kGPerCU) void gemm_gate_up_kernel(FfnPar
   });
 }
 
+// The packed MXFP4 routed experts (writing h6) and a packed fp8 shared
+// expert in one launch: items below the routed total are routed 112-token
+// items, the rest the shared expert's 64-token items, queued last so that
+// they fill the routed items' tail.
+template <bool LAZY>
+__global__ __launch_bounds__(kGThreads, kGPerCU) void gemm_gate_up_mix_kernel(FfnParams p,
+                                                                         uint32_t* qctr) {
+  extern __shared__ __align__(16) char smem[];
+  __shared__ int s_pref[kSegMax + 1];
+  __shared__ int s_tmp[kGThreads / kWave];
+  __shared__ QueueLds s_q;
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int E = p.n_experts;
+  const int routed = item_prefix<112, kGuRows, false>(p, 0, E, s_pref, s_tmp);
+  const int ntt = (p.n_tokens + 63) / 64;
+  const int total = routed + ntt * ((p.shared_inter + kGuRows - 1) / kGuRows);
+  run_queue(ItemQueue{qctr, total, qctr != nullptr}, &s_q, [&](int item, auto&& take) {
+    if (item >= routed) {
+      const int local = item - routed, rt = local / ntt, tile = local - rt * ntt;
+      GItem it;
+      it.seg = E;
+      it.slot0 = uniform(p.n_tokens * p.top_k + tile * 64);
+      it.m = uniform(min(64, p.n_tokens - tile * 64));
+      it.row0 = uniform(rt * kGuRows);
+      dispatch_nbt<4>((it.m + 15) >> 4, [&](auto nb) {
+        gate_up_item<MOE_W_FP8E4M3_B128, 64, decltype(nb)::value, true, true, LAZY, true, false>(
+            p, it, smem, wave, lane, take);
+      });
+      return;
+    }
+    const GItem it = find_item<112, kGuRows, false>(p, 0, E, s_pref, item);
+    dispatch_nbt<7>((it.m + 15) >> 4, [&](auto nb) {
+      gate_up_item<MOE_W_MXFP4, 112, decltype(nb)::value, true, true, LAZY, true, true>(
+          p, it, smem, wave, lane, take);
+    });
+  });
+}
+
 // ------------------------------------------------------------- down
 
 template <int WT, int TT, int NBT, bool SC, typename Take>
@@ -1866,6 +1904,16 @@ hipError_t gate_up_range_as(const FfnParams& p, int seg_lo, int seg_hi, hipStrea
                 queue_counters(p, seg_lo, false));
 }
 
+template <bool LAZY>
+hipError_t gate_up_mix_as(const FfnParams& p, hipStream_t stream, hipEvent_t start,
+                          hipEvent_t stop) {
+  static const hipError_t attr = allow_lds(gemm_gate_up_mix_kernel<LAZY>);
+  if (attr != hipSuccess) return attr;
+  const int grid = grid_for(items_bound(p, 0, p.n_experts + 1, 64, kGuRows, false));
+  return launch(gemm_gate_up_mix_kernel<LAZY>, dim3(grid), dim3(kGThreads), (size_t)kGemmLds,
+                stream, start, stop, p, queue_counters(p, 0, false));
+}
+
 template <int WT, int TT, bool SC, bool O32, bool PK = false, bool H6 = false>
 hipError_t gate_up_range(const FfnParams& p, int seg_lo, int seg_hi, hipStream_t stream,
                          hipEvent_t start, hipEvent_t stop) {
@@ -1961,6 +2009,10 @@ hipError_t launch_gemm_gate_up(const FfnParams& p, hipStream_t stream, hipEvent_
   const bool o32 = x_offsets_32(p);
   const bool h6 = gate_up_writes_h6(p);
   if (h6 && (p.h6 == nullptr || p.h6s == nullptr)) return hipErrorInvalidValue;
+  // the h6-writing routed experts and a packed fp8 shared expert: one launch
+  if (h6 && p.w_type == MOE_W_MXFP4 && p.has_shared && p.sw_type == MOE_W_FP8E4M3_B128)
+    return p.lazy_tau > 0.0f ? gate_up_mix_as<true>(p, stream, start, stop)
+                             : gate_up_mix_as<false>(p, stream, start, stop);
   return by_type(p, stream, start, stop, [&](int wt, int lo, int hi, hipEvent_t a, hipEvent_t b) {
     if (wt != MOE_W_MXFP4) {
       if (!o32) return gate_up_range<MOE_W_FP8E4M3_B128, 64, false, false>(p, lo, hi, stream, a, b);
