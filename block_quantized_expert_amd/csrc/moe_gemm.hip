@@ -1009,8 +1009,10 @@ __global__ __launch_bounds__(kGThreads, kGPerCU) void gemm_gate_up_kernel(FfnPar
 
 // The packed MXFP4 routed experts (writing h6) and a packed fp8 shared
 // expert in one launch: items below the routed total are routed 112-token
-// items, the rest the shared expert's 64-token items, queued last so that
-// they fill the routed items' tail.
+// items, the rest the shared expert's 64-token items.  The shared items make
+// up the last chunks of the queue: the workgroups that start there run them
+// first, the rest take them when their own chunks run dry, so no launch
+// boundary idles the chip between the two.
 template <bool LAZY>
 __global__ __launch_bounds__(kGThreads, kGPerCU) void gemm_gate_up_mix_kernel(FfnParams p,
                                                                          uint32_t* qctr) {
@@ -1021,11 +1023,14 @@ __global__ __launch_bounds__(kGThreads, kGPerCU) void gemm_gate_up_mix_kernel(Ff
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int E = p.n_experts;
   const int routed = item_prefix<112, kGuRows, false>(p, 0, E, s_pref, s_tmp);
-  const int ntt = (p.n_tokens + 63) / 64;
-  const int total = routed + ntt * ((p.shared_inter + kGuRows - 1) / kGuRows);
+  const int ntt = (p.n_tokens + 63) / 64, nrt = (p.shared_inter + kGuRows - 1) / kGuRows;
+  const int total = routed + ntt * nrt;
   run_queue(ItemQueue{qctr, total, qctr != nullptr}, &s_q, [&](int item, auto&& take) {
     if (item >= routed) {
-      const int local = item - routed, rt = local / ntt, tile = local - rt * ntt;
+      // groups of eight token tiles, row tiles outer within a group: the
+      // items in flight on one XCD share their tokens and weight rows in L2
+      const int local = item - routed, g = local / (8 * nrt), in = local - g * 8 * nrt;
+      const int gn = min(8, ntt - 8 * g), rt = in / gn, tile = 8 * g + (in - rt * gn);
       GItem it;
       it.seg = E;
       it.slot0 = uniform(p.n_tokens * p.top_k + tile * 64);
@@ -1815,7 +1820,7 @@ __device__ __forceinline__ void down6_item(const FfnParams& p, const GItem& it, 
 }
 
 // MIX: the launch also takes an fp8 shared expert (h in E4M3 parts, its
-// packed copy), whose items then fill the routed items' tail.
+// packed copy), whose items make up the last chunks of the queue.
 template <bool MIX>
 __global__ __launch_bounds__(kGThreads, kGPerCU) void gemm_down6_kernel(FfnParams p, int seg_lo,
                                                                    int seg_hi, uint32_t* qctr) {
@@ -2046,7 +2051,7 @@ hipError_t launch_gemm_down(const FfnParams& p, hipStream_t stream, hipEvent_t s
   const bool h6 = gate_up_writes_h6(p);
   if (h6 && (p.h6 == nullptr || p.h6s == nullptr)) return hipErrorInvalidValue;
   // The E2M3 routed down and the packed fp8 shared expert's down in one
-  // launch: the shared items, queued last, fill the routed items' tail.
+  // launch (no launch boundary between the two).
   if (h6 && p.w_type == MOE_W_MXFP4 && p.has_shared && p.sw_type == MOE_W_FP8E4M3_B128)
     return down6_range<true>(p, 0, p.n_experts + 1, stream, start, stop);
   return by_type(p, stream, start, stop, [&](int wt, int lo, int hi, hipEvent_t a, hipEvent_t b) {
