@@ -1831,14 +1831,25 @@ __global__ __launch_bounds__(kGThreads, kGPerCU) void gemm_down6_kernel(FfnParam
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int total = item_prefix<kD3Tok, kDnRows, true>(p, seg_lo, seg_hi, s_pref, s_tmp);
   run_queue(ItemQueue{qctr, total, qctr != nullptr}, &s_q, [&](int item, auto&& take) {
-    const GItem it = find_item<kD3Tok, kDnRows, true>(p, seg_lo, seg_hi, s_pref, item);
-    if (MIX && it.seg == p.n_experts) {
+    if (MIX && item >= s_pref[p.n_experts - seg_lo]) {
+      // the shared expert's items in groups of eight token tiles, row
+      // tiles outer within a group (as in the gate/up)
+      const int ntt = (p.n_tokens + kD3Tok - 1) / kD3Tok, nrt = p.hidden / kDnRows;
+      const int local = item - s_pref[p.n_experts - seg_lo], g = local / (8 * nrt);
+      const int in = local - g * 8 * nrt, gn = min(8, ntt - 8 * g), rt = in / gn;
+      const int tile = 8 * g + (in - rt * gn);
+      GItem it;
+      it.seg = p.n_experts;
+      it.slot0 = uniform(p.n_tokens * p.top_k + tile * kD3Tok);
+      it.m = uniform(min(kD3Tok, p.n_tokens - tile * kD3Tok));
+      it.row0 = uniform(rt * kDnRows);
       dispatch_nbt<kD3Tok / 16>((it.m + 15) >> 4, [&](auto nb) {
         down3_item<MOE_W_FP8E4M3_B128, decltype(nb)::value, true, true>(p, it, smem, wave, lane,
                                                                        take);
       });
       return;
     }
+    const GItem it = find_item<kD3Tok, kDnRows, true>(p, seg_lo, seg_hi, s_pref, item);
     dispatch_nbt<2>((it.m + 31) >> 5, [&](auto nb) {
       down6_item<decltype(nb)::value>(p, it, smem, wave, lane, take);
     });
