@@ -112,6 +112,7 @@ KERNEL_TRAFFIC_KIB = {  # (workload, packed copy used): (FETCH_SIZE, WRITE_SIZE)
     ("decode1", True): (46191.4, 82.2),         # decode_fused_kernel<8, true>
     ("decode32", True): (478980.2, 3448.8),     # gemm_gate_up_kernel<0, 112, true, true, false, true, false>
     ("prefill512", True): (1168681.3, 24638.4),
+    ("hash4096", True): (1549354.8, 147249.9),  # gemm_gate_up_mix_kernel<false>
 }
 
 
