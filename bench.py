@@ -514,7 +514,7 @@ def run_workload(name, steps, warmup, copies, n_pool, cpu_seconds, dev, variant=
     if dn_avg_s is not None:
         dissue = 3.0 if issue > 1.0 else 1.0  # h as three E4M3 parts
         rec["down_kernel"] = {
-            "kernel": "routed down kernel of moe_ffn_forward",
+            "kernel": "routed down kernel of moe_ffn_forward" + (", with the shared expert's items" if same else ""),
             "bytes_per_launch": kcosts["down_bytes"],
             "flops_per_launch": kcosts["down_flops"],
             "avg_launch_us": dn_avg_s * 1e6,
