@@ -3,8 +3,9 @@ routed slots per expert): every output against the oracle on layers whose
 reductions take 4, 8, 12 and 16 steps of 128 (each a different stretch of
 the kernel's straight-line steps and of its ring of buffers), with a shared
 MXFP4 expert of the same or of a different width in the same launch, with
-an fp8 shared expert whose E4M3-part down shares the routed down's launch,
-with the gate-first lazy skip, and with tail-pruned slots."""
+an fp8 shared expert whose gate/up and down items share the routed
+launches (over one partial and over two groups of its token tiles), with
+the gate-first lazy skip, and with tail-pruned slots."""
 
 from dataclasses import replace
 
@@ -49,10 +50,26 @@ def test_e2m3_down_against_the_oracle(inter, shared_inter, shared, lazy):
     wl = replace(BASE, inter=inter, shared_inter=shared_inter, shared=shared)
     print("case e2m3 down I=%d SI=%d %s lazy=%g" % (inter, shared_inter, shared, lazy),
           flush=True)
+    _check(wl, COUNTS, lazy)
+
+
+# 600 tokens: ten 64-token tiles of the shared expert (the last of 24), so
+# its items form one group of eight token tiles and one of two
+COUNTS600 = [20, 46, 92, 138, 162, 208, 231, 303]
+
+
+def test_e2m3_down_fp8_shared_over_two_item_groups():
+    wl = replace(BASE, n_tokens=600, vocab=600, inter=1024, shared_inter=512,
+                 shared="fp8_e4m3_b128", seed=67)
+    print("case e2m3 down fp8 shared, 600 tokens", flush=True)
+    _check(wl, COUNTS600, 0.0)
+
+
+def _check(wl, counts, lazy):
     layer = B.Layer(I.make_layer(wl, device=DEV), wl.top_k)
     assert layer.pack()
     x = I.activations(wl)
-    pairs, wts = _table(COUNTS, wl.seed)
+    pairs, wts = _table(counts, wl.seed)
     assert pairs.shape[0] * wl.top_k >= 16 * wl.n_experts  # the E2M3 path's batch size
     tok = torch.arange(wl.n_tokens, dtype=torch.int32, device=DEV)
     ids, w = B.moe_route_hash(tok, torch.from_numpy(pairs).to(DEV),
