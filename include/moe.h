@@ -367,9 +367,11 @@ moe_status moe_ffn_down(const moe_layer* layer, const void* x, int x_type, int n
  * moe_ffn_forward that also records, into caller-created events (each may
  * be NULL), the start and end of the kernel that runs the routed experts'
  * gate/up and of the kernel that runs their down projection (the shared
- * expert is in the same kernel when it has the routed experts' weight type;
- * the activation quantization of batched calls, a shared expert of another
- * type and the combine pass run outside the timed pairs).  The times come
+ * expert is in the same kernel when it has the routed experts' weight type,
+ * and an fp8 shared expert next to packed MXFP4 routed experts when the
+ * batch holds at least 16 routed slots per expert; the activation
+ * quantization of batched calls, a shared expert in launches of its own and
+ * the combine pass run outside the timed pairs).  The times come
  * from the kernels' own dispatches, so no extra packets are queued and the
  * stream runs as it would untimed.  For benchmarks and profilers:
  * hipEventElapsedTime(start, stop) is the kernel's duration.
