@@ -368,8 +368,10 @@ moe_status moe_ffn_down(const moe_layer* layer, const void* x, int x_type, int n
  * be NULL), the start and end of the kernel that runs the routed experts'
  * gate/up and of the kernel that runs their down projection (the shared
  * expert is in the same kernel when it has the routed experts' weight type,
- * and an fp8 shared expert next to packed MXFP4 routed experts when the
- * batch holds at least 16 routed slots per expert; the activation
+ * and an fp8 shared expert next to packed MXFP4 routed experts when h
+ * goes to the down as E2M3 parts: at least 16 routed slots per expert,
+ * intermediate sizes up to 2048, the quantized activations below 2 GiB;
+ * the activation
  * quantization of batched calls, a shared expert in launches of its own and
  * the combine pass run outside the timed pairs).  The times come
  * from the kernels' own dispatches, so no extra packets are queued and the
