@@ -371,12 +371,11 @@ moe_status moe_ffn_down(const moe_layer* layer, const void* x, int x_type, int n
  * and an fp8 shared expert next to packed MXFP4 routed experts when h
  * goes to the down as E2M3 parts: at least 16 routed slots per expert,
  * intermediate sizes up to 2048, the quantized activations below 2 GiB;
- * the activation
- * quantization of batched calls, a shared expert in launches of its own and
- * the combine pass run outside the timed pairs).  The times come
- * from the kernels' own dispatches, so no extra packets are queued and the
- * stream runs as it would untimed.  For benchmarks and profilers:
- * hipEventElapsedTime(start, stop) is the kernel's duration.
+ * the activation quantization of batched calls, a shared expert in
+ * launches of its own and the combine pass run outside the timed pairs).
+ * The times come from the kernels' own dispatches, so no extra packets are
+ * queued and the stream runs as it would untimed.  For benchmarks and
+ * profilers: hipEventElapsedTime(start, stop) is the kernel's duration.
  */
 moe_status moe_ffn_forward_timed(const moe_layer* layer, const void* x, int x_type,
                                  int n_tokens, const float* topk_w, const int32_t* counts,
